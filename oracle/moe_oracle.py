@@ -1,0 +1,340 @@
+"""CPU oracle for the per-GPU MoE expert layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+load this module: only the test suite, the smoke check and the CPU-baseline
+leg of the benchmark use it.  It shares no code with the HIP library (no
+kernels, headers, helpers or tables) and imports nothing from it.
+
+Everything here is plain float64 NumPy written for a reader to check by eye:
+no blocking, no fusion, no reordering beyond what each definition states.
+
+What the pages fix, and what is a reading
+-----------------------------------------
+* The local expert computation of an expert-parallel MoE layer is "permute,
+  unpermute and grouped matmul" between the two all-to-alls; the plain
+  PyTorch form of these ops is the reference implementation, and a fused
+  form may be used only where it matches it.  (Page "FSDPTurbo EP/EFSDP and
+  LlamaFactory FSDP2/CP Design", section 3, dispatcher table, rows "eager"
+  and "fused".)  Empty experts are legal (same table, "fused" row).
+* Expert tensor shapes for Qwen3-MoE-30B-A3B: 128 experts, hidden 2048,
+  intermediate 768; gate and up projections [E, I, H], down [E, H, I]; one
+  EP rank of eight holds a [16, ...] slice along dim 0.  (Page
+  "Qwen3-MoE-30B-A3B模型EP+FSDP2并行方案", sections "Qwen3-MoE-30B-A3B模型"
+  and "完整并行流程".)  The gate tensor is printed there as [128, 768, 768];
+  a product with a hidden-size-2048 token forces [128, 768, 2048], so that
+  printed shape is read as garbled.
+* The pages never state the router math, the activation or the precision.
+  Readings used throughout (each restated where it is used):
+    - logits z = x . W_r (+ bias), W_r laid out [H, E];
+    - softmax over all E experts, keep the k largest, renormalise over the
+      kept k (identical to a softmax over the k kept logits);
+    - selection is made on logits; equal logits go to the lower expert id;
+      slot order j is (logit descending, expert id ascending);
+    - rows of an expert's group are in ascending token order (the order a
+      stable sort by expert gives), dropless (no capacity limit);
+    - expert FFN(v) = W_down . (SiLU(W_gate . v) * (W_up . v)),
+      SiLU(a) = a * sigmoid(a);
+    - on an EP rank only slots whose expert lies in [e_lo, e_hi) are
+      computed; the other slots keep their weight (no re-renormalisation)
+      and contribute zero here.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# Routing
+# --------------------------------------------------------------------------
+
+def router_logits(x, w_router, bias=None) -> np.ndarray:
+    """z[t, e] = sum_h x[t, h] * W_r[h, e] (+ bias[e]), in float64.
+
+    Reading of the router GEMM: W_r is stored [H, E]; an optional per-expert
+    bias is added to the logits (it then affects both selection and weights).
+    """
+    z = _f64(x) @ _f64(w_router)
+    if bias is not None:
+        z = z + _f64(bias)[None, :]
+    return z
+
+
+def topk_experts(z, k: int) -> np.ndarray:
+    """The k experts of each token, slot j ordered by (logit desc, expert id asc).
+
+    Reading: selection on logits (softmax is monotone, so the kept set is the
+    one the probabilities would give); equal logits go to the lower expert id.
+    Implemented as a full lexicographic sort of (-z, id) per token.
+    """
+    z = _f64(z)
+    T, E = z.shape
+    if not 1 <= k <= E:
+        raise ValueError(f"need 1 <= k <= E, got k={k}, E={E}")
+    ids = np.broadcast_to(np.arange(E), (T, E))
+    order = np.lexsort((ids, -z), axis=-1)   # last key (-z) is the primary key
+    return order[:, :k].astype(np.int32)
+
+
+def softmax(z) -> np.ndarray:
+    """Row-wise softmax exp(z - max) / sum exp(z - max), float64."""
+    z = _f64(z)
+    m = z.max(axis=-1, keepdims=True)
+    e = np.exp(z - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def gate_weights(z, idx) -> np.ndarray:
+    """w[t, j] = p[t, idx[t, j]] / sum_l p[t, idx[t, l]], p = softmax over all E.
+
+    Reading: softmax over all experts, then top-k, then renormalise over the
+    kept k (a plain top-k-then-renormalise router).
+    """
+    p = softmax(z)
+    sel = np.take_along_axis(p, np.asarray(idx, dtype=np.int64), axis=1)
+    return sel / sel.sum(axis=1, keepdims=True)
+
+
+def route(x, w_router, k: int, bias=None):
+    """Logits, top-k expert ids and renormalised gate weights of every token."""
+    z = router_logits(x, w_router, bias)
+    idx = topk_experts(z, k)
+    return z, idx, gate_weights(z, idx)
+
+
+# --------------------------------------------------------------------------
+# Grouping of routed rows by expert ("permute" / "unpermute")
+# --------------------------------------------------------------------------
+
+def expert_counts(idx, e_lo: int, e_hi: int) -> np.ndarray:
+    """counts[e - e_lo] = number of (token, slot) pairs routed to expert e."""
+    idx = np.asarray(idx)
+    return np.array([np.count_nonzero(idx == e) for e in range(e_lo, e_hi)], dtype=np.int64)
+
+
+def expert_offsets(counts) -> np.ndarray:
+    """Exclusive prefix sum of the counts; offsets[E_l] = R, the routed rows."""
+    counts = np.asarray(counts, dtype=np.int64)
+    off = np.zeros(len(counts) + 1, dtype=np.int64)
+    for e in range(len(counts)):
+        off[e + 1] = off[e] + counts[e]
+    return off
+
+
+def permutation_maps(idx, e_lo: int, e_hi: int):
+    """Row maps of the expert-grouped buffer.
+
+    dest_row[t*k + j] = offsets[e - e_lo] + #{t' < t : token t' also chose e},
+    with e = idx[t, j] local; -1 for slots whose expert is not in [e_lo, e_hi).
+    src_row[r] = token whose row lands in grouped row r (inverse of dest_row).
+
+    Reading: rows of an expert group are in ascending token order, which is
+    what a stable sort of the (token, slot) list by expert id produces.  A
+    token's k experts are distinct, so this order is unique.
+    """
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    E_l = e_hi - e_lo
+    off = expert_offsets(expert_counts(idx, e_lo, e_hi))
+    seen = np.zeros(E_l, dtype=np.int64)
+    dest = np.full(T * k, -1, dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            if e_lo <= e < e_hi:
+                dest[t * k + j] = off[e - e_lo] + seen[e - e_lo]
+                seen[e - e_lo] += 1
+    R = int(off[E_l])
+    src = np.full(R, -1, dtype=np.int64)
+    for s in range(T * k):
+        if dest[s] >= 0:
+            src[dest[s]] = s // k
+    return dest, src
+
+
+def permute_rows(x, dest_row, R: int) -> np.ndarray:
+    """x_perm[dest_row[t*k+j]] = x[t] for every local slot (the permute)."""
+    x = _f64(x)
+    T = x.shape[0]
+    k = len(dest_row) // T
+    out = np.full((R, x.shape[1]), np.nan)
+    for s, r in enumerate(dest_row):
+        if r >= 0:
+            out[r] = x[s // k]
+    return out
+
+
+def unpermute_rows(y_perm, dest_row, T: int, weights=None) -> np.ndarray:
+    """y[t] = sum_j weight[t, j] * y_perm[dest_row[t*k+j]] over local slots,
+    j ascending (weight 1 when weights is None): the (weighted) unpermute."""
+    y_perm = _f64(y_perm)
+    k = len(dest_row) // T
+    out = np.zeros((T, y_perm.shape[1]))
+    for t in range(T):
+        for j in range(k):
+            r = dest_row[t * k + j]
+            if r >= 0:
+                c = 1.0 if weights is None else float(weights[t, j])
+                out[t] += c * y_perm[r]
+    return out
+
+
+# --------------------------------------------------------------------------
+# Expert FFN
+# --------------------------------------------------------------------------
+
+def sigmoid(a) -> np.ndarray:
+    a = _f64(a)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-a))
+
+
+def silu(a) -> np.ndarray:
+    """SiLU(a) = a * sigmoid(a) (reading: the SwiGLU expert activation)."""
+    a = _f64(a)
+    return a * sigmoid(a)
+
+
+def expert_ffn_parts(v, w_gate_e, w_up_e, w_down_e) -> Dict[str, np.ndarray]:
+    """One expert on rows v [n, H]: g = v.W_gate^T, u = v.W_up^T,
+    h = SiLU(g) * u, y = h.W_down^T  (W_gate/W_up [I, H], W_down [H, I])."""
+    v = _f64(v)
+    g = v @ _f64(w_gate_e).T
+    u = v @ _f64(w_up_e).T
+    h = silu(g) * u
+    y = h @ _f64(w_down_e).T
+    return {"g": g, "u": u, "h": h, "y": y}
+
+
+def expert_ffn(v, w_gate_e, w_up_e, w_down_e) -> np.ndarray:
+    return expert_ffn_parts(v, w_gate_e, w_up_e, w_down_e)["y"]
+
+
+def _local_slots(idx, e_lo, e_hi, e):
+    """(tokens, slots) of all pairs routed to expert e, tokens ascending."""
+    tt, jj = np.nonzero(np.asarray(idx) == e)
+    return tt, jj
+
+
+def moe_forward(x, idx, w, w_gate, w_up, w_down, e_lo: int, e_hi: int) -> np.ndarray:
+    """y[t] = sum over local slots j of w[t, j] * FFN_{idx[t,j]}(x[t]).
+
+    Grouped by expert with a boolean selection of the routed tokens (no
+    permutation buffer, no offsets); a token with no local slot gets zero.
+    """
+    x = _f64(x)
+    y = np.zeros_like(x)
+    for e in range(e_lo, e_hi):
+        tt, jj = _local_slots(idx, e_lo, e_hi, e)
+        if len(tt) == 0:
+            continue
+        ye = expert_ffn(x[tt], w_gate[e - e_lo], w_up[e - e_lo], w_down[e - e_lo])
+        np.add.at(y, tt, _f64(w)[tt, jj][:, None] * ye)
+    return y
+
+
+def moe_forward_pairs(x, idx, w, w_gate, w_up, w_down, e_lo: int, e_hi: int) -> np.ndarray:
+    """Literal per-(token, slot) loop of the same definition (small inputs only)."""
+    x = _f64(x)
+    T, k = np.asarray(idx).shape
+    y = np.zeros_like(x)
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            if e_lo <= e < e_hi:
+                y[t] += float(w[t, j]) * expert_ffn(x[t:t + 1], w_gate[e - e_lo], w_up[e - e_lo],
+                                                    w_down[e - e_lo])[0]
+    return y
+
+
+def pair_values(x, idx, w_gate, w_up, w_down, e_lo: int, e_hi: int,
+                tokens: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+    """Per (token, slot) intermediates g, u, h [n, k, I] and expert output y [n, k, H]
+    for the listed tokens (all when None); NaN for non-local slots."""
+    x = _f64(x)
+    idx = np.asarray(idx)
+    toks = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens)
+    k = idx.shape[1]
+    I = w_gate.shape[1]
+    H = x.shape[1]
+    out = {n: np.full((len(toks), k, d), np.nan) for n, d in (("g", I), ("u", I), ("h", I), ("y", H))}
+    for a, t in enumerate(toks):
+        for j in range(k):
+            e = int(idx[t, j])
+            if e_lo <= e < e_hi:
+                p = expert_ffn_parts(x[t:t + 1], w_gate[e - e_lo], w_up[e - e_lo], w_down[e - e_lo])
+                for n in out:
+                    out[n][a, j] = p[n][0]
+    return out
+
+
+# --------------------------------------------------------------------------
+# Backward
+# --------------------------------------------------------------------------
+
+def moe_backward(x, w_router, idx, w, w_gate, w_up, w_down, dy, e_lo: int, e_hi: int
+                 ) -> Dict[str, np.ndarray]:
+    """Gradients of L = sum(dy * y) for the layer above, hand-derived.
+
+    With e = idx[t, j] local, g = W_gate[e] x, u = W_up[e] x, h = SiLU(g) u,
+    o = W_down[e] h and delta = w[t, j] dy[t]:
+      dw[t, j]       = <dy[t], o>           (0 for non-local slots)
+      dW_down[e]    += delta h^T
+      dh             = W_down[e]^T delta
+      dg             = dh * u * s * (1 + g (1 - s)),  s = sigmoid(g)
+      du             = dh * SiLU(g)
+      dW_gate[e]    += dg x^T,  dW_up[e] += du x^T
+      dx[t]         += W_gate[e]^T dg + W_up[e]^T du
+    Router: w is a softmax over the kept logits, so
+      dz[t, idx[t, j]] = w_j (dw_j - sum_l w_l dw_l), and dz = 0 elsewhere;
+      dx[t] += W_r dz[t]  and  dW_r = x^T dz.
+    Non-local slots keep dw = 0 but still enter the softmax Jacobian (the
+    other EP ranks add their own terms; the sum over ranks is the full
+    gradient because the Jacobian is linear in dw).
+    """
+    x = _f64(x)
+    dy = _f64(dy)
+    w = _f64(w)
+    idx = np.asarray(idx)
+    T, H = x.shape
+    k = idx.shape[1]
+    E = np.asarray(w_router).shape[1]
+    E_l = e_hi - e_lo
+    I = np.asarray(w_gate).shape[1]
+
+    dw = np.zeros((T, k))
+    dx = np.zeros((T, H))
+    dWg = np.zeros((E_l, I, H))
+    dWu = np.zeros((E_l, I, H))
+    dWd = np.zeros((E_l, H, I))
+    for e in range(e_lo, e_hi):
+        tt, jj = _local_slots(idx, e_lo, e_hi, e)
+        if len(tt) == 0:
+            continue
+        Wg, Wu, Wd = _f64(w_gate[e - e_lo]), _f64(w_up[e - e_lo]), _f64(w_down[e - e_lo])
+        p = expert_ffn_parts(x[tt], Wg, Wu, Wd)
+        g, u, h, o = p["g"], p["u"], p["h"], p["y"]
+        dw[tt, jj] = np.sum(dy[tt] * o, axis=1)
+        delta = w[tt, jj][:, None] * dy[tt]
+        dWd[e - e_lo] = delta.T @ h
+        dh = delta @ Wd
+        s = sigmoid(g)
+        dg = dh * u * s * (1.0 + g * (1.0 - s))
+        du = dh * (g * s)
+        dWg[e - e_lo] = dg.T @ x[tt]
+        dWu[e - e_lo] = du.T @ x[tt]
+        np.add.at(dx, tt, dg @ Wg + du @ Wu)
+
+    dz = np.zeros((T, E))
+    inner = np.sum(w * dw, axis=1, keepdims=True)
+    np.put_along_axis(dz, idx.astype(np.int64), w * (dw - inner), axis=1)
+    Wr = _f64(w_router)
+    dx += dz @ Wr.T
+    dWr = x.T @ dz
+    return {"dw": dw, "d_logits": dz, "dx": dx, "dw_router": dWr,
+            "dw_gate": dWg, "dw_up": dWu, "dw_down": dWd}

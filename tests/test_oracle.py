@@ -1,0 +1,434 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each check compares the oracle with a closed form (hand-derived golden
+fixtures), a brute force on tiny inputs, an invariant, a special case that
+reduces to a textbook or library routine, or an independent float64 autograd
+computation.  The mutation tests at the end plant plausible mistakes in the
+oracle (on the CPU) and require at least one check to fail for each.
+"""
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle as O
+from oracle import moe_oracle as OM
+from workloads import TINY, make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------
+# helpers
+# ----------------------------------------------------------------------------
+
+def _tiny(**kw):
+    w = TINY.scaled(**kw)
+    return w, make_inputs(w)
+
+
+def _eval_expr(s):
+    """Evaluate a fixture expression over L = ln 3 (no names besides L)."""
+    return float(eval(s, {"__builtins__": {}}, {"L": math.log(3.0)}))
+
+
+def _read_gating_golden():
+    cases = []
+    with open(os.path.join(GOLDEN, "gating_closed_form.txt")) as f:
+        for line in f:
+            if not line.startswith("case "):
+                continue
+            name, k, cs, ids, ws = [p.strip() for p in line[5:].split("|")]
+            cases.append((name, int(k), [int(c) for c in cs.split()], [int(i) for i in ids.split()],
+                          [Fraction(w) for w in ws.split()]))
+    return cases
+
+
+def _read_scalar_golden():
+    vals, expect = {}, {}
+    with open(os.path.join(GOLDEN, "scalar_layer_closed_form.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            lhs, rhs = [p.strip() for p in line.split("=", 1)]
+            nums = [_eval_expr(p) for p in rhs.split(",")]
+            if lhs.startswith("expect "):
+                expect[lhs[7:].strip()] = np.array(nums)
+            else:
+                vals[lhs] = np.array(nums)
+    return vals, expect
+
+
+def _rel(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+
+
+# ----------------------------------------------------------------------------
+# checks (raise AssertionError on failure; reused by the mutation tests)
+# ----------------------------------------------------------------------------
+
+def check_gating_golden():
+    for name, k, cs, ids, ws in _read_gating_golden():
+        z = np.log(np.array([cs], dtype=np.float64))
+        idx = O.topk_experts(z, k)
+        assert idx[0].tolist() == ids, (name, idx[0].tolist(), ids)
+        w = O.gate_weights(z, idx)[0]
+        np.testing.assert_allclose(w, [float(x) for x in ws], rtol=1e-14, atol=0, err_msg=name)
+
+
+def check_topk_brute_force():
+    """Unique k-subset S with every member ahead of every non-member in the
+    order (logit desc, id asc); slots ordered within S by pairwise dominance."""
+    rng = np.random.default_rng(7)
+    for trial in range(60):
+        E = int(rng.integers(1, 7))
+        k = int(rng.integers(1, E + 1))
+        z = rng.integers(-2, 3, size=(3, E)).astype(np.float64)  # many exact ties
+        idx = O.topk_experts(z, k)
+        for t in range(z.shape[0]):
+            def ahead(a, b):
+                return z[t, a] > z[t, b] or (z[t, a] == z[t, b] and a < b)
+            good = [S for S in itertools.combinations(range(E), k)
+                    if all(ahead(s, o) for s in S for o in range(E) if o not in S)]
+            assert len(good) == 1
+            S = list(good[0])
+            # position of s = number of members ahead of it
+            ordered = sorted(S, key=lambda s: sum(ahead(o, s) for o in S))
+            assert idx[t].tolist() == ordered, (z[t], k, idx[t], ordered)
+
+
+def check_zero_input_routing():
+    w, inp = _tiny()
+    x = np.zeros_like(inp["x"])
+    z, idx, g = O.route(x, inp["w_router"], w.k)
+    assert (idx == np.arange(w.k)[None, :]).all()
+    assert (g == 1.0 / w.k).all()
+
+
+def check_duplicate_router_columns():
+    w, inp = _tiny(k=3)
+    wr = inp["w_router"].copy()
+    wr[:, 5] = wr[:, 2]
+    wr[:, 7] = wr[:, 2]
+    z, idx, g = O.route(inp["x"], wr, w.k)
+    for t in range(w.T):
+        s = idx[t].tolist()
+        for dup in (5, 7):
+            if dup in s:
+                assert 2 in s and s.index(2) < s.index(dup)
+
+
+def check_k1_and_kE():
+    w, inp = _tiny()
+    z = O.router_logits(inp["x"], inp["w_router"])
+    _, idx1, g1 = O.route(inp["x"], inp["w_router"], 1)
+    assert (g1 == 1.0).all()
+    assert (idx1[:, 0] == np.argmax(z, axis=1)).all()
+    _, idxE, gE = O.route(inp["x"], inp["w_router"], w.E)
+    ref = scipy.special.softmax(z, axis=1)
+    np.testing.assert_allclose(gE, np.take_along_axis(ref, idxE.astype(np.int64), 1), rtol=1e-13)
+
+
+def check_weights_sum_to_one():
+    w, inp = _tiny(k=3)
+    _, _, g = O.route(inp["x"], inp["w_router"], w.k)
+    assert np.abs(g.sum(1) - 1).max() < 1e-14
+    assert (g > 0).all()
+
+
+def check_counts_offsets():
+    for (k, e_lo, e_hi) in ((2, 0, 8), (3, 2, 6), (1, 7, 8)):
+        w, inp = _tiny(k=k, e_lo=e_lo, e_hi=e_hi, E=8)
+        _, idx, _ = O.route(inp["x"], inp["w_router"], k)
+        c = O.expert_counts(idx, e_lo, e_hi)
+        bc = np.bincount(idx.ravel(), minlength=8)[e_lo:e_hi]
+        assert (c == bc).all()
+        off = O.expert_offsets(c)
+        assert off[0] == 0 and (np.diff(off) >= 0).all()
+        nloc = int(((idx >= e_lo) & (idx < e_hi)).sum())
+        assert off[-1] == nloc
+        if (e_lo, e_hi) == (0, 8):
+            assert off[-1] == w.T * k
+
+
+def check_permutation_maps():
+    for (k, e_lo, e_hi) in ((2, 0, 8), (3, 2, 6), (1, 0, 8)):
+        w, inp = _tiny(k=k, e_lo=e_lo, e_hi=e_hi)
+        _, idx, _ = O.route(inp["x"], inp["w_router"], k)
+        dest, src = O.permutation_maps(idx, e_lo, e_hi)
+        off = O.expert_offsets(O.expert_counts(idx, e_lo, e_hi))
+        R = int(off[-1])
+        flat = idx.ravel()
+        local = (flat >= e_lo) & (flat < e_hi)
+        assert (dest[~local] == -1).all()
+        assert sorted(dest[local].tolist()) == list(range(R))          # bijection onto [0, R)
+        assert (src[dest[local]] == np.nonzero(local)[0] // k).all()    # inverse map
+        for e in range(e_hi - e_lo):                                   # tokens ascending per group
+            seg = src[off[e]:off[e + 1]]
+            assert (np.diff(seg) > 0).all()
+        # independent construction: stable argsort of slots by expert id
+        slots = np.nonzero(local)[0]
+        order = slots[np.argsort(flat[slots], kind="stable")]
+        assert (dest[order] == np.arange(R)).all()
+
+
+def check_permute_unpermute_identity():
+    w, inp = _tiny()
+    _, idx, _ = O.route(inp["x"], inp["w_router"], w.k)
+    dest, src = O.permutation_maps(idx, 0, w.E)
+    xp = O.permute_rows(inp["x"], dest, len(src))
+    back = O.unpermute_rows(xp, dest, w.T)
+    assert (back == w.k * inp["x"].astype(np.float64)).all()
+    w1, inp1 = _tiny(k=1)
+    _, idx1, _ = O.route(inp1["x"], inp1["w_router"], 1)
+    d1, s1 = O.permutation_maps(idx1, 0, w1.E)
+    assert (O.unpermute_rows(O.permute_rows(inp1["x"], d1, len(s1)), d1, w1.T) == inp1["x"]).all()
+
+
+def _dense_masked(x, idx, gw, wg, wu, wd, e_lo, e_hi):
+    """Every local expert on every token, then a dense [T, E_l] gate mask."""
+    x = np.asarray(x, np.float64)
+    T = x.shape[0]
+    M = np.zeros((T, e_hi - e_lo))
+    for t in range(T):
+        for j in range(idx.shape[1]):
+            if e_lo <= idx[t, j] < e_hi:
+                M[t, idx[t, j] - e_lo] = gw[t, j]
+    y = np.zeros_like(x)
+    for e in range(e_hi - e_lo):
+        g = x @ np.asarray(wg[e], np.float64).T
+        u = x @ np.asarray(wu[e], np.float64).T
+        h = g / (1.0 + np.exp(-g)) * u
+        y += M[:, e:e + 1] * (h @ np.asarray(wd[e], np.float64).T)
+    return y
+
+
+def check_dense_equals_routed():
+    for (k, e_lo, e_hi) in ((2, 0, 8), (3, 2, 5)):
+        w, inp = _tiny(k=k, e_lo=e_lo, e_hi=e_hi)
+        _, idx, gw = O.route(inp["x"], inp["w_router"], k)
+        y = O.moe_forward(inp["x"], idx, gw, inp["w_gate"], inp["w_up"], inp["w_down"], e_lo, e_hi)
+        yd = _dense_masked(inp["x"], idx, gw, inp["w_gate"], inp["w_up"], inp["w_down"], e_lo, e_hi)
+        assert _rel(y, yd) < 1e-12
+        yp = O.moe_forward_pairs(inp["x"][:32], idx[:32], gw[:32], inp["w_gate"], inp["w_up"],
+                                 inp["w_down"], e_lo, e_hi)
+        assert _rel(yp, y[:32]) < 1e-12
+
+
+def check_single_expert_is_swiglu_mlp():
+    w, inp = _tiny(E=1, k=1, e_lo=0, e_hi=1)
+    _, idx, gw = O.route(inp["x"], inp["w_router"], 1)
+    y = O.moe_forward(inp["x"], idx, gw, inp["w_gate"], inp["w_up"], inp["w_down"], 0, 1)
+    xt = torch.tensor(inp["x"], dtype=torch.float64)
+    ref = torch.nn.functional.linear(
+        torch.nn.functional.silu(torch.nn.functional.linear(xt, torch.tensor(inp["w_gate"][0], dtype=torch.float64)))
+        * torch.nn.functional.linear(xt, torch.tensor(inp["w_up"][0], dtype=torch.float64)),
+        torch.tensor(inp["w_down"][0], dtype=torch.float64))
+    assert _rel(y, ref.numpy()) < 1e-13
+
+
+def check_zero_projection_gives_zero():
+    w, inp = _tiny()
+    _, idx, gw = O.route(inp["x"], inp["w_router"], w.k)
+    for key in ("w_up", "w_gate"):
+        ww = dict(inp)
+        ww[key] = np.zeros_like(inp[key])
+        y = O.moe_forward(inp["x"], idx, gw, ww["w_gate"], ww["w_up"], ww["w_down"], 0, w.E)
+        assert (y == 0).all()
+
+
+def check_scalar_golden():
+    v, ex = _read_scalar_golden()
+    x = v["x"].reshape(1, 1)
+    wr = v["w_router"].reshape(1, 2)
+    wg = v["w_gate"].reshape(2, 1, 1)
+    wu = v["w_up"].reshape(2, 1, 1)
+    wd = v["w_down"].reshape(2, 1, 1)
+    dy = v["dy"].reshape(1, 1)
+    k = int(v["k"][0])
+    z, idx, gw = O.route(x, wr, k)
+    assert idx[0].tolist() == [int(i) for i in ex["idx"]]
+    np.testing.assert_allclose(gw[0], ex["w"], rtol=1e-14)
+    y = O.moe_forward(x, idx, gw, wg, wu, wd, 0, 2)
+    np.testing.assert_allclose(y.ravel(), ex["y"], rtol=1e-13)
+    gr = O.moe_backward(x, wr, idx, gw, wg, wu, wd, dy, 0, 2)
+    np.testing.assert_allclose(gr["dw"][0], ex["dw"], rtol=1e-13)
+    np.testing.assert_allclose(gr["d_logits"][0], ex["d_logits"], rtol=1e-13)
+    np.testing.assert_allclose(gr["dw_router"][0], ex["dw_router"], rtol=1e-13)
+    np.testing.assert_allclose(gr["dw_down"].ravel(), ex["dw_down"], rtol=1e-13)
+    np.testing.assert_allclose(gr["dw_gate"].ravel(), ex["dw_gate"], rtol=1e-13)
+    np.testing.assert_allclose(gr["dw_up"].ravel(), ex["dw_up"], rtol=1e-13)
+    np.testing.assert_allclose(gr["dx"].ravel(), ex["dx"], rtol=1e-13)
+
+
+def _torch_forward(x, wr, wg, wu, wd, idx, e_lo, e_hi):
+    """Independent float64 torch forward (dense-masked form) for autograd."""
+    z = x @ wr
+    p = torch.softmax(z, dim=-1)
+    psel = p.gather(1, idx)
+    gw = psel / psel.sum(1, keepdim=True)
+    T = x.shape[0]
+    y = torch.zeros_like(x)
+    for e in range(e_lo, e_hi):
+        m = (idx == e).to(x.dtype)                      # [T, k]
+        coef = (gw * m).sum(1, keepdim=True)            # weight of expert e per token
+        out = torch.nn.functional.linear(
+            torch.nn.functional.silu(torch.nn.functional.linear(x, wg[e - e_lo]))
+            * torch.nn.functional.linear(x, wu[e - e_lo]), wd[e - e_lo])
+        y = y + coef * out
+    return z, gw, y
+
+
+def check_backward_vs_autograd():
+    for (k, e_lo, e_hi) in ((2, 0, 8), (3, 1, 6)):
+        w, inp = _tiny(k=k, e_lo=e_lo, e_hi=e_hi, T=96)
+        rng = np.random.default_rng(3)
+        dy = rng.standard_normal((w.T, w.H))
+        _, idx, gw = O.route(inp["x"], inp["w_router"], k)
+        gr = O.moe_backward(inp["x"], inp["w_router"], idx, gw, inp["w_gate"], inp["w_up"],
+                            inp["w_down"], dy, e_lo, e_hi)
+        t = {n: torch.tensor(inp[n], dtype=torch.float64, requires_grad=True)
+             for n in ("x", "w_router", "w_gate", "w_up", "w_down")}
+        z, g, y = _torch_forward(t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"],
+                                 torch.tensor(idx, dtype=torch.int64), e_lo, e_hi)
+        z.retain_grad()
+        g.retain_grad()
+        (y * torch.tensor(dy)).sum().backward()
+        assert _rel(gr["dx"], t["x"].grad.numpy()) < 1e-11
+        assert _rel(gr["dw_router"], t["w_router"].grad.numpy()) < 1e-11
+        assert _rel(gr["dw_gate"], t["w_gate"].grad.numpy()) < 1e-11
+        assert _rel(gr["dw_up"], t["w_up"].grad.numpy()) < 1e-11
+        assert _rel(gr["dw_down"], t["w_down"].grad.numpy()) < 1e-11
+        assert _rel(gr["d_logits"], z.grad.numpy()) < 1e-11
+        assert _rel(gr["dw"], g.grad.numpy()) < 1e-11
+        assert np.abs(gr["d_logits"].sum(1)).max() < 1e-12       # softmax Jacobian rows sum to 0
+        off = np.ones_like(gr["d_logits"], dtype=bool)
+        np.put_along_axis(off, idx.astype(np.int64), False, axis=1)
+        assert (gr["d_logits"][off] == 0).all()
+        nonlocal_ = (idx < e_lo) | (idx >= e_hi)
+        assert (gr["dw"][nonlocal_] == 0).all()
+
+
+def check_finite_differences():
+    w, inp = _tiny(T=12, k=2)
+    rng = np.random.default_rng(11)
+    dy = rng.standard_normal((w.T, w.H))
+    z, idx, gw = O.route(inp["x"], inp["w_router"], w.k)
+    srt = np.sort(z, axis=1)[:, ::-1]
+    assert (srt[:, w.k - 1] - srt[:, w.k] > 1e-3).all()  # routing is stable under the step
+    gr = O.moe_backward(inp["x"], inp["w_router"], idx, gw, inp["w_gate"], inp["w_up"],
+                        inp["w_down"], dy, 0, w.E)
+
+    def loss(**over):
+        p = {n: np.asarray(inp[n], np.float64) for n in ("x", "w_router", "w_gate", "w_up", "w_down")}
+        p.update(over)
+        zz, ii, gg = O.route(p["x"], p["w_router"], w.k)
+        assert (ii == idx).all()
+        return float((O.moe_forward(p["x"], ii, gg, p["w_gate"], p["w_up"], p["w_down"], 0, w.E) * dy).sum())
+
+    h = 1e-6
+    for name, gname, pos in (("x", "dx", (3, 5)), ("x", "dx", (7, 60)), ("w_router", "dw_router", (10, 4)),
+                             ("w_gate", "dw_gate", (int(idx[0, 0]), 2, 9)),
+                             ("w_up", "dw_up", (int(idx[1, 0]), 30, 1)),
+                             ("w_down", "dw_down", (int(idx[2, 1]), 40, 7))):
+        base = np.asarray(inp[name], np.float64)
+        p1, m1 = base.copy(), base.copy()
+        p1[pos] += h
+        m1[pos] -= h
+        fd = (loss(**{name: p1}) - loss(**{name: m1})) / (2 * h)
+        an = gr[gname][pos]
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, pos, fd, an)
+
+
+ALL_CHECKS = [check_gating_golden, check_topk_brute_force, check_zero_input_routing,
+              check_duplicate_router_columns, check_k1_and_kE, check_weights_sum_to_one,
+              check_counts_offsets, check_permutation_maps, check_permute_unpermute_identity,
+              check_dense_equals_routed, check_single_expert_is_swiglu_mlp,
+              check_zero_projection_gives_zero, check_scalar_golden, check_backward_vs_autograd,
+              check_finite_differences]
+
+
+@pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
+def test_oracle_pin(check):
+    check()
+
+
+# ----------------------------------------------------------------------------
+# planted mistakes: each must make at least one pin fail
+# ----------------------------------------------------------------------------
+
+def _mut_silu_is_sigmoid(a):
+    return OM.sigmoid(a)
+
+
+def _mut_topk_ties_high(z, k):
+    z = np.asarray(z, np.float64)
+    T, E = z.shape
+    ids = np.broadcast_to(-np.arange(E), (T, E))
+    return np.lexsort((ids, -z), axis=-1)[:, :k].astype(np.int32)
+
+
+def _mut_no_renorm(z, idx):
+    return np.take_along_axis(OM.softmax(z), np.asarray(idx, np.int64), axis=1)
+
+
+def _mut_group_tokens_descending(idx, e_lo, e_hi):
+    dest, src = _ORIG["permutation_maps"](idx, e_lo, e_hi)
+    idx = np.asarray(idx)
+    off = OM.expert_offsets(OM.expert_counts(idx, e_lo, e_hi))
+    for e in range(e_hi - e_lo):
+        src[off[e]:off[e + 1]] = src[off[e]:off[e + 1]][::-1].copy()
+    k = idx.shape[1]
+    for r, t in enumerate(src):
+        for j in range(k):
+            if idx[t, j] - e_lo == np.searchsorted(off, r, side="right") - 1:
+                dest[t * k + j] = r
+    return dest, src
+
+
+def _mut_backward_sign(*a, **kw):
+    g = _ORIG["moe_backward"](*a, **kw)
+    g["d_logits"] = -g["d_logits"]
+    return g
+
+
+def _mut_backward_drop_router_dx(x, w_router, idx, w, *rest):
+    g = _ORIG["moe_backward"](x, np.zeros_like(np.asarray(w_router)), idx, w, *rest)
+    g["dw_router"] = _ORIG["moe_backward"](x, w_router, idx, w, *rest)["dw_router"]
+    return g
+
+
+def _mut_ffn_drops_up(v, wg, wu, wd):
+    p = _ORIG["expert_ffn_parts"](v, wg, wu, wd)
+    p["h"] = OM.silu(p["g"])          # dropped factor: the up projection
+    p["y"] = p["h"] @ np.asarray(wd, np.float64).T
+    return p
+
+
+_ORIG = {n: getattr(OM, n) for n in ("silu", "topk_experts", "gate_weights", "permutation_maps",
+                                     "moe_backward", "expert_ffn_parts")}
+
+MUTATIONS = [("silu", _mut_silu_is_sigmoid), ("topk_experts", _mut_topk_ties_high),
+             ("gate_weights", _mut_no_renorm), ("permutation_maps", _mut_group_tokens_descending),
+             ("moe_backward", _mut_backward_sign), ("moe_backward", _mut_backward_drop_router_dx),
+             ("expert_ffn_parts", _mut_ffn_drops_up)]
+
+
+@pytest.mark.parametrize("name,mut", MUTATIONS, ids=[m[1].__name__ for m in MUTATIONS])
+def test_planted_mistake_is_caught(monkeypatch, name, mut):
+    monkeypatch.setattr(OM, name, mut)
+    monkeypatch.setattr(O, name, mut, raising=False)
+    failed = []
+    for chk in ALL_CHECKS:
+        try:
+            chk()
+        except AssertionError:
+            failed.append(chk.__name__)
+    assert failed, f"no pin caught the planted mistake in {name}"
