@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark of the per-GPU MoE expert layer on one MI355X.
+
+One step = the whole layer on one batch of seeded synthetic inputs already
+resident in HBM: router GEMM + top-k, permute, grouped SwiGLU FFN, combine,
+and (for training workloads) the backward of every one of them.  The default
+workload is the training step of one EP rank's share of the 128-expert
+Qwen3-MoE-30B-A3B-shaped layer (T=8192 tokens, H=2048, I=768, 16 local experts
+of 128, top-8, bf16, fp32 accumulation and fp32 weight gradients).
+
+Prints ONE JSON line.  value = algorithmic TFLOP/s of the whole step
+(router 2THE, expert FFN 6RHI forward and 12RHI backward, router backward
+2THE + 2TkH; R = routed rows kept on this GPU).
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (vector/matrix)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+KERNELS = ["ROUTE", "PERMUTE_HIST", "PERMUTE_SCAN", "PERMUTE_SCATTER", "FFN_GATEUP", "FFN_DOWN",
+           "COMBINE", "COMBINE_BWD", "ROUTE_BWD_DZ", "ROUTE_BWD_DW", "FFN_DOWN_DGRAD",
+           "FFN_DOWN_WGRAD", "FFN_GATEUP_DGRAD", "FFN_GATEUP_WGRAD"]
+
+
+def step_flops(w, R):
+    f = 2.0 * w.T * w.H * w.E + 6.0 * R * w.H * w.I
+    if w.train:
+        f += 12.0 * R * w.H * w.I + 2.0 * w.T * w.H * w.E + 2.0 * w.T * w.k * w.H
+    return f
+
+
+def kernel_work(name, w, R, launches):
+    """Algorithmic (flops, HBM bytes) of ONE launch of a kernel."""
+    T, H, I, E, k, El = w.T, w.H, w.I, w.E, w.k, w.E_l
+    b = 2 if w.dtype == "bf16" else 4
+    gu = 2 * I * b * R if w.train else 0
+    tab = {
+        "ROUTE": (2.0 * T * H * E, T * H * b + H * E * b + T * E * 4 + T * k * 8),
+        "PERMUTE_HIST": (0, T * k * 8 + (T // 256 + 1) * El * 4),
+        "PERMUTE_SCAN": (0, 2 * (T // 256 + 1) * El * 4),
+        "PERMUTE_SCATTER": (0, T * H * b + R * H * b + T * k * 12 + R * 4),
+        "FFN_GATEUP": (4.0 * R * H * I, R * H * b + 2 * El * I * H * b + R * I * b + gu),
+        "FFN_DOWN": (2.0 * R * H * I, R * I * b + El * H * I * b + R * H * b),
+        "COMBINE_BWD": (0, 2 * T * H * b + 2 * R * H * b + T * k * 12),
+        "ROUTE_BWD_DZ": (2.0 * T * k * H, T * k * 12 + E * H * b + T * E * 4 + T * H * 4 + T * 2 * E * 2),
+        "ROUTE_BWD_DW": (2.0 * T * H * E, T * H * b + T * 2 * E * 2 + H * E * 4),
+        "FFN_DOWN_DGRAD": (2.0 * R * H * I, R * H * b + El * H * I * b + 2 * R * 2 * I * b),
+        "FFN_DOWN_WGRAD": (2.0 * R * H * I, R * H * b + R * I * b + El * H * I * 4),
+        "FFN_GATEUP_DGRAD": (4.0 * R * H * I, R * 2 * I * b + 2 * El * I * H * b + R * H * b),
+        "FFN_GATEUP_WGRAD": (4.0 * R * H * I, R * 2 * I * b + R * H * b + 2 * El * I * H * 4),
+    }
+    if name == "COMBINE":
+        fwd = R * H * b + T * k * 8 + T * H * b
+        bwd = R * H * b + T * k * 4 + T * H * 4 + T * H * b
+        return 0.0, (fwd + bwd) / 2.0 if (w.train and launches == 2) else fwd
+    return tab[name]
+
+
+def roofline_of(name, w, R, avg_us, launches):
+    flops, nbytes = kernel_work(name, w, R, launches)
+    peak_f = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    t_f = flops / (peak_f * 1e12)
+    t_b = nbytes / (PEAK_HBM_GBS * 1e9)
+    if flops > 0 and t_f >= t_b:
+        ach = flops / (avg_us * 1e-6) / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak_f, "unit": "TFLOP/s",
+                "frac": round(ach / peak_f, 4), "traffic": None,
+                "kernel": name, "algorithmic_per_launch": flops, "avg_us": round(avg_us, 2),
+                "hbm_floor_us": round(t_b * 1e6, 2), "mfma_floor_us": round(t_f * 1e6, 2)}
+    ach = nbytes / (avg_us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+            "kernel": name, "algorithmic_per_launch": nbytes, "avg_us": round(avg_us, 2),
+            "hbm_floor_us": round(t_b * 1e6, 2), "mfma_floor_us": round(t_f * 1e6, 2)}
+
+
+def cpu_baseline(w, inp, target_s=12.0):
+    """The CPU oracle as it stands, on the first Ts tokens of the same workload."""
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    import numpy as np
+
+    import oracle as O
+
+    def run(Ts):
+        x = inp["x"][:Ts]
+        t0 = time.perf_counter()
+        z, idx, gw = O.route(x, inp["w_router"], w.k, inp.get("bias"))
+        O.moe_forward(x, idx, gw, inp["w_gate"], inp["w_up"], inp["w_down"], w.e_lo, w.e_hi)
+        if w.train:
+            O.moe_backward(x, inp["w_router"], idx, gw, inp["w_gate"], inp["w_up"], inp["w_down"],
+                           inp["dy"][:Ts], w.e_lo, w.e_hi)
+        dt = time.perf_counter() - t0
+        R = int(((idx >= w.e_lo) & (idx < w.e_hi)).sum())
+        return dt, R
+
+    Ts = min(w.T, 128)
+    dt, R = run(Ts)
+    if dt < target_s / 4 and Ts < w.T:
+        Ts = int(min(w.T, max(Ts, Ts * target_s / max(dt, 1e-3))))
+        dt, R = run(Ts)
+    sub = w.scaled(T=Ts)
+    fl = step_flops(sub, R)
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle", "tokens_per_s": round(Ts / dt, 1), "seconds": round(dt, 2),
+            "sample": f"first {Ts} of {w.T} tokens of {w.name}, float64 NumPy "
+                      f"{'forward+backward' if w.train else 'forward'}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="ep16_train_t8192_h2048_i768_e128_k8")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-times", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this layer build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_expert_layer_router_amd as moe
+    from workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    inp = make_inputs(w)
+    t = {n: torch.from_numpy(v).to(dev).to(dt).contiguous() for n, v in inp.items() if n != "bias"}
+    bias = torch.from_numpy(inp["bias"]).to(dev) if "bias" in inp else None
+    layer = moe.MoELayer(w.T, w.H, w.I, w.E, w.k, w.e_lo, w.e_hi, dt, dev, train=w.train)
+
+    def step():
+        layer.forward(t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"], bias=bias)
+        if w.train:
+            layer.backward(t["dy"], t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"])
+
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    R = int(layer.buf["offsets"][-1].item())
+    ref_out = (layer.buf["dx"] if w.train else layer.buf["y"]).clone()
+
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        out = layer.buf["dx"] if w.train else layer.buf["y"]
+        if not torch.equal(out.view(torch.int16) if dt == torch.bfloat16 else out, ref_out.view(torch.int16)
+                           if dt == torch.bfloat16 else ref_out):
+            print("graph replay differs from eager result; timing eager launches", file=sys.stderr)
+            graph = None
+
+    run = graph.replay if graph is not None else step
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = e0.elapsed_time(e1) / args.steps
+
+    flops = step_flops(w, R)
+    result = {
+        "metric": "MoE layer fwd+bwd TFLOP/s and tokens/s, 128e/H2048/I768 top-8 bf16",
+        "value": round(flops / (ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded normal draws, random-init weights)",
+        "config": {"workload": w.name, "T": w.T, "H": w.H, "I": w.I, "E": w.E, "k": w.k,
+                   "local_experts": [w.e_lo, w.e_hi], "routed_rows": R,
+                   "pass": "forward+backward" if w.train else "forward",
+                   "timing": "hip-graph replay" if graph is not None else "eager launches"},
+        "tokens_per_s": round(w.T / (ms * 1e-3), 1),
+        "flops_per_step": flops,
+        "wall_s_timed_region": round(wall, 3),
+    }
+
+    if not args.no_kernel_times:
+        # Live per-kernel durations: events recorded by the library around each
+        # launch of one kernel, on the stream it is launched on (eager steps).
+        kt = {}
+        n = args.steps
+        for kid, name in enumerate(KERNELS):
+            starts = [torch.cuda.Event(enable_timing=True) for _ in range(4 * n)]
+            stops = [torch.cuda.Event(enable_timing=True) for _ in range(4 * n)]
+            # torch creates the HIP event on first record; the library records it again
+            for e in starts + stops:
+                e.record()
+            torch.cuda.synchronize()
+            arr_s = (ctypes.c_void_p * (4 * n))(*[ctypes.c_void_p(e.cuda_event) for e in starts])
+            arr_e = (ctypes.c_void_p * (4 * n))(*[ctypes.c_void_p(e.cuda_event) for e in stops])
+            moe.lib.moe_profile_kernel(kid, arr_s, arr_e, 4 * n)
+            for _ in range(n):
+                step()
+            torch.cuda.synchronize()
+            cnt = moe.lib.moe_profile_recorded()
+            moe.lib.moe_profile_kernel(-1, None, None, 0)
+            if cnt == 0:
+                continue
+            times = [starts[i].elapsed_time(stops[i]) * 1e3 for i in range(cnt)]
+            per_step = cnt // n
+            kt[name] = {"avg_us": sum(times) / cnt, "launches_per_step": per_step,
+                        "us_per_step": sum(times) / n}
+        result["kernels_us_per_step"] = {k: round(v["us_per_step"], 2) for k, v in kt.items()}
+        dom = max(kt, key=lambda k: kt[k]["us_per_step"])
+        result["roofline"] = roofline_of(dom, w, R, kt[dom]["avg_us"], kt[dom]["launches_per_step"])
+        result["roofline_all"] = {k: {kk: vv for kk, vv in
+                                      roofline_of(k, w, R, v["avg_us"], v["launches_per_step"]).items()
+                                      if kk in ("bound", "achieved", "unit", "frac", "avg_us")}
+                                  for k, v in kt.items()}
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, inp)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

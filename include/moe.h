@@ -1,0 +1,207 @@
+/*
+ * moe.h - C ABI of the per-GPU MoE expert layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the local part of an expert-parallel MoE block: router GEMM,
+ * softmax/top-k gating, permutation of routed token rows into contiguous
+ * per-expert groups, a grouped SwiGLU expert FFN and the weighted
+ * unpermute/combine, plus the backward of each step.  The op split follows
+ * the local expert computation named on the page "FSDPTurbo EP/EFSDP and
+ * LlamaFactory FSDP2/CP Design" (section 3, dispatcher table: permute,
+ * unpermute and grouped matmul between the two all-to-alls; empty experts
+ * are legal).  Expert tensor shapes follow the page
+ * "Qwen3-MoE-30B-A3B模型EP+FSDP2并行方案" (section "Qwen3-MoE-30B-A3B模型":
+ * gate/up [E, I, H], down [E, H, I]; section "完整并行流程": one EP rank of
+ * eight holds a 16-expert slice along dim 0, passed here as plain local
+ * tensors).
+ *
+ * Conventions (all entry points)
+ *   - Tensor arguments are DEVICE pointers owned by the caller, row-major,
+ *     dense.  Activations and weights are bf16 (MOE_BF16) or fp32 (MOE_F32);
+ *     indices are int32; gate weights, logits and weight gradients are fp32.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
+ *     null stream).  No call synchronises, allocates device memory or keeps
+ *     state between calls.  Scratch memory is the caller's `ws` buffer, sized
+ *     by moe_workspace_bytes() and aligned to 256 bytes.
+ *   - Arguments are validated on the host before any HIP call.  On error the
+ *     call enqueues nothing and returns a negative moe_status; moe_last_error()
+ *     returns a per-thread message.  MOE_EHIP reports a failed launch.
+ *   - T = 0 is legal and enqueues nothing.
+ *   - Routed-row buffers have capacity R_cap = T*k rows.  The routed row
+ *     count R = offsets[E_l] stays on the device; rows >= R of capacity
+ *     buffers are never written and never read for a result.
+ *   - All results are deterministic: identical inputs give bitwise identical
+ *     outputs (no floating-point atomics anywhere).
+ *   - Shape limits: 1 <= k <= min(E, 32), E <= 256, H % 8 == 0 (bf16) or
+ *     H % 4 == 0 (fp32).  The bf16 router and expert GEMMs additionally need
+ *     H % 64 == 0 and I % 64 == 0 (else MOE_EUNSUPPORTED).  Pointers to
+ *     row data must be 16-byte aligned.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,        /* bad argument: null pointer, shape or range */
+  MOE_EUNSUPPORTED = -2,  /* legal request this build does not implement */
+  MOE_EWORKSPACE = -3,    /* ws_bytes smaller than moe_workspace_bytes() */
+  MOE_EHIP = -4           /* a HIP launch failed; see moe_last_error() */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum {
+  MOE_OP_ROUTE = 0,
+  MOE_OP_PERMUTE = 1,
+  MOE_OP_FFN_FWD = 2,
+  MOE_OP_FFN_BWD = 3,
+  MOE_OP_ROUTE_BWD = 4
+} moe_op;
+
+/* Returns MOE_ABI_VERSION of the loaded library. */
+int moe_abi_version(void);
+
+/* Message of the last failed call on this thread ("" if none).  The string
+ * is owned by the library and valid until the next call on this thread. */
+const char* moe_last_error(void);
+
+/* Bytes of workspace the op needs for these sizes (0 if none), or a negative
+ * moe_status for invalid sizes.  I is ignored by ROUTE/PERMUTE/ROUTE_BWD;
+ * e_lo/e_hi are ignored by ROUTE/ROUTE_BWD. */
+int64_t moe_workspace_bytes(int op, int T, int H, int I, int E, int k, int e_lo, int e_hi,
+                            int dtype);
+
+/* Router GEMM and top-k gating.
+ *   z[t,e]   = sum_h x[t,h] * w_router[h,e] (+ bias[e]), fp32 accumulation
+ *   topk_idx[t,j] = the k experts with the largest z[t,:], slot j in order of
+ *             (logit descending, expert id ascending): equal logits go to
+ *             the lower expert id
+ *   topk_w[t,j]   = softmax over all E, restricted to the k kept experts and
+ *             renormalised (equal to exp(z_j - z_max) / sum over kept)
+ * The pages do not state the router; this is the plain top-k-then-renormalise
+ * router, selecting on logits.
+ *   x        [T,H] dtype          w_router [H,E] dtype      bias [E] fp32 or NULL
+ *   logits   [T,E] fp32 or NULL (written when given)
+ *   topk_idx [T,k] int32          topk_w   [T,k] fp32
+ *   ws       MOE_OP_ROUTE workspace */
+int moe_route(const void* x, const void* w_router, const float* bias, int T, int H, int E, int k,
+              int dtype, float* logits, int32_t* topk_idx, float* topk_w, void* ws,
+              size_t ws_bytes, void* stream);
+
+/* The selection and gating half of moe_route on given fp32 logits [T,E]. */
+int moe_route_from_logits(const float* logits, int T, int E, int k, int32_t* topk_idx,
+                          float* topk_w, void* stream);
+
+/* Permutation of routed rows into contiguous per-expert groups (the
+ * "permute" of the dispatcher table).  Only experts in [e_lo, e_hi) are kept
+ * (E_l = e_hi - e_lo local experts of one EP rank; the full layer uses
+ * [0, E)).  Rows of one expert are in ascending token order.
+ *   counts   [E_l]   int32: routed rows per local expert (0 is legal)
+ *   offsets  [E_l+1] int32: exclusive prefix sum, offsets[E_l] = R
+ *   dest_row [T*k]   int32: grouped row of slot (t,j), or -1 if not local
+ *   src_row  [T*k]   int32: token of grouped row r, for r < R
+ *   x_perm   [T*k,H] dtype: x_perm[dest_row[t*k+j]] = x[t], bitwise
+ *   ws       MOE_OP_PERMUTE workspace */
+int moe_permute(const void* x, const int32_t* topk_idx, int T, int H, int E, int k, int e_lo,
+                int e_hi, int dtype, int32_t* counts, int32_t* offsets, int32_t* dest_row,
+                int32_t* src_row, void* x_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* Grouped SwiGLU expert FFN (the "grouped matmul"), forward.  For each local
+ * expert e and each of its rows r in [offsets[e], offsets[e+1]):
+ *   g = x_perm[r] . w_gate[e]^T, u = x_perm[r] . w_up[e]^T     (fp32 accumulate)
+ *   h_perm[r] = SiLU(g) * u,  SiLU(a) = a * sigmoid(a)          (fp32, stored as dtype)
+ *   y_perm[r] = h_perm[r] . w_down[e]^T                         (fp32 accumulate)
+ *   x_perm [R_cap,H], w_gate/w_up [E_l,I,H], w_down [E_l,H,I]  dtype
+ *   gu_saved [R_cap,2I] dtype or NULL: g in columns [0,I), u in [I,2I)
+ *   h_perm [R_cap,I], y_perm [R_cap,H]  dtype
+ *   ws       MOE_OP_FFN_FWD workspace (the tile schedule) */
+int moe_grouped_ffn_fwd(const void* x_perm, const int32_t* offsets, int E_l, int R_cap, int H,
+                        int I, const void* w_gate, const void* w_up, const void* w_down, int dtype,
+                        void* gu_saved, void* h_perm, void* y_perm, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* Weighted unpermute ("combine"): for every token, in slot order j = 0..k-1,
+ *   y[t] = sum_{j: dest_row[t*k+j] >= 0} topk_w[t,j] * y_perm[dest_row[t*k+j]]  (+ addend[t])
+ * accumulated in fp32 and rounded once to dtype.  topk_w == NULL means
+ * weight 1 (the unweighted unpermute-reduce of the backward).  A token with
+ * no local slot gets addend[t] (or 0).
+ *   y_perm [R_cap,H] dtype, topk_w [T,k] fp32 or NULL, dest_row [T*k] int32,
+ *   addend [T,H] fp32 or NULL, y [T,H] dtype */
+int moe_combine(const void* y_perm, const float* topk_w, const int32_t* dest_row,
+                const float* addend, int T, int H, int k, int dtype, void* y, void* stream);
+
+/* Backward of moe_combine for upstream gradient dy [T,H] (dtype):
+ *   dy_perm[dest_row[t*k+j]] = topk_w[t,j] * dy[t]           (stored as dtype)
+ *   d_topk_w[t,j] = <dy[t], y_perm[dest_row[t*k+j]]>         (fp32; 0 for non-local slots) */
+int moe_combine_bwd(const void* dy, const void* y_perm, const float* topk_w,
+                    const int32_t* dest_row, int T, int H, int k, int dtype, void* dy_perm,
+                    float* d_topk_w, void* stream);
+
+/* Backward of the grouped FFN, given dy_perm [R_cap,H] and the forward's
+ * x_perm, gu_saved (required) and h_perm:
+ *   dx_perm [R_cap,H] dtype   gradient wrt x_perm
+ *   dw_gate, dw_up [E_l,I,H] fp32, dw_down [E_l,H,I] fp32: overwritten
+ *   (accumulate == 0) or added to (accumulate == 1); an expert with no rows
+ *   gets exact zeros (or is left unchanged when accumulating).
+ *   ws       MOE_OP_FFN_BWD workspace (schedule and the [R_cap,2I] gradient
+ *            of g and u) */
+int moe_grouped_ffn_bwd(const void* dy_perm, const void* x_perm, const void* gu_saved,
+                        const void* h_perm, const int32_t* offsets, int E_l, int R_cap, int H,
+                        int I, const void* w_gate, const void* w_up, const void* w_down,
+                        int dtype, void* dx_perm, float* dw_gate, float* dw_up, float* dw_down,
+                        int accumulate, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of moe_route, given the gradient d_topk_w [T,k] of the gate weights:
+ *   d_logits[t, topk_idx[t,j]] = w_j * (dw_j - sum_l w_l dw_l), 0 elsewhere  [T,E] fp32
+ *   dx_router[t] = sum_e d_logits[t,e] * w_router[:,e]      [T,H] fp32 or NULL
+ *   dw_router    = x^T . d_logits                           [H,E] fp32 or NULL (overwritten)
+ *   ws       MOE_OP_ROUTE_BWD workspace
+ * The bf16 path also needs E % 4 == 0 (else MOE_EUNSUPPORTED). */
+int moe_route_bwd(const float* d_topk_w, const float* topk_w, const int32_t* topk_idx,
+                  const void* x, const void* w_router, int T, int H, int E, int k, int dtype,
+                  float* d_logits, float* dx_router, float* dw_router, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/* Kernel timing hook (benchmarks and profilers).  After this call the library
+ * records start_events[i] and stop_events[i] (each a hipEvent_t created by
+ * the caller) on the launch stream immediately before and after the i-th
+ * launch of kernel `kernel_id`, for i < n; later launches are not recorded.
+ * kernel_id < 0 switches recording off.  The arrays must stay valid while
+ * recording is on.  Process-wide state: not for concurrent use from several
+ * threads.  Returns MOE_OK or MOE_EINVAL. */
+typedef enum {
+  MOE_KERNEL_ROUTE = 0,           /* router GEMM + top-k */
+  MOE_KERNEL_PERMUTE_HIST = 1,
+  MOE_KERNEL_PERMUTE_SCAN = 2,
+  MOE_KERNEL_PERMUTE_SCATTER = 3,
+  MOE_KERNEL_FFN_GATEUP = 4,      /* gate/up GEMM + SiLU*up */
+  MOE_KERNEL_FFN_DOWN = 5,
+  MOE_KERNEL_COMBINE = 6,
+  MOE_KERNEL_COMBINE_BWD = 7,
+  MOE_KERNEL_ROUTE_BWD_DZ = 8,
+  MOE_KERNEL_ROUTE_BWD_DW = 9,
+  MOE_KERNEL_FFN_DOWN_DGRAD = 10,
+  MOE_KERNEL_FFN_DOWN_WGRAD = 11,
+  MOE_KERNEL_FFN_GATEUP_DGRAD = 12,
+  MOE_KERNEL_FFN_GATEUP_WGRAD = 13,
+  MOE_KERNEL_COUNT = 14
+} moe_kernel;
+
+int moe_profile_kernel(int kernel_id, void** start_events, void** stop_events, int n);
+
+/* Number of launches recorded since the last moe_profile_kernel() call. */
+int moe_profile_recorded(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,288 @@
+"""Python binding of the gfx950 MoE expert layer library (libmoe.so).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind the C ABI declared in include/moe.h.  PyTorch provides device memory
+(outputs and workspaces are torch tensors) and the stream (the current torch
+stream).  There is no fallback: importing this package fails when the built
+library is missing, and every call raises MoEError when the library reports
+an error.
+
+Functions keep the C names (moe_route, moe_permute, moe_grouped_ffn_fwd,
+moe_combine, moe_combine_bwd, moe_grouped_ffn_bwd, moe_route_bwd) and return
+freshly allocated torch tensors; each also accepts preallocated outputs via
+``out=`` dictionaries so that steady-state loops allocate nothing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import torch  # loads torch's HIP runtime first, so libmoe binds to the same one
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD, MOE_OP_ROUTE_BWD = range(5)
+ABI_VERSION = 1
+
+
+class MoEError(RuntimeError):
+    pass
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc --offload-arch=gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "moe_abi_version": ([], I32),
+        "moe_last_error": ([], ctypes.c_char_p),
+        "moe_workspace_bytes": ([I32] * 9, I64),
+        "moe_route": ([P, P, P, I32, I32, I32, I32, I32, P, P, P, P, SZ, P], I32),
+        "moe_route_from_logits": ([P, I32, I32, I32, P, P, P], I32),
+        "moe_permute": ([P, P, I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, SZ, P], I32),
+        "moe_grouped_ffn_fwd": ([P, P, I32, I32, I32, I32, P, P, P, I32, P, P, P, P, SZ, P], I32),
+        "moe_combine": ([P, P, P, P, I32, I32, I32, I32, P, P], I32),
+        "moe_combine_bwd": ([P, P, P, P, I32, I32, I32, I32, P, P, P], I32),
+        "moe_grouped_ffn_bwd": ([P, P, P, P, P, I32, I32, I32, I32, P, P, P, I32, P, P, P, P, I32,
+                                 P, SZ, P], I32),
+        "moe_route_bwd": ([P, P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, SZ, P], I32),
+        "moe_profile_kernel": ([I32, ctypes.POINTER(P), ctypes.POINTER(P), I32], I32),
+        "moe_profile_recorded": ([], I32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    if lib.moe_abi_version() != ABI_VERSION:
+        raise ImportError(f"libmoe ABI {lib.moe_abi_version()} != binding ABI {ABI_VERSION}")
+    return lib
+
+
+lib = _load()
+
+
+def hip_runtimes_mapped():
+    """Paths of every libamdhip64 mapped into this process (should be one)."""
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise MoEError(f"{what} failed ({rc}): {lib.moe_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmoe must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def workspace_bytes(op: int, T: int, H: int, I: int, E: int, k: int, e_lo: int, e_hi: int,
+                    dtype: int) -> int:
+    n = lib.moe_workspace_bytes(op, T, H, I, E, k, e_lo, e_hi, dtype)
+    if n < 0:
+        _check(int(n), "moe_workspace_bytes")
+    return int(n)
+
+
+def _ws(nbytes: int, device, ws: Optional[torch.Tensor] = None) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return ws
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError(f"workspace too small: {nbytes} bytes needed")
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+# ---------------------------------------------------------------------------
+# ABI wrappers
+# ---------------------------------------------------------------------------
+
+def moe_route(x: torch.Tensor, w_router: torch.Tensor, k: int, bias: Optional[torch.Tensor] = None,
+              want_logits: bool = False, ws: Optional[torch.Tensor] = None,
+              out: Optional[Dict[str, torch.Tensor]] = None):
+    """Router GEMM + top-k gating.  Returns (topk_idx int32 [T,k], topk_w fp32 [T,k], logits|None)."""
+    T, H = x.shape
+    E = w_router.shape[1]
+    dt = _dtype_code(x)
+    out = out or {}
+    idx = out.get("topk_idx")
+    if idx is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = out.get("topk_w")
+    if w is None:
+        w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    logits = out.get("logits")
+    if want_logits and logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    ws = _ws(workspace_bytes(MOE_OP_ROUTE, T, H, 1, E, k, 0, E, dt), x.device, ws)
+    _check(lib.moe_route(_ptr(x), _ptr(w_router), _ptr(bias), T, H, E, k, dt, _ptr(logits),
+                         _ptr(idx), _ptr(w), _ptr(ws), _nbytes(ws), _stream()), "moe_route")
+    return idx, w, logits
+
+
+def moe_route_from_logits(logits: torch.Tensor, k: int):
+    T, E = logits.shape
+    idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check(lib.moe_route_from_logits(_ptr(logits), T, E, k, _ptr(idx), _ptr(w), _stream()),
+           "moe_route_from_logits")
+    return idx, w
+
+
+def moe_permute(x: torch.Tensor, topk_idx: torch.Tensor, E: int, e_lo: int, e_hi: int,
+                ws: Optional[torch.Tensor] = None, out: Optional[Dict[str, torch.Tensor]] = None):
+    """Group routed rows by expert.  Returns dict counts, offsets, dest_row, src_row, x_perm."""
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    dt = _dtype_code(x)
+    E_l = e_hi - e_lo
+    dev = x.device
+    o = dict(out or {})
+    o.setdefault("counts", torch.empty(E_l, dtype=torch.int32, device=dev))
+    o.setdefault("offsets", torch.empty(E_l + 1, dtype=torch.int32, device=dev))
+    o.setdefault("dest_row", torch.empty(T * k, dtype=torch.int32, device=dev))
+    o.setdefault("src_row", torch.empty(T * k, dtype=torch.int32, device=dev))
+    o.setdefault("x_perm", torch.empty((T * k, H), dtype=x.dtype, device=dev))
+    ws = _ws(workspace_bytes(MOE_OP_PERMUTE, T, H, 1, E, k, e_lo, e_hi, dt), dev, ws)
+    _check(lib.moe_permute(_ptr(x), _ptr(topk_idx), T, H, E, k, e_lo, e_hi, dt, _ptr(o["counts"]),
+                           _ptr(o["offsets"]), _ptr(o["dest_row"]), _ptr(o["src_row"]),
+                           _ptr(o["x_perm"]), _ptr(ws), _nbytes(ws), _stream()), "moe_permute")
+    return o
+
+
+def moe_grouped_ffn_fwd(x_perm: torch.Tensor, offsets: torch.Tensor, w_gate: torch.Tensor,
+                        w_up: torch.Tensor, w_down: torch.Tensor, save_gu: bool = True,
+                        ws: Optional[torch.Tensor] = None,
+                        out: Optional[Dict[str, torch.Tensor]] = None):
+    """Grouped SwiGLU FFN forward.  Returns dict h_perm, y_perm, gu (or None)."""
+    R_cap, H = x_perm.shape
+    E_l, I, _ = w_gate.shape
+    dt = _dtype_code(x_perm)
+    dev = x_perm.device
+    o = dict(out or {})
+    o.setdefault("h_perm", torch.empty((R_cap, I), dtype=x_perm.dtype, device=dev))
+    o.setdefault("y_perm", torch.empty((R_cap, H), dtype=x_perm.dtype, device=dev))
+    if save_gu:
+        o.setdefault("gu", torch.empty((R_cap, 2 * I), dtype=x_perm.dtype, device=dev))
+    else:
+        o["gu"] = None
+    nb = lib.moe_workspace_bytes(MOE_OP_FFN_FWD, max(R_cap, 0), H, I, max(E_l, 1), 1, 0, E_l, dt)
+    if nb < 0:
+        _check(int(nb), "moe_workspace_bytes")
+    ws = _ws(int(nb), dev, ws)
+    _check(lib.moe_grouped_ffn_fwd(_ptr(x_perm), _ptr(offsets), E_l, R_cap, H, I, _ptr(w_gate),
+                                   _ptr(w_up), _ptr(w_down), dt, _ptr(o["gu"]), _ptr(o["h_perm"]),
+                                   _ptr(o["y_perm"]), _ptr(ws), _nbytes(ws), _stream()),
+           "moe_grouped_ffn_fwd")
+    return o
+
+
+def moe_combine(y_perm: torch.Tensor, topk_w: Optional[torch.Tensor], dest_row: torch.Tensor, T: int,
+                addend: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """Weighted (or, with topk_w None, unweighted) unpermute-reduce.  Returns y [T,H]."""
+    H = y_perm.shape[1]
+    k = dest_row.numel() // max(T, 1)
+    y = out if out is not None else torch.empty((T, H), dtype=y_perm.dtype, device=y_perm.device)
+    _check(lib.moe_combine(_ptr(y_perm), _ptr(topk_w), _ptr(dest_row), _ptr(addend), T, H, k,
+                           _dtype_code(y_perm), _ptr(y), _stream()), "moe_combine")
+    return y
+
+
+def moe_combine_bwd(dy: torch.Tensor, y_perm: torch.Tensor, topk_w: torch.Tensor,
+                    dest_row: torch.Tensor, out: Optional[Dict[str, torch.Tensor]] = None):
+    """Returns dict dy_perm [R_cap,H], d_topk_w [T,k]."""
+    T, H = dy.shape
+    k = topk_w.shape[1]
+    o = dict(out or {})
+    o.setdefault("dy_perm", torch.empty_like(y_perm))
+    o.setdefault("d_topk_w", torch.empty((T, k), dtype=torch.float32, device=dy.device))
+    _check(lib.moe_combine_bwd(_ptr(dy), _ptr(y_perm), _ptr(topk_w), _ptr(dest_row), T, H, k,
+                               _dtype_code(dy), _ptr(o["dy_perm"]), _ptr(o["d_topk_w"]), _stream()),
+           "moe_combine_bwd")
+    return o
+
+
+def moe_grouped_ffn_bwd(dy_perm: torch.Tensor, x_perm: torch.Tensor, gu: torch.Tensor,
+                        h_perm: torch.Tensor, offsets: torch.Tensor, w_gate: torch.Tensor,
+                        w_up: torch.Tensor, w_down: torch.Tensor, accumulate: bool = False,
+                        ws: Optional[torch.Tensor] = None,
+                        out: Optional[Dict[str, torch.Tensor]] = None):
+    """Returns dict dx_perm, dw_gate, dw_up, dw_down (fp32 weight gradients)."""
+    R_cap, H = x_perm.shape
+    E_l, I, _ = w_gate.shape
+    dt = _dtype_code(x_perm)
+    dev = x_perm.device
+    o = dict(out or {})
+    o.setdefault("dx_perm", torch.empty_like(x_perm))
+    for n, shp in (("dw_gate", (E_l, I, H)), ("dw_up", (E_l, I, H)), ("dw_down", (E_l, H, I))):
+        o.setdefault(n, torch.empty(shp, dtype=torch.float32, device=dev))
+    nb = lib.moe_workspace_bytes(MOE_OP_FFN_BWD, R_cap, H, I, max(E_l, 1), 1, 0, E_l, dt)
+    if nb < 0:
+        _check(int(nb), "moe_workspace_bytes")
+    ws = _ws(int(nb), dev, ws)
+    _check(lib.moe_grouped_ffn_bwd(_ptr(dy_perm), _ptr(x_perm), _ptr(gu), _ptr(h_perm),
+                                   _ptr(offsets), E_l, R_cap, H, I, _ptr(w_gate), _ptr(w_up),
+                                   _ptr(w_down), dt, _ptr(o["dx_perm"]), _ptr(o["dw_gate"]),
+                                   _ptr(o["dw_up"]), _ptr(o["dw_down"]), int(accumulate),
+                                   _ptr(ws), _nbytes(ws), _stream()), "moe_grouped_ffn_bwd")
+    return o
+
+
+def moe_route_bwd(d_topk_w: torch.Tensor, topk_w: torch.Tensor, topk_idx: torch.Tensor,
+                  x: torch.Tensor, w_router: torch.Tensor, want_dx: bool = True,
+                  want_dw: bool = True, ws: Optional[torch.Tensor] = None,
+                  out: Optional[Dict[str, torch.Tensor]] = None):
+    """Returns dict d_logits [T,E], dx_router [T,H] fp32 (or None), dw_router [H,E] fp32 (or None)."""
+    T, H = x.shape
+    E = w_router.shape[1]
+    k = topk_idx.shape[1]
+    dt = _dtype_code(x)
+    dev = x.device
+    o = dict(out or {})
+    o.setdefault("d_logits", torch.empty((T, E), dtype=torch.float32, device=dev))
+    if want_dx:
+        o.setdefault("dx_router", torch.empty((T, H), dtype=torch.float32, device=dev))
+    else:
+        o["dx_router"] = None
+    if want_dw:
+        o.setdefault("dw_router", torch.empty((H, E), dtype=torch.float32, device=dev))
+    else:
+        o["dw_router"] = None
+    ws = _ws(workspace_bytes(MOE_OP_ROUTE_BWD, T, H, 1, E, k, 0, E, dt), dev, ws)
+    _check(lib.moe_route_bwd(_ptr(d_topk_w), _ptr(topk_w), _ptr(topk_idx), _ptr(x),
+                             _ptr(w_router), T, H, E, k, dt, _ptr(o["d_logits"]),
+                             _ptr(o["dx_router"]), _ptr(o["dw_router"]), _ptr(ws), _nbytes(ws),
+                             _stream()), "moe_route_bwd")
+    return o
+
+
+from .layer import MoELayer  # noqa: E402,F401

@@ -1,0 +1,402 @@
+// C ABI of the gfx950 MoE expert layer: argument validation (host only, before
+// any HIP call), workspace layout and dispatch to the kernels.  Declarations
+// and the contract of every entry point are in include/moe.h.
+#include "../../include/moe.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_EHIP, "%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));
+}
+
+inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline int elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+
+int check_dtype(int dtype, const char* fn) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return fail(MOE_EINVAL, "%s: unknown dtype %d", fn, dtype);
+  return MOE_OK;
+}
+
+int check_row_width(int H, int dtype, const char* fn) {
+  if (H <= 0) return fail(MOE_EINVAL, "%s: H must be positive (got %d)", fn, H);
+  const int q = dtype == MOE_BF16 ? 8 : 4;
+  if (H % q != 0) return fail(MOE_EINVAL, "%s: H=%d must be a multiple of %d for this dtype", fn, H, q);
+  return MOE_OK;
+}
+
+int check_routing_shape(int T, int E, int k, const char* fn) {
+  if (T < 0) return fail(MOE_EINVAL, "%s: T must be >= 0 (got %d)", fn, T);
+  if (E < 1 || E > kMaxE) return fail(MOE_EINVAL, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
+  if (k < 1 || k > E || k > kMaxK)
+    return fail(MOE_EINVAL, "%s: k=%d outside [1, min(E=%d, %d)]", fn, k, E, kMaxK);
+  if ((long long)T * k > 0x7fffffffLL) return fail(MOE_EINVAL, "%s: T*k overflows int32", fn);
+  return MOE_OK;
+}
+
+int check_ptr(const void* p, const char* name, const char* fn, bool need16 = false) {
+  if (p == nullptr) return fail(MOE_EINVAL, "%s: %s must not be NULL", fn, name);
+  if (need16 && !aligned16(p)) return fail(MOE_EINVAL, "%s: %s must be 16-byte aligned", fn, name);
+  return MOE_OK;
+}
+
+int check_ws(const void* ws, size_t have, size_t need, const char* fn) {
+  if (need == 0) return MOE_OK;
+  if (ws == nullptr || have < need)
+    return fail(MOE_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                ws == nullptr ? (size_t)0 : have);
+  if (((uintptr_t)ws & 255u) != 0) return fail(MOE_EINVAL, "%s: ws must be 256-byte aligned", fn);
+  return MOE_OK;
+}
+
+int route_bwd_splits(int T) { return std::max(1, std::min(16, (T + 1023) / 1024)); }
+
+size_t ws_route(int H, int E, int dtype) {
+  return dtype == MOE_BF16 ? align256((size_t)E * H * 2) : 0;
+}
+size_t ws_ffn_fwd(int R_cap, int E_l, int dtype) {
+  return dtype == MOE_BF16 ? ffn_sched_bytes(R_cap, E_l) : 0;
+}
+size_t ws_ffn_bwd(int R_cap, int E_l, int I, int dtype) {
+  if (dtype == MOE_BF16) return ffn_sched_bytes(R_cap, E_l) + align256((size_t)R_cap * 2 * I * 2);
+  return align256((size_t)R_cap * 2 * I * 4);
+}
+size_t ws_route_bwd(int T, int H, int E, int dtype) {
+  const size_t wt = align256((size_t)E * H * elem_bytes(dtype));
+  if (dtype != MOE_BF16) return wt;
+  return wt + align256((size_t)T * 2 * E * 2) +
+         align256((size_t)route_bwd_splits(T) * H * 2 * E * sizeof(float));
+}
+
+int check_ffn_shape(int E_l, int R_cap, int H, int I, int dtype, const char* fn) {
+  if (E_l < 1 || E_l > kMaxE) return fail(MOE_EINVAL, "%s: E_l=%d outside [1, %d]", fn, E_l, kMaxE);
+  if (R_cap < 0) return fail(MOE_EINVAL, "%s: R_cap must be >= 0", fn);
+  if (I <= 0) return fail(MOE_EINVAL, "%s: I must be positive", fn);
+  if (int rc = check_row_width(H, dtype, fn)) return rc;
+  if (dtype == MOE_BF16 && (H % 64 != 0 || I % 64 != 0))
+    return fail(MOE_EUNSUPPORTED, "%s: bf16 expert GEMMs need H %% 64 == 0 and I %% 64 == 0 (H=%d, I=%d)",
+                fn, H, I);
+  return MOE_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// kernel timing hook
+// ---------------------------------------------------------------------------
+namespace {
+int g_prof_id = -1;
+void** g_prof_start = nullptr;
+void** g_prof_stop = nullptr;
+int g_prof_n = 0;
+int g_prof_next = 0;
+}  // namespace
+
+namespace moe {
+ProfScope::ProfScope(int kernel_id, hipStream_t s) : slot(-1), stream(s) {
+  if (kernel_id == g_prof_id && g_prof_next < g_prof_n) {
+    slot = g_prof_next++;
+    (void)hipEventRecord((hipEvent_t)g_prof_start[slot], s);
+  }
+}
+ProfScope::~ProfScope() {
+  if (slot >= 0) (void)hipEventRecord((hipEvent_t)g_prof_stop[slot], stream);
+}
+}  // namespace moe
+
+extern "C" {
+
+int moe_profile_kernel(int kernel_id, void** start_events, void** stop_events, int n) {
+  if (kernel_id >= MOE_KERNEL_COUNT) return fail(MOE_EINVAL, "moe_profile_kernel: unknown kernel %d", kernel_id);
+  if (kernel_id >= 0 && (n < 0 || (n > 0 && (start_events == nullptr || stop_events == nullptr))))
+    return fail(MOE_EINVAL, "moe_profile_kernel: need n >= 0 and event arrays");
+  g_prof_id = kernel_id < 0 ? -1 : kernel_id;
+  g_prof_start = start_events;
+  g_prof_stop = stop_events;
+  g_prof_n = kernel_id < 0 ? 0 : n;
+  g_prof_next = 0;
+  return MOE_OK;
+}
+
+int moe_profile_recorded(void) { return g_prof_next; }
+
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_last_error(void) { return g_err; }
+
+int64_t moe_workspace_bytes(int op, int T, int H, int I, int E, int k, int e_lo, int e_hi,
+                            int dtype) {
+  const char* fn = "moe_workspace_bytes";
+  if (int rc = check_dtype(dtype, fn)) return rc;
+  if (int rc = check_routing_shape(T, E, k, fn)) return rc;
+  if (int rc = check_row_width(H, dtype, fn)) return rc;
+  const int R_cap = T * k;
+  switch (op) {
+    case MOE_OP_ROUTE:
+      return (int64_t)ws_route(H, E, dtype);
+    case MOE_OP_ROUTE_BWD:
+      return (int64_t)ws_route_bwd(T, H, E, dtype);
+    case MOE_OP_PERMUTE:
+    case MOE_OP_FFN_FWD:
+    case MOE_OP_FFN_BWD: {
+      if (e_lo < 0 || e_hi > E || e_lo >= e_hi)
+        return fail(MOE_EINVAL, "%s: need 0 <= e_lo < e_hi <= E", fn);
+      const int E_l = e_hi - e_lo;
+      if (op == MOE_OP_PERMUTE) return (int64_t)permute_ws_bytes(T, k, E_l);
+      if (I <= 0) return fail(MOE_EINVAL, "%s: I must be positive", fn);
+      if (op == MOE_OP_FFN_FWD) return (int64_t)ws_ffn_fwd(R_cap, E_l, dtype);
+      return (int64_t)ws_ffn_bwd(R_cap, E_l, I, dtype);
+    }
+    default:
+      return fail(MOE_EINVAL, "%s: unknown op %d", fn, op);
+  }
+}
+
+int moe_route(const void* x, const void* w_router, const float* bias, int T, int H, int E, int k,
+              int dtype, float* logits, int32_t* topk_idx, float* topk_w, void* ws,
+              size_t ws_bytes, void* stream) {
+  const char* fn = "moe_route";
+  if (int rc = check_dtype(dtype, fn)) return rc;
+  if (int rc = check_routing_shape(T, E, k, fn)) return rc;
+  if (int rc = check_row_width(H, dtype, fn)) return rc;
+  if (dtype == MOE_BF16 && H % 64 != 0)
+    return fail(MOE_EUNSUPPORTED, "%s: the bf16 router needs H %% 64 == 0 (H=%d)", fn, H);
+  if (int rc = check_ptr(x, "x", fn, true)) return rc;
+  if (int rc = check_ptr(w_router, "w_router", fn, true)) return rc;
+  if (int rc = check_ptr(topk_idx, "topk_idx", fn)) return rc;
+  if (int rc = check_ptr(topk_w, "topk_w", fn)) return rc;
+  if (int rc = check_ws(ws, ws_bytes, ws_route(H, E, dtype), fn)) return rc;
+  if (T == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (dtype == MOE_BF16)
+    e = launch_route_bf16((const bf16_t*)x, (const bf16_t*)w_router, bias, T, H, E, k, logits,
+                          topk_idx, topk_w, (bf16_t*)ws, s);
+  else
+    e = launch_route_f32((const float*)x, (const float*)w_router, bias, T, H, E, k, logits,
+                         topk_idx, topk_w, s);
+  return hip_status(e, fn);
+}
+
+int moe_route_from_logits(const float* logits, int T, int E, int k, int32_t* topk_idx,
+                          float* topk_w, void* stream) {
+  const char* fn = "moe_route_from_logits";
+  if (int rc = check_routing_shape(T, E, k, fn)) return rc;
+  if (int rc = check_ptr(logits, "logits", fn)) return rc;
+  if (int rc = check_ptr(topk_idx, "topk_idx", fn)) return rc;
+  if (int rc = check_ptr(topk_w, "topk_w", fn)) return rc;
+  if (T == 0) return MOE_OK;
+  return hip_status(launch_route_from_logits(logits, T, E, k, topk_idx, topk_w, (hipStream_t)stream),
+                    fn);
+}
+
+int moe_permute(const void* x, const int32_t* topk_idx, int T, int H, int E, int k, int e_lo,
+                int e_hi, int dtype, int32_t* counts, int32_t* offsets, int32_t* dest_row,
+                int32_t* src_row, void* x_perm, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "moe_permute";
+  if (int rc = check_dtype(dtype, fn)) return rc;
+  if (int rc = check_routing_shape(T, E, k, fn)) return rc;
+  if (int rc = check_row_width(H, dtype, fn)) return rc;
+  if (e_lo < 0 || e_hi > E || e_lo >= e_hi)
+    return fail(MOE_EINVAL, "%s: need 0 <= e_lo < e_hi <= E (got %d, %d, E=%d)", fn, e_lo, e_hi, E);
+  if (int rc = check_ptr(counts, "counts", fn)) return rc;
+  if (int rc = check_ptr(offsets, "offsets", fn)) return rc;
+  if (T > 0) {
+    if (int rc = check_ptr(x, "x", fn, true)) return rc;
+    if (int rc = check_ptr(topk_idx, "topk_idx", fn)) return rc;
+    if (int rc = check_ptr(dest_row, "dest_row", fn)) return rc;
+    if (int rc = check_ptr(src_row, "src_row", fn)) return rc;
+    if (int rc = check_ptr(x_perm, "x_perm", fn, true)) return rc;
+  }
+  const int E_l = e_hi - e_lo;
+  if (int rc = check_ws(ws, ws_bytes, permute_ws_bytes(T, k, E_l), fn)) return rc;
+  return hip_status(launch_permute(x, topk_idx, T, H, k, e_lo, e_hi, elem_bytes(dtype), counts,
+                                   offsets, dest_row, src_row, x_perm, ws, (hipStream_t)stream),
+                    fn);
+}
+
+int moe_grouped_ffn_fwd(const void* x_perm, const int32_t* offsets, int E_l, int R_cap, int H,
+                        int I, const void* w_gate, const void* w_up, const void* w_down, int dtype,
+                        void* gu_saved, void* h_perm, void* y_perm, void* ws, size_t ws_bytes,
+                        void* stream) {
+  const char* fn = "moe_grouped_ffn_fwd";
+  if (int rc = check_dtype(dtype, fn)) return rc;
+  if (int rc = check_ffn_shape(E_l, R_cap, H, I, dtype, fn)) return rc;
+  if (int rc = check_ptr(offsets, "offsets", fn)) return rc;
+  if (int rc = check_ptr(w_gate, "w_gate", fn, true)) return rc;
+  if (int rc = check_ptr(w_up, "w_up", fn, true)) return rc;
+  if (int rc = check_ptr(w_down, "w_down", fn, true)) return rc;
+  if (R_cap > 0) {
+    if (int rc = check_ptr(x_perm, "x_perm", fn, true)) return rc;
+    if (int rc = check_ptr(h_perm, "h_perm", fn, true)) return rc;
+    if (int rc = check_ptr(y_perm, "y_perm", fn, true)) return rc;
+  }
+  if (int rc = check_ws(ws, ws_bytes, ws_ffn_fwd(R_cap, E_l, dtype), fn)) return rc;
+  if (R_cap == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (dtype == MOE_BF16)
+    e = launch_ffn_fwd_bf16((const bf16_t*)x_perm, offsets, E_l, R_cap, H, I,
+                            (const bf16_t*)w_gate, (const bf16_t*)w_up, (const bf16_t*)w_down,
+                            (bf16_t*)gu_saved, (bf16_t*)h_perm, (bf16_t*)y_perm, ws, s);
+  else
+    e = launch_ffn_fwd_f32((const float*)x_perm, offsets, E_l, R_cap, H, I, (const float*)w_gate,
+                           (const float*)w_up, (const float*)w_down, (float*)gu_saved,
+                           (float*)h_perm, (float*)y_perm, s);
+  return hip_status(e, fn);
+}
+
+int moe_combine(const void* y_perm, const float* topk_w, const int32_t* dest_row,
+                const float* addend, int T, int H, int k, int dtype, void* y, void* stream) {
+  const char* fn = "moe_combine";
+  if (int rc = check_dtype(dtype, fn)) return rc;
+  if (T < 0) return fail(MOE_EINVAL, "%s: T must be >= 0", fn);
+  if (k < 1 || k > kMaxK) return fail(MOE_EINVAL, "%s: k=%d outside [1, %d]", fn, k, kMaxK);
+  if (int rc = check_row_width(H, dtype, fn)) return rc;
+  if (T == 0) return MOE_OK;
+  if (int rc = check_ptr(y_perm, "y_perm", fn, true)) return rc;
+  if (int rc = check_ptr(dest_row, "dest_row", fn)) return rc;
+  if (int rc = check_ptr(y, "y", fn, true)) return rc;
+  if (addend != nullptr && !aligned16(addend)) return fail(MOE_EINVAL, "%s: addend must be 16-byte aligned", fn);
+  return hip_status(launch_combine(y_perm, topk_w, dest_row, addend, T, H, k, dtype == MOE_BF16, y,
+                                   (hipStream_t)stream),
+                    fn);
+}
+
+int moe_combine_bwd(const void* dy, const void* y_perm, const float* topk_w,
+                    const int32_t* dest_row, int T, int H, int k, int dtype, void* dy_perm,
+                    float* d_topk_w, void* stream) {
+  const char* fn = "moe_combine_bwd";
+  if (int rc = check_dtype(dtype, fn)) return rc;
+  if (T < 0) return fail(MOE_EINVAL, "%s: T must be >= 0", fn);
+  if (k < 1 || k > kMaxK) return fail(MOE_EINVAL, "%s: k=%d outside [1, %d]", fn, k, kMaxK);
+  if (int rc = check_row_width(H, dtype, fn)) return rc;
+  if (T == 0) return MOE_OK;
+  if (int rc = check_ptr(dy, "dy", fn, true)) return rc;
+  if (int rc = check_ptr(y_perm, "y_perm", fn, true)) return rc;
+  if (int rc = check_ptr(topk_w, "topk_w", fn)) return rc;
+  if (int rc = check_ptr(dest_row, "dest_row", fn)) return rc;
+  if (int rc = check_ptr(dy_perm, "dy_perm", fn, true)) return rc;
+  if (int rc = check_ptr(d_topk_w, "d_topk_w", fn)) return rc;
+  return hip_status(launch_combine_bwd(dy, y_perm, topk_w, dest_row, T, H, k, dtype == MOE_BF16,
+                                       dy_perm, d_topk_w, (hipStream_t)stream),
+                    fn);
+}
+
+int moe_grouped_ffn_bwd(const void* dy_perm, const void* x_perm, const void* gu_saved,
+                        const void* h_perm, const int32_t* offsets, int E_l, int R_cap, int H,
+                        int I, const void* w_gate, const void* w_up, const void* w_down,
+                        int dtype, void* dx_perm, float* dw_gate, float* dw_up, float* dw_down,
+                        int accumulate, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "moe_grouped_ffn_bwd";
+  if (int rc = check_dtype(dtype, fn)) return rc;
+  if (int rc = check_ffn_shape(E_l, R_cap, H, I, dtype, fn)) return rc;
+  if (accumulate != 0 && accumulate != 1) return fail(MOE_EINVAL, "%s: accumulate must be 0 or 1", fn);
+  if (int rc = check_ptr(offsets, "offsets", fn)) return rc;
+  if (int rc = check_ptr(w_gate, "w_gate", fn, true)) return rc;
+  if (int rc = check_ptr(w_up, "w_up", fn, true)) return rc;
+  if (int rc = check_ptr(w_down, "w_down", fn, true)) return rc;
+  if (int rc = check_ptr(dw_gate, "dw_gate", fn)) return rc;
+  if (int rc = check_ptr(dw_up, "dw_up", fn)) return rc;
+  if (int rc = check_ptr(dw_down, "dw_down", fn)) return rc;
+  if (R_cap > 0) {
+    if (int rc = check_ptr(dy_perm, "dy_perm", fn, true)) return rc;
+    if (int rc = check_ptr(x_perm, "x_perm", fn, true)) return rc;
+    if (int rc = check_ptr(gu_saved, "gu_saved", fn, true)) return rc;
+    if (int rc = check_ptr(h_perm, "h_perm", fn, true)) return rc;
+    if (int rc = check_ptr(dx_perm, "dx_perm", fn, true)) return rc;
+  }
+  if (int rc = check_ws(ws, ws_bytes, ws_ffn_bwd(R_cap, E_l, I, dtype), fn)) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (dtype == MOE_BF16)
+    e = launch_ffn_bwd_bf16((const bf16_t*)dy_perm, (const bf16_t*)x_perm,
+                            (const bf16_t*)gu_saved, (const bf16_t*)h_perm, offsets, E_l, R_cap, H,
+                            I, (const bf16_t*)w_gate, (const bf16_t*)w_up, (const bf16_t*)w_down,
+                            (bf16_t*)dx_perm, dw_gate, dw_up, dw_down, accumulate != 0, ws, s);
+  else
+    e = launch_ffn_bwd_f32((const float*)dy_perm, (const float*)x_perm, (const float*)gu_saved,
+                           (const float*)h_perm, offsets, E_l, R_cap, H, I, (const float*)w_gate,
+                           (const float*)w_up, (const float*)w_down, (float*)dx_perm, dw_gate,
+                           dw_up, dw_down, accumulate != 0, (float*)ws, s);
+  return hip_status(e, fn);
+}
+
+int moe_route_bwd(const float* d_topk_w, const float* topk_w, const int32_t* topk_idx,
+                  const void* x, const void* w_router, int T, int H, int E, int k, int dtype,
+                  float* d_logits, float* dx_router, float* dw_router, void* ws, size_t ws_bytes,
+                  void* stream) {
+  const char* fn = "moe_route_bwd";
+  if (int rc = check_dtype(dtype, fn)) return rc;
+  if (int rc = check_routing_shape(T, E, k, fn)) return rc;
+  if (int rc = check_row_width(H, dtype, fn)) return rc;
+  if (dtype == MOE_BF16 && (H % 64 != 0 || E % 4 != 0))
+    return fail(MOE_EUNSUPPORTED,
+                "%s: the bf16 router backward needs H %% 64 == 0 and E %% 4 == 0 (H=%d, E=%d)", fn, H, E);
+  if (int rc = check_ptr(w_router, "w_router", fn, true)) return rc;
+  if (int rc = check_ptr(d_logits, "d_logits", fn)) return rc;
+  if (dx_router != nullptr && !aligned16(dx_router))
+    return fail(MOE_EINVAL, "%s: dx_router must be 16-byte aligned", fn);
+  if (T > 0) {
+    if (int rc = check_ptr(d_topk_w, "d_topk_w", fn)) return rc;
+    if (int rc = check_ptr(topk_w, "topk_w", fn)) return rc;
+    if (int rc = check_ptr(topk_idx, "topk_idx", fn)) return rc;
+    if (dw_router != nullptr)
+      if (int rc = check_ptr(x, "x", fn, true)) return rc;
+  }
+  if (int rc = check_ws(ws, ws_bytes, ws_route_bwd(T, H, E, dtype), fn)) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = dtype == MOE_BF16;
+  char* w = (char*)ws;
+  void* wt = w;
+  w += align256((size_t)E * H * elem_bytes(dtype));
+  bf16_t* dz_hilo = nullptr;
+  float* partials = nullptr;
+  const int nsplit = route_bwd_splits(T);
+  if (bf16) {
+    dz_hilo = (bf16_t*)w;
+    w += align256((size_t)T * 2 * E * 2);
+    partials = (float*)w;
+  }
+  hipError_t e = hipSuccess;
+  if (T > 0 && dx_router != nullptr) e = launch_transpose(w_router, wt, H, E, elem_bytes(dtype), s);
+  if (e == hipSuccess && T > 0)
+    e = launch_route_bwd_dz(d_topk_w, topk_w, topk_idx, wt, T, H, E, k, bf16, d_logits, dx_router,
+                            (bf16 && dw_router != nullptr) ? dz_hilo : nullptr, s);
+  if (e == hipSuccess && dw_router != nullptr) {
+    if (bf16) {
+      if (T > 0) {
+        e = launch_dw_router_bf16((const bf16_t*)x, dz_hilo, T, H, E, nsplit, nullptr, partials, s);
+        if (e == hipSuccess) e = launch_dw_router_reduce(partials, nsplit, H, E, dw_router, s);
+      } else {
+        e = launch_dw_router_reduce(partials, 0, H, E, dw_router, s);  // writes zeros
+      }
+    } else {
+      e = launch_dw_router_f32((const float*)x, d_logits, T, H, E, dw_router, s);
+    }
+  }
+  return hip_status(e, fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,157 @@
+// Shared device helpers and internal launch declarations of the gfx950 MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef uint16_t bf16_t;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kMaxE = 256;
+constexpr int kMaxK = 32;
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// Round to nearest, ties to even.  NaN stays NaN (quietened), infinities pass.
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (bf16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// Unpack 8 bf16 held in a uint4 into fp32.
+__device__ __forceinline__ void unpack8(const uint4& v, float* f) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ uint4 pack8(const float* f) {
+  return make_uint4(pack_bf2(f[0], f[1]), pack_bf2(f[2], f[3]), pack_bf2(f[4], f[5]),
+                    pack_bf2(f[6], f[7]));
+}
+
+// ---------------------------------------------------------------------------
+// Wave-level reductions (64 lanes, fixed butterfly order => deterministic)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+// Logical workgroup id with consecutive ids on the same XCD.  The hardware
+// hands workgroup i to XCD i % 8; remapping makes each XCD own a contiguous
+// slice of the logical range, so neighbouring tiles share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  const int per = nblocks / 8;
+  if (bid >= per * 8) return bid;  // ragged tail keeps its id
+  return (bid % 8) * per + bid / 8;
+}
+
+}  // namespace moe
+
+// ---------------------------------------------------------------------------
+// Optional event recording around one kernel's launches (see moe_profile_kernel).
+// ---------------------------------------------------------------------------
+namespace moe {
+struct ProfScope {
+  ProfScope(int kernel_id, hipStream_t s);
+  ~ProfScope();
+  int slot;
+  hipStream_t stream;
+};
+}  // namespace moe
+
+// ---------------------------------------------------------------------------
+// Internal launchers (host side).  Arguments were validated by the C ABI.
+// Each returns hipSuccess or the launch error.
+// ---------------------------------------------------------------------------
+namespace moe {
+
+// route.hip
+hipError_t launch_route_bf16(const bf16_t* x, const bf16_t* w_router, const float* bias, int T,
+                             int H, int E, int k, float* logits, int32_t* topk_idx, float* topk_w,
+                             bf16_t* wt_ws, hipStream_t s);
+hipError_t launch_route_f32(const float* x, const float* w_router, const float* bias, int T, int H,
+                            int E, int k, float* logits, int32_t* topk_idx, float* topk_w,
+                            hipStream_t s);
+hipError_t launch_route_from_logits(const float* logits, int T, int E, int k, int32_t* topk_idx,
+                                    float* topk_w, hipStream_t s);
+hipError_t launch_transpose(const void* src, void* dst, int rows, int cols, int elem_bytes,
+                            hipStream_t s);
+
+// permute.hip
+constexpr int kPermBlock = 256;  // tokens per histogram block
+size_t permute_ws_bytes(int T, int k, int E_l);
+hipError_t launch_permute(const void* x, const int32_t* topk_idx, int T, int H, int k, int e_lo,
+                          int e_hi, int elem_bytes, int32_t* counts, int32_t* offsets,
+                          int32_t* dest_row, int32_t* src_row, void* x_perm, void* ws,
+                          hipStream_t s);
+
+// combine.hip
+hipError_t launch_combine(const void* y_perm, const float* topk_w, const int32_t* dest_row,
+                          const float* addend, int T, int H, int k, bool bf16, void* y,
+                          hipStream_t s);
+hipError_t launch_combine_bwd(const void* dy, const void* y_perm, const float* topk_w,
+                              const int32_t* dest_row, int T, int H, int k, bool bf16,
+                              void* dy_perm, float* d_topk_w, hipStream_t s);
+hipError_t launch_route_bwd_dz(const float* d_topk_w, const float* topk_w,
+                               const int32_t* topk_idx, const void* w_router_t, int T, int H, int E,
+                               int k, bool bf16, float* d_logits, float* dx_router,
+                               bf16_t* dz_hilo, hipStream_t s);
+hipError_t launch_dw_router_f32(const float* x, const float* d_logits, int T, int H, int E,
+                                float* dw_router, hipStream_t s);
+hipError_t launch_dw_router_reduce(const float* partials, int nsplit, int H, int E,
+                                   float* dw_router, hipStream_t s);
+
+// gemm.hip (bf16 MFMA grouped GEMMs)
+size_t ffn_sched_bytes(int R_cap, int E_l);
+hipError_t launch_ffn_fwd_bf16(const bf16_t* x_perm, const int32_t* offsets, int E_l, int R_cap,
+                               int H, int I, const bf16_t* w_gate, const bf16_t* w_up,
+                               const bf16_t* w_down, bf16_t* gu, bf16_t* h_perm, bf16_t* y_perm,
+                               void* ws, hipStream_t s);
+hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, const bf16_t* gu,
+                               const bf16_t* h_perm, const int32_t* offsets, int E_l, int R_cap,
+                               int H, int I, const bf16_t* w_gate, const bf16_t* w_up,
+                               const bf16_t* w_down, bf16_t* dx_perm, float* dw_gate,
+                               float* dw_up, float* dw_down, bool accumulate, void* ws,
+                               hipStream_t s);
+// X^T . [dz_hi | dz_lo] split over token chunks: partials [nsplit][H][2E] fp32.
+hipError_t launch_dw_router_bf16(const bf16_t* x, const bf16_t* dz_hilo, int T, int H, int E,
+                                 int nsplit, int32_t* split_offsets, float* partials,
+                                 hipStream_t s);
+
+// gemm_f32.hip (plain fp32 kernels for the fp32 path)
+hipError_t launch_ffn_fwd_f32(const float* x_perm, const int32_t* offsets, int E_l, int R_cap,
+                              int H, int I, const float* w_gate, const float* w_up,
+                              const float* w_down, float* gu, float* h_perm, float* y_perm,
+                              hipStream_t s);
+hipError_t launch_ffn_bwd_f32(const float* dy_perm, const float* x_perm, const float* gu,
+                              const float* h_perm, const int32_t* offsets, int E_l, int R_cap,
+                              int H, int I, const float* w_gate, const float* w_up,
+                              const float* w_down, float* dx_perm, float* dw_gate, float* dw_up,
+                              float* dw_down, bool accumulate, float* dgu_ws, hipStream_t s);
+
+}  // namespace moe

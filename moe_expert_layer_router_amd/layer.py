@@ -1,0 +1,108 @@
+"""A whole MoE expert layer (forward and backward) over preallocated buffers.
+
+Chains the C-ABI calls in the order of the layer: route -> permute ->
+grouped FFN -> combine, and for the backward combine_bwd -> route_bwd ->
+grouped FFN backward -> unweighted combine of dx_perm plus the router's dx.
+All buffers and workspaces are allocated once in the constructor, so
+forward()/backward() only enqueue kernels on the current stream (and can be
+captured into a HIP graph).
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, Optional
+
+import torch
+
+from . import (MOE_BF16, MOE_F32, MOE_OP_FFN_BWD, MOE_OP_FFN_FWD, MOE_OP_PERMUTE, MOE_OP_ROUTE,
+               MOE_OP_ROUTE_BWD, _check, _stream, lib, workspace_bytes)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+class MoELayer:
+    def __init__(self, T: int, H: int, I: int, E: int, k: int, e_lo: int, e_hi: int,
+                 dtype: torch.dtype, device="cuda", train: bool = True):
+        self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
+        self.e_lo, self.e_hi, self.E_l = e_lo, e_hi, e_hi - e_lo
+        self.dtype = dtype
+        self.dt = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
+        self.R_cap = T * k
+        self.train = train
+        dev = torch.device(device)
+        f32, i32 = torch.float32, torch.int32
+        R, E_l = self.R_cap, self.E_l
+        b = {}
+        b["topk_idx"] = torch.empty((T, k), dtype=i32, device=dev)
+        b["topk_w"] = torch.empty((T, k), dtype=f32, device=dev)
+        b["logits"] = torch.empty((T, E), dtype=f32, device=dev)
+        b["counts"] = torch.empty(E_l, dtype=i32, device=dev)
+        b["offsets"] = torch.empty(E_l + 1, dtype=i32, device=dev)
+        b["dest_row"] = torch.empty(T * k, dtype=i32, device=dev)
+        b["src_row"] = torch.empty(T * k, dtype=i32, device=dev)
+        b["x_perm"] = torch.empty((R, H), dtype=dtype, device=dev)
+        b["h_perm"] = torch.empty((R, I), dtype=dtype, device=dev)
+        b["y_perm"] = torch.empty((R, H), dtype=dtype, device=dev)
+        b["gu"] = torch.empty((R, 2 * I), dtype=dtype, device=dev) if train else None
+        b["y"] = torch.empty((T, H), dtype=dtype, device=dev)
+        if train:
+            b["dy_perm"] = torch.empty((R, H), dtype=dtype, device=dev)
+            b["d_topk_w"] = torch.empty((T, k), dtype=f32, device=dev)
+            b["d_logits"] = torch.empty((T, E), dtype=f32, device=dev)
+            b["dx_router"] = torch.empty((T, H), dtype=f32, device=dev)
+            b["dw_router"] = torch.empty((H, E), dtype=f32, device=dev)
+            b["dx_perm"] = torch.empty((R, H), dtype=dtype, device=dev)
+            b["dw_gate"] = torch.empty((E_l, I, H), dtype=f32, device=dev)
+            b["dw_up"] = torch.empty((E_l, I, H), dtype=f32, device=dev)
+            b["dw_down"] = torch.empty((E_l, H, I), dtype=f32, device=dev)
+            b["dx"] = torch.empty((T, H), dtype=dtype, device=dev)
+        self.buf = b
+        ops = [MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN_FWD]
+        if train:
+            ops += [MOE_OP_FFN_BWD, MOE_OP_ROUTE_BWD]
+        nb = max(workspace_bytes(op, T, H, I, E, k, e_lo, e_hi, self.dt) for op in ops)
+        # one workspace serves every call: the calls run one after another on one stream
+        self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+        self.ws_bytes = self.ws.numel()
+
+    def forward(self, x, w_router, w_gate, w_up, w_down, bias=None, save_logits=True):
+        b, T, H, I, E, k = self.buf, self.T, self.H, self.I, self.E, self.k
+        s = _stream()
+        ws, wsb = _p(self.ws), self.ws_bytes
+        _check(lib.moe_route(_p(x), _p(w_router), _p(bias), T, H, E, k, self.dt,
+                             _p(b["logits"]) if save_logits else None, _p(b["topk_idx"]),
+                             _p(b["topk_w"]), ws, wsb, s), "moe_route")
+        _check(lib.moe_permute(_p(x), _p(b["topk_idx"]), T, H, E, k, self.e_lo, self.e_hi, self.dt,
+                               _p(b["counts"]), _p(b["offsets"]), _p(b["dest_row"]),
+                               _p(b["src_row"]), _p(b["x_perm"]), ws, wsb, s), "moe_permute")
+        _check(lib.moe_grouped_ffn_fwd(_p(b["x_perm"]), _p(b["offsets"]), self.E_l, self.R_cap, H, I,
+                                       _p(w_gate), _p(w_up), _p(w_down), self.dt, _p(b["gu"]),
+                                       _p(b["h_perm"]), _p(b["y_perm"]), ws, wsb, s),
+               "moe_grouped_ffn_fwd")
+        _check(lib.moe_combine(_p(b["y_perm"]), _p(b["topk_w"]), _p(b["dest_row"]), None, T, H, k,
+                               self.dt, _p(b["y"]), s), "moe_combine")
+        return b["y"]
+
+    def backward(self, dy, x, w_router, w_gate, w_up, w_down) -> Dict[str, torch.Tensor]:
+        if not self.train:
+            raise RuntimeError("layer was built without training buffers")
+        b, T, H, I, E, k = self.buf, self.T, self.H, self.I, self.E, self.k
+        s = _stream()
+        ws, wsb = _p(self.ws), self.ws_bytes
+        _check(lib.moe_combine_bwd(_p(dy), _p(b["y_perm"]), _p(b["topk_w"]), _p(b["dest_row"]), T, H,
+                                   k, self.dt, _p(b["dy_perm"]), _p(b["d_topk_w"]), s),
+               "moe_combine_bwd")
+        _check(lib.moe_route_bwd(_p(b["d_topk_w"]), _p(b["topk_w"]), _p(b["topk_idx"]), _p(x),
+                                 _p(w_router), T, H, E, k, self.dt, _p(b["d_logits"]),
+                                 _p(b["dx_router"]), _p(b["dw_router"]), ws, wsb, s), "moe_route_bwd")
+        _check(lib.moe_grouped_ffn_bwd(_p(b["dy_perm"]), _p(b["x_perm"]), _p(b["gu"]), _p(b["h_perm"]),
+                                       _p(b["offsets"]), self.E_l, self.R_cap, H, I, _p(w_gate),
+                                       _p(w_up), _p(w_down), self.dt, _p(b["dx_perm"]),
+                                       _p(b["dw_gate"]), _p(b["dw_up"]), _p(b["dw_down"]), 0, ws,
+                                       wsb, s), "moe_grouped_ffn_bwd")
+        _check(lib.moe_combine(_p(b["dx_perm"]), None, _p(b["dest_row"]), _p(b["dx_router"]), T, H, k,
+                               self.dt, _p(b["dx"]), s), "moe_combine")
+        return {n: b[n] for n in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "d_logits",
+                                  "d_topk_w")}

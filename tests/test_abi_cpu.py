@@ -1,0 +1,174 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/moe.h, and rejects bad arguments on the host before any
+HIP call (so these run on a machine without a GPU)."""
+import ctypes
+import importlib.util
+import os
+import re
+import threading
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+LIB = os.path.join(ROOT, "moe_expert_layer_router_amd", "libmoe.so")
+
+
+def _ensure_built():
+    if not os.path.exists(LIB):
+        spec = importlib.util.spec_from_file_location(
+            "_moe_build", os.path.join(ROOT, "moe_expert_layer_router_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build_library()
+
+
+_ensure_built()
+import moe_expert_layer_router_amd as moe  # noqa: E402
+
+L = moe.lib
+OK, EINVAL, EUNSUP, EWS = 0, -1, -2, -3
+BF16, F32 = moe.MOE_BF16, moe.MOE_F32
+A = ctypes.c_void_p(0x100000)   # fake, 256-byte aligned; never dereferenced by a failing call
+U = ctypes.c_void_p(0x100002)   # misaligned fake pointer
+N = None
+S = ctypes.c_void_p(0)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 10
+    raw = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(raw, n), f"libmoe.so does not export {n}"
+
+
+def test_abi_version_and_single_hip_runtime():
+    assert L.moe_abi_version() == moe.ABI_VERSION == 1
+    libs = moe.hip_runtimes_mapped()
+    assert len(libs) <= 1, libs
+
+
+def _err():
+    return L.moe_last_error().decode()
+
+
+def test_workspace_bytes_and_errors():
+    ws = lambda *a: L.moe_workspace_bytes(*a)
+    assert ws(moe.MOE_OP_ROUTE, 16384, 2048, 768, 128, 8, 0, 128, F32) == 0
+    assert ws(moe.MOE_OP_ROUTE, 16384, 2048, 768, 128, 8, 0, 128, BF16) == 128 * 2048 * 2
+    assert ws(moe.MOE_OP_PERMUTE, 16384, 2048, 768, 128, 8, 0, 128, BF16) > 16384 * 8 * 4
+    assert ws(moe.MOE_OP_FFN_BWD, 8192, 2048, 768, 128, 8, 0, 16, BF16) >= 8192 * 8 * 2 * 768 * 2
+    assert ws(moe.MOE_OP_PERMUTE, 0, 2048, 768, 128, 8, 0, 16, BF16) == 0
+    assert ws(9, 16, 64, 32, 8, 2, 0, 8, F32) == EINVAL and "unknown op" in _err()
+    assert ws(moe.MOE_OP_ROUTE, 16, 64, 32, 8, 9, 0, 8, F32) == EINVAL and "k=9" in _err()
+    assert ws(moe.MOE_OP_ROUTE, 16, 64, 32, 300, 2, 0, 8, F32) == EINVAL
+    assert ws(moe.MOE_OP_ROUTE, 16, 62, 32, 8, 2, 0, 8, BF16) == EINVAL and "multiple of 8" in _err()
+    assert ws(moe.MOE_OP_PERMUTE, 16, 64, 32, 8, 2, 5, 5, F32) == EINVAL
+    assert ws(moe.MOE_OP_PERMUTE, 16, 64, 32, 8, 2, 0, 9, F32) == EINVAL
+    assert ws(moe.MOE_OP_ROUTE, 16, 64, 32, 8, 2, 0, 8, 7) == EINVAL and "dtype" in _err()
+
+
+def test_route_errors():
+    r = lambda *a: L.moe_route(*a)
+    assert r(A, A, N, 32, 128, 8, 9, F32, N, A, A, N, 0, S) == EINVAL and "k=9" in _err()
+    assert r(A, A, N, 32, 128, 8, 0, F32, N, A, A, N, 0, S) == EINVAL
+    assert r(A, A, N, 32, 128, 0, 1, F32, N, A, A, N, 0, S) == EINVAL
+    assert r(A, A, N, 32, 128, 257, 8, F32, N, A, A, N, 0, S) == EINVAL
+    assert r(A, A, N, 32, 128, 64, 33, F32, N, A, A, N, 0, S) == EINVAL
+    assert r(A, A, N, -1, 128, 8, 2, F32, N, A, A, N, 0, S) == EINVAL
+    assert r(N, A, N, 32, 128, 8, 2, F32, N, A, A, N, 0, S) == EINVAL and "x must not be NULL" in _err()
+    assert r(U, A, N, 32, 128, 8, 2, F32, N, A, A, N, 0, S) == EINVAL and "aligned" in _err()
+    assert r(A, A, N, 32, 128, 8, 2, F32, N, N, A, N, 0, S) == EINVAL and "topk_idx" in _err()
+    assert r(A, A, N, 32, 100, 8, 2, BF16, N, A, A, A, 1 << 20, S) == EINVAL       # H % 8
+    assert r(A, A, N, 32, 96, 8, 2, BF16, N, A, A, A, 1 << 20, S) == EUNSUP        # H % 64
+    assert r(A, A, N, 32, 128, 8, 2, BF16, N, A, A, A, 100, S) == EWS and "workspace" in _err()
+    assert r(A, A, N, 32, 128, 8, 2, BF16, N, A, A, N, 0, S) == EWS
+    assert r(A, A, N, 32, 128, 8, 2, 5, N, A, A, N, 0, S) == EINVAL
+    # valid arguments with T == 0: nothing to enqueue, no HIP call
+    assert r(A, A, N, 0, 128, 8, 2, F32, N, A, A, N, 0, S) == OK
+
+
+def test_route_from_logits_errors():
+    f = L.moe_route_from_logits
+    assert f(A, 10, 8, 9, A, A, S) == EINVAL
+    assert f(N, 10, 8, 2, A, A, S) == EINVAL
+    assert f(A, 0, 8, 2, A, A, S) == OK
+
+
+def test_permute_errors():
+    p = lambda *a: L.moe_permute(*a)
+    big = 1 << 30
+    assert p(A, A, 64, 128, 16, 4, 4, 4, BF16, A, A, A, A, A, A, big, S) == EINVAL     # e_lo == e_hi
+    assert p(A, A, 64, 128, 16, 4, 0, 17, BF16, A, A, A, A, A, A, big, S) == EINVAL    # e_hi > E
+    assert p(A, A, 64, 128, 16, 4, -1, 8, BF16, A, A, A, A, A, A, big, S) == EINVAL
+    assert p(A, A, 64, 128, 16, 4, 0, 16, BF16, N, A, A, A, A, A, big, S) == EINVAL and "counts" in _err()
+    assert p(A, A, 64, 128, 16, 4, 0, 16, BF16, A, A, A, A, U, A, big, S) == EINVAL    # x_perm misaligned
+    assert p(A, A, 64, 128, 16, 4, 0, 16, BF16, A, A, A, A, A, A, 8, S) == EWS
+    assert p(A, A, 64, 128, 16, 4, 0, 16, BF16, A, A, A, A, A, U, big, S) == EINVAL    # ws misaligned
+    assert p(A, A, 64, 129, 16, 4, 0, 16, BF16, A, A, A, A, A, A, big, S) == EINVAL    # H % 8
+
+
+def test_ffn_fwd_errors():
+    f = lambda *a: L.moe_grouped_ffn_fwd(*a)
+    big = 1 << 30
+    assert f(A, A, 16, 512, 128, 96, A, A, A, BF16, N, A, A, A, big, S) == EUNSUP     # I % 64
+    assert f(A, A, 16, 512, 96, 64, A, A, A, BF16, N, A, A, A, big, S) == EUNSUP      # H % 64
+    assert f(A, A, 0, 512, 128, 64, A, A, A, BF16, N, A, A, A, big, S) == EINVAL      # E_l
+    assert f(A, A, 257, 512, 128, 64, A, A, A, BF16, N, A, A, A, big, S) == EINVAL
+    assert f(A, A, 16, -1, 128, 64, A, A, A, BF16, N, A, A, A, big, S) == EINVAL
+    assert f(A, A, 16, 512, 128, 64, N, A, A, BF16, N, A, A, A, big, S) == EINVAL and "w_gate" in _err()
+    assert f(A, A, 16, 512, 128, 64, A, A, A, BF16, N, N, A, A, big, S) == EINVAL and "h_perm" in _err()
+    assert f(A, A, 16, 512, 128, 64, A, A, A, BF16, N, A, A, A, 4, S) == EWS
+    assert f(A, A, 16, 0, 128, 64, A, A, A, BF16, N, N, N, A, big, S) == OK            # nothing routed
+
+
+def test_combine_errors():
+    c = lambda *a: L.moe_combine(*a)
+    assert c(A, A, A, N, 8, 128, 0, BF16, A, S) == EINVAL
+    assert c(A, A, A, N, 8, 128, 33, BF16, A, S) == EINVAL
+    assert c(A, A, A, N, 8, 100, 2, BF16, A, S) == EINVAL
+    assert c(A, A, A, N, -3, 128, 2, BF16, A, S) == EINVAL
+    assert c(N, A, A, N, 8, 128, 2, BF16, A, S) == EINVAL
+    assert c(A, A, A, U, 8, 128, 2, BF16, A, S) == EINVAL and "addend" in _err()
+    assert c(A, A, A, N, 0, 128, 2, BF16, A, S) == OK
+    b = lambda *a: L.moe_combine_bwd(*a)
+    assert b(A, A, N, A, 8, 128, 2, BF16, A, A, S) == EINVAL and "topk_w" in _err()
+    assert b(A, A, A, A, 8, 128, 2, BF16, U, A, S) == EINVAL
+    assert b(A, A, A, A, 0, 128, 2, BF16, A, A, S) == OK
+
+
+def test_ffn_bwd_and_route_bwd_errors():
+    f = lambda *a: L.moe_grouped_ffn_bwd(*a)
+    big = 1 << 30
+    args = [A, A, A, A, A, 16, 512, 128, 64, A, A, A, BF16, A, A, A, A, 0, A, big, S]
+    bad = list(args); bad[17] = 2
+    assert f(*bad) == EINVAL and "accumulate" in _err()
+    bad = list(args); bad[2] = N
+    assert f(*bad) == EINVAL and "gu_saved" in _err()
+    bad = list(args); bad[19] = 16
+    assert f(*bad) == EWS
+    bad = list(args); bad[8] = 32
+    assert f(*bad) == EUNSUP
+    r = lambda *a: L.moe_route_bwd(*a)
+    assert r(A, A, A, A, A, 64, 128, 8, 9, F32, A, A, A, A, big, S) == EINVAL
+    assert r(A, A, A, A, A, 64, 128, 8, 2, F32, N, A, A, A, big, S) == EINVAL and "d_logits" in _err()
+    assert r(A, A, A, A, A, 64, 128, 8, 2, F32, A, U, A, A, big, S) == EINVAL
+    assert r(A, A, A, A, A, 64, 96, 8, 2, BF16, A, A, A, A, big, S) == EUNSUP
+    assert r(A, A, A, A, A, 64, 128, 8, 2, BF16, A, A, A, A, 8, S) == EWS
+
+
+def test_last_error_is_per_thread():
+    L.moe_route(N, A, N, 32, 128, 8, 2, F32, N, A, A, N, 0, S)
+    assert "x must not be NULL" in _err()
+    seen = []
+    th = threading.Thread(target=lambda: seen.append(L.moe_last_error().decode()))
+    th.start()
+    th.join()
+    assert seen == [""]

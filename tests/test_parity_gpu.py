@@ -1,0 +1,381 @@
+"""Parity of the HIP layer (through the C ABI) against the CPU oracle.
+
+Integer results (top-k indices, counts, offsets, row maps, permuted rows) must
+match bit for bit; floating-point results must be within the stated
+tolerances of the float64 oracle:
+  bf16 layers: max-abs error <= 2e-2 and rel-L2 <= 5e-3,
+  fp32 layers: max-abs error <= 1e-4 and rel-L2 <= 1e-5.
+Routing contract (near ties make "same top-k as an independent fp64 router"
+ill-posed): the GPU's top-k must equal the oracle's top-k applied to the GPU's
+own fp32 logits; GPU logits must be within the fp32 dot-product error bound
+of the fp64 logits; and the indices must equal the fully independent oracle's
+on every token whose k-th/(k+1)-th logit margin exceeds twice that bound.
+Float outputs are compared with the oracle run on the GPU's routing.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from workloads import EP_SHARE, FULL, SKEWED, TINY, TRAIN, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+moe = pytest.importorskip("moe_expert_layer_router_amd")
+DEV = torch.device("cuda:0")
+
+TOL = {"bf16": (2e-2, 5e-3), "f32": (1e-4, 1e-5)}
+
+
+# ----------------------------------------------------------------------------
+# helpers
+# ----------------------------------------------------------------------------
+
+@functools.lru_cache(maxsize=4)
+def _inputs(w: Workload):
+    return make_inputs(w)
+
+
+def _dev(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(dtype).contiguous()
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _tdtype(w):
+    return torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+
+def _gpu_tensors(w, inp):
+    dt = _tdtype(w)
+    t = {n: _dev(inp[n], dt) for n in ("x", "w_router", "w_gate", "w_up", "w_down")}
+    t["bias"] = _dev(inp["bias"], torch.float32) if "bias" in inp else None
+    if "dy" in inp:
+        t["dy"] = _dev(inp["dy"], dt)
+    return t
+
+
+def assert_close(name, got, ref, dtype):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{name}: non-finite values"
+    max_abs, rel_l2 = TOL[dtype]
+    err = np.abs(got - ref).max() if got.size else 0.0
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+    print(f"  {name}: max-abs {err:.3e} rel-L2 {rel:.3e}", flush=True)
+    assert err <= max_abs and rel <= rel_l2, f"{name}: max-abs {err:.3e}, rel-L2 {rel:.3e}"
+
+
+def logit_bound(x, w_router):
+    """Standard bound for an fp32 dot product of length H: gamma_H * sum |x||w|."""
+    H = x.shape[1]
+    u = 2.0 ** -24
+    gamma = H * u / (1 - H * u)
+    return gamma * (np.abs(np.asarray(x, np.float64)) @ np.abs(np.asarray(w_router, np.float64))) + 1e-30
+
+
+def check_routing(w, inp, idx_g, w_g, logits_g):
+    z_ref = O.router_logits(inp["x"], inp["w_router"], inp.get("bias"))
+    bound = logit_bound(inp["x"], inp["w_router"])
+    dz = np.abs(logits_g - z_ref)
+    assert (dz <= bound).all(), f"logit error {dz.max():.3e} exceeds the fp32 bound"
+    # exact top-k on the GPU's own logits
+    idx_own = O.topk_experts(logits_g, w.k)
+    assert np.array_equal(idx_g, idx_own), "top-k differs from the oracle's on the GPU's logits"
+    w_own = O.gate_weights(logits_g, idx_own)
+    np.testing.assert_allclose(w_g, w_own, rtol=1e-6, atol=1e-7)
+    assert np.abs(w_g.sum(1) - 1).max() < 1e-6
+    # independent oracle on every token with a safe margin
+    idx_ref = O.topk_experts(z_ref, w.k)
+    srt = np.sort(z_ref, axis=1)[:, ::-1]
+    if w.k < w.E:
+        margin = srt[:, w.k - 1] - srt[:, w.k]
+        safe = margin > 2 * bound.max(axis=1)
+    else:
+        safe = np.ones(w.T, bool)
+    # within the kept set, equal-ish logits may also swap slot order; compare sets + order on safe tokens
+    mism = ~np.all(idx_g == idx_ref, axis=1)
+    print(f"  routing: {int((~safe).sum())} near-tie tokens, {int(mism.sum())} differing tokens", flush=True)
+    assert not (mism & safe).any() or _only_order_ties(idx_g, idx_ref, z_ref, bound, mism & safe)
+
+
+def _only_order_ties(idx_g, idx_ref, z, bound, rows):
+    """Differences on margin-safe tokens are allowed only as slot-order swaps of
+    experts whose logits are themselves within the error bound of each other."""
+    for t in np.nonzero(rows)[0]:
+        if set(idx_g[t]) != set(idx_ref[t]):
+            return False
+        for a, b in zip(idx_g[t], idx_ref[t]):
+            if a != b and abs(z[t, a] - z[t, b]) > 2 * bound[t].max():
+                return False
+    return True
+
+
+def run_route(w, t):
+    idx, gw, logits = moe.moe_route(t["x"], t["w_router"], w.k, bias=t["bias"], want_logits=True)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), gw.cpu().numpy().astype(np.float64), logits.cpu().numpy().astype(np.float64)
+
+
+def check_permute(w, inp, idx_g, p, x_t):
+    dest_ref, src_ref = O.permutation_maps(idx_g, w.e_lo, w.e_hi)
+    counts_ref = O.expert_counts(idx_g, w.e_lo, w.e_hi)
+    off_ref = O.expert_offsets(counts_ref)
+    R = int(off_ref[-1])
+    assert np.array_equal(p["counts"].cpu().numpy(), counts_ref)
+    assert np.array_equal(p["offsets"].cpu().numpy(), off_ref)
+    assert np.array_equal(p["dest_row"].cpu().numpy(), dest_ref)
+    assert np.array_equal(p["src_row"].cpu().numpy()[:R], src_ref)
+    src = p["src_row"][:R].long()
+    assert torch.equal(p["x_perm"][:R].view(torch.int16 if x_t.dtype == torch.bfloat16 else torch.int32),
+                       x_t[src].view(torch.int16 if x_t.dtype == torch.bfloat16 else torch.int32))
+    return R, dest_ref, src_ref
+
+
+# ----------------------------------------------------------------------------
+# routing
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("w", [TINY, EP_SHARE, FULL, SKEWED], ids=lambda w: w.name)
+def test_route_matches_oracle(w):
+    inp = _inputs(w)
+    t = _gpu_tensors(w, inp)
+    idx, gw, logits = run_route(w, t)
+    check_routing(w, inp, idx, gw, logits)
+    if w.skew:
+        counts = np.bincount(idx.ravel(), minlength=w.E)
+        print(f"  skewed load: {int((counts == 0).sum())} empty experts, max {counts.max()}", flush=True)
+        assert (counts == 0).sum() > 0
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (33, 16, 16), (777, 128, 8), (1024, 256, 32), (500, 64, 1)])
+def test_route_from_logits_ties_exact(T, E, k):
+    rng = np.random.default_rng(T + E + k)
+    z = rng.integers(-2, 3, size=(T, E)).astype(np.float32)   # dense exact ties
+    idx, gw = moe.moe_route_from_logits(_dev(z, torch.float32), k)
+    torch.cuda.synchronize()
+    idx_ref = O.topk_experts(z, k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    np.testing.assert_allclose(gw.cpu().numpy(), O.gate_weights(z, idx_ref), rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_route_degenerate_cases(dtype):
+    w = Workload("t", 300, 128, 64, 16, 3, 0, 16, dtype)
+    inp = make_inputs(w)
+    tdt = _tdtype(w)
+    # x = 0: every logit is 0, so slots take ids 0..k-1 with weight 1/k
+    idx, gw, _ = moe.moe_route(torch.zeros((w.T, w.H), dtype=tdt, device=DEV), _dev(inp["w_router"], tdt), w.k)
+    assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(w.k), (w.T, 1)))
+    np.testing.assert_allclose(gw.cpu().numpy(), 1.0 / w.k, rtol=1e-7)
+    # duplicated router columns: exact ties resolved toward the lower id
+    wr = inp["w_router"].copy()
+    wr[:, 9] = wr[:, 3]
+    wr[:, 12] = wr[:, 3]
+    idx, gw, logits = moe.moe_route(_dev(inp["x"], tdt), _dev(wr, tdt), w.k, want_logits=True)
+    idx = idx.cpu().numpy()
+    lg = logits.cpu().numpy()
+    assert np.array_equal(lg[:, 9], lg[:, 3]) and np.array_equal(lg[:, 12], lg[:, 3])
+    assert np.array_equal(idx, O.topk_experts(lg, w.k))
+    hit = 0
+    for row in idx:
+        r = row.tolist()
+        for d in (9, 12):
+            if d in r:
+                assert 3 in r and r.index(3) < r.index(d)
+                hit += 1
+    assert hit > 0
+    # k = 1 gives weight 1; k = E gives the full softmax
+    _, g1, _ = moe.moe_route(_dev(inp["x"], tdt), _dev(inp["w_router"], tdt), 1)
+    assert (g1.cpu().numpy() == 1.0).all()
+    idxE, gE, lE = moe.moe_route(_dev(inp["x"], tdt), _dev(inp["w_router"], tdt), w.E, want_logits=True)
+    lE = lE.cpu().numpy().astype(np.float64)
+    ref = O.softmax(lE)
+    np.testing.assert_allclose(gE.cpu().numpy(), np.take_along_axis(ref, idxE.cpu().numpy().astype(np.int64), 1),
+                               rtol=2e-6, atol=1e-7)
+
+
+# ----------------------------------------------------------------------------
+# permutation
+# ----------------------------------------------------------------------------
+
+PERMUTE_CASES = [TINY, EP_SHARE, FULL, SKEWED,
+                 TINY.scaled(name="ragged_t1000_k3_local3_11", T=1000, k=3, E=16, e_lo=3, e_hi=11),
+                 TINY.scaled(name="k1_t513", T=513, k=1),
+                 EP_SHARE.scaled(name="ep_last_rank", e_lo=112, e_hi=128, T=2048)]
+
+
+@pytest.mark.parametrize("w", PERMUTE_CASES, ids=lambda w: w.name)
+def test_permute_bit_exact(w):
+    inp = _inputs(w)
+    t = _gpu_tensors(w, inp)
+    idx_t, _, _ = moe.moe_route(t["x"], t["w_router"], w.k, bias=t["bias"])
+    sentinel = torch.full((w.T * w.k, w.H), float("nan"), dtype=t["x"].dtype, device=DEV)
+    p = moe.moe_permute(t["x"], idx_t, w.E, w.e_lo, w.e_hi, out={"x_perm": sentinel})
+    torch.cuda.synchronize()
+    R, _, _ = check_permute(w, inp, idx_t.cpu().numpy(), p, t["x"])
+    assert torch.isnan(p["x_perm"][R:].float()).all(), "rows beyond R were written"
+    print(f"  R = {R} of capacity {w.T * w.k}", flush=True)
+
+
+def test_permute_empty_input():
+    x = torch.empty((0, 128), dtype=torch.bfloat16, device=DEV)
+    idx = torch.empty((0, 4), dtype=torch.int32, device=DEV)
+    counts = torch.full((8,), 7, dtype=torch.int32, device=DEV)
+    offsets = torch.full((9,), 7, dtype=torch.int32, device=DEV)
+    p = moe.moe_permute(x, idx, 16, 4, 12, out={"counts": counts, "offsets": offsets})
+    torch.cuda.synchronize()
+    assert (p["counts"].cpu() == 0).all() and (p["offsets"].cpu() == 0).all()
+
+
+@pytest.mark.parametrize("k", [1, 8])
+def test_permute_then_unweighted_combine_is_k_times_x(k):
+    w = FULL.scaled(name="id", T=4096, k=k, E=128, e_lo=0, e_hi=128)
+    inp = _inputs(w)
+    t = _gpu_tensors(w, inp)
+    idx_t, _, _ = moe.moe_route(t["x"], t["w_router"], k)
+    p = moe.moe_permute(t["x"], idx_t, w.E, 0, w.E)
+    y = moe.moe_combine(p["x_perm"], None, p["dest_row"], w.T)
+    torch.cuda.synchronize()
+    # k * x is exact in bf16 for k a power of two, and the fp32 sum of k equal values is exact
+    assert torch.equal(y.float(), t["x"].float() * k)
+
+
+# ----------------------------------------------------------------------------
+# forward
+# ----------------------------------------------------------------------------
+
+def run_forward(w, t):
+    idx_t, gw_t, lg_t = moe.moe_route(t["x"], t["w_router"], w.k, bias=t["bias"], want_logits=True)
+    p = moe.moe_permute(t["x"], idx_t, w.E, w.e_lo, w.e_hi)
+    f = moe.moe_grouped_ffn_fwd(p["x_perm"], p["offsets"], t["w_gate"], t["w_up"], t["w_down"],
+                                save_gu=True)
+    y = moe.moe_combine(f["y_perm"], gw_t, p["dest_row"], w.T)
+    torch.cuda.synchronize()
+    return idx_t, gw_t, lg_t, p, f, y
+
+
+def _oracle_weights(inp, idx):
+    z = O.router_logits(inp["x"], inp["w_router"], inp.get("bias"))
+    return O.gate_weights(z, idx)
+
+
+FWD_CASES = [TINY, EP_SHARE, FULL, SKEWED,
+             EP_SHARE.scaled(name="ragged_bf16_t1000_h192_i128_e24_k3", T=1000, H=192, I=128, E=24,
+                             k=3, e_lo=5, e_hi=21)]
+
+
+@pytest.mark.parametrize("w", FWD_CASES, ids=lambda w: w.name)
+def test_forward_matches_oracle(w):
+    inp = _inputs(w)
+    t = _gpu_tensors(w, inp)
+    idx_t, gw_t, lg_t, p, f, y = run_forward(w, t)
+    idx = idx_t.cpu().numpy()
+    R, dest, src = check_permute(w, inp, idx, p, t["x"])
+    gw = _oracle_weights(inp, idx)
+    # sample tokens at full size; all tokens for small layers
+    if w.T * w.k * w.H * w.I > 3e10:
+        rng = np.random.default_rng(1)
+        toks = np.sort(rng.choice(w.T, 96, replace=False))
+    else:
+        toks = np.arange(w.T)
+    y_ref = O.moe_forward(inp["x"][toks], idx[toks], gw[toks], inp["w_gate"], inp["w_up"],
+                          inp["w_down"], w.e_lo, w.e_hi)
+    assert_close("y", _np(y)[toks], y_ref, w.dtype)
+    # intermediates of the sampled tokens' routed rows
+    pv = O.pair_values(inp["x"], idx, inp["w_gate"], inp["w_up"], inp["w_down"], w.e_lo, w.e_hi,
+                       tokens=toks[:48])
+    rows, sel = [], []
+    for a, tok in enumerate(toks[:48]):
+        for j in range(w.k):
+            r = dest[tok * w.k + j]
+            if r >= 0:
+                rows.append(r)
+                sel.append((a, j))
+    rows = torch.tensor(rows, dtype=torch.long, device=DEV)
+    aa = np.array([s[0] for s in sel])
+    jj = np.array([s[1] for s in sel])
+    I = w.I
+    assert_close("h_perm", _np(f["h_perm"][rows]), pv["h"][aa, jj], w.dtype)
+    assert_close("gu.g", _np(f["gu"][rows][:, :I]), pv["g"][aa, jj], w.dtype)
+    assert_close("gu.u", _np(f["gu"][rows][:, I:]), pv["u"][aa, jj], w.dtype)
+    assert_close("y_perm", _np(f["y_perm"][rows]), pv["y"][aa, jj], w.dtype)
+
+
+# ----------------------------------------------------------------------------
+# backward
+# ----------------------------------------------------------------------------
+
+BWD_CASES = [TINY.scaled(name="tiny_fp32_train", train=True),
+             TRAIN,
+             TRAIN.scaled(name="ragged_bf16_train_t1000_h192_i128_e24_k3", T=1000, H=192, I=128,
+                          E=24, k=3, e_lo=5, e_hi=21),
+             TRAIN.scaled(name="skewed_bf16_train_t4096_e32", T=4096, E=32, k=4, e_lo=0, e_hi=32,
+                          skew=True)]
+
+
+def run_layer(w, t):
+    layer = moe.MoELayer(w.T, w.H, w.I, w.E, w.k, w.e_lo, w.e_hi, t["x"].dtype, DEV)
+    y = layer.forward(t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"], bias=t["bias"])
+    g = layer.backward(t["dy"], t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"])
+    torch.cuda.synchronize()
+    return layer, y, g
+
+
+@pytest.mark.parametrize("w", BWD_CASES, ids=lambda w: w.name)
+def test_backward_matches_oracle(w):
+    inp = _inputs(w)
+    t = _gpu_tensors(w, inp)
+    layer, y, g = run_layer(w, t)
+    idx = layer.buf["topk_idx"].cpu().numpy()
+    gw = _oracle_weights(inp, idx)
+    y_ref = O.moe_forward(inp["x"], idx, gw, inp["w_gate"], inp["w_up"], inp["w_down"], w.e_lo, w.e_hi)
+    assert_close("y", _np(y), y_ref, w.dtype)
+    ref = O.moe_backward(inp["x"], inp["w_router"], idx, gw, inp["w_gate"], inp["w_up"],
+                         inp["w_down"], inp["dy"], w.e_lo, w.e_hi)
+    assert_close("d_topk_w", _np(g["d_topk_w"]), ref["dw"], w.dtype)
+    assert_close("d_logits", _np(g["d_logits"]), ref["d_logits"], w.dtype)
+    assert_close("dw_router", _np(g["dw_router"]), ref["dw_router"], w.dtype)
+    assert_close("dw_down", _np(g["dw_down"]), ref["dw_down"], w.dtype)
+    assert_close("dw_gate", _np(g["dw_gate"]), ref["dw_gate"], w.dtype)
+    assert_close("dw_up", _np(g["dw_up"]), ref["dw_up"], w.dtype)
+    assert_close("dx", _np(g["dx"]), ref["dx"], w.dtype)
+    counts = layer.buf["counts"].cpu().numpy()
+    for e in np.nonzero(counts == 0)[0]:
+        for n in ("dw_gate", "dw_up", "dw_down"):
+            assert (g[n][e] == 0).all(), f"{n} of empty expert {e} is not exactly zero"
+    nonlocal_ = (idx < w.e_lo) | (idx >= w.e_hi)
+    assert (g["d_topk_w"].cpu().numpy()[nonlocal_] == 0).all()
+
+
+def test_weight_grad_accumulate():
+    w = TRAIN.scaled(name="acc", T=512, H=256, I=128, E=16, k=4, e_lo=0, e_hi=8)
+    inp = _inputs(w)
+    t = _gpu_tensors(w, inp)
+    layer, _, g = run_layer(w, t)
+    base = {n: g[n].clone() for n in ("dw_gate", "dw_up", "dw_down")}
+    prior = {n: torch.randn_like(base[n]) for n in base}
+    out = {n: prior[n].clone() for n in base}
+    b = layer.buf
+    moe.moe_grouped_ffn_bwd(b["dy_perm"], b["x_perm"], b["gu"], b["h_perm"], b["offsets"], t["w_gate"],
+                            t["w_up"], t["w_down"], accumulate=True, out=out)
+    torch.cuda.synchronize()
+    for n in base:
+        torch.testing.assert_close(out[n], prior[n] + base[n], rtol=0, atol=1e-6)
+
+
+def test_layer_is_deterministic():
+    w = TRAIN.scaled(name="det", T=2048)
+    inp = _inputs(w)
+    t = _gpu_tensors(w, inp)
+    _, y1, g1 = run_layer(w, t)
+    y1, g1 = y1.clone(), {n: v.clone() for n, v in g1.items()}
+    _, y2, g2 = run_layer(w, t)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    for n in g1:
+        assert torch.equal(g1[n], g2[n]), n
