@@ -13,6 +13,9 @@ typedef uint16_t bf16_t;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// 16 bytes as a native vector: staging values stay in registers (the
+// union-based HIP uint4 is not always split into registers by the compiler).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kMaxE = 256;
@@ -23,17 +26,18 @@ constexpr int kMaxK = 32;
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
-// Round to nearest, ties to even.  NaN stays NaN (quietened), infinities pass.
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return (bf16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+// Round to nearest, ties to even, with the gfx950 conversion instruction
+// (v_cvt_pk_bf16_f32); NaN stays NaN, infinities pass.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
+
+// 1 / x with the hardware reciprocal (about 1 ulp).
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // Unpack 8 bf16 held in a uint4 into fp32.
 __device__ __forceinline__ void unpack8(const uint4& v, float* f) {
