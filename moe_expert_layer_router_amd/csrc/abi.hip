@@ -69,10 +69,17 @@ int check_ws(const void* ws, size_t have, size_t need, const char* fn) {
   return MOE_OK;
 }
 
-int route_bwd_splits(int T) { return std::max(1, std::min(16, (T + 1023) / 1024)); }
+// Split of the token (K) dimension of dW_r = x^T dz: enough (H/128) x (2E/256)
+// tiles x splits to fill 256 compute units, each split at least 256 tokens,
+// at most 32 splits.
+int route_bwd_splits(int T, int H, int E) {
+  const int tiles = ((H + 127) / 128) * ((2 * E + 255) / 256);
+  const int want = (256 + tiles - 1) / tiles;
+  return std::max(1, std::min(std::min(32, want), (T + 255) / 256));
+}
 
 size_t ws_route(int H, int E, int dtype) {
-  return dtype == MOE_BF16 ? align256((size_t)E * H * 2) : 0;
+  return dtype == MOE_BF16 ? align256(route_ws_bytes(H, E)) : 0;
 }
 size_t ws_ffn_fwd(int R_cap, int E_l, int dtype) {
   return dtype == MOE_BF16 ? ffn_sched_bytes(R_cap, E_l) : 0;
@@ -85,7 +92,7 @@ size_t ws_route_bwd(int T, int H, int E, int dtype) {
   const size_t wt = align256((size_t)E * H * elem_bytes(dtype));
   if (dtype != MOE_BF16) return wt;
   return wt + align256((size_t)T * 2 * E * 2) +
-         align256((size_t)route_bwd_splits(T) * H * 2 * E * sizeof(float));
+         align256((size_t)route_bwd_splits(T, H, E) * H * 2 * E * sizeof(float));
 }
 
 int check_ffn_shape(int E_l, int R_cap, int H, int I, int dtype, const char* fn) {
@@ -373,7 +380,7 @@ int moe_route_bwd(const float* d_topk_w, const float* topk_w, const int32_t* top
   w += align256((size_t)E * H * elem_bytes(dtype));
   bf16_t* dz_hilo = nullptr;
   float* partials = nullptr;
-  const int nsplit = route_bwd_splits(T);
+  const int nsplit = route_bwd_splits(T, H, E);
   if (bf16) {
     dz_hilo = (bf16_t*)w;
     w += align256((size_t)T * 2 * E * 2);

@@ -2,47 +2,106 @@
 //
 // The "unpermute" of the dispatcher table (page "FSDPTurbo EP/EFSDP and
 // LlamaFactory FSDP2/CP Design", section 3) becomes a per-token gather-reduce:
-// one wave owns one token, reads its k grouped rows with 16-byte vectors and
-// sums them in fp32 in slot order j = 0..k-1.  No atomics, so the result is
+// one wave owns one token, packs its local slots into the low lanes, issues
+// the 16-byte loads of up to four grouped rows x four chunks per lane at once
+// and sums them in fp32 in slot order j = 0..k-1.  No atomics, so the result is
 // deterministic and independent of the launch shape.
 #include "common.h"
 
 namespace moe {
 
-// 16 bytes of a row as fp32: 8 bf16 or 4 fp32 elements.
+// 16 bytes of a row: 8 bf16 or 4 fp32 elements, held as a native vector.
 template <bool BF16>
-struct Vec {
+struct Row {
   static constexpr int N = BF16 ? 8 : 4;
-  __device__ static void load(const void* base, size_t elem, float* f) {
-    const uint4 v = *reinterpret_cast<const uint4*>((const char*)base + elem * (BF16 ? 2 : 4));
-    if constexpr (BF16) {
-      unpack8(v, f);
-    } else {
-      f[0] = __uint_as_float(v.x);
-      f[1] = __uint_as_float(v.y);
-      f[2] = __uint_as_float(v.z);
-      f[3] = __uint_as_float(v.w);
+  static constexpr int EB = BF16 ? 2 : 4;
+  __device__ static u32x4_t ld(const void* base, size_t elem) {
+    return *reinterpret_cast<const u32x4_t*>((const char*)base + elem * EB);
+  }
+  __device__ static void st(void* base, size_t elem, u32x4_t v) {
+    *reinterpret_cast<u32x4_t*>((char*)base + elem * EB) = v;
+  }
+  __device__ static void to_f32(u32x4_t v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (BF16) {
+        f[2 * i] = __uint_as_float(v[i] << 16);
+        f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+      } else {
+        f[i] = __uint_as_float(v[i]);
+      }
     }
   }
-  __device__ static void store(void* base, size_t elem, const float* f) {
-    uint4 v;
-    if constexpr (BF16) {
-      v = pack8(f);
-    } else {
-      v = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
-                     __float_as_uint(f[3]));
-    }
-    *reinterpret_cast<uint4*>((char*)base + elem * (BF16 ? 2 : 4)) = v;
+  __device__ static u32x4_t from_f32(const float* f) {
+    u32x4_t v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = BF16 ? pack_bf2(f[2 * i], f[2 * i + 1]) : __float_as_uint(f[i]);
+    return v;
   }
 };
 
+// Chunks of 16 bytes per lane per pass and slots whose rows are loaded
+// together: all CU x SG row loads of a pass are in flight at once.
+constexpr int kCU = 4;
+constexpr int kSG = 4;
+
+// Moves the lanes holding a local slot (d >= 0; lanes >= k hold d = -1) to
+// lanes 0..n-1, keeping slot order; returns n.  Lane i then holds that slot's
+// row d, weight w and slot index j.  Lanes without a slot all send to lane
+// 63, which is never read (n <= k <= 32).
+__device__ __forceinline__ int pack_slots(int d, float w, int& dc, float& wc, int& jc) {
+  const int lane = lane_id();
+  const uint64_t m = __ballot(d >= 0);
+  const int rank = __popcll(m & ((1ull << lane) - 1ull));
+  const int to = (d >= 0 ? rank : 63) << 2;
+  dc = __builtin_amdgcn_ds_permute(to, d);
+  wc = __int_as_float(__builtin_amdgcn_ds_permute(to, __float_as_int(w)));
+  jc = __builtin_amdgcn_ds_permute(to, lane);
+  return __popcll(m);
+}
+
+// out[c] = sum over packed slots j < n (ascending) of wc_j * rows[dc_j][c] for
+// this lane's chunks c0 + u * 64 + lane; fp32 accumulation.
+template <bool BF16>
+__device__ __forceinline__ void gather_rows(const void* __restrict__ rows, int H, int nch, int c0,
+                                            int n, int dc, float wc,
+                                            float (&acc)[kCU][Row<BF16>::N]) {
+  using R = Row<BF16>;
+  const int lane = lane_id();
+  for (int j0 = 0; j0 < n; j0 += kSG) {
+    u32x4_t raw[kSG][kCU];
+    float wj[kSG];
+#pragma unroll
+    for (int s = 0; s < kSG; ++s) {
+      const int j = j0 + s;  // < 36: a valid lane index
+      const int dj = __shfl(dc, j, kWave);
+      wj[s] = (j < n) ? __shfl(wc, j, kWave) : 0.f;
+#pragma unroll
+      for (int u = 0; u < kCU; ++u) {
+        const int c = c0 + u * kWave + lane;
+        raw[s][u] = (j < n && c < nch) ? R::ld(rows, (size_t)dj * H + (size_t)c * R::N) : u32x4_t{};
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < kSG; ++s)
+#pragma unroll
+      for (int u = 0; u < kCU; ++u) {
+        float v[R::N];
+        R::to_f32(raw[s][u], v);
+#pragma unroll
+        for (int i = 0; i < R::N; ++i) acc[u][i] = fmaf(wj[s], v[i], acc[u][i]);
+      }
+  }
+}
+
+// y[t] = sum over local slots j (ascending) of w_j * y_perm[dest_j] (+ addend[t]).
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y_perm,
                                                       const float* __restrict__ topk_w,
                                                       const int32_t* __restrict__ dest_row,
                                                       const float* __restrict__ addend, int T,
                                                       int H, int k, void* __restrict__ y) {
-  using V = Vec<BF16>;
+  using R = Row<BF16>;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int lane = lane_id();
@@ -52,40 +111,44 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     d = dest_row[(size_t)t * k + lane];
     if (topk_w != nullptr) w = topk_w[(size_t)t * k + lane];
   }
-  const int nch = H / V::N;
-  // Wave-uniform trip count: every lane joins every shuffle.
-  for (int c0 = 0; c0 < nch; c0 += kWave) {
-    const int c = c0 + lane;
-    const bool on = c < nch;
-    float acc[V::N];
+  int dc, jc;
+  float wc;
+  const int n = pack_slots(d, w, dc, wc, jc);
+  const int nch = H / R::N;
+  for (int c0 = 0; c0 < nch; c0 += kWave * kCU) {
+    float acc[kCU][R::N];
 #pragma unroll
-    for (int i = 0; i < V::N; ++i) acc[i] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int dj = __shfl(d, j, kWave);
-      const float wj = __shfl(w, j, kWave);
-      if (dj < 0 || !on) continue;
-      float v[V::N];
-      V::load(y_perm, (size_t)dj * H + (size_t)c * V::N, v);
+    for (int u = 0; u < kCU; ++u)
 #pragma unroll
-      for (int i = 0; i < V::N; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
-    }
-    if (!on) continue;
+      for (int i = 0; i < R::N; ++i) acc[u][i] = 0.f;
+    f32x4_t add[kCU][R::N / 4];
     if (addend != nullptr) {
-      const float4* ad = reinterpret_cast<const float4*>(addend + (size_t)t * H + (size_t)c * V::N);
 #pragma unroll
-      for (int q = 0; q < V::N / 4; ++q) {
-        const float4 a = ad[q];
-        acc[4 * q] += a.x;
-        acc[4 * q + 1] += a.y;
-        acc[4 * q + 2] += a.z;
-        acc[4 * q + 3] += a.w;
+      for (int u = 0; u < kCU; ++u) {
+        const int c = c0 + u * kWave + lane;
+#pragma unroll
+        for (int q = 0; q < R::N / 4; ++q)
+          add[u][q] = c < nch ? *reinterpret_cast<const f32x4_t*>(addend + (size_t)t * H +
+                                                                   (size_t)c * R::N + 4 * q)
+                              : f32x4_t{};
       }
     }
-    V::store(y, (size_t)t * H + (size_t)c * V::N, acc);
+    gather_rows<BF16>(y_perm, H, nch, c0, n, dc, wc, acc);
+#pragma unroll
+    for (int u = 0; u < kCU; ++u) {
+      const int c = c0 + u * kWave + lane;
+      if (c >= nch) continue;
+      if (addend != nullptr) {
+#pragma unroll
+        for (int i = 0; i < R::N; ++i) acc[u][i] += add[u][i / 4][i % 4];
+      }
+      R::st(y, (size_t)t * H + (size_t)c * R::N, R::from_f32(acc[u]));
+    }
   }
 }
 
-// dy_perm[dest] = w * dy[t];  d_topk_w[t, j] = <dy[t], y_perm[dest]>.
+// dy_perm[dest_j] = w_j * dy[t];  d_topk_w[t, j] = <dy[t], y_perm[dest_j]>
+// (0 for slots of other experts).
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const void* __restrict__ dy,
                                                           const void* __restrict__ y_perm,
@@ -94,32 +157,65 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const void* __restrict
                                                           int T, int H, int k,
                                                           void* __restrict__ dy_perm,
                                                           float* __restrict__ d_topk_w) {
-  using V = Vec<BF16>;
+  using R = Row<BF16>;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int lane = lane_id();
-  const int nch = H / V::N;
-  for (int j = 0; j < k; ++j) {
-    const int d = dest_row[(size_t)t * k + j];
-    if (d < 0) {
-      if (lane == 0) d_topk_w[(size_t)t * k + j] = 0.f;
-      continue;
-    }
-    const float w = topk_w[(size_t)t * k + j];
-    float dot = 0.f;
-    for (int c = lane; c < nch; c += kWave) {
-      float g[V::N], v[V::N];
-      V::load(dy, (size_t)t * H + (size_t)c * V::N, g);
-      V::load(y_perm, (size_t)d * H + (size_t)c * V::N, v);
+  int d = -1;
+  float w = 0.f;
+  if (lane < k) {
+    d = dest_row[(size_t)t * k + lane];
+    w = topk_w[(size_t)t * k + lane];
+    if (d < 0) d_topk_w[(size_t)t * k + lane] = 0.f;
+  }
+  int dc, jc;
+  float wc;
+  const int n = pack_slots(d, w, dc, wc, jc);
+  const int nch = H / R::N;
+  for (int j0 = 0; j0 < n; j0 += kSG) {
+    int dj[kSG];
+    float wj[kSG], dot[kSG];
 #pragma unroll
-      for (int i = 0; i < V::N; ++i) {
-        dot = fmaf(g[i], v[i], dot);
-        g[i] *= w;
-      }
-      V::store(dy_perm, (size_t)d * H + (size_t)c * V::N, g);
+    for (int s = 0; s < kSG; ++s) {
+      dj[s] = __shfl(dc, j0 + s, kWave);
+      wj[s] = __shfl(wc, j0 + s, kWave);
+      dot[s] = 0.f;
     }
-    dot = wave_sum(dot);
-    if (lane == 0) d_topk_w[(size_t)t * k + j] = dot;
+    for (int c0 = 0; c0 < nch; c0 += kWave * kCU) {
+      u32x4_t g[kCU], raw[kSG][kCU];
+#pragma unroll
+      for (int u = 0; u < kCU; ++u) {
+        const int c = c0 + u * kWave + lane;
+        g[u] = c < nch ? R::ld(dy, (size_t)t * H + (size_t)c * R::N) : u32x4_t{};
+#pragma unroll
+        for (int s = 0; s < kSG; ++s)
+          raw[s][u] = (j0 + s < n && c < nch) ? R::ld(y_perm, (size_t)dj[s] * H + (size_t)c * R::N)
+                                              : u32x4_t{};
+      }
+#pragma unroll
+      for (int u = 0; u < kCU; ++u) {
+        const int c = c0 + u * kWave + lane;
+        float gf[R::N];
+        R::to_f32(g[u], gf);
+#pragma unroll
+        for (int s = 0; s < kSG; ++s) {
+          float v[R::N], o[R::N];
+          R::to_f32(raw[s][u], v);
+#pragma unroll
+          for (int i = 0; i < R::N; ++i) {
+            dot[s] = fmaf(gf[i], v[i], dot[s]);
+            o[i] = wj[s] * gf[i];
+          }
+          if (j0 + s < n && c < nch) R::st(dy_perm, (size_t)dj[s] * H + (size_t)c * R::N, R::from_f32(o));
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < kSG; ++s) {
+      const float sum = wave_sum(dot[s]);
+      const int js = __shfl(jc, j0 + s, kWave);
+      if (lane == 0 && j0 + s < n) d_topk_w[(size_t)t * k + js] = sum;
+    }
   }
 }
 
@@ -134,7 +230,7 @@ __global__ __launch_bounds__(256) void route_bwd_dz_kernel(
     const int32_t* __restrict__ topk_idx, const void* __restrict__ w_router_t, int T, int H,
     int E, int k, float* __restrict__ d_logits, float* __restrict__ dx_router,
     bf16_t* __restrict__ dz_hilo) {
-  using V = Vec<BF16>;
+  using R = Row<BF16>;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int lane = lane_id();
@@ -165,27 +261,23 @@ __global__ __launch_bounds__(256) void route_bwd_dz_kernel(
     }
   }
   if (dx_router == nullptr) return;
-  const int nch = H / V::N;
-  for (int c0 = 0; c0 < nch; c0 += kWave) {
-    const int c = c0 + lane;
-    const bool on = c < nch;
-    float acc[V::N];
+  const int nch = H / R::N;
+  for (int c0 = 0; c0 < nch; c0 += kWave * kCU) {
+    float acc[kCU][R::N];
 #pragma unroll
-    for (int i = 0; i < V::N; ++i) acc[i] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int ij = __shfl(id, j, kWave);
-      const float dj = __shfl(dz, j, kWave);
-      if (!on) continue;
-      float v[V::N];
-      V::load(w_router_t, (size_t)ij * H + (size_t)c * V::N, v);
+    for (int u = 0; u < kCU; ++u)
 #pragma unroll
-      for (int i = 0; i < V::N; ++i) acc[i] = fmaf(dj, v[i], acc[i]);
+      for (int i = 0; i < R::N; ++i) acc[u][i] = 0.f;
+    gather_rows<BF16>(w_router_t, H, nch, c0, k, id, dz, acc);
+#pragma unroll
+    for (int u = 0; u < kCU; ++u) {
+      const int c = c0 + u * kWave + lane;
+      if (c >= nch) continue;
+#pragma unroll
+      for (int q = 0; q < R::N / 4; ++q)
+        *reinterpret_cast<f32x4_t*>(dx_router + (size_t)t * H + (size_t)c * R::N + 4 * q) =
+            f32x4_t{acc[u][4 * q], acc[u][4 * q + 1], acc[u][4 * q + 2], acc[u][4 * q + 3]};
     }
-    if (!on) continue;
-    float4* out = reinterpret_cast<float4*>(dx_router + (size_t)t * H + (size_t)c * V::N);
-#pragma unroll
-    for (int q = 0; q < V::N / 4; ++q)
-      out[q] = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
   }
 }
 

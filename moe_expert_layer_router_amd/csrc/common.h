@@ -95,9 +95,11 @@ struct ProfScope {
 namespace moe {
 
 // route.hip
+int route_nb(int E);                      // 32-expert column blocks of the bf16 router
+size_t route_ws_bytes(int H, int E);      // packed W_r fragments of the bf16 router
 hipError_t launch_route_bf16(const bf16_t* x, const bf16_t* w_router, const float* bias, int T,
                              int H, int E, int k, float* logits, int32_t* topk_idx, float* topk_w,
-                             bf16_t* wt_ws, hipStream_t s);
+                             bf16_t* wp_ws, hipStream_t s);
 hipError_t launch_route_f32(const float* x, const float* w_router, const float* bias, int T, int H,
                             int E, int k, float* logits, int32_t* topk_idx, float* topk_w,
                             hipStream_t s);

@@ -11,8 +11,9 @@
 //     block (popcount of the mask bits below it).
 //  2. scan: one workgroup turns block counts into counts, offsets and the base
 //     row of every (block, expert) pair.
-//  3. scatter: one wave per token computes its k destination rows and copies
-//     the token row once from HBM into k grouped rows with 16-byte vectors.
+//  3. scatter: one wave per token computes its k destination rows and, if
+//     any slot is local, copies the token row once from HBM into its grouped
+//     rows with 16-byte vectors.
 #include "common.h"
 
 namespace moe {
@@ -28,110 +29,159 @@ __global__ __launch_bounds__(kPermBlock) void hist_rank_kernel(const int32_t* __
                                                                int T, int k, int e_lo, int E_l,
                                                                int32_t* __restrict__ block_counts,
                                                                int32_t* __restrict__ rank) {
-  __shared__ uint32_t mask[kMaxE][kPermBlock / 32];
+  constexpr int NW = kPermBlock / 32;  // mask words per expert
+  __shared__ uint32_t mask[kMaxE][NW];
+  __shared__ int16_t s_e[kPermBlock * kMaxK];  // local expert of each slot of the block, or -1
+  __shared__ int32_t s_pre[kMaxE][NW];         // set bits of mask[e] in words before w
   const int tid = threadIdx.x;
-  const int t = blockIdx.x * kPermBlock + tid;
-  for (int i = tid; i < E_l * (kPermBlock / 32); i += kPermBlock) (&mask[0][0])[i] = 0u;
+  const int t0 = blockIdx.x * kPermBlock;
+  const int nt = min(kPermBlock, T - t0);
+  const int nslot = nt * k;
+  for (int i = tid; i < E_l * NW; i += kPermBlock) (&mask[0][0])[i] = 0u;
+  // Coalesced copy of the block's [nt, k] slice of idx, four loads in flight
+  // per thread before any is used.
+  const int32_t* src = idx + (size_t)t0 * k;
+  for (int i0 = 0; i0 < nslot; i0 += 4 * kPermBlock) {
+    int v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * kPermBlock + tid;
+      v[u] = i < nslot ? src[i] - e_lo : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * kPermBlock + tid;
+      if (i < nslot) s_e[i] = (v[u] >= 0 && v[u] < E_l) ? (int16_t)v[u] : (int16_t)-1;
+    }
+  }
   __syncthreads();
   const int word = tid >> 5;
   const uint32_t bit = 1u << (tid & 31);
-  if (t < T) {
+  if (tid < nt) {
     for (int j = 0; j < k; ++j) {
-      const int e = idx[(size_t)t * k + j] - e_lo;
-      if (e >= 0 && e < E_l) atomicOr(&mask[e][word], bit);
+      const int e = s_e[tid * k + j];
+      if (e >= 0) atomicOr(&mask[e][word], bit);
     }
   }
   __syncthreads();
-  if (t < T) {
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[(size_t)t * k + j] - e_lo;
-      int r = -1;
-      if (e >= 0 && e < E_l) {
-        r = __popc(mask[e][word] & (bit - 1u));
-        for (int w = 0; w < word; ++w) r += __popc(mask[e][w]);
-      }
-      rank[(size_t)t * k + j] = r;
-    }
-  }
   for (int e = tid; e < E_l; e += kPermBlock) {
     int c = 0;
 #pragma unroll
-    for (int w = 0; w < kPermBlock / 32; ++w) c += __popc(mask[e][w]);
+    for (int w = 0; w < NW; ++w) {
+      s_pre[e][w] = c;
+      c += __popc(mask[e][w]);
+    }
     block_counts[(size_t)blockIdx.x * E_l + e] = c;
+  }
+  __syncthreads();
+  if (tid < nt) {
+    for (int j = 0; j < k; ++j) {
+      const int e = s_e[tid * k + j];
+      rank[(size_t)(t0 + tid) * k + j] =
+          e >= 0 ? s_pre[e][word] + __popc(mask[e][word] & (bit - 1u)) : -1;
+    }
   }
 }
 
-// One workgroup of kMaxE threads; thread e owns local expert e.
+// One workgroup of kMaxE threads; thread e owns local expert e.  Block counts
+// are read 32 blocks at a time with all loads in flight together.
 __global__ __launch_bounds__(kMaxE) void scan_kernel(const int32_t* __restrict__ block_counts,
                                                      int nblk, int E_l,
                                                      int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ base) {
+  constexpr int CH = 32;
   __shared__ int s[kMaxE];
   const int e = threadIdx.x;
+  const bool own = e < E_l;
   int total = 0;
-  if (e < E_l)
-    for (int b = 0; b < nblk; ++b) total += block_counts[(size_t)b * E_l + e];
+  int v[CH];
+  for (int b0 = 0; b0 < nblk; b0 += CH) {
+#pragma unroll
+    for (int u = 0; u < CH; ++u)
+      v[u] = (own && b0 + u < nblk) ? block_counts[(size_t)(b0 + u) * E_l + e] : 0;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) total += v[u];
+  }
   s[e] = total;
   __syncthreads();
   // Hillis-Steele inclusive scan over the kMaxE entries.
   for (int o = 1; o < kMaxE; o <<= 1) {
-    const int v = (e >= o) ? s[e - o] : 0;
+    const int x = (e >= o) ? s[e - o] : 0;
     __syncthreads();
-    s[e] += v;
+    s[e] += x;
     __syncthreads();
   }
   const int excl = s[e] - total;
-  if (e < E_l) {
-    counts[e] = total;
-    offsets[e] = excl;
-    if (e == E_l - 1) offsets[E_l] = excl + total;
-    int run = excl;
-    for (int b = 0; b < nblk; ++b) {
-      base[(size_t)b * E_l + e] = run;
-      run += block_counts[(size_t)b * E_l + e];
+  if (!own) return;
+  counts[e] = total;
+  offsets[e] = excl;
+  if (e == E_l - 1) offsets[E_l] = excl + total;
+  int run = excl;
+  for (int b0 = 0; b0 < nblk; b0 += CH) {
+    if (nblk > CH) {  // the values of this chunk are no longer in registers
+#pragma unroll
+      for (int u = 0; u < CH; ++u)
+        v[u] = b0 + u < nblk ? block_counts[(size_t)(b0 + u) * E_l + e] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      if (b0 + u < nblk) base[(size_t)(b0 + u) * E_l + e] = run;
+      run += v[u];
     }
   }
 }
 
-// One wave per token: destination rows, inverse map, and the row copy.
-__global__ __launch_bounds__(256) void scatter_kernel(const uint4* __restrict__ x,
+// One wave per token: destination rows, inverse map, and the row copy.  The
+// token row is read only when at least one of its slots is local, together
+// with the slots' ranks and block bases.
+__global__ __launch_bounds__(256) void scatter_kernel(const u32x4_t* __restrict__ x,
                                                       const int32_t* __restrict__ idx,
                                                       const int32_t* __restrict__ rank,
                                                       const int32_t* __restrict__ base, int T,
                                                       int k, int e_lo, int E_l, int nvec,
                                                       int32_t* __restrict__ dest_row,
                                                       int32_t* __restrict__ src_row,
-                                                      uint4* __restrict__ x_perm) {
+                                                      u32x4_t* __restrict__ x_perm) {
+  constexpr int CU = 4;  // 16-byte vectors per lane in flight
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int lane = lane_id();
   const int b = t / kPermBlock;
-  int dest = -1;
+  int e = -1;
   if (lane < k) {
-    const int e = idx[(size_t)t * k + lane] - e_lo;
-    if (e >= 0 && e < E_l) {
-      dest = base[(size_t)b * E_l + e] + rank[(size_t)t * k + lane];
-      src_row[dest] = t;
-    }
-    dest_row[(size_t)t * k + lane] = dest;
+    e = idx[(size_t)t * k + lane] - e_lo;
+    if (e >= E_l) e = -1;
   }
-  const uint4* xs = x + (size_t)t * nvec;
-  // Wave-uniform trip count: every lane joins every shuffle.
-  for (int v00 = 0; v00 < nvec; v00 += 4 * kWave) {
-    const int v0 = v00 + lane;
-    uint4 r[4];
+  const uint64_t m = __ballot(e >= 0);
+  if (m == 0) {
+    if (lane < k) dest_row[(size_t)t * k + lane] = -1;
+    return;
+  }
+  int dest = -1;
+  if (e >= 0) dest = base[(size_t)b * E_l + e] + rank[(size_t)t * k + lane];
+  const u32x4_t* xs = x + (size_t)t * nvec;
+  u32x4_t r[CU];
+  int v0 = lane;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (v0 + u * kWave < nvec) r[u] = xs[v0 + u * kWave];
-    for (int j = 0; j < k; ++j) {
-      const int d = __shfl(dest, j, kWave);
-      if (d < 0) continue;
-      uint4* xd = x_perm + (size_t)d * nvec;
+  for (int u = 0; u < CU; ++u) r[u] = (v0 + u * kWave < nvec) ? xs[v0 + u * kWave] : u32x4_t{};
+  if (lane < k) {
+    dest_row[(size_t)t * k + lane] = dest;
+    if (dest >= 0) src_row[dest] = t;
+  }
+  // Wave-uniform trip counts: every lane joins every shuffle.
+  for (;;) {
+    for (uint64_t mm = m; mm != 0; mm &= mm - 1) {
+      const int d = __shfl(dest, __ffsll((long long)mm) - 1, kWave);
+      u32x4_t* xd = x_perm + (size_t)d * nvec;
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < CU; ++u)
         if (v0 + u * kWave < nvec) xd[v0 + u * kWave] = r[u];
     }
+    v0 += CU * kWave;
+    if (v0 - lane >= nvec) break;
+#pragma unroll
+    for (int u = 0; u < CU; ++u) r[u] = (v0 + u * kWave < nvec) ? xs[v0 + u * kWave] : u32x4_t{};
   }
 }
 
@@ -165,8 +215,9 @@ hipError_t launch_permute(const void* x, const int32_t* topk_idx, int T, int H, 
   if (T == 0) return hipSuccess;
   const int nvec = H * elem_bytes / 16;
   ProfScope ps(MOE_KERNEL_PERMUTE_SCATTER, s);
-  scatter_kernel<<<(T + 3) / 4, 256, 0, s>>>((const uint4*)x, topk_idx, rank, base, T, k, e_lo,
-                                              E_l, nvec, dest_row, src_row, (uint4*)x_perm);
+  scatter_kernel<<<(T + 3) / 4, 256, 0, s>>>((const u32x4_t*)x, topk_idx, rank, base, T, k,
+                                              e_lo, E_l, nvec, dest_row, src_row,
+                                              (u32x4_t*)x_perm);
   return hipGetLastError();
 }
 

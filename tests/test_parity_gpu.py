@@ -166,7 +166,14 @@ def check_permute(w, inp, idx_g, p, x_t):
 # routing
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("w", [TINY, EP_SHARE, FULL, SKEWED], ids=lambda w: w.name)
+ROUTE_CASES = [TINY, EP_SHARE, FULL, SKEWED,
+               EP_SHARE.scaled(name="route_bf16_t777_h192_e256_k16", T=777, H=192, E=256, k=16,
+                               e_lo=0, e_hi=256),
+               EP_SHARE.scaled(name="route_bf16_t301_h320_e40_k5", T=301, H=320, E=40, k=5,
+                               e_lo=0, e_hi=40)]
+
+
+@pytest.mark.parametrize("w", ROUTE_CASES, ids=lambda w: w.name)
 def test_route_matches_oracle(w):
     inp = _inputs(w)
     t = _gpu_tensors(w, inp)
