@@ -24,6 +24,15 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
+// Entry points launch only after their arguments validated.  The launchers
+// report hipGetLastError(), which is sticky per thread: clear an error left
+// by some earlier, unrelated HIP call first, so that only this call's own
+// launch errors are reported.
+hipStream_t begin_launch(void* stream) {
+  (void)hipGetLastError();
+  return (hipStream_t)stream;
+}
+
 int hip_status(hipError_t e, const char* where) {
   if (e == hipSuccess) return MOE_OK;
   return fail(MOE_EHIP, "%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));
@@ -69,13 +78,13 @@ int check_ws(const void* ws, size_t have, size_t need, const char* fn) {
   return MOE_OK;
 }
 
-// Split of the token (K) dimension of dW_r = x^T dz: enough (H/128) x (2E/256)
-// tiles x splits to fill 256 compute units, each split at least 256 tokens,
-// at most 32 splits.
+// Split of the token (K) dimension of dW_r = x^T dz: about 128 (tile, split)
+// work items, each split at least 256 tokens, at most 16 splits (every split
+// writes an H x 2E fp32 partial that a second pass sums).
 int route_bwd_splits(int T, int H, int E) {
-  const int tiles = ((H + 127) / 128) * ((2 * E + 255) / 256);
-  const int want = (256 + tiles - 1) / tiles;
-  return std::max(1, std::min(std::min(32, want), (T + 255) / 256));
+  const int tiles = gemm_tiles(H, 2 * E);
+  const int want = (128 + tiles - 1) / tiles;
+  return std::max(1, std::min(std::min(16, want), (T + 255) / 256));
 }
 
 size_t ws_route(int H, int E, int dtype) {
@@ -195,7 +204,7 @@ int moe_route(const void* x, const void* w_router, const float* bias, int T, int
   if (int rc = check_ptr(topk_w, "topk_w", fn)) return rc;
   if (int rc = check_ws(ws, ws_bytes, ws_route(H, E, dtype), fn)) return rc;
   if (T == 0) return MOE_OK;
-  hipStream_t s = (hipStream_t)stream;
+  hipStream_t s = begin_launch(stream);
   hipError_t e;
   if (dtype == MOE_BF16)
     e = launch_route_bf16((const bf16_t*)x, (const bf16_t*)w_router, bias, T, H, E, k, logits,
@@ -214,7 +223,7 @@ int moe_route_from_logits(const float* logits, int T, int E, int k, int32_t* top
   if (int rc = check_ptr(topk_idx, "topk_idx", fn)) return rc;
   if (int rc = check_ptr(topk_w, "topk_w", fn)) return rc;
   if (T == 0) return MOE_OK;
-  return hip_status(launch_route_from_logits(logits, T, E, k, topk_idx, topk_w, (hipStream_t)stream),
+  return hip_status(launch_route_from_logits(logits, T, E, k, topk_idx, topk_w, begin_launch(stream)),
                     fn);
 }
 
@@ -239,7 +248,7 @@ int moe_permute(const void* x, const int32_t* topk_idx, int T, int H, int E, int
   const int E_l = e_hi - e_lo;
   if (int rc = check_ws(ws, ws_bytes, permute_ws_bytes(T, k, E_l), fn)) return rc;
   return hip_status(launch_permute(x, topk_idx, T, H, k, e_lo, e_hi, elem_bytes(dtype), counts,
-                                   offsets, dest_row, src_row, x_perm, ws, (hipStream_t)stream),
+                                   offsets, dest_row, src_row, x_perm, ws, begin_launch(stream)),
                     fn);
 }
 
@@ -261,7 +270,7 @@ int moe_grouped_ffn_fwd(const void* x_perm, const int32_t* offsets, int E_l, int
   }
   if (int rc = check_ws(ws, ws_bytes, ws_ffn_fwd(R_cap, E_l, dtype), fn)) return rc;
   if (R_cap == 0) return MOE_OK;
-  hipStream_t s = (hipStream_t)stream;
+  hipStream_t s = begin_launch(stream);
   hipError_t e;
   if (dtype == MOE_BF16)
     e = launch_ffn_fwd_bf16((const bf16_t*)x_perm, offsets, E_l, R_cap, H, I,
@@ -287,7 +296,7 @@ int moe_combine(const void* y_perm, const float* topk_w, const int32_t* dest_row
   if (int rc = check_ptr(y, "y", fn, true)) return rc;
   if (addend != nullptr && !aligned16(addend)) return fail(MOE_EINVAL, "%s: addend must be 16-byte aligned", fn);
   return hip_status(launch_combine(y_perm, topk_w, dest_row, addend, T, H, k, dtype == MOE_BF16, y,
-                                   (hipStream_t)stream),
+                                   begin_launch(stream)),
                     fn);
 }
 
@@ -307,7 +316,7 @@ int moe_combine_bwd(const void* dy, const void* y_perm, const float* topk_w,
   if (int rc = check_ptr(dy_perm, "dy_perm", fn, true)) return rc;
   if (int rc = check_ptr(d_topk_w, "d_topk_w", fn)) return rc;
   return hip_status(launch_combine_bwd(dy, y_perm, topk_w, dest_row, T, H, k, dtype == MOE_BF16,
-                                       dy_perm, d_topk_w, (hipStream_t)stream),
+                                       dy_perm, d_topk_w, begin_launch(stream)),
                     fn);
 }
 
@@ -335,7 +344,7 @@ int moe_grouped_ffn_bwd(const void* dy_perm, const void* x_perm, const void* gu_
     if (int rc = check_ptr(dx_perm, "dx_perm", fn, true)) return rc;
   }
   if (int rc = check_ws(ws, ws_bytes, ws_ffn_bwd(R_cap, E_l, I, dtype), fn)) return rc;
-  hipStream_t s = (hipStream_t)stream;
+  hipStream_t s = begin_launch(stream);
   hipError_t e;
   if (dtype == MOE_BF16)
     e = launch_ffn_bwd_bf16((const bf16_t*)dy_perm, (const bf16_t*)x_perm,
@@ -373,7 +382,7 @@ int moe_route_bwd(const float* d_topk_w, const float* topk_w, const int32_t* top
       if (int rc = check_ptr(x, "x", fn, true)) return rc;
   }
   if (int rc = check_ws(ws, ws_bytes, ws_route_bwd(T, H, E, dtype), fn)) return rc;
-  hipStream_t s = (hipStream_t)stream;
+  hipStream_t s = begin_launch(stream);
   const bool bf16 = dtype == MOE_BF16;
   char* w = (char*)ws;
   void* wt = w;

@@ -133,6 +133,7 @@ hipError_t launch_dw_router_reduce(const float* partials, int nsplit, int H, int
                                    float* dw_router, hipStream_t s);
 
 // gemm.hip (bf16 MFMA grouped GEMMs)
+int gemm_tiles(int M, int N);  // output tiles of one M x N product
 size_t ffn_sched_bytes(int R_cap, int E_l);
 hipError_t launch_ffn_fwd_bf16(const bf16_t* x_perm, const int32_t* offsets, int E_l, int R_cap,
                                int H, int I, const bf16_t* w_gate, const bf16_t* w_up,

@@ -14,16 +14,18 @@
 // and a tile table (built on the device from the offsets) maps M tiles to
 // experts.  "K-grouped": the reduction runs over an expert's rows.
 //
-// Tiling: 256 threads = 4 waves in a 2x2 grid, block tile 128 x 256, K step 64,
-// each wave a 64 x 128 sub-tile of 2 x 4 MFMA 32x32x16 bf16 blocks with fp32
-// accumulators.  Operand tiles stream into a 3-stage LDS ring (144 KB, one
-// workgroup per CU) by buffer->LDS DMA (buffer_load_dwordx4 ... lds): no
-// staging registers, and the buffer range check turns every row outside the
-// tile's valid range into zeros, which handles ragged expert groups.  The DMA
-// of K step k+2 is in flight while step k computes; waits are explicit
-// (s_waitcnt vmcnt / lgkmcnt and s_barrier).
+// Tiling: 256 threads = 4 waves in a 2x2 grid, block tile 256 x 256, K step 32,
+// each wave a 128 x 128 sub-tile of 4 x 4 MFMA 32x32x16 bf16 blocks with fp32
+// accumulators (256 accumulator registers).  The wave tile is this large so
+// that the LDS traffic per MFMA fits the CU's LDS bandwidth: per k16 sub-step
+// a wave reads 8 KB of fragments for 16 MFMAs.  Operand tiles stream into a
+// 4-stage LDS ring (128 KB, one workgroup per CU) by buffer->LDS DMA
+// (buffer_load_dwordx4 ... lds): no staging registers, and the buffer range
+// check turns every row outside the tile's valid range into zeros, which
+// handles ragged expert groups.  The DMA of K step k+3 is in flight while step
+// k computes; waits are explicit (s_waitcnt vmcnt / lgkmcnt and s_barrier).
 //   K-contiguous operands ("KC": activations in the forward, A of the data
-//   gradients) are stored as rows of 64 bf16 with the 16-byte chunks
+//   gradients) are stored as rows of 32 bf16 with the 16-byte chunks
 //   XOR-swizzled by row and read as MFMA fragments with ds_read_b128.
 //   MN-contiguous operands ("MC": weights in the data gradients, both operands
 //   of the weight gradients) are stored untransposed (rows = k) with 16-byte
@@ -37,12 +39,16 @@
 
 namespace moe {
 
-constexpr int BM = 128, BN = 256, BK = 64, NST = 3, NTH = 256;
-constexpr int kPersistentBlocks = 256;  // one 144 KB workgroup per CU
+constexpr int BM = 256, BN = 256, BK = 32, NST = 4, NTH = 256;
+constexpr int WM = 128, WN = 128;       // wave sub-tile
+constexpr int MI = WM / 32, NI = WN / 32;  // MFMA blocks per wave
+constexpr int KSUB = BK / 16;           // k16 sub-steps per K step
+constexpr int kPersistentBlocks = 256;  // one 128 KB workgroup per CU
 constexpr int kStageA = BM * BK;        // bf16 elements per A stage
 constexpr int kStageB = BN * BK;        // bf16 elements per B stage
-constexpr int NIA = BM / 32;            // DMA instructions per wave per stage, A
-constexpr int NIB = BN / 32;            // ... B
+constexpr int NIA = kStageA * 2 / 1024 / 4;  // DMA instructions (1 KB each) per wave per stage, A
+constexpr int NIB = kStageB * 2 / 1024 / 4;  // ... B
+constexpr int KCH = BK / 8;             // 16-byte chunks per KC row
 
 enum GemmKind { K_GATEUP_FWD = 0, K_DOWN_FWD = 1, K_DOWN_DGRAD = 2, K_GATEUP_DGRAD = 3, K_WGRAD = 4 };
 
@@ -85,10 +91,14 @@ template <int KIND> struct Traits {
 // ---------------------------------------------------------------------------
 // LDS layouts
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int kc_swz(int r) { return (r ^ (r >> 3)) & 7; }
-// KC tile [rows][64]: first element of logical 16-byte chunk `chunk` of row r.
+// KC tile [rows][32]: rows are 64 bytes, two per 128-byte bank line.  The 8
+// lanes of one ds_read_b128 phase read the same logical chunk of 8
+// consecutive rows; XOR with (r / 2) % 4 puts them on 8 distinct 16-byte bank
+// groups.
+__device__ __forceinline__ int kc_swz(int r) { return (r >> 1) & 3; }
+// first element of logical 16-byte chunk `chunk` of row r
 __device__ __forceinline__ int kc_idx(int r, int chunk) { return r * BK + ((chunk ^ kc_swz(r)) << 3); }
-// MC tile [64][W]: LDS position of logical 16-byte chunk c of row k (and back).
+// MC tile [BK][W]: LDS position of logical 16-byte chunk c of row k (and back).
 __device__ __forceinline__ int mc_chunk(int k, int c) { return c ^ ((k & 3) << 1); }
 
 // ---------------------------------------------------------------------------
@@ -138,20 +148,20 @@ struct Operand {
 };
 
 // KC operand: DMA instruction u of wave w covers 16-byte LDS chunks
-// p = (w*NI + u)*64 + lane, i.e. tile row p/8, LDS chunk p%8, which holds the
-// logical k chunk (p%8) ^ swz(row).
-template <int NI>
+// p = (w*N + u)*64 + lane, i.e. tile row p/KCH, LDS chunk p%KCH, which holds
+// the logical k chunk (p%KCH) ^ swz(row).
+template <int N>
 __device__ __forceinline__ void kc_rows(int wave, int lane, int u, int& row, int& chunk) {
-  const int p = (wave * NI + u) * 64 + lane;
-  row = p >> 3;
-  chunk = (p & 7) ^ kc_swz(row);
+  const int p = (wave * N + u) * 64 + lane;
+  row = p / KCH;
+  chunk = (p % KCH) ^ kc_swz(row);
 }
 
 // MC operand of width W: chunk p -> k row p / (W/8), LDS chunk p % (W/8),
 // holding logical chunk mc_chunk(row, p % (W/8)).
-template <int NI, int W>
+template <int N, int W>
 __device__ __forceinline__ void mc_rows(int wave, int lane, int u, int& row, int& chunk) {
-  const int p = (wave * NI + u) * 64 + lane;
+  const int p = (wave * N + u) * 64 + lane;
   row = p / (W / 8);
   chunk = mc_chunk(row, p % (W / 8));
 }
@@ -159,157 +169,229 @@ __device__ __forceinline__ void mc_rows(int wave, int lane, int u, int& row, int
 // ---------------------------------------------------------------------------
 // MFMA fragments from LDS
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bf16x8_t frag_kc(const bf16_t* tile, int r, int chunk) {
-  return *reinterpret_cast<const bf16x8_t*>(&tile[kc_idx(r, chunk)]);
+// GATEUP_FWD B tile rows interleave 32 gate rows and 32 up rows; DMA
+// instruction u of a wave fills tile rows 16 (w NIB + u) .. + 15 (w NIB even),
+// so whether it carries up rows depends on u alone.
+__device__ __forceinline__ bool gateup_is_up(int u) { return ((u * 64 / KCH) >> 5) & 1; }
+
+// DMA of one K step (k0 = first k) into the wave's part of a ring slot
+// (la, lb: LDS byte addresses).
+// DMA instruction u of one K step (k0 = first k) into the wave's part of a
+// ring slot (la, lb: LDS byte addresses); u < NIA: A, else B.  u is a
+// compile-time constant at every call (unrolled loops).  The K loop issues
+// every stage unconditionally, also the ones past the end of K, so that it
+// has no branches (a branch between MFMAs costs the matrix core about 40% of
+// its rate): for those `kill` = 2^31 moves the offset beyond every operand's
+// buffer range (all below 2 GiB), the hardware drops the read and writes
+// zeros into a slot that is not read again.
+constexpr uint32_t kDmaKill = 0x80000000u;
+
+template <int KIND>
+__device__ __forceinline__ void dma_piece(const GemmArgs& p, const Operand<NIA>& opA,
+                                          const Operand<NIB>& opB, uint32_t la, uint32_t lb,
+                                          int k0, uint32_t kill, int u) {
+  if (u < NIA) {
+    dma16(opA.rsrc, (opA.voff[u] + (uint32_t)k0 * opA.kstep) | kill, la + u * 1024);
+    return;
+  }
+  const int v = u - NIA;
+  if constexpr (KIND == K_GATEUP_FWD) {
+    // each instruction fills 16 rows of one gate or up block
+    dma16(gateup_is_up(v) ? opB.rsrc2 : opB.rsrc, (opB.voff[v] + (uint32_t)k0 * 2) | kill, lb + v * 1024);
+  } else if constexpr (KIND == K_GATEUP_DGRAD) {
+    const bool up = k0 >= p.I;
+    const uint32_t kk = (uint32_t)(up ? k0 - p.I : k0);
+    dma16(up ? opB.rsrc2 : opB.rsrc, (opB.voff[v] + kk * opB.kstep) | kill, lb + v * 1024);
+  } else {
+    dma16(opB.rsrc, (opB.voff[v] + (uint32_t)k0 * opB.kstep) | kill, lb + v * 1024);
+  }
 }
 
-// Lane l gets column c0 + l % 32, k = kbase + 8 * (l / 32) + 0..7.
+template <int KIND>
+__device__ __forceinline__ void issue_stage(const GemmArgs& p, const Operand<NIA>& opA,
+                                            const Operand<NIB>& opB, uint32_t la, uint32_t lb,
+                                            int k0, uint32_t kill) {
+#pragma unroll
+  for (int u = 0; u < NIA + NIB; ++u) dma_piece<KIND>(p, opA, opB, la, lb, k0, kill, u);
+}
+
+// ---------------------------------------------------------------------------
+// The LDS ring: NST slots of A, then NST slots of B, in one array.  Slots are
+// addressed with a wave-uniform byte offset, so one per-lane base register
+// serves every slot (the DMA is inline asm, so the compiler adds no waits of
+// its own between the DMA and the fragment reads; the explicit waits below
+// order the ring).
+// ---------------------------------------------------------------------------
+constexpr int kSlotA = kStageA * 2, kSlotB = kStageB * 2;  // bytes
+constexpr int kOffB = NST * kSlotA;                        // B slots start here
+__shared__ __attribute__((aligned(1024))) bf16_t g_lds[NST * (kStageA + kStageB)];
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
+
+__device__ __forceinline__ lds_char_t* lds_ptr(uint32_t byte) {
+  return (lds_char_t*)((lds_void_t*)g_lds) + byte;
+}
+
+// Per-lane byte offsets of the MFMA fragments inside a tile slot, fixed for the
+// kernel's life; everything else in a fragment address is wave-uniform or a
+// compile-time constant.
+//   KC (rows of BK bf16): lane l reads row l % 32 of a 32-row block, logical
+//   chunk 2 s + l / 32; the block's first row (a multiple of 8) does not change
+//   the swizzle, so kc[s] is the offset for block row 0.
+//   MC (transposing reads, width W): with g = l / 16, i = l % 16 the lane reads
+//   k = 16 s + 8 (g / 2) + i / 4 and column c0 + 16 (g % 2) + 4 (i % 4) of the
+//   32-column block c0 = cb + 32 mi (cb a multiple of 128).  The chunk swizzle
+//   XORs bits 1..2 of the chunk index 4 mi + x, which moves the read by +-4
+//   chunks depending on the parity of mi: mc[p] is the offset for parity p
+//   (biased by +32 elements for odd mi so that it is never negative).
+struct FragLanes {
+  uint32_t kc[KSUB];
+  uint32_t mc_a[2];
+  uint32_t mc_b[2];
+};
+
 template <int W>
-__device__ __forceinline__ bf16x8_t frag_mc(const bf16_t* tile, int kbase, int c0, int lane) {
+__device__ __forceinline__ void mc_lane_offsets(int lane, uint32_t (&mc)[2]) {
   const int g = lane >> 4, i = lane & 15;
-  const int k = kbase + 8 * (g >> 1) + (i >> 2);
-  const int col = c0 + 16 * (g & 1) + 4 * (i & 3);
-  const int e0 = k * W + (mc_chunk(k, col >> 3) << 3) + (col & 7);
-  const int e1 = (k + 4) * W + (mc_chunk(k + 4, col >> 3) << 3) + (col & 7);
-  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tile + e0));
-  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tile + e1));
+  const int x = 2 * (g & 1) + ((i & 3) >> 1);
+  const int y = ((i >> 2) & 3) << 1;
+  const int z = x ^ y;
+  const int d0 = z, d1 = (z & 3) - 4 * (z >> 2);
+  const int rowpart = (8 * (g >> 1) + (i >> 2)) * W + 4 * (i & 1);
+  mc[0] = (uint32_t)(2 * (rowpart + 8 * d0));
+  mc[1] = (uint32_t)(2 * (rowpart + 8 * d1 + 32));
+}
+
+__device__ __forceinline__ FragLanes frag_lanes(int lane) {
+  FragLanes L;
+  const int r = lane & 31;
+#pragma unroll
+  for (int s = 0; s < KSUB; ++s)
+    L.kc[s] = (uint32_t)(r * BK * 2 + (((2 * s + (lane >> 5)) ^ kc_swz(r)) << 4));
+  mc_lane_offsets<BM>(lane, L.mc_a);
+  mc_lane_offsets<BN>(lane, L.mc_b);
+  return L;
+}
+
+// KC fragment: block of 32 rows starting at byte `blk` of the slot.
+__device__ __forceinline__ bf16x8_t frag_kc(uint32_t slot, uint32_t lane_off, int blk) {
+  return *(const lds_bf16x8_t*)(lds_ptr(slot + lane_off) + blk);
+}
+
+// MC fragment: lane l gets column c0 + l % 32, k = 16 s + 8 (l / 32) + 0..7,
+// from two transposing reads (rows k and k + 4 of each 16-lane group).
+template <int W>
+__device__ __forceinline__ bf16x8_t frag_mc(uint32_t slot, uint32_t lane_off, int cst) {
+  lds_char_t* q = lds_ptr(slot + lane_off) + cst;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)q);
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(q + 8 * W));
   const i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// DMA of one K step (k0 = first k) into the wave's part of a ring slot
-// (la, lb: LDS byte addresses).
-template <int KIND>
-__device__ __forceinline__ void issue_stage(const GemmArgs& p, const Operand<NIA>& opA,
-                                            const Operand<NIB>& opB, uint32_t la, uint32_t lb,
-                                            int k0) {
-#pragma unroll
-  for (int u = 0; u < NIA; ++u) dma16(opA.rsrc, opA.voff[u] + (uint32_t)k0 * opA.kstep, la + u * 1024);
-  if constexpr (KIND == K_GATEUP_FWD) {
-#pragma unroll
-    for (int u = 0; u < NIB; ++u)  // instructions with (u >> 2) & 1 == 1 carry up rows
-      dma16(((u >> 2) & 1) ? opB.rsrc2 : opB.rsrc, opB.voff[u] + (uint32_t)k0 * 2, lb + u * 1024);
-  } else if constexpr (KIND == K_GATEUP_DGRAD) {
-    const bool up = k0 >= p.I;
-    const uint32_t kk = (uint32_t)(up ? k0 - p.I : k0);
-#pragma unroll
-    for (int u = 0; u < NIB; ++u)
-      dma16(up ? opB.rsrc2 : opB.rsrc, opB.voff[u] + kk * opB.kstep, lb + u * 1024);
-  } else {
-#pragma unroll
-    for (int u = 0; u < NIB; ++u) dma16(opB.rsrc, opB.voff[u] + (uint32_t)k0 * opB.kstep, lb + u * 1024);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// The LDS ring: one array per slot and operand.  Distinct objects let the
-// compiler see that the DMA into slot k+2 cannot touch slot k, so it adds no
-// wait of its own before the fragment reads (the explicit waits below order
-// the ring).
-// ---------------------------------------------------------------------------
-__shared__ __attribute__((aligned(1024))) bf16_t g_sA0[kStageA];
-__shared__ __attribute__((aligned(1024))) bf16_t g_sA1[kStageA];
-__shared__ __attribute__((aligned(1024))) bf16_t g_sA2[kStageA];
-__shared__ __attribute__((aligned(1024))) bf16_t g_sB0[kStageB];
-__shared__ __attribute__((aligned(1024))) bf16_t g_sB1[kStageB];
-__shared__ __attribute__((aligned(1024))) bf16_t g_sB2[kStageB];
-
-template <int S> __device__ __forceinline__ bf16_t* slot_a() {
-  if constexpr (S == 0) return g_sA0;
-  else if constexpr (S == 1) return g_sA1;
-  else return g_sA2;
-}
-template <int S> __device__ __forceinline__ bf16_t* slot_b() {
-  if constexpr (S == 0) return g_sB0;
-  else if constexpr (S == 1) return g_sB1;
-  else return g_sB2;
-}
-
-// MFMA fragments of one k = 16 sub-step of a wave's 64 x 128 sub-tile.
+// MFMA fragments of one k = 16 sub-step of a wave's 128 x 128 sub-tile.
 struct Frags {
-  bf16x8_t a[2];
-  bf16x8_t b[4];
+  bf16x8_t a[MI];
+  bf16x8_t b[NI];
 };
 
-template <int KIND, int S>
-__device__ __forceinline__ void load_frags(Frags& f, int s, int wave, int lane) {
+// sa / sb: byte offsets of the A / B slot plus the wave's block base
+// (KC: first row * BK * 2; MC: first column * 2).
+// Fragment j of a sub-step, in the order the MFMAs of the next sub-step need
+// them: A0, B0, B1, B2, B3, A1, A2, A3 (MFMAs run mi-major).
+__host__ __device__ constexpr int frag_order(int j) { return j == 0 ? 0 : j <= NI ? MI + j - 1 : j - NI; }
+
+template <int KIND>
+__device__ __forceinline__ void load_frag(Frags& f, int j, int s, uint32_t sa, uint32_t sb,
+                                          const FragLanes& L) {
   using Tr = Traits<KIND>;
-  const int wm = wave >> 1, wn = wave & 1;
-  const bf16_t* ta = slot_a<S>();
-  const bf16_t* tb = slot_b<S>();
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
+  const int q = frag_order(j);
+  if (q < MI) {
+    const int mi = q;
     if constexpr (Tr::A_KC)
-      f.a[mi] = frag_kc(ta, wm * 64 + mi * 32 + (lane & 31), 2 * s + (lane >> 5));
+      f.a[mi] = frag_kc(sa, L.kc[s], mi * 32 * BK * 2);
     else
-      f.a[mi] = frag_mc<BM>(ta, 16 * s, wm * 64 + mi * 32, lane);
-  }
-#pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
+      f.a[mi] = frag_mc<BM>(sa, L.mc_a[mi & 1], 2 * (32 * (mi & ~1) + 16 * s * BM));
+  } else {
+    const int ni = q - MI;
     if constexpr (Tr::B_KC)
-      f.b[ni] = frag_kc(tb, wn * 128 + ni * 32 + (lane & 31), 2 * s + (lane >> 5));
+      f.b[ni] = frag_kc(sb, L.kc[s], ni * 32 * BK * 2);
     else
-      f.b[ni] = frag_mc<BN>(tb, 16 * s, wn * 128 + ni * 32, lane);
+      f.b[ni] = frag_mc<BN>(sb, L.mc_b[ni & 1], 2 * (32 * (ni & ~1) + 16 * s * BN));
   }
 }
 
-__device__ __forceinline__ void mma(f32x16_t (&acc)[2][4], const Frags& f) {
+template <int KIND>
+__device__ __forceinline__ void load_frags(Frags& f, int s, uint32_t sa, uint32_t sb,
+                                           const FragLanes& L) {
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
+  for (int j = 0; j < MI + NI; ++j) load_frag<KIND>(f, j, s, sa, sb, L);
 }
 
-// One K step on ring slot S, software pipelined: on entry `cur` holds the
-// fragments of sub-step 0; the fragments of sub-step s + 1 are read while the
-// MFMAs of sub-step s run.  Before the MFMAs of the last sub-step the wave
-// waits for step kt + 1 to land (barrier), starts the DMA of step kt + 3 into
-// this slot (every wave has finished reading it) and reads the next step's
-// first fragments, so that the barrier and LDS latency hide behind MFMAs.
-template <int KIND, int S>
-__device__ __forceinline__ void k_step(const GemmArgs& p, const Operand<NIA>& opA,
-                                       const Operand<NIB>& opB, f32x16_t (&acc)[2][4],
-                                       Frags& cur, int kt, int nk, int wave, int lane) {
-  Frags nxt;
+__device__ __forceinline__ void mfma1(f32x16_t& acc, bf16x8_t a, bf16x8_t b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mma(f32x16_t (&acc)[MI][NI], const Frags& f) {
 #pragma unroll
-  for (int s = 0; s < 3; ++s) {
-    load_frags<KIND, S>(nxt, s + 1, wave, lane);
-    mma(acc, cur);
-    cur = nxt;
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) mfma1(acc[mi][ni], f.a[mi], f.b[ni]);
+}
+
+// With one wave per SIMD every stall in a wave's instruction stream idles its
+// matrix core, and a wave runs at most about one MFMA ahead of the pipe.  So
+// the other work of a K step is spread between the MFMAs, one or two
+// instructions after each (the scheduling barriers keep this order):
+//   sub-step 0: MFMA j, then fragment j of the next sub-step (j < 8);
+//   sub-step 1: MFMA j, then DMA instruction j / 2 of step kt + NST (even j)
+//               or fragment j / 2 of the next step's sub-step 0 (odd j).
+template <int KIND>
+__device__ __forceinline__ void mma_read_next(f32x16_t (&acc)[MI][NI], const Frags& cur,
+                                              Frags& nxt, int s_next, uint32_t sa, uint32_t sb,
+                                              const FragLanes& L) {
+#pragma unroll
+  for (int j = 0; j < MI * NI; ++j) {
+    mfma1(acc[j / NI][j % NI], cur.a[j / NI], cur.b[j % NI]);
+    if (j < MI + NI) load_frag<KIND>(nxt, j, s_next, sa, sb, L);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  if (kt + 1 < nk) {
-    // Step kt + 1 has landed when at most one newer step (NIA + NIB loads) is in flight.
-    if (kt + 2 < nk)
-      wait_vm<NIA + NIB>();
+}
+
+template <int KIND>
+__device__ __forceinline__ void mma_dma_read(f32x16_t (&acc)[MI][NI], const Frags& cur,
+                                             Frags& nxt, uint32_t sa, uint32_t sb,
+                                             const FragLanes& L, const GemmArgs& p,
+                                             const Operand<NIA>& opA, const Operand<NIB>& opB,
+                                             uint32_t la, uint32_t lb, int k0, uint32_t kill) {
+  static_assert(NIA + NIB == MI * NI / 2 && MI + NI == MI * NI / 2, "interleave pattern");
+#pragma unroll
+  for (int j = 0; j < MI * NI; ++j) {
+    mfma1(acc[j / NI][j % NI], cur.a[j / NI], cur.b[j % NI]);
+    if ((j & 1) == 0)
+      dma_piece<KIND>(p, opA, opB, la, lb, k0, kill, j / 2);
     else
-      wait_vm<0>();
-    lds_barrier();  // every wave: step kt + 1 landed, slot S fully read
-    if (kt + 3 < nk)
-      issue_stage<KIND>(p, opA, opB, lds_addr(slot_a<S>()) + wave * NIA * 1024,
-                        lds_addr(slot_b<S>()) + wave * NIB * 1024, (kt + 3) * BK);
-    load_frags<KIND, (S + 1) % NST>(nxt, 0, wave, lane);
+      load_frag<KIND>(nxt, j / 2, 0, sa, sb, L);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  mma(acc, cur);
-  cur = nxt;
 }
 
 // ---------------------------------------------------------------------------
 // Epilogue: the accumulators go through LDS so that global stores are 16-byte
-// row segments.  Each wave stages one 32 x 128 fp32 half of its 64 x 128
-// sub-tile at a time into its own 16 KB of a B ring slot (16-byte chunks
+// row segments.  Each wave stages one 32 x 128 fp32 quarter of its 128 x 128
+// sub-tile at a time into its own 16 KB ring slot (16-byte chunks
 // XOR-swizzled so the row pairs written by one MFMA output register hit
 // different banks), then every lane handles 8 consecutive columns of a row.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float* stage_area(int wave) {
-  return reinterpret_cast<float*>(wave < 2 ? g_sB0 : g_sB1) + (wave & 1) * 4096;
+  return reinterpret_cast<float*>(g_lds + wave * kStageA);  // A slot `wave`, 16 KB
 }
 // fp32 element (row r < 32, col c < 128) of a wave's staging area
 __device__ __forceinline__ int stage_idx(int r, int c) { return r * 128 + (c ^ (((r >> 2) & 1) << 5)); }
 
-__device__ __forceinline__ void stage_half(float* st, const f32x16_t (&acc)[2][4], int mi, int lane) {
+__device__ __forceinline__ void stage_part(float* st, const f32x16_t (&acc)[MI][NI], int mi, int lane) {
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni)
+  for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int r = 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
@@ -327,14 +409,27 @@ __device__ __forceinline__ void load8(const float* st, int r, int c, float* v) {
 }
 
 template <int KIND>
-__device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc)[2][4], int e,
+__device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc)[MI][NI], int e,
                                          int nt, int n0, int m0, int row0, int row1, int wave,
                                          int lane) {
   const int wm = wave >> 1, wn = wave & 1;
   float* st = stage_area(wave);
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
-    stage_half(st, acc, mi, lane);
+  for (int mi = 0; mi < MI; ++mi) {
+    // DOWN_DGRAD reads the saved g / u of its rows: all loads of the pass are
+    // issued before the staging, so they cost one round trip per pass.
+    u32x4_t graw[8], uraw[8];
+    if constexpr (KIND == K_DOWN_DGRAD) {
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const long row = row0 + wm * WM + mi * 32 + it * 4 + (lane >> 4);
+        const int n = n0 + wn * WN + (lane & 15) * 8;
+        const bool ok = row < row1 && n < p.N;
+        graw[it] = ok ? *reinterpret_cast<const u32x4_t*>(p.gu + row * 2 * p.I + n) : u32x4_t{};
+        uraw[it] = ok ? *reinterpret_cast<const u32x4_t*>(p.gu + row * 2 * p.I + p.I + n) : u32x4_t{};
+      }
+    }
+    stage_part(st, acc, mi, lane);
     if constexpr (KIND == K_GATEUP_FWD) {
       // staged columns: [g 32 | u 32 | g 32 | u 32] for h columns nt*128 + wn*64 + 0..63
 #pragma unroll
@@ -342,7 +437,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
         const int r = it * 8 + (lane >> 3);
         const int hc = (lane & 7) * 8;           // 0..56: h column within the wave
         const int sc = (hc >> 5) * 64 + (hc & 31);  // staged gate column
-        const long row = row0 + wm * 64 + mi * 32 + r;
+        const long row = row0 + wm * WM + mi * 32 + r;
         const int col = nt * 128 + wn * 64 + hc;
         if (row >= row1 || col >= p.I) continue;
         float g[8], u[8], h[8];
@@ -361,8 +456,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
       for (int it = 0; it < 8; ++it) {
         const int r = it * 4 + (lane >> 4);
         const int c = (lane & 15) * 8;
-        const int m = m0 + wm * 64 + mi * 32 + r;
-        const int n = n0 + wn * 128 + c;
+        const int m = m0 + wm * WM + mi * 32 + r;
+        const int n = n0 + wn * WN + c;
         if (m >= p.M || n >= p.N) continue;
         float v[8];
         load8(st, r, c, v);
@@ -383,16 +478,21 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
       for (int it = 0; it < 8; ++it) {
         const int r = it * 4 + (lane >> 4);
         const int c = (lane & 15) * 8;
-        const long row = row0 + wm * 64 + mi * 32 + r;
-        const int n = n0 + wn * 128 + c;
+        const long row = row0 + wm * WM + mi * 32 + r;
+        const int n = n0 + wn * WN + c;
         if (row >= row1 || n >= p.N) continue;
         float v[8];
         load8(st, r, c, v);
         if constexpr (KIND == K_DOWN_DGRAD) {
           // v = dh; dG = dh * u * s * (1 + g (1 - s)), dU = dh * SiLU(g), s = sigmoid(g)
           float g[8], u[8], dg[8], du[8];
-          unpack8(*reinterpret_cast<const uint4*>(p.gu + row * 2 * p.I + n), g);
-          unpack8(*reinterpret_cast<const uint4*>(p.gu + row * 2 * p.I + p.I + n), u);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            g[2 * q] = __uint_as_float(graw[it][q] << 16);
+            g[2 * q + 1] = __uint_as_float(graw[it][q] & 0xffff0000u);
+            u[2 * q] = __uint_as_float(uraw[it][q] << 16);
+            u[2 * q + 1] = __uint_as_float(uraw[it][q] & 0xffff0000u);
+          }
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const float sg = fast_rcp(1.f + __expf(-g[j]));
@@ -406,7 +506,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
         }
       }
     }
-    // the other half reuses the staging area
+    // the next quarter reuses the staging area
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
 }
@@ -422,6 +522,7 @@ __global__ __launch_bounds__(NTH) void gemm_kernel(const GemmArgs p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
+  const FragLanes L = frag_lanes(lane);
 
   int total;
   if constexpr (KIND == K_WGRAD)
@@ -536,40 +637,54 @@ __global__ __launch_bounds__(NTH) void gemm_kernel(const GemmArgs p) {
       }
     }
 
-    f32x16_t acc[2][4];
+    f32x16_t acc[MI][NI];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x16_t{};
+      for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16_t{};
 
     const int nk = (kend - kbeg + BK - 1) / BK;
     if (nk > 0) {
-      // three steps in flight, then step 0's first fragments
-      issue_stage<KIND>(p, opA, opB, lds_addr(slot_a<0>()) + wave * NIA * 1024,
-                        lds_addr(slot_b<0>()) + wave * NIB * 1024, 0);
-      if (nk > 1)
-        issue_stage<KIND>(p, opA, opB, lds_addr(slot_a<1>()) + wave * NIA * 1024,
-                          lds_addr(slot_b<1>()) + wave * NIB * 1024, BK);
-      if (nk > 2)
-        issue_stage<KIND>(p, opA, opB, lds_addr(slot_a<2>()) + wave * NIA * 1024,
-                          lds_addr(slot_b<2>()) + wave * NIB * 1024, 2 * BK);
-      if (nk > 2)
-        wait_vm<2 * (NIA + NIB)>();
-      else if (nk > 1)
-        wait_vm<NIA + NIB>();
-      else
-        wait_vm<0>();
+      const uint32_t dma_a = lds_addr(g_lds) + wave * NIA * 1024;  // this wave's DMA area
+      const uint32_t dma_b = dma_a + kOffB - wave * NIA * 1024 + wave * NIB * 1024;
+      // wave block bases inside a slot
+      const uint32_t wa = Tr::A_KC ? (uint32_t)(wm * WM * BK * 2) : (uint32_t)(wm * WM * 2);
+      const uint32_t wb = Tr::B_KC ? (uint32_t)(wn * WN * BK * 2) : (uint32_t)(wn * WN * 2);
+      // NST steps in flight (the ones past K dropped), then step 0's first fragments
+#pragma unroll
+      for (int st = 0; st < NST; ++st)
+        issue_stage<KIND>(p, opA, opB, dma_a + st * kSlotA, dma_b + st * kSlotB, st * BK,
+                          st < nk ? 0u : kDmaKill);
+      wait_vm<(NST - 1) * (NIA + NIB)>();
       lds_barrier();
-      Frags cur;
-      load_frags<KIND, 0>(cur, 0, wave, lane);
-      for (int kt = 0; kt < nk; kt += NST) {
-        k_step<KIND, 0>(p, opA, opB, acc, cur, kt, nk, wave, lane);
-        if (kt + 1 >= nk) break;
-        k_step<KIND, 1>(p, opA, opB, acc, cur, kt + 1, nk, wave, lane);
-        if (kt + 2 >= nk) break;
-        k_step<KIND, 2>(p, opA, opB, acc, cur, kt + 2, nk, wave, lane);
+      // Two fragment sets, no copies between them: f0 holds sub-step 0 (read
+      // at the end of the previous step), f1 sub-step 1.
+      static_assert(KSUB == 2, "the fragment pipeline below assumes two k16 sub-steps");
+      Frags f0, f1;
+      load_frags<KIND>(f0, 0, wa, kOffB + wb, L);
+      int slot = 0;
+      // One K step per iteration on ring slot `slot`, software pipelined: the
+      // fragments of sub-step 1 are read during the first MFMAs of sub-step 0.
+      // Before the MFMAs of sub-step 1 the wave waits for step kt + 1 to land
+      // (barrier); between those MFMAs it starts the DMA of step kt + NST into
+      // this slot (every wave has finished reading it) and reads the next
+      // step's sub-step 0 fragments.
+      for (int kt = 0; kt < nk; ++kt) {
+        const uint32_t sa = slot * kSlotA + wa, sb = kOffB + slot * kSlotB + wb;
+        mma_read_next<KIND>(acc, f0, f1, 1, sa, sb, L);
+        const int nslot = slot + 1 == NST ? 0 : slot + 1;
+        // Steps kt + 1 .. kt + NST - 1 are in flight; step kt + 1 has landed
+        // when only the newer ones (NIA + NIB loads each) remain.
+        wait_vm<(NST - 2) * (NIA + NIB)>();
+        lds_barrier();  // every wave: step kt + 1 landed, slot `slot` fully read
+        mma_dma_read<KIND>(acc, f1, f0, nslot * kSlotA + wa, kOffB + nslot * kSlotB + wb, L, p,
+                           opA, opB, dma_a + slot * kSlotA, dma_b + slot * kSlotB,
+                           (kt + NST) * BK, kt + NST < nk ? 0u : kDmaKill);
+        slot = nslot;
       }
-      // Every wave is done with the ring before the epilogue stages into it.
+      // Every wave is done with the ring, and every DMA (also the dropped
+      // ones, which write zeros) has landed, before the epilogue stages into it.
+      wait_vm<0>();
       lds_barrier();
     }
 
@@ -614,6 +729,8 @@ __global__ __launch_bounds__(kMaxE) void ffn_sched_kernel(const int32_t* __restr
 
 static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+int gemm_tiles(int M, int N) { return ((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
+
 size_t ffn_sched_bytes(int R_cap, int E_l) {
   const size_t entries = (size_t)R_cap / BM + E_l + 1;
   return align256((1 + 3 * entries) * sizeof(int32_t));
@@ -649,7 +766,7 @@ hipError_t launch_ffn_fwd_bf16(const bf16_t* x_perm, const int32_t* offsets, int
   g.K = H;
   g.N = I;
   g.I = I;
-  g.n_ntiles = (I + 127) / 128;
+  g.n_ntiles = (I + BN / 2 - 1) / (BN / 2);  // BN / 2 h columns (gate + up) per tile
   g.c0 = h_perm;
   g.ldc = I;
   g.c1 = gu;
