@@ -14,16 +14,24 @@
 // and a tile table (built on the device from the offsets) maps M tiles to
 // experts.  "K-grouped": the reduction runs over an expert's rows.
 //
-// Tiling: 256 threads = 4 waves in a 2x2 grid, block tile 256 x 256, K step 32,
-// each wave a 128 x 128 sub-tile of 4 x 4 MFMA 32x32x16 bf16 blocks with fp32
-// accumulators (256 accumulator registers).  The wave tile is this large so
-// that the LDS traffic per MFMA fits the CU's LDS bandwidth: per k16 sub-step
-// a wave reads 8 KB of fragments for 16 MFMAs.  Operand tiles stream into a
-// 4-stage LDS ring (128 KB, one workgroup per CU) by buffer->LDS DMA
+// Tiling: 256 threads = 4 waves in a 2x2 grid, block tile BM x 256, K step 32,
+// each wave a BM/2 x 128 sub-tile of (BM/64) x 4 MFMA 32x32x16 bf16 blocks with
+// fp32 accumulators.  Two block heights:
+//   BM = 256: 128 x 128 wave tiles (256 accumulator registers, one wave per
+//     SIMD), 4-stage ring of 128 KB, one workgroup per CU.  Per k16 sub-step a
+//     wave reads 8 KB of fragments for 16 MFMAs, which keeps the LDS traffic
+//     per MFMA well inside the CU's LDS bandwidth.
+//   BM = 128: 64 x 128 wave tiles (128 accumulators), 3-stage ring of 72 KB,
+//     two workgroups per CU: twice the LDS traffic per MFMA, but half the tile
+//     height (less padding of ragged expert groups, more tiles to spread over
+//     256 CUs) and a second workgroup whose MFMAs fill the gaps of the other's
+//     barriers, prologue and epilogue.
+// Operand tiles stream into the LDS ring by buffer->LDS DMA
 // (buffer_load_dwordx4 ... lds): no staging registers, and the buffer range
 // check turns every row outside the tile's valid range into zeros, which
-// handles ragged expert groups.  The DMA of K step k+3 is in flight while step
-// k computes; waits are explicit (s_waitcnt vmcnt / lgkmcnt and s_barrier).
+// handles ragged expert groups.  The DMA of K step k + NST - 1 is in flight
+// while step k computes; waits are explicit (s_waitcnt vmcnt / lgkmcnt and
+// s_barrier).
 //   K-contiguous operands ("KC": activations in the forward, A of the data
 //   gradients) are stored as rows of 32 bf16 with the 16-byte chunks
 //   XOR-swizzled by row and read as MFMA fragments with ds_read_b128.
@@ -39,16 +47,39 @@
 
 namespace moe {
 
-constexpr int BM = 256, BN = 256, BK = 32, NST = 4, NTH = 256;
-constexpr int WM = 128, WN = 128;       // wave sub-tile
-constexpr int MI = WM / 32, NI = WN / 32;  // MFMA blocks per wave
-constexpr int KSUB = BK / 16;           // k16 sub-steps per K step
-constexpr int kPersistentBlocks = 256;  // one 128 KB workgroup per CU
-constexpr int kStageA = BM * BK;        // bf16 elements per A stage
-constexpr int kStageB = BN * BK;        // bf16 elements per B stage
-constexpr int NIA = kStageA * 2 / 1024 / 4;  // DMA instructions (1 KB each) per wave per stage, A
-constexpr int NIB = kStageB * 2 / 1024 / 4;  // ... B
-constexpr int KCH = BK / 8;             // 16-byte chunks per KC row
+constexpr int BN = 256, BK = 32, NTH = 256;
+constexpr int WN = 128;                  // wave sub-tile width
+constexpr int NI = WN / 32;              // MFMA blocks per wave along N
+constexpr int KSUB = BK / 16;            // k16 sub-steps per K step
+constexpr int kCUs = 256;
+constexpr int kStageB = BN * BK;         // bf16 elements per B stage
+constexpr int NIB = kStageB * 2 / 1024 / 4;  // DMA instructions (1 KB each) per wave per stage, B
+constexpr int KCH = BK / 8;              // 16-byte chunks per KC row
+constexpr int kSlotB = kStageB * 2;      // bytes
+
+// Block-height dependent parameters.
+template <int BM_>
+struct Cfg {
+  static constexpr int BM = BM_;
+  static constexpr int WM = BM / 2;                    // wave sub-tile height
+  static constexpr int MI = WM / 32;                   // MFMA blocks per wave along M
+  static constexpr int NST = BM == 256 ? 4 : 3;        // ring stages
+  static constexpr int kStageA = BM * BK;              // bf16 elements per A stage
+  static constexpr int NIA = kStageA * 2 / 1024 / 4;   // DMA instructions per wave per stage, A
+  static constexpr int kSlotA = kStageA * 2;           // bytes
+  static constexpr int kOffB = NST * kSlotA;           // B slots start here
+  static constexpr int kLdsBytes = NST * (kSlotA + kSlotB);
+  static constexpr int kWavesPerSimd = BM == 256 ? 1 : 2;  // = workgroups per CU
+  static_assert(kLdsBytes * kWavesPerSimd <= 160 * 1024, "LDS per CU");
+  static_assert(kLdsBytes >= 4 * 16384, "the epilogue stages 16 KB per wave in the ring");
+};
+// Tile heights in use (chosen per product by measurement on the 128-expert
+// layer: 256 wherever the larger tile's lower L2 and LDS traffic per MFMA wins
+// over the finer tiling of 128; the down-projection weight gradient, whose
+// K = expert rows is short, runs faster with 128).
+constexpr int kBmGrouped = 256;
+constexpr int kBmWgrad = 256;
+constexpr int kBmWgradDown = 128;
 
 enum GemmKind { K_GATEUP_FWD = 0, K_DOWN_FWD = 1, K_DOWN_DGRAD = 2, K_GATEUP_DGRAD = 3, K_WGRAD = 4 };
 
@@ -186,10 +217,11 @@ __device__ __forceinline__ bool gateup_is_up(int u) { return ((u * 64 / KCH) >> 
 // zeros into a slot that is not read again.
 constexpr uint32_t kDmaKill = 0x80000000u;
 
-template <int KIND>
-__device__ __forceinline__ void dma_piece(const GemmArgs& p, const Operand<NIA>& opA,
+template <int KIND, class C>
+__device__ __forceinline__ void dma_piece(const GemmArgs& p, const Operand<C::NIA>& opA,
                                           const Operand<NIB>& opB, uint32_t la, uint32_t lb,
                                           int k0, uint32_t kill, int u) {
+  constexpr int NIA = C::NIA;
   if (u < NIA) {
     dma16(opA.rsrc, (opA.voff[u] + (uint32_t)k0 * opA.kstep) | kill, la + u * 1024);
     return;
@@ -207,24 +239,22 @@ __device__ __forceinline__ void dma_piece(const GemmArgs& p, const Operand<NIA>&
   }
 }
 
-template <int KIND>
-__device__ __forceinline__ void issue_stage(const GemmArgs& p, const Operand<NIA>& opA,
+template <int KIND, class C>
+__device__ __forceinline__ void issue_stage(const GemmArgs& p, const Operand<C::NIA>& opA,
                                             const Operand<NIB>& opB, uint32_t la, uint32_t lb,
                                             int k0, uint32_t kill) {
 #pragma unroll
-  for (int u = 0; u < NIA + NIB; ++u) dma_piece<KIND>(p, opA, opB, la, lb, k0, kill, u);
+  for (int u = 0; u < C::NIA + NIB; ++u) dma_piece<KIND, C>(p, opA, opB, la, lb, k0, kill, u);
 }
 
 // ---------------------------------------------------------------------------
-// The LDS ring: NST slots of A, then NST slots of B, in one array.  Slots are
-// addressed with a wave-uniform byte offset, so one per-lane base register
-// serves every slot (the DMA is inline asm, so the compiler adds no waits of
-// its own between the DMA and the fragment reads; the explicit waits below
-// order the ring).
+// The LDS ring (dynamic LDS of Cfg::kLdsBytes): NST slots of A, then NST slots
+// of B.  Slots are addressed with a wave-uniform byte offset, so one per-lane
+// base register serves every slot (the DMA is inline asm, so the compiler adds
+// no waits of its own between the DMA and the fragment reads; the explicit
+// waits below order the ring).
 // ---------------------------------------------------------------------------
-constexpr int kSlotA = kStageA * 2, kSlotB = kStageB * 2;  // bytes
-constexpr int kOffB = NST * kSlotA;                        // B slots start here
-__shared__ __attribute__((aligned(1024))) bf16_t g_lds[NST * (kStageA + kStageB)];
+extern __shared__ bf16_t g_lds[];
 typedef __attribute__((address_space(3))) char lds_char_t;
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
 
@@ -249,6 +279,8 @@ struct FragLanes {
   uint32_t mc_a[2];
   uint32_t mc_b[2];
 };
+// (the MC derivation needs the wave's first column cb to be a multiple of 64,
+// which holds for both wave heights)
 
 template <int W>
 __device__ __forceinline__ void mc_lane_offsets(int lane, uint32_t (&mc)[2]) {
@@ -262,13 +294,14 @@ __device__ __forceinline__ void mc_lane_offsets(int lane, uint32_t (&mc)[2]) {
   mc[1] = (uint32_t)(2 * (rowpart + 8 * d1 + 32));
 }
 
+template <class C>
 __device__ __forceinline__ FragLanes frag_lanes(int lane) {
   FragLanes L;
   const int r = lane & 31;
 #pragma unroll
   for (int s = 0; s < KSUB; ++s)
     L.kc[s] = (uint32_t)(r * BK * 2 + (((2 * s + (lane >> 5)) ^ kc_swz(r)) << 4));
-  mc_lane_offsets<BM>(lane, L.mc_a);
+  mc_lane_offsets<C::BM>(lane, L.mc_a);
   mc_lane_offsets<BN>(lane, L.mc_b);
   return L;
 }
@@ -289,23 +322,28 @@ __device__ __forceinline__ bf16x8_t frag_mc(uint32_t slot, uint32_t lane_off, in
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// MFMA fragments of one k = 16 sub-step of a wave's 128 x 128 sub-tile.
+// MFMA fragments of one k = 16 sub-step of a wave's sub-tile.
+template <class C>
 struct Frags {
-  bf16x8_t a[MI];
+  bf16x8_t a[C::MI];
   bf16x8_t b[NI];
 };
 
 // sa / sb: byte offsets of the A / B slot plus the wave's block base
 // (KC: first row * BK * 2; MC: first column * 2).
 // Fragment j of a sub-step, in the order the MFMAs of the next sub-step need
-// them: A0, B0, B1, B2, B3, A1, A2, A3 (MFMAs run mi-major).
-__host__ __device__ constexpr int frag_order(int j) { return j == 0 ? 0 : j <= NI ? MI + j - 1 : j - NI; }
+// them: A0, B0, B1, B2, B3, A1, A2, ... (MFMAs run mi-major).
+template <class C>
+__host__ __device__ constexpr int frag_order(int j) {
+  return j == 0 ? 0 : j <= NI ? C::MI + j - 1 : j - NI;
+}
 
-template <int KIND>
-__device__ __forceinline__ void load_frag(Frags& f, int j, int s, uint32_t sa, uint32_t sb,
+template <int KIND, class C>
+__device__ __forceinline__ void load_frag(Frags<C>& f, int j, int s, uint32_t sa, uint32_t sb,
                                           const FragLanes& L) {
   using Tr = Traits<KIND>;
-  const int q = frag_order(j);
+  constexpr int MI = C::MI, BM = C::BM;
+  const int q = frag_order<C>(j);
   if (q < MI) {
     const int mi = q;
     if constexpr (Tr::A_KC)
@@ -321,74 +359,80 @@ __device__ __forceinline__ void load_frag(Frags& f, int j, int s, uint32_t sa, u
   }
 }
 
-template <int KIND>
-__device__ __forceinline__ void load_frags(Frags& f, int s, uint32_t sa, uint32_t sb,
+template <int KIND, class C>
+__device__ __forceinline__ void load_frags(Frags<C>& f, int s, uint32_t sa, uint32_t sb,
                                            const FragLanes& L) {
 #pragma unroll
-  for (int j = 0; j < MI + NI; ++j) load_frag<KIND>(f, j, s, sa, sb, L);
+  for (int j = 0; j < C::MI + NI; ++j) load_frag<KIND, C>(f, j, s, sa, sb, L);
 }
 
 __device__ __forceinline__ void mfma1(f32x16_t& acc, bf16x8_t a, bf16x8_t b) {
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
 }
 
-__device__ __forceinline__ void mma(f32x16_t (&acc)[MI][NI], const Frags& f) {
+template <class C>
+__device__ __forceinline__ void mma(f32x16_t (&acc)[C::MI][NI], const Frags<C>& f) {
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
+  for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) mfma1(acc[mi][ni], f.a[mi], f.b[ni]);
 }
 
-// With one wave per SIMD every stall in a wave's instruction stream idles its
-// matrix core, and a wave runs at most about one MFMA ahead of the pipe.  So
-// the other work of a K step is spread between the MFMAs, one or two
-// instructions after each (the scheduling barriers keep this order):
-//   sub-step 0: MFMA j, then fragment j of the next sub-step (j < 8);
-//   sub-step 1: MFMA j, then DMA instruction j / 2 of step kt + NST (even j)
-//               or fragment j / 2 of the next step's sub-step 0 (odd j).
-template <int KIND>
-__device__ __forceinline__ void mma_read_next(f32x16_t (&acc)[MI][NI], const Frags& cur,
-                                              Frags& nxt, int s_next, uint32_t sa, uint32_t sb,
+// A stall in a wave's instruction stream idles its matrix core unless another
+// wave has MFMAs ready, and a wave runs at most about one MFMA ahead of the
+// pipe.  So the other work of a K step is spread between the MFMAs, one or
+// two instructions after each (the scheduling barriers keep this order), and
+// the K loop has no branches (a branch between MFMAs costs the matrix core
+// about 40% of its rate):
+//   sub-step 0: MFMA j, then fragment j of the next sub-step (j < MI + NI);
+//   sub-step 1: MFMA j, then DMA instruction j of step kt + NST (j < NIA + NIB)
+//               and fragment j - (MI NI - MI - NI) of the next step's
+//               sub-step 0 (the reads end with the last MFMA).
+template <int KIND, class C>
+__device__ __forceinline__ void mma_read_next(f32x16_t (&acc)[C::MI][NI], const Frags<C>& cur,
+                                              Frags<C>& nxt, int s_next, uint32_t sa, uint32_t sb,
                                               const FragLanes& L) {
+  constexpr int NM = C::MI * NI, NR = C::MI + NI;
+  static_assert(NR <= NM, "interleave pattern");
 #pragma unroll
-  for (int j = 0; j < MI * NI; ++j) {
+  for (int j = 0; j < NM; ++j) {
     mfma1(acc[j / NI][j % NI], cur.a[j / NI], cur.b[j % NI]);
-    if (j < MI + NI) load_frag<KIND>(nxt, j, s_next, sa, sb, L);
+    if (j < NR) load_frag<KIND, C>(nxt, j, s_next, sa, sb, L);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-template <int KIND>
-__device__ __forceinline__ void mma_dma_read(f32x16_t (&acc)[MI][NI], const Frags& cur,
-                                             Frags& nxt, uint32_t sa, uint32_t sb,
+template <int KIND, class C>
+__device__ __forceinline__ void mma_dma_read(f32x16_t (&acc)[C::MI][NI], const Frags<C>& cur,
+                                             Frags<C>& nxt, uint32_t sa, uint32_t sb,
                                              const FragLanes& L, const GemmArgs& p,
-                                             const Operand<NIA>& opA, const Operand<NIB>& opB,
+                                             const Operand<C::NIA>& opA, const Operand<NIB>& opB,
                                              uint32_t la, uint32_t lb, int k0, uint32_t kill) {
-  static_assert(NIA + NIB == MI * NI / 2 && MI + NI == MI * NI / 2, "interleave pattern");
+  constexpr int NM = C::MI * NI, NR = C::MI + NI, ND = C::NIA + NIB;
+  static_assert(NR <= NM && ND <= NM, "interleave pattern");
 #pragma unroll
-  for (int j = 0; j < MI * NI; ++j) {
+  for (int j = 0; j < NM; ++j) {
     mfma1(acc[j / NI][j % NI], cur.a[j / NI], cur.b[j % NI]);
-    if ((j & 1) == 0)
-      dma_piece<KIND>(p, opA, opB, la, lb, k0, kill, j / 2);
-    else
-      load_frag<KIND>(nxt, j / 2, 0, sa, sb, L);
+    if (j < ND) dma_piece<KIND, C>(p, opA, opB, la, lb, k0, kill, j);
+    if (j >= NM - NR) load_frag<KIND, C>(nxt, j - (NM - NR), 0, sa, sb, L);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Epilogue: the accumulators go through LDS so that global stores are 16-byte
-// row segments.  Each wave stages one 32 x 128 fp32 quarter of its 128 x 128
-// sub-tile at a time into its own 16 KB ring slot (16-byte chunks
+// row segments.  Each wave stages one 32 x 128 fp32 block row of its sub-tile
+// at a time into its own 16 KB of the ring (16-byte chunks
 // XOR-swizzled so the row pairs written by one MFMA output register hit
 // different banks), then every lane handles 8 consecutive columns of a row.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float* stage_area(int wave) {
-  return reinterpret_cast<float*>(g_lds + wave * kStageA);  // A slot `wave`, 16 KB
+  return reinterpret_cast<float*>(g_lds) + wave * 4096;  // 16 KB per wave
 }
 // fp32 element (row r < 32, col c < 128) of a wave's staging area
 __device__ __forceinline__ int stage_idx(int r, int c) { return r * 128 + (c ^ (((r >> 2) & 1) << 5)); }
 
+template <int MI>
 __device__ __forceinline__ void stage_part(float* st, const f32x16_t (&acc)[MI][NI], int mi, int lane) {
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni)
@@ -408,10 +452,11 @@ __device__ __forceinline__ void load8(const float* st, int r, int c, float* v) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-template <int KIND>
-__device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc)[MI][NI], int e,
+template <int KIND, class C>
+__device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc)[C::MI][NI], int e,
                                          int nt, int n0, int m0, int row0, int row1, int wave,
                                          int lane) {
+  constexpr int MI = C::MI, WM = C::WM;
   const int wm = wave >> 1, wn = wave & 1;
   float* st = stage_area(wave);
 #pragma unroll
@@ -514,15 +559,20 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
-template <int KIND>
-__global__ __launch_bounds__(NTH) void gemm_kernel(const GemmArgs p) {
+template <int KIND, int BM_>
+__global__ __launch_bounds__(NTH)
+__attribute__((amdgpu_waves_per_eu(Cfg<BM_>::kWavesPerSimd, Cfg<BM_>::kWavesPerSimd)))
+void gemm_kernel(const GemmArgs p) {
   using Tr = Traits<KIND>;
+  using C = Cfg<BM_>;
+  constexpr int BM = C::BM, WM = C::WM, MI = C::MI, NST = C::NST, NIA = C::NIA;
+  constexpr int kSlotA = C::kSlotA, kOffB = C::kOffB;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const FragLanes L = frag_lanes(lane);
+  const FragLanes L = frag_lanes<C>(lane);
 
   int total;
   if constexpr (KIND == K_WGRAD)
@@ -646,22 +696,22 @@ __global__ __launch_bounds__(NTH) void gemm_kernel(const GemmArgs p) {
     const int nk = (kend - kbeg + BK - 1) / BK;
     if (nk > 0) {
       const uint32_t dma_a = lds_addr(g_lds) + wave * NIA * 1024;  // this wave's DMA area
-      const uint32_t dma_b = dma_a + kOffB - wave * NIA * 1024 + wave * NIB * 1024;
+      const uint32_t dma_b = lds_addr(g_lds) + kOffB + wave * NIB * 1024;
       // wave block bases inside a slot
       const uint32_t wa = Tr::A_KC ? (uint32_t)(wm * WM * BK * 2) : (uint32_t)(wm * WM * 2);
       const uint32_t wb = Tr::B_KC ? (uint32_t)(wn * WN * BK * 2) : (uint32_t)(wn * WN * 2);
       // NST steps in flight (the ones past K dropped), then step 0's first fragments
 #pragma unroll
       for (int st = 0; st < NST; ++st)
-        issue_stage<KIND>(p, opA, opB, dma_a + st * kSlotA, dma_b + st * kSlotB, st * BK,
-                          st < nk ? 0u : kDmaKill);
+        issue_stage<KIND, C>(p, opA, opB, dma_a + st * kSlotA, dma_b + st * kSlotB, st * BK,
+                             st < nk ? 0u : kDmaKill);
       wait_vm<(NST - 1) * (NIA + NIB)>();
       lds_barrier();
       // Two fragment sets, no copies between them: f0 holds sub-step 0 (read
       // at the end of the previous step), f1 sub-step 1.
       static_assert(KSUB == 2, "the fragment pipeline below assumes two k16 sub-steps");
-      Frags f0, f1;
-      load_frags<KIND>(f0, 0, wa, kOffB + wb, L);
+      Frags<C> f0, f1;
+      load_frags<KIND, C>(f0, 0, wa, kOffB + wb, L);
       int slot = 0;
       // One K step per iteration on ring slot `slot`, software pipelined: the
       // fragments of sub-step 1 are read during the first MFMAs of sub-step 0.
@@ -671,15 +721,15 @@ __global__ __launch_bounds__(NTH) void gemm_kernel(const GemmArgs p) {
       // step's sub-step 0 fragments.
       for (int kt = 0; kt < nk; ++kt) {
         const uint32_t sa = slot * kSlotA + wa, sb = kOffB + slot * kSlotB + wb;
-        mma_read_next<KIND>(acc, f0, f1, 1, sa, sb, L);
+        mma_read_next<KIND, C>(acc, f0, f1, 1, sa, sb, L);
         const int nslot = slot + 1 == NST ? 0 : slot + 1;
         // Steps kt + 1 .. kt + NST - 1 are in flight; step kt + 1 has landed
         // when only the newer ones (NIA + NIB loads each) remain.
         wait_vm<(NST - 2) * (NIA + NIB)>();
         lds_barrier();  // every wave: step kt + 1 landed, slot `slot` fully read
-        mma_dma_read<KIND>(acc, f1, f0, nslot * kSlotA + wa, kOffB + nslot * kSlotB + wb, L, p,
-                           opA, opB, dma_a + slot * kSlotA, dma_b + slot * kSlotB,
-                           (kt + NST) * BK, kt + NST < nk ? 0u : kDmaKill);
+        mma_dma_read<KIND, C>(acc, f1, f0, nslot * kSlotA + wa, kOffB + nslot * kSlotB + wb, L,
+                              p, opA, opB, dma_a + slot * kSlotA, dma_b + slot * kSlotB,
+                              (kt + NST) * BK, kt + NST < nk ? 0u : kDmaKill);
         slot = nslot;
       }
       // Every wave is done with the ring, and every DMA (also the dropped
@@ -689,20 +739,21 @@ __global__ __launch_bounds__(NTH) void gemm_kernel(const GemmArgs p) {
     }
 
     // ------------------------------------------------------------ epilogue
-    epilogue<KIND>(p, acc, e, nt, n0, m0, row0, row1, wave, lane);
+    epilogue<KIND, C>(p, acc, e, nt, n0, m0, row0, row1, wave, lane);
     // The next tile's first DMA overwrites the epilogue's staging area.
     lds_barrier();
   }
 }
 
 // Tile table of the M-grouped products: for every expert with rows, one entry
-// (expert, first row, end row) per BM rows.  sched[0] = number of entries.
+// (expert, first row, end row) per `rows` rows.  sched[0] = number of entries.
 __global__ __launch_bounds__(kMaxE) void ffn_sched_kernel(const int32_t* __restrict__ offsets,
-                                                          int E_l, int32_t* __restrict__ sched) {
+                                                          int E_l, int rows,
+                                                          int32_t* __restrict__ sched) {
   __shared__ int s[kMaxE + 1];
   const int e = threadIdx.x;
   const int n = (e < E_l) ? offsets[e + 1] - offsets[e] : 0;
-  const int tiles = (n + BM - 1) / BM;
+  const int tiles = (n + rows - 1) / rows;
   s[e + 1] = tiles;
   if (e == 0) s[0] = 0;
   __syncthreads();
@@ -720,28 +771,29 @@ __global__ __launch_bounds__(kMaxE) void ffn_sched_kernel(const int32_t* __restr
       const int mid = (lo + hi + 1) >> 1;
       if (s[mid] <= i) lo = mid; else hi = mid - 1;
     }
-    const int r0 = offsets[lo] + (i - s[lo]) * BM;
+    const int r0 = offsets[lo] + (i - s[lo]) * rows;
     sched[1 + 3 * i] = lo;
     sched[2 + 3 * i] = r0;
-    sched[3 + 3 * i] = min(r0 + BM, offsets[lo + 1]);
+    sched[3 + 3 * i] = min(r0 + rows, offsets[lo + 1]);
   }
 }
 
 static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-int gemm_tiles(int M, int N) { return ((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
+int gemm_tiles(int M, int N) { return ((M + kBmWgrad - 1) / kBmWgrad) * ((N + BN - 1) / BN); }
 
 size_t ffn_sched_bytes(int R_cap, int E_l) {
-  const size_t entries = (size_t)R_cap / BM + E_l + 1;
+  const size_t entries = (size_t)R_cap / kBmGrouped + E_l + 1;
   return align256((1 + 3 * entries) * sizeof(int32_t));
 }
 
-template <int KIND>
+template <int KIND, int BM_>
 static hipError_t launch_gemm(const GemmArgs& a, int work_upper, int kernel_id, hipStream_t s) {
+  using C = Cfg<BM_>;
   if (work_upper <= 0) return hipSuccess;
-  int grid = std::min(work_upper, kPersistentBlocks);
+  const int grid = std::min(work_upper, kCUs * C::kWavesPerSimd);  // persistent
   ProfScope ps(kernel_id, s);
-  gemm_kernel<KIND><<<grid, NTH, 0, s>>>(a);
+  gemm_kernel<KIND, BM_><<<grid, NTH, C::kLdsBytes, s>>>(a);
   return hipGetLastError();
 }
 
@@ -750,10 +802,10 @@ hipError_t launch_ffn_fwd_bf16(const bf16_t* x_perm, const int32_t* offsets, int
                                const bf16_t* w_down, bf16_t* gu, bf16_t* h_perm, bf16_t* y_perm,
                                void* ws, hipStream_t s) {
   int32_t* sched = (int32_t*)ws;
-  ffn_sched_kernel<<<1, kMaxE, 0, s>>>(offsets, E_l, sched);
+  ffn_sched_kernel<<<1, kMaxE, 0, s>>>(offsets, E_l, kBmGrouped, sched);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int mt_upper = R_cap / BM + E_l;
+  const int mt_upper = R_cap / kBmGrouped + E_l;
 
   GemmArgs g{};
   g.a = x_perm;
@@ -770,7 +822,7 @@ hipError_t launch_ffn_fwd_bf16(const bf16_t* x_perm, const int32_t* offsets, int
   g.c0 = h_perm;
   g.ldc = I;
   g.c1 = gu;
-  err = launch_gemm<K_GATEUP_FWD>(g, mt_upper * g.n_ntiles, MOE_KERNEL_FFN_GATEUP, s);
+  err = launch_gemm<K_GATEUP_FWD, kBmGrouped>(g, mt_upper * g.n_ntiles, MOE_KERNEL_FFN_GATEUP, s);
   if (err != hipSuccess) return err;
 
   GemmArgs d{};
@@ -786,7 +838,7 @@ hipError_t launch_ffn_fwd_bf16(const bf16_t* x_perm, const int32_t* offsets, int
   d.n_ntiles = (H + BN - 1) / BN;
   d.c0 = y_perm;
   d.ldc = H;
-  return launch_gemm<K_DOWN_FWD>(d, mt_upper * d.n_ntiles, MOE_KERNEL_FFN_DOWN, s);
+  return launch_gemm<K_DOWN_FWD, kBmGrouped>(d, mt_upper * d.n_ntiles, MOE_KERNEL_FFN_DOWN, s);
 }
 
 hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, const bf16_t* gu,
@@ -797,10 +849,10 @@ hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, cons
                                hipStream_t s) {
   int32_t* sched = (int32_t*)ws;
   bf16_t* dgu = (bf16_t*)((char*)ws + ffn_sched_bytes(R_cap, E_l));
-  ffn_sched_kernel<<<1, kMaxE, 0, s>>>(offsets, E_l, sched);
+  ffn_sched_kernel<<<1, kMaxE, 0, s>>>(offsets, E_l, kBmGrouped, sched);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int mt_upper = R_cap / BM + E_l;
+  const int mt_upper = R_cap / kBmGrouped + E_l;
 
   // dh = dY_e W_down[e]  ->  [dG dU] through the SiLU' epilogue.
   GemmArgs a{};
@@ -816,7 +868,7 @@ hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, cons
   a.n_ntiles = (I + BN - 1) / BN;
   a.gu = gu;
   a.c0 = dgu;
-  err = launch_gemm<K_DOWN_DGRAD>(a, mt_upper * a.n_ntiles, MOE_KERNEL_FFN_DOWN_DGRAD, s);
+  err = launch_gemm<K_DOWN_DGRAD, kBmGrouped>(a, mt_upper * a.n_ntiles, MOE_KERNEL_FFN_DOWN_DGRAD, s);
   if (err != hipSuccess) return err;
 
   // dW_down[e] = dY_e^T h_e
@@ -829,14 +881,14 @@ hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, cons
   b.N = I;
   b.offsets = offsets;
   b.groups = E_l;
-  b.n_mtiles = (H + BM - 1) / BM;
+  b.n_mtiles = (H + kBmWgradDown - 1) / kBmWgradDown;
   b.n_ntiles = (I + BN - 1) / BN;
   b.f0 = dw_down;
   b.m_split = H;
   b.ldc = I;
   b.f_group_stride = (long)H * I;
   b.accumulate = accumulate ? 1 : 0;
-  err = launch_gemm<K_WGRAD>(b, E_l * b.n_mtiles * b.n_ntiles, MOE_KERNEL_FFN_DOWN_WGRAD, s);
+  err = launch_gemm<K_WGRAD, kBmWgradDown>(b, E_l * b.n_mtiles * b.n_ntiles, MOE_KERNEL_FFN_DOWN_WGRAD, s);
   if (err != hipSuccess) return err;
 
   // dX_e = dG W_gate[e] + dU W_up[e]
@@ -854,7 +906,7 @@ hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, cons
   c.n_ntiles = (H + BN - 1) / BN;
   c.c0 = dx_perm;
   c.ldc = H;
-  err = launch_gemm<K_GATEUP_DGRAD>(c, mt_upper * c.n_ntiles, MOE_KERNEL_FFN_GATEUP_DGRAD, s);
+  err = launch_gemm<K_GATEUP_DGRAD, kBmGrouped>(c, mt_upper * c.n_ntiles, MOE_KERNEL_FFN_GATEUP_DGRAD, s);
   if (err != hipSuccess) return err;
 
   // dW_gate[e] = dG_e^T X_e, dW_up[e] = dU_e^T X_e (one product with M = 2I).
@@ -867,7 +919,7 @@ hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, cons
   w.N = H;
   w.offsets = offsets;
   w.groups = E_l;
-  w.n_mtiles = (2 * I + BM - 1) / BM;
+  w.n_mtiles = (2 * I + kBmWgrad - 1) / kBmWgrad;
   w.n_ntiles = (H + BN - 1) / BN;
   w.f0 = dw_gate;
   w.f1 = dw_up;
@@ -875,7 +927,7 @@ hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, cons
   w.ldc = H;
   w.f_group_stride = (long)I * H;
   w.accumulate = accumulate ? 1 : 0;
-  return launch_gemm<K_WGRAD>(w, E_l * w.n_mtiles * w.n_ntiles, MOE_KERNEL_FFN_GATEUP_WGRAD, s);
+  return launch_gemm<K_WGRAD, kBmWgrad>(w, E_l * w.n_mtiles * w.n_ntiles, MOE_KERNEL_FFN_GATEUP_WGRAD, s);
 }
 
 hipError_t launch_dw_router_bf16(const bf16_t* x, const bf16_t* dz_hilo, int T, int H, int E,
@@ -892,14 +944,14 @@ hipError_t launch_dw_router_bf16(const bf16_t* x, const bf16_t* dz_hilo, int T, 
   w.groups = nsplit;
   w.split_rows = (T + nsplit - 1) / nsplit;
   w.ktot = T;
-  w.n_mtiles = (H + BM - 1) / BM;
+  w.n_mtiles = (H + kBmWgrad - 1) / kBmWgrad;
   w.n_ntiles = (2 * E + BN - 1) / BN;
   w.f0 = partials;
   w.m_split = H;
   w.ldc = 2 * E;
   w.f_group_stride = (long)H * 2 * E;
   w.accumulate = 0;
-  return launch_gemm<K_WGRAD>(w, nsplit * w.n_mtiles * w.n_ntiles, MOE_KERNEL_ROUTE_BWD_DW, s);
+  return launch_gemm<K_WGRAD, kBmWgrad>(w, nsplit * w.n_mtiles * w.n_ntiles, MOE_KERNEL_ROUTE_BWD_DW, s);
 }
 
 }  // namespace moe
