@@ -14,8 +14,11 @@ Prints ONE JSON line.  value = algorithmic TFLOP/s of the whole step
 """
 import argparse
 import ctypes
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -38,19 +41,22 @@ def step_flops(w, R):
     return f
 
 
-def kernel_work(name, w, R, launches):
-    """Algorithmic (flops, HBM bytes) of ONE launch of a kernel."""
+def kernel_work(name, w, R, launches, A=None):
+    """Algorithmic (flops, HBM bytes) of ONE launch of a kernel.  R = routed rows
+    kept on this GPU, A = tokens with at least one of them (rows of x, dy that
+    the scatter and the combine backward must read; all T when not given)."""
     T, H, I, E, k, El = w.T, w.H, w.I, w.E, w.k, w.E_l
+    A = T if A is None else A
     b = 2 if w.dtype == "bf16" else 4
     gu = 2 * I * b * R if w.train else 0
     tab = {
         "ROUTE": (2.0 * T * H * E, T * H * b + H * E * b + T * E * 4 + T * k * 8),
         "PERMUTE_HIST": (0, T * k * 8 + (T // 256 + 1) * El * 4),
         "PERMUTE_SCAN": (0, 2 * (T // 256 + 1) * El * 4),
-        "PERMUTE_SCATTER": (0, T * H * b + R * H * b + T * k * 12 + R * 4),
+        "PERMUTE_SCATTER": (0, A * H * b + R * H * b + T * k * 12 + R * 4),
         "FFN_GATEUP": (4.0 * R * H * I, R * H * b + 2 * El * I * H * b + R * I * b + gu),
         "FFN_DOWN": (2.0 * R * H * I, R * I * b + El * H * I * b + R * H * b),
-        "COMBINE_BWD": (0, 2 * T * H * b + 2 * R * H * b + T * k * 12),
+        "COMBINE_BWD": (0, A * H * b + 2 * R * H * b + T * k * 12),
         "ROUTE_BWD_DZ": (2.0 * T * k * H, T * k * 12 + E * H * b + T * E * 4 + T * H * 4 + T * 2 * E * 2),
         "ROUTE_BWD_DW": (2.0 * T * H * E, T * H * b + T * 2 * E * 2 + H * E * 4),
         "FFN_DOWN_DGRAD": (2.0 * R * H * I, R * H * b + El * H * I * b + 2 * R * 2 * I * b),
@@ -65,20 +71,57 @@ def kernel_work(name, w, R, launches):
     return tab[name]
 
 
-def roofline_of(name, w, R, avg_us, launches):
-    flops, nbytes = kernel_work(name, w, R, launches)
+# Measured HBM traffic per launch (rocprofv3 FETCH_SIZE and WRITE_SIZE passes,
+# scaled by what the same counters read for a plain copy of known size): a
+# committed summary under profiles/, valid only for the kernel sources it was
+# taken with.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_ep16_train_t8192.md")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "moe_expert_layer_router_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed summary, or None."""
+    try:
+        text = open(TRAFFIC_FILE, encoding="utf-8").read()
+    except OSError:
+        return None
+    m = re.search(r"kernel source hash: `([0-9a-f]+)`", text)
+    if not m or m.group(1) != kernel_source_hash() or f"workload: `{workload}`" not in text:
+        return None
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) >= 5 and cells[0] == kernel:
+            try:
+                return int(float(cells[4]))
+            except ValueError:
+                return None
+    return None
+
+
+def roofline_of(name, w, R, avg_us, launches, A=None):
+    flops, nbytes = kernel_work(name, w, R, launches, A)
     peak_f = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     t_f = flops / (peak_f * 1e12)
     t_b = nbytes / (PEAK_HBM_GBS * 1e9)
+    traffic = measured_traffic(name, w.name)
     if flops > 0 and t_f >= t_b:
         ach = flops / (avg_us * 1e-6) / 1e12
         return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak_f, "unit": "TFLOP/s",
-                "frac": round(ach / peak_f, 4), "traffic": None,
+                "frac": round(ach / peak_f, 4), "traffic": traffic,
                 "kernel": name, "algorithmic_per_launch": flops, "avg_us": round(avg_us, 2),
                 "hbm_floor_us": round(t_b * 1e6, 2), "mfma_floor_us": round(t_f * 1e6, 2)}
     ach = nbytes / (avg_us * 1e-6) / 1e9
     return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
             "kernel": name, "algorithmic_per_launch": nbytes, "avg_us": round(avg_us, 2),
             "hbm_floor_us": round(t_b * 1e6, 2), "mfma_floor_us": round(t_f * 1e6, 2)}
 
@@ -128,6 +171,9 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-times", action="store_true")
+    ap.add_argument("--pmc-calibration", action="store_true",
+                    help="after the warm-up, copy 256 MiB device to device once (outside the timed "
+                         "region): the copy kernel's FETCH_SIZE / WRITE_SIZE calibrate counter runs")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -159,7 +205,14 @@ def main():
         step()
     torch.cuda.synchronize()
     R = int(layer.buf["offsets"][-1].item())
+    A = int((layer.buf["dest_row"].view(w.T, w.k) >= 0).any(dim=1).sum().item())
     ref_out = (layer.buf["dx"] if w.train else layer.buf["y"]).clone()
+    if args.pmc_calibration:
+        src = torch.ones(128 << 20, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     graph = None
     if not args.eager:
@@ -198,6 +251,7 @@ def main():
         "data": "synthetic (seeded normal draws, random-init weights)",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "I": w.I, "E": w.E, "k": w.k,
                    "local_experts": [w.e_lo, w.e_hi], "routed_rows": R,
+                   "tokens_with_local_slots": A,
                    "pass": "forward+backward" if w.train else "forward",
                    "timing": "hip-graph replay" if graph is not None else "eager launches"},
         "tokens_per_s": round(w.T / (ms * 1e-3), 1),
@@ -233,9 +287,9 @@ def main():
                         "us_per_step": sum(times) / n}
         result["kernels_us_per_step"] = {k: round(v["us_per_step"], 2) for k, v in kt.items()}
         dom = max(kt, key=lambda k: kt[k]["us_per_step"])
-        result["roofline"] = roofline_of(dom, w, R, kt[dom]["avg_us"], kt[dom]["launches_per_step"])
+        result["roofline"] = roofline_of(dom, w, R, kt[dom]["avg_us"], kt[dom]["launches_per_step"], A)
         result["roofline_all"] = {k: {kk: vv for kk, vv in
-                                      roofline_of(k, w, R, v["avg_us"], v["launches_per_step"]).items()
+                                      roofline_of(k, w, R, v["avg_us"], v["launches_per_step"], A).items()
                                       if kk in ("bound", "achieved", "unit", "frac", "avg_us")}
                                   for k, v in kt.items()}
 
