@@ -31,7 +31,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 KERNELS = ["ROUTE", "PERMUTE_HIST", "PERMUTE_SCAN", "PERMUTE_SCATTER", "FFN_GATEUP", "FFN_DOWN",
            "COMBINE", "COMBINE_BWD", "ROUTE_BWD_DZ", "ROUTE_BWD_DW", "FFN_DOWN_DGRAD",
-           "FFN_DOWN_WGRAD", "FFN_GATEUP_DGRAD", "FFN_GATEUP_WGRAD"]
+           "FFN_DOWN_WGRAD", "FFN_GATEUP_DGRAD", "FFN_GATEUP_WGRAD", "COMBINE_DX"]
 
 
 def step_flops(w, R):
@@ -57,7 +57,8 @@ def kernel_work(name, w, R, launches, A=None):
         "FFN_GATEUP": (4.0 * R * H * I, R * H * b + 2 * El * I * H * b + R * I * b + gu),
         "FFN_DOWN": (2.0 * R * H * I, R * I * b + El * H * I * b + R * H * b),
         "COMBINE_BWD": (0, A * H * b + 2 * R * H * b + T * k * 12),
-        "ROUTE_BWD_DZ": (2.0 * T * k * H, T * k * 12 + E * H * b + T * E * 4 + T * H * 4 + T * 2 * E * 2),
+        "ROUTE_BWD_DZ": (0, T * k * 12 + T * E * 4 + T * 2 * E * 2),
+        "COMBINE_DX": (2.0 * T * k * H, R * H * b + E * H * b + T * k * 16 + T * H * b),
         "ROUTE_BWD_DW": (2.0 * T * H * E, T * H * b + T * 2 * E * 2 + H * E * 4),
         "FFN_DOWN_DGRAD": (2.0 * R * H * I, R * H * b + El * H * I * b + 2 * R * 2 * I * b),
         "FFN_DOWN_WGRAD": (2.0 * R * H * I, R * H * b + R * I * b + El * H * I * 4),
@@ -65,9 +66,7 @@ def kernel_work(name, w, R, launches, A=None):
         "FFN_GATEUP_WGRAD": (4.0 * R * H * I, R * 2 * I * b + R * H * b + 2 * El * I * H * 4),
     }
     if name == "COMBINE":
-        fwd = R * H * b + T * k * 8 + T * H * b
-        bwd = R * H * b + T * k * 4 + T * H * 4 + T * H * b
-        return 0.0, (fwd + bwd) / 2.0 if (w.train and launches == 2) else fwd
+        return 0.0, R * H * b + T * k * 8 + T * H * b
     return tab[name]
 
 

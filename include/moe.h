@@ -63,7 +63,8 @@ typedef enum {
   MOE_OP_PERMUTE = 1,
   MOE_OP_FFN_FWD = 2,
   MOE_OP_FFN_BWD = 3,
-  MOE_OP_ROUTE_BWD = 4
+  MOE_OP_ROUTE_BWD = 4,
+  MOE_OP_COMBINE_DX = 5
 } moe_op;
 
 /* Returns MOE_ABI_VERSION of the loaded library. */
@@ -145,6 +146,24 @@ int moe_combine_bwd(const void* dy, const void* y_perm, const float* topk_w,
                     const int32_t* dest_row, int T, int H, int k, int dtype, void* dy_perm,
                     float* d_topk_w, void* stream);
 
+/* The layer's input gradient in one pass: the unweighted unpermute-reduce of
+ * the experts' input gradient plus the router's input gradient, for every
+ * token
+ *   dx[t] = sum_{j: dest_row[t*k+j] >= 0} dx_perm[dest_row[t*k+j]]
+ *         + sum_j dz_j * w_router[:, topk_idx[t,j]],
+ *   dz_j = w_j (dw_j - sum_l w_l dw_l),   w = topk_w[t,:], dw = d_topk_w[t,:]
+ * accumulated in fp32 (local rows in slot order, then the router term in slot
+ * order) and rounded once to dtype.  It equals moe_combine(dx_perm, NULL,
+ * dest_row, dx_router) with dx_router from moe_route_bwd, without that
+ * [T,H] fp32 intermediate.
+ *   dx_perm [R_cap,H] dtype, dest_row [T*k] int32, d_topk_w, topk_w [T,k]
+ *   fp32, topk_idx [T,k] int32, w_router [H,E] dtype, dx [T,H] dtype
+ *   ws       MOE_OP_COMBINE_DX workspace (the transposed router weight) */
+int moe_combine_dx(const void* dx_perm, const int32_t* dest_row, const float* d_topk_w,
+                   const float* topk_w, const int32_t* topk_idx, const void* w_router, int T,
+                   int H, int E, int k, int dtype, void* dx, void* ws, size_t ws_bytes,
+                   void* stream);
+
 /* Backward of the grouped FFN, given dy_perm [R_cap,H] and the forward's
  * x_perm, gu_saved (required) and h_perm:
  *   dx_perm [R_cap,H] dtype   gradient wrt x_perm
@@ -192,7 +211,8 @@ typedef enum {
   MOE_KERNEL_FFN_DOWN_WGRAD = 11,
   MOE_KERNEL_FFN_GATEUP_DGRAD = 12,
   MOE_KERNEL_FFN_GATEUP_WGRAD = 13,
-  MOE_KERNEL_COUNT = 14
+  MOE_KERNEL_COMBINE_DX = 14,     /* fused input gradient (moe_combine_dx) */
+  MOE_KERNEL_COUNT = 15
 } moe_kernel;
 
 int moe_profile_kernel(int kernel_id, void** start_events, void** stop_events, int n);

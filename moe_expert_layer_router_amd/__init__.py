@@ -24,7 +24,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_F32, MOE_BF16 = 0, 1
-MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD, MOE_OP_ROUTE_BWD = range(5)
+(MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD, MOE_OP_ROUTE_BWD,
+ MOE_OP_COMBINE_DX) = range(6)
 ABI_VERSION = 1
 
 
@@ -48,6 +49,7 @@ def _load():
         "moe_grouped_ffn_fwd": ([P, P, I32, I32, I32, I32, P, P, P, I32, P, P, P, P, SZ, P], I32),
         "moe_combine": ([P, P, P, P, I32, I32, I32, I32, P, P], I32),
         "moe_combine_bwd": ([P, P, P, P, I32, I32, I32, I32, P, P, P], I32),
+        "moe_combine_dx": ([P, P, P, P, P, P, I32, I32, I32, I32, I32, P, P, SZ, P], I32),
         "moe_grouped_ffn_bwd": ([P, P, P, P, P, I32, I32, I32, I32, P, P, P, I32, P, P, P, P, I32,
                                  P, SZ, P], I32),
         "moe_route_bwd": ([P, P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, SZ, P], I32),
@@ -229,6 +231,21 @@ def moe_combine_bwd(dy: torch.Tensor, y_perm: torch.Tensor, topk_w: torch.Tensor
                                _dtype_code(dy), _ptr(o["dy_perm"]), _ptr(o["d_topk_w"]), _stream()),
            "moe_combine_bwd")
     return o
+
+
+def moe_combine_dx(dx_perm: torch.Tensor, dest_row: torch.Tensor, d_topk_w: torch.Tensor,
+                   topk_w: torch.Tensor, topk_idx: torch.Tensor, w_router: torch.Tensor,
+                   ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """The layer's input gradient in one pass.  Returns dx [T,H] (dtype of dx_perm)."""
+    T, k = topk_w.shape
+    H, E = w_router.shape
+    dt = _dtype_code(dx_perm)
+    dx = out if out is not None else torch.empty((T, H), dtype=dx_perm.dtype, device=dx_perm.device)
+    ws = _ws(workspace_bytes(MOE_OP_COMBINE_DX, T, H, 1, E, k, 0, E, dt), dx_perm.device, ws)
+    _check(lib.moe_combine_dx(_ptr(dx_perm), _ptr(dest_row), _ptr(d_topk_w), _ptr(topk_w),
+                              _ptr(topk_idx), _ptr(w_router), T, H, E, k, dt, _ptr(dx), _ptr(ws),
+                              _nbytes(ws), _stream()), "moe_combine_dx")
+    return dx
 
 
 def moe_grouped_ffn_bwd(dy_perm: torch.Tensor, x_perm: torch.Tensor, gu: torch.Tensor,

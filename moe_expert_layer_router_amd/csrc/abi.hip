@@ -173,6 +173,8 @@ int64_t moe_workspace_bytes(int op, int T, int H, int I, int E, int k, int e_lo,
       return (int64_t)ws_route(H, E, dtype);
     case MOE_OP_ROUTE_BWD:
       return (int64_t)ws_route_bwd(T, H, E, dtype);
+    case MOE_OP_COMBINE_DX:
+      return (int64_t)align256((size_t)E * H * elem_bytes(dtype));
     case MOE_OP_PERMUTE:
     case MOE_OP_FFN_FWD:
     case MOE_OP_FFN_BWD: {
@@ -298,6 +300,31 @@ int moe_combine(const void* y_perm, const float* topk_w, const int32_t* dest_row
   return hip_status(launch_combine(y_perm, topk_w, dest_row, addend, T, H, k, dtype == MOE_BF16, y,
                                    begin_launch(stream)),
                     fn);
+}
+
+int moe_combine_dx(const void* dx_perm, const int32_t* dest_row, const float* d_topk_w,
+                   const float* topk_w, const int32_t* topk_idx, const void* w_router, int T,
+                   int H, int E, int k, int dtype, void* dx, void* ws, size_t ws_bytes,
+                   void* stream) {
+  const char* fn = "moe_combine_dx";
+  if (int rc = check_dtype(dtype, fn)) return rc;
+  if (int rc = check_routing_shape(T, E, k, fn)) return rc;
+  if (int rc = check_row_width(H, dtype, fn)) return rc;
+  if (int rc = check_ws(ws, ws_bytes, align256((size_t)E * H * elem_bytes(dtype)), fn)) return rc;
+  if (T == 0) return MOE_OK;
+  if (int rc = check_ptr(dx_perm, "dx_perm", fn, true)) return rc;
+  if (int rc = check_ptr(dest_row, "dest_row", fn)) return rc;
+  if (int rc = check_ptr(d_topk_w, "d_topk_w", fn)) return rc;
+  if (int rc = check_ptr(topk_w, "topk_w", fn)) return rc;
+  if (int rc = check_ptr(topk_idx, "topk_idx", fn)) return rc;
+  if (int rc = check_ptr(w_router, "w_router", fn, true)) return rc;
+  if (int rc = check_ptr(dx, "dx", fn, true)) return rc;
+  hipStream_t s = begin_launch(stream);
+  hipError_t e = launch_transpose(w_router, ws, H, E, elem_bytes(dtype), s);
+  if (e == hipSuccess)
+    e = launch_combine_dx(dx_perm, dest_row, d_topk_w, topk_w, topk_idx, ws, T, H, k,
+                          dtype == MOE_BF16, dx, s);
+  return hip_status(e, fn);
 }
 
 int moe_combine_bwd(const void* dy, const void* y_perm, const float* topk_w,

@@ -219,6 +219,50 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const void* __restrict
   }
 }
 
+// Input gradient, one wave per token:
+//   dx[t] = sum over local slots of dx_perm[dest_j]  +  sum_j dz_j * W_r^T[idx_j]
+// with dz_j = w_j (dw_j - sum_l w_l dw_l) computed in the wave (lanes >= k
+// hold w = 0, so their dz is 0).
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_dx_kernel(
+    const void* __restrict__ dx_perm, const int32_t* __restrict__ dest_row,
+    const float* __restrict__ d_topk_w, const float* __restrict__ topk_w,
+    const int32_t* __restrict__ topk_idx, const void* __restrict__ w_router_t, int T, int H,
+    int k, void* __restrict__ dx) {
+  using R = Row<BF16>;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = lane_id();
+  int d = -1, id = -1;
+  float w = 0.f, dw = 0.f;
+  if (lane < k) {
+    d = dest_row[(size_t)t * k + lane];
+    w = topk_w[(size_t)t * k + lane];
+    dw = d_topk_w[(size_t)t * k + lane];
+    id = topk_idx[(size_t)t * k + lane];
+  }
+  const float inner = wave_sum(w * dw);
+  const float dz = w * (dw - inner);
+  int dc, jc;
+  float wc;
+  const int n = pack_slots(d, 1.f, dc, wc, jc);
+  const int nch = H / R::N;
+  for (int c0 = 0; c0 < nch; c0 += kWave * kCU) {
+    float acc[kCU][R::N];
+#pragma unroll
+    for (int u = 0; u < kCU; ++u)
+#pragma unroll
+      for (int i = 0; i < R::N; ++i) acc[u][i] = 0.f;
+    gather_rows<BF16>(dx_perm, H, nch, c0, n, dc, wc, acc);
+    gather_rows<BF16>(w_router_t, H, nch, c0, k, id, dz, acc);
+#pragma unroll
+    for (int u = 0; u < kCU; ++u) {
+      const int c = c0 + u * kWave + lane;
+      if (c < nch) R::st(dx, (size_t)t * H + (size_t)c * R::N, R::from_f32(acc[u]));
+    }
+  }
+}
+
 // Router backward, one wave per token:
 //   dz_j = w_j (dw_j - sum_l w_l dw_l) on the kept experts, 0 elsewhere;
 //   dx_router[t] = sum_j dz_j * W_r[:, idx_j]   (rows of the transposed W_r);
@@ -333,6 +377,20 @@ hipError_t launch_combine_bwd(const void* dy, const void* y_perm, const float* t
   else
     combine_bwd_kernel<false><<<blocks, 256, 0, s>>>(dy, y_perm, topk_w, dest_row, T, H, k,
                                                       dy_perm, d_topk_w);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_dx(const void* dx_perm, const int32_t* dest_row, const float* d_topk_w,
+                             const float* topk_w, const int32_t* topk_idx, const void* w_router_t,
+                             int T, int H, int k, bool bf16, void* dx, hipStream_t s) {
+  const int blocks = (T + 3) / 4;
+  ProfScope ps(MOE_KERNEL_COMBINE_DX, s);
+  if (bf16)
+    combine_dx_kernel<true><<<blocks, 256, 0, s>>>(dx_perm, dest_row, d_topk_w, topk_w, topk_idx,
+                                                    w_router_t, T, H, k, dx);
+  else
+    combine_dx_kernel<false><<<blocks, 256, 0, s>>>(dx_perm, dest_row, d_topk_w, topk_w, topk_idx,
+                                                     w_router_t, T, H, k, dx);
   return hipGetLastError();
 }
 

@@ -123,6 +123,9 @@ hipError_t launch_combine(const void* y_perm, const float* topk_w, const int32_t
 hipError_t launch_combine_bwd(const void* dy, const void* y_perm, const float* topk_w,
                               const int32_t* dest_row, int T, int H, int k, bool bf16,
                               void* dy_perm, float* d_topk_w, hipStream_t s);
+hipError_t launch_combine_dx(const void* dx_perm, const int32_t* dest_row, const float* d_topk_w,
+                             const float* topk_w, const int32_t* topk_idx, const void* w_router_t,
+                             int T, int H, int k, bool bf16, void* dx, hipStream_t s);
 hipError_t launch_route_bwd_dz(const float* d_topk_w, const float* topk_w,
                                const int32_t* topk_idx, const void* w_router_t, int T, int H, int E,
                                int k, bool bf16, float* d_logits, float* dx_router,

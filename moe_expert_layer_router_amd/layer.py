@@ -14,8 +14,8 @@ from typing import Dict, Optional
 
 import torch
 
-from . import (MOE_BF16, MOE_F32, MOE_OP_FFN_BWD, MOE_OP_FFN_FWD, MOE_OP_PERMUTE, MOE_OP_ROUTE,
-               MOE_OP_ROUTE_BWD, _check, _stream, lib, workspace_bytes)
+from . import (MOE_BF16, MOE_F32, MOE_OP_COMBINE_DX, MOE_OP_FFN_BWD, MOE_OP_FFN_FWD, MOE_OP_PERMUTE,
+               MOE_OP_ROUTE, MOE_OP_ROUTE_BWD, _check, _stream, lib, workspace_bytes)
 
 
 def _p(t: Optional[torch.Tensor]):
@@ -51,7 +51,6 @@ class MoELayer:
             b["dy_perm"] = torch.empty((R, H), dtype=dtype, device=dev)
             b["d_topk_w"] = torch.empty((T, k), dtype=f32, device=dev)
             b["d_logits"] = torch.empty((T, E), dtype=f32, device=dev)
-            b["dx_router"] = torch.empty((T, H), dtype=f32, device=dev)
             b["dw_router"] = torch.empty((H, E), dtype=f32, device=dev)
             b["dx_perm"] = torch.empty((R, H), dtype=dtype, device=dev)
             b["dw_gate"] = torch.empty((E_l, I, H), dtype=f32, device=dev)
@@ -61,7 +60,7 @@ class MoELayer:
         self.buf = b
         ops = [MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN_FWD]
         if train:
-            ops += [MOE_OP_FFN_BWD, MOE_OP_ROUTE_BWD]
+            ops += [MOE_OP_FFN_BWD, MOE_OP_ROUTE_BWD, MOE_OP_COMBINE_DX]
         nb = max(workspace_bytes(op, T, H, I, E, k, e_lo, e_hi, self.dt) for op in ops)
         # one workspace serves every call: the calls run one after another on one stream
         self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
@@ -96,13 +95,15 @@ class MoELayer:
                "moe_combine_bwd")
         _check(lib.moe_route_bwd(_p(b["d_topk_w"]), _p(b["topk_w"]), _p(b["topk_idx"]), _p(x),
                                  _p(w_router), T, H, E, k, self.dt, _p(b["d_logits"]),
-                                 _p(b["dx_router"]), _p(b["dw_router"]), ws, wsb, s), "moe_route_bwd")
+                                 None, _p(b["dw_router"]), ws, wsb, s), "moe_route_bwd")
         _check(lib.moe_grouped_ffn_bwd(_p(b["dy_perm"]), _p(b["x_perm"]), _p(b["gu"]), _p(b["h_perm"]),
                                        _p(b["offsets"]), self.E_l, self.R_cap, H, I, _p(w_gate),
                                        _p(w_up), _p(w_down), self.dt, _p(b["dx_perm"]),
                                        _p(b["dw_gate"]), _p(b["dw_up"]), _p(b["dw_down"]), 0, ws,
                                        wsb, s), "moe_grouped_ffn_bwd")
-        _check(lib.moe_combine(_p(b["dx_perm"]), None, _p(b["dest_row"]), _p(b["dx_router"]), T, H, k,
-                               self.dt, _p(b["dx"]), s), "moe_combine")
+        # input gradient: the experts' part and the router's part in one pass
+        _check(lib.moe_combine_dx(_p(b["dx_perm"]), _p(b["dest_row"]), _p(b["d_topk_w"]),
+                                  _p(b["topk_w"]), _p(b["topk_idx"]), _p(w_router), T, H, E, k,
+                                  self.dt, _p(b["dx"]), ws, wsb, s), "moe_combine_dx")
         return {n: b[n] for n in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "d_logits",
                                   "d_topk_w")}

@@ -172,3 +172,29 @@ def test_last_error_is_per_thread():
     th.start()
     th.join()
     assert seen == [""]
+
+
+def test_combine_dx_errors():
+    f = lambda *a: L.moe_combine_dx(*a)
+    big = 1 << 30
+    args = [A, A, A, A, A, A, 64, 128, 8, 2, BF16, A, A, big, S]
+    bad = list(args); bad[9] = 9        # k > E
+    assert f(*bad) == EINVAL
+    bad = list(args); bad[0] = N        # dx_perm
+    assert f(*bad) == EINVAL and "dx_perm" in _err()
+    bad = list(args); bad[13] = 16      # workspace too small
+    assert f(*bad) == EWS
+    bad = list(args); bad[6] = 0        # T = 0: nothing to do
+    assert f(*bad) == OK
+
+
+def test_layer_buffers_and_workspace_on_host():
+    """The layer's set-up (buffers, one workspace for every call) needs no GPU."""
+    import torch
+    import moe_expert_layer_router_amd as moe
+    for train in (False, True):
+        layer = moe.MoELayer(64, 128, 64, 8, 2, 0, 8, torch.bfloat16, device="cpu", train=train)
+        need = max(moe.workspace_bytes(op, 64, 128, 64, 8, 2, 0, 8, moe.MOE_BF16)
+                   for op in range(6 if train else 3))
+        assert layer.ws_bytes >= need
+        assert ("dx" in layer.buf) == train

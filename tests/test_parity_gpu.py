@@ -389,6 +389,33 @@ def test_backward_matches_oracle(w):
     assert (g["d_topk_w"].cpu().numpy()[nonlocal_] == 0).all()
 
 
+@pytest.mark.parametrize("w", [TINY.scaled(name="tiny_fp32_train", train=True),
+                               TRAIN.scaled(name="ragged_bf16_train_t1000_h192_i128_e24_k3", T=1000,
+                                            H=192, I=128, E=24, k=3, e_lo=5, e_hi=21)],
+                         ids=lambda w: w.name)
+def test_combine_dx_equals_unfused(w):
+    """moe_combine_dx == moe_combine(dx_perm, addend = dx_router of moe_route_bwd), up to
+    the one rounding of the output (the fp32 sums run in a different order)."""
+    inp = _inputs(w)
+    t = _gpu_tensors(w, inp)
+    layer, _, g = run_layer(w, t)
+    b = layer.buf
+    rb = moe.moe_route_bwd(b["d_topk_w"], b["topk_w"], b["topk_idx"], t["x"], t["w_router"],
+                           want_dx=True, want_dw=False)
+    unfused = moe.moe_combine(b["dx_perm"], None, b["dest_row"], w.T, addend=rb["dx_router"])
+    fused = moe.moe_combine_dx(b["dx_perm"], b["dest_row"], b["d_topk_w"], b["topk_w"], b["topk_idx"],
+                               t["w_router"])
+    torch.cuda.synchronize()
+    a, r = fused.float(), unfused.float()
+    ulp = 2.0 ** -7 if w.dtype == "bf16" else 2.0 ** -20
+    bad = (a - r).abs() > ulp * r.abs() + 1e-6
+    print(f"  {w.name}: max |fused - unfused| = {(a - r).abs().max().item():.3g}, "
+          f"{int(bad.sum())} elements beyond one rounding", flush=True)
+    assert not bad.any()
+    assert torch.equal(fused.view(torch.int16) if w.dtype == "bf16" else fused,
+                       g["dx"].view(torch.int16) if w.dtype == "bf16" else g["dx"])
+
+
 def test_weight_grad_accumulate():
     w = TRAIN.scaled(name="acc", T=512, H=256, I=128, E=16, k=4, e_lo=0, e_hi=8)
     inp = _inputs(w)
