@@ -453,6 +453,21 @@ __device__ __forceinline__ void load8(const float* st, int r, int c, float* v) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// Output descriptors of the M-grouped products cover exactly the tile's rows
+// [row0, row1) of a buffer: the hardware range check drops stores of rows past
+// the tile (and any offset at or past kOutKill), so the stores are issued
+// unconditionally and the compiler counts them exactly (no branch-forced
+// drains of the memory counter).  A null buffer gets an empty range.
+typedef __amdgpu_buffer_rsrc_t out_rsrc_t;
+constexpr uint32_t kOutKill = 0x80000000u;
+__device__ __forceinline__ out_rsrc_t out_rsrc(const bf16_t* base, long row0, long row1, long ld) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base) + (base ? row0 * ld : 0), 0,
+                                           base ? (int)((row1 - row0) * ld * 2) : 0, 0x00020000);
+}
+__device__ __forceinline__ void store16(out_rsrc_t r, uint32_t off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, r, off, 0, 0);
+}
+
 template <int KIND, class C>
 __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc)[C::MI][NI], int e,
                                          int nt, int n0, int m0, int row0, int row1, int wave,
@@ -460,44 +475,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
   constexpr int MI = C::MI, WM = C::WM;
   const int wm = wave >> 1, wn = wave & 1;
   float* st = stage_area(wave);
+  if constexpr (KIND == K_WGRAD) {
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
-    // DOWN_DGRAD reads the saved g / u of its rows: all loads of the pass are
-    // issued before the staging, so they cost one round trip per pass.
-    u32x4_t graw[8], uraw[8];
-    if constexpr (KIND == K_DOWN_DGRAD) {
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const long row = row0 + wm * WM + mi * 32 + it * 4 + (lane >> 4);
-        const int n = n0 + wn * WN + (lane & 15) * 8;
-        const bool ok = row < row1 && n < p.N;
-        graw[it] = ok ? *reinterpret_cast<const u32x4_t*>(p.gu + row * 2 * p.I + n) : u32x4_t{};
-        uraw[it] = ok ? *reinterpret_cast<const u32x4_t*>(p.gu + row * 2 * p.I + p.I + n) : u32x4_t{};
-      }
-    }
-    stage_part(st, acc, mi, lane);
-    if constexpr (KIND == K_GATEUP_FWD) {
-      // staged columns: [g 32 | u 32 | g 32 | u 32] for h columns nt*128 + wn*64 + 0..63
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int r = it * 8 + (lane >> 3);
-        const int hc = (lane & 7) * 8;           // 0..56: h column within the wave
-        const int sc = (hc >> 5) * 64 + (hc & 31);  // staged gate column
-        const long row = row0 + wm * WM + mi * 32 + r;
-        const int col = nt * 128 + wn * 64 + hc;
-        if (row >= row1 || col >= p.I) continue;
-        float g[8], u[8], h[8];
-        load8(st, r, sc, g);
-        load8(st, r, sc + 32, u);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) h[j] = g[j] * fast_rcp(1.f + __expf(-g[j])) * u[j];
-        *reinterpret_cast<uint4*>(p.c0 + row * p.ldc + col) = pack8(h);
-        if (p.c1 != nullptr) {
-          *reinterpret_cast<uint4*>(p.c1 + row * 2 * p.I + col) = pack8(g);
-          *reinterpret_cast<uint4*>(p.c1 + row * 2 * p.I + p.I + col) = pack8(u);
-        }
-      }
-    } else if constexpr (KIND == K_WGRAD) {
+    for (int mi = 0; mi < MI; ++mi) {
+      stage_part(st, acc, mi, lane);
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
         const int r = it * 4 + (lane >> 4);
@@ -519,25 +500,83 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
           d4[1] = make_float4(v[4], v[5], v[6], v[7]);
         }
       }
-    } else {  // DOWN_FWD, GATEUP_DGRAD, DOWN_DGRAD: rows of the grouped buffer
+      // the next quarter reuses the staging area
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+  } else if constexpr (KIND == K_GATEUP_FWD) {
+    // staged columns: [g 32 | u 32 | g 32 | u 32] for h columns nt*128 + wn*64 + 0..63
+    const out_rsrc_t rh = out_rsrc(p.c0, row0, row1, p.ldc);
+    const out_rsrc_t rgu = out_rsrc(p.c1, row0, row1, 2L * p.I);
+    const int hc = (lane & 7) * 8;              // 0..56: h column within the wave
+    const int sc = (hc >> 5) * 64 + (hc & 31);  // staged gate column
+    const int col = nt * 128 + wn * 64 + hc;
+    const bool col_ok = col < p.I;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      stage_part(st, acc, mi, lane);
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int r = it * 8 + (lane >> 3);
+        const int lrow = wm * WM + mi * 32 + r;  // row within the tile
+        float g[8], u[8], h[8];
+        load8(st, r, sc, g);
+        load8(st, r, sc + 32, u);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) h[j] = g[j] * fast_rcp(1.f + __expf(-g[j])) * u[j];
+        const uint32_t oh = col_ok ? (uint32_t)((lrow * p.ldc + col) * 2) : kOutKill;
+        const uint32_t og = col_ok ? (uint32_t)((lrow * 2 * p.I + col) * 2) : kOutKill;
+        store16(rh, oh, pack8(h));
+        store16(rgu, og, pack8(g));
+        store16(rgu, og + (col_ok ? p.I * 2 : 0), pack8(u));
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+  } else {  // DOWN_FWD, GATEUP_DGRAD, DOWN_DGRAD: rows of the grouped buffer
+    const int c = (lane & 15) * 8;
+    const int n = n0 + wn * WN + c;
+    const bool col_ok = n < p.N;
+    const long ldo = (KIND == K_DOWN_DGRAD) ? 2L * p.I : p.ldc;
+    const out_rsrc_t ro = out_rsrc(p.c0, row0, row1, ldo);
+    // DOWN_DGRAD reads the saved g / u of its rows through the same kind of
+    // descriptor (rows past the tile read as zero).  The loads of pass mi + 1
+    // are issued before pass mi's math and stores, so their latency hides
+    // behind a whole pass.
+    out_rsrc_t rg;
+    u32x4_t graw[2][8], uraw[2][8];
+    if constexpr (KIND == K_DOWN_DGRAD) rg = out_rsrc(p.gu, row0, row1, 2L * p.I);
+    auto load_gu = [&](int mi, int b) {
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int lrow = wm * WM + mi * 32 + it * 4 + (lane >> 4);
+        const uint32_t o = col_ok ? (uint32_t)((lrow * 2 * p.I + n) * 2) : kOutKill;
+        graw[b][it] = __builtin_amdgcn_raw_buffer_load_b128(rg, o, 0, 0);
+        uraw[b][it] = __builtin_amdgcn_raw_buffer_load_b128(rg, o + (col_ok ? p.I * 2 : 0), 0, 0);
+      }
+    };
+    if constexpr (KIND == K_DOWN_DGRAD) load_gu(0, 0);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      if constexpr (KIND == K_DOWN_DGRAD)
+        if (mi + 1 < MI) load_gu(mi + 1, (mi + 1) & 1);
+      stage_part(st, acc, mi, lane);
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
         const int r = it * 4 + (lane >> 4);
-        const int c = (lane & 15) * 8;
-        const long row = row0 + wm * WM + mi * 32 + r;
-        const int n = n0 + wn * WN + c;
-        if (row >= row1 || n >= p.N) continue;
+        const int lrow = wm * WM + mi * 32 + r;
         float v[8];
         load8(st, r, c, v);
+        const uint32_t o = col_ok ? (uint32_t)((lrow * ldo + n) * 2) : kOutKill;
         if constexpr (KIND == K_DOWN_DGRAD) {
           // v = dh; dG = dh * u * s * (1 + g (1 - s)), dU = dh * SiLU(g), s = sigmoid(g)
           float g[8], u[8], dg[8], du[8];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            g[2 * q] = __uint_as_float(graw[it][q] << 16);
-            g[2 * q + 1] = __uint_as_float(graw[it][q] & 0xffff0000u);
-            u[2 * q] = __uint_as_float(uraw[it][q] << 16);
-            u[2 * q + 1] = __uint_as_float(uraw[it][q] & 0xffff0000u);
+            const u32x4_t& gw = graw[mi & 1][it];
+            const u32x4_t& uw = uraw[mi & 1][it];
+            g[2 * q] = __uint_as_float(gw[q] << 16);
+            g[2 * q + 1] = __uint_as_float(gw[q] & 0xffff0000u);
+            u[2 * q] = __uint_as_float(uw[q] << 16);
+            u[2 * q + 1] = __uint_as_float(uw[q] & 0xffff0000u);
           }
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
@@ -545,15 +584,15 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
             dg[j] = v[j] * u[j] * sg * (1.f + g[j] * (1.f - sg));
             du[j] = v[j] * g[j] * sg;
           }
-          *reinterpret_cast<uint4*>(p.c0 + row * 2 * p.I + n) = pack8(dg);
-          *reinterpret_cast<uint4*>(p.c0 + row * 2 * p.I + p.I + n) = pack8(du);
+          store16(ro, o, pack8(dg));
+          store16(ro, o + (col_ok ? p.I * 2 : 0), pack8(du));
         } else {
-          *reinterpret_cast<uint4*>(p.c0 + row * p.ldc + n) = pack8(v);
+          store16(ro, o, pack8(v));
         }
       }
+      // the next quarter reuses the staging area
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
-    // the next quarter reuses the staging area
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
 }
 
