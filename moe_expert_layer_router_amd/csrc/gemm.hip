@@ -37,7 +37,7 @@
 //   XOR-swizzled by row and read as MFMA fragments with ds_read_b128.
 //   MN-contiguous operands ("MC": weights in the data gradients, both operands
 //   of the weight gradients) are stored untransposed (rows = k) with 16-byte
-//   chunks XOR-swizzled by 2 * (k & 3), and each MFMA fragment is assembled
+//   chunks XOR-swizzled by 4 * (k & 3), and each MFMA fragment is assembled
 //   from two transposing reads (ds_read_b64_tr_b16): within each 16-lane
 //   group, lane i points at row kb + i/4, column c0 + 4 * (i % 4), and lane l
 //   receives the four consecutive-k values of column c0 + l.
@@ -131,7 +131,7 @@ __device__ __forceinline__ int kc_swz(int r) { return (r >> 2) & 3; }
 // first element of logical 16-byte chunk `chunk` of row r
 __device__ __forceinline__ int kc_idx(int r, int chunk) { return r * BK + ((chunk ^ kc_swz(r)) << 3); }
 // MC tile [BK][W]: LDS position of logical 16-byte chunk c of row k (and back).
-__device__ __forceinline__ int mc_chunk(int k, int c) { return c ^ ((k & 3) << 1); }
+__device__ __forceinline__ int mc_chunk(int k, int c) { return c ^ ((k & 3) << 2); }
 
 // ---------------------------------------------------------------------------
 // buffer -> LDS DMA and explicit synchronisation
@@ -270,40 +270,42 @@ __device__ __forceinline__ lds_char_t* lds_ptr(uint32_t byte) {
 //   chunk 2 s + l / 32; the block's first row (a multiple of 16) does not
 //   change the swizzle, so kc[s] is the offset for block row 0.
 //   MC (transposing reads, width W): with g = l / 16, i = l % 16 the lane reads
-//   k = 16 s + 8 (g / 2) + i / 4 and column c0 + 16 (g % 2) + 4 (i % 4) of the
-//   32-column block c0 = cb + 32 mi (cb a multiple of 128).  The chunk swizzle
-//   XORs bits 1..2 of the chunk index 4 mi + x, which moves the read by +-4
-//   chunks depending on the parity of mi: mc[p] is the offset for parity p
-//   (biased by +32 elements for odd mi so that it is never negative).
+//   k = 16 s + 8 (g / 2) + i / 4 and column 32 M + 16 (g % 2) + 4 (i % 4) of the
+//   slot row, M the absolute 32-column block (wave base plus fragment index),
+//   i.e. logical chunk 4 M + x, x = 2 (g % 2) + (i % 4) / 2, which sits at
+//   chunk 4 (M ^ (k % 4)) + x.  The four k rows one half-wave reads (k % 4 =
+//   0..3) thus fall in four different 64-byte quarters of the 256-byte bank
+//   line: the 32 lanes cover all 64 banks once.  mc[j] is the whole offset of
+//   fragment j (wave base included; the k sub-step is added per read).
 struct FragLanes {
   uint32_t kc[KSUB];
-  uint32_t mc_a[2];
-  uint32_t mc_b[2];
+  uint32_t mc_a[4];
+  uint32_t mc_b[NI];
 };
-// (the MC derivation needs the wave's first column cb to be a multiple of 64,
-// which holds for both wave heights)
 
-template <int W>
-__device__ __forceinline__ void mc_lane_offsets(int lane, uint32_t (&mc)[2]) {
+template <int W, int N>
+__device__ __forceinline__ void mc_lane_offsets(int lane, int mb, uint32_t (&mc)[N], int n) {
   const int g = lane >> 4, i = lane & 15;
   const int x = 2 * (g & 1) + ((i & 3) >> 1);
-  const int y = ((i >> 2) & 3) << 1;
-  const int z = x ^ y;
-  const int d0 = z, d1 = (z & 3) - 4 * (z >> 2);
+  const int r = (i >> 2) & 3;
   const int rowpart = (8 * (g >> 1) + (i >> 2)) * W + 4 * (i & 1);
-  mc[0] = (uint32_t)(2 * (rowpart + 8 * d0));
-  mc[1] = (uint32_t)(2 * (rowpart + 8 * d1 + 32));
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const int M = mb + j;
+    const int c = 4 * ((M & ~3) | ((M & 3) ^ r)) + x;
+    mc[j] = j < n ? (uint32_t)(2 * (rowpart + 8 * c)) : 0u;
+  }
 }
 
 template <class C>
-__device__ __forceinline__ FragLanes frag_lanes(int lane) {
+__device__ __forceinline__ FragLanes frag_lanes(int lane, int wave) {
   FragLanes L;
   const int r = lane & 31;
 #pragma unroll
   for (int s = 0; s < KSUB; ++s)
     L.kc[s] = (uint32_t)(r * BK * 2 + (((2 * s + (lane >> 5)) ^ kc_swz(r)) << 4));
-  mc_lane_offsets<C::BM>(lane, L.mc_a);
-  mc_lane_offsets<BN>(lane, L.mc_b);
+  mc_lane_offsets<C::BM>(lane, (wave >> 1) * (C::WM / 32), L.mc_a, C::MI);
+  mc_lane_offsets<BN>(lane, (wave & 1) * (WN / 32), L.mc_b, NI);
   return L;
 }
 
@@ -350,13 +352,13 @@ __device__ __forceinline__ void load_frag(Frags<C>& f, int j, int s, uint32_t sa
     if constexpr (Tr::A_KC)
       f.a[mi] = frag_kc(sa, L.kc[s], mi * 32 * BK * 2);
     else
-      f.a[mi] = frag_mc<BM>(sa, L.mc_a[mi & 1], 2 * (32 * (mi & ~1) + 16 * s * BM));
+      f.a[mi] = frag_mc<BM>(sa, L.mc_a[mi], 2 * (16 * s * BM));
   } else {
     const int ni = q - MI;
     if constexpr (Tr::B_KC)
       f.b[ni] = frag_kc(sb, L.kc[s], ni * 32 * BK * 2);
     else
-      f.b[ni] = frag_mc<BN>(sb, L.mc_b[ni & 1], 2 * (32 * (ni & ~1) + 16 * s * BN));
+      f.b[ni] = frag_mc<BN>(sb, L.mc_b[ni], 2 * (16 * s * BN));
   }
 }
 
@@ -538,11 +540,13 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
     const long ldo = (KIND == K_DOWN_DGRAD) ? 2L * p.I : p.ldc;
     const out_rsrc_t ro = out_rsrc(p.c0, row0, row1, ldo);
     // DOWN_DGRAD reads the saved g / u of its rows through the same kind of
-    // descriptor (rows past the tile read as zero).  The loads of pass mi + 1
-    // are issued before pass mi's math and stores, so their latency hides
-    // behind a whole pass.
+    // descriptor (rows past the tile read as zero).  With 256-row tiles the
+    // loads of pass mi + 1 are issued before pass mi's math and stores, so
+    // their latency hides behind a whole pass; 128-row tiles (half the
+    // registers per wave) load each pass's own at its start.
+    constexpr int NBUF = C::BM == 256 ? 2 : 1;
     out_rsrc_t rg;
-    u32x4_t graw[2][8], uraw[2][8];
+    u32x4_t graw[NBUF][8], uraw[NBUF][8];
     if constexpr (KIND == K_DOWN_DGRAD) rg = out_rsrc(p.gu, row0, row1, 2L * p.I);
     auto load_gu = [&](int mi, int b) {
 #pragma unroll
@@ -553,11 +557,16 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
         uraw[b][it] = __builtin_amdgcn_raw_buffer_load_b128(rg, o + (col_ok ? p.I * 2 : 0), 0, 0);
       }
     };
-    if constexpr (KIND == K_DOWN_DGRAD) load_gu(0, 0);
+    if constexpr (KIND == K_DOWN_DGRAD && NBUF == 2) load_gu(0, 0);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
-      if constexpr (KIND == K_DOWN_DGRAD)
-        if (mi + 1 < MI) load_gu(mi + 1, (mi + 1) & 1);
+      if constexpr (KIND == K_DOWN_DGRAD) {
+        if constexpr (NBUF == 2) {
+          if (mi + 1 < MI) load_gu(mi + 1, (mi + 1) & 1);
+        } else {
+          load_gu(mi, 0);
+        }
+      }
       stage_part(st, acc, mi, lane);
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
@@ -571,8 +580,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
           float g[8], u[8], dg[8], du[8];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const u32x4_t& gw = graw[mi & 1][it];
-            const u32x4_t& uw = uraw[mi & 1][it];
+            const u32x4_t& gw = graw[mi % NBUF][it];
+            const u32x4_t& uw = uraw[mi % NBUF][it];
             g[2 * q] = __uint_as_float(gw[q] << 16);
             g[2 * q + 1] = __uint_as_float(gw[q] & 0xffff0000u);
             u[2 * q] = __uint_as_float(uw[q] << 16);
@@ -612,7 +621,7 @@ void gemm_kernel(const GemmArgs p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const FragLanes L = frag_lanes<C>(lane);
+  const FragLanes L = frag_lanes<C>(lane, wave);
 
   int total;
   if constexpr (KIND == K_WGRAD)
@@ -738,8 +747,9 @@ void gemm_kernel(const GemmArgs p) {
       const uint32_t dma_a = lds_addr(g_lds) + wave * NIA * 1024;  // this wave's DMA area
       const uint32_t dma_b = lds_addr(g_lds) + kOffB + wave * NIB * 1024;
       // wave block bases inside a slot
-      const uint32_t wa = Tr::A_KC ? (uint32_t)(wm * WM * BK * 2) : (uint32_t)(wm * WM * 2);
-      const uint32_t wb = Tr::B_KC ? (uint32_t)(wn * WN * BK * 2) : (uint32_t)(wn * WN * 2);
+      // (MC fragment offsets hold the wave's columns themselves)
+      const uint32_t wa = Tr::A_KC ? (uint32_t)(wm * WM * BK * 2) : 0u;
+      const uint32_t wb = Tr::B_KC ? (uint32_t)(wn * WN * BK * 2) : 0u;
       // NST steps in flight (the ones past K dropped), then step 0's first fragments
 #pragma unroll
       for (int st = 0; st < NST; ++st)
