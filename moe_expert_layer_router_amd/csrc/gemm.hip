@@ -240,14 +240,6 @@ __device__ __forceinline__ void dma_piece(const GemmArgs& p, const Operand<C::NI
   }
 }
 
-template <int KIND, class C>
-__device__ __forceinline__ void issue_stage(const GemmArgs& p, const Operand<C::NIA>& opA,
-                                            const Operand<NIB>& opB, uint32_t la, uint32_t lb,
-                                            int k0, uint32_t kill) {
-#pragma unroll
-  for (int u = 0; u < C::NIA + NIB; ++u) dma_piece<KIND, C>(p, opA, opB, la, lb, k0, kill, u);
-}
-
 // ---------------------------------------------------------------------------
 // The LDS ring (dynamic LDS of Cfg::kLdsBytes): NST slots of A, then NST slots
 // of B.  Slots are addressed with a wave-uniform byte offset, so one per-lane
@@ -386,21 +378,38 @@ __device__ __forceinline__ void mma(f32x16_t (&acc)[C::MI][NI], const Frags<C>& 
 // pipe.  So the other work of a K step is spread between the MFMAs, one or
 // two instructions after each (the scheduling barriers keep this order), and
 // the K loop has no branches (a branch between MFMAs costs the matrix core
-// about 40% of its rate):
-//   sub-step 0: MFMA j, then fragment j of the next sub-step (j < MI + NI);
-//   sub-step 1: MFMA j, then DMA instruction j of step kt + NST (j < NIA + NIB)
-//               and fragment j - (MI NI - MI - NI) of the next step's
-//               sub-step 0 (the reads end with the last MFMA).
+// about 40% of its rate).  A step's DMA is issued in two halves, each spread
+// evenly over the MFMAs of one sub-step (every DSTR-th MFMA): four waves'
+// DMA instructions bunched together outrun the texture unit and stall the
+// issuing waves.
+//   sub-step 0: MFMA j, then fragment j of the next sub-step (j < MI + NI)
+//               and the second half of the DMA of step kt + NST - 1;
+//   sub-step 1: MFMA j, then the first half of the DMA of step kt + NST and
+//               fragment j - (MI NI - MI - NI) of the next step's sub-step 0
+//               (the reads end with the last MFMA).
+template <class C>
+struct DmaSplit {
+  static constexpr int ND = C::NIA + NIB;  // DMA instructions per wave per step
+  static constexpr int NH = ND / 2;        // per half
+  static constexpr int DSTR = C::MI * NI / NH;
+  static_assert(ND % 2 == 0 && DSTR >= 1, "DMA halves");
+};
+
 template <int KIND, class C>
 __device__ __forceinline__ void mma_read_next(f32x16_t (&acc)[C::MI][NI], const Frags<C>& cur,
                                               Frags<C>& nxt, int s_next, uint32_t sa, uint32_t sb,
-                                              const FragLanes& L) {
+                                              const FragLanes& L, const GemmArgs& p,
+                                              const Operand<C::NIA>& opA, const Operand<NIB>& opB,
+                                              uint32_t la, uint32_t lb, int k0, uint32_t kill) {
   constexpr int NM = C::MI * NI, NR = C::MI + NI;
+  using D = DmaSplit<C>;
   static_assert(NR <= NM, "interleave pattern");
 #pragma unroll
   for (int j = 0; j < NM; ++j) {
     mfma1(acc[j / NI][j % NI], cur.a[j / NI], cur.b[j % NI]);
     if (j < NR) load_frag<KIND, C>(nxt, j, s_next, sa, sb, L);
+    if (j % D::DSTR == 0 && j / D::DSTR < D::NH)
+      dma_piece<KIND, C>(p, opA, opB, la, lb, k0, kill, D::NH + j / D::DSTR);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -411,12 +420,14 @@ __device__ __forceinline__ void mma_dma_read(f32x16_t (&acc)[C::MI][NI], const F
                                              const FragLanes& L, const GemmArgs& p,
                                              const Operand<C::NIA>& opA, const Operand<NIB>& opB,
                                              uint32_t la, uint32_t lb, int k0, uint32_t kill) {
-  constexpr int NM = C::MI * NI, NR = C::MI + NI, ND = C::NIA + NIB;
-  static_assert(NR <= NM && ND <= NM, "interleave pattern");
+  constexpr int NM = C::MI * NI, NR = C::MI + NI;
+  using D = DmaSplit<C>;
+  static_assert(NR <= NM, "interleave pattern");
 #pragma unroll
   for (int j = 0; j < NM; ++j) {
     mfma1(acc[j / NI][j % NI], cur.a[j / NI], cur.b[j % NI]);
-    if (j < ND) dma_piece<KIND, C>(p, opA, opB, la, lb, k0, kill, j);
+    if (j % D::DSTR == 0 && j / D::DSTR < D::NH)
+      dma_piece<KIND, C>(p, opA, opB, la, lb, k0, kill, j / D::DSTR);
     if (j >= NM - NR) load_frag<KIND, C>(nxt, j - (NM - NR), 0, sa, sb, L);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -750,12 +761,17 @@ void gemm_kernel(const GemmArgs p) {
       // (MC fragment offsets hold the wave's columns themselves)
       const uint32_t wa = Tr::A_KC ? (uint32_t)(wm * WM * BK * 2) : 0u;
       const uint32_t wb = Tr::B_KC ? (uint32_t)(wn * WN * BK * 2) : 0u;
-      // NST steps in flight (the ones past K dropped), then step 0's first fragments
+      // Steps 0 .. NST - 2 and the first half of step NST - 1 in flight (the
+      // ones past K dropped); step 0 has landed when only the newer remain.
+      constexpr int ND = NIA + NIB;
 #pragma unroll
-      for (int st = 0; st < NST; ++st)
-        issue_stage<KIND, C>(p, opA, opB, dma_a + st * kSlotA, dma_b + st * kSlotB, st * BK,
-                             st < nk ? 0u : kDmaKill);
-      wait_vm<(NST - 1) * (NIA + NIB)>();
+      for (int st = 0; st < NST; ++st) {
+        const uint32_t kill = st < nk ? 0u : kDmaKill;
+#pragma unroll
+        for (int u = 0; u < (st < NST - 1 ? ND : ND / 2); ++u)
+          dma_piece<KIND, C>(p, opA, opB, dma_a + st * kSlotA, dma_b + st * kSlotB, st * BK, kill, u);
+      }
+      wait_vm<(NST - 2) * ND + ND / 2>();
       lds_barrier();
       // Two fragment sets, no copies between them: f0 holds sub-step 0 (read
       // at the end of the previous step), f1 sub-step 1.
@@ -764,14 +780,19 @@ void gemm_kernel(const GemmArgs p) {
       load_frags<KIND, C>(f0, 0, wa, kOffB + wb, L);
       int slot = 0;
       // One K step per iteration on ring slot `slot`, software pipelined: the
-      // fragments of sub-step 1 are read during the first MFMAs of sub-step 0.
-      // Before the MFMAs of sub-step 1 the wave waits for step kt + 1 to land
-      // (barrier); between those MFMAs it starts the DMA of step kt + NST into
-      // this slot (every wave has finished reading it) and reads the next
-      // step's sub-step 0 fragments.
+      // fragments of sub-step 1 are read during the first MFMAs of sub-step 0,
+      // together with the second half of the DMA of step kt + NST - 1 into the
+      // previous slot (every wave finished reading it before the previous
+      // barrier).  Before the MFMAs of sub-step 1 the wave waits for step
+      // kt + 1 to land (barrier); between those MFMAs it starts the first half
+      // of the DMA of step kt + NST into this slot (every wave has finished
+      // reading it) and reads the next step's sub-step 0 fragments.
       for (int kt = 0; kt < nk; ++kt) {
         const uint32_t sa = slot * kSlotA + wa, sb = kOffB + slot * kSlotB + wb;
-        mma_read_next<KIND, C>(acc, f0, f1, 1, sa, sb, L);
+        const int pslot = slot == 0 ? NST - 1 : slot - 1;
+        mma_read_next<KIND, C>(acc, f0, f1, 1, sa, sb, L, p, opA, opB, dma_a + pslot * kSlotA,
+                               dma_b + pslot * kSlotB, (kt + NST - 1) * BK,
+                               kt + NST - 1 < nk ? 0u : kDmaKill);
         const int nslot = slot + 1 == NST ? 0 : slot + 1;
         // Steps kt + 1 .. kt + NST - 1 are in flight; step kt + 1 has landed
         // when only the newer ones (NIA + NIB loads each) remain.
