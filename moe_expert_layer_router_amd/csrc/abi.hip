@@ -81,10 +81,12 @@ int check_ws(const void* ws, size_t have, size_t need, const char* fn) {
 // Split of the token (K) dimension of dW_r = x^T dz: about 128 (tile, split)
 // work items, each split at least 256 tokens, at most 16 splits (every split
 // writes an H x 2E fp32 partial that a second pass sums).
+// K splits of the router weight gradient x^T . dz: enough workgroups for one
+// per CU, each split at least 256 token rows.
 int route_bwd_splits(int T, int H, int E) {
   const int tiles = gemm_tiles(H, 2 * E);
-  const int want = (128 + tiles - 1) / tiles;
-  return std::max(1, std::min(std::min(16, want), (T + 255) / 256));
+  const int want = (kCUs + tiles - 1) / tiles;
+  return std::max(1, std::min(std::min(32, want), (T + 255) / 256));
 }
 
 size_t ws_route(int H, int E, int dtype) {
@@ -101,7 +103,8 @@ size_t ws_route_bwd(int T, int H, int E, int dtype) {
   const size_t wt = align256((size_t)E * H * elem_bytes(dtype));
   if (dtype != MOE_BF16) return wt;
   return wt + align256((size_t)T * 2 * E * 2) +
-         align256((size_t)route_bwd_splits(T, H, E) * H * 2 * E * sizeof(float));
+         align256((size_t)route_bwd_splits(T, H, E) * H * (dw_router_folds(E) ? 1 : 2) * E *
+                  sizeof(float));
 }
 
 int check_ffn_shape(int E_l, int R_cap, int H, int I, int dtype, const char* fn) {
@@ -431,9 +434,10 @@ int moe_route_bwd(const float* d_topk_w, const float* topk_w, const int32_t* top
     if (bf16) {
       if (T > 0) {
         e = launch_dw_router_bf16((const bf16_t*)x, dz_hilo, T, H, E, nsplit, nullptr, partials, s);
-        if (e == hipSuccess) e = launch_dw_router_reduce(partials, nsplit, H, E, dw_router, s);
+        if (e == hipSuccess)
+          e = launch_dw_router_reduce(partials, nsplit, H, E, dw_router_folds(E), dw_router, s);
       } else {
-        e = launch_dw_router_reduce(partials, 0, H, E, dw_router, s);  // writes zeros
+        e = launch_dw_router_reduce(partials, 0, H, E, false, dw_router, s);  // writes zeros
       }
     } else {
       e = launch_dw_router_f32((const float*)x, d_logits, T, H, E, dw_router, s);

@@ -338,18 +338,25 @@ __global__ __launch_bounds__(256) void dw_router_f32_kernel(const float* __restr
   dw[i] = acc;
 }
 
-// dw_router[h, e] = sum over splits s (ascending) of P[s][h][e] + P[s][h][E + e].
+// dw_router[h, e] = sum over splits s (ascending) of P[s][h][e] (folded
+// partials [nsplit, H, E], hi + lo added by the product) or of
+// P[s][h][e] + P[s][h][E + e] ([nsplit, H, 2E]).
 __global__ __launch_bounds__(256) void dw_router_reduce_kernel(const float* __restrict__ part,
                                                                int nsplit, int H, int E,
+                                                               int folded,
                                                                float* __restrict__ dw) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= H * E) return;
-  const int h = i / E, e = i % E;
   float acc = 0.f;
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const float* p = part + ((size_t)sp * H + h) * 2 * E;
-    acc += p[e];
-    acc += p[E + e];
+  if (folded) {
+    for (int sp = 0; sp < nsplit; ++sp) acc += part[(size_t)sp * H * E + i];
+  } else {
+    const int h = i / E, e = i % E;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float* p = part + ((size_t)sp * H + h) * 2 * E;
+      acc += p[e];
+      acc += p[E + e];
+    }
   }
   dw[i] = acc;
 }
@@ -415,10 +422,10 @@ hipError_t launch_dw_router_f32(const float* x, const float* d_logits, int T, in
   return hipGetLastError();
 }
 
-hipError_t launch_dw_router_reduce(const float* partials, int nsplit, int H, int E,
+hipError_t launch_dw_router_reduce(const float* partials, int nsplit, int H, int E, bool folded,
                                    float* dw_router, hipStream_t s) {
   dw_router_reduce_kernel<<<(H * E + 255) / 256, 256, 0, s>>>(partials, nsplit, H, E,
-                                                               dw_router);
+                                                               folded ? 1 : 0, dw_router);
   return hipGetLastError();
 }
 

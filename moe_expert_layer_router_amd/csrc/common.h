@@ -20,6 +20,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kMaxE = 256;
 constexpr int kMaxK = 32;
+constexpr int kCUs = 256;  // compute units of one MI355X
 
 // ---------------------------------------------------------------------------
 // bf16 <-> fp32
@@ -132,11 +133,14 @@ hipError_t launch_route_bwd_dz(const float* d_topk_w, const float* topk_w,
                                bf16_t* dz_hilo, hipStream_t s);
 hipError_t launch_dw_router_f32(const float* x, const float* d_logits, int T, int H, int E,
                                 float* dw_router, hipStream_t s);
-hipError_t launch_dw_router_reduce(const float* partials, int nsplit, int H, int E,
+hipError_t launch_dw_router_reduce(const float* partials, int nsplit, int H, int E, bool folded,
                                    float* dw_router, hipStream_t s);
 
 // gemm.hip (bf16 MFMA grouped GEMMs)
 int gemm_tiles(int M, int N);  // output tiles of one M x N product
+// Whether the router weight gradient's split products add their hi and lo
+// halves before storing ([nsplit, H, E] partials instead of [nsplit, H, 2E]).
+bool dw_router_folds(int E);
 size_t ffn_sched_bytes(int R_cap, int E_l);
 hipError_t launch_ffn_fwd_bf16(const bf16_t* x_perm, const int32_t* offsets, int E_l, int R_cap,
                                int H, int I, const bf16_t* w_gate, const bf16_t* w_up,

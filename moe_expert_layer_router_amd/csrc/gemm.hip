@@ -51,7 +51,6 @@ constexpr int BN = 256, BK = 32, NTH = 256;
 constexpr int WN = 128;                  // wave sub-tile width
 constexpr int NI = WN / 32;              // MFMA blocks per wave along N
 constexpr int KSUB = BK / 16;            // k16 sub-steps per K step
-constexpr int kCUs = 256;
 constexpr int kStageB = BN * BK;         // bf16 elements per B stage
 constexpr int NIB = kStageB * 2 / 1024 / 4;  // DMA instructions (1 KB each) per wave per stage, B
 constexpr int KCH = BK / 8;              // 16-byte chunks per KC row
@@ -106,6 +105,7 @@ struct GemmArgs {
   int m_split;
   long f_group_stride;
   int accumulate;
+  int fold;                 // WGRAD: F > 0 stores column c + column F + c (c < F), 0 = plain
 };
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -489,6 +489,34 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
   const int wm = wave >> 1, wn = wave & 1;
   float* st = stage_area(wave);
   if constexpr (KIND == K_WGRAD) {
+    if (p.fold > 0) {  // uniform: the whole workgroup takes this path
+      // Output column c (< F) is the sum of tile columns c and F + c, which
+      // may belong to the other wave of the row pair: all four waves stage a
+      // block, then every thread adds pairs of 8 columns.
+      const int F = p.fold;
+      const int tasks = 2 * 32 * (F / 8);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        stage_part(st, acc, mi, lane);
+        __syncthreads();
+        for (int q = threadIdx.x; q < tasks; q += NTH) {
+          const int c = (q % (F / 8)) * 8;
+          const int r = (q / (F / 8)) % 32;
+          const int pw = q / (F / 8) / 32;  // wave row of the pair
+          const int m = m0 + pw * WM + mi * 32 + r;
+          if (m >= p.M) continue;
+          float lo[8], hi[8];
+          load8(stage_area(pw * 2 + c / WN), r, c % WN, lo);
+          load8(stage_area(pw * 2 + (F + c) / WN), r, (F + c) % WN, hi);
+          float* dst = p.f0 + e * p.f_group_stride + (long)m * p.ldc + c;
+          float4* d4 = reinterpret_cast<float4*>(dst);
+          d4[0] = make_float4(lo[0] + hi[0], lo[1] + hi[1], lo[2] + hi[2], lo[3] + hi[3]);
+          d4[1] = make_float4(lo[4] + hi[4], lo[5] + hi[5], lo[6] + hi[6], lo[7] + hi[7]);
+        }
+        __syncthreads();
+      }
+      return;
+    }
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
       stage_part(st, acc, mi, lane);
@@ -853,6 +881,8 @@ static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 int gemm_tiles(int M, int N) { return ((M + kBmWgrad - 1) / kBmWgrad) * ((N + BN - 1) / BN); }
 
+bool dw_router_folds(int E) { return E % 8 == 0 && 2 * E <= BN; }
+
 size_t ffn_sched_bytes(int R_cap, int E_l) {
   const size_t entries = (size_t)R_cap / kBmGrouped + E_l + 1;
   return align256((1 + 3 * entries) * sizeof(int32_t));
@@ -1019,8 +1049,10 @@ hipError_t launch_dw_router_bf16(const bf16_t* x, const bf16_t* dz_hilo, int T, 
   w.n_ntiles = (2 * E + BN - 1) / BN;
   w.f0 = partials;
   w.m_split = H;
-  w.ldc = 2 * E;
-  w.f_group_stride = (long)H * 2 * E;
+  const int F = dw_router_folds(E) ? E : 0;  // one N tile: hi in columns 0..E-1, lo in E..2E-1
+  w.fold = F;
+  w.ldc = F > 0 ? E : 2 * E;
+  w.f_group_stride = (long)H * w.ldc;
   w.accumulate = 0;
   return launch_gemm<K_WGRAD, kBmWgrad>(w, nsplit * w.n_mtiles * w.n_ntiles, MOE_KERNEL_ROUTE_BWD_DW, s);
 }
