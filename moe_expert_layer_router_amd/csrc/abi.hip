@@ -89,8 +89,8 @@ int route_bwd_splits(int T, int H, int E) {
   return std::max(1, std::min(std::min(32, want), (T + 255) / 256));
 }
 
-size_t ws_route(int H, int E, int dtype) {
-  return dtype == MOE_BF16 ? align256(route_ws_bytes(H, E)) : 0;
+size_t ws_route(int T, int H, int E, int dtype) {
+  return dtype == MOE_BF16 ? align256(route_ws_bytes(T, H, E)) : 0;
 }
 size_t ws_ffn_fwd(int R_cap, int E_l, int dtype) {
   return dtype == MOE_BF16 ? ffn_sched_bytes(R_cap, E_l) : 0;
@@ -173,7 +173,7 @@ int64_t moe_workspace_bytes(int op, int T, int H, int I, int E, int k, int e_lo,
   const int R_cap = T * k;
   switch (op) {
     case MOE_OP_ROUTE:
-      return (int64_t)ws_route(H, E, dtype);
+      return (int64_t)ws_route(T, H, E, dtype);
     case MOE_OP_ROUTE_BWD:
       return (int64_t)ws_route_bwd(T, H, E, dtype);
     case MOE_OP_COMBINE_DX:
@@ -207,13 +207,13 @@ int moe_route(const void* x, const void* w_router, const float* bias, int T, int
   if (int rc = check_ptr(w_router, "w_router", fn, true)) return rc;
   if (int rc = check_ptr(topk_idx, "topk_idx", fn)) return rc;
   if (int rc = check_ptr(topk_w, "topk_w", fn)) return rc;
-  if (int rc = check_ws(ws, ws_bytes, ws_route(H, E, dtype), fn)) return rc;
+  if (int rc = check_ws(ws, ws_bytes, ws_route(T, H, E, dtype), fn)) return rc;
   if (T == 0) return MOE_OK;
   hipStream_t s = begin_launch(stream);
   hipError_t e;
   if (dtype == MOE_BF16)
     e = launch_route_bf16((const bf16_t*)x, (const bf16_t*)w_router, bias, T, H, E, k, logits,
-                          topk_idx, topk_w, (bf16_t*)ws, s);
+                          topk_idx, topk_w, (float*)ws, s);
   else
     e = launch_route_f32((const float*)x, (const float*)w_router, bias, T, H, E, k, logits,
                          topk_idx, topk_w, s);

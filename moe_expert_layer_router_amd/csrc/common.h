@@ -16,6 +16,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // 16 bytes as a native vector: staging values stay in registers (the
 // union-based HIP uint4 is not always split into registers by the compiler).
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 constexpr int kMaxE = 256;
@@ -97,10 +99,10 @@ namespace moe {
 
 // route.hip
 int route_nb(int E);                      // 32-expert column blocks of the bf16 router
-size_t route_ws_bytes(int H, int E);      // packed W_r fragments of the bf16 router
+size_t route_ws_bytes(int T, int H, int E);  // partial logits of the bf16 router
 hipError_t launch_route_bf16(const bf16_t* x, const bf16_t* w_router, const float* bias, int T,
                              int H, int E, int k, float* logits, int32_t* topk_idx, float* topk_w,
-                             bf16_t* wp_ws, hipStream_t s);
+                             float* part_ws, hipStream_t s);
 hipError_t launch_route_f32(const float* x, const float* w_router, const float* bias, int T, int H,
                             int E, int k, float* logits, int32_t* topk_idx, float* topk_w,
                             hipStream_t s);

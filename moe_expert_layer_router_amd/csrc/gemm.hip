@@ -108,8 +108,6 @@ struct GemmArgs {
   int fold;                 // WGRAD: F > 0 stores column c + column F + c (c < F), 0 = plain
 };
 
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef int rsrc_t __attribute__((ext_vector_type(4)));  // buffer descriptor (4 SGPRs)

@@ -6,15 +6,17 @@
 // gate weights = softmax over the kept logits (identical to a softmax over all
 // experts renormalised over the kept ones).
 //
-// bf16 path: one workgroup (8 waves) owns 32 tokens and all E <= 256 experts.
-// The eight waves split the hidden dimension H into interleaved 64-wide
-// chunks and run bf16 32x32x16 MFMAs straight from global memory (x rows, and
-// W_r repacked in MFMA fragment order, which is small and stays in L2), with
-// the next chunk's loads in flight during the current chunk's MFMAs; the
-// partial logit tiles are summed through LDS in a fixed order, so logits are
-// deterministic.  Then each half wave takes one token: every lane holds up to
-// eight logits (expert e = lane % 32 + 32 i) and k rounds of a branch-free
-// arg-max over unique (logit, id) keys pick the experts.
+// bf16 path, two launches.  (1) A workgroup of four waves takes 128 tokens and
+// one slice of HS rows of W_r (all E experts): the slice is copied once into
+// LDS, so the L2 traffic for W_r is one slice per 128 tokens, and each wave
+// multiplies its 32 tokens' x fragments (all of the slice's loads in flight
+// at once, straight from global memory) by the slice with bf16 32x32x16
+// MFMAs, reading the W_r fragments with transposing LDS reads.  Each wave
+// stores its fp32 partial logits.  (2) One half wave per token adds the
+// slices' partials in slice order (+ bias), stores the logits, and takes the
+// top k: every lane holds up to eight logits (expert e = lane % 32 + 32 i)
+// and k rounds of a branch-free arg-max over unique (logit, id) keys pick the
+// experts.  Every sum runs in a fixed order, so logits are deterministic.
 #include "common.h"
 
 #include <math.h>
@@ -105,171 +107,194 @@ __device__ __forceinline__ void topk_softmax_half(const float (&v)[NV], int E, i
   }
 }
 
-// W_r [H, E] -> MFMA B fragments: for every k16-step sg and 32-expert block nb
-// one 1 KB record whose lane l holds W_r[16 sg + 8 (l / 32) + q][32 nb + l % 32],
-// q = 0..7 (zero for experts >= E), so each fragment load of the router is
-// one contiguous 1 KB read.
-__global__ __launch_bounds__(256) void pack_router_kernel(const bf16_t* __restrict__ w,
-                                                          bf16_t* __restrict__ wp, int H, int E,
-                                                          int NB) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= (H / 16) * NB * 64) return;
-  const int l = i & 63, nb = (i >> 6) % NB, sg = (i >> 6) / NB;
-  const int e = nb * 32 + (l & 31);
-  const int h0 = sg * 16 + (l >> 5) * 8;
-  u32x4_t out;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t lo = e < E ? w[(size_t)(h0 + 2 * q) * E + e] : 0u;
-    const uint32_t hi = e < E ? w[(size_t)(h0 + 2 * q + 1) * E + e] : 0u;
-    out[q] = lo | (hi << 16);
-  }
-  *reinterpret_cast<u32x4_t*>(wp + (size_t)i * 8) = out;
-}
-
 int route_nb(int E) { return E <= 32 ? 1 : E <= 64 ? 2 : E <= 128 ? 4 : 8; }
-size_t route_ws_bytes(int H, int E) { return (size_t)H * 32 * route_nb(E) * sizeof(bf16_t); }
 
 // ---------------------------------------------------------------------------
-// bf16: MFMA router GEMM fused with top-k
+// bf16: sliced router GEMM (partial logits), then sum + top-k
 // ---------------------------------------------------------------------------
-constexpr int kRouteTB = 32;  // tokens per workgroup
-constexpr int kRouteWaves = 8;
+constexpr int kRtTokens = 128;  // tokens per workgroup: 4 waves x 32
+constexpr int kRtMaxRows = 512;  // rows of W_r per slice at most (x fragments held in registers)
 
-// Operands of one k chunk (CH k16-steps) for the 32 tokens x (32 NB) experts
-// tile: A fragments (x rows) and B fragments (rows of W_r^T).
-template <int CH, int NB>
-struct RouteChunk {
-  bf16x8_t a[CH];
-  bf16x8_t b[CH][NB];
-};
-
-// x fragments: xa points at this lane's row and k offset 8 (lane / 32);
-// W fragments: wpl points at this lane's 16 bytes of the packed record of
-// (k16-step 0, block 0); records are 512 elements apart.
-template <int CH, int NB>
-__device__ __forceinline__ void route_load(RouteChunk<CH, NB>& c, const bf16_t* xa,
-                                           const bf16_t* wpl, int k0) {
-#pragma unroll
-  for (int s = 0; s < CH; ++s) {
-    c.a[s] = *reinterpret_cast<const bf16x8_t*>(xa + k0 + 16 * s);
-    const bf16_t* rec = wpl + (size_t)((k0 >> 4) + s) * NB * 512;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) c.b[s][nb] = *reinterpret_cast<const bf16x8_t*>(rec + nb * 512);
+// Slice count S (slice HS = H / S rows, a multiple of 64): the fewest slices
+// whose W_r copy fits 128 KB of LDS and whose x fragments fit the registers,
+// then more while the grid has fewer workgroups than CUs.
+int route_slices(int T, int H, int E) {
+  const int EP = 32 * route_nb(E);
+  const int units = H / 64;
+  const int tiles = (T + kRtTokens - 1) / kRtTokens;
+  int S = units;
+  for (int d = 1; d <= units; ++d) {
+    const int HS = H / d;
+    if (units % d == 0 && HS <= kRtMaxRows && (size_t)HS * EP * 2 <= 128 * 1024) {
+      S = d;
+      break;
+    }
   }
+  for (int d = S + 1; d <= units && tiles * S < kCUs; ++d)
+    if (units % d == 0) S = d;
+  return S;
+}
+size_t route_ws_bytes(int T, int H, int E) {
+  return (size_t)route_slices(T, H, E) * T * E * sizeof(float);
 }
 
-// MFMAs of one chunk; a chunk past the end of H (valid == false, uniform)
-// contributes zero operands.
-template <int CH, int NB>
-__device__ __forceinline__ void route_mma(const RouteChunk<CH, NB>& c, bool valid,
-                                          f32x16_t (&acc)[NB]) {
-#pragma unroll
-  for (int s = 0; s < CH; ++s) {
-    const bf16x8_t a = valid ? c.a[s] : bf16x8_t{};
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, c.b[s][nb], acc[nb], 0, 0, 0);
-  }
+// LDS copy of a W_r slice: row h (= k of the product) holds EP bf16 (experts,
+// zero past E) as 16-byte chunks; logical chunk c sits at c ^ swz(h), which
+// spreads the four rows a transposing read touches over the bank line.
+template <int NB>
+__device__ __forceinline__ int rt_swz(int h) { return ((h & 3) << 2) & (4 * NB - 1); }
+
+// B fragment of k16-step j, expert block nb: lane l gets expert 32 nb + l % 32,
+// k = 16 j + 8 (l / 32) + 0..7, from two transposing reads (rows k and k + 4
+// of each 16-lane group): within a group, lane i points at row
+// 16 j + 8 (g / 2) + i / 4 and column 32 nb + 16 (g % 2) + 4 (i % 4).
+template <int NB>
+__device__ __forceinline__ bf16x8_t rt_frag(const bf16_t* s_w, int j, int nb, int lane) {
+  constexpr int EP = 32 * NB;
+  const int g = lane >> 4, i = lane & 15;
+  const int h = 16 * j + 8 * (g >> 1) + (i >> 2);  // h % 4 == (i >> 2) % 4, also for h + 4
+  const int c = (4 * nb + 2 * (g & 1) + ((i & 3) >> 1)) ^ rt_swz<NB>(h);
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  const auto* q = (const __attribute__((address_space(3))) char*)(
+      (const __attribute__((address_space(3))) void*)s_w) + (h * EP + c * 8 + 4 * (i & 1)) * 2;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)q);
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(q + 4 * EP * 2));
+  const i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
 }
 
-template <int NB>  // NB = number of 32-expert column blocks (E <= 32*NB)
-__global__ __launch_bounds__(kRouteWaves * kWave)
-__attribute__((amdgpu_waves_per_eu(2, 2))) void route_bf16_kernel(
-    const bf16_t* __restrict__ x, const bf16_t* __restrict__ wp, const float* __restrict__ bias,
-    int T, int H, int E, int k, float* __restrict__ logits, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w) {
-  constexpr int EP = NB * 32;
-  constexpr int CH = NB <= 4 ? 4 : 1;  // k16-steps per chunk (register budget)
-  constexpr int KC = 16 * CH;
-  constexpr int NTH = kRouteWaves * kWave;
-  extern __shared__ float s_part[];  // [4][kRouteTB][EP]
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
+// part[(s T + t) E + e] = sum over h in slice s (ascending, in MFMA k-steps) of x[t][h] W_r[h][e].
+template <int NB, int NSMAX>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void route_part_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, int T, int H,
+                       int E, int HS, float* __restrict__ part) {
+  constexpr int EP = 32 * NB;
+  constexpr int CPR = EP / 8;  // 16-byte chunks per LDS row
+  extern __shared__ __align__(16) bf16_t s_w[];  // [HS][EP]
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int t0 = blockIdx.x * kRouteTB;
-  const int nC = H / KC;  // H % 64 == 0
+  const int sl = blockIdx.y, h0 = sl * HS;
+  const int nstep = HS / 16;
+  const int t0 = blockIdx.x * kRtTokens + wave * 32;
 
-  int trow = t0 + (lane & 31);
-  if (trow >= T) trow = T - 1;  // ragged last block: duplicate a valid row, never stored
-  const bf16_t* xa = x + (size_t)trow * H + (lane >> 5) * 8;
-  const bf16_t* wpl = wp + lane * 8;  // packed W_r fragments (zero for experts >= E)
+  // Load order: this thread's chunks of the W_r slice (at most 32: the slice
+  // is at most 128 KB), then the x fragments of the whole slice, all in
+  // flight together; the LDS stores of the slice wait only for the W_r loads
+  // (older in the in-order memory counter), and each MFMA step only for its
+  // own x fragment, so the MFMAs overlap the x stream.
+  //   x: lane row t0 + l % 32 (clamped into range; rows past T are computed but
+  //   never stored), k = 16 j + 8 (l / 32) + 0..7.
+  const int nchunk = HS * CPR;
+  constexpr int kMaxChunks = 128 * 1024 / 16 / 256;
+  const bool vec = E % 8 == 0;
+  u32x4_t wv[kMaxChunks];
+  if (vec) {
+#pragma unroll
+    for (int u = 0; u < kMaxChunks; ++u) {
+      const int c = threadIdx.x + u * 256;
+      const int h = c / CPR, ch = c % CPR;
+      wv[u] = (c < nchunk && ch * 8 < E)
+                  ? *reinterpret_cast<const u32x4_t*>(w + (size_t)(h0 + h) * E + ch * 8)
+                  : u32x4_t{};
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  int trow = min(t0 + (lane & 31), T - 1);
+  const bf16_t* xa = x + (size_t)trow * H + h0 + (lane >> 5) * 8;
+  bf16x8_t a[NSMAX];
+#pragma unroll
+  for (int j = 0; j < NSMAX; ++j) a[j] = *reinterpret_cast<const bf16x8_t*>(xa + 16 * min(j, nstep - 1));
+  __builtin_amdgcn_sched_barrier(0);
+
+  // W_r[h0 .. h0 + HS) -> s_w
+  if (vec) {
+#pragma unroll
+    for (int u = 0; u < kMaxChunks; ++u) {
+      const int c = threadIdx.x + u * 256;
+      if (c >= nchunk) break;
+      const int h = c / CPR, ch = c % CPR;
+      *reinterpret_cast<u32x4_t*>(s_w + h * EP + ((ch ^ rt_swz<NB>(h)) * 8)) = wv[u];
+    }
+  } else {
+    for (int i = threadIdx.x; i < HS * EP; i += 256) {
+      const int h = i / EP, e = i % EP;
+      s_w[h * EP + (((e >> 3) ^ rt_swz<NB>(h)) << 3) + (e & 7)] =
+          e < E ? w[(size_t)(h0 + h) * E + e] : bf16_t(0);
+    }
+  }
+  __syncthreads();
+
   f32x16_t acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16_t{};
-
-  // Wave w takes chunks w, w + 8, w + 16, ...  Two register buffers alternate
-  // (no copies between them) and every wave runs the same trip count with
-  // every load issued unconditionally from a clamped, always valid chunk, so
-  // each load has a use on every path and stays where it is issued: one chunk
-  // is in flight while the previous one feeds the MFMAs.  Chunks past the end
-  // of H are multiplied as zeros.
-  RouteChunk<CH, NB> A, B;
-  const int n_it = (nC + 2 * kRouteWaves - 1) / (2 * kRouteWaves);
-  route_load<CH, NB>(A, xa, wpl, min(wave, nC - 1) * KC);
-  for (int it = 0; it < n_it; ++it) {
-    const int ch = wave + it * 2 * kRouteWaves;
-    // The scheduling barriers keep each chunk's loads ahead of the previous
-    // chunk's MFMAs (the scheduler would otherwise sink them to their uses).
-    route_load<CH, NB>(B, xa, wpl, min(ch + kRouteWaves, nC - 1) * KC);
-    __builtin_amdgcn_sched_barrier(0);
-    route_mma<CH, NB>(A, ch < nC, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    route_load<CH, NB>(A, xa, wpl, min(ch + 2 * kRouteWaves, nC - 1) * KC);
-    __builtin_amdgcn_sched_barrier(0);
-    route_mma<CH, NB>(B, ch + kRouteWaves < nC, acc);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  // Fixed-order reduction of the eight partial tiles: waves 4..7 store, waves
-  // 0..3 add their partner's tile to their own and store, then
-  // z = ((s0 + s1) + s2) + s3.
-  float* slot = s_part + (wave & 3) * kRouteTB * EP;
-  if (wave >= 4) {
+#pragma unroll
+  for (int j = 0; j < NSMAX; ++j) {
+    // steps past the slice multiply zeros (by a fragment of step 0)
+    const bool on = j < nstep;
+    const bf16x8_t av = on ? a[j] : bf16x8_t{};
+    const int js = on ? j : 0;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int row = 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-        slot[row * EP + nb * 32 + (lane & 31)] = acc[nb][q];
-      }
+      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, rt_frag<NB>(s_w, js, nb, lane), acc[nb], 0,
+                                                        0, 0);
   }
-  __syncthreads();
-  if (wave < 4) {
+  float* ps = part + (size_t)sl * T * E;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+  for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int row = 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-        float* p = slot + row * EP + nb * 32 + (lane & 31);
-        *p = acc[nb][q] + *p;
-      }
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < kRouteTB * EP; i += NTH) {
-    const int row = i / EP, e = i % EP;
-    float z = s_part[i] + s_part[kRouteTB * EP + i];
-    z += s_part[2 * kRouteTB * EP + i];
-    z += s_part[3 * kRouteTB * EP + i];
-    if (bias != nullptr && e < E) z += bias[e];
-    s_part[i] = z;
-    if (logits != nullptr && e < E && t0 + row < T) logits[(size_t)(t0 + row) * E + e] = z;
-  }
-  __syncthreads();
-  // two tokens per wave: half 0 takes token tt, half 1 token tt + 1
-  for (int tt = 2 * wave; tt < kRouteTB; tt += 2 * kRouteWaves) {
-    const int ts = tt + (lane >> 5);
-    const int t = t0 + ts;
-    if (t0 + tt >= T) break;  // wave-uniform
-    float v[NB];
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int e = (lane & 31) + 32 * i;
-      v[i] = (e < E) ? s_part[ts * EP + e] : 0.f;
+    for (int q = 0; q < 16; ++q) {
+      const int t = t0 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+      const int e = nb * 32 + (lane & 31);
+      if (t < T && e < E) ps[(size_t)t * E + e] = acc[nb][q];
     }
-    const bool active = t < T;
-    topk_softmax_half<NB>(v, E, k, active, topk_idx + (size_t)(active ? t : 0) * k,
-                          topk_w + (size_t)(active ? t : 0) * k);
+}
+
+// Logits z[t][e] = sum over slices s (ascending) of part[s][t][e] (+ bias[e]),
+// then the top-k.  Two tokens per wave, one per half.
+template <int NB>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ part, int S,
+                                                         int T, int E, int k,
+                                                         const float* __restrict__ bias,
+                                                         float* __restrict__ logits,
+                                                         int32_t* __restrict__ topk_idx,
+                                                         float* __restrict__ topk_w) {
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (2 * pair >= T) return;
+  const int t = 2 * pair + ((threadIdx.x >> 5) & 1);
+  const bool active = t < T;
+  const int tr = active ? t : T - 1;
+  const int h32 = lane_id() & 31;
+  float v[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) v[i] = 0.f;
+  // four slices' loads in flight at a time, added in slice order
+  for (int s0 = 0; s0 < S; s0 += 4) {
+    float pv[4][NB];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float* ps = part + ((size_t)min(s0 + u, S - 1) * T + tr) * E;
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int e = h32 + 32 * i;
+        pv[u][i] = (e < E) ? ps[e] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (s0 + u < S) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) v[i] += pv[u][i];
+      }
   }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int e = h32 + 32 * i;
+    if (e < E) {
+      if (bias != nullptr) v[i] += bias[e];
+      if (logits != nullptr && active) logits[(size_t)t * E + e] = v[i];
+    }
+  }
+  topk_softmax_half<NB>(v, E, k, active, topk_idx + (size_t)tr * k, topk_w + (size_t)tr * k);
 }
 
 // ---------------------------------------------------------------------------
@@ -357,22 +382,27 @@ hipError_t launch_transpose(const void* src, void* dst, int rows, int cols, int 
 
 hipError_t launch_route_bf16(const bf16_t* x, const bf16_t* w_router, const float* bias, int T,
                              int H, int E, int k, float* logits, int32_t* topk_idx, float* topk_w,
-                             bf16_t* wp_ws, hipStream_t s) {
+                             float* part_ws, hipStream_t s) {
   const int nb = route_nb(E);
-  const int nrec = (H / 16) * nb * 64;
-  pack_router_kernel<<<(nrec + 255) / 256, 256, 0, s>>>(w_router, wp_ws, H, E, nb);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const int blocks = (T + kRouteTB - 1) / kRouteTB;
+  const int S = route_slices(T, H, E);
+  const int HS = H / S;
+  const dim3 grid((T + kRtTokens - 1) / kRtTokens, S);
+  const size_t lds = (size_t)HS * 32 * nb * sizeof(bf16_t);
   ProfScope ps(MOE_KERNEL_ROUTE, s);
-#define MOE_ROUTE_CASE(NB)                                                                  \
-  route_bf16_kernel<NB><<<blocks, kRouteWaves * kWave, 4 * kRouteTB * NB * 32 * sizeof(float), \
-                          s>>>(x, wp_ws, bias, T, H, E, k, logits, topk_idx, topk_w)
-  if (nb == 1) MOE_ROUTE_CASE(1);
-  else if (nb == 2) MOE_ROUTE_CASE(2);
-  else if (nb == 4) MOE_ROUTE_CASE(4);
-  else MOE_ROUTE_CASE(8);
-#undef MOE_ROUTE_CASE
+#define MOE_RT_CASE(NB)                                                                        \
+  do {                                                                                         \
+    if (HS <= 256)                                                                             \
+      route_part_kernel<NB, 16><<<grid, 256, lds, s>>>(x, w_router, T, H, E, HS, part_ws);     \
+    else                                                                                       \
+      route_part_kernel<NB, 32><<<grid, 256, lds, s>>>(x, w_router, T, H, E, HS, part_ws);     \
+    route_topk_kernel<NB><<<(T + 7) / 8, 256, 0, s>>>(part_ws, S, T, E, k, bias, logits,       \
+                                                      topk_idx, topk_w);                      \
+  } while (0)
+  if (nb == 1) MOE_RT_CASE(1);
+  else if (nb == 2) MOE_RT_CASE(2);
+  else if (nb == 4) MOE_RT_CASE(4);
+  else MOE_RT_CASE(8);
+#undef MOE_RT_CASE
   return hipGetLastError();
 }
 

@@ -62,7 +62,8 @@ def _err():
 def test_workspace_bytes_and_errors():
     ws = lambda *a: L.moe_workspace_bytes(*a)
     assert ws(moe.MOE_OP_ROUTE, 16384, 2048, 768, 128, 8, 0, 128, F32) == 0
-    assert ws(moe.MOE_OP_ROUTE, 16384, 2048, 768, 128, 8, 0, 128, BF16) == 128 * 2048 * 2
+    # bf16 router: fp32 partial logits of S slices of H (S = 4 for H=2048, E=128: 512-row slices)
+    assert ws(moe.MOE_OP_ROUTE, 16384, 2048, 768, 128, 8, 0, 128, BF16) == 4 * 16384 * 128 * 4
     assert ws(moe.MOE_OP_PERMUTE, 16384, 2048, 768, 128, 8, 0, 128, BF16) > 16384 * 8 * 4
     assert ws(moe.MOE_OP_FFN_BWD, 8192, 2048, 768, 128, 8, 0, 16, BF16) >= 8192 * 8 * 2 * 768 * 2
     assert ws(moe.MOE_OP_PERMUTE, 0, 2048, 768, 128, 8, 0, 16, BF16) == 0
