@@ -67,10 +67,18 @@ struct Cfg {
   static constexpr int NIA = kStageA * 2 / 1024 / 4;   // DMA instructions per wave per stage, A
   static constexpr int kSlotA = kStageA * 2;           // bytes
   static constexpr int kOffB = NST * kSlotA;           // B slots start here
-  static constexpr int kLdsBytes = NST * (kSlotA + kSlotB);
+  static constexpr int kRingBytes = NST * (kSlotA + kSlotB);
   static constexpr int kWavesPerSimd = BM == 256 ? 1 : 2;  // = workgroups per CU
+  // The epilogue stages 16 x 128 fp32 (8 KB) per wave.  256-row tiles keep
+  // that area after the ring, so the next tile's first K steps are loaded
+  // during the epilogue; 128-row tiles (two workgroups per CU) stage in the
+  // ring and start the next tile's loads after it.
+  static constexpr bool kSepStage = BM == 256;
+  static constexpr int kStageBytes = 4 * 8192;
+  static constexpr int kStageOff = kSepStage ? kRingBytes : 0;
+  static constexpr int kLdsBytes = kSepStage ? kRingBytes + kStageBytes : kRingBytes;
   static_assert(kLdsBytes * kWavesPerSimd <= 160 * 1024, "LDS per CU");
-  static_assert(kLdsBytes >= 4 * 16384, "the epilogue stages 16 KB per wave in the ring");
+  static_assert(kSepStage || kRingBytes >= kStageBytes, "staging area inside the ring");
 };
 // Tile heights in use (chosen per product by measurement on the 128-expert
 // layer: 256 wherever the larger tile's lower L2 and LDS traffic per MFMA wins
@@ -433,24 +441,28 @@ __device__ __forceinline__ void mma_dma_read(f32x16_t (&acc)[C::MI][NI], const F
 
 // ---------------------------------------------------------------------------
 // Epilogue: the accumulators go through LDS so that global stores are 16-byte
-// row segments.  Each wave stages one 32 x 128 fp32 block row of its sub-tile
-// at a time into its own 16 KB of the ring (16-byte chunks
-// XOR-swizzled so the row pairs written by one MFMA output register hit
-// different banks), then every lane handles 8 consecutive columns of a row.
+// row segments.  Each wave stages 16 rows x 128 fp32 of its sub-tile at a time
+// (half of a 32-row MFMA block row: output registers q = 8 h .. 8 h + 7) into
+// its own 8 KB (16-byte chunks XOR-swizzled so the row pairs written by one
+// MFMA output register hit different banks), then every lane handles 8
+// consecutive columns of a row.
 // ---------------------------------------------------------------------------
+template <class C>
 __device__ __forceinline__ float* stage_area(int wave) {
-  return reinterpret_cast<float*>(g_lds) + wave * 4096;  // 16 KB per wave
+  return reinterpret_cast<float*>(reinterpret_cast<char*>(g_lds) + C::kStageOff) + wave * 2048;
 }
-// fp32 element (row r < 32, col c < 128) of a wave's staging area
+// fp32 element (row r < 16, col c < 128) of a wave's staging area
 __device__ __forceinline__ int stage_idx(int r, int c) { return r * 128 + (c ^ (((r >> 2) & 1) << 5)); }
 
 template <int MI>
-__device__ __forceinline__ void stage_part(float* st, const f32x16_t (&acc)[MI][NI], int mi, int lane) {
+__device__ __forceinline__ void stage_half(float* st, const f32x16_t (&acc)[MI][NI], int mi, int h,
+                                           int lane) {
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int r = 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+    for (int q8 = 0; q8 < 8; ++q8) {
+      const int q = 8 * h + q8;
+      const int r = 8 * (q8 >> 2) + 4 * (lane >> 5) + (q & 3);  // row within the half
       st[stage_idx(r, ni * 32 + (lane & 31))] = acc[mi][ni][q];
     }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -485,63 +497,67 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
                                          int lane) {
   constexpr int MI = C::MI, WM = C::WM;
   const int wm = wave >> 1, wn = wave & 1;
-  float* st = stage_area(wave);
+  float* st = stage_area<C>(wave);
   if constexpr (KIND == K_WGRAD) {
     if (p.fold > 0) {  // uniform: the whole workgroup takes this path
       // Output column c (< F) is the sum of tile columns c and F + c, which
       // may belong to the other wave of the row pair: all four waves stage a
-      // block, then every thread adds pairs of 8 columns.
+      // half block row, then every thread adds pairs of 8 columns.
       const int F = p.fold;
-      const int tasks = 2 * 32 * (F / 8);
+      const int tasks = 2 * 16 * (F / 8);
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        stage_part(st, acc, mi, lane);
-        __syncthreads();
-        for (int q = threadIdx.x; q < tasks; q += NTH) {
-          const int c = (q % (F / 8)) * 8;
-          const int r = (q / (F / 8)) % 32;
-          const int pw = q / (F / 8) / 32;  // wave row of the pair
-          const int m = m0 + pw * WM + mi * 32 + r;
-          if (m >= p.M) continue;
-          float lo[8], hi[8];
-          load8(stage_area(pw * 2 + c / WN), r, c % WN, lo);
-          load8(stage_area(pw * 2 + (F + c) / WN), r, (F + c) % WN, hi);
-          float* dst = p.f0 + e * p.f_group_stride + (long)m * p.ldc + c;
-          float4* d4 = reinterpret_cast<float4*>(dst);
-          d4[0] = make_float4(lo[0] + hi[0], lo[1] + hi[1], lo[2] + hi[2], lo[3] + hi[3]);
-          d4[1] = make_float4(lo[4] + hi[4], lo[5] + hi[5], lo[6] + hi[6], lo[7] + hi[7]);
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          stage_half(st, acc, mi, h, lane);
+          __syncthreads();
+          for (int q = threadIdx.x; q < tasks; q += NTH) {
+            const int c = (q % (F / 8)) * 8;
+            const int r = (q / (F / 8)) % 16;
+            const int pw = q / (F / 8) / 16;  // wave row of the pair
+            const int m = m0 + pw * WM + mi * 32 + 16 * h + r;
+            if (m >= p.M) continue;
+            float lo[8], hi[8];
+            load8(stage_area<C>(pw * 2 + c / WN), r, c % WN, lo);
+            load8(stage_area<C>(pw * 2 + (F + c) / WN), r, (F + c) % WN, hi);
+            float* dst = p.f0 + e * p.f_group_stride + (long)m * p.ldc + c;
+            float4* d4 = reinterpret_cast<float4*>(dst);
+            d4[0] = make_float4(lo[0] + hi[0], lo[1] + hi[1], lo[2] + hi[2], lo[3] + hi[3]);
+            d4[1] = make_float4(lo[4] + hi[4], lo[5] + hi[5], lo[6] + hi[6], lo[7] + hi[7]);
+          }
+          __syncthreads();
         }
-        __syncthreads();
-      }
       return;
     }
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      stage_part(st, acc, mi, lane);
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int r = it * 4 + (lane >> 4);
-        const int c = (lane & 15) * 8;
-        const int m = m0 + wm * WM + mi * 32 + r;
-        const int n = n0 + wn * WN + c;
-        if (m >= p.M || n >= p.N) continue;
-        float v[8];
-        load8(st, r, c, v);
-        float* dst = (m < p.m_split) ? p.f0 + e * p.f_group_stride + (long)m * p.ldc + n
-                                     : p.f1 + e * p.f_group_stride + (long)(m - p.m_split) * p.ldc + n;
-        float4* d4 = reinterpret_cast<float4*>(dst);
-        if (p.accumulate) {
-          const float4 o0 = d4[0], o1 = d4[1];
-          d4[0] = make_float4(o0.x + v[0], o0.y + v[1], o0.z + v[2], o0.w + v[3]);
-          d4[1] = make_float4(o1.x + v[4], o1.y + v[5], o1.z + v[6], o1.w + v[7]);
-        } else {
-          d4[0] = make_float4(v[0], v[1], v[2], v[3]);
-          d4[1] = make_float4(v[4], v[5], v[6], v[7]);
+      for (int h = 0; h < 2; ++h) {
+        stage_half(st, acc, mi, h, lane);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int r = it * 4 + (lane >> 4);
+          const int c = (lane & 15) * 8;
+          const int m = m0 + wm * WM + mi * 32 + 16 * h + r;
+          const int n = n0 + wn * WN + c;
+          if (m >= p.M || n >= p.N) continue;
+          float v[8];
+          load8(st, r, c, v);
+          float* dst = (m < p.m_split) ? p.f0 + e * p.f_group_stride + (long)m * p.ldc + n
+                                       : p.f1 + e * p.f_group_stride + (long)(m - p.m_split) * p.ldc + n;
+          float4* d4 = reinterpret_cast<float4*>(dst);
+          if (p.accumulate) {
+            const float4 o0 = d4[0], o1 = d4[1];
+            d4[0] = make_float4(o0.x + v[0], o0.y + v[1], o0.z + v[2], o0.w + v[3]);
+            d4[1] = make_float4(o1.x + v[4], o1.y + v[5], o1.z + v[6], o1.w + v[7]);
+          } else {
+            d4[0] = make_float4(v[0], v[1], v[2], v[3]);
+            d4[1] = make_float4(v[4], v[5], v[6], v[7]);
+          }
         }
+        // the next half reuses the staging area
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
-      // the next quarter reuses the staging area
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    }
   } else if constexpr (KIND == K_GATEUP_FWD) {
     // staged columns: [g 32 | u 32 | g 32 | u 32] for h columns nt*128 + wn*64 + 0..63
     const out_rsrc_t rh = out_rsrc(p.c0, row0, row1, p.ldc);
@@ -551,25 +567,27 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
     const int col = nt * 128 + wn * 64 + hc;
     const bool col_ok = col < p.I;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      stage_part(st, acc, mi, lane);
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int r = it * 8 + (lane >> 3);
-        const int lrow = wm * WM + mi * 32 + r;  // row within the tile
-        float g[8], u[8], h[8];
-        load8(st, r, sc, g);
-        load8(st, r, sc + 32, u);
+      for (int h = 0; h < 2; ++h) {
+        stage_half(st, acc, mi, h, lane);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) h[j] = g[j] * fast_rcp(1.f + __expf(-g[j])) * u[j];
-        const uint32_t oh = col_ok ? (uint32_t)((lrow * p.ldc + col) * 2) : kOutKill;
-        const uint32_t og = col_ok ? (uint32_t)((lrow * 2 * p.I + col) * 2) : kOutKill;
-        store16(rh, oh, pack8(h));
-        store16(rgu, og, pack8(g));
-        store16(rgu, og + (col_ok ? p.I * 2 : 0), pack8(u));
+        for (int it = 0; it < 2; ++it) {
+          const int r = it * 8 + (lane >> 3);
+          const int lrow = wm * WM + mi * 32 + 16 * h + r;  // row within the tile
+          float g[8], u[8], hv[8];
+          load8(st, r, sc, g);
+          load8(st, r, sc + 32, u);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) hv[j] = g[j] * fast_rcp(1.f + __expf(-g[j])) * u[j];
+          const uint32_t oh = col_ok ? (uint32_t)((lrow * p.ldc + col) * 2) : kOutKill;
+          const uint32_t og = col_ok ? (uint32_t)((lrow * 2 * p.I + col) * 2) : kOutKill;
+          store16(rh, oh, pack8(hv));
+          store16(rgu, og, pack8(g));
+          store16(rgu, og + (col_ok ? p.I * 2 : 0), pack8(u));
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    }
   } else {  // DOWN_FWD, GATEUP_DGRAD, DOWN_DGRAD: rows of the grouped buffer
     const int c = (lane & 15) * 8;
     const int n = n0 + wn * WN + c;
@@ -577,38 +595,33 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
     const long ldo = (KIND == K_DOWN_DGRAD) ? 2L * p.I : p.ldc;
     const out_rsrc_t ro = out_rsrc(p.c0, row0, row1, ldo);
     // DOWN_DGRAD reads the saved g / u of its rows through the same kind of
-    // descriptor (rows past the tile read as zero).  With 256-row tiles the
-    // loads of pass mi + 1 are issued before pass mi's math and stores, so
-    // their latency hides behind a whole pass; 128-row tiles (half the
-    // registers per wave) load each pass's own at its start.
-    constexpr int NBUF = C::BM == 256 ? 2 : 1;
+    // descriptor (rows past the tile read as zero).  The loads of half pass
+    // q + 1 are issued before half pass q's math and stores, so their latency
+    // hides behind a pass.
+    constexpr int NP = 2 * MI;  // half passes
     out_rsrc_t rg;
-    u32x4_t graw[NBUF][8], uraw[NBUF][8];
+    u32x4_t graw[2][4], uraw[2][4];
     if constexpr (KIND == K_DOWN_DGRAD) rg = out_rsrc(p.gu, row0, row1, 2L * p.I);
-    auto load_gu = [&](int mi, int b) {
+    auto load_gu = [&](int pq, int b) {
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int lrow = wm * WM + mi * 32 + it * 4 + (lane >> 4);
+      for (int it = 0; it < 4; ++it) {
+        const int lrow = wm * WM + (pq >> 1) * 32 + 16 * (pq & 1) + it * 4 + (lane >> 4);
         const uint32_t o = col_ok ? (uint32_t)((lrow * 2 * p.I + n) * 2) : kOutKill;
         graw[b][it] = __builtin_amdgcn_raw_buffer_load_b128(rg, o, 0, 0);
         uraw[b][it] = __builtin_amdgcn_raw_buffer_load_b128(rg, o + (col_ok ? p.I * 2 : 0), 0, 0);
       }
     };
-    if constexpr (KIND == K_DOWN_DGRAD && NBUF == 2) load_gu(0, 0);
+    if constexpr (KIND == K_DOWN_DGRAD) load_gu(0, 0);
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      if constexpr (KIND == K_DOWN_DGRAD) {
-        if constexpr (NBUF == 2) {
-          if (mi + 1 < MI) load_gu(mi + 1, (mi + 1) & 1);
-        } else {
-          load_gu(mi, 0);
-        }
-      }
-      stage_part(st, acc, mi, lane);
+    for (int pq = 0; pq < NP; ++pq) {
+      const int mi = pq >> 1, h = pq & 1;
+      if constexpr (KIND == K_DOWN_DGRAD)
+        if (pq + 1 < NP) load_gu(pq + 1, (pq + 1) & 1);
+      stage_half(st, acc, mi, h, lane);
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
+      for (int it = 0; it < 4; ++it) {
         const int r = it * 4 + (lane >> 4);
-        const int lrow = wm * WM + mi * 32 + r;
+        const int lrow = wm * WM + mi * 32 + 16 * h + r;
         float v[8];
         load8(st, r, c, v);
         const uint32_t o = col_ok ? (uint32_t)((lrow * ldo + n) * 2) : kOutKill;
@@ -617,8 +630,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
           float g[8], u[8], dg[8], du[8];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const u32x4_t& gw = graw[mi % NBUF][it];
-            const u32x4_t& uw = uraw[mi % NBUF][it];
+            const u32x4_t& gw = graw[pq & 1][it];
+            const u32x4_t& uw = uraw[pq & 1][it];
             g[2 * q] = __uint_as_float(gw[q] << 16);
             g[2 * q + 1] = __uint_as_float(gw[q] & 0xffff0000u);
             u[2 * q] = __uint_as_float(uw[q] << 16);
@@ -636,7 +649,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
           store16(ro, o, pack8(v));
         }
       }
-      // the next quarter reuses the staging area
+      // the next half reuses the staging area
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
   }
@@ -645,14 +658,212 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
+// The K steps of one tile (the ring holds steps 0 .. NST - 2 and half of step
+// NST - 1 when it starts; f0 holds step 0's sub-step 0 fragments).
+// One K step per iteration on ring slot `slot`, software pipelined: the
+// fragments of sub-step 1 are read during the first MFMAs of sub-step 0,
+// together with the second half of the DMA of step kt + NST - 1 into the
+// previous slot (every wave finished reading it before the previous barrier).
+// Before the MFMAs of sub-step 1 the wave waits for step kt + 1 to land
+// (barrier); between those MFMAs it starts the first half of the DMA of step
+// kt + NST into this slot (every wave has finished reading it) and reads the
+// next step's sub-step 0 fragments.
+template <int KIND, class C>
+__device__ __forceinline__ void k_steps(f32x16_t (&acc)[C::MI][NI], Frags<C>& f0, Frags<C>& f1,
+                                        const FragLanes& L, const GemmArgs& p,
+                                        const Operand<C::NIA>& opA, const Operand<NIB>& opB,
+                                        uint32_t dma_a, uint32_t dma_b, uint32_t wa, uint32_t wb,
+                                        int nk) {
+  constexpr int NST = C::NST, NIA = C::NIA, kSlotA = C::kSlotA, kOffB = C::kOffB;
+  int slot = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint32_t sa = slot * kSlotA + wa, sb = kOffB + slot * kSlotB + wb;
+    const int pslot = slot == 0 ? NST - 1 : slot - 1;
+    mma_read_next<KIND, C>(acc, f0, f1, 1, sa, sb, L, p, opA, opB, dma_a + pslot * kSlotA,
+                           dma_b + pslot * kSlotB, (kt + NST - 1) * BK,
+                           kt + NST - 1 < nk ? 0u : kDmaKill);
+    const int nslot = slot + 1 == NST ? 0 : slot + 1;
+    // Steps kt + 1 .. kt + NST - 1 are in flight; step kt + 1 has landed
+    // when only the newer ones (NIA + NIB loads each) remain.
+    wait_vm<(NST - 2) * (NIA + NIB)>();
+    lds_barrier();  // every wave: step kt + 1 landed, slot `slot` fully read
+    mma_dma_read<KIND, C>(acc, f1, f0, nslot * kSlotA + wa, kOffB + nslot * kSlotB + wb, L, p,
+                          opA, opB, dma_a + slot * kSlotA, dma_b + slot * kSlotB, (kt + NST) * BK,
+                          kt + NST < nk ? 0u : kDmaKill);
+    slot = nslot;
+  }
+}
+
+// Vector memory instructions each lane issues in the epilogue of an M-grouped
+// product (the buffer stores and loads there are unconditional: the range
+// checks drop the ones outside the tile), or -1 where the count depends on the
+// data (WGRAD).  A K loop that starts after the previous tile's epilogue (its
+// first DMAs issued before that epilogue) waits past exactly these.
+template <int KIND, class C>
+__host__ __device__ constexpr int epilogue_vmem_ops() {
+  return KIND == K_GATEUP_FWD   ? 12 * C::MI   // 3 stores x 2 rows x 2 halves per block row
+         : KIND == K_DOWN_DGRAD ? 32 * C::MI   // 2 loads + 2 stores x 4 rows x 2 halves
+         : KIND == K_WGRAD      ? -1
+                                : 8 * C::MI;   // 1 store x 4 rows x 2 halves
+}
+
+// One output tile: expert / group e, N tile nt and its first column n0; the
+// M-grouped products' rows [row0, row1), the K-grouped products' first output
+// row m0 and rows [kbeg, kend) of the reduction; nk K steps.
+struct Tile {
+  int e, nt, n0, row0, row1, m0, kbeg, kend, nk;
+};
+
+template <int KIND, class C>
+__device__ __forceinline__ Tile decode_tile(const GemmArgs& p, int work) {
+  constexpr int BM = C::BM;
+  int e, nt, row0 = 0, row1 = 0, m0 = 0, kbeg = 0, kend = 0;
+  if constexpr (KIND == K_WGRAD) {
+    e = work / (p.n_mtiles * p.n_ntiles);
+    const int rem = work - e * p.n_mtiles * p.n_ntiles;
+    m0 = (rem / p.n_ntiles) * BM;
+    nt = rem % p.n_ntiles;
+    if (p.offsets != nullptr) {
+      kbeg = p.offsets[e];
+      kend = p.offsets[e + 1];
+    } else {
+      kbeg = min(e * p.split_rows, p.ktot);
+      kend = min(kbeg + p.split_rows, p.ktot);
+    }
+  } else {
+    const int mt = work / p.n_ntiles;
+    nt = work - mt * p.n_ntiles;
+    e = p.sched[1 + 3 * mt];
+    row0 = p.sched[2 + 3 * mt];
+    row1 = p.sched[3 + 3 * mt];
+    kend = p.K;
+  }
+  // Tile scalars are wave-uniform; saying so keeps buffer descriptors and
+  // DMA addresses in SGPRs (no per-lane waterfall loops).
+  e = __builtin_amdgcn_readfirstlane(e);
+  nt = __builtin_amdgcn_readfirstlane(nt);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  row1 = __builtin_amdgcn_readfirstlane(row1);
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  kbeg = __builtin_amdgcn_readfirstlane(kbeg);
+  kend = __builtin_amdgcn_readfirstlane(kend);
+
+  Tile t;
+  t.e = e;
+  t.nt = nt;
+  t.n0 = nt * BN;
+  t.row0 = row0;
+  t.row1 = row1;
+  t.m0 = m0;
+  t.kbeg = kbeg;
+  t.kend = kend;
+  t.nk = (kend - kbeg + BK - 1) / BK;
+  return t;
+}
+
+// Buffer descriptors and per-lane DMA offsets of a tile's operands.
+template <int KIND, class C>
+__device__ __forceinline__ void setup_operands(const GemmArgs& p, const Tile& t, int wave, int lane,
+                                               Operand<C::NIA>& opA, Operand<NIB>& opB) {
+  using Tr = Traits<KIND>;
+  constexpr int BM = C::BM, NIA = C::NIA;
+  const int e = t.e, nt = t.nt, n0 = t.n0, row0 = t.row0, row1 = t.row1, m0 = t.m0;
+  const int kbeg = t.kbeg, kend = t.kend;
+  if constexpr (Tr::A_KC) {
+    // the tile's rows [row0, row1) of A; rows past row1 read as zero
+    opA.rsrc = make_rsrc(p.a + (long)row0 * p.lda, (uint32_t)((row1 - row0) * p.lda * 2));
+    opA.kstep = 2;
+#pragma unroll
+    for (int u = 0; u < NIA; ++u) {
+      int r, c;
+      kc_rows<NIA>(wave, lane, u, r, c);
+      opA.voff[u] = (uint32_t)(r * p.lda * 2 + c * 16);
+    }
+  } else {  // WGRAD: A[k = row of the group][m]; rows past the group read as zero
+    opA.rsrc = make_rsrc(p.a + (long)kbeg * p.lda, (uint32_t)((kend - kbeg) * p.lda * 2));
+    opA.kstep = (uint32_t)(p.lda * 2);
+#pragma unroll
+    for (int u = 0; u < NIA; ++u) {
+      int r, c;
+      mc_rows<NIA, BM>(wave, lane, u, r, c);
+      const int col = min(m0 + c * 8, p.M - 8);  // tail columns: any in-row data, never stored
+      opA.voff[u] = (uint32_t)(r * p.lda * 2 + col * 2);
+    }
+  }
+  if constexpr (KIND == K_GATEUP_FWD) {
+    // Tile rows interleave 32 gate rows and 32 up rows, so each wave's N
+    // blocks (g, u, g, u) pair gate and up values of the same h columns.
+    const long est = (long)e * p.b_group_stride;
+    opB.rsrc = make_rsrc(p.b0 + est, (uint32_t)(p.I * p.ldb * 2));
+    opB.rsrc2 = make_rsrc(p.b1 + est, (uint32_t)(p.I * p.ldb * 2));
+    opB.kstep = 2;
+#pragma unroll
+    for (int u = 0; u < NIB; ++u) {
+      int r, c;
+      kc_rows<NIB>(wave, lane, u, r, c);
+      const int col = nt * 128 + (r >> 6) * 32 + (r & 31);
+      opB.voff[u] = (uint32_t)(col * p.ldb * 2 + c * 16);
+    }
+  } else if constexpr (KIND == K_DOWN_FWD) {
+    opB.rsrc = make_rsrc(p.b0 + (long)e * p.b_group_stride, (uint32_t)(p.N * p.ldb * 2));
+    opB.kstep = 2;
+#pragma unroll
+    for (int u = 0; u < NIB; ++u) {
+      int r, c;
+      kc_rows<NIB>(wave, lane, u, r, c);
+      opB.voff[u] = (uint32_t)((n0 + r) * p.ldb * 2 + c * 16);
+    }
+  } else if constexpr (KIND == K_DOWN_DGRAD || KIND == K_GATEUP_DGRAD) {
+    // B[k][n] = weight row k, column n (MN-contiguous), whole expert matrix
+    const long est = (long)e * p.b_group_stride;
+    const uint32_t rows = (KIND == K_DOWN_DGRAD) ? (uint32_t)p.K : (uint32_t)p.I;
+    opB.rsrc = make_rsrc(p.b0 + est, rows * (uint32_t)p.ldb * 2);
+    if constexpr (KIND == K_GATEUP_DGRAD) opB.rsrc2 = make_rsrc(p.b1 + est, rows * (uint32_t)p.ldb * 2);
+    opB.kstep = (uint32_t)(p.ldb * 2);
+#pragma unroll
+    for (int u = 0; u < NIB; ++u) {
+      int r, c;
+      mc_rows<NIB, BN>(wave, lane, u, r, c);
+      const int col = min(n0 + c * 8, p.N - 8);
+      opB.voff[u] = (uint32_t)(r * p.ldb * 2 + col * 2);
+    }
+  } else {  // WGRAD B
+    opB.rsrc = make_rsrc(p.b0 + (long)kbeg * p.ldb, (uint32_t)((kend - kbeg) * p.ldb * 2));
+    opB.kstep = (uint32_t)(p.ldb * 2);
+#pragma unroll
+    for (int u = 0; u < NIB; ++u) {
+      int r, c;
+      mc_rows<NIB, BN>(wave, lane, u, r, c);
+      const int col = min(n0 + c * 8, p.N - 8);
+      opB.voff[u] = (uint32_t)(r * p.ldb * 2 + col * 2);
+    }
+  }
+}
+
+// Steps 0 .. NST - 2 and the first half of step NST - 1 of a tile into the
+// ring (the ones past K dropped).
+template <int KIND, class C>
+__device__ __forceinline__ void issue_prologue(const GemmArgs& p, const Operand<C::NIA>& opA,
+                                               const Operand<NIB>& opB, uint32_t dma_a,
+                                               uint32_t dma_b, int nk) {
+  constexpr int NST = C::NST, ND = C::NIA + NIB;
+#pragma unroll
+  for (int st = 0; st < NST; ++st) {
+    const uint32_t kill = st < nk ? 0u : kDmaKill;
+#pragma unroll
+    for (int u = 0; u < (st < NST - 1 ? ND : ND / 2); ++u)
+      dma_piece<KIND, C>(p, opA, opB, dma_a + st * C::kSlotA, dma_b + st * kSlotB, st * BK, kill, u);
+  }
+}
+
 template <int KIND, int BM_>
 __global__ __launch_bounds__(NTH)
 __attribute__((amdgpu_waves_per_eu(Cfg<BM_>::kWavesPerSimd, Cfg<BM_>::kWavesPerSimd)))
 void gemm_kernel(const GemmArgs p) {
   using Tr = Traits<KIND>;
   using C = Cfg<BM_>;
-  constexpr int BM = C::BM, WM = C::WM, MI = C::MI, NST = C::NST, NIA = C::NIA;
-  constexpr int kSlotA = C::kSlotA, kOffB = C::kOffB;
+  constexpr int WM = C::WM, MI = C::MI, NST = C::NST, NIA = C::NIA;
+  constexpr int kOffB = C::kOffB;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -666,179 +877,82 @@ void gemm_kernel(const GemmArgs p) {
   else
     total = p.sched[0] * p.n_ntiles;
 
-  for (int work = xcd_remap(blockIdx.x, gridDim.x); work < total; work += gridDim.x) {
-    // ---------------------------------------------------------------- tile
-    int e, nt, row0 = 0, row1 = 0, m0 = 0, kbeg = 0, kend = 0;
-    if constexpr (KIND == K_WGRAD) {
-      e = work / (p.n_mtiles * p.n_ntiles);
-      const int rem = work - e * p.n_mtiles * p.n_ntiles;
-      m0 = (rem / p.n_ntiles) * BM;
-      nt = rem % p.n_ntiles;
-      if (p.offsets != nullptr) {
-        kbeg = p.offsets[e];
-        kend = p.offsets[e + 1];
-      } else {
-        kbeg = min(e * p.split_rows, p.ktot);
-        kend = min(kbeg + p.split_rows, p.ktot);
-      }
-    } else {
-      const int mt = work / p.n_ntiles;
-      nt = work - mt * p.n_ntiles;
-      e = p.sched[1 + 3 * mt];
-      row0 = p.sched[2 + 3 * mt];
-      row1 = p.sched[3 + 3 * mt];
-      kend = p.K;
-    }
-    // Tile scalars are wave-uniform; saying so keeps buffer descriptors and
-    // DMA addresses in SGPRs (no per-lane waterfall loops).
-    e = __builtin_amdgcn_readfirstlane(e);
-    nt = __builtin_amdgcn_readfirstlane(nt);
-    row0 = __builtin_amdgcn_readfirstlane(row0);
-    row1 = __builtin_amdgcn_readfirstlane(row1);
-    m0 = __builtin_amdgcn_readfirstlane(m0);
-    kbeg = __builtin_amdgcn_readfirstlane(kbeg);
-    kend = __builtin_amdgcn_readfirstlane(kend);
-    const int n0 = nt * BN;
+  int work = xcd_remap(blockIdx.x, gridDim.x);
+  if (work >= total) return;
+  const uint32_t dma_a = lds_addr(g_lds) + wave * NIA * 1024;  // this wave's DMA area
+  const uint32_t dma_b = lds_addr(g_lds) + kOffB + wave * NIB * 1024;
+  // wave block bases inside a slot
+  // (MC fragment offsets hold the wave's columns themselves)
+  const uint32_t wa = Tr::A_KC ? (uint32_t)(wm * WM * BK * 2) : 0u;
+  const uint32_t wb = Tr::B_KC ? (uint32_t)(wn * WN * BK * 2) : 0u;
+  constexpr int ND = NIA + NIB;
 
-    // ------------------------------------------------------ operand setup
-    Operand<NIA> opA;
-    Operand<NIB> opB;
-    if constexpr (Tr::A_KC) {
-      // the tile's rows [row0, row1) of A; rows past row1 read as zero
-      opA.rsrc = make_rsrc(p.a + (long)row0 * p.lda, (uint32_t)((row1 - row0) * p.lda * 2));
-      opA.kstep = 2;
-#pragma unroll
-      for (int u = 0; u < NIA; ++u) {
-        int r, c;
-        kc_rows<NIA>(wave, lane, u, r, c);
-        opA.voff[u] = (uint32_t)(r * p.lda * 2 + c * 16);
-      }
-    } else {  // WGRAD: A[k = row of the group][m]; rows past the group read as zero
-      opA.rsrc = make_rsrc(p.a + (long)kbeg * p.lda, (uint32_t)((kend - kbeg) * p.lda * 2));
-      opA.kstep = (uint32_t)(p.lda * 2);
-#pragma unroll
-      for (int u = 0; u < NIA; ++u) {
-        int r, c;
-        mc_rows<NIA, BM>(wave, lane, u, r, c);
-        const int col = min(m0 + c * 8, p.M - 8);  // tail columns: any in-row data, never stored
-        opA.voff[u] = (uint32_t)(r * p.lda * 2 + col * 2);
-      }
-    }
-    if constexpr (KIND == K_GATEUP_FWD) {
-      // Tile rows interleave 32 gate rows and 32 up rows, so each wave's N
-      // blocks (g, u, g, u) pair gate and up values of the same h columns.
-      const long est = (long)e * p.b_group_stride;
-      opB.rsrc = make_rsrc(p.b0 + est, (uint32_t)(p.I * p.ldb * 2));
-      opB.rsrc2 = make_rsrc(p.b1 + est, (uint32_t)(p.I * p.ldb * 2));
-      opB.kstep = 2;
-#pragma unroll
-      for (int u = 0; u < NIB; ++u) {
-        int r, c;
-        kc_rows<NIB>(wave, lane, u, r, c);
-        const int col = nt * 128 + (r >> 6) * 32 + (r & 31);
-        opB.voff[u] = (uint32_t)(col * p.ldb * 2 + c * 16);
-      }
-    } else if constexpr (KIND == K_DOWN_FWD) {
-      opB.rsrc = make_rsrc(p.b0 + (long)e * p.b_group_stride, (uint32_t)(p.N * p.ldb * 2));
-      opB.kstep = 2;
-#pragma unroll
-      for (int u = 0; u < NIB; ++u) {
-        int r, c;
-        kc_rows<NIB>(wave, lane, u, r, c);
-        opB.voff[u] = (uint32_t)((n0 + r) * p.ldb * 2 + c * 16);
-      }
-    } else if constexpr (KIND == K_DOWN_DGRAD || KIND == K_GATEUP_DGRAD) {
-      // B[k][n] = weight row k, column n (MN-contiguous), whole expert matrix
-      const long est = (long)e * p.b_group_stride;
-      const uint32_t rows = (KIND == K_DOWN_DGRAD) ? (uint32_t)p.K : (uint32_t)p.I;
-      opB.rsrc = make_rsrc(p.b0 + est, rows * (uint32_t)p.ldb * 2);
-      if constexpr (KIND == K_GATEUP_DGRAD) opB.rsrc2 = make_rsrc(p.b1 + est, rows * (uint32_t)p.ldb * 2);
-      opB.kstep = (uint32_t)(p.ldb * 2);
-#pragma unroll
-      for (int u = 0; u < NIB; ++u) {
-        int r, c;
-        mc_rows<NIB, BN>(wave, lane, u, r, c);
-        const int col = min(n0 + c * 8, p.N - 8);
-        opB.voff[u] = (uint32_t)(r * p.ldb * 2 + col * 2);
-      }
-    } else {  // WGRAD B
-      opB.rsrc = make_rsrc(p.b0 + (long)kbeg * p.ldb, (uint32_t)((kend - kbeg) * p.ldb * 2));
-      opB.kstep = (uint32_t)(p.ldb * 2);
-#pragma unroll
-      for (int u = 0; u < NIB; ++u) {
-        int r, c;
-        mc_rows<NIB, BN>(wave, lane, u, r, c);
-        const int col = min(n0 + c * 8, p.N - 8);
-        opB.voff[u] = (uint32_t)(r * p.ldb * 2 + col * 2);
-      }
-    }
+  Tile t = decode_tile<KIND, C>(p, work);
+  Operand<NIA> opA;
+  Operand<NIB> opB;
+  setup_operands<KIND, C>(p, t, wave, lane, opA, opB);
+  if (t.nk > 0) issue_prologue<KIND, C>(p, opA, opB, dma_a, dma_b, t.nk);
+  // Whether the previous tile's epilogue (a known number of memory
+  // operations) was issued after this tile's first DMAs.
+  bool after_epi = false;
 
+  for (;;) {
     f32x16_t acc[MI][NI];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16_t{};
 
-    const int nk = (kend - kbeg + BK - 1) / BK;
-    if (nk > 0) {
-      const uint32_t dma_a = lds_addr(g_lds) + wave * NIA * 1024;  // this wave's DMA area
-      const uint32_t dma_b = lds_addr(g_lds) + kOffB + wave * NIB * 1024;
-      // wave block bases inside a slot
-      // (MC fragment offsets hold the wave's columns themselves)
-      const uint32_t wa = Tr::A_KC ? (uint32_t)(wm * WM * BK * 2) : 0u;
-      const uint32_t wb = Tr::B_KC ? (uint32_t)(wn * WN * BK * 2) : 0u;
-      // Steps 0 .. NST - 2 and the first half of step NST - 1 in flight (the
-      // ones past K dropped); step 0 has landed when only the newer remain.
-      constexpr int ND = NIA + NIB;
-#pragma unroll
-      for (int st = 0; st < NST; ++st) {
-        const uint32_t kill = st < nk ? 0u : kDmaKill;
-#pragma unroll
-        for (int u = 0; u < (st < NST - 1 ? ND : ND / 2); ++u)
-          dma_piece<KIND, C>(p, opA, opB, dma_a + st * kSlotA, dma_b + st * kSlotB, st * BK, kill, u);
-      }
-      wait_vm<(NST - 2) * ND + ND / 2>();
+    if (t.nk > 0) {
+      // Step 0 has landed when only the newer DMAs remain (memory operations
+      // retire in order).  After an epilogue of a known size the wait also
+      // lets those newer operations stay in flight (up to the counter's 63);
+      // otherwise the epilogue's operations only make the wait stronger.
+      constexpr int kFirst = (NST - 2) * ND + ND / 2;
+      constexpr int kEpi = epilogue_vmem_ops<KIND, C>();
+      constexpr int kAfter = kEpi < 0 ? kFirst : (kFirst + kEpi > 63 ? 63 : kFirst + kEpi);
+      if (C::kSepStage && after_epi)
+        wait_vm<kAfter>();
+      else
+        wait_vm<kFirst>();
       lds_barrier();
       // Two fragment sets, no copies between them: f0 holds sub-step 0 (read
       // at the end of the previous step), f1 sub-step 1.
       static_assert(KSUB == 2, "the fragment pipeline below assumes two k16 sub-steps");
       Frags<C> f0, f1;
       load_frags<KIND, C>(f0, 0, wa, kOffB + wb, L);
-      int slot = 0;
-      // One K step per iteration on ring slot `slot`, software pipelined: the
-      // fragments of sub-step 1 are read during the first MFMAs of sub-step 0,
-      // together with the second half of the DMA of step kt + NST - 1 into the
-      // previous slot (every wave finished reading it before the previous
-      // barrier).  Before the MFMAs of sub-step 1 the wave waits for step
-      // kt + 1 to land (barrier); between those MFMAs it starts the first half
-      // of the DMA of step kt + NST into this slot (every wave has finished
-      // reading it) and reads the next step's sub-step 0 fragments.
-      for (int kt = 0; kt < nk; ++kt) {
-        const uint32_t sa = slot * kSlotA + wa, sb = kOffB + slot * kSlotB + wb;
-        const int pslot = slot == 0 ? NST - 1 : slot - 1;
-        mma_read_next<KIND, C>(acc, f0, f1, 1, sa, sb, L, p, opA, opB, dma_a + pslot * kSlotA,
-                               dma_b + pslot * kSlotB, (kt + NST - 1) * BK,
-                               kt + NST - 1 < nk ? 0u : kDmaKill);
-        const int nslot = slot + 1 == NST ? 0 : slot + 1;
-        // Steps kt + 1 .. kt + NST - 1 are in flight; step kt + 1 has landed
-        // when only the newer ones (NIA + NIB loads each) remain.
-        wait_vm<(NST - 2) * (NIA + NIB)>();
-        lds_barrier();  // every wave: step kt + 1 landed, slot `slot` fully read
-        mma_dma_read<KIND, C>(acc, f1, f0, nslot * kSlotA + wa, kOffB + nslot * kSlotB + wb, L,
-                              p, opA, opB, dma_a + slot * kSlotA, dma_b + slot * kSlotB,
-                              (kt + NST) * BK, kt + NST < nk ? 0u : kDmaKill);
-        slot = nslot;
-      }
+      k_steps<KIND, C>(acc, f0, f1, L, p, opA, opB, dma_a, dma_b, wa, wb, t.nk);
       // Every wave is done with the ring, and every DMA (also the dropped
-      // ones, which write zeros) has landed, before the epilogue stages into it.
+      // ones, which write zeros) has landed, before the ring is reused.
       wait_vm<0>();
       lds_barrier();
     }
 
     // ------------------------------------------------------------ epilogue
-    epilogue<KIND, C>(p, acc, e, nt, n0, m0, row0, row1, wave, lane);
-    // The next tile's first DMA overwrites the epilogue's staging area.
+    const int next = work + gridDim.x;
+    const bool more = next < total;
+    Tile tn = t;
+    if constexpr (C::kSepStage) {
+      // the next tile's first steps load during this tile's epilogue
+      if (more) {
+        tn = decode_tile<KIND, C>(p, next);
+        setup_operands<KIND, C>(p, tn, wave, lane, opA, opB);
+        if (tn.nk > 0) issue_prologue<KIND, C>(p, opA, opB, dma_a, dma_b, tn.nk);
+      }
+    }
+    after_epi = C::kSepStage;
+    epilogue<KIND, C>(p, acc, t.e, t.nt, t.n0, t.m0, t.row0, t.row1, wave, lane);
+    // The staging area is reused by the next epilogue (and, for tiles staged
+    // in the ring, overwritten by the next tile's first DMA).
     lds_barrier();
+    if (!more) break;
+    if constexpr (!C::kSepStage) {
+      tn = decode_tile<KIND, C>(p, next);
+      setup_operands<KIND, C>(p, tn, wave, lane, opA, opB);
+      if (tn.nk > 0) issue_prologue<KIND, C>(p, opA, opB, dma_a, dma_b, tn.nk);
+    }
+    t = tn;
+    work = next;
   }
 }
 
