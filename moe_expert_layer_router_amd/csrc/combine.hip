@@ -361,6 +361,33 @@ __global__ __launch_bounds__(256) void dw_router_reduce_kernel(const float* __re
   dw[i] = acc;
 }
 
+// Folded partials, 4 outputs per lane: 64 float4 outputs per workgroup, wave
+// w summing splits w, w + 4, ... (ascending), then the four wave sums in wave
+// order.  Every wave keeps its split loads in flight together.
+__global__ __launch_bounds__(256) void dw_router_reduce4_kernel(const f32x4_t* __restrict__ part,
+                                                                int nsplit, int n4,
+                                                                f32x4_t* __restrict__ dw) {
+  __shared__ f32x4_t s[3][64];
+  const int c = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int i = blockIdx.x * 64 + c;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  if (i < n4) {
+    int sp = w;
+    for (; sp + 12 < nsplit; sp += 16) {  // four splits of this wave at a time
+      const f32x4_t a = part[(size_t)sp * n4 + i], b = part[(size_t)(sp + 4) * n4 + i];
+      const f32x4_t d = part[(size_t)(sp + 8) * n4 + i], e = part[(size_t)(sp + 12) * n4 + i];
+      acc += a;
+      acc += b;
+      acc += d;
+      acc += e;
+    }
+    for (; sp < nsplit; sp += 4) acc += part[(size_t)sp * n4 + i];
+  }
+  if (w > 0) s[w - 1][c] = acc;
+  __syncthreads();
+  if (w == 0 && i < n4) dw[i] = ((acc + s[0][c]) + s[1][c]) + s[2][c];
+}
+
 hipError_t launch_combine(const void* y_perm, const float* topk_w, const int32_t* dest_row,
                           const float* addend, int T, int H, int k, bool bf16, void* y,
                           hipStream_t s) {
@@ -424,8 +451,15 @@ hipError_t launch_dw_router_f32(const float* x, const float* d_logits, int T, in
 
 hipError_t launch_dw_router_reduce(const float* partials, int nsplit, int H, int E, bool folded,
                                    float* dw_router, hipStream_t s) {
-  dw_router_reduce_kernel<<<(H * E + 255) / 256, 256, 0, s>>>(partials, nsplit, H, E,
-                                                               folded ? 1 : 0, dw_router);
+  if (folded && (H * E) % 4 == 0 && ((uintptr_t)dw_router & 15) == 0 &&
+      ((uintptr_t)partials & 15) == 0) {
+    const int n4 = H * E / 4;
+    dw_router_reduce4_kernel<<<(n4 + 63) / 64, 256, 0, s>>>(
+        reinterpret_cast<const f32x4_t*>(partials), nsplit, n4, reinterpret_cast<f32x4_t*>(dw_router));
+  } else {
+    dw_router_reduce_kernel<<<(H * E + 255) / 256, 256, 0, s>>>(partials, nsplit, H, E,
+                                                                 folded ? 1 : 0, dw_router);
+  }
   return hipGetLastError();
 }
 

@@ -66,6 +66,12 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Workgroup barrier that orders LDS only: global loads stay in flight and
+// stores are not waited for (__syncthreads waits for every memory operation).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
 // Logical workgroup id with consecutive ids on the same XCD.  The hardware

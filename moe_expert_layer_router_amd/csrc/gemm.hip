@@ -171,9 +171,6 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // One operand of one tile: buffer resource(s) and, per DMA instruction of this
 // lane, the byte offset at k = 0.
@@ -961,19 +958,27 @@ void gemm_kernel(const GemmArgs p) {
 __global__ __launch_bounds__(kMaxE) void ffn_sched_kernel(const int32_t* __restrict__ offsets,
                                                           int E_l, int rows,
                                                           int32_t* __restrict__ sched) {
-  __shared__ int s[kMaxE + 1];
-  const int e = threadIdx.x;
-  const int n = (e < E_l) ? offsets[e + 1] - offsets[e] : 0;
-  const int tiles = (n + rows - 1) / rows;
-  s[e + 1] = tiles;
+  __shared__ int s[kMaxE + 1];      // s[g] = tiles of experts < g
+  __shared__ int s_off[kMaxE + 1];  // the offsets, in LDS for the tile loop
+  __shared__ int s_wave[kMaxE / kWave];
+  const int e = threadIdx.x, lane = e & (kWave - 1), w = e / kWave;
+  const int o0 = (e < E_l) ? offsets[e] : 0;
+  const int o1 = (e < E_l) ? offsets[e + 1] : 0;
+  s_off[e] = o0;
+  if (e == E_l - 1) s_off[E_l] = o1;
+  int v = (o1 - o0 + rows - 1) / rows;  // this expert's tiles
+  // inclusive scan: within each wave by shuffles, then the waves' totals
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int t = __shfl_up(v, d, kWave);
+    if (lane >= d) v += t;
+  }
+  if (lane == kWave - 1) s_wave[w] = v;
+  __syncthreads();
+  for (int q = 0; q < w; ++q) v += s_wave[q];
+  s[e + 1] = v;
   if (e == 0) s[0] = 0;
   __syncthreads();
-  for (int o = 1; o <= kMaxE; o <<= 1) {  // inclusive scan of s[1..kMaxE]
-    const int v = (e + 1 - o >= 1) ? s[e + 1 - o] : 0;
-    __syncthreads();
-    s[e + 1] += v;
-    __syncthreads();
-  }
   const int count = s[E_l];
   if (e == 0) sched[0] = count;
   for (int i = e; i < count; i += kMaxE) {
@@ -982,10 +987,10 @@ __global__ __launch_bounds__(kMaxE) void ffn_sched_kernel(const int32_t* __restr
       const int mid = (lo + hi + 1) >> 1;
       if (s[mid] <= i) lo = mid; else hi = mid - 1;
     }
-    const int r0 = offsets[lo] + (i - s[lo]) * rows;
+    const int r0 = s_off[lo] + (i - s[lo]) * rows;
     sched[1 + 3 * i] = lo;
     sched[2 + 3 * i] = r0;
-    sched[3 + 3 * i] = min(r0 + rows, offsets[lo + 1]);
+    sched[3 + 3 * i] = min(r0 + rows, s_off[lo + 1]);
   }
 }
 

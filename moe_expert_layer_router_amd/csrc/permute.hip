@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kMaxE) void scan_kernel(const int32_t* __restrict__
                                                      int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ base) {
   constexpr int CH = 32;
-  __shared__ int s[kMaxE];
+  __shared__ int s[kMaxE / kWave];
   const int e = threadIdx.x;
   const bool own = e < E_l;
   int total = 0;
@@ -103,16 +103,19 @@ __global__ __launch_bounds__(kMaxE) void scan_kernel(const int32_t* __restrict__
 #pragma unroll
     for (int u = 0; u < CH; ++u) total += v[u];
   }
-  s[e] = total;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over the kMaxE entries.
-  for (int o = 1; o < kMaxE; o <<= 1) {
-    const int x = (e >= o) ? s[e - o] : 0;
-    __syncthreads();
-    s[e] += x;
-    __syncthreads();
+  // inclusive scan of the totals: within each wave by shuffles, then the
+  // waves' sums
+  const int lane = e & (kWave - 1), w = e / kWave;
+  int incl = total;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int t = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += t;
   }
-  const int excl = s[e] - total;
+  if (lane == kWave - 1) s[w] = incl;
+  __syncthreads();
+  for (int q = 0; q < w; ++q) incl += s[q];
+  const int excl = incl - total;
   if (!own) return;
   counts[e] = total;
   offsets[e] = excl;

@@ -277,6 +277,30 @@ def pair_values(x, idx, w_gate, w_up, w_down, e_lo: int, e_hi: int,
 # Backward
 # --------------------------------------------------------------------------
 
+def router_logit_grad(w, dw, idx, E: int) -> np.ndarray:
+    """dz = dL/dz [T, E] from the gradient dw [T, k] of the kept gate weights.
+
+    The gate weights are a softmax over the kept logits, so for slot j
+    (expert idx[t, j]) the contribution is w_j (dw_j - sum_l w_l dw_l); every
+    other logit gets 0.  Reading: an expert listed in several slots of one
+    token (top-k never does this) receives the sum of its slots'
+    contributions, as the chain rule gives for a logit read several times.
+    """
+    w = _f64(w)
+    dw = _f64(dw)
+    idx = np.asarray(idx).astype(np.int64)
+    T = w.shape[0]
+    inner = np.sum(w * dw, axis=1, keepdims=True)
+    dz = np.zeros((T, E))
+    np.add.at(dz, (np.arange(T)[:, None].repeat(idx.shape[1], 1), idx), w * (dw - inner))
+    return dz
+
+
+def router_input_grad(dz, w_router) -> np.ndarray:
+    """dx_router[t] = W_r dz[t] = sum_e dz[t, e] W_r[:, e]  (logits z = x . W_r)."""
+    return _f64(dz) @ _f64(w_router).T
+
+
 def moe_backward(x, w_router, idx, w, w_gate, w_up, w_down, dy, e_lo: int, e_hi: int
                  ) -> Dict[str, np.ndarray]:
     """Gradients of L = sum(dy * y) for the layer above, hand-derived.
@@ -330,11 +354,8 @@ def moe_backward(x, w_router, idx, w, w_gate, w_up, w_down, dy, e_lo: int, e_hi:
         dWu[e - e_lo] = du.T @ x[tt]
         np.add.at(dx, tt, dg @ Wg + du @ Wu)
 
-    dz = np.zeros((T, E))
-    inner = np.sum(w * dw, axis=1, keepdims=True)
-    np.put_along_axis(dz, idx.astype(np.int64), w * (dw - inner), axis=1)
-    Wr = _f64(w_router)
-    dx += dz @ Wr.T
+    dz = router_logit_grad(w, dw, idx, E)
+    dx += router_input_grad(dz, w_router)
     dWr = x.T @ dz
     return {"dw": dw, "d_logits": dz, "dx": dx, "dw_router": dWr,
             "dw_gate": dWg, "dw_up": dWu, "dw_down": dWd}

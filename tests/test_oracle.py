@@ -347,12 +347,31 @@ def check_finite_differences():
         assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, pos, fd, an)
 
 
+def check_router_grads_vs_autograd():
+    """router_logit_grad against autograd of sum(dw * softmax(z[idx])) (rows with a
+    repeated expert included: that logit is read twice), and router_input_grad
+    against autograd of sum(dz * (x . W_r)) with respect to x."""
+    rng = np.random.default_rng(21)
+    T, E, k, H = 6, 9, 3, 5
+    idx = np.array([[4, 1, 7], [2, 2, 5], [0, 8, 0], [3, 6, 1], [5, 5, 5], [8, 7, 6]])
+    z = torch.tensor(rng.standard_normal((T, E)), requires_grad=True)
+    dw = rng.standard_normal((T, k))
+    w = torch.softmax(z.gather(1, torch.tensor(idx)), dim=1)
+    (w * torch.tensor(dw)).sum().backward()
+    got = O.router_logit_grad(w.detach().numpy(), dw, idx, E)
+    assert _rel(got, z.grad.numpy()) < 1e-13
+    x = torch.tensor(rng.standard_normal((T, H)), requires_grad=True)
+    wr = rng.standard_normal((H, E))
+    (torch.tensor(got) * (x @ torch.tensor(wr))).sum().backward()
+    assert _rel(O.router_input_grad(got, wr), x.grad.numpy()) < 1e-13
+
+
 ALL_CHECKS = [check_gating_golden, check_topk_brute_force, check_zero_input_routing,
               check_duplicate_router_columns, check_k1_and_kE, check_weights_sum_to_one,
               check_counts_offsets, check_permutation_maps, check_permute_unpermute_identity,
               check_dense_equals_routed, check_single_expert_is_swiglu_mlp,
               check_zero_projection_gives_zero, check_scalar_golden, check_backward_vs_autograd,
-              check_finite_differences]
+              check_finite_differences, check_router_grads_vs_autograd]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
@@ -412,13 +431,26 @@ def _mut_ffn_drops_up(v, wg, wu, wd):
     return p
 
 
+def _mut_repeated_expert_overwrites(w, dw, idx, E):
+    w, dw = np.asarray(w, np.float64), np.asarray(dw, np.float64)
+    dz = np.zeros((w.shape[0], E))
+    np.put_along_axis(dz, np.asarray(idx, np.int64), w * (dw - np.sum(w * dw, 1, keepdims=True)), 1)
+    return dz
+
+
+def _mut_router_dx_transposed_sign(dz, w_router):
+    return -np.asarray(dz, np.float64) @ np.asarray(w_router, np.float64).T
+
+
 _ORIG = {n: getattr(OM, n) for n in ("silu", "topk_experts", "gate_weights", "permutation_maps",
                                      "moe_backward", "expert_ffn_parts")}
 
 MUTATIONS = [("silu", _mut_silu_is_sigmoid), ("topk_experts", _mut_topk_ties_high),
              ("gate_weights", _mut_no_renorm), ("permutation_maps", _mut_group_tokens_descending),
              ("moe_backward", _mut_backward_sign), ("moe_backward", _mut_backward_drop_router_dx),
-             ("expert_ffn_parts", _mut_ffn_drops_up)]
+             ("expert_ffn_parts", _mut_ffn_drops_up),
+             ("router_logit_grad", _mut_repeated_expert_overwrites),
+             ("router_input_grad", _mut_router_dx_transposed_sign)]
 
 
 @pytest.mark.parametrize("name,mut", MUTATIONS, ids=[m[1].__name__ for m in MUTATIONS])

@@ -14,6 +14,7 @@ on every token whose k-th/(k+1)-th logit margin exceeds twice that bound.
 Float outputs are compared with the oracle run on the GPU's routing.
 """
 import functools
+import zlib
 
 import numpy as np
 import pytest
@@ -414,6 +415,60 @@ def test_combine_dx_equals_unfused(w):
     assert not bad.any()
     assert torch.equal(fused.view(torch.int16) if w.dtype == "bf16" else fused,
                        g["dx"].view(torch.int16) if w.dtype == "bf16" else g["dx"])
+
+
+# (name, dtype, T, H, E, k, share of local slots, repeated experts)
+DX_CASES = [("bf16_t1000_h192_e24_k3", "bf16", 1000, 192, 24, 3, 0.5, False),
+            ("bf16_t777_h2048_e128_k8", "bf16", 777, 2048, 128, 8, 0.125, False),
+            ("bf16_t130_h264_e40_k16_all_local", "bf16", 130, 264, 40, 16, 1.0, False),
+            ("bf16_t200_h256_e32_k4_repeated_expert", "bf16", 200, 256, 32, 4, 0.5, True),
+            ("bf16_t64_h128_e16_k2_no_local", "bf16", 64, 128, 16, 2, 0.0, False),
+            ("bf16_t300_h256_e64_k20", "bf16", 300, 256, 64, 20, 0.3, False),
+            ("bf16_t300_h256_e20_k4", "bf16", 300, 256, 20, 4, 0.3, False),
+            ("f32_t300_h192_e24_k3", "f32", 300, 192, 24, 3, 0.5, False)]
+
+
+@pytest.mark.parametrize("case", DX_CASES, ids=lambda c: c[0])
+def test_combine_dx_matches_oracle(case):
+    """moe_combine_dx on direct inputs (ragged T and H, k up to 20, tokens with no and
+    with all slots local, an expert repeated within a token's list) against the
+    oracle's unpermute plus router input gradient.  Elementwise bound: one rounding
+    of the output (2^-8 |ref| covers bf16's half ulp) plus 2^-14 of the sum of
+    absolute terms (fp32 accumulation)."""
+    name, dtype, T, H, E, k, share, repeat = case
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    if repeat:
+        idx[::3, 1] = idx[::3, 0]
+        idx[::5, k - 1] = idx[::5, 0]
+    local = rng.random((T, k)) < share
+    R = int(local.sum())
+    dest = np.full(T * k, -1, np.int32)
+    dest[local.reshape(-1)] = rng.permutation(R).astype(np.int32)
+    tw = rng.random((T, k)) + 0.1
+    tw /= tw.sum(1, keepdims=True)
+    dtw = rng.standard_normal((T, k))
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dxp = _dev(rng.standard_normal((max(R, 1), H)), dt)
+    wr = _dev(rng.standard_normal((H, E)) / np.sqrt(H), dt)
+    g_tw = _dev(tw, torch.float32)
+    g_dtw = _dev(dtw, torch.float32)
+    g_idx = torch.from_numpy(idx).to(DEV)
+    g_dest = torch.from_numpy(dest).to(DEV)
+    print(f"  case {name}: T={T} H={H} E={E} k={k} R={R}", flush=True)
+    dx = moe.moe_combine_dx(dxp, g_dest, g_dtw, g_tw, g_idx, wr)
+    torch.cuda.synchronize()
+    tw64, dtw64 = _np(g_tw), _np(g_dtw)
+    dxp64, wr64 = _np(dxp)[:R], _np(wr)
+    dz = O.router_logit_grad(tw64, dtw64, idx, E)
+    ref = O.unpermute_rows(dxp64, dest, T) + O.router_input_grad(dz, wr64)
+    absref = O.unpermute_rows(np.abs(dxp64), dest, T) + O.router_input_grad(np.abs(dz), np.abs(wr64))
+    got = _np(dx)
+    rel = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -22
+    bound = rel * np.abs(ref) + 2.0 ** -14 * absref + 1e-30
+    err = np.abs(got - ref)
+    print(f"  max err {err.max():.3g}, max err / bound {(err / bound).max():.3g}", flush=True)
+    assert (err <= bound).all()
 
 
 def test_weight_grad_accumulate():
