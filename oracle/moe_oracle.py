@@ -274,6 +274,134 @@ def pair_values(x, idx, w_gate, w_up, w_down, e_lo: int, e_hi: int,
 
 
 # --------------------------------------------------------------------------
+# FP8 variant of the expert FFN (forward)
+# --------------------------------------------------------------------------
+# The pages name FP8 as their only kernel-level speed lever (page
+# "Qwen3-MoE-30B-A3B模型EP+FSDP2并行方案", the closing throughput table) and
+# fix no format or scaling.  Readings used here:
+#   - format OCP FP8 E4M3 ("fn": no infinities, one NaN code per sign, largest
+#     finite 448, smallest subnormal 2^-9);
+#   - every row (a token of the activations, an output channel of a weight
+#     matrix, a row of h) has its own power-of-two scale s = 2^e with e the
+#     smallest integer such that max|row| <= 448 * 2^e (e = 0 for a zero row);
+#     a value v is stored as the code of v / s rounded to nearest, ties to
+#     even.  Dividing by a power of two is exact, so the codes do not depend
+#     on the precision the division runs in;
+#   - products accumulate the exact products of the codes' values, and the
+#     row scale times the column scale multiplies the sum;
+#   - h = SiLU(g) * u is rounded to bf16 (as the bf16 layer stores it) before
+#     its rows are quantized for the down projection.
+
+def fp8_e4m3_decode(codes) -> np.ndarray:
+    """Value of each E4M3 code: sign bit 7, exponent bits 6..3 (bias 7),
+    mantissa bits 2..0; exponent 0 is subnormal (m * 2^-9); 0x7f / 0xff NaN."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    ex = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(ex == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(ex.astype(np.float64) - 7.0))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def fp8_e4m3_encode(v) -> np.ndarray:
+    """Code of the E4M3 value nearest to v (ties to the even mantissa), for
+    finite |v| <= 448; -0.0 and negative values that round to zero keep the
+    sign bit."""
+    v = _f64(v)
+    if not np.all(np.abs(v) <= 448.0):
+        raise ValueError("fp8_e4m3_encode: |v| > 448 or NaN")
+    neg = np.signbit(v)
+    a = np.abs(v)
+    # round the magnitude to 3 mantissa bits in its binade (binades below
+    # 2^-6 share the subnormal spacing 2^-9); a / spacing is exact
+    _, fe = np.frexp(a)                         # a = f * 2^fe, f in [0.5, 1)
+    spacing = np.exp2(np.maximum(fe - 1, -6) - 3.0)
+    mag = np.rint(a / spacing) * spacing        # ties to even; may carry into the next binade
+    sub = mag < 2.0 ** -6
+    _, fe2 = np.frexp(mag)
+    mant = np.where(sub, mag * 2.0 ** 9, mag / np.exp2(fe2 - 4.0) - 8)
+    bexp = np.where(sub, 0, fe2 - 1 + 7)
+    code = (bexp.astype(np.int64) << 3) | mant.astype(np.int64)
+    return (code | np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+def fp8_row_exponent(amax) -> np.ndarray:
+    """Smallest integer e with amax <= 448 * 2^e (0 where amax == 0).  With
+    amax = f * 2^E (f in [0.5, 1)) and 448 = 0.875 * 2^9 this is
+    E - 9, plus 1 when f > 0.875."""
+    amax = _f64(amax)
+    f, E = np.frexp(amax)
+    e = E - 9 + (f > 0.875).astype(np.int64)
+    return np.where(amax == 0, 0, e).astype(np.int64)
+
+
+def quantize_rows_fp8(a):
+    """Per-row power-of-two scaled E4M3 codes of a [rows, cols]:
+    returns (codes uint8 [rows, cols], scale float64 [rows] = 2^e)."""
+    a = _f64(a)
+    e = fp8_row_exponent(np.max(np.abs(a), axis=1) if a.shape[1] else np.zeros(a.shape[0]))
+    s = np.exp2(e.astype(np.float64))
+    return fp8_e4m3_encode(a / s[:, None]), s
+
+
+def fp8_matmul_rows(aq, sa, bq, sb) -> np.ndarray:
+    """(sa_r * codes_a[r]) . (sb_n * codes_b[n])  for row-scaled operands
+    a [M, K] and b [N, K]: the sum of the codes' exact products, times
+    sa[r] * sb[n]."""
+    acc = fp8_e4m3_decode(aq) @ fp8_e4m3_decode(bq).T
+    return acc * _f64(sa)[:, None] * _f64(sb)[None, :]
+
+
+def round_bf16(a) -> np.ndarray:
+    """a rounded to the nearest bfloat16 (ties to even), as float64."""
+    a32 = np.asarray(a, dtype=np.float32)
+    bits = a32.view(np.uint32).astype(np.uint64)
+    bits = (bits + 0x7FFF + ((bits >> 16) & 1)) >> 16 << 16
+    return bits.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def expert_ffn_fp8_parts(vq, sv, wgq, sg, wuq, su, wdq, sd) -> Dict[str, np.ndarray]:
+    """One expert on quantized rows (vq, sv): g, u from the row-scaled
+    products with the quantized gate / up weights, h = bf16(SiLU(g) * u),
+    its rows quantized (hq, sh), y = the down product with (wdq, sd)."""
+    g = fp8_matmul_rows(vq, sv, wgq, sg)
+    u = fp8_matmul_rows(vq, sv, wuq, su)
+    h = round_bf16(silu(g) * u)
+    hq, sh = quantize_rows_fp8(h)
+    y = fp8_matmul_rows(hq, sh, wdq, sd)
+    return {"g": g, "u": u, "h": h, "hq": hq, "sh": sh, "y": y}
+
+
+def quantize_expert_weights_fp8(w):
+    """Row-scaled codes of an expert weight stack [E_l, N, K]: codes [E_l, N, K]
+    and scales [E_l, N] (each output channel its own scale)."""
+    w = _f64(w)
+    El, N, K = w.shape
+    q, s = quantize_rows_fp8(w.reshape(El * N, K))
+    return q.reshape(El, N, K), s.reshape(El, N)
+
+
+def moe_forward_fp8(x, idx, w, w_gate, w_up, w_down, e_lo: int, e_hi: int) -> np.ndarray:
+    """The forward of moe_forward with the FP8 recipe above: tokens quantized
+    per row once, weights per output channel, h per row; the gate-weighted
+    sum over local slots as in moe_forward."""
+    xq, sx = quantize_rows_fp8(x)
+    gq, gs = quantize_expert_weights_fp8(w_gate)
+    uq, us = quantize_expert_weights_fp8(w_up)
+    dq, ds = quantize_expert_weights_fp8(w_down)
+    y = np.zeros(_f64(x).shape)
+    for e in range(e_lo, e_hi):
+        tt, jj = _local_slots(idx, e_lo, e_hi, e)
+        if len(tt) == 0:
+            continue
+        i = e - e_lo
+        ye = expert_ffn_fp8_parts(xq[tt], sx[tt], gq[i], gs[i], uq[i], us[i], dq[i], ds[i])["y"]
+        np.add.at(y, tt, _f64(w)[tt, jj][:, None] * ye)
+    return y
+
+
+# --------------------------------------------------------------------------
 # Backward
 # --------------------------------------------------------------------------
 

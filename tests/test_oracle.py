@@ -366,12 +366,99 @@ def check_router_grads_vs_autograd():
     assert _rel(O.router_input_grad(got, wr), x.grad.numpy()) < 1e-13
 
 
+def check_fp8_codes_vs_torch():
+    """E4M3 decode of all 256 codes and encode of random values, every code's value
+    and every midpoint between neighbours, against torch's float8_e4m3fn."""
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    dec = O.fp8_e4m3_decode(codes)
+    assert np.array_equal(np.isnan(ref), np.isnan(dec))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], dec[ok])
+    assert dec[0x7E] == 448.0 and dec[0x01] == 2.0 ** -9 and dec[0x08] == 2.0 ** -6
+    vals = np.sort(dec[ok & (dec >= 0)])
+    rng = np.random.default_rng(5)
+    v = np.concatenate([rng.uniform(-448, 448, 4000), rng.uniform(-0.03, 0.03, 4000), vals, -vals,
+                        (vals[:-1] + vals[1:]) / 2, -(vals[:-1] + vals[1:]) / 2])
+    v = v.astype(np.float32).astype(np.float64)
+    got = O.fp8_e4m3_encode(v)
+    exp = torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, exp)
+
+
+def check_fp8_row_scale_is_minimal():
+    """Per-row exponent: amax <= 448 * 2^e and amax > 448 * 2^(e - 1) (brute force over
+    values at, just below and just above the boundaries); zero rows get e = 0."""
+    rng = np.random.default_rng(6)
+    b = 448.0 * np.exp2(np.arange(-30, 30, dtype=np.float64))
+    amax = np.concatenate([b, np.nextafter(b, 0), np.nextafter(b, np.inf), rng.uniform(1e-6, 1e6, 500)])
+    e = O.fp8_row_exponent(amax)
+    assert np.all(amax <= 448.0 * np.exp2(e.astype(np.float64)))
+    assert np.all(amax > 448.0 * np.exp2(e.astype(np.float64) - 1))
+    assert O.fp8_row_exponent(np.array([0.0]))[0] == 0
+    a = rng.standard_normal((7, 33)) * np.exp2(rng.integers(-20, 20, size=(7, 1)))
+    a[3] = 0.0
+    q, sc = O.quantize_rows_fp8(a)
+    back = O.fp8_e4m3_decode(q) * sc[:, None]
+    # each value within half a step of its binade (relative 2^-4 for normals)
+    assert np.all(np.abs(back - a) <= np.maximum(2.0 ** -4 * np.abs(a), sc[:, None] * 2.0 ** -10))
+    assert np.all(np.abs(O.fp8_e4m3_decode(q)).max(axis=1)[[0, 1, 2, 4, 5, 6]] >= 224.0)
+    assert (q[3] == 0).all() and sc[3] == 1.0
+
+
+def check_fp8_matmul_brute_force():
+    """fp8_matmul_rows against a per-element loop over decoded codes, with distinct
+    row and column scales (catches a scale on the wrong axis)."""
+    rng = np.random.default_rng(7)
+    aq = rng.integers(0, 256, size=(5, 9)).astype(np.uint8)
+    bq = rng.integers(0, 256, size=(4, 9)).astype(np.uint8)
+    aq[(aq & 0x7F) == 0x7F] = 0x3C
+    bq[(bq & 0x7F) == 0x7F] = 0x41
+    sa = np.exp2(rng.integers(-5, 5, size=5).astype(np.float64))
+    sb = np.exp2(rng.integers(-5, 5, size=4).astype(np.float64))
+    got = O.fp8_matmul_rows(aq, sa, bq, sb)
+    da, db = O.fp8_e4m3_decode(aq), O.fp8_e4m3_decode(bq)
+    for r in range(5):
+        for n in range(4):
+            ref = sum(da[r, k] * db[n, k] for k in range(9)) * sa[r] * sb[n]
+            assert abs(got[r, n] - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
+def check_fp8_forward_close_to_exact():
+    """The FP8 forward stays near the exact forward: four quantized operands (x, the
+    gate / up weights, h, the down weights), each rounded within 2^-4 relative, give
+    a rel-L2 well under 12% (an unapplied scale or a dropped factor lands far
+    outside).  And on operands that lie on the E4M3 grid with row maximum 448 (scale
+    1), the quantized gate / up products equal the plain fp64 ones exactly."""
+    w, inp = _tiny(T=64, k=2)
+    z, idx, gw = O.route(inp["x"], inp["w_router"], w.k)
+    ref = O.moe_forward(inp["x"], idx, gw, inp["w_gate"], inp["w_up"], inp["w_down"], 0, w.E)
+    got = O.moe_forward_fp8(inp["x"], idx, gw, inp["w_gate"], inp["w_up"], inp["w_down"], 0, w.E)
+    assert _rel(got, ref) < 0.12
+    rng = np.random.default_rng(8)
+    grid = O.fp8_e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    pick = lambda *sh: rng.choice(np.concatenate([grid, -grid]), size=sh)
+    x, wg, wu, wd = pick(6, 16), pick(1, 8, 16), pick(1, 8, 16), pick(1, 16, 8)
+    for a in (x, wg[0], wu[0], wd[0]):
+        a[:, 0] = 448.0
+    xq, sx = O.quantize_rows_fp8(x)
+    assert (sx == 1.0).all()
+    qg, sg = O.quantize_expert_weights_fp8(wg)
+    qu, su = O.quantize_expert_weights_fp8(wu)
+    qd, sd = O.quantize_expert_weights_fp8(wd)
+    parts = O.expert_ffn_fp8_parts(xq, sx, qg[0], sg[0], qu[0], su[0], qd[0], sd[0])
+    exact = O.expert_ffn_parts(x, wg[0], wu[0], wd[0])
+    assert np.array_equal(parts["g"], exact["g"]) and np.array_equal(parts["u"], exact["u"])
+
+
 ALL_CHECKS = [check_gating_golden, check_topk_brute_force, check_zero_input_routing,
               check_duplicate_router_columns, check_k1_and_kE, check_weights_sum_to_one,
               check_counts_offsets, check_permutation_maps, check_permute_unpermute_identity,
               check_dense_equals_routed, check_single_expert_is_swiglu_mlp,
               check_zero_projection_gives_zero, check_scalar_golden, check_backward_vs_autograd,
-              check_finite_differences, check_router_grads_vs_autograd]
+              check_finite_differences, check_router_grads_vs_autograd, check_fp8_codes_vs_torch,
+              check_fp8_row_scale_is_minimal, check_fp8_matmul_brute_force,
+              check_fp8_forward_close_to_exact]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
@@ -442,15 +529,39 @@ def _mut_router_dx_transposed_sign(dz, w_router):
     return -np.asarray(dz, np.float64) @ np.asarray(w_router, np.float64).T
 
 
+def _mut_fp8_round_half_away(v):
+    v = np.asarray(v, np.float64)
+    out = _ORIG["fp8_e4m3_encode"](v)
+    dec = OM.fp8_e4m3_decode(out)
+    nxt = OM.fp8_e4m3_decode(np.where(out & 0x7F == 0x7E, out, out + 1).astype(np.uint8))
+    tie = np.abs(np.abs(v) - (np.abs(dec) + np.abs(nxt)) / 2) == 0
+    return np.where(tie & (np.abs(v) > np.abs(dec)), out + 1, out).astype(np.uint8)
+
+
+def _mut_fp8_exponent_one_high(amax):
+    e = _ORIG["fp8_row_exponent"](amax)
+    return np.where(np.asarray(amax) == 0, 0, e + 1)
+
+
+def _mut_fp8_scale_wrong_axis(aq, sa, bq, sb):
+    acc = OM.fp8_e4m3_decode(aq) @ OM.fp8_e4m3_decode(bq).T
+    n = min(len(sa), len(sb))
+    return acc * np.asarray(sa, np.float64)[:, None] * np.asarray(sb, np.float64)[:n].mean()
+
+
 _ORIG = {n: getattr(OM, n) for n in ("silu", "topk_experts", "gate_weights", "permutation_maps",
-                                     "moe_backward", "expert_ffn_parts")}
+                                     "moe_backward", "expert_ffn_parts", "fp8_e4m3_encode",
+                                     "fp8_row_exponent")}
 
 MUTATIONS = [("silu", _mut_silu_is_sigmoid), ("topk_experts", _mut_topk_ties_high),
              ("gate_weights", _mut_no_renorm), ("permutation_maps", _mut_group_tokens_descending),
              ("moe_backward", _mut_backward_sign), ("moe_backward", _mut_backward_drop_router_dx),
              ("expert_ffn_parts", _mut_ffn_drops_up),
              ("router_logit_grad", _mut_repeated_expert_overwrites),
-             ("router_input_grad", _mut_router_dx_transposed_sign)]
+             ("router_input_grad", _mut_router_dx_transposed_sign),
+             ("fp8_e4m3_encode", _mut_fp8_round_half_away),
+             ("fp8_row_exponent", _mut_fp8_exponent_one_high),
+             ("fp8_matmul_rows", _mut_fp8_scale_wrong_axis)]
 
 
 @pytest.mark.parametrize("name,mut", MUTATIONS, ids=[m[1].__name__ for m in MUTATIONS])
