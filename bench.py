@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (vector/matrix)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
@@ -161,6 +162,104 @@ def cpu_baseline(w, inp, target_s=12.0):
                       f"{'forward+backward' if w.train else 'forward'}"}
 
 
+def _kernel_avg_us(moe, torch, kid, fn, n):
+    """Average duration of kernel `kid` over n calls of fn (library events on its stream)."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    stops = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in starts + stops:
+        e.record()
+    torch.cuda.synchronize()
+    arr_s = (ctypes.c_void_p * n)(*[ctypes.c_void_p(e.cuda_event) for e in starts])
+    arr_e = (ctypes.c_void_p * n)(*[ctypes.c_void_p(e.cuda_event) for e in stops])
+    moe.lib.moe_profile_kernel(kid, arr_s, arr_e, n)
+    for _ in range(n):
+        fn()
+    torch.cuda.synchronize()
+    cnt = moe.lib.moe_profile_recorded()
+    moe.lib.moe_profile_kernel(-1, None, None, 0)
+    return sum(starts[i].elapsed_time(stops[i]) * 1e3 for i in range(cnt)) / max(cnt, 1)
+
+
+def fp8_ffn_bench(w, args):
+    """Grouped SwiGLU FFN forward, bf16 versus the FP8 recipe (E4M3 codes, one
+    power-of-two scale per row), on the routing of the bf16 router.  FLOPs are
+    the algorithmic 6 R H I of the FFN; the FP8 time includes its schedule, row-
+    scale gather and the quantization of h (the activation quantization before
+    the permute is timed on its own)."""
+    import torch
+
+    import moe_expert_layer_router_amd as moe
+    from workloads import make_inputs
+
+    dev = torch.device("cuda:0")
+    inp = make_inputs(w)
+    t = {n: torch.from_numpy(v).to(dev).to(torch.bfloat16).contiguous() for n, v in inp.items()
+         if n not in ("bias", "dy")}
+    bias = torch.from_numpy(inp["bias"]).to(dev) if "bias" in inp else None
+    idx, _, _ = moe.moe_route(t["x"], t["w_router"], w.k, bias=bias)
+    pb = moe.moe_permute(t["x"], idx, w.E, w.e_lo, w.e_hi)
+    xq, sx = moe.moe_quantize_fp8(t["x"])
+    pq = moe.moe_permute(xq, idx, w.E, w.e_lo, w.e_hi)
+    wq = {}
+    for n in ("w_gate", "w_up", "w_down"):
+        El, N, K = t[n].shape
+        q, s8 = moe.moe_quantize_fp8(t[n].view(El * N, K))
+        wq[n] = (q.view(El, N, K), s8.view(El, N))
+    torch.cuda.synchronize()
+    R = int(pb["offsets"][-1].item())
+    ob = moe.moe_grouped_ffn_fwd(pb["x_perm"], pb["offsets"], t["w_gate"], t["w_up"], t["w_down"],
+                                 save_gu=False)
+    o8 = moe.moe_grouped_ffn_fwd_fp8(pq["x_perm"], sx, pq["src_row"], pq["offsets"], wq["w_gate"],
+                                     wq["w_up"], wq["w_down"])
+    f_b = lambda: moe.moe_grouped_ffn_fwd(pb["x_perm"], pb["offsets"], t["w_gate"], t["w_up"],
+                                          t["w_down"], save_gu=False, out=ob)
+    f_8 = lambda: moe.moe_grouped_ffn_fwd_fp8(pq["x_perm"], sx, pq["src_row"], pq["offsets"],
+                                              wq["w_gate"], wq["w_up"], wq["w_down"], out=o8)
+    f_q = lambda: moe.moe_quantize_fp8(t["x"], out={"q": xq, "scale": sx})
+
+    def timed(fn, n):
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    n = args.steps
+    us_b, us_8, us_q = timed(f_b, n), timed(f_8, n), timed(f_q, n)
+    flops = 6.0 * R * w.H * w.I
+    kern = {}
+    for name, kid, fl in (("FFN_GATEUP", 4, 4.0 * R * w.H * w.I), ("FFN_DOWN", 5, 2.0 * R * w.H * w.I)):
+        for tag, fn, peak in (("bf16", f_b, PEAK_BF16_TFLOPS), ("fp8", f_8, PEAK_FP8_TFLOPS)):
+            avg = _kernel_avg_us(moe, torch, kid, fn, n)
+            ach = fl / (avg * 1e-6) / 1e12
+            kern[f"{name}_{tag}"] = {"avg_us": round(avg, 2), "achieved_tflops": round(ach, 1),
+                                     "peak_tflops": peak, "frac": round(ach / peak, 4)}
+    tf8 = flops / (us_8 * 1e-6) / 1e12
+    dom = max(("FFN_GATEUP_fp8", "FFN_DOWN_fp8"), key=lambda k: kern[k]["avg_us"])
+    return {
+        "metric": "grouped expert FFN forward TFLOP/s, FP8 recipe vs bf16",
+        "value": round(tf8, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": n, "warmup": args.warmup,
+        "higher_is_better": True, "vs_baseline": None,
+        "dtype": "fp8 e4m3 operands (row scales), fp32 accumulate, bf16 out",
+        "data": "synthetic (seeded normal draws, random-init weights)",
+        "config": {"workload": w.name, "T": w.T, "H": w.H, "I": w.I, "E": w.E, "k": w.k,
+                   "local_experts": [w.e_lo, w.e_hi], "routed_rows": R},
+        "us_per_ffn_forward": {"fp8": round(us_8, 2), "bf16": round(us_b, 2)},
+        "bf16_tflops": round(flops / (us_b * 1e-6) / 1e12, 2),
+        "speedup_vs_bf16": round(us_b / us_8, 3),
+        "activation_quantize_us": round(us_q, 2),
+        "kernels": kern,
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": kern[dom]["achieved_tflops"],
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": kern[dom]["frac"],
+                     "traffic": None},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +269,9 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-times", action="store_true")
+    ap.add_argument("--fp8-ffn", action="store_true",
+                    help="instead of the layer step: time the grouped FFN forward in bf16 and in the "
+                         "FP8 recipe on the same routing (default workload: the full 128-expert layer)")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="after the warm-up, copy 256 MiB device to device once (outside the timed "
                          "region): the copy kernel's FETCH_SIZE / WRITE_SIZE calibrate counter runs")
@@ -186,6 +288,11 @@ def main():
 
     import moe_expert_layer_router_amd as moe
     from workloads import WORKLOADS, make_inputs
+
+    if args.fp8_ffn:
+        wl = args.workload if args.workload != ap.get_default("workload") else "full_t16384_h2048_i768_e128_k8"
+        print(json.dumps(fp8_ffn_bench(WORKLOADS[wl], args)), flush=True)
+        return
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")

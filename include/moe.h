@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -56,7 +56,8 @@ typedef enum {
   MOE_EHIP = -4           /* a HIP launch failed; see moe_last_error() */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+/* MOE_FP8: one byte per value (E4M3 codes); accepted by moe_permute only. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8 = 2 } moe_dtype;
 
 typedef enum {
   MOE_OP_ROUTE = 0,
@@ -64,7 +65,8 @@ typedef enum {
   MOE_OP_FFN_FWD = 2,
   MOE_OP_FFN_BWD = 3,
   MOE_OP_ROUTE_BWD = 4,
-  MOE_OP_COMBINE_DX = 5
+  MOE_OP_COMBINE_DX = 5,
+  MOE_OP_FFN_FWD_FP8 = 6
 } moe_op;
 
 /* Returns MOE_ABI_VERSION of the loaded library. */
@@ -112,7 +114,8 @@ int moe_route_from_logits(const float* logits, int T, int E, int k, int32_t* top
  *   dest_row [T*k]   int32: grouped row of slot (t,j), or -1 if not local
  *   src_row  [T*k]   int32: token of grouped row r, for r < R
  *   x_perm   [T*k,H] dtype: x_perm[dest_row[t*k+j]] = x[t], bitwise
- *   ws       MOE_OP_PERMUTE workspace */
+ *   ws       MOE_OP_PERMUTE workspace
+ * dtype MOE_FP8 moves rows of H one-byte codes (H % 16 == 0). */
 int moe_permute(const void* x, const int32_t* topk_idx, int T, int H, int E, int k, int e_lo,
                 int e_hi, int dtype, int32_t* counts, int32_t* offsets, int32_t* dest_row,
                 int32_t* src_row, void* x_perm, void* ws, size_t ws_bytes, void* stream);
@@ -130,6 +133,45 @@ int moe_grouped_ffn_fwd(const void* x_perm, const int32_t* offsets, int E_l, int
                         int I, const void* w_gate, const void* w_up, const void* w_down, int dtype,
                         void* gu_saved, void* h_perm, void* y_perm, void* ws, size_t ws_bytes,
                         void* stream);
+
+/* FP8 recipe of the expert FFN.  The pages name FP8 as their only
+ * kernel-level speed lever (page "Qwen3-MoE-30B-A3B模型EP+FSDP2并行方案",
+ * closing throughput table) and fix no format or scaling; this library's
+ * reading: OCP E4M3 codes (largest finite 448, subnormals down to 2^-9), one
+ * power-of-two scale per row (token row of the activations, output channel of
+ * a weight matrix, row of h).
+ *
+ * Row quantization: for each row i < rows (and i < *nrows when nrows is not
+ * NULL; nrows is a DEVICE pointer, e.g. offsets + E_l), scale[i] = 2^e with e
+ * the smallest integer such that max_c |src[i,c]| <= 448 * 2^e (e = 0 for a
+ * zero row), and q[i,c] = the E4M3 code nearest to src[i,c] / scale[i], ties
+ * to even (the division is exact).  Rows >= *nrows are not written.
+ *   src [rows,cols] MOE_BF16 or MOE_F32, q [rows,cols] uint8, scale [rows] fp32
+ *   cols % 16 == 0; src and q 16-byte aligned. */
+int moe_quantize_fp8(const void* src, int rows, int cols, int dtype, const int32_t* nrows,
+                     uint8_t* q, float* scale, void* stream);
+
+/* Grouped SwiGLU expert FFN, forward, on E4M3 codes.  With x_q the permuted
+ * code rows (moe_permute with MOE_FP8 of moe_quantize_fp8's token rows) and
+ * x_scale the per-TOKEN scales (row r uses x_scale[src_row[r]]):
+ *   g[r,n] = x_scale[src_row[r]] * wg_scale[e,n] * sum_c code(x_q[r,c]) code(wg_q[e,n,c])
+ *   (u likewise with wu), h_perm[r] = bf16(SiLU(g) * u),
+ *   h's rows quantized as moe_quantize_fp8 does (codes and scales in ws),
+ *   y_perm[r,m] = sh[r] * wd_scale[e,m] * sum_i code(hq[r,i]) code(wd_q[e,m,i])
+ * Code products are exact and summed in fp32; outputs are rounded once.
+ *   x_q [R_cap,H] uint8, x_scale [T] fp32, src_row [R_cap] int32,
+ *   wg_q / wu_q [E_l,I,H] uint8 with wg_scale / wu_scale [E_l,I] fp32,
+ *   wd_q [E_l,H,I] uint8 with wd_scale [E_l,H] fp32,
+ *   gu_saved [R_cap,2I] bf16 or NULL (g, u as in moe_grouped_ffn_fwd),
+ *   h_perm [R_cap,I] bf16, y_perm [R_cap,H] bf16
+ *   ws       MOE_OP_FFN_FWD_FP8 workspace (schedule, row scales, codes of h)
+ * Needs H % 128 == 0 and I % 128 == 0 (else MOE_EUNSUPPORTED). */
+int moe_grouped_ffn_fwd_fp8(const uint8_t* x_q, const float* x_scale, const int32_t* src_row,
+                            const int32_t* offsets, int E_l, int R_cap, int H, int I,
+                            const uint8_t* wg_q, const float* wg_scale, const uint8_t* wu_q,
+                            const float* wu_scale, const uint8_t* wd_q, const float* wd_scale,
+                            void* gu_saved, void* h_perm, void* y_perm, void* ws, size_t ws_bytes,
+                            void* stream);
 
 /* Weighted unpermute ("combine"): for every token, in slot order j = 0..k-1,
  *   y[t] = sum_{j: dest_row[t*k+j] >= 0} topk_w[t,j] * y_perm[dest_row[t*k+j]]  (+ addend[t])

@@ -8,7 +8,8 @@ library is missing, and every call raises MoEError when the library reports
 an error.
 
 Functions keep the C names (moe_route, moe_permute, moe_grouped_ffn_fwd,
-moe_combine, moe_combine_bwd, moe_grouped_ffn_bwd, moe_route_bwd) and return
+moe_combine, moe_combine_bwd, moe_grouped_ffn_bwd, moe_route_bwd, and the FP8
+forward: moe_quantize_fp8, moe_grouped_ffn_fwd_fp8) and return
 freshly allocated torch tensors; each also accepts preallocated outputs via
 ``out=`` dictionaries so that steady-state loops allocate nothing.
 """
@@ -23,10 +24,10 @@ import torch  # loads torch's HIP runtime first, so libmoe binds to the same one
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-MOE_F32, MOE_BF16 = 0, 1
+MOE_F32, MOE_BF16, MOE_FP8 = 0, 1, 2
 (MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD, MOE_OP_ROUTE_BWD,
- MOE_OP_COMBINE_DX) = range(6)
-ABI_VERSION = 1
+ MOE_OP_COMBINE_DX, MOE_OP_FFN_FWD_FP8) = range(7)
+ABI_VERSION = 2
 
 
 class MoEError(RuntimeError):
@@ -53,6 +54,9 @@ def _load():
         "moe_grouped_ffn_bwd": ([P, P, P, P, P, I32, I32, I32, I32, P, P, P, I32, P, P, P, P, I32,
                                  P, SZ, P], I32),
         "moe_route_bwd": ([P, P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, SZ, P], I32),
+        "moe_quantize_fp8": ([P, I32, I32, I32, P, P, P, P], I32),
+        "moe_grouped_ffn_fwd_fp8": ([P, P, P, P, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, P,
+                                     SZ, P], I32),
         "moe_profile_kernel": ([I32, ctypes.POINTER(P), ctypes.POINTER(P), I32], I32),
         "moe_profile_recorded": ([], I32),
     }
@@ -99,6 +103,8 @@ def _dtype_code(t: torch.Tensor) -> int:
         return MOE_BF16
     if t.dtype == torch.float32:
         return MOE_F32
+    if t.dtype == torch.uint8:  # E4M3 codes
+        return MOE_FP8
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
@@ -303,3 +309,48 @@ def moe_route_bwd(d_topk_w: torch.Tensor, topk_w: torch.Tensor, topk_idx: torch.
 
 
 from .layer import MoELayer  # noqa: E402,F401
+
+
+def moe_quantize_fp8(src: torch.Tensor, nrows: Optional[torch.Tensor] = None,
+                     out: Optional[Dict[str, torch.Tensor]] = None):
+    """E4M3 codes of the rows of src [rows, cols] (bf16 / fp32), one power-of-two scale
+    per row.  nrows: optional int32 device tensor whose first element bounds the
+    rows written.  Returns (q uint8 [rows, cols], scale fp32 [rows])."""
+    rows, cols = src.shape
+    o = dict(out or {})
+    o.setdefault("q", torch.empty((rows, cols), dtype=torch.uint8, device=src.device))
+    o.setdefault("scale", torch.empty(rows, dtype=torch.float32, device=src.device))
+    _check(lib.moe_quantize_fp8(_ptr(src), rows, cols, _dtype_code(src), _ptr(nrows), _ptr(o["q"]),
+                                _ptr(o["scale"]), _stream()), "moe_quantize_fp8")
+    return o["q"], o["scale"]
+
+
+def moe_grouped_ffn_fwd_fp8(x_q: torch.Tensor, x_scale: torch.Tensor, src_row: torch.Tensor,
+                            offsets: torch.Tensor, wg: tuple, wu: tuple, wd: tuple,
+                            save_gu: bool = False, ws: Optional[torch.Tensor] = None,
+                            out: Optional[Dict[str, torch.Tensor]] = None):
+    """Grouped SwiGLU FFN forward on E4M3 codes.  x_q [R_cap, H] uint8 (permuted
+    rows), x_scale [T] per-token scales, src_row [R_cap]; wg / wu / wd = (codes
+    uint8 [E_l, N, K], scales fp32 [E_l, N]).  Returns dict h_perm, y_perm (bf16)
+    and gu (or None)."""
+    R_cap, H = x_q.shape
+    E_l, I, _ = wg[0].shape
+    dev = x_q.device
+    o = dict(out or {})
+    o.setdefault("h_perm", torch.empty((R_cap, I), dtype=torch.bfloat16, device=dev))
+    o.setdefault("y_perm", torch.empty((R_cap, H), dtype=torch.bfloat16, device=dev))
+    if save_gu:
+        o.setdefault("gu", torch.empty((R_cap, 2 * I), dtype=torch.bfloat16, device=dev))
+    else:
+        o["gu"] = None
+    nb = lib.moe_workspace_bytes(MOE_OP_FFN_FWD_FP8, max(R_cap, 0), H, I, max(E_l, 1), 1, 0, E_l,
+                                 MOE_BF16)
+    if nb < 0:
+        _check(int(nb), "moe_workspace_bytes")
+    ws = _ws(int(nb), dev, ws)
+    _check(lib.moe_grouped_ffn_fwd_fp8(_ptr(x_q), _ptr(x_scale), _ptr(src_row), _ptr(offsets), E_l,
+                                       R_cap, H, I, _ptr(wg[0]), _ptr(wg[1]), _ptr(wu[0]),
+                                       _ptr(wu[1]), _ptr(wd[0]), _ptr(wd[1]), _ptr(o["gu"]),
+                                       _ptr(o["h_perm"]), _ptr(o["y_perm"]), _ptr(ws), _nbytes(ws),
+                                       _stream()), "moe_grouped_ffn_fwd_fp8")
+    return o

@@ -40,7 +40,7 @@ int hip_status(hipError_t e, const char* where) {
 
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-inline int elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+inline int elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : dtype == MOE_FP8 ? 1 : 4; }
 
 int check_dtype(int dtype, const char* fn) {
   if (dtype != MOE_F32 && dtype != MOE_BF16) return fail(MOE_EINVAL, "%s: unknown dtype %d", fn, dtype);
@@ -49,7 +49,7 @@ int check_dtype(int dtype, const char* fn) {
 
 int check_row_width(int H, int dtype, const char* fn) {
   if (H <= 0) return fail(MOE_EINVAL, "%s: H must be positive (got %d)", fn, H);
-  const int q = dtype == MOE_BF16 ? 8 : 4;
+  const int q = dtype == MOE_BF16 ? 8 : dtype == MOE_FP8 ? 16 : 4;
   if (H % q != 0) return fail(MOE_EINVAL, "%s: H=%d must be a multiple of %d for this dtype", fn, H, q);
   return MOE_OK;
 }
@@ -167,7 +167,12 @@ const char* moe_last_error(void) { return g_err; }
 int64_t moe_workspace_bytes(int op, int T, int H, int I, int E, int k, int e_lo, int e_hi,
                             int dtype) {
   const char* fn = "moe_workspace_bytes";
-  if (int rc = check_dtype(dtype, fn)) return rc;
+  if (dtype == MOE_FP8) {
+    if (op != MOE_OP_PERMUTE && op != MOE_OP_FFN_FWD_FP8)
+      return fail(MOE_EINVAL, "%s: MOE_FP8 applies to MOE_OP_PERMUTE and MOE_OP_FFN_FWD_FP8 only", fn);
+  } else if (int rc = check_dtype(dtype, fn)) {
+    return rc;
+  }
   if (int rc = check_routing_shape(T, E, k, fn)) return rc;
   if (int rc = check_row_width(H, dtype, fn)) return rc;
   const int R_cap = T * k;
@@ -178,6 +183,12 @@ int64_t moe_workspace_bytes(int op, int T, int H, int I, int E, int k, int e_lo,
       return (int64_t)ws_route_bwd(T, H, E, dtype);
     case MOE_OP_COMBINE_DX:
       return (int64_t)align256((size_t)E * H * elem_bytes(dtype));
+    case MOE_OP_FFN_FWD_FP8: {
+      if (e_lo < 0 || e_hi > E || e_lo >= e_hi)
+        return fail(MOE_EINVAL, "%s: need 0 <= e_lo < e_hi <= E", fn);
+      if (I <= 0) return fail(MOE_EINVAL, "%s: I must be positive", fn);
+      return (int64_t)ffn_fwd_fp8_ws_bytes(R_cap, e_hi - e_lo, I);
+    }
     case MOE_OP_PERMUTE:
     case MOE_OP_FFN_FWD:
     case MOE_OP_FFN_BWD: {
@@ -236,7 +247,8 @@ int moe_permute(const void* x, const int32_t* topk_idx, int T, int H, int E, int
                 int e_hi, int dtype, int32_t* counts, int32_t* offsets, int32_t* dest_row,
                 int32_t* src_row, void* x_perm, void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "moe_permute";
-  if (int rc = check_dtype(dtype, fn)) return rc;
+  if (dtype != MOE_FP8)
+    if (int rc = check_dtype(dtype, fn)) return rc;
   if (int rc = check_routing_shape(T, E, k, fn)) return rc;
   if (int rc = check_row_width(H, dtype, fn)) return rc;
   if (e_lo < 0 || e_hi > E || e_lo >= e_hi)
@@ -286,6 +298,54 @@ int moe_grouped_ffn_fwd(const void* x_perm, const int32_t* offsets, int E_l, int
                            (const float*)w_up, (const float*)w_down, (float*)gu_saved,
                            (float*)h_perm, (float*)y_perm, s);
   return hip_status(e, fn);
+}
+
+int moe_quantize_fp8(const void* src, int rows, int cols, int dtype, const int32_t* nrows,
+                     uint8_t* q, float* scale, void* stream) {
+  const char* fn = "moe_quantize_fp8";
+  if (int rc = check_dtype(dtype, fn)) return rc;
+  if (rows < 0) return fail(MOE_EINVAL, "%s: rows must be >= 0", fn);
+  if (cols <= 0 || cols % 16 != 0) return fail(MOE_EINVAL, "%s: cols=%d must be a positive multiple of 16", fn, cols);
+  if (rows == 0) return MOE_OK;
+  if (int rc = check_ptr(src, "src", fn, true)) return rc;
+  if (int rc = check_ptr(q, "q", fn, true)) return rc;
+  if (int rc = check_ptr(scale, "scale", fn)) return rc;
+  return hip_status(launch_quantize_fp8(src, rows, cols, dtype == MOE_BF16, nrows, q, scale,
+                                        begin_launch(stream)),
+                    fn);
+}
+
+int moe_grouped_ffn_fwd_fp8(const uint8_t* x_q, const float* x_scale, const int32_t* src_row,
+                            const int32_t* offsets, int E_l, int R_cap, int H, int I,
+                            const uint8_t* wg_q, const float* wg_scale, const uint8_t* wu_q,
+                            const float* wu_scale, const uint8_t* wd_q, const float* wd_scale,
+                            void* gu_saved, void* h_perm, void* y_perm, void* ws, size_t ws_bytes,
+                            void* stream) {
+  const char* fn = "moe_grouped_ffn_fwd_fp8";
+  if (int rc = check_ffn_shape(E_l, R_cap, H, I, MOE_FP8, fn)) return rc;
+  if (H % 128 != 0 || I % 128 != 0)
+    return fail(MOE_EUNSUPPORTED, "%s: needs H %% 128 == 0 and I %% 128 == 0 (H=%d, I=%d)", fn, H, I);
+  if (int rc = check_ptr(offsets, "offsets", fn)) return rc;
+  if (int rc = check_ptr(wg_q, "wg_q", fn, true)) return rc;
+  if (int rc = check_ptr(wu_q, "wu_q", fn, true)) return rc;
+  if (int rc = check_ptr(wd_q, "wd_q", fn, true)) return rc;
+  if (int rc = check_ptr(wg_scale, "wg_scale", fn, true)) return rc;
+  if (int rc = check_ptr(wu_scale, "wu_scale", fn, true)) return rc;
+  if (int rc = check_ptr(wd_scale, "wd_scale", fn, true)) return rc;
+  if (R_cap > 0) {
+    if (int rc = check_ptr(x_q, "x_q", fn, true)) return rc;
+    if (int rc = check_ptr(x_scale, "x_scale", fn)) return rc;
+    if (int rc = check_ptr(src_row, "src_row", fn)) return rc;
+    if (int rc = check_ptr(h_perm, "h_perm", fn, true)) return rc;
+    if (int rc = check_ptr(y_perm, "y_perm", fn, true)) return rc;
+  }
+  if (gu_saved != nullptr && !aligned16(gu_saved)) return fail(MOE_EINVAL, "%s: gu_saved must be 16-byte aligned", fn);
+  if (int rc = check_ws(ws, ws_bytes, ffn_fwd_fp8_ws_bytes(R_cap, E_l, I), fn)) return rc;
+  if (R_cap == 0) return MOE_OK;
+  return hip_status(launch_ffn_fwd_fp8(x_q, x_scale, src_row, offsets, E_l, R_cap, H, I, wg_q,
+                                       wg_scale, wu_q, wu_scale, wd_q, wd_scale, (bf16_t*)gu_saved,
+                                       (bf16_t*)h_perm, (bf16_t*)y_perm, ws, begin_launch(stream)),
+                    fn);
 }
 
 int moe_combine(const void* y_perm, const float* topk_w, const int32_t* dest_row,

@@ -154,6 +154,15 @@ hipError_t launch_ffn_fwd_bf16(const bf16_t* x_perm, const int32_t* offsets, int
                                int H, int I, const bf16_t* w_gate, const bf16_t* w_up,
                                const bf16_t* w_down, bf16_t* gu, bf16_t* h_perm, bf16_t* y_perm,
                                void* ws, hipStream_t s);
+// FP8 forward (gemm.hip) and E4M3 row quantization (fp8.hip)
+size_t ffn_fwd_fp8_ws_bytes(int R_cap, int E_l, int I);
+hipError_t launch_ffn_fwd_fp8(const uint8_t* x_q, const float* x_scale, const int32_t* src_row,
+                              const int32_t* offsets, int E_l, int R_cap, int H, int I,
+                              const uint8_t* wg_q, const float* wg_s, const uint8_t* wu_q,
+                              const float* wu_s, const uint8_t* wd_q, const float* wd_s,
+                              bf16_t* gu, bf16_t* h_perm, bf16_t* y_perm, void* ws, hipStream_t s);
+hipError_t launch_quantize_fp8(const void* src, int rows, int cols, bool bf16,
+                               const int32_t* nrows, uint8_t* q, float* scale, hipStream_t s);
 hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, const bf16_t* gu,
                                const bf16_t* h_perm, const int32_t* offsets, int E_l, int R_cap,
                                int H, int I, const bf16_t* w_gate, const bf16_t* w_up,

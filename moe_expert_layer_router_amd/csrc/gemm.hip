@@ -10,6 +10,7 @@
 //   DOWN_DGRAD   [dG dU] = SiLU'(dY_e W_down)               M-grouped, fused SiLU' epilogue
 //   GATEUP_DGRAD dX_e = dG W_gate + dU W_up                 M-grouped
 //   WGRAD        dW_e = A_e^T B_e over the expert's rows    K-grouped, fp32 out
+// and, with FP8 = true, the two forward products on E4M3 codes (below).
 // "M-grouped": each expert owns a contiguous row range of the grouped buffer
 // and a tile table (built on the device from the offsets) maps M tiles to
 // experts.  "K-grouped": the reduction runs over an expert's rows.
@@ -41,6 +42,18 @@
 //   from two transposing reads (ds_read_b64_tr_b16): within each 16-lane
 //   group, lane i points at row kb + i/4, column c0 + 4 * (i % 4), and lane l
 //   receives the four consecutive-k values of column c0 + l.
+//
+// FP8 forward (FP8 = true, GATEUP_FWD and DOWN_FWD): operands are E4M3 codes
+// with one power-of-two scale per row (activation rows, weight output
+// channels).  At the byte level a row of K codes is a row of K / 2 bf16 slots,
+// so the launcher passes K / 2 and row pitches / 2 and the DMA ring, the
+// swizzles and the fragment reads run unchanged: a 64-byte K step holds 64
+// codes.  Per K step each (mi, ni) block takes one v_mfma_scale_f32_32x32x64
+// _f8f6f4 (unit block scales) whose 32 operand bytes per lane are the two
+// 16-byte fragments the bf16 path reads for its two k16 sub-steps (a
+// permutation of K applied to both operands, so the sum is the same).  The
+// epilogue multiplies each accumulator by its row scale times its column
+// scale (both powers of two: exact) before the SwiGLU.
 #include "common.h"
 
 #include <algorithm>
@@ -114,6 +127,12 @@ struct GemmArgs {
   long f_group_stride;
   int accumulate;
   int fold;                 // WGRAD: F > 0 stores column c + column F + c (c < F), 0 = plain
+  // FP8 forward: row scales of A (grouped-row order) and column scales of the
+  // B tensors ([groups][N] floats, sb_group_stride apart)
+  const float* sa;
+  const float* sb0;
+  const float* sb1;
+  long sb_group_stride;
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -376,6 +395,33 @@ __device__ __forceinline__ void mma(f32x16_t (&acc)[C::MI][NI], const Frags<C>& 
     for (int ni = 0; ni < NI; ++ni) mfma1(acc[mi][ni], f.a[mi], f.b[ni]);
 }
 
+// FP8: a (mi, ni) block's operands for one 64-code K step: bytes 0..15 of the
+// lane's 32 are the fragment of bf16 sub-step 0, bytes 16..31 that of
+// sub-step 1.
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+template <class C>
+struct Frags8 {
+  i32x8_t a[C::MI];
+  i32x8_t b[NI];
+};
+
+__device__ __forceinline__ void mfma_f8(f32x16_t& acc, const i32x8_t& a, const i32x8_t& b) {
+  // format 0 = E4M3 for both operands; scale 127 = 2^0 for every 32-code block
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
+}
+
+template <class C>
+__device__ __forceinline__ void read_a8(Frags8<C>& f, int mi, int s, uint32_t sa, const FragLanes& L) {
+  const i32x4_t v = __builtin_bit_cast(i32x4_t, frag_kc(sa, L.kc[s], mi * 32 * BK * 2));
+  if (s == 0) f.a[mi].lo = v; else f.a[mi].hi = v;
+}
+template <class C>
+__device__ __forceinline__ void read_b8(Frags8<C>& f, int ni, int s, uint32_t sb, const FragLanes& L) {
+  const i32x4_t v = __builtin_bit_cast(i32x4_t, frag_kc(sb, L.kc[s], ni * 32 * BK * 2));
+  if (s == 0) f.b[ni].lo = v; else f.b[ni].hi = v;
+}
+
 // A stall in a wave's instruction stream idles its matrix core unless another
 // wave has MFMAs ready, and a wave runs at most about one MFMA ahead of the
 // pipe.  So the other work of a K step is spread between the MFMAs, one or
@@ -488,10 +534,91 @@ __device__ __forceinline__ void store16(out_rsrc_t r, uint32_t off, uint4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, r, off, 0, 0);
 }
 
+// FP8 epilogue scales of one tile, loaded after the previous tile's epilogue
+// (so that no wait for them lands behind this tile's DMAs): the lane's row
+// scales in the order the epilogue visits its rows, and its 8 columns' scales
+// (GATEUP_FWD: gate then up).
 template <int KIND, class C>
+struct Scales {
+  static constexpr int NR = KIND == K_GATEUP_FWD ? 4 * C::MI : 8 * C::MI;
+  static constexpr int NC = KIND == K_GATEUP_FWD ? 16 : 8;
+  float row[NR];
+  float col[NC];
+};
+
+template <int KIND, class C>
+__device__ __forceinline__ void load_scales(const GemmArgs& p, int e, int nt, int n0, int row0,
+                                            int row1, int wave, int lane, Scales<KIND, C>& S) {
+  constexpr int MI = C::MI, WM = C::WM;
+  const int wm = wave >> 1, wn = wave & 1;
+  // rows [row0, row1) of the row scales; the ones past row1 read as zero
+  const out_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.sa) + row0, 0,
+                                                          (row1 - row0) * 4, 0x00020000);
+  const float* cb = p.sb0 + (long)e * p.sb_group_stride;
+  if constexpr (KIND == K_GATEUP_FWD) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+          const int lrow = wm * WM + mi * 32 + 16 * h + it * 8 + (lane >> 3);
+          S.row[(mi * 2 + h) * 2 + it] =
+              __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rr, lrow * 4, 0, 0));
+        }
+    const int col = nt * 128 + wn * 64 + (lane & 7) * 8;
+    const uint32_t o = col < p.I ? (uint32_t)col * 4 : kOutKill;
+    const out_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(cb), 0, p.I * 4, 0x00020000);
+    const out_rsrc_t ru = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(p.sb1 + (long)e * p.sb_group_stride), 0, p.I * 4, 0x00020000);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const u32x4_t g = __builtin_amdgcn_raw_buffer_load_b128(rg, o + 16 * q, 0, 0);
+      const u32x4_t u = __builtin_amdgcn_raw_buffer_load_b128(ru, o + 16 * q, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        S.col[4 * q + i] = __uint_as_float(g[i]);
+        S.col[8 + 4 * q + i] = __uint_as_float(u[i]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int lrow = wm * WM + mi * 32 + 16 * h + it * 4 + (lane >> 4);
+          S.row[(mi * 2 + h) * 4 + it] =
+              __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rr, lrow * 4, 0, 0));
+        }
+    const int n = n0 + wn * WN + (lane & 15) * 8;
+    const uint32_t o = n < p.N ? (uint32_t)n * 4 : kOutKill;
+    const out_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(cb), 0, p.N * 4, 0x00020000);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(rc, o + 16 * q, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S.col[4 * q + i] = __uint_as_float(c[i]);
+    }
+  }
+}
+
+// The scale registers are ready (called after the K loop has drained the
+// memory counter, so the compiler's wait for them costs nothing there).
+template <int KIND, class C>
+__device__ __forceinline__ void touch_scales(const Scales<KIND, C>& S) {
+#pragma unroll
+  for (int i = 0; i < Scales<KIND, C>::NR; ++i) asm volatile("" ::"v"(S.row[i]));
+#pragma unroll
+  for (int i = 0; i < Scales<KIND, C>::NC; ++i) asm volatile("" ::"v"(S.col[i]));
+}
+
+template <int KIND, class C, bool F8 = false>
 __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc)[C::MI][NI], int e,
                                          int nt, int n0, int m0, int row0, int row1, int wave,
-                                         int lane) {
+                                         int lane,
+                                         const Scales<KIND, C>& S) {
   constexpr int MI = C::MI, WM = C::WM;
   const int wm = wave >> 1, wn = wave & 1;
   float* st = stage_area<C>(wave);
@@ -575,6 +702,14 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
           float g[8], u[8], hv[8];
           load8(st, r, sc, g);
           load8(st, r, sc + 32, u);
+          if constexpr (F8) {
+            const float sr = S.row[(mi * 2 + h) * 2 + it];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              g[j] *= sr * S.col[j];
+              u[j] *= sr * S.col[8 + j];
+            }
+          }
 #pragma unroll
           for (int j = 0; j < 8; ++j) hv[j] = g[j] * fast_rcp(1.f + __expf(-g[j])) * u[j];
           const uint32_t oh = col_ok ? (uint32_t)((lrow * p.ldc + col) * 2) : kOutKill;
@@ -621,6 +756,11 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
         const int lrow = wm * WM + mi * 32 + 16 * h + r;
         float v[8];
         load8(st, r, c, v);
+        if constexpr (F8) {
+          const float sr = S.row[pq * 4 + it];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] *= sr * S.col[j];
+        }
         const uint32_t o = col_ok ? (uint32_t)((lrow * ldo + n) * 2) : kOutKill;
         if constexpr (KIND == K_DOWN_DGRAD) {
           // v = dh; dG = dh * u * s * (1 + g (1 - s)), dU = dh * SiLU(g), s = sigmoid(g)
@@ -691,17 +831,79 @@ __device__ __forceinline__ void k_steps(f32x16_t (&acc)[C::MI][NI], Frags<C>& f0
   }
 }
 
+// FP8 K loop, on the same ring and DMA schedule as k_steps.  On entry f holds
+// the A blocks mi < MI / 2 and every B block of step 0.  Per step:
+//   phase 1: MFMAs of the blocks mi < MI / 2; between them the A blocks
+//            mi >= MI / 2 of this step are read and the second half of the
+//            DMA of step kt + NST - 1 is issued;
+//   wait for step kt + 1, barrier;
+//   phase 2: MFMAs of the blocks mi >= MI / 2 (ni-major); after the last use
+//            of B block ni it is read for step kt + 1, the A blocks
+//            mi < MI / 2 of step kt + 1 are read in between, and the first
+//            half of the DMA of step kt + NST is issued.
+template <int KIND, class C>
+__device__ __forceinline__ void k_steps_f8(f32x16_t (&acc)[C::MI][NI], Frags8<C>& f,
+                                           const FragLanes& L, const GemmArgs& p,
+                                           const Operand<C::NIA>& opA, const Operand<NIB>& opB,
+                                           uint32_t dma_a, uint32_t dma_b, uint32_t wa, uint32_t wb,
+                                           int nk) {
+  constexpr int NST = C::NST, NIA = C::NIA, kSlotA = C::kSlotA, kOffB = C::kOffB, MI = C::MI;
+  constexpr int MH = MI / 2, NP = MH * NI;  // MFMAs per phase
+  using D = DmaSplit<C>;
+  constexpr int STR = NP / D::NH;           // one DMA piece every STR MFMAs
+  static_assert(MI % 2 == 0 && NP % D::NH == 0 && STR >= 1, "FP8 phase split");
+  static_assert(2 * MH <= NP, "A reads of phase 1");
+  int slot = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint32_t sa = slot * kSlotA + wa, sb = kOffB + slot * kSlotB + wb;
+    const int pslot = slot == 0 ? NST - 1 : slot - 1;
+    const uint32_t kill1 = kt + NST - 1 < nk ? 0u : kDmaKill;
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      mfma_f8(acc[j / NI][j % NI], f.a[j / NI], f.b[j % NI]);
+      if (j < 2 * MH) read_a8<C>(f, MH + j / 2, j % 2, sa, L);
+      if (j % STR == 0)
+        dma_piece<KIND, C>(p, opA, opB, dma_a + pslot * kSlotA, dma_b + pslot * kSlotB,
+                           (kt + NST - 1) * BK, kill1, D::NH + j / STR);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int nslot = slot + 1 == NST ? 0 : slot + 1;
+    wait_vm<(NST - 2) * (NIA + NIB)>();
+    lds_barrier();  // every wave: step kt + 1 landed, slot `slot` fully read
+    const uint32_t na = nslot * kSlotA + wa, nb = kOffB + nslot * kSlotB + wb;
+    const uint32_t kill2 = kt + NST < nk ? 0u : kDmaKill;
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int ni = j / MH, mi = MH + j % MH;
+      mfma_f8(acc[mi][ni], f.a[mi], f.b[ni]);
+      if (j % MH == MH - 1) {  // last use of B block ni in this step
+        read_b8<C>(f, ni, 0, nb, L);
+        read_b8<C>(f, ni, 1, nb, L);
+      }
+      if (j < 2 * MH) read_a8<C>(f, j / 2, j % 2, na, L);
+      if (j % STR == 0)
+        dma_piece<KIND, C>(p, opA, opB, dma_a + slot * kSlotA, dma_b + slot * kSlotB,
+                           (kt + NST) * BK, kill2, j / STR);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    slot = nslot;
+  }
+}
+
 // Vector memory instructions each lane issues in the epilogue of an M-grouped
 // product (the buffer stores and loads there are unconditional: the range
 // checks drop the ones outside the tile), or -1 where the count depends on the
 // data (WGRAD).  A K loop that starts after the previous tile's epilogue (its
 // first DMAs issued before that epilogue) waits past exactly these.
-template <int KIND, class C>
+template <int KIND, class C, bool F8 = false>
 __host__ __device__ constexpr int epilogue_vmem_ops() {
-  return KIND == K_GATEUP_FWD   ? 12 * C::MI   // 3 stores x 2 rows x 2 halves per block row
-         : KIND == K_DOWN_DGRAD ? 32 * C::MI   // 2 loads + 2 stores x 4 rows x 2 halves
-         : KIND == K_WGRAD      ? -1
-                                : 8 * C::MI;   // 1 store x 4 rows x 2 halves
+  // FP8: the next tile's scale loads follow the epilogue (rows, then columns
+  // four at a time)
+  return (F8 ? Scales<KIND, C>::NR + Scales<KIND, C>::NC / 4 : 0) +
+         (KIND == K_GATEUP_FWD   ? 12 * C::MI   // 3 stores x 2 rows x 2 halves per block row
+          : KIND == K_DOWN_DGRAD ? 32 * C::MI   // 2 loads + 2 stores x 4 rows x 2 halves
+          : KIND == K_WGRAD      ? -1
+                                 : 8 * C::MI);  // 1 store x 4 rows x 2 halves
 }
 
 // One output tile: expert / group e, N tile nt and its first column n0; the
@@ -853,10 +1055,11 @@ __device__ __forceinline__ void issue_prologue(const GemmArgs& p, const Operand<
   }
 }
 
-template <int KIND, int BM_>
+template <int KIND, int BM_, bool F8 = false>
 __global__ __launch_bounds__(NTH)
 __attribute__((amdgpu_waves_per_eu(Cfg<BM_>::kWavesPerSimd, Cfg<BM_>::kWavesPerSimd)))
 void gemm_kernel(const GemmArgs p) {
+  static_assert(!F8 || KIND == K_GATEUP_FWD || KIND == K_DOWN_FWD, "FP8: forward products only");
   using Tr = Traits<KIND>;
   using C = Cfg<BM_>;
   constexpr int WM = C::WM, MI = C::MI, NST = C::NST, NIA = C::NIA;
@@ -889,6 +1092,8 @@ void gemm_kernel(const GemmArgs p) {
   Operand<NIB> opB;
   setup_operands<KIND, C>(p, t, wave, lane, opA, opB);
   if (t.nk > 0) issue_prologue<KIND, C>(p, opA, opB, dma_a, dma_b, t.nk);
+  Scales<KIND, C> S;
+  if constexpr (F8) load_scales<KIND, C>(p, t.e, t.nt, t.n0, t.row0, t.row1, wave, lane, S);
   // Whether the previous tile's epilogue (a known number of memory
   // operations) was issued after this tile's first DMAs.
   bool after_epi = false;
@@ -906,7 +1111,7 @@ void gemm_kernel(const GemmArgs p) {
       // lets those newer operations stay in flight (up to the counter's 63);
       // otherwise the epilogue's operations only make the wait stronger.
       constexpr int kFirst = (NST - 2) * ND + ND / 2;
-      constexpr int kEpi = epilogue_vmem_ops<KIND, C>();
+      constexpr int kEpi = epilogue_vmem_ops<KIND, C, F8>();
       constexpr int kAfter = kEpi < 0 ? kFirst : (kFirst + kEpi > 63 ? 63 : kFirst + kEpi);
       if (C::kSepStage && after_epi)
         wait_vm<kAfter>();
@@ -916,14 +1121,30 @@ void gemm_kernel(const GemmArgs p) {
       // Two fragment sets, no copies between them: f0 holds sub-step 0 (read
       // at the end of the previous step), f1 sub-step 1.
       static_assert(KSUB == 2, "the fragment pipeline below assumes two k16 sub-steps");
-      Frags<C> f0, f1;
-      load_frags<KIND, C>(f0, 0, wa, kOffB + wb, L);
-      k_steps<KIND, C>(acc, f0, f1, L, p, opA, opB, dma_a, dma_b, wa, wb, t.nk);
+      if constexpr (F8) {
+        Frags8<C> f;
+#pragma unroll
+        for (int mi = 0; mi < MI / 2; ++mi) {
+          read_a8<C>(f, mi, 0, wa, L);
+          read_a8<C>(f, mi, 1, wa, L);
+        }
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          read_b8<C>(f, ni, 0, kOffB + wb, L);
+          read_b8<C>(f, ni, 1, kOffB + wb, L);
+        }
+        k_steps_f8<KIND, C>(acc, f, L, p, opA, opB, dma_a, dma_b, wa, wb, t.nk);
+      } else {
+        Frags<C> f0, f1;
+        load_frags<KIND, C>(f0, 0, wa, kOffB + wb, L);
+        k_steps<KIND, C>(acc, f0, f1, L, p, opA, opB, dma_a, dma_b, wa, wb, t.nk);
+      }
       // Every wave is done with the ring, and every DMA (also the dropped
       // ones, which write zeros) has landed, before the ring is reused.
       wait_vm<0>();
       lds_barrier();
     }
+    if constexpr (F8) touch_scales<KIND, C>(S);
 
     // ------------------------------------------------------------ epilogue
     const int next = work + gridDim.x;
@@ -938,11 +1159,12 @@ void gemm_kernel(const GemmArgs p) {
       }
     }
     after_epi = C::kSepStage;
-    epilogue<KIND, C>(p, acc, t.e, t.nt, t.n0, t.m0, t.row0, t.row1, wave, lane);
+    epilogue<KIND, C, F8>(p, acc, t.e, t.nt, t.n0, t.m0, t.row0, t.row1, wave, lane, S);
     // The staging area is reused by the next epilogue (and, for tiles staged
     // in the ring, overwritten by the next tile's first DMA).
     lds_barrier();
     if (!more) break;
+    if constexpr (F8) load_scales<KIND, C>(p, tn.e, tn.nt, tn.n0, tn.row0, tn.row1, wave, lane, S);
     if constexpr (!C::kSepStage) {
       tn = decode_tile<KIND, C>(p, next);
       setup_operands<KIND, C>(p, tn, wave, lane, opA, opB);
@@ -1005,13 +1227,13 @@ size_t ffn_sched_bytes(int R_cap, int E_l) {
   return align256((1 + 3 * entries) * sizeof(int32_t));
 }
 
-template <int KIND, int BM_>
+template <int KIND, int BM_, bool F8 = false>
 static hipError_t launch_gemm(const GemmArgs& a, int work_upper, int kernel_id, hipStream_t s) {
   using C = Cfg<BM_>;
   if (work_upper <= 0) return hipSuccess;
   const int grid = std::min(work_upper, kCUs * C::kWavesPerSimd);  // persistent
   ProfScope ps(kernel_id, s);
-  gemm_kernel<KIND, BM_><<<grid, NTH, C::kLdsBytes, s>>>(a);
+  gemm_kernel<KIND, BM_, F8><<<grid, NTH, C::kLdsBytes, s>>>(a);
   return hipGetLastError();
 }
 
@@ -1057,6 +1279,91 @@ hipError_t launch_ffn_fwd_bf16(const bf16_t* x_perm, const int32_t* offsets, int
   d.c0 = y_perm;
   d.ldc = H;
   return launch_gemm<K_DOWN_FWD, kBmGrouped>(d, mt_upper * d.n_ntiles, MOE_KERNEL_FFN_DOWN, s);
+}
+
+// Row scales of the permuted activations: sxp[r] = sx[src_row[r]] for the
+// R = offsets[E_l] rows in use.
+__global__ __launch_bounds__(256) void gather_row_scales_kernel(const float* __restrict__ sx,
+                                                                const int32_t* __restrict__ src_row,
+                                                                const int32_t* __restrict__ offsets,
+                                                                int E_l, int R_cap,
+                                                                float* __restrict__ sxp) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= R_cap || r >= offsets[E_l]) return;
+  sxp[r] = sx[src_row[r]];
+}
+
+size_t ffn_fwd_fp8_ws_bytes(int R_cap, int E_l, int I) {
+  return ffn_sched_bytes(R_cap, E_l) + align256((size_t)R_cap * 4) + align256((size_t)R_cap * I) +
+         align256((size_t)R_cap * 4);
+}
+
+hipError_t launch_ffn_fwd_fp8(const uint8_t* x_q, const float* x_scale, const int32_t* src_row,
+                              const int32_t* offsets, int E_l, int R_cap, int H, int I,
+                              const uint8_t* wg_q, const float* wg_s, const uint8_t* wu_q,
+                              const float* wu_s, const uint8_t* wd_q, const float* wd_s,
+                              bf16_t* gu, bf16_t* h_perm, bf16_t* y_perm, void* ws,
+                              hipStream_t s) {
+  char* w = (char*)ws;
+  int32_t* sched = (int32_t*)w;
+  w += ffn_sched_bytes(R_cap, E_l);
+  float* sxp = (float*)w;
+  w += align256((size_t)R_cap * 4);
+  uint8_t* hq = (uint8_t*)w;
+  w += align256((size_t)R_cap * I);
+  float* sh = (float*)w;
+  ffn_sched_kernel<<<1, kMaxE, 0, s>>>(offsets, E_l, kBmGrouped, sched);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  gather_row_scales_kernel<<<(R_cap + 255) / 256, 256, 0, s>>>(x_scale, src_row, offsets, E_l,
+                                                               R_cap, sxp);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int mt_upper = R_cap / kBmGrouped + E_l;
+
+  // E4M3 rows of K codes run through the ring as rows of K / 2 bf16 slots.
+  GemmArgs g{};
+  g.a = (const bf16_t*)x_q;
+  g.lda = H / 2;
+  g.b0 = (const bf16_t*)wg_q;
+  g.b1 = (const bf16_t*)wu_q;
+  g.ldb = H / 2;
+  g.b_group_stride = (long)I * H / 2;
+  g.sched = sched;
+  g.K = H / 2;
+  g.N = I;
+  g.I = I;
+  g.n_ntiles = (I + BN / 2 - 1) / (BN / 2);
+  g.c0 = h_perm;
+  g.ldc = I;
+  g.c1 = gu;
+  g.sa = sxp;
+  g.sb0 = wg_s;
+  g.sb1 = wu_s;
+  g.sb_group_stride = I;
+  err = launch_gemm<K_GATEUP_FWD, kBmGrouped, true>(g, mt_upper * g.n_ntiles, MOE_KERNEL_FFN_GATEUP, s);
+  if (err != hipSuccess) return err;
+
+  err = launch_quantize_fp8(h_perm, R_cap, I, true, offsets + E_l, hq, sh, s);
+  if (err != hipSuccess) return err;
+
+  GemmArgs d{};
+  d.a = (const bf16_t*)hq;
+  d.lda = I / 2;
+  d.b0 = (const bf16_t*)wd_q;
+  d.ldb = I / 2;
+  d.b_group_stride = (long)H * I / 2;
+  d.sched = sched;
+  d.K = I / 2;
+  d.N = H;
+  d.I = I;
+  d.n_ntiles = (H + BN - 1) / BN;
+  d.c0 = y_perm;
+  d.ldc = H;
+  d.sa = sh;
+  d.sb0 = wd_s;
+  d.sb_group_stride = H;
+  return launch_gemm<K_DOWN_FWD, kBmGrouped, true>(d, mt_upper * d.n_ntiles, MOE_KERNEL_FFN_DOWN, s);
 }
 
 hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, const bf16_t* gu,

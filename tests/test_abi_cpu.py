@@ -28,7 +28,7 @@ import moe_expert_layer_router_amd as moe  # noqa: E402
 
 L = moe.lib
 OK, EINVAL, EUNSUP, EWS = 0, -1, -2, -3
-BF16, F32 = moe.MOE_BF16, moe.MOE_F32
+BF16, F32, FP8 = moe.MOE_BF16, moe.MOE_F32, moe.MOE_FP8
 A = ctypes.c_void_p(0x100000)   # fake, 256-byte aligned; never dereferenced by a failing call
 U = ctypes.c_void_p(0x100002)   # misaligned fake pointer
 N = None
@@ -50,7 +50,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_single_hip_runtime():
-    assert L.moe_abi_version() == moe.ABI_VERSION == 1
+    assert L.moe_abi_version() == moe.ABI_VERSION == 2
     libs = moe.hip_runtimes_mapped()
     assert len(libs) <= 1, libs
 
@@ -128,6 +128,36 @@ def test_ffn_fwd_errors():
     assert f(A, A, 16, 512, 128, 64, A, A, A, BF16, N, N, A, A, big, S) == EINVAL and "h_perm" in _err()
     assert f(A, A, 16, 512, 128, 64, A, A, A, BF16, N, A, A, A, 4, S) == EWS
     assert f(A, A, 16, 0, 128, 64, A, A, A, BF16, N, N, N, A, big, S) == OK            # nothing routed
+
+
+def test_fp8_entry_points_errors():
+    q = lambda *a: L.moe_quantize_fp8(*a)
+    assert q(A, 64, 2040, BF16, N, A, A, S) == EINVAL and "multiple of 16" in _err()
+    assert q(A, -1, 2048, BF16, N, A, A, S) == EINVAL
+    assert q(A, 64, 2048, FP8, N, A, A, S) == EINVAL and "dtype" in _err()     # source must be bf16/fp32
+    assert q(U, 64, 2048, BF16, N, A, A, S) == EINVAL                          # src misaligned
+    assert q(A, 64, 2048, BF16, N, N, A, S) == EINVAL and "q" in _err()
+    assert q(N, 0, 2048, BF16, N, N, N, S) == OK                               # no rows
+    f = lambda *a: L.moe_grouped_ffn_fwd_fp8(*a)
+    big = 1 << 30
+    args = lambda H=2048, I=768, El=16, R=512, ws=big, xq=A, wg=A, h=A: (
+        xq, A, A, A, El, R, H, I, wg, A, A, A, A, A, N, h, A, A, ws, S)
+    assert f(*args(I=704)) == EUNSUP and "128" in _err()                       # I % 128
+    assert f(*args(H=1984)) == EUNSUP                                          # H % 128
+    assert f(*args(H=2040)) == EINVAL                                          # H % 16 (row width)
+    assert f(*args(El=0)) == EINVAL
+    assert f(*args(wg=N)) == EINVAL and "wg_q" in _err()
+    assert f(*args(h=N)) == EINVAL and "h_perm" in _err()
+    assert f(*args(xq=U)) == EINVAL
+    assert f(*args(ws=8)) == EWS
+    assert f(*args(R=0, xq=N, h=N)) == OK                                      # nothing routed
+    ws = lambda *a: L.moe_workspace_bytes(*a)
+    n = ws(moe.MOE_OP_FFN_FWD_FP8, 8192, 2048, 768, 128, 8, 0, 16, BF16)
+    assert n >= 8192 * 8 * (768 + 8)                                           # codes + scales of h
+    assert ws(moe.MOE_OP_FFN_FWD_FP8, 8192, 2048, 768, 128, 8, 0, 16, FP8) == n
+    assert ws(moe.MOE_OP_ROUTE, 16, 64, 32, 8, 2, 0, 8, FP8) == EINVAL and "MOE_FP8" in _err()
+    p = lambda *a: L.moe_permute(*a)
+    assert p(A, A, 64, 2040, 16, 4, 0, 16, FP8, A, A, A, A, A, A, big, S) == EINVAL   # H % 16 for codes
 
 
 def test_combine_errors():

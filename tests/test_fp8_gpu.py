@@ -1,0 +1,168 @@
+"""Parity of the FP8 forward of the expert FFN (through the C ABI) against the oracle.
+
+Row quantization (codes and power-of-two scales) and the FP8 permute must match
+bit for bit: the codes come from exact roundings, so both sides take the same
+decisions.  h and y of moe_grouped_ffn_fwd_fp8 are compared with the oracle's
+FP8 recipe on the same codes:
+  h: within one bf16 step plus the fp32 summation error carried through
+     h = SiLU(g) u: |d| <= 2^-7 |h| + 2 (|u| dg + (|g| + 1) du) with
+     dg = K 2^-24 sum_c |code products| * scales (du likewise), the standard
+     bound for a K-term fp32 sum;
+  y: the layer's bf16 bar, max|d| <= 2e-2 * max(1, max|ref|) and rel-L2 <=
+     5e-3, plus, elementwise, what the h elements that rounded to the
+     neighbouring bf16 (fp32 versus fp64 sums) can move: such an element may
+     land on the other side of an E4M3 step, so its code may differ by one step
+     (<= |h|/8 + the subnormal step 2^-9 of its row scale), times |W_down|.
+     Both codes are correct for the recipe.  A row whose largest |h| differs
+     could change its scale; such rows (expected none) are only checked against
+     the exact forward;
+and the recipe as a whole stays within its quantization error of the exact
+forward (rel-L2 < 0.12, as the oracle's own pin).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from workloads import EP_SHARE, SKEWED, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+import moe_expert_layer_router_amd as moe  # noqa: E402  (no skip: a missing library must fail)
+
+DEV = torch.device("cuda:0")
+
+
+def _dev(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(dtype).contiguous()
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quantize_fp8_bit_exact(dtype):
+    rng = np.random.default_rng(31)
+    rows, cols = 300, 2048 if dtype == "bf16" else 512
+    a = rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-40, 40, size=(rows, 1)))
+    a[5] = 0.0                                           # zero row: scale 1, codes 0
+    a[7] = -0.0
+    a[9, :] = 1.0
+    a[9, 3] = 448.0 * 2.0 ** 5                           # max exactly on a boundary
+    a[11, 7] = -448.0 * 2.0 ** -3
+    a[13, :] = rng.standard_normal(cols) * 2.0 ** -12    # many values in the subnormal codes
+    a[13, 0] = 1.0
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    src = _dev(a.astype(np.float32), tdt)
+    print(f"  quantize {dtype} rows={rows} cols={cols}", flush=True)
+    q, s = moe.moe_quantize_fp8(src)
+    torch.cuda.synchronize()
+    ref_q, ref_s = O.quantize_rows_fp8(_np(src))
+    got_q = q.cpu().numpy()
+    bad = np.nonzero(got_q != ref_q)
+    assert bad[0].size == 0, f"{bad[0].size} codes differ, first at {bad[0][0]},{bad[1][0]}: " \
+                             f"{got_q[bad][0]:#x} vs {ref_q[bad][0]:#x}"
+    assert np.array_equal(s.cpu().numpy().astype(np.float64), ref_s)
+    # a device row bound: rows at or past it are left as they were
+    nrows = torch.tensor([150], dtype=torch.int32, device=DEV)
+    q2 = torch.full_like(q, 0xAA)
+    s2 = torch.full_like(s, -1.0)
+    moe.moe_quantize_fp8(src, nrows=nrows, out={"q": q2, "scale": s2})
+    torch.cuda.synchronize()
+    assert torch.equal(q2[:150], q[:150]) and torch.equal(s2[:150], s[:150])
+    assert (q2[150:] == 0xAA).all() and (s2[150:] == -1.0).all()
+
+
+FP8_CASES = [
+    EP_SHARE.scaled(name="fp8_t512_h256_i128_e32_k4_local4to20", T=512, H=256, I=128, E=32, k=4,
+                    e_lo=4, e_hi=20),
+    SKEWED.scaled(name="fp8_skewed_t1024_h256_i256_e32_k4", T=1024, H=256, I=256, E=32, k=4, e_lo=0,
+                  e_hi=32),
+    EP_SHARE.scaled(name="fp8_t2048_h2048_i768_e16_k4_all_local", T=2048, E=16, k=4, e_lo=0, e_hi=16),
+]
+
+
+@pytest.mark.parametrize("w", FP8_CASES, ids=lambda w: w.name)
+def test_ffn_fwd_fp8_matches_oracle(w):
+    inp = make_inputs(w)
+    _, idx, _ = O.route(inp["x"], inp["w_router"], w.k, inp.get("bias"))
+    print(f"  case {w.name}", flush=True)
+    bf = torch.bfloat16
+    x = _dev(inp["x"], bf)
+    wts = {n: _dev(inp[n], bf) for n in ("w_gate", "w_up", "w_down")}
+    # quantize tokens and weights on the GPU; the codes must be the oracle's
+    xq, sx = moe.moe_quantize_fp8(x)
+    wq = {}
+    for n, t in wts.items():
+        El, N, K = t.shape
+        q, s = moe.moe_quantize_fp8(t.view(El * N, K))
+        wq[n] = (q.view(El, N, K), s.view(El, N))
+    torch.cuda.synchronize()
+    ref_xq, ref_sx = O.quantize_rows_fp8(inp["x"])
+    assert np.array_equal(xq.cpu().numpy(), ref_xq) and np.array_equal(_np(sx), ref_sx)
+    ref_w = {n: O.quantize_expert_weights_fp8(inp[n]) for n in wts}
+    for n in wts:
+        assert np.array_equal(wq[n][0].cpu().numpy(), ref_w[n][0]), n
+        assert np.array_equal(_np(wq[n][1]), ref_w[n][1]), n
+    # FP8 permute: rows of codes move bit for bit
+    perm = moe.moe_permute(xq, torch.from_numpy(idx.astype(np.int32)).to(DEV), w.E, w.e_lo, w.e_hi)
+    out = moe.moe_grouped_ffn_fwd_fp8(perm["x_perm"], sx, perm["src_row"], perm["offsets"],
+                                      wq["w_gate"], wq["w_up"], wq["w_down"], save_gu=True)
+    torch.cuda.synchronize()
+    offsets = perm["offsets"].cpu().numpy()
+    R = int(offsets[-1])
+    src_row = perm["src_row"].cpu().numpy()[:R]
+    assert np.array_equal(perm["x_perm"][:R].cpu().numpy(), ref_xq[src_row])
+    h_got, y_got = _np(out["h_perm"][:R]), _np(out["y_perm"][:R])
+    h_ref, y_ref, y_exact = np.zeros_like(h_got), np.zeros_like(y_got), np.zeros_like(y_got)
+    h_slack, y_flip = np.zeros_like(h_got), np.zeros_like(y_got)
+    same_max = np.zeros(R, dtype=bool)
+    empty = 0
+    for e in range(w.e_lo, w.e_hi):
+        i = e - w.e_lo
+        tt, _ = np.nonzero(np.asarray(idx) == e)
+        assert offsets[i + 1] - offsets[i] == len(tt)
+        if len(tt) == 0:
+            empty += 1
+            continue
+        p = O.expert_ffn_fp8_parts(ref_xq[tt], ref_sx[tt], ref_w["w_gate"][0][i], ref_w["w_gate"][1][i],
+                                   ref_w["w_up"][0][i], ref_w["w_up"][1][i], ref_w["w_down"][0][i],
+                                   ref_w["w_down"][1][i])
+        sl = slice(offsets[i], offsets[i + 1])
+        h_ref[sl], y_ref[sl] = p["h"], p["y"]
+        # absolute sums of the code products: the fp32 accumulation error scale
+        mag = lambda q: q & np.uint8(0x7F)
+        ga = O.fp8_matmul_rows(mag(ref_xq[tt]), ref_sx[tt], mag(ref_w["w_gate"][0][i]), ref_w["w_gate"][1][i])
+        ua = O.fp8_matmul_rows(mag(ref_xq[tt]), ref_sx[tt], mag(ref_w["w_up"][0][i]), ref_w["w_up"][1][i])
+        gam = w.H * 2.0 ** -24
+        h_slack[sl] = 2 * (np.abs(p["u"]) * gam * ga + (np.abs(p["g"]) + 1) * gam * ua)
+        d = h_got[sl] != p["h"]
+        step = np.abs(p["h"]) / 8 + p["sh"][:, None] * 2.0 ** -9
+        wdq = np.abs(O.fp8_e4m3_decode(ref_w["w_down"][0][i])) * ref_w["w_down"][1][i][:, None]
+        y_flip[sl] = (d * step) @ wdq.T
+        same_max[sl] = np.abs(h_got[sl]).max(axis=1) == np.abs(p["h"]).max(axis=1)
+        y_exact[sl] = O.expert_ffn(inp["x"][tt], inp["w_gate"][i], inp["w_up"][i], inp["w_down"][i])
+    hb = 2.0 ** -7 * np.abs(h_ref) + h_slack
+    hbad = int((np.abs(h_got - h_ref) > hb).sum())
+    ok_rows = same_max
+    bar = 2e-2 * max(1.0, np.abs(y_ref).max())
+    over = np.abs(y_got - y_ref) - (bar + y_flip)
+    rel = np.linalg.norm(y_got - y_ref) / np.linalg.norm(y_ref)
+    rel_exact = np.linalg.norm(y_got - y_exact) / np.linalg.norm(y_exact)
+    print(f"  R={R} empty experts={empty}: h beyond one bf16 step: {hbad}; y max-abs "
+          f"{np.abs(y_got - y_ref).max():.3e} (bar {bar:.3e}, largest code-step allowance "
+          f"{y_flip.max():.3e}) rel-L2 {rel:.3e}; rows with a different max|h|: "
+          f"{int((~ok_rows).sum())}; vs exact forward rel-L2 {rel_exact:.3e}", flush=True)
+    assert hbad == 0
+    assert (over[ok_rows] <= 0).all() and rel <= 5e-3
+    assert (~ok_rows).mean() < 0.01
+    assert rel_exact < 0.12
+    # the saved g / u are the scaled products
+    gu = _np(out["gu"][:R])
+    I = w.I
+    g_ref = np.concatenate([O.fp8_matmul_rows(ref_xq[np.nonzero(np.asarray(idx) == e)[0]],
+                                              ref_sx[np.nonzero(np.asarray(idx) == e)[0]],
+                                              ref_w["w_gate"][0][e - w.e_lo], ref_w["w_gate"][1][e - w.e_lo])
+                            for e in range(w.e_lo, w.e_hi)], axis=0)
+    assert np.abs(gu[:, :I] - g_ref).max() <= 2.0 ** -7 * np.abs(g_ref).max()
