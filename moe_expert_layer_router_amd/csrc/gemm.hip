@@ -57,10 +57,12 @@
 #include "common.h"
 
 #include <algorithm>
+#include <mutex>
 
 namespace moe {
 
 constexpr int BN = 256, BK = 32, NTH = 256;
+constexpr int kTileCtrs = 4;             // dynamic tile counters in the FFN workspace
 constexpr int WN = 128;                  // wave sub-tile width
 constexpr int NI = WN / 32;              // MFMA blocks per wave along N
 constexpr int KSUB = BK / 16;            // k16 sub-steps per K step
@@ -133,6 +135,11 @@ struct GemmArgs {
   const float* sb0;
   const float* sb1;
   long sb_group_stride;
+  // Dynamic tile order: null = static (workgroup g takes tiles g, g + grid,
+  // ...); else a zeroed counter from which workgroups draw their tiles after
+  // the first (tile grid + ticket), so that kernels running side by side
+  // share CUs as they free up.
+  int* tile_ctr;
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -1079,6 +1086,10 @@ void gemm_kernel(const GemmArgs p) {
 
   int work = xcd_remap(blockIdx.x, gridDim.x);
   if (work >= total) return;
+  // Dynamic order: thread 0 holds the ticket of the tile after next; it is
+  // read only after a K loop has drained the memory counter.
+  int ticket = 0;
+  if (p.tile_ctr != nullptr && tid == 0) ticket = atomicAdd(p.tile_ctr, 1);
   const uint32_t dma_a = lds_addr(g_lds) + wave * NIA * 1024;  // this wave's DMA area
   const uint32_t dma_b = lds_addr(g_lds) + kOffB + wave * NIB * 1024;
   // wave block bases inside a slot
@@ -1147,7 +1158,20 @@ void gemm_kernel(const GemmArgs p) {
     if constexpr (F8) touch_scales<KIND, C>(S);
 
     // ------------------------------------------------------------ epilogue
-    const int next = work + gridDim.x;
+    int next = work + gridDim.x;
+    if (p.tile_ctr != nullptr) {  // uniform
+      // hand thread 0's ticket to the workgroup through the first word of
+      // the ring (idle here: this tile's K loop is done, the next tile's DMA
+      // is not issued yet), and draw the next ticket
+      volatile int* slot0 = reinterpret_cast<volatile int*>(g_lds);
+      if (tid == 0) {
+        slot0[0] = (int)gridDim.x + ticket;
+        ticket = atomicAdd(p.tile_ctr, 1);
+      }
+      lds_barrier();
+      next = __builtin_amdgcn_readfirstlane(slot0[0]);
+      lds_barrier();  // every wave has it before the ring is written again
+    }
     const bool more = next < total;
     Tile tn = t;
     if constexpr (C::kSepStage) {
@@ -1179,7 +1203,10 @@ void gemm_kernel(const GemmArgs p) {
 // (expert, first row, end row) per `rows` rows.  sched[0] = number of entries.
 __global__ __launch_bounds__(kMaxE) void ffn_sched_kernel(const int32_t* __restrict__ offsets,
                                                           int E_l, int rows,
-                                                          int32_t* __restrict__ sched) {
+                                                          int32_t* __restrict__ sched,
+                                                          int32_t* __restrict__ ctrs) {
+  // the dynamic tile counters of the products that follow start at zero
+  if (ctrs != nullptr && threadIdx.x < kTileCtrs) ctrs[threadIdx.x] = 0;
   __shared__ int s[kMaxE + 1];      // s[g] = tiles of experts < g
   __shared__ int s_off[kMaxE + 1];  // the offsets, in LDS for the tile loop
   __shared__ int s_wave[kMaxE / kWave];
@@ -1222,9 +1249,14 @@ int gemm_tiles(int M, int N) { return ((M + kBmWgrad - 1) / kBmWgrad) * ((N + BN
 
 bool dw_router_folds(int E) { return E % 8 == 0 && 2 * E <= BN; }
 
-size_t ffn_sched_bytes(int R_cap, int E_l) {
+// Tile table, then kTileCtrs dynamic tile counters (256 bytes).
+static size_t ffn_sched_table_bytes(int R_cap, int E_l) {
   const size_t entries = (size_t)R_cap / kBmGrouped + E_l + 1;
   return align256((1 + 3 * entries) * sizeof(int32_t));
+}
+size_t ffn_sched_bytes(int R_cap, int E_l) { return ffn_sched_table_bytes(R_cap, E_l) + 256; }
+static int32_t* ffn_tile_ctrs(void* ws, int R_cap, int E_l) {
+  return (int32_t*)((char*)ws + ffn_sched_table_bytes(R_cap, E_l));
 }
 
 template <int KIND, int BM_, bool F8 = false>
@@ -1242,7 +1274,7 @@ hipError_t launch_ffn_fwd_bf16(const bf16_t* x_perm, const int32_t* offsets, int
                                const bf16_t* w_down, bf16_t* gu, bf16_t* h_perm, bf16_t* y_perm,
                                void* ws, hipStream_t s) {
   int32_t* sched = (int32_t*)ws;
-  ffn_sched_kernel<<<1, kMaxE, 0, s>>>(offsets, E_l, kBmGrouped, sched);
+  ffn_sched_kernel<<<1, kMaxE, 0, s>>>(offsets, E_l, kBmGrouped, sched, nullptr);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int mt_upper = R_cap / kBmGrouped + E_l;
@@ -1312,7 +1344,7 @@ hipError_t launch_ffn_fwd_fp8(const uint8_t* x_q, const float* x_scale, const in
   uint8_t* hq = (uint8_t*)w;
   w += align256((size_t)R_cap * I);
   float* sh = (float*)w;
-  ffn_sched_kernel<<<1, kMaxE, 0, s>>>(offsets, E_l, kBmGrouped, sched);
+  ffn_sched_kernel<<<1, kMaxE, 0, s>>>(offsets, E_l, kBmGrouped, sched, nullptr);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   gather_row_scales_kernel<<<(R_cap + 255) / 256, 256, 0, s>>>(x_scale, src_row, offsets, E_l,
@@ -1366,6 +1398,36 @@ hipError_t launch_ffn_fwd_fp8(const uint8_t* x_q, const float* x_scale, const in
   return launch_gemm<K_DOWN_FWD, kBmGrouped, true>(d, mt_upper * d.n_ntiles, MOE_KERNEL_FFN_DOWN, s);
 }
 
+// A second stream of the calling device for products that may run beside
+// others (created once per device, default priority, never destroyed), and
+// the events that fork it from and join it back to the caller's stream.  Null
+// when it cannot be created: everything then runs on the caller's stream.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, mid = nullptr, join = nullptr;
+};
+
+static SideStream* side_stream() {
+  static SideStream per_dev[64];
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(mu);
+  SideStream& ss = per_dev[dev];
+  if (ss.s == nullptr) {
+    hipStream_t st = nullptr;
+    hipEvent_t e[3] = {nullptr, nullptr, nullptr};
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    for (int i = 0; i < 3; ++i)
+      if (hipEventCreateWithFlags(&e[i], hipEventDisableTiming) != hipSuccess) return nullptr;
+    ss.fork = e[0];
+    ss.mid = e[1];
+    ss.join = e[2];
+    ss.s = st;
+  }
+  return &ss;
+}
+
 hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, const bf16_t* gu,
                                const bf16_t* h_perm, const int32_t* offsets, int E_l, int R_cap,
                                int H, int I, const bf16_t* w_gate, const bf16_t* w_up,
@@ -1374,10 +1436,23 @@ hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, cons
                                hipStream_t s) {
   int32_t* sched = (int32_t*)ws;
   bf16_t* dgu = (bf16_t*)((char*)ws + ffn_sched_bytes(R_cap, E_l));
-  ffn_sched_kernel<<<1, kMaxE, 0, s>>>(offsets, E_l, kBmGrouped, sched);
+  int32_t* ctrs = ffn_tile_ctrs(ws, R_cap, E_l);
+  ffn_sched_kernel<<<1, kMaxE, 0, s>>>(offsets, E_l, kBmGrouped, sched, ctrs);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int mt_upper = R_cap / kBmGrouped + E_l;
+  // The weight gradients run on a side stream beside the data gradients:
+  //   s:  DOWN_DGRAD -> (mid) -> GATEUP_DGRAD -> wait(join)
+  //   s2: wait(fork) -> DOWN_WGRAD -> wait(mid) -> GATEUP_WGRAD -> (join)
+  // The data-gradient products leave CUs idle on this layer's shapes (few N
+  // tiles, a short last round), which the weight-gradient tiles then use.
+  SideStream* side = side_stream();
+  hipStream_t s2 = s;
+  if (side != nullptr) {
+    if ((err = hipEventRecord(side->fork, s)) != hipSuccess) return err;
+    if ((err = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return err;
+    s2 = side->s;
+  }
 
   // dh = dY_e W_down[e]  ->  [dG dU] through the SiLU' epilogue.
   GemmArgs a{};
@@ -1393,8 +1468,10 @@ hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, cons
   a.n_ntiles = (I + BN - 1) / BN;
   a.gu = gu;
   a.c0 = dgu;
+  a.tile_ctr = ctrs + 0;
   err = launch_gemm<K_DOWN_DGRAD, kBmGrouped>(a, mt_upper * a.n_ntiles, MOE_KERNEL_FFN_DOWN_DGRAD, s);
   if (err != hipSuccess) return err;
+  if (side != nullptr && (err = hipEventRecord(side->mid, s)) != hipSuccess) return err;
 
   // dW_down[e] = dY_e^T h_e
   GemmArgs b{};
@@ -1413,7 +1490,8 @@ hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, cons
   b.ldc = I;
   b.f_group_stride = (long)H * I;
   b.accumulate = accumulate ? 1 : 0;
-  err = launch_gemm<K_WGRAD, kBmWgradDown>(b, E_l * b.n_mtiles * b.n_ntiles, MOE_KERNEL_FFN_DOWN_WGRAD, s);
+  b.tile_ctr = ctrs + 1;
+  err = launch_gemm<K_WGRAD, kBmWgradDown>(b, E_l * b.n_mtiles * b.n_ntiles, MOE_KERNEL_FFN_DOWN_WGRAD, s2);
   if (err != hipSuccess) return err;
 
   // dX_e = dG W_gate[e] + dU W_up[e]
@@ -1431,6 +1509,7 @@ hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, cons
   c.n_ntiles = (H + BN - 1) / BN;
   c.c0 = dx_perm;
   c.ldc = H;
+  c.tile_ctr = ctrs + 2;
   err = launch_gemm<K_GATEUP_DGRAD, kBmGrouped>(c, mt_upper * c.n_ntiles, MOE_KERNEL_FFN_GATEUP_DGRAD, s);
   if (err != hipSuccess) return err;
 
@@ -1452,7 +1531,15 @@ hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, cons
   w.ldc = H;
   w.f_group_stride = (long)I * H;
   w.accumulate = accumulate ? 1 : 0;
-  return launch_gemm<K_WGRAD, kBmWgrad>(w, E_l * w.n_mtiles * w.n_ntiles, MOE_KERNEL_FFN_GATEUP_WGRAD, s);
+  w.tile_ctr = ctrs + 3;
+  if (side != nullptr && (err = hipStreamWaitEvent(s2, side->mid, 0)) != hipSuccess) return err;
+  err = launch_gemm<K_WGRAD, kBmWgrad>(w, E_l * w.n_mtiles * w.n_ntiles, MOE_KERNEL_FFN_GATEUP_WGRAD, s2);
+  if (err != hipSuccess) return err;
+  if (side != nullptr) {
+    if ((err = hipEventRecord(side->join, s2)) != hipSuccess) return err;
+    if ((err = hipStreamWaitEvent(s, side->join, 0)) != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_dw_router_bf16(const bf16_t* x, const bf16_t* dz_hilo, int T, int H, int E,
