@@ -222,6 +222,19 @@ int moe_grouped_ffn_bwd(const void* dy_perm, const void* x_perm, const void* gu_
                         int dtype, void* dx_perm, float* dw_gate, float* dw_up, float* dw_down,
                         int accumulate, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_grouped_ffn_bwd with the weight gradients left on a second stream, so
+ * that the caller can overlap them with later work (e.g. moe_combine_dx).
+ * dx_perm is complete in `stream` order; dw_gate, dw_up and dw_down are
+ * complete in `wgrad_stream` order (which this call makes wait for the data it
+ * reads).  ws must not be reused by any work until both streams have passed
+ * this call.  wgrad_stream must differ from stream (else MOE_EINVAL). */
+int moe_grouped_ffn_bwd_split(const void* dy_perm, const void* x_perm, const void* gu_saved,
+                              const void* h_perm, const int32_t* offsets, int E_l, int R_cap,
+                              int H, int I, const void* w_gate, const void* w_up,
+                              const void* w_down, int dtype, void* dx_perm, float* dw_gate,
+                              float* dw_up, float* dw_down, int accumulate, void* ws,
+                              size_t ws_bytes, void* stream, void* wgrad_stream);
+
 /* Backward of moe_route, given the gradient d_topk_w [T,k] of the gate weights:
  *   d_logits[t, topk_idx[t,j]] = w_j * (dw_j - sum_l w_l dw_l), 0 elsewhere  [T,E] fp32
  *   dx_router[t] = sum_e d_logits[t,e] * w_router[:,e]      [T,H] fp32 or NULL

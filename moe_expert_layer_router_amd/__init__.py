@@ -53,6 +53,8 @@ def _load():
         "moe_combine_dx": ([P, P, P, P, P, P, I32, I32, I32, I32, I32, P, P, SZ, P], I32),
         "moe_grouped_ffn_bwd": ([P, P, P, P, P, I32, I32, I32, I32, P, P, P, I32, P, P, P, P, I32,
                                  P, SZ, P], I32),
+        "moe_grouped_ffn_bwd_split": ([P, P, P, P, P, I32, I32, I32, I32, P, P, P, I32, P, P, P, P,
+                                       I32, P, SZ, P, P], I32),
         "moe_route_bwd": ([P, P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, SZ, P], I32),
         "moe_quantize_fp8": ([P, I32, I32, I32, P, P, P, P], I32),
         "moe_grouped_ffn_fwd_fp8": ([P, P, P, P, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, P,

@@ -410,12 +410,12 @@ int moe_combine_bwd(const void* dy, const void* y_perm, const float* topk_w,
                     fn);
 }
 
-int moe_grouped_ffn_bwd(const void* dy_perm, const void* x_perm, const void* gu_saved,
-                        const void* h_perm, const int32_t* offsets, int E_l, int R_cap, int H,
-                        int I, const void* w_gate, const void* w_up, const void* w_down,
-                        int dtype, void* dx_perm, float* dw_gate, float* dw_up, float* dw_down,
-                        int accumulate, void* ws, size_t ws_bytes, void* stream) {
-  const char* fn = "moe_grouped_ffn_bwd";
+namespace {
+int ffn_bwd(const char* fn, const void* dy_perm, const void* x_perm, const void* gu_saved,
+            const void* h_perm, const int32_t* offsets, int E_l, int R_cap, int H, int I,
+            const void* w_gate, const void* w_up, const void* w_down, int dtype, void* dx_perm,
+            float* dw_gate, float* dw_up, float* dw_down, int accumulate, void* ws,
+            size_t ws_bytes, void* stream, void* wgrad_stream) {
   if (int rc = check_dtype(dtype, fn)) return rc;
   if (int rc = check_ffn_shape(E_l, R_cap, H, I, dtype, fn)) return rc;
   if (accumulate != 0 && accumulate != 1) return fail(MOE_EINVAL, "%s: accumulate must be 0 or 1", fn);
@@ -440,13 +440,40 @@ int moe_grouped_ffn_bwd(const void* dy_perm, const void* x_perm, const void* gu_
     e = launch_ffn_bwd_bf16((const bf16_t*)dy_perm, (const bf16_t*)x_perm,
                             (const bf16_t*)gu_saved, (const bf16_t*)h_perm, offsets, E_l, R_cap, H,
                             I, (const bf16_t*)w_gate, (const bf16_t*)w_up, (const bf16_t*)w_down,
-                            (bf16_t*)dx_perm, dw_gate, dw_up, dw_down, accumulate != 0, ws, s);
+                            (bf16_t*)dx_perm, dw_gate, dw_up, dw_down, accumulate != 0, ws, s,
+                            (hipStream_t)wgrad_stream);
   else
     e = launch_ffn_bwd_f32((const float*)dy_perm, (const float*)x_perm, (const float*)gu_saved,
                            (const float*)h_perm, offsets, E_l, R_cap, H, I, (const float*)w_gate,
                            (const float*)w_up, (const float*)w_down, (float*)dx_perm, dw_gate,
                            dw_up, dw_down, accumulate != 0, (float*)ws, s);
+  if (e == hipSuccess && wgrad_stream != nullptr && dtype != MOE_BF16)
+    e = order_after(s, (hipStream_t)wgrad_stream);  // weight gradients in wgrad_stream's order
   return hip_status(e, fn);
+}
+}  // namespace
+
+int moe_grouped_ffn_bwd(const void* dy_perm, const void* x_perm, const void* gu_saved,
+                        const void* h_perm, const int32_t* offsets, int E_l, int R_cap, int H,
+                        int I, const void* w_gate, const void* w_up, const void* w_down,
+                        int dtype, void* dx_perm, float* dw_gate, float* dw_up, float* dw_down,
+                        int accumulate, void* ws, size_t ws_bytes, void* stream) {
+  return ffn_bwd("moe_grouped_ffn_bwd", dy_perm, x_perm, gu_saved, h_perm, offsets, E_l, R_cap, H,
+                 I, w_gate, w_up, w_down, dtype, dx_perm, dw_gate, dw_up, dw_down, accumulate, ws,
+                 ws_bytes, stream, nullptr);
+}
+
+int moe_grouped_ffn_bwd_split(const void* dy_perm, const void* x_perm, const void* gu_saved,
+                              const void* h_perm, const int32_t* offsets, int E_l, int R_cap,
+                              int H, int I, const void* w_gate, const void* w_up,
+                              const void* w_down, int dtype, void* dx_perm, float* dw_gate,
+                              float* dw_up, float* dw_down, int accumulate, void* ws,
+                              size_t ws_bytes, void* stream, void* wgrad_stream) {
+  if (wgrad_stream == nullptr || wgrad_stream == stream)
+    return fail(MOE_EINVAL, "moe_grouped_ffn_bwd_split: wgrad_stream must be a second stream");
+  return ffn_bwd("moe_grouped_ffn_bwd_split", dy_perm, x_perm, gu_saved, h_perm, offsets, E_l,
+                 R_cap, H, I, w_gate, w_up, w_down, dtype, dx_perm, dw_gate, dw_up, dw_down,
+                 accumulate, ws, ws_bytes, stream, wgrad_stream);
 }
 
 int moe_route_bwd(const float* d_topk_w, const float* topk_w, const int32_t* topk_idx,

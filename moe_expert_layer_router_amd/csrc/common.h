@@ -163,12 +163,14 @@ hipError_t launch_ffn_fwd_fp8(const uint8_t* x_q, const float* x_scale, const in
                               bf16_t* gu, bf16_t* h_perm, bf16_t* y_perm, void* ws, hipStream_t s);
 hipError_t launch_quantize_fp8(const void* src, int rows, int cols, bool bf16,
                                const int32_t* nrows, uint8_t* q, float* scale, hipStream_t s);
+hipError_t order_after(hipStream_t s, hipStream_t waiter);
 hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, const bf16_t* gu,
                                const bf16_t* h_perm, const int32_t* offsets, int E_l, int R_cap,
                                int H, int I, const bf16_t* w_gate, const bf16_t* w_up,
                                const bf16_t* w_down, bf16_t* dx_perm, float* dw_gate,
                                float* dw_up, float* dw_down, bool accumulate, void* ws,
-                               hipStream_t s);
+                               hipStream_t s,
+                               hipStream_t wgrad_stream = nullptr);
 // X^T . [dz_hi | dz_lo] split over token chunks: partials [nsplit][H][2E] fp32.
 hipError_t launch_dw_router_bf16(const bf16_t* x, const bf16_t* dz_hilo, int T, int H, int E,
                                  int nsplit, int32_t* split_offsets, float* partials,

@@ -1428,12 +1428,20 @@ static SideStream* side_stream() {
   return &ss;
 }
 
+// waiter runs the rest of its work after everything enqueued on s so far.
+hipError_t order_after(hipStream_t s, hipStream_t waiter) {
+  SideStream* side = side_stream();
+  if (side == nullptr) return hipErrorNotInitialized;
+  hipError_t e = hipEventRecord(side->join, s);
+  return e == hipSuccess ? hipStreamWaitEvent(waiter, side->join, 0) : e;
+}
+
 hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, const bf16_t* gu,
                                const bf16_t* h_perm, const int32_t* offsets, int E_l, int R_cap,
                                int H, int I, const bf16_t* w_gate, const bf16_t* w_up,
                                const bf16_t* w_down, bf16_t* dx_perm, float* dw_gate,
                                float* dw_up, float* dw_down, bool accumulate, void* ws,
-                               hipStream_t s) {
+                               hipStream_t s, hipStream_t wgrad_stream) {
   int32_t* sched = (int32_t*)ws;
   bf16_t* dgu = (bf16_t*)((char*)ws + ffn_sched_bytes(R_cap, E_l));
   int32_t* ctrs = ffn_tile_ctrs(ws, R_cap, E_l);
@@ -1446,12 +1454,14 @@ hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, cons
   //   s2: wait(fork) -> DOWN_WGRAD -> wait(mid) -> GATEUP_WGRAD -> (join)
   // The data-gradient products leave CUs idle on this layer's shapes (few N
   // tiles, a short last round), which the weight-gradient tiles then use.
+  // wgrad_stream (a caller's stream, not joined here) takes the place of the
+  // side stream when given.
   SideStream* side = side_stream();
   hipStream_t s2 = s;
   if (side != nullptr) {
+    s2 = wgrad_stream != nullptr ? wgrad_stream : side->s;
     if ((err = hipEventRecord(side->fork, s)) != hipSuccess) return err;
-    if ((err = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return err;
-    s2 = side->s;
+    if ((err = hipStreamWaitEvent(s2, side->fork, 0)) != hipSuccess) return err;
   }
 
   // dh = dY_e W_down[e]  ->  [dG dU] through the SiLU' epilogue.
@@ -1535,7 +1545,7 @@ hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, cons
   if (side != nullptr && (err = hipStreamWaitEvent(s2, side->mid, 0)) != hipSuccess) return err;
   err = launch_gemm<K_WGRAD, kBmWgrad>(w, E_l * w.n_mtiles * w.n_ntiles, MOE_KERNEL_FFN_GATEUP_WGRAD, s2);
   if (err != hipSuccess) return err;
-  if (side != nullptr) {
+  if (side != nullptr && wgrad_stream == nullptr) {
     if ((err = hipEventRecord(side->join, s2)) != hipSuccess) return err;
     if ((err = hipStreamWaitEvent(s, side->join, 0)) != hipSuccess) return err;
   }

@@ -4,8 +4,12 @@ Chains the C-ABI calls in the order of the layer: route -> permute ->
 grouped FFN -> combine, and for the backward combine_bwd -> route_bwd ->
 grouped FFN backward -> unweighted combine of dx_perm plus the router's dx.
 All buffers and workspaces are allocated once in the constructor, so
-forward()/backward() only enqueue kernels on the current stream (and can be
-captured into a HIP graph).
+forward()/backward() only enqueue kernels (and can be captured into a HIP
+graph).  In the backward, the grouped FFN's weight gradients and then the
+router backward run on a second stream (default priority) beside the data
+gradients and the input-gradient pass; each concurrent call has its own
+workspace, and the current stream waits for the second one before
+backward() returns.
 """
 from __future__ import annotations
 
@@ -62,9 +66,16 @@ class MoELayer:
         if train:
             ops += [MOE_OP_FFN_BWD, MOE_OP_ROUTE_BWD, MOE_OP_COMBINE_DX]
         nb = max(workspace_bytes(op, T, H, I, E, k, e_lo, e_hi, self.dt) for op in ops)
-        # one workspace serves every call: the calls run one after another on one stream
+        # one workspace for the calls that run one after another on the current
+        # stream; the backward's concurrent calls get their own
         self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
         self.ws_bytes = self.ws.numel()
+        if train:
+            ws = lambda op: torch.empty(max(workspace_bytes(op, T, H, I, E, k, e_lo, e_hi, self.dt), 256),
+                                        dtype=torch.uint8, device=dev)
+            self.ws_dx = ws(MOE_OP_COMBINE_DX)
+            self.ws_rb = ws(MOE_OP_ROUTE_BWD)
+            self.side = torch.cuda.Stream(device=dev) if dev.type == "cuda" else None
 
     def forward(self, x, w_router, w_gate, w_up, w_down, bias=None, save_logits=True):
         b, T, H, I, E, k = self.buf, self.T, self.H, self.I, self.E, self.k
@@ -93,17 +104,26 @@ class MoELayer:
         _check(lib.moe_combine_bwd(_p(dy), _p(b["y_perm"]), _p(b["topk_w"]), _p(b["dest_row"]), T, H,
                                    k, self.dt, _p(b["dy_perm"]), _p(b["d_topk_w"]), s),
                "moe_combine_bwd")
-        _check(lib.moe_route_bwd(_p(b["d_topk_w"]), _p(b["topk_w"]), _p(b["topk_idx"]), _p(x),
-                                 _p(w_router), T, H, E, k, self.dt, _p(b["d_logits"]),
-                                 None, _p(b["dw_router"]), ws, wsb, s), "moe_route_bwd")
-        _check(lib.moe_grouped_ffn_bwd(_p(b["dy_perm"]), _p(b["x_perm"]), _p(b["gu"]), _p(b["h_perm"]),
-                                       _p(b["offsets"]), self.E_l, self.R_cap, H, I, _p(w_gate),
-                                       _p(w_up), _p(w_down), self.dt, _p(b["dx_perm"]),
-                                       _p(b["dw_gate"]), _p(b["dw_up"]), _p(b["dw_down"]), 0, ws,
-                                       wsb, s), "moe_grouped_ffn_bwd")
+        main = torch.cuda.current_stream()
+        side = ctypes.c_void_p(self.side.cuda_stream)
+        # data gradients on this stream; the weight gradients continue on the side stream
+        _check(lib.moe_grouped_ffn_bwd_split(_p(b["dy_perm"]), _p(b["x_perm"]), _p(b["gu"]),
+                                             _p(b["h_perm"]), _p(b["offsets"]), self.E_l, self.R_cap,
+                                             H, I, _p(w_gate), _p(w_up), _p(w_down), self.dt,
+                                             _p(b["dx_perm"]), _p(b["dw_gate"]), _p(b["dw_up"]),
+                                             _p(b["dw_down"]), 0, ws, wsb, s, side),
+               "moe_grouped_ffn_bwd_split")
         # input gradient: the experts' part and the router's part in one pass
         _check(lib.moe_combine_dx(_p(b["dx_perm"]), _p(b["dest_row"]), _p(b["d_topk_w"]),
                                   _p(b["topk_w"]), _p(b["topk_idx"]), _p(w_router), T, H, E, k,
-                                  self.dt, _p(b["dx"]), ws, wsb, s), "moe_combine_dx")
+                                  self.dt, _p(b["dx"]), _p(self.ws_dx), self.ws_dx.numel(), s),
+               "moe_combine_dx")
+        # router backward behind the weight gradients (the side stream already
+        # waits for d_topk_w: the FFN call forked it after the combine backward)
+        _check(lib.moe_route_bwd(_p(b["d_topk_w"]), _p(b["topk_w"]), _p(b["topk_idx"]), _p(x),
+                                 _p(w_router), T, H, E, k, self.dt, _p(b["d_logits"]),
+                                 None, _p(b["dw_router"]), _p(self.ws_rb), self.ws_rb.numel(), side),
+               "moe_route_bwd")
+        main.wait_stream(self.side)
         return {n: b[n] for n in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "d_logits",
                                   "d_topk_w")}

@@ -160,6 +160,13 @@ def test_fp8_entry_points_errors():
     assert p(A, A, 64, 2040, 16, 4, 0, 16, FP8, A, A, A, A, A, A, big, S) == EINVAL   # H % 16 for codes
 
 
+def test_ffn_bwd_split_needs_a_second_stream():
+    f = lambda *a: L.moe_grouped_ffn_bwd_split(*a)
+    args = (A, A, A, A, A, 16, 512, 2048, 768, A, A, A, BF16, A, A, A, A, 0, A, 1 << 30)
+    assert f(*args, S, S) == EINVAL and "second stream" in _err()
+    assert f(*args, ctypes.c_void_p(0x1234), None) == EINVAL
+
+
 def test_combine_errors():
     c = lambda *a: L.moe_combine(*a)
     assert c(A, A, A, N, 8, 128, 0, BF16, A, S) == EINVAL
