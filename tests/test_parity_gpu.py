@@ -13,6 +13,7 @@ of the fp64 logits; and the indices must equal the fully independent oracle's
 on every token whose k-th/(k+1)-th logit margin exceeds twice that bound.
 Float outputs are compared with the oracle run on the GPU's routing.
 """
+import ctypes
 import functools
 import zlib
 
@@ -497,3 +498,68 @@ def test_layer_is_deterministic():
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
     for n in g1:
         assert torch.equal(g1[n], g2[n]), n
+
+
+def test_ffn_bwd_split_equals_single_stream():
+    """moe_grouped_ffn_bwd_split (weight gradients on a second stream) gives bit for bit
+    the results of moe_grouped_ffn_bwd."""
+    w = TRAIN.scaled(name="split", T=1024)
+    inp = _inputs(w)
+    t = _gpu_tensors(w, inp)
+    layer, _, g = run_layer(w, t)
+    b = layer.buf
+    out = {n: torch.full_like(g[n], float("nan")) for n in ("dw_gate", "dw_up", "dw_down")}
+    dxp = torch.full_like(b["dx_perm"], float("nan"))
+    moe.moe_grouped_ffn_bwd(b["dy_perm"], b["x_perm"], b["gu"], b["h_perm"], b["offsets"], t["w_gate"],
+                            t["w_up"], t["w_down"], out=dict(out, dx_perm=dxp))
+    side = torch.cuda.Stream(device=DEV)
+    out2 = {n: torch.full_like(v, float("nan")) for n, v in out.items()}
+    dxp2 = torch.full_like(dxp, float("nan"))
+    ws = torch.empty(moe.workspace_bytes(moe.MOE_OP_FFN_BWD, w.T, w.H, w.I, w.E, w.k, w.e_lo, w.e_hi,
+                                         moe.MOE_BF16), dtype=torch.uint8, device=DEV)
+    P = lambda x: ctypes.c_void_p(x.data_ptr())
+    rc = moe.lib.moe_grouped_ffn_bwd_split(
+        P(b["dy_perm"]), P(b["x_perm"]), P(b["gu"]), P(b["h_perm"]), P(b["offsets"]), w.E_l, w.T * w.k,
+        w.H, w.I, P(t["w_gate"]), P(t["w_up"]), P(t["w_down"]), moe.MOE_BF16, P(dxp2), P(out2["dw_gate"]),
+        P(out2["dw_up"]), P(out2["dw_down"]), 0, P(ws), ws.numel(),
+        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream), ctypes.c_void_p(side.cuda_stream))
+    assert rc == 0, moe.lib.moe_last_error()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    R = int(b["offsets"][-1].item())
+    assert torch.equal(dxp2[:R].view(torch.int16), dxp[:R].view(torch.int16))
+    for n in out:
+        assert torch.equal(out2[n], out[n]), n
+
+
+def test_layer_graph_replays_match_eager():
+    """The layer step (forward + backward over three streams) captured in a HIP graph:
+    every replay, with eager work of the program in between, equals the eager result."""
+    w = TRAIN.scaled(name="graph", T=1024)
+    inp = _inputs(w)
+    t = _gpu_tensors(w, inp)
+    layer = moe.MoELayer(w.T, w.H, w.I, w.E, w.k, w.e_lo, w.e_hi, t["x"].dtype, DEV)
+
+    def step():
+        layer.forward(t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"])
+        layer.backward(t["dy"], t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"])
+
+    step()
+    torch.cuda.synchronize()
+    names = ("y", "dx", "dw_router", "dw_gate", "dw_up", "dw_down", "d_logits")
+    ref = {n: layer.buf[n].clone() for n in names}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        for n in names:
+            layer.buf[n].fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for n in names:
+            a, b = layer.buf[n], ref[n]
+            same = torch.equal(a.view(torch.int16), b.view(torch.int16)) if a.dtype == torch.bfloat16 \
+                else torch.equal(a, b)
+            assert same, f"replay {r}: {n} differs from the eager result"
+        step()  # eager work between the replays
+        torch.cuda.synchronize()
