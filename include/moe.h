@@ -94,9 +94,10 @@ int64_t moe_workspace_bytes(int op, int T, int H, int I, int E, int k, int e_lo,
  *   x        [T,H] dtype          w_router [H,E] dtype      bias [E] fp32 or NULL
  *   logits   [T,E] fp32 or NULL (written when given)
  *   topk_idx [T,k] int32          topk_w   [T,k] fp32
- *   ws       MOE_OP_ROUTE workspace (bf16: the fp32 partial logits of the H
- *            slices, S*T*E*4 bytes with S = 1..H/64 chosen from T, H, E;
- *            fp32: none) */
+ *   ws       MOE_OP_ROUTE workspace: none for fp32 and for bf16 with E % 8 == 0
+ *            and E <= 128 (one launch); other bf16 shapes hold the fp32
+ *            partial logits of S slices of H, S*T*E*4 bytes with S = 1..H/64
+ *            chosen from T, H, E */
 int moe_route(const void* x, const void* w_router, const float* bias, int T, int H, int E, int k,
               int dtype, float* logits, int32_t* topk_idx, float* topk_w, void* ws,
               size_t ws_bytes, void* stream);

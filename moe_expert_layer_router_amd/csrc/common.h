@@ -83,6 +83,46 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return (bid % 8) * per + bid / 8;
 }
 
+// ---------------------------------------------------------------------------
+// buffer -> LDS DMA and explicit synchronisation
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef int rsrc_t __attribute__((ext_vector_type(4)));  // buffer descriptor (4 SGPRs)
+
+// Raw buffer descriptor: 48-bit base, stride 0, byte range nbytes, word 3 =
+// 0x00020000 (32-bit untyped data); byte offsets >= nbytes read as zero.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  rsrc_t r;
+  r[0] = (int)(uint32_t)b;
+  r[1] = (int)((b >> 32) & 0xffffu);
+  r[2] = (int)nbytes;
+  r[3] = 0x00020000;
+  return r;
+}
+
+// LDS byte address of a __shared__ pointer (wave-uniform by construction).
+__device__ __forceinline__ uint32_t lds_addr(const bf16_t* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)p);
+}
+
+// 64 lanes x 16 bytes into LDS at lds + 16 * lane.  Issued through inline asm:
+// the compiler then keeps no counter for these loads and adds no waits of its
+// own; the ring's explicit vmcnt waits and barriers order every access.
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(r) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Offset that moves a DMA beyond every buffer range used here (all below
+// 2 GiB): the hardware drops the read and writes zeros into LDS.
+constexpr uint32_t kDmaKill = 0x80000000u;
+
 }  // namespace moe
 
 // ---------------------------------------------------------------------------

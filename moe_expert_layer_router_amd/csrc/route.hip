@@ -6,17 +6,23 @@
 // gate weights = softmax over the kept logits (identical to a softmax over all
 // experts renormalised over the kept ones).
 //
-// bf16 path, two launches.  (1) A workgroup of four waves takes 128 tokens and
-// one slice of HS rows of W_r (all E experts): the slice is copied once into
-// LDS, so the L2 traffic for W_r is one slice per 128 tokens, and each wave
-// multiplies its 32 tokens' x fragments (all of the slice's loads in flight
-// at once, straight from global memory) by the slice with bf16 32x32x16
-// MFMAs, reading the W_r fragments with transposing LDS reads.  Each wave
-// stores its fp32 partial logits.  (2) One half wave per token adds the
-// slices' partials in slice order (+ bias), stores the logits, and takes the
-// top k: every lane holds up to eight logits (expert e = lane % 32 + 32 i)
-// and k rounds of a branch-free arg-max over unique (logit, id) keys pick the
-// experts.  Every sum runs in a fixed order, so logits are deterministic.
+// bf16, E % 8 == 0 and E <= 128: one launch.  A workgroup of eight waves
+// takes 32 tokens and all of W_r, each wave one eighth of H, streamed through
+// a private LDS ring by DMA (no barrier in the K loop); bf16 32x32x16 MFMAs
+// with W_r as the A operand leave each lane four consecutive experts of one
+// token.  The waves' fp32 partial logits meet in LDS, are added in wave order
+// (+ bias), and one 16-lane group per token takes the top k: each lane sorts
+// its eight (logit, id) keys once, then k rounds take the group maximum of
+// the lanes' first keys.  Nothing but logits and the selection leaves the chip.
+//
+// Other bf16 shapes, two launches.  (1) A workgroup of four waves takes 128
+// tokens and one slice of HS rows of W_r (all E experts), copied once into
+// LDS; each wave multiplies its 32 tokens' x fragments by the slice and
+// stores fp32 partial logits.  (2) One half wave per token adds the slices'
+// partials in slice order (+ bias), stores the logits and takes the top k
+// with k rounds of a branch-free arg-max over unique (logit, id) keys.
+//
+// Every sum runs in a fixed order, so logits are deterministic.
 #include "common.h"
 
 #include <math.h>
@@ -134,8 +140,9 @@ int route_slices(int T, int H, int E) {
     if (units % d == 0) S = d;
   return S;
 }
+bool route_fused(int H, int E);
 size_t route_ws_bytes(int T, int H, int E) {
-  return (size_t)route_slices(T, H, E) * T * E * sizeof(float);
+  return route_fused(H, E) ? 0 : (size_t)route_slices(T, H, E) * T * E * sizeof(float);
 }
 
 // LDS copy of a W_r slice: row h (= k of the product) holds EP bf16 (experts,
@@ -298,6 +305,310 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// bf16, one launch: a workgroup of eight waves multiplies 32 tokens by all of
+// W_r, the waves splitting H into eight ranges; the waves' partial logits are
+// added through LDS and the same workgroup takes the top k.
+// ---------------------------------------------------------------------------
+// Each wave streams its own H range through a private LDS ring, so the K loop
+// has no barrier.  A step is 16 rows of H (one MFMA k-step): W_r[h .. h+16)
+// [0 .. EP), DMA'd into the swizzled rows of the sliced kernel and read back
+// with transposing reads, DW steps ahead.  x comes in stages of 64 columns
+// (four steps): x[32 tokens][h .. h+64), whole 128-byte rows per 8 lanes, so
+// every request is a full cache line, DXQ stages ahead; the 16-byte chunks of
+// a row are XOR-swizzled by (row / 2) % 8 so that the fragment reads (32 rows
+// of one chunk) spread over all banks.  Every load is a DMA with explicit
+// counter waits.  Expert columns past E and token rows past T are read as
+// zeros (outside the buffer range), as are the stages past a wave's range,
+// which keeps the loop free of branches.
+constexpr int kRfWaves = 8;
+
+template <int NB>
+struct RfCfg {
+  static constexpr int EP = 32 * NB;
+  static constexpr int CPR = EP / 8;                  // 16-byte chunks per W_r row
+  static constexpr int DW = NB == 4 ? 3 : 4;          // W_r stages (16 rows) in the ring
+  static constexpr int DXQ = 2;                       // x stages (64 columns) in the ring
+  static constexpr int WST = 16 * EP * 2;             // bytes of one W_r stage
+  static constexpr int XST = 32 * 64 * 2;             // bytes of one x stage
+  static constexpr int RING = DW * WST + DXQ * XST;   // one wave's ring
+  static constexpr int NJ = EP > 64 ? EP / 64 : 1;   // 4-expert groups per lane in the top-k
+  static constexpr int NV = 4 * NJ;                   // logits per lane in the top-k
+  static constexpr int RLD = 64 * NJ + 4;             // fp32 pitch of a reduction row
+  static constexpr int RED = kRfWaves * 32 * RLD * 4;
+  static constexpr int LDS = kRfWaves * RING > RED ? kRfWaves * RING : RED;
+  static_assert(LDS <= 160 * 1024 && 4 * DXQ >= DW && DW >= 3, "router ring");
+  // Issue order: after step i, the W_r stage of step i + DW; after the last
+  // step of x stage q, also x stage q + DXQ.  The fragments of step i are
+  // read while step i - 1 multiplies, i.e. before the issue that follows step
+  // i - 1 (lag 1; lag 0 for step 0).  The wait leaves in flight the DMA
+  // instructions issued after the later of the two stages step i reads.
+  static constexpr int vm_wait(int s, int lag) {
+    const int i = 400 + s;
+    const int ew = i - DW, ex = (i - s) - 4 * DXQ + 3;
+    const int later = ew > ex ? ew : ex;
+    int n = 0;
+    for (int j = later; j < i - lag; ++j) {
+      const int nx = (j % 4 == 3) ? 4 : 0;
+      n += (j == later) ? (later == ex ? 0 : nx) : NB + nx;
+    }
+    return n;
+  }
+  static constexpr int NR = 1 + 2 * NB;  // LDS reads of one step's fragments
+};
+
+template <int NB, int S, int LAG>
+__device__ __forceinline__ void rf_wait() {
+  constexpr int n = RfCfg<NB>::vm_wait(S, LAG);
+  static_assert(n < 64, "vmcnt");
+  wait_vm<n>();
+}
+
+// 16-lane group reductions (xor 1, xor 2, i <-> 7 - i, i <-> 15 - i): every
+// lane of the group ends with the group's result.
+__device__ __forceinline__ float sum16_f32(float v) {
+  v += __uint_as_float(dpp32<kDppXor1>(__float_as_uint(v)));
+  v += __uint_as_float(dpp32<kDppXor2>(__float_as_uint(v)));
+  v += __uint_as_float(dpp32<kDppHalfMirror>(__float_as_uint(v)));
+  return v + __uint_as_float(dpp32<kDppMirror>(__float_as_uint(v)));
+}
+// Sorting networks (descending) on the selection keys of one lane.
+template <int NV>
+struct SortNet;
+template <>
+struct SortNet<4> {
+  static constexpr int n = 5;
+  static constexpr int a[5] = {0, 2, 0, 1, 1}, b[5] = {1, 3, 2, 3, 2};
+};
+template <>
+struct SortNet<8> {
+  static constexpr int n = 19;
+  static constexpr int a[19] = {0, 1, 4, 5, 0, 1, 2, 3, 0, 2, 4, 6, 2, 3, 1, 3, 1, 3, 5};
+  static constexpr int b[19] = {2, 3, 6, 7, 4, 5, 6, 7, 1, 3, 5, 7, 4, 5, 4, 6, 2, 4, 6};
+};
+
+__device__ __forceinline__ uint64_t max16_u64(uint64_t k) {
+  k = max_u64(k, dpp64<kDppXor1>(k));
+  k = max_u64(k, dpp64<kDppXor2>(k));
+  k = max_u64(k, dpp64<kDppHalfMirror>(k));
+  return max_u64(k, dpp64<kDppMirror>(k));
+}
+
+// k-round selection + softmax of one token held by a 16-lane group: key[i]
+// is the selection key of expert ids[i] (0 for none).  The lane's keys are
+// sorted once; a round then takes the group maximum of the lanes' first keys
+// (keys are unique, so one lane holds it) and that lane drops its first key.
+// Lane h keeps rounds h and h + 16 and writes those slots.
+template <int NV>
+__device__ __forceinline__ void topk_softmax_16(uint64_t (&key)[NV], int k, bool active,
+                                                int32_t* idx_out, float* w_out) {
+  const int h = lane_id() & 15;
+#pragma unroll
+  for (int c = 0; c < SortNet<NV>::n; ++c) {
+    const int a = SortNet<NV>::a[c], b = SortNet<NV>::b[c];
+    const uint64_t hi = max_u64(key[a], key[b]), lo = key[a] ^ key[b] ^ hi;
+    key[a] = hi;
+    key[b] = lo;
+  }
+  uint64_t mine0 = 0, mine1 = 0;
+  for (int j = 0; j < k; ++j) {
+    const uint64_t best = max16_u64(key[0]);
+    // the winning lane drops its first key (a mask, not a select: a select
+    // between neighbours becomes an indexed access over the whole array)
+    const uint64_t m = 0ull - (uint64_t)(key[0] == best);
+#pragma unroll
+    for (int i = 0; i + 1 < NV; ++i) key[i] = (key[i + 1] & m) | (key[i] & ~m);
+    key[NV - 1] &= ~m;
+    mine0 = (j == h) ? best : mine0;
+    mine1 = (j == h + 16) ? best : mine1;
+  }
+  const float z0 = key_value(mine0), z1 = key_value(mine1);
+  const float zmax = __shfl(z0, lane_id() & ~15, kWave);  // slot 0 of this group
+  const float ex0 = h < k ? expf(z0 - zmax) : 0.f;
+  const float ex1 = h + 16 < k ? expf(z1 - zmax) : 0.f;
+  const float sum = sum16_f32(ex0 + ex1);
+  if (active) {
+    if (h < k) {
+      idx_out[h] = key_expert(mine0);
+      w_out[h] = ex0 / sum;
+    }
+    if (h + 16 < k) {
+      idx_out[h + 16] = key_expert(mine1);
+      w_out[h + 16] = ex1 / sum;
+    }
+  }
+}
+
+template <int NB>
+__global__ __launch_bounds__(512) void route_fused_kernel(const bf16_t* __restrict__ x,
+                                                          const bf16_t* __restrict__ w,
+                                                          const float* __restrict__ bias, int T,
+                                                          int H, int E, int k,
+                                                          float* __restrict__ logits,
+                                                          int32_t* __restrict__ topk_idx,
+                                                          float* __restrict__ topk_w) {
+  using C = RfCfg<NB>;
+  extern __shared__ __align__(16) bf16_t s_rf[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int tok0 = blockIdx.x * 32;
+  const int nq = H / 64;
+  const int q0 = wave * nq / kRfWaves;
+  const int nqw = (wave + 1) * nq / kRfWaves - q0;  // this wave's x stages (may be 0)
+  const int ns = 4 * nqw;
+
+  const rsrc_t rw = make_rsrc(w, (uint32_t)H * E * 2);
+  const int rows = min(T - tok0, 32);
+  const rsrc_t rx = make_rsrc(x + (size_t)tok0 * H, (uint32_t)rows * H * 2);
+  const uint32_t ring = lds_addr(s_rf) + wave * C::RING;
+  const uint32_t xring = ring + C::DW * C::WST;
+  // byte offsets at this wave's first step / stage.  W_r: DMA instruction u
+  // fills LDS chunk p = 64 u + lane = row p / CPR, logical chunk
+  // (p % CPR) ^ swz(row).  x: instruction u fills rows 8 u + lane / 8, LDS
+  // chunk lane % 8 = logical chunk (lane % 8) ^ ((row / 2) % 8).
+  uint32_t wo[NB], xo[4];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    const int p = u * 64 + lane, r = p / C::CPR;
+    const int c = (p % C::CPR) ^ rt_swz<NB>(r);
+    wo[u] = 8 * c < E ? (uint32_t)(((64 * q0 + r) * E + 8 * c) * 2) : kDmaKill;
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = 8 * u + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    xo[u] = (uint32_t)((r * H + 64 * q0 + 8 * c) * 2);
+  }
+  const uint32_t wstep = 32u * (uint32_t)E;  // bytes of 16 rows of W_r
+
+  auto issue_w = [&](int i) {
+    const uint32_t kill = i < ns ? 0u : kDmaKill;
+    const uint32_t dst = ring + (uint32_t)(i % C::DW) * C::WST;
+#pragma unroll
+    for (int u = 0; u < NB; ++u) dma16(rw, (wo[u] + (uint32_t)i * wstep) | kill, dst + u * 1024);
+  };
+  auto issue_x = [&](int q) {
+    const uint32_t kill = q < nqw ? 0u : kDmaKill;
+    const uint32_t dst = xring + (uint32_t)(q % C::DXQ) * C::XST;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dma16(rx, (xo[u] + 128u * (uint32_t)q) | kill, dst + u * 1024);
+  };
+  // prologue: the steady state's issue order for the steps before step 0
+#pragma unroll
+  for (int j = -(4 * C::DXQ > C::DW ? 4 * C::DXQ : C::DW); j < 0; ++j) {
+    if (j + C::DW >= 0) issue_w(j + C::DW);
+    if ((j & 3) == 3 && (j >> 2) + C::DXQ >= 0) issue_x((j >> 2) + C::DXQ);
+  }
+
+  // fragments of step i: x from stage i / 4 (lane: token row lane % 32,
+  // logical chunk 2 (i % 4) + lane / 32), W_r from ring slot i % DW
+  const int arow = lane & 31;
+  const bf16_t* xbase = s_rf + (wave * C::RING + C::DW * C::WST) / 2 + arow * 64;
+  auto read_frags = [&](int i, bf16x8_t& a, bf16x8_t (&b)[NB]) {
+    const int c = (2 * (i & 3) + (lane >> 5)) ^ ((arow >> 1) & 7);
+    a = *reinterpret_cast<const bf16x8_t*>(xbase + ((i >> 2) % C::DXQ) * (C::XST / 2) + c * 8);
+    const bf16_t* sw = s_rf + (wave * C::RING + (i % C::DW) * C::WST) / 2;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) b[nb] = rt_frag<NB>(sw, 0, nb, lane);
+  };
+
+  f32x16_t acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16_t{};
+  bf16x8_t a, b[NB];
+  rf_wait<NB, 0, 0>();
+  read_frags(0, a, b);
+  for (int q = 0; q < nqw; ++q) {
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int i = 4 * q + s4;
+      // step i + 1's fragments (past the wave's range: zeros, unused) are read
+      // while step i multiplies
+      if (s4 == 0) rf_wait<NB, 1, 1>();
+      else if (s4 == 1) rf_wait<NB, 2, 1>();
+      else if (s4 == 2) rf_wait<NB, 3, 1>();
+      else rf_wait<NB, 0, 1>();
+      bf16x8_t an, bn[NB];
+      read_frags(i + 1, an, bn);
+      // the compiler keeps this order (reads of step i + 1, then the MFMAs of
+      // step i, then the refill): left free, it moves the MFMAs behind reads
+      // they do not need and waits for those too
+      __builtin_amdgcn_sched_barrier(0);
+      // W_r fragment as A (experts are the rows of the product), x as B
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[nb], a, acc[nb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // step i's slots are refilled next: its reads (older than step i + 1's)
+      // must have returned
+      asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(C::NR) : "memory");
+      issue_w(i + C::DW);
+      if (s4 == 3) issue_x(q + C::DXQ);
+      a = an;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) b[nb] = bn[nb];
+    }
+  }
+  wait_vm<0>();  // the trailing (zero-filling) stages land before LDS is reused
+  __syncthreads();
+
+  // acc[nb][q] = partial logit of expert 32 nb + 8 (q / 4) + 4 (lane / 32) + q % 4
+  // for token lane % 32: four consecutive experts per 16-byte LDS store.
+  float* red = reinterpret_cast<float*>(s_rf);  // [wave][token][RLD]
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<f32x4_t*>(red + (wave * 32 + (lane & 31)) * C::RLD + 32 * nb + 8 * g +
+                                  4 * (lane >> 5)) =
+          f32x4_t{acc[nb][4 * g], acc[nb][4 * g + 1], acc[nb][4 * g + 2], acc[nb][4 * g + 3]};
+  __syncthreads();
+  // wave w: token rows 4 w .. 4 w + 3, one per 16-lane group; lane h of a
+  // group holds experts 4 h + 64 j + 0..3.  Logit = sum over waves (H ranges
+  // ascending) + bias.
+  const int r = 4 * wave + (lane >> 4), h = lane & 15;
+  const int t = tok0 + r;
+  const bool active = t < T;
+  const bool vec = ((uintptr_t)logits & 15) == 0 && ((uintptr_t)bias & 15) == 0;
+  uint64_t key[C::NV];
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j) {
+    const int e0 = 4 * h + 64 * j;
+    f32x4_t z = f32x4_t{};
+#pragma unroll
+    for (int wv = 0; wv < kRfWaves; ++wv)
+      z += *reinterpret_cast<const f32x4_t*>(red + (wv * 32 + r) * C::RLD + e0);
+    if (e0 < E) {  // E % 8 == 0: the four experts are all valid
+      if (bias != nullptr) {
+        if (vec) {
+          z += *reinterpret_cast<const f32x4_t*>(bias + e0);
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) z[c] += bias[e0 + c];
+        }
+      }
+      if (logits != nullptr && active) {
+        if (vec) {
+          *reinterpret_cast<f32x4_t*>(logits + (size_t)t * E + e0) = z;
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) logits[(size_t)t * E + e0 + c] = z[c];
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) key[4 * j + c] = e0 < E ? topk_key(z[c], e0 + c) : 0ull;
+  }
+  const int tr = active ? t : T - 1;
+  topk_softmax_16<C::NV>(key, k, active, topk_idx + (size_t)tr * k, topk_w + (size_t)tr * k);
+}
+
+// Shapes the one-launch router takes (else the sliced two-launch path).
+bool route_fused(int H, int E) {
+  return E % 8 == 0 && E <= 128 && H % 64 == 0 && (size_t)H * E * 2 < (1u << 31) &&
+         (size_t)32 * H * 2 < (1u << 31);
+}
+
+// ---------------------------------------------------------------------------
 // fp32: one wave per token, plain FMA dot products in h order
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict__ x,
@@ -384,6 +695,17 @@ hipError_t launch_route_bf16(const bf16_t* x, const bf16_t* w_router, const floa
                              int H, int E, int k, float* logits, int32_t* topk_idx, float* topk_w,
                              float* part_ws, hipStream_t s) {
   const int nb = route_nb(E);
+  if (route_fused(H, E)) {
+    ProfScope ps(MOE_KERNEL_ROUTE, s);
+    const int grid = (T + 31) / 32;
+    if (nb == 1)
+      route_fused_kernel<1><<<grid, 512, RfCfg<1>::LDS, s>>>(x, w_router, bias, T, H, E, k, logits, topk_idx, topk_w);
+    else if (nb == 2)
+      route_fused_kernel<2><<<grid, 512, RfCfg<2>::LDS, s>>>(x, w_router, bias, T, H, E, k, logits, topk_idx, topk_w);
+    else
+      route_fused_kernel<4><<<grid, 512, RfCfg<4>::LDS, s>>>(x, w_router, bias, T, H, E, k, logits, topk_idx, topk_w);
+    return hipGetLastError();
+  }
   const int S = route_slices(T, H, E);
   const int HS = H / S;
   const dim3 grid((T + kRtTokens - 1) / kRtTokens, S);

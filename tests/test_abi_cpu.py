@@ -62,8 +62,13 @@ def _err():
 def test_workspace_bytes_and_errors():
     ws = lambda *a: L.moe_workspace_bytes(*a)
     assert ws(moe.MOE_OP_ROUTE, 16384, 2048, 768, 128, 8, 0, 128, F32) == 0
-    # bf16 router: fp32 partial logits of S slices of H (S = 4 for H=2048, E=128: 512-row slices)
-    assert ws(moe.MOE_OP_ROUTE, 16384, 2048, 768, 128, 8, 0, 128, BF16) == 4 * 16384 * 128 * 4
+    # bf16 router, E % 8 == 0 and E <= 128: one launch, no workspace
+    assert ws(moe.MOE_OP_ROUTE, 16384, 2048, 768, 128, 8, 0, 128, BF16) == 0
+    assert ws(moe.MOE_OP_ROUTE, 16384, 2048, 768, 40, 8, 0, 40, BF16) == 0
+    # other bf16 shapes: fp32 partial logits of S slices of H (E=256: the slice
+    # copy fits 128 KB of LDS at 256 rows, so S = 8; E=20: S = 4, 512-row slices)
+    assert ws(moe.MOE_OP_ROUTE, 16384, 2048, 768, 256, 8, 0, 256, BF16) == 8 * 16384 * 256 * 4
+    assert ws(moe.MOE_OP_ROUTE, 16384, 2048, 768, 20, 8, 0, 20, BF16) == 4 * 16384 * 20 * 4
     assert ws(moe.MOE_OP_PERMUTE, 16384, 2048, 768, 128, 8, 0, 128, BF16) > 16384 * 8 * 4
     assert ws(moe.MOE_OP_FFN_BWD, 8192, 2048, 768, 128, 8, 0, 16, BF16) >= 8192 * 8 * 2 * 768 * 2
     assert ws(moe.MOE_OP_PERMUTE, 0, 2048, 768, 128, 8, 0, 16, BF16) == 0
@@ -89,8 +94,9 @@ def test_route_errors():
     assert r(A, A, N, 32, 128, 8, 2, F32, N, N, A, N, 0, S) == EINVAL and "topk_idx" in _err()
     assert r(A, A, N, 32, 100, 8, 2, BF16, N, A, A, A, 1 << 20, S) == EINVAL       # H % 8
     assert r(A, A, N, 32, 96, 8, 2, BF16, N, A, A, A, 1 << 20, S) == EUNSUP        # H % 64
-    assert r(A, A, N, 32, 128, 8, 2, BF16, N, A, A, A, 100, S) == EWS and "workspace" in _err()
-    assert r(A, A, N, 32, 128, 8, 2, BF16, N, A, A, N, 0, S) == EWS
+    # E % 8 != 0: the sliced bf16 router, which needs a workspace
+    assert r(A, A, N, 32, 128, 20, 2, BF16, N, A, A, A, 100, S) == EWS and "workspace" in _err()
+    assert r(A, A, N, 32, 128, 20, 2, BF16, N, A, A, N, 0, S) == EWS
     assert r(A, A, N, 32, 128, 8, 2, 5, N, A, A, N, 0, S) == EINVAL
     # valid arguments with T == 0: nothing to enqueue, no HIP call
     assert r(A, A, N, 0, 128, 8, 2, F32, N, A, A, N, 0, S) == OK

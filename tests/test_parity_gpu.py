@@ -172,7 +172,15 @@ ROUTE_CASES = [TINY, EP_SHARE, FULL, SKEWED,
                EP_SHARE.scaled(name="route_bf16_t777_h192_e256_k16", T=777, H=192, E=256, k=16,
                                e_lo=0, e_hi=256),
                EP_SHARE.scaled(name="route_bf16_t301_h320_e40_k5", T=301, H=320, E=40, k=5,
-                               e_lo=0, e_hi=40)]
+                               e_lo=0, e_hi=40),
+               # two 32-token tiles per workgroup, ragged last workgroup
+               EP_SHARE.scaled(name="route_bf16_t16411_h256_e128_k8", T=16411, H=256),
+               # 4 K steps over 8 waves (some waves have none), one 8-expert chunk
+               EP_SHARE.scaled(name="route_bf16_t1000_h64_e8_k2", T=1000, H=64, E=8, k=2, e_lo=0,
+                               e_hi=8),
+               # E % 8 != 0: the sliced two-launch router
+               EP_SHARE.scaled(name="route_bf16_t515_h192_e20_k3", T=515, H=192, E=20, k=3,
+                               e_lo=0, e_hi=20)]
 
 
 @pytest.mark.parametrize("w", ROUTE_CASES, ids=lambda w: w.name)
