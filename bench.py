@@ -260,6 +260,33 @@ def fp8_ffn_bench(w, args):
     }
 
 
+def step_stats(run, n, dev):
+    """Per-step times after the timed region: each step bracketed by its own
+    event pair, median / p10 / p90 over n steps.  "warm": back to back, so the
+    weights stay in the 256 MiB Infinity Cache and L2 between steps.  "cold":
+    a 512 MiB buffer is written before each step's start event (outside the
+    bracket), which evicts the previous step's data from both caches."""
+    import torch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    out = {}
+    for mode in ("warm", "cold"):
+        ts = []
+        for i in range(n):
+            if mode == "cold":
+                flush.fill_(i & 0xff)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            run()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        ts.sort()
+        q = lambda f: ts[min(len(ts) - 1, int(round(f * (len(ts) - 1))))]
+        out[mode] = {"median": round(q(0.5), 4), "p10": round(q(0.1), 4), "p90": round(q(0.9), 4)}
+    del flush
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -269,6 +296,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-times", action="store_true")
+    ap.add_argument("--no-step-stats", action="store_true",
+                    help="skip the per-step warm / cold (cache-flushed) timing pass")
     ap.add_argument("--fp8-ffn", action="store_true",
                     help="instead of the layer step: time the grouped FFN forward in bf16 and in the "
                          "FP8 recipe on the same routing (default workload: the full 128-expert layer)")
@@ -364,6 +393,9 @@ def main():
         "flops_per_step": flops,
         "wall_s_timed_region": round(wall, 3),
     }
+
+    if not args.no_step_stats:
+        result["step_ms"] = step_stats(run, args.steps, dev)
 
     if not args.no_kernel_times:
         # Live per-kernel durations: events recorded by the library around each
