@@ -200,6 +200,14 @@ def silu(a) -> np.ndarray:
     return a * sigmoid(a)
 
 
+def swiglu_grad(dh, g, u):
+    """Gradients of h = SiLU(g) * u for the upstream gradient dh:
+    dg = dh * u * s * (1 + g (1 - s)) and du = dh * SiLU(g), s = sigmoid(g)."""
+    dh, g, u = _f64(dh), _f64(g), _f64(u)
+    s = sigmoid(g)
+    return dh * u * s * (1.0 + g * (1.0 - s)), dh * (g * s)
+
+
 def expert_ffn_parts(v, w_gate_e, w_up_e, w_down_e) -> Dict[str, np.ndarray]:
     """One expert on rows v [n, H]: g = v.W_gate^T, u = v.W_up^T,
     h = SiLU(g) * u, y = h.W_down^T  (W_gate/W_up [I, H], W_down [H, I])."""
@@ -402,6 +410,47 @@ def moe_forward_fp8(x, idx, w, w_gate, w_up, w_down, e_lo: int, e_hi: int) -> np
 
 
 # --------------------------------------------------------------------------
+# FP8 variant of the expert data gradients (backward)
+# --------------------------------------------------------------------------
+# The pages fix no FP8 backward either.  Readings, on top of the forward's:
+#   - the two data-gradient products run on E4M3 codes with per-row
+#     power-of-two scales: the rows of dy (grouped rows, over H); the down
+#     weight per input channel (a row of W_down^T, over H); the gate and up
+#     weights per input channel h, over their 2I concatenated columns (a row
+#     of [W_gate^T | W_up^T]);
+#   - dh is rounded to bf16; dg, du follow from dh and the saved g, u as in the
+#     bf16 backward and are rounded to bf16 (the weight gradients, which stay
+#     bf16, take them as they are); the rows of [dg | du] are quantized for
+#     the gate / up data gradient.
+
+def quantize_expert_weights_t_fp8(w0, w1=None):
+    """Per-input-channel codes of expert weights w0 [E_l, N, K] (and w1 of the
+    same shape): the rows of [w0^T | w1^T] quantized, codes [E_l, K, N] (or
+    [E_l, K, 2N]) and scales [E_l, K]."""
+    parts = [_f64(w0).transpose(0, 2, 1)]
+    if w1 is not None:
+        parts.append(_f64(w1).transpose(0, 2, 1))
+    a = np.concatenate(parts, axis=2)
+    El, K, N = a.shape
+    q, s = quantize_rows_fp8(a.reshape(El * K, N))
+    return q.reshape(El, K, N), s.reshape(El, K)
+
+
+def expert_dgrad_fp8_parts(dyq, sdy, g, u, wdtq, sdt, wgutq, sgut) -> Dict[str, np.ndarray]:
+    """Data gradients of one expert on quantized rows: dh = bf16 of the
+    product of the dy rows (dyq, sdy) with the rows of W_down^T (wdtq, sdt);
+    [dg | du] = bf16 of swiglu_grad(dh, g, u), its rows quantized (dguq,
+    sdgu); dx = the product with the rows of [W_gate^T | W_up^T] (wgutq,
+    sgut)."""
+    dh = round_bf16(fp8_matmul_rows(dyq, sdy, wdtq, sdt))
+    dg, du = swiglu_grad(dh, g, u)
+    dgu = round_bf16(np.concatenate([dg, du], axis=1))
+    dguq, sdgu = quantize_rows_fp8(dgu)
+    dx = fp8_matmul_rows(dguq, sdgu, wgutq, sgut)
+    return {"dh": dh, "dgu": dgu, "dguq": dguq, "sdgu": sdgu, "dx": dx}
+
+
+# --------------------------------------------------------------------------
 # Backward
 # --------------------------------------------------------------------------
 
@@ -475,9 +524,7 @@ def moe_backward(x, w_router, idx, w, w_gate, w_up, w_down, dy, e_lo: int, e_hi:
         delta = w[tt, jj][:, None] * dy[tt]
         dWd[e - e_lo] = delta.T @ h
         dh = delta @ Wd
-        s = sigmoid(g)
-        dg = dh * u * s * (1.0 + g * (1.0 - s))
-        du = dh * (g * s)
+        dg, du = swiglu_grad(dh, g, u)
         dWg[e - e_lo] = dg.T @ x[tt]
         dWu[e - e_lo] = du.T @ x[tt]
         np.add.at(dx, tt, dg @ Wg + du @ Wu)

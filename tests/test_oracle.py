@@ -451,6 +451,59 @@ def check_fp8_forward_close_to_exact():
     assert np.array_equal(parts["g"], exact["g"]) and np.array_equal(parts["u"], exact["u"])
 
 
+def check_fp8_weight_t_scales_per_input_channel():
+    """The transposed weight quantization scales each input channel (a column of
+    the stored [N, K] weight, over N; for gate / up over both matrices) by the
+    smallest power of two that brings its maximum to <= 448, and its codes
+    decode to that column within the E4M3 step."""
+    rng = np.random.default_rng(9)
+    w0 = rng.standard_normal((2, 12, 10)) * np.exp2(rng.integers(-12, 12, size=(2, 1, 10)))
+    w1 = rng.standard_normal((2, 12, 10)) * np.exp2(rng.integers(-12, 12, size=(2, 1, 10)))
+    for q, sc, cols in ((*O.quantize_expert_weights_t_fp8(w0), np.abs(w0).max(axis=1)),
+                        (*O.quantize_expert_weights_t_fp8(w0, w1),
+                         np.maximum(np.abs(w0).max(axis=1), np.abs(w1).max(axis=1)))):
+        assert q.shape[:2] == (2, 10) and sc.shape == (2, 10)
+        assert np.all(cols <= 448.0 * sc) and np.all(cols > 224.0 * sc)
+    q, sc = O.quantize_expert_weights_t_fp8(w0, w1)
+    back = O.fp8_e4m3_decode(q) * sc[:, :, None]
+    ref = np.concatenate([w0.transpose(0, 2, 1), w1.transpose(0, 2, 1)], axis=2)
+    assert np.all(np.abs(back - ref) <= np.maximum(2.0 ** -4 * np.abs(ref), sc[:, :, None] * 2.0 ** -10))
+
+
+def check_fp8_dgrad_close_to_exact():
+    """The FP8 data gradients of one expert stay near the exact ones (five
+    quantized operands, each within 2^-4 relative: rel-L2 under 12%; a swapped
+    gate / up order or a dropped scale lands far outside).  On dy and W_down on
+    the E4M3 grid with every quantized row's maximum 448 (scale 1), dh is the
+    bf16 of the exact product."""
+    rng = np.random.default_rng(10)
+    n, H, I = 24, 64, 32
+    x = rng.standard_normal((n, H))
+    wg, wu = rng.standard_normal((1, I, H)) / 8, rng.standard_normal((1, I, H)) / 8
+    wd = rng.standard_normal((1, H, I)) / 6
+    dy = rng.standard_normal((n, H))
+    g, u = x @ wg[0].T, x @ wu[0].T
+    dg, du = O.swiglu_grad(dy @ wd[0], g, u)
+    exact = dg @ wg[0] + du @ wu[0]
+    dyq, sdy = O.quantize_rows_fp8(dy)
+    qd, sd = O.quantize_expert_weights_t_fp8(wd)
+    qgu, sgu = O.quantize_expert_weights_t_fp8(wg, wu)
+    p = O.expert_dgrad_fp8_parts(dyq, sdy, g, u, qd[0], sd[0], qgu[0], sgu[0])
+    assert _rel(p["dx"], exact) < 0.12
+    assert np.array_equal(p["dgu"], O.round_bf16(p["dgu"]))
+    grid = O.fp8_e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    pick = lambda *sh: rng.choice(np.concatenate([grid, -grid]), size=sh)
+    dy2, wd2 = pick(5, 16), pick(1, 16, 8)
+    dy2[:, 0] = 448.0
+    wd2[0, 0, :] = 448.0          # every input channel (column) reaches 448
+    dyq2, sdy2 = O.quantize_rows_fp8(dy2)
+    qd2, sd2 = O.quantize_expert_weights_t_fp8(wd2)
+    assert (sdy2 == 1.0).all() and (sd2 == 1.0).all()
+    p2 = O.expert_dgrad_fp8_parts(dyq2, sdy2, np.zeros((5, 8)), np.zeros((5, 8)), qd2[0], sd2[0],
+                                  np.zeros((16, 16), np.uint8), np.ones(16))
+    assert np.array_equal(p2["dh"], O.round_bf16(dy2 @ wd2[0]))
+
+
 ALL_CHECKS = [check_gating_golden, check_topk_brute_force, check_zero_input_routing,
               check_duplicate_router_columns, check_k1_and_kE, check_weights_sum_to_one,
               check_counts_offsets, check_permutation_maps, check_permute_unpermute_identity,
@@ -458,7 +511,8 @@ ALL_CHECKS = [check_gating_golden, check_topk_brute_force, check_zero_input_rout
               check_zero_projection_gives_zero, check_scalar_golden, check_backward_vs_autograd,
               check_finite_differences, check_router_grads_vs_autograd, check_fp8_codes_vs_torch,
               check_fp8_row_scale_is_minimal, check_fp8_matmul_brute_force,
-              check_fp8_forward_close_to_exact]
+              check_fp8_forward_close_to_exact, check_fp8_weight_t_scales_per_input_channel,
+              check_fp8_dgrad_close_to_exact]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
@@ -549,9 +603,25 @@ def _mut_fp8_scale_wrong_axis(aq, sa, bq, sb):
     return acc * np.asarray(sa, np.float64)[:, None] * np.asarray(sb, np.float64)[:n].mean()
 
 
+def _mut_fp8_t_gate_up_swapped(w0, w1=None):
+    return _ORIG["quantize_expert_weights_t_fp8"](w1, w0) if w1 is not None else \
+        _ORIG["quantize_expert_weights_t_fp8"](w0)
+
+
+def _mut_fp8_t_scales_per_output_channel(w0, w1=None):
+    """codes of the transposed layout, but each scale taken over the output channel"""
+    a = [np.asarray(w0, np.float64)] + ([] if w1 is None else [np.asarray(w1, np.float64)])
+    a = np.concatenate([m.transpose(0, 2, 1) for m in a], axis=2)
+    El, K, N = a.shape
+    amax = np.abs(a).max(axis=1, keepdims=True)              # over K, per output channel
+    sc = np.exp2(OM.fp8_row_exponent(amax.reshape(-1)).astype(np.float64)).reshape(El, 1, N)
+    q = OM.fp8_e4m3_encode(a / sc)
+    return q, np.broadcast_to(sc.max(axis=2), (El, K)).copy()
+
+
 _ORIG = {n: getattr(OM, n) for n in ("silu", "topk_experts", "gate_weights", "permutation_maps",
                                      "moe_backward", "expert_ffn_parts", "fp8_e4m3_encode",
-                                     "fp8_row_exponent")}
+                                     "fp8_row_exponent", "quantize_expert_weights_t_fp8")}
 
 MUTATIONS = [("silu", _mut_silu_is_sigmoid), ("topk_experts", _mut_topk_ties_high),
              ("gate_weights", _mut_no_renorm), ("permutation_maps", _mut_group_tokens_descending),
@@ -561,7 +631,9 @@ MUTATIONS = [("silu", _mut_silu_is_sigmoid), ("topk_experts", _mut_topk_ties_hig
              ("router_input_grad", _mut_router_dx_transposed_sign),
              ("fp8_e4m3_encode", _mut_fp8_round_half_away),
              ("fp8_row_exponent", _mut_fp8_exponent_one_high),
-             ("fp8_matmul_rows", _mut_fp8_scale_wrong_axis)]
+             ("fp8_matmul_rows", _mut_fp8_scale_wrong_axis),
+             ("quantize_expert_weights_t_fp8", _mut_fp8_t_gate_up_swapped),
+             ("quantize_expert_weights_t_fp8", _mut_fp8_t_scales_per_output_channel)]
 
 
 @pytest.mark.parametrize("name,mut", MUTATIONS, ids=[m[1].__name__ for m in MUTATIONS])
