@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -66,7 +66,8 @@ typedef enum {
   MOE_OP_FFN_BWD = 3,
   MOE_OP_ROUTE_BWD = 4,
   MOE_OP_COMBINE_DX = 5,
-  MOE_OP_FFN_FWD_FP8 = 6
+  MOE_OP_FFN_FWD_FP8 = 6,
+  MOE_OP_FFN_DGRAD_FP8 = 7
 } moe_op;
 
 /* Returns MOE_ABI_VERSION of the loaded library. */
@@ -173,6 +174,38 @@ int moe_grouped_ffn_fwd_fp8(const uint8_t* x_q, const float* x_scale, const int3
                             const float* wu_scale, const uint8_t* wd_q, const float* wd_scale,
                             void* gu_saved, void* h_perm, void* y_perm, void* ws, size_t ws_bytes,
                             void* stream);
+
+/* Per-input-channel E4M3 codes of expert weights, for the FP8 data
+ * gradients (same scale rule as moe_quantize_fp8, applied to the columns):
+ * with src0 (and src1, or NULL) [batch,N,K] bf16, row k of batch b of the
+ * output is column k of src0[b] followed by column k of src1[b]:
+ *   q [batch,K,n*N] uint8 (n = 1 or 2), scale [batch,K] fp32.
+ * W_down [E_l,H,I] gives the rows of W_down^T ([E_l,I,H]); W_gate and W_up
+ * [E_l,I,H] give the rows of [W_gate^T | W_up^T] ([E_l,H,2I]).
+ * N % 64 == 0 and K % 64 == 0 (else MOE_EUNSUPPORTED); pointers 16-byte
+ * aligned. */
+int moe_quantize_fp8_t(const void* src0, const void* src1, int batch, int N, int K, int dtype,
+                       uint8_t* q, float* scale, void* stream);
+
+/* Data gradients of the grouped SwiGLU FFN on E4M3 codes (the weight
+ * gradients stay with moe_grouped_ffn_bwd in bf16).  With dy_q / dy_scale the
+ * rows of dy_perm quantized by moe_quantize_fp8, wdt_* the codes of W_down^T
+ * and wgut_* those of [W_gate^T | W_up^T] from moe_quantize_fp8_t:
+ *   dh[r,i]  = bf16(dy_scale[r] * wdt_scale[e,i] * sum_h code(dy_q[r,h]) code(wdt_q[e,i,h]))
+ *   dg, du   = SiLU derivative of the saved g, u (as moe_grouped_ffn_bwd);
+ *   dgu[r]   = bf16([dg | du]), its row quantized as moe_quantize_fp8 does
+ *   dx_perm[r,m] = bf16(sdgu[r] * wgut_scale[e,m] * sum_c code(dguq[r,c]) code(wgut_q[e,m,c]))
+ * Code products are exact and summed in fp32.
+ *   dy_q [R_cap,H] uint8, dy_scale [R_cap] fp32, gu_saved [R_cap,2I] bf16,
+ *   wdt_q [E_l,I,H] uint8 / wdt_scale [E_l,I], wgut_q [E_l,H,2I] uint8 /
+ *   wgut_scale [E_l,H], dgu [R_cap,2I] bf16 (out), dx_perm [R_cap,H] bf16 (out)
+ *   ws       MOE_OP_FFN_DGRAD_FP8 workspace (schedule, dh, codes of [dg | du])
+ * Needs H % 128 == 0, I % 128 == 0 and I <= 2048 (else MOE_EUNSUPPORTED). */
+int moe_grouped_ffn_dgrad_fp8(const uint8_t* dy_q, const float* dy_scale, const void* gu_saved,
+                              const int32_t* offsets, int E_l, int R_cap, int H, int I,
+                              const uint8_t* wdt_q, const float* wdt_scale, const uint8_t* wgut_q,
+                              const float* wgut_scale, void* dgu, void* dx_perm, void* ws,
+                              size_t ws_bytes, void* stream);
 
 /* Weighted unpermute ("combine"): for every token, in slot order j = 0..k-1,
  *   y[t] = sum_{j: dest_row[t*k+j] >= 0} topk_w[t,j] * y_perm[dest_row[t*k+j]]  (+ addend[t])

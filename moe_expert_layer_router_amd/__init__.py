@@ -9,7 +9,8 @@ an error.
 
 Functions keep the C names (moe_route, moe_permute, moe_grouped_ffn_fwd,
 moe_combine, moe_combine_bwd, moe_grouped_ffn_bwd, moe_route_bwd, and the FP8
-forward: moe_quantize_fp8, moe_grouped_ffn_fwd_fp8) and return
+forward: moe_quantize_fp8, moe_grouped_ffn_fwd_fp8; data gradients:
+moe_quantize_fp8_t, moe_grouped_ffn_dgrad_fp8) and return
 freshly allocated torch tensors; each also accepts preallocated outputs via
 ``out=`` dictionaries so that steady-state loops allocate nothing.
 """
@@ -26,8 +27,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_F32, MOE_BF16, MOE_FP8 = 0, 1, 2
 (MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD, MOE_OP_ROUTE_BWD,
- MOE_OP_COMBINE_DX, MOE_OP_FFN_FWD_FP8) = range(7)
-ABI_VERSION = 2
+ MOE_OP_COMBINE_DX, MOE_OP_FFN_FWD_FP8, MOE_OP_FFN_DGRAD_FP8) = range(8)
+ABI_VERSION = 3
 
 
 class MoEError(RuntimeError):
@@ -57,6 +58,8 @@ def _load():
                                        I32, P, SZ, P, P], I32),
         "moe_route_bwd": ([P, P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, SZ, P], I32),
         "moe_quantize_fp8": ([P, I32, I32, I32, P, P, P, P], I32),
+        "moe_quantize_fp8_t": ([P, P, I32, I32, I32, I32, P, P, P], I32),
+        "moe_grouped_ffn_dgrad_fp8": ([P, P, P, P, I32, I32, I32, I32, P, P, P, P, P, P, P, SZ, P], I32),
         "moe_grouped_ffn_fwd_fp8": ([P, P, P, P, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, P,
                                      SZ, P], I32),
         "moe_profile_kernel": ([I32, ctypes.POINTER(P), ctypes.POINTER(P), I32], I32),
@@ -355,4 +358,46 @@ def moe_grouped_ffn_fwd_fp8(x_q: torch.Tensor, x_scale: torch.Tensor, src_row: t
                                        _ptr(wu[1]), _ptr(wd[0]), _ptr(wd[1]), _ptr(o["gu"]),
                                        _ptr(o["h_perm"]), _ptr(o["y_perm"]), _ptr(ws), _nbytes(ws),
                                        _stream()), "moe_grouped_ffn_fwd_fp8")
+    return o
+
+
+def moe_quantize_fp8_t(w0: torch.Tensor, w1: Optional[torch.Tensor] = None,
+                       out: Optional[Dict[str, torch.Tensor]] = None):
+    """Per-input-channel E4M3 codes of bf16 expert weights w0 (and w1) [E_l, N, K]:
+    rows of [w0^T | w1^T].  Returns (q uint8 [E_l, K, n N], scale fp32 [E_l, K])."""
+    B, N, K = w0.shape
+    n = 1 if w1 is None else 2
+    o = dict(out or {})
+    o.setdefault("q", torch.empty((B, K, n * N), dtype=torch.uint8, device=w0.device))
+    o.setdefault("scale", torch.empty((B, K), dtype=torch.float32, device=w0.device))
+    _check(lib.moe_quantize_fp8_t(_ptr(w0), _ptr(w1), B, N, K, _dtype_code(w0), _ptr(o["q"]),
+                                  _ptr(o["scale"]), _stream()), "moe_quantize_fp8_t")
+    return o["q"], o["scale"]
+
+
+def moe_grouped_ffn_dgrad_fp8(dy_q: torch.Tensor, dy_scale: torch.Tensor, gu: torch.Tensor,
+                              offsets: torch.Tensor, wdt: tuple, wgut: tuple,
+                              ws: Optional[torch.Tensor] = None,
+                              out: Optional[Dict[str, torch.Tensor]] = None):
+    """Data gradients of the grouped SwiGLU FFN on E4M3 codes.  dy_q [R_cap, H] uint8
+    with per-row dy_scale [R_cap]; gu [R_cap, 2I] bf16 (saved g, u); wdt = (codes
+    [E_l, I, H], scales [E_l, I]) of W_down^T; wgut = (codes [E_l, H, 2I], scales
+    [E_l, H]) of [W_gate^T | W_up^T].  Returns dict dgu [R_cap, 2I] and dx_perm
+    [R_cap, H] (bf16)."""
+    R_cap, H = dy_q.shape
+    E_l, I, _ = wdt[0].shape
+    dev = dy_q.device
+    o = dict(out or {})
+    o.setdefault("dgu", torch.empty((R_cap, 2 * I), dtype=torch.bfloat16, device=dev))
+    o.setdefault("dx_perm", torch.empty((R_cap, H), dtype=torch.bfloat16, device=dev))
+    nb = lib.moe_workspace_bytes(MOE_OP_FFN_DGRAD_FP8, max(R_cap, 0), H, I, max(E_l, 1), 1, 0, E_l,
+                                 MOE_BF16)
+    if nb < 0:
+        _check(int(nb), "moe_workspace_bytes")
+    ws = _ws(int(nb), dev, ws)
+    _check(lib.moe_grouped_ffn_dgrad_fp8(_ptr(dy_q), _ptr(dy_scale), _ptr(gu), _ptr(offsets), E_l,
+                                         R_cap, H, I, _ptr(wdt[0]), _ptr(wdt[1]), _ptr(wgut[0]),
+                                         _ptr(wgut[1]), _ptr(o["dgu"]), _ptr(o["dx_perm"]),
+                                         _ptr(ws), _nbytes(ws), _stream()),
+           "moe_grouped_ffn_dgrad_fp8")
     return o

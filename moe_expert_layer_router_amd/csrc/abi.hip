@@ -168,8 +168,8 @@ int64_t moe_workspace_bytes(int op, int T, int H, int I, int E, int k, int e_lo,
                             int dtype) {
   const char* fn = "moe_workspace_bytes";
   if (dtype == MOE_FP8) {
-    if (op != MOE_OP_PERMUTE && op != MOE_OP_FFN_FWD_FP8)
-      return fail(MOE_EINVAL, "%s: MOE_FP8 applies to MOE_OP_PERMUTE and MOE_OP_FFN_FWD_FP8 only", fn);
+    if (op != MOE_OP_PERMUTE && op != MOE_OP_FFN_FWD_FP8 && op != MOE_OP_FFN_DGRAD_FP8)
+      return fail(MOE_EINVAL, "%s: MOE_FP8 applies to MOE_OP_PERMUTE and the FP8 FFN ops only", fn);
   } else if (int rc = check_dtype(dtype, fn)) {
     return rc;
   }
@@ -183,11 +183,13 @@ int64_t moe_workspace_bytes(int op, int T, int H, int I, int E, int k, int e_lo,
       return (int64_t)ws_route_bwd(T, H, E, dtype);
     case MOE_OP_COMBINE_DX:
       return (int64_t)align256((size_t)E * H * elem_bytes(dtype));
-    case MOE_OP_FFN_FWD_FP8: {
+    case MOE_OP_FFN_FWD_FP8:
+    case MOE_OP_FFN_DGRAD_FP8: {
       if (e_lo < 0 || e_hi > E || e_lo >= e_hi)
         return fail(MOE_EINVAL, "%s: need 0 <= e_lo < e_hi <= E", fn);
       if (I <= 0) return fail(MOE_EINVAL, "%s: I must be positive", fn);
-      return (int64_t)ffn_fwd_fp8_ws_bytes(R_cap, e_hi - e_lo, I);
+      return (int64_t)(op == MOE_OP_FFN_FWD_FP8 ? ffn_fwd_fp8_ws_bytes(R_cap, e_hi - e_lo, I)
+                                                : ffn_dgrad_fp8_ws_bytes(R_cap, e_hi - e_lo, I));
     }
     case MOE_OP_PERMUTE:
     case MOE_OP_FFN_FWD:
@@ -345,6 +347,53 @@ int moe_grouped_ffn_fwd_fp8(const uint8_t* x_q, const float* x_scale, const int3
   return hip_status(launch_ffn_fwd_fp8(x_q, x_scale, src_row, offsets, E_l, R_cap, H, I, wg_q,
                                        wg_scale, wu_q, wu_scale, wd_q, wd_scale, (bf16_t*)gu_saved,
                                        (bf16_t*)h_perm, (bf16_t*)y_perm, ws, begin_launch(stream)),
+                    fn);
+}
+
+int moe_quantize_fp8_t(const void* src0, const void* src1, int batch, int N, int K, int dtype,
+                       uint8_t* q, float* scale, void* stream) {
+  const char* fn = "moe_quantize_fp8_t";
+  if (dtype != MOE_BF16) return fail(MOE_EUNSUPPORTED, "%s: needs MOE_BF16 weights", fn);
+  if (batch < 0 || N <= 0 || K <= 0)
+    return fail(MOE_EINVAL, "%s: need batch >= 0, N > 0, K > 0 (batch=%d, N=%d, K=%d)", fn, batch, N, K);
+  if (N % 64 != 0 || K % 64 != 0)
+    return fail(MOE_EUNSUPPORTED, "%s: needs N %% 64 == 0 and K %% 64 == 0 (N=%d, K=%d)", fn, N, K);
+  if (batch == 0) return MOE_OK;
+  if (int rc = check_ptr(src0, "src0", fn, true)) return rc;
+  if (src1 != nullptr && !aligned16(src1)) return fail(MOE_EINVAL, "%s: src1 must be 16-byte aligned", fn);
+  if (int rc = check_ptr(q, "q", fn, true)) return rc;
+  if (int rc = check_ptr(scale, "scale", fn)) return rc;
+  return hip_status(launch_quantize_t_fp8((const bf16_t*)src0, (const bf16_t*)src1, batch, N, K, q,
+                                          scale, begin_launch(stream)),
+                    fn);
+}
+
+int moe_grouped_ffn_dgrad_fp8(const uint8_t* dy_q, const float* dy_scale, const void* gu_saved,
+                              const int32_t* offsets, int E_l, int R_cap, int H, int I,
+                              const uint8_t* wdt_q, const float* wdt_scale, const uint8_t* wgut_q,
+                              const float* wgut_scale, void* dgu, void* dx_perm, void* ws,
+                              size_t ws_bytes, void* stream) {
+  const char* fn = "moe_grouped_ffn_dgrad_fp8";
+  if (int rc = check_ffn_shape(E_l, R_cap, H, I, MOE_FP8, fn)) return rc;
+  if (H % 128 != 0 || I % 128 != 0 || I > 2048)
+    return fail(MOE_EUNSUPPORTED, "%s: needs H %% 128 == 0, I %% 128 == 0 and I <= 2048 (H=%d, I=%d)", fn, H, I);
+  if (int rc = check_ptr(offsets, "offsets", fn)) return rc;
+  if (int rc = check_ptr(wdt_q, "wdt_q", fn, true)) return rc;
+  if (int rc = check_ptr(wgut_q, "wgut_q", fn, true)) return rc;
+  if (int rc = check_ptr(wdt_scale, "wdt_scale", fn, true)) return rc;
+  if (int rc = check_ptr(wgut_scale, "wgut_scale", fn, true)) return rc;
+  if (R_cap > 0) {
+    if (int rc = check_ptr(dy_q, "dy_q", fn, true)) return rc;
+    if (int rc = check_ptr(dy_scale, "dy_scale", fn)) return rc;
+    if (int rc = check_ptr(gu_saved, "gu_saved", fn, true)) return rc;
+    if (int rc = check_ptr(dgu, "dgu", fn, true)) return rc;
+    if (int rc = check_ptr(dx_perm, "dx_perm", fn, true)) return rc;
+  }
+  if (int rc = check_ws(ws, ws_bytes, ffn_dgrad_fp8_ws_bytes(R_cap, E_l, I), fn)) return rc;
+  if (R_cap == 0) return MOE_OK;
+  return hip_status(launch_ffn_dgrad_fp8(dy_q, dy_scale, (const bf16_t*)gu_saved, offsets, E_l,
+                                         R_cap, H, I, wdt_q, wdt_scale, wgut_q, wgut_scale,
+                                         (bf16_t*)dgu, (bf16_t*)dx_perm, ws, begin_launch(stream)),
                     fn);
 }
 

@@ -203,6 +203,19 @@ hipError_t launch_ffn_fwd_fp8(const uint8_t* x_q, const float* x_scale, const in
                               bf16_t* gu, bf16_t* h_perm, bf16_t* y_perm, void* ws, hipStream_t s);
 hipError_t launch_quantize_fp8(const void* src, int rows, int cols, bool bf16,
                                const int32_t* nrows, uint8_t* q, float* scale, hipStream_t s);
+// per-input-channel (transposed) weight codes and the SiLU derivative + row
+// quantization of the FP8 data gradients (fp8.hip)
+hipError_t launch_quantize_t_fp8(const bf16_t* src0, const bf16_t* src1, int batch, int N, int K,
+                                 uint8_t* q, float* scale, hipStream_t s);
+hipError_t launch_swiglu_bwd_fp8(const bf16_t* dh, const bf16_t* gu, int rows, int I,
+                                 const int32_t* nrows, bf16_t* dgu, uint8_t* q, float* scale,
+                                 hipStream_t s);
+size_t ffn_dgrad_fp8_ws_bytes(int R_cap, int E_l, int I);
+hipError_t launch_ffn_dgrad_fp8(const uint8_t* dy_q, const float* dy_scale, const bf16_t* gu,
+                                const int32_t* offsets, int E_l, int R_cap, int H, int I,
+                                const uint8_t* wdt_q, const float* wdt_s, const uint8_t* wgut_q,
+                                const float* wgut_s, bf16_t* dgu, bf16_t* dx_perm, void* ws,
+                                hipStream_t s);
 hipError_t order_after(hipStream_t s, hipStream_t waiter);
 hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, const bf16_t* gu,
                                const bf16_t* h_perm, const int32_t* offsets, int E_l, int R_cap,

@@ -14,6 +14,23 @@
 
 namespace moe {
 
+// Exponent of the row scale for a row maximum amax (0 for a zero row).
+__device__ __forceinline__ int fp8_exponent(float amax) {
+  int E;
+  const float f = frexpf(amax, &E);
+  return amax == 0.f ? 0 : E - 9 + (f > 0.875f ? 1 : 0);
+}
+
+// Eight values -> eight E4M3 codes of v * 2^-e (two dwords).
+__device__ __forceinline__ uint2 fp8_codes8(const float* v, int e) {
+  int w0 = 0, w1 = 0;
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[0], -e), ldexpf(v[1], -e), w0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[2], -e), ldexpf(v[3], -e), w0, true);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4], -e), ldexpf(v[5], -e), w1, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[6], -e), ldexpf(v[7], -e), w1, true);
+  return make_uint2((uint32_t)w0, (uint32_t)w1);
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(const void* __restrict__ src,
                                                                 int rows, int cols,
@@ -42,9 +59,7 @@ __global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(const void* __re
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
-  int E;
-  const float f = frexpf(amax, &E);
-  const int e = amax == 0.f ? 0 : E - 9 + (f > 0.875f ? 1 : 0);
+  const int e = fp8_exponent(amax);
   if (lane == 0) scale[row] = ldexpf(1.f, e);
   for (int c = lane; c < nch; c += kWave) {
     float v[8];
@@ -56,13 +71,139 @@ __global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(const void* __re
       v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
       v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     }
-    int w0 = 0, w1 = 0;
-    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[0], -e), ldexpf(v[1], -e), w0, false);
-    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[2], -e), ldexpf(v[3], -e), w0, true);
-    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4], -e), ldexpf(v[5], -e), w1, false);
-    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[6], -e), ldexpf(v[7], -e), w1, true);
-    *reinterpret_cast<uint2*>(q + (size_t)row * cols + c * 8) = make_uint2((uint32_t)w0, (uint32_t)w1);
+    *reinterpret_cast<uint2*>(q + (size_t)row * cols + c * 8) = fp8_codes8(v, e);
   }
+}
+
+// Per-input-channel codes of expert weights for the data-gradient products:
+// src0 (and src1) [B][N][K] bf16 -> q [B][K][n N], row k = the column k of
+// src0 followed by the column k of src1, scaled by one power of two per k.
+// A workgroup takes 64 columns of one batch: pass 1 the column maxima (each
+// thread 8 columns of every 32nd row, then an LDS reduction), pass 2 the
+// codes, through 64 x 64 tiles in LDS so that each thread writes 16
+// consecutive codes of one output row.  N % 64 == 0, K % 64 == 0.
+__global__ __launch_bounds__(256) void quantize_t_fp8_kernel(const bf16_t* __restrict__ src0,
+                                                             const bf16_t* __restrict__ src1,
+                                                             int N, int K,
+                                                             uint8_t* __restrict__ q,
+                                                             float* __restrict__ scale) {
+  __shared__ float s_max[32][65];
+  __shared__ int s_e[64];
+  __shared__ __align__(16) bf16_t s_tile[64][64];
+  const int b = blockIdx.y, c0 = blockIdx.x * 64, t = threadIdx.x;
+  const int nsrc = src1 != nullptr ? 2 : 1;
+  const int cc = t & 7, r0 = t >> 3;  // 8 columns 8 cc .. + 7 of rows r0, r0 + 32, ...
+  float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int si = 0; si < nsrc; ++si) {
+    const bf16_t* src = (si == 0 ? src0 : src1) + (size_t)b * N * K + c0 + 8 * cc;
+    for (int r = r0; r < N; r += 32) {
+      float v[8];
+      unpack8(*reinterpret_cast<const uint4*>(src + (size_t)r * K), v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf(v[i]));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s_max[r0][8 * cc + i] = m[i];
+  __syncthreads();
+  if (t < 64) {
+    float a = 0.f;
+    for (int r = 0; r < 32; ++r) a = fmaxf(a, s_max[r][t]);
+    const int e = fp8_exponent(a);
+    s_e[t] = e;
+    scale[(size_t)b * K + c0 + t] = ldexpf(1.f, e);
+  }
+  __syncthreads();
+  const int oc = t & 63, og = t >> 6;  // output row c0 + oc, 16 source rows 16 og .. + 15
+  const int e = s_e[oc];
+  uint8_t* qrow = q + ((size_t)b * K + c0 + oc) * (size_t)(nsrc * N);
+  for (int si = 0; si < nsrc; ++si) {
+    const bf16_t* src = (si == 0 ? src0 : src1) + (size_t)b * N * K + c0;
+    for (int n0 = 0; n0 < N; n0 += 64) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = (t >> 3) + 32 * h;
+        *reinterpret_cast<uint4*>(&s_tile[r][8 * cc]) =
+            *reinterpret_cast<const uint4*>(src + (size_t)(n0 + r) * K + 8 * cc);
+      }
+      __syncthreads();
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = bf2f(s_tile[16 * og + i][oc]);
+      const uint2 lo = fp8_codes8(v, e), hi = fp8_codes8(v + 8, e);
+      *reinterpret_cast<uint4*>(qrow + (size_t)si * N + n0 + 16 * og) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      __syncthreads();
+    }
+  }
+}
+
+hipError_t launch_quantize_t_fp8(const bf16_t* src0, const bf16_t* src1, int batch, int N, int K,
+                                 uint8_t* q, float* scale, hipStream_t s) {
+  if (batch <= 0) return hipSuccess;
+  quantize_t_fp8_kernel<<<dim3(K / 64, batch), 256, 0, s>>>(src0, src1, N, K, q, scale);
+  return hipGetLastError();
+}
+
+// Gradients of h = SiLU(g) * u for the FP8 gate / up data gradient, one wave
+// per grouped row r < nrows: dg = dh u s (1 + g (1 - s)), du = dh SiLU(g),
+// s = sigmoid(g), in fp32 from the bf16 dh and the saved g, u; [dg | du] is
+// stored in bf16 (for the weight gradients) and its row, as rounded,
+// quantized like quantize_rows_fp8 (codes + scale).  I % 8 == 0, I <= 2048.
+constexpr int kSwiMaxChunks = 4;  // chunks of 8 columns per lane: I <= 64 * 8 * 4
+__global__ __launch_bounds__(256) void swiglu_bwd_fp8_kernel(const bf16_t* __restrict__ dh,
+                                                             const bf16_t* __restrict__ gu,
+                                                             int rows, int I,
+                                                             const int32_t* __restrict__ nrows,
+                                                             bf16_t* __restrict__ dgu,
+                                                             uint8_t* __restrict__ q,
+                                                             float* __restrict__ scale) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = lane_id();
+  if (row >= rows || row >= *nrows) return;
+  const int nch = I / 8;
+  float dg[kSwiMaxChunks][8], du[kSwiMaxChunks][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < kSwiMaxChunks; ++j) {
+    const int c = lane + kWave * j;
+    if (c >= nch) break;
+    float d[8], g[8], u[8];
+    unpack8(*reinterpret_cast<const uint4*>(dh + (size_t)row * I + 8 * c), d);
+    unpack8(*reinterpret_cast<const uint4*>(gu + (size_t)row * 2 * I + 8 * c), g);
+    unpack8(*reinterpret_cast<const uint4*>(gu + (size_t)row * 2 * I + I + 8 * c), u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float sg = fast_rcp(1.f + __expf(-g[i]));
+      dg[j][i] = d[i] * u[i] * sg * (1.f + g[i] * (1.f - sg));
+      du[j][i] = d[i] * g[i] * sg;
+    }
+    const uint4 pg = pack8(dg[j]), pu = pack8(du[j]);
+    *reinterpret_cast<uint4*>(dgu + (size_t)row * 2 * I + 8 * c) = pg;
+    *reinterpret_cast<uint4*>(dgu + (size_t)row * 2 * I + I + 8 * c) = pu;
+    unpack8(pg, dg[j]);  // the rounded values are what gets quantized
+    unpack8(pu, du[j]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fmaxf(fabsf(dg[j][i]), fabsf(du[j][i])));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+  const int e = fp8_exponent(amax);
+  if (lane == 0) scale[row] = ldexpf(1.f, e);
+#pragma unroll
+  for (int j = 0; j < kSwiMaxChunks; ++j) {
+    const int c = lane + kWave * j;
+    if (c >= nch) break;
+    *reinterpret_cast<uint2*>(q + (size_t)row * 2 * I + 8 * c) = fp8_codes8(dg[j], e);
+    *reinterpret_cast<uint2*>(q + (size_t)row * 2 * I + I + 8 * c) = fp8_codes8(du[j], e);
+  }
+}
+
+hipError_t launch_swiglu_bwd_fp8(const bf16_t* dh, const bf16_t* gu, int rows, int I,
+                                 const int32_t* nrows, bf16_t* dgu, uint8_t* q, float* scale,
+                                 hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  swiglu_bwd_fp8_kernel<<<(rows + 3) / 4, 256, 0, s>>>(dh, gu, rows, I, nrows, dgu, q, scale);
+  return hipGetLastError();
 }
 
 hipError_t launch_quantize_fp8(const void* src, int rows, int cols, bool bf16,

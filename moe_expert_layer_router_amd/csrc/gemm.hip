@@ -1033,7 +1033,7 @@ template <int KIND, int BM_, bool F8 = false>
 __global__ __launch_bounds__(NTH)
 __attribute__((amdgpu_waves_per_eu(Cfg<BM_>::kWavesPerSimd, Cfg<BM_>::kWavesPerSimd)))
 void gemm_kernel(const GemmArgs p) {
-  static_assert(!F8 || KIND == K_GATEUP_FWD || KIND == K_DOWN_FWD, "FP8: forward products only");
+  static_assert(!F8 || KIND == K_GATEUP_FWD || KIND == K_DOWN_FWD, "FP8: K-contiguous products only");
   using Tr = Traits<KIND>;
   using C = Cfg<BM_>;
   constexpr int WM = C::WM, MI = C::MI, NST = C::NST, NIA = C::NIA;
@@ -1363,6 +1363,76 @@ hipError_t launch_ffn_fwd_fp8(const uint8_t* x_q, const float* x_scale, const in
   d.sb0 = wd_s;
   d.sb_group_stride = H;
   return launch_gemm<K_DOWN_FWD, kBmGrouped, true>(d, mt_upper * d.n_ntiles, MOE_KERNEL_FFN_DOWN, s);
+}
+
+// FP8 data gradients of the expert FFN.  Both products are the FP8 down
+// kernel (A and B K-contiguous, row x column scales): dh [R, I] = dy codes x
+// rows of W_down^T (N = I, K = H), then, after the SiLU derivative and the row
+// quantization of [dg | du], dx [R, H] = [dg | du] codes x rows of
+// [W_gate^T | W_up^T] (N = H, K = 2I).
+size_t ffn_dgrad_fp8_ws_bytes(int R_cap, int E_l, int I) {
+  return ffn_sched_bytes(R_cap, E_l) + align256((size_t)R_cap * I * 2) +
+         align256((size_t)R_cap * 2 * I) + align256((size_t)R_cap * 4);
+}
+
+hipError_t launch_ffn_dgrad_fp8(const uint8_t* dy_q, const float* dy_scale, const bf16_t* gu,
+                                const int32_t* offsets, int E_l, int R_cap, int H, int I,
+                                const uint8_t* wdt_q, const float* wdt_s, const uint8_t* wgut_q,
+                                const float* wgut_s, bf16_t* dgu, bf16_t* dx_perm, void* ws,
+                                hipStream_t s) {
+  char* w = (char*)ws;
+  int32_t* sched = (int32_t*)w;
+  w += ffn_sched_bytes(R_cap, E_l);
+  bf16_t* dh = (bf16_t*)w;
+  w += align256((size_t)R_cap * I * 2);
+  uint8_t* dguq = (uint8_t*)w;
+  w += align256((size_t)R_cap * 2 * I);
+  float* sdgu = (float*)w;
+  ffn_sched_kernel<<<1, kMaxE, 0, s>>>(offsets, E_l, kBmGrouped, sched, nullptr);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int mt_upper = R_cap / kBmGrouped + E_l;
+
+  // E4M3 rows of K codes run through the ring as rows of K / 2 bf16 slots.
+  GemmArgs d{};
+  d.a = (const bf16_t*)dy_q;
+  d.lda = H / 2;
+  d.b0 = (const bf16_t*)wdt_q;
+  d.ldb = H / 2;
+  d.b_group_stride = (long)I * H / 2;
+  d.sched = sched;
+  d.K = H / 2;
+  d.N = I;
+  d.I = I;
+  d.n_ntiles = (I + BN - 1) / BN;
+  d.c0 = dh;
+  d.ldc = I;
+  d.sa = dy_scale;
+  d.sb0 = wdt_s;
+  d.sb_group_stride = I;
+  err = launch_gemm<K_DOWN_FWD, kBmGrouped, true>(d, mt_upper * d.n_ntiles, MOE_KERNEL_FFN_DOWN_DGRAD, s);
+  if (err != hipSuccess) return err;
+
+  err = launch_swiglu_bwd_fp8(dh, gu, R_cap, I, offsets + E_l, dgu, dguq, sdgu, s);
+  if (err != hipSuccess) return err;
+
+  GemmArgs x{};
+  x.a = (const bf16_t*)dguq;
+  x.lda = I;  // 2I codes
+  x.b0 = (const bf16_t*)wgut_q;
+  x.ldb = I;
+  x.b_group_stride = (long)H * I;
+  x.sched = sched;
+  x.K = I;
+  x.N = H;
+  x.I = I;
+  x.n_ntiles = (H + BN - 1) / BN;
+  x.c0 = dx_perm;
+  x.ldc = H;
+  x.sa = sdgu;
+  x.sb0 = wgut_s;
+  x.sb_group_stride = H;
+  return launch_gemm<K_DOWN_FWD, kBmGrouped, true>(x, mt_upper * x.n_ntiles, MOE_KERNEL_FFN_GATEUP_DGRAD, s);
 }
 
 // A second stream of the calling device for products that may run beside

@@ -50,7 +50,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_single_hip_runtime():
-    assert L.moe_abi_version() == moe.ABI_VERSION == 2
+    assert L.moe_abi_version() == moe.ABI_VERSION == 3
     libs = moe.hip_runtimes_mapped()
     assert len(libs) <= 1, libs
 
@@ -164,6 +164,34 @@ def test_fp8_entry_points_errors():
     assert ws(moe.MOE_OP_ROUTE, 16, 64, 32, 8, 2, 0, 8, FP8) == EINVAL and "MOE_FP8" in _err()
     p = lambda *a: L.moe_permute(*a)
     assert p(A, A, 64, 2040, 16, 4, 0, 16, FP8, A, A, A, A, A, A, big, S) == EINVAL   # H % 16 for codes
+
+
+def test_fp8_dgrad_entry_points_errors():
+    t = lambda *a: L.moe_quantize_fp8_t(*a)
+    assert t(A, N, 16, 2048, 768, F32, A, A, S) == EUNSUP and "BF16" in _err()
+    assert t(A, N, 16, 2048, 760, BF16, A, A, S) == EUNSUP and "64" in _err()    # K % 64
+    assert t(A, A, 16, 2000, 768, BF16, A, A, S) == EUNSUP                       # N % 64
+    assert t(A, N, -1, 2048, 768, BF16, A, A, S) == EINVAL
+    assert t(A, U, 16, 2048, 768, BF16, A, A, S) == EINVAL and "src1" in _err()
+    assert t(A, N, 16, 2048, 768, BF16, N, A, S) == EINVAL and "q" in _err()
+    assert t(N, N, 0, 2048, 768, BF16, N, N, S) == OK                            # empty batch
+    d = lambda *a: L.moe_grouped_ffn_dgrad_fp8(*a)
+    big = 1 << 30
+    args = lambda H=2048, I=768, El=16, R=512, ws=big, dq=A, wd=A, dx=A, gu=A: (
+        dq, A, gu, A, El, R, H, I, wd, A, A, A, A, dx, A, ws, S)
+    assert d(*args(I=704)) == EUNSUP and "128" in _err()
+    assert d(*args(I=2176)) == EUNSUP and "2048" in _err()
+    assert d(*args(H=1984)) == EUNSUP
+    assert d(*args(El=0)) == EINVAL
+    assert d(*args(wd=N)) == EINVAL and "wdt_q" in _err()
+    assert d(*args(dx=N)) == EINVAL and "dx_perm" in _err()
+    assert d(*args(gu=U)) == EINVAL and "gu_saved" in _err()
+    assert d(*args(ws=8)) == EWS
+    assert d(*args(R=0, dq=N, dx=N, gu=N)) == OK
+    ws = lambda *a: L.moe_workspace_bytes(*a)
+    n = ws(moe.MOE_OP_FFN_DGRAD_FP8, 8192, 2048, 768, 128, 8, 0, 16, BF16)
+    assert n >= 8192 * 8 * (768 * 2 + 2 * 768 + 4)                            # dh, codes, scales
+    assert ws(moe.MOE_OP_FFN_DGRAD_FP8, 8192, 2048, 768, 128, 8, 0, 16, FP8) == n
 
 
 def test_ffn_bwd_split_needs_a_second_stream():

@@ -19,6 +19,8 @@ FP8 recipe on the same codes:
 and the recipe as a whole stays within its quantization error of the exact
 forward (rel-L2 < 0.12, as the oracle's own pin).
 """
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -166,3 +168,120 @@ def test_ffn_fwd_fp8_matches_oracle(w):
                                               ref_w["w_gate"][0][e - w.e_lo], ref_w["w_gate"][1][e - w.e_lo])
                             for e in range(w.e_lo, w.e_hi)], axis=0)
     assert np.abs(gu[:, :I] - g_ref).max() <= 2.0 ** -7 * np.abs(g_ref).max()
+
+
+# ----------------------------------------------------------------------------
+# FP8 data gradients
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("pair", [False, True])
+def test_quantize_fp8_t_bit_exact(pair):
+    rng = np.random.default_rng(41)
+    B, N, K = 2, 192, 128
+    w0 = rng.standard_normal((B, N, K)) * np.exp2(rng.integers(-20, 20, size=(B, 1, K)))
+    w1 = rng.standard_normal((B, N, K)) * np.exp2(rng.integers(-20, 20, size=(B, 1, K)))
+    w0[0, :, 5] = 0.0
+    if pair:
+        w1[0, :, 5] = 0.0                                   # zero input channel: scale 1, codes 0
+    w0[1, 7, 9] = 448.0 * 2.0 ** 3                          # a maximum exactly on the boundary
+    w1[1, :, 9] = 0.0
+    t0, t1 = _dev(w0.astype(np.float32), torch.bfloat16), _dev(w1.astype(np.float32), torch.bfloat16)
+    print(f"  quantize_t pair={pair} B={B} N={N} K={K}", flush=True)
+    q, s = moe.moe_quantize_fp8_t(t0, t1 if pair else None)
+    torch.cuda.synchronize()
+    ref_q, ref_s = O.quantize_expert_weights_t_fp8(_np(t0), _np(t1) if pair else None)
+    assert q.shape == ref_q.shape
+    bad = np.nonzero(q.cpu().numpy() != ref_q)
+    assert bad[0].size == 0, f"{bad[0].size} codes differ, first at {[b[0] for b in bad]}"
+    assert np.array_equal(_np(s), ref_s)
+
+
+DGRAD_CASES = [
+    EP_SHARE.scaled(name="dgrad_fp8_t512_h256_i128_e32_k4_local4to20", T=512, H=256, I=128, E=32, k=4,
+                    e_lo=4, e_hi=20),
+    SKEWED.scaled(name="dgrad_fp8_skewed_t1024_h256_i256_e32_k4", T=1024, H=256, I=256, E=32, k=4,
+                  e_lo=0, e_hi=32),
+    EP_SHARE.scaled(name="dgrad_fp8_t2048_h2048_i768_e16_k4_all_local", T=2048, E=16, k=4, e_lo=0, e_hi=16),
+]
+
+
+@pytest.mark.parametrize("w", DGRAD_CASES, ids=lambda w: w.name)
+def test_ffn_dgrad_fp8_matches_oracle(w):
+    """Two stages against the oracle's FP8 data gradients:
+      dgu: within one bf16 step, plus what a dh that rounded to the neighbouring
+           bf16 (fp32 versus fp64 sums, bound: one bf16 step of dh plus the
+           standard K-term fp32 summation error of its code products) moves
+           through the SiLU derivative: |d dg / d dh| = |u s (1 + g (1 - s))|,
+           |d du / d dh| = |g s|;
+      dx:  against the oracle's second product applied to the GPU's own dgu rows
+           (their quantization must match bit for bit): the layer's bf16 bar,
+           max|d| <= 2e-2 * max(1, max|ref|) and rel-L2 <= 5e-3;
+    rows >= R are left as they were, and the result stays within the recipe's
+    quantization error of the exact data gradient (rel-L2 < 0.12, the oracle's
+    own pin)."""
+    inp = make_inputs(w)
+    _, idx, _ = O.route(inp["x"], inp["w_router"], w.k, inp.get("bias"))
+    print(f"  case {w.name}", flush=True)
+    bf = torch.bfloat16
+    x = _dev(inp["x"], bf)
+    perm = moe.moe_permute(x, torch.from_numpy(idx.astype(np.int32)).to(DEV), w.E, w.e_lo, w.e_hi)
+    offsets = perm["offsets"]
+    off = offsets.cpu().numpy()
+    R, R_cap, E_l = int(off[-1]), w.T * w.k, w.e_hi - w.e_lo
+    rng = np.random.default_rng(zlib.crc32(w.name.encode()))
+    g = rng.standard_normal((R_cap, w.I)) * 2.0
+    u = rng.standard_normal((R_cap, w.I))
+    gu = _dev(np.concatenate([g, u], axis=1).astype(np.float32), bf)
+    dy = _dev((rng.standard_normal((R_cap, w.H)) * 0.05).astype(np.float32), bf)
+    wts = {n: _dev(inp[n], bf) for n in ("w_gate", "w_up", "w_down")}
+    dyq, sdy = moe.moe_quantize_fp8(dy, nrows=offsets[E_l:])
+    wdt = moe.moe_quantize_fp8_t(wts["w_down"])
+    wgut = moe.moe_quantize_fp8_t(wts["w_gate"], wts["w_up"])
+    nan = float("nan")
+    out = {"dgu": torch.full((R_cap, 2 * w.I), nan, dtype=bf, device=DEV),
+           "dx_perm": torch.full((R_cap, w.H), nan, dtype=bf, device=DEV)}
+    moe.moe_grouped_ffn_dgrad_fp8(dyq, sdy, gu, offsets, wdt, wgut, out=out)
+    torch.cuda.synchronize()
+    gu_np, dy_np = _np(gu), _np(dy)
+    ref_dyq, ref_sdy = O.quantize_rows_fp8(dy_np[:R])
+    assert np.array_equal(dyq[:R].cpu().numpy(), ref_dyq) and np.array_equal(_np(sdy[:R]), ref_sdy)
+    ref_wdt = O.quantize_expert_weights_t_fp8(_np(wts["w_down"]))
+    ref_wgut = O.quantize_expert_weights_t_fp8(_np(wts["w_gate"]), _np(wts["w_up"]))
+    assert np.array_equal(wdt[0].cpu().numpy(), ref_wdt[0]) and np.array_equal(_np(wdt[1]), ref_wdt[1])
+    assert np.array_equal(wgut[0].cpu().numpy(), ref_wgut[0]) and np.array_equal(_np(wgut[1]), ref_wgut[1])
+    dgu_got, dx_got = _np(out["dgu"]), _np(out["dx_perm"])
+    assert np.isnan(dgu_got[R:]).all() and np.isnan(dx_got[R:]).all()
+    dgu_got, dx_got = dgu_got[:R], dx_got[:R]
+    dgu_ref, dgu_bound = np.zeros_like(dgu_got), np.zeros_like(dgu_got)
+    dx_ref, dx_exact = np.zeros_like(dx_got), np.zeros_like(dx_got)
+    mag = lambda q: q & np.uint8(0x7F)
+    for i in range(E_l):
+        sl = slice(off[i], off[i + 1])
+        if off[i + 1] == off[i]:
+            continue
+        gg, uu = gu_np[sl, :w.I], gu_np[sl, w.I:]
+        p = O.expert_dgrad_fp8_parts(ref_dyq[sl], ref_sdy[sl], gg, uu, ref_wdt[0][i], ref_wdt[1][i],
+                                     ref_wgut[0][i], ref_wgut[1][i])
+        dgu_ref[sl] = p["dgu"]
+        dh_abs = O.fp8_matmul_rows(mag(ref_dyq[sl]), ref_sdy[sl], mag(ref_wdt[0][i]), ref_wdt[1][i])
+        dh_slack = 2.0 ** -7 * np.abs(p["dh"]) + 2 * w.H * 2.0 ** -24 * dh_abs
+        s = O.sigmoid(gg)
+        ddg, ddu = np.abs(uu * s * (1 + gg * (1 - s))), np.abs(gg * s)
+        dgu_bound[sl] = 2.0 ** -7 * np.abs(p["dgu"]) + np.concatenate([ddg * dh_slack, ddu * dh_slack],
+                                                                       axis=1) + 1e-30
+        # second stage on the GPU's own dgu rows
+        q2, s2 = O.quantize_rows_fp8(dgu_got[sl])
+        dx_ref[sl] = O.fp8_matmul_rows(q2, s2, ref_wgut[0][i], ref_wgut[1][i])
+        # exact data gradient of the same operands
+        dg, du = O.swiglu_grad(dy_np[sl] @ _np(wts["w_down"][i]), gg, uu)
+        dx_exact[sl] = dg @ _np(wts["w_gate"][i]) + du @ _np(wts["w_up"][i])
+    over = np.abs(dgu_got - dgu_ref) > dgu_bound
+    bar = 2e-2 * max(1.0, np.abs(dx_ref).max())
+    rel = np.linalg.norm(dx_got - dx_ref) / max(np.linalg.norm(dx_ref), 1e-30)
+    rel_exact = np.linalg.norm(dx_got - dx_exact) / max(np.linalg.norm(dx_exact), 1e-30)
+    print(f"  R={R}: dgu beyond bound {int(over.sum())} of {over.size} (max |d| {np.abs(dgu_got - dgu_ref).max():.3e}); "
+          f"dx max-abs {np.abs(dx_got - dx_ref).max():.3e} (bar {bar:.3e}) rel-L2 {rel:.3e}; "
+          f"vs exact rel-L2 {rel_exact:.3e}", flush=True)
+    assert over.sum() == 0
+    assert np.abs(dx_got - dx_ref).max() <= bar and rel <= 5e-3
+    assert rel_exact < 0.12
