@@ -240,6 +240,7 @@ def fp8_ffn_bench(w, args):
             kern[f"{name}_{tag}"] = {"avg_us": round(avg, 2), "achieved_tflops": round(ach, 1),
                                      "peak_tflops": peak, "frac": round(ach / peak, 4)}
     tf8 = flops / (us_8 * 1e-6) / 1e12
+    dgrad = fp8_dgrad_bench(w, args, moe, torch, t, pb, timed, n)
     dom = max(("FFN_GATEUP_fp8", "FFN_DOWN_fp8"), key=lambda k: kern[k]["avg_us"])
     return {
         "metric": "grouped expert FFN forward TFLOP/s, FP8 recipe vs bf16",
@@ -254,10 +255,78 @@ def fp8_ffn_bench(w, args):
         "speedup_vs_bf16": round(us_b / us_8, 3),
         "activation_quantize_us": round(us_q, 2),
         "kernels": kern,
+        "data_gradients": dgrad,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": kern[dom]["achieved_tflops"],
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": kern[dom]["frac"],
                      "traffic": None},
     }
+
+
+def fp8_dgrad_bench(w, args, moe, torch, t, pb, timed, n):
+    """The two data-gradient products of the expert FFN, bf16 (those of
+    moe_grouped_ffn_bwd_split, with the weight-gradient stream held back by a
+    sleep kernel so that they run alone) versus moe_grouped_ffn_dgrad_fp8 (both
+    FP8 products, the SiLU derivative and the row quantization of [dg | du]).
+    FLOPs: 6 R H I.  The quantization of dy_perm and of the transposed weights
+    is timed on its own."""
+    dev = torch.device("cuda:0")
+    R_cap, H, I = w.T * w.k, w.H, w.I
+    E_l = w.e_hi - w.e_lo
+    offsets = pb["offsets"]
+    R = int(offsets[-1].item())
+    g = torch.Generator().manual_seed(11)
+    dy = (torch.randn(R_cap, H, generator=g) * 0.05).to(dev).to(torch.bfloat16)
+    fw = moe.moe_grouped_ffn_fwd(pb["x_perm"], offsets, t["w_gate"], t["w_up"], t["w_down"],
+                                 save_gu=True)
+    gu, h_perm = fw["gu"], fw["h_perm"]
+    dyq, sdy = moe.moe_quantize_fp8(dy, nrows=offsets[E_l:])
+    wdt = moe.moe_quantize_fp8_t(t["w_down"])
+    wgut = moe.moe_quantize_fp8_t(t["w_gate"], t["w_up"])
+    o8 = moe.moe_grouped_ffn_dgrad_fp8(dyq, sdy, gu, offsets, wdt, wgut)
+    bufs = {"dx": torch.empty_like(pb["x_perm"]),
+            "dwg": torch.empty((E_l, I, H), dtype=torch.float32, device=dev),
+            "dwu": torch.empty((E_l, I, H), dtype=torch.float32, device=dev),
+            "dwd": torch.empty((E_l, H, I), dtype=torch.float32, device=dev)}
+    nb = moe.lib.moe_workspace_bytes(moe.MOE_OP_FFN_BWD, R_cap, H, I, max(E_l, 1), 1, 0, E_l, moe.MOE_BF16)
+    ws = torch.empty(int(nb), dtype=torch.uint8, device=dev)
+    side = torch.cuda.Stream(device=dev)
+    P = lambda x: ctypes.c_void_p(x.data_ptr())
+    main = torch.cuda.current_stream()
+
+    def f_bd():
+        with torch.cuda.stream(side):
+            torch.cuda._sleep(20_000_000)  # the weight gradients start after the data gradients
+        rc = moe.lib.moe_grouped_ffn_bwd_split(
+            P(dy), P(pb["x_perm"]), P(gu), P(h_perm), P(offsets), E_l, R_cap, H, I, P(t["w_gate"]),
+            P(t["w_up"]), P(t["w_down"]), moe.MOE_BF16, P(bufs["dx"]), P(bufs["dwg"]), P(bufs["dwu"]),
+            P(bufs["dwd"]), 0, P(ws), ctypes.c_size_t(ws.numel()), ctypes.c_void_p(main.cuda_stream),
+            ctypes.c_void_p(side.cuda_stream))
+        assert rc == 0, moe.lib.moe_last_error()
+        main.wait_stream(side)
+
+    f_8 = lambda: moe.moe_grouped_ffn_dgrad_fp8(dyq, sdy, gu, offsets, wdt, wgut, out=o8)
+    f_qdy = lambda: moe.moe_quantize_fp8(dy, nrows=offsets[E_l:], out={"q": dyq, "scale": sdy})
+    f_qw = lambda: (moe.moe_quantize_fp8_t(t["w_down"], out={"q": wdt[0], "scale": wdt[1]}),
+                    moe.moe_quantize_fp8_t(t["w_gate"], t["w_up"], out={"q": wgut[0], "scale": wgut[1]}))
+    us_8 = timed(f_8, n)
+    kid = {k: KERNELS.index(k) for k in ("FFN_DOWN_DGRAD", "FFN_GATEUP_DGRAD")}
+    fl = {"FFN_DOWN_DGRAD": 2.0 * R * H * I, "FFN_GATEUP_DGRAD": 4.0 * R * H * I}
+    kern = {}
+    for name in kid:
+        for tag, fn, peak in (("bf16", f_bd, PEAK_BF16_TFLOPS), ("fp8", f_8, PEAK_FP8_TFLOPS)):
+            avg = _kernel_avg_us(moe, torch, kid[name], fn, n)
+            ach = fl[name] / (avg * 1e-6) / 1e12
+            kern[f"{name}_{tag}"] = {"avg_us": round(avg, 2), "achieved_tflops": round(ach, 1),
+                                     "peak_tflops": peak, "frac": round(ach / peak, 4)}
+    us_b = kern["FFN_DOWN_DGRAD_bf16"]["avg_us"] + kern["FFN_GATEUP_DGRAD_bf16"]["avg_us"]
+    flops = 6.0 * R * H * I
+    return {"us": {"fp8": round(us_8, 2), "bf16_products": round(us_b, 2)},
+            "fp8_tflops": round(flops / (us_8 * 1e-6) / 1e12, 1),
+            "bf16_tflops": round(flops / (us_b * 1e-6) / 1e12, 1),
+            "speedup_vs_bf16": round(us_b / us_8, 3),
+            "dy_quantize_us": round(timed(f_qdy, n), 2),
+            "weight_quantize_t_us": round(timed(f_qw, n), 2),
+            "kernels": kern}
 
 
 def step_stats(run, n, dev):
