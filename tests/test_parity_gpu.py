@@ -178,6 +178,11 @@ ROUTE_CASES = [TINY, EP_SHARE, FULL, SKEWED,
                # 4 K steps over 8 waves (some waves have none), one 8-expert chunk
                EP_SHARE.scaled(name="route_bf16_t1000_h64_e8_k2", T=1000, H=64, E=8, k=2, e_lo=0,
                                e_hi=8),
+               # k > 16: slots 16.. come from each lane's second kept round
+               EP_SHARE.scaled(name="route_bf16_t999_h256_e128_k32", T=999, H=256, E=128, k=32,
+                               e_lo=0, e_hi=128),
+               EP_SHARE.scaled(name="route_bf16_t300_h128_e64_k17", T=300, H=128, E=64, k=17,
+                               e_lo=0, e_hi=64),
                # E % 8 != 0: the sliced two-launch router
                EP_SHARE.scaled(name="route_bf16_t515_h192_e20_k3", T=515, H=192, E=20, k=3,
                                e_lo=0, e_hi=20)]
