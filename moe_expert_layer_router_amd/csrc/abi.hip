@@ -78,11 +78,9 @@ int check_ws(const void* ws, size_t have, size_t need, const char* fn) {
   return MOE_OK;
 }
 
-// Split of the token (K) dimension of dW_r = x^T dz: about 128 (tile, split)
-// work items, each split at least 256 tokens, at most 16 splits (every split
-// writes an H x 2E fp32 partial that a second pass sums).
 // K splits of the router weight gradient x^T . dz: enough workgroups for one
-// per CU, each split at least 256 token rows.
+// per CU, each split at least 256 token rows, at most 32 (every split writes an
+// fp32 partial that a second pass sums).
 int route_bwd_splits(int T, int H, int E) {
   const int tiles = gemm_tiles(H, 2 * E);
   const int want = (kCUs + tiles - 1) / tiles;

@@ -303,10 +303,12 @@ __global__ __launch_bounds__(256) void route_bwd_dz_kernel(
   for (int e0 = 0; e0 < E; e0 += kWave) {
     const int e = e0 + lane;
     float v = 0.f;
+    // slot j's (expert, dz) broadcast from lane j (uniform j: a scalar read);
+    // an expert named by several slots gets their sum, in slot order
     for (int j = 0; j < k; ++j) {
-      const int ij = __shfl(id, j, kWave);
-      const float dj = __shfl(dz, j, kWave);
-      if (ij == e) v = dj;
+      const int ij = __builtin_amdgcn_readlane(id, j);
+      const float dj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dz), j));
+      v += (ij == e) ? dj : 0.f;
     }
     if (e >= E) continue;
     d_logits[(size_t)t * E + e] = v;

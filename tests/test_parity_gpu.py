@@ -483,6 +483,24 @@ def test_combine_dx_matches_oracle(case):
     err = np.abs(got - ref)
     print(f"  max err {err.max():.3g}, max err / bound {(err / bound).max():.3g}", flush=True)
     assert (err <= bound).all()
+    if dtype == "bf16" and H % 64 == 0 and E % 4 == 0:
+        # the router backward on the same slots (a repeated expert sums its slots):
+        # d_logits within 32 fp32 ulps of w (|dw| + sum |w dw|) (a 64-lane tree
+        # sum, a subtraction, a product), dx_router within 2^-14 of its absolute
+        # sum, dw_router within 2^-12 (dz enters the bf16 product as two bf16
+        # halves, about 16 bits, and T-term fp32 sums)
+        x = _dev(rng.standard_normal((T, H)), dt)
+        rb = moe.moe_route_bwd(g_dtw, g_tw, g_idx, x, wr)
+        torch.cuda.synchronize()
+        inner = np.abs(tw64 * dtw64).sum(1, keepdims=True)
+        zb = np.zeros((T, E))
+        np.add.at(zb, (np.arange(T)[:, None].repeat(k, 1), idx), tw64 * (np.abs(dtw64) + inner))
+        assert (np.abs(_np(rb["d_logits"]) - dz) <= 2.0 ** -19 * zb + 1e-30).all()
+        x64 = _np(x)
+        dxr_bound = 2.0 ** -14 * O.router_input_grad(np.abs(dz), np.abs(wr64)) + 1e-30
+        assert (np.abs(_np(rb["dx_router"]) - O.router_input_grad(dz, wr64)) <= dxr_bound).all()
+        dwr_bound = 2.0 ** -12 * (np.abs(x64).T @ np.abs(dz)) + 1e-30
+        assert (np.abs(_np(rb["dw_router"]) - x64.T @ dz) <= dwr_bound).all()
 
 
 def test_weight_grad_accumulate():
