@@ -174,10 +174,11 @@ def test_ffn_fwd_fp8_matches_oracle(w):
 # FP8 data gradients
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("pair", [False, True])
-def test_quantize_fp8_t_bit_exact(pair):
+@pytest.mark.parametrize("pair,N", [(False, 192), (True, 192), (True, 1152)],
+                         ids=["single_n192", "pair_n192", "pair_n1152"])
+def test_quantize_fp8_t_bit_exact(pair, N):
     rng = np.random.default_rng(41)
-    B, N, K = 2, 192, 128
+    B, K = 2, 128
     w0 = rng.standard_normal((B, N, K)) * np.exp2(rng.integers(-20, 20, size=(B, 1, K)))
     w1 = rng.standard_normal((B, N, K)) * np.exp2(rng.integers(-20, 20, size=(B, 1, K)))
     w0[0, :, 5] = 0.0
