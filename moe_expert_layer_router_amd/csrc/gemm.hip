@@ -649,8 +649,11 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
             d4[0] = make_float4(o0.x + v[0], o0.y + v[1], o0.z + v[2], o0.w + v[3]);
             d4[1] = make_float4(o1.x + v[4], o1.y + v[5], o1.z + v[6], o1.w + v[7]);
           } else {
-            d4[0] = make_float4(v[0], v[1], v[2], v[3]);
-            d4[1] = make_float4(v[4], v[5], v[6], v[7]);
+            // written once per step and read only by the optimizer: streaming
+            // stores, which leave L2 to the operands of the products beside
+            f32x4_t* q4 = reinterpret_cast<f32x4_t*>(dst);
+            __builtin_nontemporal_store(f32x4_t{v[0], v[1], v[2], v[3]}, q4);
+            __builtin_nontemporal_store(f32x4_t{v[4], v[5], v[6], v[7]}, q4 + 1);
           }
         }
         // the next half reuses the staging area
