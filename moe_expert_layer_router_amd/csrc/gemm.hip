@@ -507,6 +507,12 @@ __device__ __forceinline__ out_rsrc_t out_rsrc(const bf16_t* base, long row0, lo
 __device__ __forceinline__ void store16(out_rsrc_t r, uint32_t off, uint4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, r, off, 0, 0);
 }
+// The same with the non-temporal cache policy (gfx950 cache-policy bit NT):
+// for outputs that the next kernels do not read.
+constexpr int kCpolNT = 2;
+__device__ __forceinline__ void store16_nt(out_rsrc_t r, uint32_t off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, r, off, 0, kCpolNT);
+}
 
 // FP8 epilogue scales of one tile, loaded after the previous tile's epilogue
 // (so that no wait for them lands behind this tile's DMAs): the lane's row
@@ -692,8 +698,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
           const uint32_t oh = col_ok ? (uint32_t)((lrow * p.ldc + col) * 2) : kOutKill;
           const uint32_t og = col_ok ? (uint32_t)((lrow * 2 * p.I + col) * 2) : kOutKill;
           store16(rh, oh, pack8(hv));
-          store16(rgu, og, pack8(g));
-          store16(rgu, og + (col_ok ? p.I * 2 : 0), pack8(u));
+          // g and u are read again only by the backward
+          store16_nt(rgu, og, pack8(g));
+          store16_nt(rgu, og + (col_ok ? p.I * 2 : 0), pack8(u));
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
