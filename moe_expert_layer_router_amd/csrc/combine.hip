@@ -3,7 +3,7 @@
 // The "unpermute" of the dispatcher table (page "FSDPTurbo EP/EFSDP and
 // LlamaFactory FSDP2/CP Design", section 3) becomes a per-token gather-reduce:
 // one wave owns one token, packs its local slots into the low lanes, issues
-// the 16-byte loads of up to eight grouped rows x four chunks per lane at once
+// the 16-byte loads of up to four grouped rows x four chunks per lane at once
 // and sums them in fp32 in slot order j = 0..k-1.  No atomics, so the result is
 // deterministic and independent of the launch shape.
 #include "common.h"
@@ -51,10 +51,12 @@ struct Row {
 };
 
 // Chunks of 16 bytes per lane per pass and slots whose rows are loaded
-// together: all CU x SG row loads of a pass are in flight at once (eight
-// slots: a top-8 token's rows in one round trip).
+// together: all CU x SG row loads of a pass are in flight at once.  Eight
+// slots (a top-8 token in one round trip) double the load registers and halve
+// the waves per SIMD, which costs more on an EP share (about one local slot
+// per token) than it gains on the full layer.
 constexpr int kCU = 4;
-constexpr int kSG = 8;
+constexpr int kSG = 4;
 
 // Moves the lanes holding a local slot (d >= 0; lanes >= k hold d = -1) to
 // lanes 0..n-1, keeping slot order; returns n.  Lane i then holds that slot's
@@ -281,7 +283,9 @@ __global__ __launch_bounds__(256) void combine_dx_kernel(
 //   dx_router[t] = sum_j dz_j * W_r[:, idx_j]   (rows of the transposed W_r);
 //   bf16 path also writes dz split as bf16 hi + lo ([T, 2E]) for the MFMA
 //   product x^T . dz.
-template <bool BF16>
+// DX: the router input gradient is wanted (its row gather needs registers the
+// logit-gradient-only form does without).
+template <bool BF16, bool DX>
 __global__ __launch_bounds__(256) void route_bwd_dz_kernel(
     const float* __restrict__ d_topk_w, const float* __restrict__ topk_w,
     const int32_t* __restrict__ topk_idx, const void* __restrict__ w_router_t, int T, int H,
@@ -319,7 +323,7 @@ __global__ __launch_bounds__(256) void route_bwd_dz_kernel(
       dz_hilo[(size_t)t * 2 * E + E + e] = lo;
     }
   }
-  if (dx_router == nullptr) return;
+  if constexpr (!DX) return;
   const int nch = H / R::N;
   for (int c0 = 0; c0 < nch; c0 += kWave * kCU) {
     float acc[kCU][R::N];
@@ -449,12 +453,15 @@ hipError_t launch_route_bwd_dz(const float* d_topk_w, const float* topk_w,
                                bf16_t* dz_hilo, hipStream_t s) {
   const int blocks = (T + 3) / 4;
   ProfScope ps(MOE_KERNEL_ROUTE_BWD_DZ, s);
-  if (bf16)
-    route_bwd_dz_kernel<true><<<blocks, 256, 0, s>>>(d_topk_w, topk_w, topk_idx, w_router_t, T,
-                                                      H, E, k, d_logits, dx_router, dz_hilo);
-  else
-    route_bwd_dz_kernel<false><<<blocks, 256, 0, s>>>(d_topk_w, topk_w, topk_idx, w_router_t, T,
-                                                       H, E, k, d_logits, dx_router, dz_hilo);
+#define MOE_DZ(B, D)                                                                             \
+  route_bwd_dz_kernel<B, D><<<blocks, 256, 0, s>>>(d_topk_w, topk_w, topk_idx, w_router_t, T, H, E, \
+                                                   k, d_logits, dx_router, dz_hilo)
+  if (bf16) {
+    if (dx_router != nullptr) MOE_DZ(true, true); else MOE_DZ(true, false);
+  } else {
+    if (dx_router != nullptr) MOE_DZ(false, true); else MOE_DZ(false, false);
+  }
+#undef MOE_DZ
   return hipGetLastError();
 }
 
