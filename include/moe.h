@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,
@@ -241,6 +241,24 @@ int moe_combine_dx(const void* dx_perm, const int32_t* dest_row, const float* d_
                    const float* topk_w, const int32_t* topk_idx, const void* w_router, int T,
                    int H, int E, int k, int dtype, void* dx, void* ws, size_t ws_bytes,
                    void* stream);
+
+/* moe_combine_dx with the router weight already transposed,
+ *   w_router_t [E,H] dtype (w_router_t[e,h] = w_router[h,e], 16-byte aligned),
+ * e.g. from moe_router_weight_t; the other arguments, the result and the
+ * accumulation order are those of moe_combine_dx, and no workspace is used.
+ * Lets a caller make the transpose where the chip is idle (before the
+ * backward's concurrent products) instead of in front of the gather. */
+int moe_combine_dx_t(const void* dx_perm, const int32_t* dest_row, const float* d_topk_w,
+                     const float* topk_w, const int32_t* topk_idx, const void* w_router_t, int T,
+                     int H, int E, int k, int dtype, void* dx, void* stream);
+
+/* Transpose of the router weight, the operand of the router's input
+ * gradient (dx_router = dz . w_router^T, the router product's backward):
+ *   w_router [H,E] dtype -> w_router_t [E,H] dtype, a bit copy.
+ * H and E in [0, 2^20]; nothing is launched when H*E = 0.  Caller-owned
+ * device buffers, which must not overlap. */
+int moe_router_weight_t(const void* w_router, int H, int E, int dtype, void* w_router_t,
+                        void* stream);
 
 /* Backward of the grouped FFN, given dy_perm [R_cap,H] and the forward's
  * x_perm, gu_saved (required) and h_perm:

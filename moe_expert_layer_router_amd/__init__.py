@@ -28,7 +28,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_F32, MOE_BF16, MOE_FP8 = 0, 1, 2
 (MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD, MOE_OP_ROUTE_BWD,
  MOE_OP_COMBINE_DX, MOE_OP_FFN_FWD_FP8, MOE_OP_FFN_DGRAD_FP8) = range(8)
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class MoEError(RuntimeError):
@@ -52,6 +52,8 @@ def _load():
         "moe_combine": ([P, P, P, P, I32, I32, I32, I32, P, P], I32),
         "moe_combine_bwd": ([P, P, P, P, I32, I32, I32, I32, P, P, P], I32),
         "moe_combine_dx": ([P, P, P, P, P, P, I32, I32, I32, I32, I32, P, P, SZ, P], I32),
+        "moe_combine_dx_t": ([P, P, P, P, P, P, I32, I32, I32, I32, I32, P, P], I32),
+        "moe_router_weight_t": ([P, I32, I32, I32, P, P], I32),
         "moe_grouped_ffn_bwd": ([P, P, P, P, P, I32, I32, I32, I32, P, P, P, I32, P, P, P, P, I32,
                                  P, SZ, P], I32),
         "moe_grouped_ffn_bwd_split": ([P, P, P, P, P, I32, I32, I32, I32, P, P, P, I32, P, P, P, P,
@@ -256,6 +258,28 @@ def moe_combine_dx(dx_perm: torch.Tensor, dest_row: torch.Tensor, d_topk_w: torc
     _check(lib.moe_combine_dx(_ptr(dx_perm), _ptr(dest_row), _ptr(d_topk_w), _ptr(topk_w),
                               _ptr(topk_idx), _ptr(w_router), T, H, E, k, dt, _ptr(dx), _ptr(ws),
                               _nbytes(ws), _stream()), "moe_combine_dx")
+    return dx
+
+
+def moe_router_weight_t(w_router: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """The router weight [H,E] transposed to [E,H] (operand of moe_combine_dx_t)."""
+    H, E = w_router.shape
+    wt = out if out is not None else torch.empty((E, H), dtype=w_router.dtype, device=w_router.device)
+    _check(lib.moe_router_weight_t(_ptr(w_router), H, E, _dtype_code(w_router), _ptr(wt), _stream()),
+           "moe_router_weight_t")
+    return wt
+
+
+def moe_combine_dx_t(dx_perm: torch.Tensor, dest_row: torch.Tensor, d_topk_w: torch.Tensor,
+                     topk_w: torch.Tensor, topk_idx: torch.Tensor, w_router_t: torch.Tensor,
+                     out: Optional[torch.Tensor] = None):
+    """moe_combine_dx with the transposed router weight [E,H].  Returns dx [T,H]."""
+    T, k = topk_w.shape
+    E, H = w_router_t.shape
+    dx = out if out is not None else torch.empty((T, H), dtype=dx_perm.dtype, device=dx_perm.device)
+    _check(lib.moe_combine_dx_t(_ptr(dx_perm), _ptr(dest_row), _ptr(d_topk_w), _ptr(topk_w),
+                                _ptr(topk_idx), _ptr(w_router_t), T, H, E, k, _dtype_code(dx_perm),
+                                _ptr(dx), _stream()), "moe_combine_dx_t")
     return dx
 
 

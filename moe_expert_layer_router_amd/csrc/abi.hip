@@ -412,29 +412,69 @@ int moe_combine(const void* y_perm, const float* topk_w, const int32_t* dest_row
                     fn);
 }
 
-int moe_combine_dx(const void* dx_perm, const int32_t* dest_row, const float* d_topk_w,
-                   const float* topk_w, const int32_t* topk_idx, const void* w_router, int T,
-                   int H, int E, int k, int dtype, void* dx, void* ws, size_t ws_bytes,
-                   void* stream) {
-  const char* fn = "moe_combine_dx";
+// Argument checks shared by the two forms of the fused input gradient (the
+// router weight as given, [H,E], or already transposed, [E,H]).
+static int check_combine_dx(const void* dx_perm, const int32_t* dest_row, const float* d_topk_w,
+                            const float* topk_w, const int32_t* topk_idx, const void* w_router,
+                            const char* w_name, int T, int H, int E, int k, int dtype, void* dx,
+                            const char* fn) {
   if (int rc = check_dtype(dtype, fn)) return rc;
   if (int rc = check_routing_shape(T, E, k, fn)) return rc;
   if (int rc = check_row_width(H, dtype, fn)) return rc;
-  if (int rc = check_ws(ws, ws_bytes, align256((size_t)E * H * elem_bytes(dtype)), fn)) return rc;
   if (T == 0) return MOE_OK;
   if (int rc = check_ptr(dx_perm, "dx_perm", fn, true)) return rc;
   if (int rc = check_ptr(dest_row, "dest_row", fn)) return rc;
   if (int rc = check_ptr(d_topk_w, "d_topk_w", fn)) return rc;
   if (int rc = check_ptr(topk_w, "topk_w", fn)) return rc;
   if (int rc = check_ptr(topk_idx, "topk_idx", fn)) return rc;
-  if (int rc = check_ptr(w_router, "w_router", fn, true)) return rc;
+  if (int rc = check_ptr(w_router, w_name, fn, true)) return rc;
   if (int rc = check_ptr(dx, "dx", fn, true)) return rc;
+  return MOE_OK;
+}
+
+int moe_combine_dx(const void* dx_perm, const int32_t* dest_row, const float* d_topk_w,
+                   const float* topk_w, const int32_t* topk_idx, const void* w_router, int T,
+                   int H, int E, int k, int dtype, void* dx, void* ws, size_t ws_bytes,
+                   void* stream) {
+  const char* fn = "moe_combine_dx";
+  if (int rc = check_combine_dx(dx_perm, dest_row, d_topk_w, topk_w, topk_idx, w_router,
+                                "w_router", T, H, E, k, dtype, dx, fn))
+    return rc;
+  if (int rc = check_ws(ws, ws_bytes, align256((size_t)E * H * elem_bytes(dtype)), fn)) return rc;
+  if (T == 0) return MOE_OK;
   hipStream_t s = begin_launch(stream);
   hipError_t e = launch_transpose(w_router, ws, H, E, elem_bytes(dtype), s);
   if (e == hipSuccess)
     e = launch_combine_dx(dx_perm, dest_row, d_topk_w, topk_w, topk_idx, ws, T, H, k,
                           dtype == MOE_BF16, dx, s);
   return hip_status(e, fn);
+}
+
+int moe_combine_dx_t(const void* dx_perm, const int32_t* dest_row, const float* d_topk_w,
+                     const float* topk_w, const int32_t* topk_idx, const void* w_router_t, int T,
+                     int H, int E, int k, int dtype, void* dx, void* stream) {
+  const char* fn = "moe_combine_dx_t";
+  if (int rc = check_combine_dx(dx_perm, dest_row, d_topk_w, topk_w, topk_idx, w_router_t,
+                                "w_router_t", T, H, E, k, dtype, dx, fn))
+    return rc;
+  if (T == 0) return MOE_OK;
+  hipStream_t s = begin_launch(stream);
+  return hip_status(launch_combine_dx(dx_perm, dest_row, d_topk_w, topk_w, topk_idx, w_router_t,
+                                      T, H, k, dtype == MOE_BF16, dx, s),
+                    fn);
+}
+
+int moe_router_weight_t(const void* w_router, int H, int E, int dtype, void* w_router_t,
+                        void* stream) {
+  const char* fn = "moe_router_weight_t";
+  if (int rc = check_dtype(dtype, fn)) return rc;
+  if (H < 0 || H > (1 << 20) || E < 0 || E > (1 << 20))
+    return fail(MOE_EINVAL, "%s: H=%d and E=%d must lie in [0, 2^20]", fn, H, E);
+  if ((long long)H * E == 0) return MOE_OK;
+  if (int rc = check_ptr(w_router, "w_router", fn)) return rc;
+  if (int rc = check_ptr(w_router_t, "w_router_t", fn)) return rc;
+  hipStream_t s = begin_launch(stream);
+  return hip_status(launch_transpose(w_router, w_router_t, H, E, elem_bytes(dtype), s), fn);
 }
 
 int moe_combine_bwd(const void* dy, const void* y_perm, const float* topk_w,

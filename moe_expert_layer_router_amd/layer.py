@@ -1,8 +1,9 @@
 """A whole MoE expert layer (forward and backward) over preallocated buffers.
 
 Chains the C-ABI calls in the order of the layer: route -> permute ->
-grouped FFN -> combine, and for the backward combine_bwd -> route_bwd ->
-grouped FFN backward -> unweighted combine of dx_perm plus the router's dx.
+grouped FFN -> combine, and for the backward the router weight's transpose ->
+combine_bwd -> grouped FFN backward -> unweighted combine of dx_perm plus the
+router's dx (on that transpose) -> route_bwd.
 All buffers and workspaces are allocated once in the constructor, so
 forward()/backward() only enqueue kernels (and can be captured into a HIP
 graph).  In the backward, the grouped FFN's weight gradients and then the
@@ -18,7 +19,7 @@ from typing import Dict, Optional
 
 import torch
 
-from . import (MOE_BF16, MOE_F32, MOE_OP_COMBINE_DX, MOE_OP_FFN_BWD, MOE_OP_FFN_FWD, MOE_OP_PERMUTE,
+from . import (MOE_BF16, MOE_F32, MOE_OP_FFN_BWD, MOE_OP_FFN_FWD, MOE_OP_PERMUTE,
                MOE_OP_ROUTE, MOE_OP_ROUTE_BWD, _check, _stream, lib, workspace_bytes)
 
 
@@ -61,10 +62,11 @@ class MoELayer:
             b["dw_up"] = torch.empty((E_l, I, H), dtype=f32, device=dev)
             b["dw_down"] = torch.empty((E_l, H, I), dtype=f32, device=dev)
             b["dx"] = torch.empty((T, H), dtype=dtype, device=dev)
+            b["w_router_t"] = torch.empty((E, H), dtype=dtype, device=dev)
         self.buf = b
         ops = [MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN_FWD]
         if train:
-            ops += [MOE_OP_FFN_BWD, MOE_OP_ROUTE_BWD, MOE_OP_COMBINE_DX]
+            ops += [MOE_OP_FFN_BWD, MOE_OP_ROUTE_BWD]
         nb = max(workspace_bytes(op, T, H, I, E, k, e_lo, e_hi, self.dt) for op in ops)
         # one workspace for the calls that run one after another on the current
         # stream; the backward's concurrent calls get their own
@@ -73,7 +75,6 @@ class MoELayer:
         if train:
             ws = lambda op: torch.empty(max(workspace_bytes(op, T, H, I, E, k, e_lo, e_hi, self.dt), 256),
                                         dtype=torch.uint8, device=dev)
-            self.ws_dx = ws(MOE_OP_COMBINE_DX)
             self.ws_rb = ws(MOE_OP_ROUTE_BWD)
             self.side = torch.cuda.Stream(device=dev) if dev.type == "cuda" else None
 
@@ -101,6 +102,11 @@ class MoELayer:
         b, T, H, I, E, k = self.buf, self.T, self.H, self.I, self.E, self.k
         s = _stream()
         ws, wsb = _p(self.ws), self.ws_bytes
+        # the router weight's transpose while nothing else runs: later, behind
+        # the data gradients, its small grid would wait for CUs that the
+        # concurrent weight-gradient product holds
+        _check(lib.moe_router_weight_t(_p(w_router), H, E, self.dt, _p(b["w_router_t"]), s),
+               "moe_router_weight_t")
         _check(lib.moe_combine_bwd(_p(dy), _p(b["y_perm"]), _p(b["topk_w"]), _p(b["dest_row"]), T, H,
                                    k, self.dt, _p(b["dy_perm"]), _p(b["d_topk_w"]), s),
                "moe_combine_bwd")
@@ -114,10 +120,10 @@ class MoELayer:
                                              _p(b["dw_down"]), 0, ws, wsb, s, side),
                "moe_grouped_ffn_bwd_split")
         # input gradient: the experts' part and the router's part in one pass
-        _check(lib.moe_combine_dx(_p(b["dx_perm"]), _p(b["dest_row"]), _p(b["d_topk_w"]),
-                                  _p(b["topk_w"]), _p(b["topk_idx"]), _p(w_router), T, H, E, k,
-                                  self.dt, _p(b["dx"]), _p(self.ws_dx), self.ws_dx.numel(), s),
-               "moe_combine_dx")
+        _check(lib.moe_combine_dx_t(_p(b["dx_perm"]), _p(b["dest_row"]), _p(b["d_topk_w"]),
+                                    _p(b["topk_w"]), _p(b["topk_idx"]), _p(b["w_router_t"]), T, H,
+                                    E, k, self.dt, _p(b["dx"]), s),
+               "moe_combine_dx_t")
         # router backward behind the weight gradients (the side stream already
         # waits for d_topk_w: the FFN call forked it after the combine backward)
         _check(lib.moe_route_bwd(_p(b["d_topk_w"]), _p(b["topk_w"]), _p(b["topk_idx"]), _p(x),

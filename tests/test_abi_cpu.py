@@ -50,7 +50,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_single_hip_runtime():
-    assert L.moe_abi_version() == moe.ABI_VERSION == 3
+    assert L.moe_abi_version() == moe.ABI_VERSION == 4
     libs = moe.hip_runtimes_mapped()
     assert len(libs) <= 1, libs
 
@@ -260,6 +260,26 @@ def test_combine_dx_errors():
     assert f(*bad) == OK
 
 
+def test_combine_dx_t_and_router_weight_t_errors():
+    f = lambda *a: L.moe_combine_dx_t(*a)
+    args = [A, A, A, A, A, A, 64, 128, 8, 2, BF16, A, S]
+    bad = list(args); bad[9] = 9        # k > E
+    assert f(*bad) == EINVAL
+    bad = list(args); bad[5] = N        # transposed router weight
+    assert f(*bad) == EINVAL and "w_router_t" in _err()
+    bad = list(args); bad[7] = 100      # H not a multiple of 8 (bf16 rows of 16 bytes)
+    assert f(*bad) == EINVAL
+    bad = list(args); bad[6] = 0        # T = 0: nothing to do
+    assert f(*bad) == OK
+    g = lambda *a: L.moe_router_weight_t(*a)
+    assert g(A, 128, 8, 7, A, S) == EINVAL                     # dtype
+    assert g(A, -1, 8, BF16, A, S) == EINVAL
+    assert g(A, 128, (1 << 20) + 1, BF16, A, S) == EINVAL
+    assert g(N, 128, 8, BF16, A, S) == EINVAL and "w_router" in _err()
+    assert g(A, 128, 8, BF16, N, S) == EINVAL and "w_router_t" in _err()
+    assert g(N, 0, 8, BF16, N, S) == OK                        # empty: nothing to do
+
+
 def test_layer_buffers_and_workspace_on_host():
     """The layer's set-up (buffers, one workspace for every call) needs no GPU."""
     import torch
@@ -267,6 +287,6 @@ def test_layer_buffers_and_workspace_on_host():
     for train in (False, True):
         layer = moe.MoELayer(64, 128, 64, 8, 2, 0, 8, torch.bfloat16, device="cpu", train=train)
         need = max(moe.workspace_bytes(op, 64, 128, 64, 8, 2, 0, 8, moe.MOE_BF16)
-                   for op in range(6 if train else 3))
+                   for op in range(5 if train else 3))
         assert layer.ws_bytes >= need
         assert ("dx" in layer.buf) == train

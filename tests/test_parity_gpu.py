@@ -471,7 +471,14 @@ def test_combine_dx_matches_oracle(case):
     g_dest = torch.from_numpy(dest).to(DEV)
     print(f"  case {name}: T={T} H={H} E={E} k={k} R={R}", flush=True)
     dx = moe.moe_combine_dx(dxp, g_dest, g_dtw, g_tw, g_idx, wr)
+    # the two-call form: a bit copy of the transposed router weight, then the
+    # same gather, so the same bits
+    wt = moe.moe_router_weight_t(wr)
+    dx_t = moe.moe_combine_dx_t(dxp, g_dest, g_dtw, g_tw, g_idx, wt)
     torch.cuda.synchronize()
+    ib = torch.int16 if dtype == "bf16" else torch.int32
+    assert torch.equal(wt.cpu().view(ib), wr.cpu().t().contiguous().view(ib))
+    assert torch.equal(dx_t.cpu().view(ib), dx.cpu().view(ib))
     tw64, dtw64 = _np(g_tw), _np(g_dtw)
     dxp64, wr64 = _np(dxp)[:R], _np(wr)
     dz = O.router_logit_grad(tw64, dtw64, idx, E)
