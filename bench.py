@@ -157,7 +157,7 @@ def cpu_baseline(w, inp, target_s=12.0):
     while dt < target_s / 4 and Ts < w.T:
         Ts = int(min(w.T, max(2 * Ts, Ts * target_s / max(dt, 1e-3))))
         dt, R = run(Ts)
-    reps = max(1, min(10, int(target_s / 2 / max(dt, 1e-3))))
+    reps = max(1, min(20, int(target_s / max(dt, 1e-3))))
     for _ in range(reps - 1):
         dt += run(Ts)[0]
     dt /= reps
