@@ -262,22 +262,27 @@ def moe_forward_pairs(x, idx, w, w_gate, w_up, w_down, e_lo: int, e_hi: int) -> 
 
 def pair_values(x, idx, w_gate, w_up, w_down, e_lo: int, e_hi: int,
                 tokens: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
-    """Per (token, slot) intermediates g, u, h [n, k, I] and expert output y [n, k, H]
-    for the listed tokens (all when None); NaN for non-local slots."""
+    """Per (token, slot) intermediates of the expert FFN for the listed tokens
+    (all when None): g, u, h [n, k, I] and the expert output y [n, k, H] of
+    slot j of token t, i.e. expert_ffn_parts(x[t], expert idx[t, j]).  Slots
+    whose expert is not in [e_lo, e_hi) stay NaN (nothing is computed for
+    them on this rank).  Each local expert takes the rows of all listed
+    tokens that chose it at once (boolean selection, as moe_forward does)."""
     x = _f64(x)
     idx = np.asarray(idx)
     toks = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens)
+    sub = idx[toks]
     k = idx.shape[1]
-    I = w_gate.shape[1]
+    I = np.asarray(w_gate).shape[1]
     H = x.shape[1]
     out = {n: np.full((len(toks), k, d), np.nan) for n, d in (("g", I), ("u", I), ("h", I), ("y", H))}
-    for a, t in enumerate(toks):
-        for j in range(k):
-            e = int(idx[t, j])
-            if e_lo <= e < e_hi:
-                p = expert_ffn_parts(x[t:t + 1], w_gate[e - e_lo], w_up[e - e_lo], w_down[e - e_lo])
-                for n in out:
-                    out[n][a, j] = p[n][0]
+    for e in range(e_lo, e_hi):
+        aa, jj = np.nonzero(sub == e)          # positions in the token list, slots
+        if len(aa) == 0:
+            continue
+        p = expert_ffn_parts(x[toks[aa]], w_gate[e - e_lo], w_up[e - e_lo], w_down[e - e_lo])
+        for n in out:
+            out[n][aa, jj] = p[n]
     return out
 
 
@@ -362,11 +367,26 @@ def fp8_matmul_rows(aq, sa, bq, sb) -> np.ndarray:
 
 
 def round_bf16(a) -> np.ndarray:
-    """a rounded to the nearest bfloat16 (ties to even), as float64."""
-    a32 = np.asarray(a, dtype=np.float32)
-    bits = a32.view(np.uint32).astype(np.uint64)
-    bits = (bits + 0x7FFF + ((bits >> 16) & 1)) >> 16 << 16
-    return bits.astype(np.uint32).view(np.float32).astype(np.float64)
+    """a rounded to the nearest bfloat16 value (ties to the even mantissa), as
+    float64, rounded once and directly from the float64 input.
+
+    bfloat16 keeps 8 significant bits (7 stored) over float32's exponent
+    range: for |a| in [2^(E-1), 2^E) the spacing of representable values is
+    2^(E-8), and below the smallest normal 2^-126 the subnormal spacing
+    2^-133 applies.  a / spacing is exact (a power of two), np.rint rounds it
+    to the nearest integer with ties to even, which is the even stored
+    mantissa.  Magnitudes that round past the largest finite value
+    (2 - 2^-7) * 2^127 become infinities; the sign of zero is kept.
+    """
+    a = _f64(a)
+    mag = np.abs(a)
+    _, fe = np.frexp(mag)                                  # mag = f * 2^fe, f in [0.5, 1)
+    spacing = np.exp2(np.maximum(fe - 1, -126) - 7.0)
+    with np.errstate(over="ignore"):
+        r = np.rint(mag / spacing) * spacing
+    r = np.where(r > (2.0 - 2.0 ** -7) * 2.0 ** 127, np.inf, r)
+    r = np.where(np.isnan(a), np.nan, r)
+    return np.copysign(r, a)
 
 
 def expert_ffn_fp8_parts(vq, sv, wgq, sg, wuq, su, wdq, sd) -> Dict[str, np.ndarray]:

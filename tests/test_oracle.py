@@ -504,6 +504,71 @@ def check_fp8_dgrad_close_to_exact():
     assert np.array_equal(p2["dh"], O.round_bf16(dy2 @ wd2[0]))
 
 
+def check_round_bf16_vs_torch():
+    """round_bf16 against torch's float32 -> bfloat16 conversion (round to nearest
+    even): random values over the whole exponent range, exact half-way cases with an
+    even and with an odd kept mantissa, values at and past the largest finite
+    bfloat16, float32 subnormals, and -0.  On float64 inputs the rounding is direct:
+    a value just past a half-way point goes up even where float32 would first have
+    rounded it onto that point."""
+    rng = np.random.default_rng(12)
+    v = (rng.standard_normal(20000) * np.exp2(rng.integers(-140, 128, 20000))).astype(np.float32)
+    base = torch.tensor(rng.integers(0, 1 << 16, 4000, dtype=np.int64).astype(np.int16)).view(torch.bfloat16)
+    base = base[torch.isfinite(base)].float().numpy().astype(np.float32)
+    # half-way points above each base value: the low 16 bits 0x8000 exactly
+    half = (base.view(np.uint32) | np.uint32(0x8000)).view(np.float32)
+    half = half[np.isfinite(half)]
+    edge = np.array([3.3895314e38, 3.3961776e38, 3.3961778e38, 3.4e38, -3.4e38, np.finfo(np.float32).max,
+                     1e-40, -1e-40, 9.2e-41, 1e-45, 2.0 ** -133, 3 * 2.0 ** -134, 2.0 ** -134,
+                     -0.0, 0.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 3 * 2 ** -8)], dtype=np.float32)
+    for arr in (v, half, edge):
+        ref = torch.from_numpy(arr).to(torch.bfloat16).double().numpy()
+        got = O.round_bf16(arr.astype(np.float64))
+        same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+        assert same.all(), (arr[~same][:4], got[~same][:4], ref[~same][:4])
+        assert np.array_equal(np.signbit(got), np.signbit(ref))
+    odd_mid = 1.0 + 3 * 2.0 ** -8                 # between 1 + 2^-7 and 1 + 2^-6: ties to 1 + 2^-6
+    assert O.round_bf16(odd_mid) == 1.0 + 2.0 ** -6
+    assert O.round_bf16(1.0 + 2.0 ** -8) == 1.0   # between 1 and 1 + 2^-7: ties to 1
+    just_past = 1.0 + 2.0 ** -8 + 2.0 ** -40      # float32 would round this onto the half-way point
+    assert np.float32(just_past) == np.float32(1.0 + 2.0 ** -8)
+    assert O.round_bf16(just_past) == 1.0 + 2.0 ** -7
+
+
+def check_pair_values_rows():
+    """pair_values on an EP rank (e_lo != 0): each local slot's g, u, h, y equal a
+    per-element loop of the SwiGLU expert written out here (sums over H and I
+    in Python), non-local slots are NaN, and the gate-weighted sum of a token's
+    local slots is moe_forward's output."""
+    w, inp = _tiny(T=12, H=8, I=4, E=6, k=3, e_lo=2, e_hi=5)
+    z, idx, gw = O.route(inp["x"], inp["w_router"], w.k)
+    pv = O.pair_values(inp["x"], idx, inp["w_gate"], inp["w_up"], inp["w_down"], w.e_lo, w.e_hi)
+    x = np.asarray(inp["x"], np.float64)
+    nloc = 0
+    for t in range(w.T):
+        for j in range(w.k):
+            e = int(idx[t, j])
+            if not w.e_lo <= e < w.e_hi:
+                assert all(np.isnan(pv[n][t, j]).all() for n in pv)
+                continue
+            nloc += 1
+            Wg, Wu, Wd = (np.asarray(inp[n][e - w.e_lo], np.float64) for n in ("w_gate", "w_up", "w_down"))
+            g = [sum(x[t, h] * Wg[i, h] for h in range(w.H)) for i in range(w.I)]
+            u = [sum(x[t, h] * Wu[i, h] for h in range(w.H)) for i in range(w.I)]
+            hh = [g[i] / (1.0 + math.exp(-g[i])) * u[i] for i in range(w.I)]
+            y = [sum(hh[i] * Wd[m, i] for i in range(w.I)) for m in range(w.H)]
+            for n, ref in (("g", g), ("u", u), ("h", hh), ("y", y)):
+                assert np.allclose(pv[n][t, j], ref, rtol=1e-12, atol=1e-14), (n, t, j)
+    assert 0 < nloc < w.T * w.k
+    ysum = np.nansum(pv["y"] * np.asarray(gw)[:, :, None], axis=1)
+    ref = O.moe_forward(inp["x"], idx, gw, inp["w_gate"], inp["w_up"], inp["w_down"], w.e_lo, w.e_hi)
+    assert np.allclose(ysum, ref, rtol=1e-12, atol=1e-14)
+    sub = O.pair_values(inp["x"], idx, inp["w_gate"], inp["w_up"], inp["w_down"], w.e_lo, w.e_hi,
+                        tokens=[7, 2])
+    for n in pv:
+        assert np.allclose(sub[n], pv[n][[7, 2]], rtol=1e-12, atol=1e-14, equal_nan=True)
+
+
 ALL_CHECKS = [check_gating_golden, check_topk_brute_force, check_zero_input_routing,
               check_duplicate_router_columns, check_k1_and_kE, check_weights_sum_to_one,
               check_counts_offsets, check_permutation_maps, check_permute_unpermute_identity,
@@ -512,7 +577,7 @@ ALL_CHECKS = [check_gating_golden, check_topk_brute_force, check_zero_input_rout
               check_finite_differences, check_router_grads_vs_autograd, check_fp8_codes_vs_torch,
               check_fp8_row_scale_is_minimal, check_fp8_matmul_brute_force,
               check_fp8_forward_close_to_exact, check_fp8_weight_t_scales_per_input_channel,
-              check_fp8_dgrad_close_to_exact]
+              check_fp8_dgrad_close_to_exact, check_round_bf16_vs_torch, check_pair_values_rows]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
@@ -619,9 +684,38 @@ def _mut_fp8_t_scales_per_output_channel(w0, w1=None):
     return q, np.broadcast_to(sc.max(axis=2), (El, K)).copy()
 
 
+def _mut_bf16_truncates(a):
+    a32 = np.asarray(a, np.float32)
+    return (a32.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32).astype(np.float64)
+
+
+def _mut_bf16_ties_away(a):
+    a32 = np.asarray(a, np.float32)
+    b = a32.view(np.uint32).astype(np.uint64)
+    return ((b + 0x8000) >> 16 << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _mut_bf16_via_float32(a):
+    """rounds to float32 first, then to bfloat16 (double rounding)"""
+    return _ORIG["round_bf16"](np.asarray(a, np.float32).astype(np.float64))
+
+
+def _mut_pair_values_global_index(x, idx, w_gate, w_up, w_down, e_lo, e_hi, tokens=None):
+    """indexes the local weight stacks by the global expert id"""
+    E_l = e_hi - e_lo
+    roll = lambda wt: np.roll(np.asarray(wt), -e_lo % E_l, axis=0)
+    return _ORIG["pair_values"](x, idx, roll(w_gate), roll(w_up), roll(w_down), e_lo, e_hi, tokens)
+
+
+def _mut_pair_values_slot_order(x, idx, w_gate, w_up, w_down, e_lo, e_hi, tokens=None):
+    out = _ORIG["pair_values"](x, idx, w_gate, w_up, w_down, e_lo, e_hi, tokens)
+    return {n: v[:, ::-1].copy() for n, v in out.items()}
+
+
 _ORIG = {n: getattr(OM, n) for n in ("silu", "topk_experts", "gate_weights", "permutation_maps",
                                      "moe_backward", "expert_ffn_parts", "fp8_e4m3_encode",
-                                     "fp8_row_exponent", "quantize_expert_weights_t_fp8")}
+                                     "fp8_row_exponent", "quantize_expert_weights_t_fp8",
+                                     "round_bf16", "pair_values")}
 
 MUTATIONS = [("silu", _mut_silu_is_sigmoid), ("topk_experts", _mut_topk_ties_high),
              ("gate_weights", _mut_no_renorm), ("permutation_maps", _mut_group_tokens_descending),
@@ -633,7 +727,11 @@ MUTATIONS = [("silu", _mut_silu_is_sigmoid), ("topk_experts", _mut_topk_ties_hig
              ("fp8_row_exponent", _mut_fp8_exponent_one_high),
              ("fp8_matmul_rows", _mut_fp8_scale_wrong_axis),
              ("quantize_expert_weights_t_fp8", _mut_fp8_t_gate_up_swapped),
-             ("quantize_expert_weights_t_fp8", _mut_fp8_t_scales_per_output_channel)]
+             ("quantize_expert_weights_t_fp8", _mut_fp8_t_scales_per_output_channel),
+             ("round_bf16", _mut_bf16_truncates), ("round_bf16", _mut_bf16_ties_away),
+             ("round_bf16", _mut_bf16_via_float32),
+             ("pair_values", _mut_pair_values_global_index),
+             ("pair_values", _mut_pair_values_slot_order)]
 
 
 @pytest.mark.parametrize("name,mut", MUTATIONS, ids=[m[1].__name__ for m in MUTATIONS])
@@ -644,6 +742,6 @@ def test_planted_mistake_is_caught(monkeypatch, name, mut):
     for chk in ALL_CHECKS:
         try:
             chk()
-        except AssertionError:
+        except Exception:          # a pin that fails or breaks on the mistake catches it
             failed.append(chk.__name__)
     assert failed, f"no pin caught the planted mistake in {name}"
