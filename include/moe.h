@@ -19,9 +19,13 @@
  *     dense.  Activations and weights are bf16 (MOE_BF16) or fp32 (MOE_F32);
  *     indices are int32; gate weights, logits and weight gradients are fp32.
  *   - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
- *     null stream).  No call synchronises, allocates device memory or keeps
- *     state between calls.  Scratch memory is the caller's `ws` buffer, sized
- *     by moe_workspace_bytes() and aligned to 256 bytes.
+ *     null stream).  No call synchronises, allocates device memory or passes
+ *     data from one call to the next.  Scratch memory is the caller's `ws`
+ *     buffer, sized by moe_workspace_bytes() and aligned to 256 bytes.  The
+ *     only objects the library keeps are, per calling thread and device, the
+ *     second stream and three events of moe_grouped_ffn_bwd (and the events of
+ *     moe_grouped_ffn_bwd_split), created on first use and held until the
+ *     process ends; calls from different host threads share none of them.
  *   - Arguments are validated on the host before any HIP call.  On error the
  *     call enqueues nothing and returns a negative moe_status; moe_last_error()
  *     returns a per-thread message.  MOE_EHIP reports a failed launch.
@@ -35,6 +39,10 @@
  *     H % 4 == 0 (fp32).  The bf16 router and expert GEMMs additionally need
  *     H % 64 == 0 and I % 64 == 0 (else MOE_EUNSUPPORTED).  Pointers to
  *     row data must be 16-byte aligned.
+ *   - The bf16 and FP8 matrix-core kernels address operands with 32-bit byte
+ *     ranges: R_cap * max(H, 2I) * elem, 2 * I * H * elem (one expert's gate
+ *     and up weights) and, for the bf16 router weight gradient, T * H * 2
+ *     must each stay below 2^31 bytes (else MOE_EUNSUPPORTED).
  */
 #ifndef MOE_H
 #define MOE_H
@@ -117,7 +125,10 @@ int moe_route_from_logits(const float* logits, int T, int E, int k, int32_t* top
  *   src_row  [T*k]   int32: token of grouped row r, for r < R
  *   x_perm   [T*k,H] dtype: x_perm[dest_row[t*k+j]] = x[t], bitwise
  *   ws       MOE_OP_PERMUTE workspace
- * dtype MOE_FP8 moves rows of H one-byte codes (H % 16 == 0). */
+ * dtype MOE_FP8 moves rows of H one-byte codes (H % 16 == 0).
+ * A row of topk_idx may name one expert in several slots (moe_route never
+ * does): each such slot gets its own grouped row, the slots of one token in
+ * slot order, and counts count slots. */
 int moe_permute(const void* x, const int32_t* topk_idx, int T, int H, int E, int k, int e_lo,
                 int e_hi, int dtype, int32_t* counts, int32_t* offsets, int32_t* dest_row,
                 int32_t* src_row, void* x_perm, void* ws, size_t ws_bytes, void* stream);
@@ -137,8 +148,9 @@ int moe_grouped_ffn_fwd(const void* x_perm, const int32_t* offsets, int E_l, int
                         void* stream);
 
 /* FP8 recipe of the expert FFN.  The pages name FP8 as their only
- * kernel-level speed lever (page "Qwen3-MoE-30B-A3B模型EP+FSDP2并行方案",
- * closing throughput table) and fix no format or scaling; this library's
+ * kernel-level speed lever (page "TorchTitan FSDP2 完全指南", section
+ * "性能表现", H100 benchmark table, row FSDP + compile + FP8) and fix no
+ * format or scaling; this library's
  * reading: OCP E4M3 codes (largest finite 448, subnormals down to 2^-9), one
  * power-of-two scale per row (token row of the activations, output channel of
  * a weight matrix, row of h).
@@ -303,8 +315,9 @@ int moe_route_bwd(const float* d_topk_w, const float* topk_w, const int32_t* top
  * the caller) on the launch stream immediately before and after the i-th
  * launch of kernel `kernel_id`, for i < n; later launches are not recorded.
  * kernel_id < 0 switches recording off.  The arrays must stay valid while
- * recording is on.  Process-wide state: not for concurrent use from several
- * threads.  Returns MOE_OK or MOE_EINVAL. */
+ * recording is on.  The hook is per calling thread: it records launches made
+ * by the thread that armed it, and other threads' calls are not affected.
+ * Returns MOE_OK or MOE_EINVAL. */
 typedef enum {
   MOE_KERNEL_ROUTE = 0,           /* router GEMM + top-k */
   MOE_KERNEL_PERMUTE_HIST = 1,
@@ -326,7 +339,8 @@ typedef enum {
 
 int moe_profile_kernel(int kernel_id, void** start_events, void** stop_events, int n);
 
-/* Number of launches recorded since the last moe_profile_kernel() call. */
+/* Number of launches recorded since the calling thread's last
+ * moe_profile_kernel() call. */
 int moe_profile_recorded(void);
 
 #ifdef __cplusplus

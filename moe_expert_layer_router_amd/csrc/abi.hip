@@ -105,6 +105,19 @@ size_t ws_route_bwd(int T, int H, int E, int dtype) {
                   sizeof(float));
 }
 
+// The MFMA kernels address their operands through buffer descriptors with
+// 32-bit byte ranges, and move the DMA of K steps past the end to offset 2^31
+// (where the hardware drops it): every range they read or write must stay
+// below 2 GiB.
+constexpr int64_t kMaxRangeBytes = (int64_t)1 << 31;
+
+int check_range(int64_t bytes, const char* what, const char* fn) {
+  if (bytes >= kMaxRangeBytes)
+    return fail(MOE_EUNSUPPORTED, "%s: %s spans %lld bytes; the MFMA kernels need every operand "
+                "below 2 GiB", fn, what, (long long)bytes);
+  return MOE_OK;
+}
+
 int check_ffn_shape(int E_l, int R_cap, int H, int I, int dtype, const char* fn) {
   if (E_l < 1 || E_l > kMaxE) return fail(MOE_EINVAL, "%s: E_l=%d outside [1, %d]", fn, E_l, kMaxE);
   if (R_cap < 0) return fail(MOE_EINVAL, "%s: R_cap must be >= 0", fn);
@@ -113,6 +126,11 @@ int check_ffn_shape(int E_l, int R_cap, int H, int I, int dtype, const char* fn)
   if (dtype == MOE_BF16 && (H % 64 != 0 || I % 64 != 0))
     return fail(MOE_EUNSUPPORTED, "%s: bf16 expert GEMMs need H %% 64 == 0 and I %% 64 == 0 (H=%d, I=%d)",
                 fn, H, I);
+  if (dtype != MOE_F32) {  // the fp32 kernels index with 64-bit offsets
+    const int64_t eb = elem_bytes(dtype);
+    if (int rc = check_range((int64_t)R_cap * std::max(H, 2 * I) * eb, "a grouped-row buffer", fn)) return rc;
+    if (int rc = check_range((int64_t)2 * I * H * eb, "one expert's gate and up weights", fn)) return rc;
+  }
   return MOE_OK;
 }
 
@@ -121,12 +139,14 @@ int check_ffn_shape(int E_l, int R_cap, int H, int I, int dtype, const char* fn)
 // ---------------------------------------------------------------------------
 // kernel timing hook
 // ---------------------------------------------------------------------------
+// Per calling thread: only launches made by the thread that armed the hook
+// are recorded.
 namespace {
-int g_prof_id = -1;
-void** g_prof_start = nullptr;
-void** g_prof_stop = nullptr;
-int g_prof_n = 0;
-int g_prof_next = 0;
+thread_local int g_prof_id = -1;
+thread_local void** g_prof_start = nullptr;
+thread_local void** g_prof_stop = nullptr;
+thread_local int g_prof_n = 0;
+thread_local int g_prof_next = 0;
 }  // namespace
 
 namespace moe {
@@ -574,6 +594,10 @@ int moe_route_bwd(const float* d_topk_w, const float* topk_w, const int32_t* top
   if (dtype == MOE_BF16 && (H % 64 != 0 || E % 4 != 0))
     return fail(MOE_EUNSUPPORTED,
                 "%s: the bf16 router backward needs H %% 64 == 0 and E %% 4 == 0 (H=%d, E=%d)", fn, H, E);
+  if (dtype == MOE_BF16 && dw_router != nullptr) {  // x^T . dz runs on the MFMA kernel
+    if (int rc = check_range((int64_t)T * H * 2, "x", fn)) return rc;
+    if (int rc = check_range((int64_t)T * 4 * E, "the split logit gradient", fn)) return rc;
+  }
   if (int rc = check_ptr(w_router, "w_router", fn, true)) return rc;
   if (int rc = check_ptr(d_logits, "d_logits", fn)) return rc;
   if (dx_router != nullptr && !aligned16(dx_router))

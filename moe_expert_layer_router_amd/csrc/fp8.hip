@@ -1,7 +1,8 @@
 // E4M3 quantization of rows with one power-of-two scale per row, the FP8
 // recipe of the expert FFN (the pages name FP8 as their kernel-level speed
-// lever, page "Qwen3-MoE-30B-A3B模型EP+FSDP2并行方案", closing throughput
-// table; the format and the scaling are this library's reading).
+// lever, page "TorchTitan FSDP2 完全指南", section "性能表现", H100 benchmark
+// table, row FSDP + compile + FP8; the format and the scaling are this
+// library's reading).
 //
 // Row scale s = 2^e, e the smallest integer with max|row| <= 448 * 2^e
 // (e = 0 for a zero row): with max|row| = f * 2^E, f in [0.5, 1), and

@@ -57,7 +57,6 @@
 #include "common.h"
 
 #include <algorithm>
-#include <mutex>
 
 namespace moe {
 
@@ -1190,7 +1189,9 @@ __global__ __launch_bounds__(kMaxE) void ffn_sched_kernel(const int32_t* __restr
   const int e = threadIdx.x, lane = e & (kWave - 1), w = e / kWave;
   const int o0 = (e < E_l) ? offsets[e] : 0;
   const int o1 = (e < E_l) ? offsets[e + 1] : 0;
-  s_off[e] = o0;
+  // Only the owners write: s_off[E_l] comes from thread E_l - 1 alone (thread
+  // E_l, in another wave when E_l % 64 == 0, must not store its zero there).
+  if (e < E_l) s_off[e] = o0;
   if (e == E_l - 1) s_off[E_l] = o1;
   int v = (o1 - o0 + rows - 1) / rows;  // this expert's tiles
   // inclusive scan: within each wave by shuffles, then the waves' totals
@@ -1446,20 +1447,24 @@ hipError_t launch_ffn_dgrad_fp8(const uint8_t* dy_q, const float* dy_scale, cons
 }
 
 // A second stream of the calling device for products that may run beside
-// others (created once per device, default priority, never destroyed), and
-// the events that fork it from and join it back to the caller's stream.  Null
-// when it cannot be created: everything then runs on the caller's stream.
+// others, and the events that fork it from and join it back to the caller's
+// stream.  One set per calling thread and device (created on first use,
+// default priority, held until the process ends), so that calls from several
+// host threads never record or wait on each other's events.  Within one
+// thread, each call records an event and enqueues the waits on it before it
+// returns, so a later call's record does not move an earlier call's wait.
+// Null when it cannot be created: everything then runs on the caller's stream.
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, mid = nullptr, join = nullptr;
 };
 
+constexpr int kMaxDevices = 64;
+
 static SideStream* side_stream() {
-  static SideStream per_dev[64];
-  static std::mutex mu;
+  thread_local SideStream per_dev[kMaxDevices];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  std::lock_guard<std::mutex> lk(mu);
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
   SideStream& ss = per_dev[dev];
   if (ss.s == nullptr) {
     hipStream_t st = nullptr;

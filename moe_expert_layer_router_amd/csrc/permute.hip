@@ -8,7 +8,9 @@
 //  1. hist_rank: each block of 256 tokens builds, in LDS, one 256-bit token
 //     mask per local expert with atomicOr (order independent), then reads off
 //     per-expert block counts and each slot's rank among earlier tokens of the
-//     block (popcount of the mask bits below it).
+//     block (popcount of the mask bits below it).  A block in which a token
+//     lists one local expert twice ranks its slots by a walk in (token, slot)
+//     order instead.
 //  2. scan: one workgroup turns block counts into counts, offsets and the base
 //     row of every (block, expert) pair.
 //  3. scatter: one wave per token computes its k destination rows and, if
@@ -33,7 +35,9 @@ __global__ __launch_bounds__(kPermBlock) void hist_rank_kernel(const int32_t* __
   __shared__ uint32_t mask[kMaxE][NW];
   __shared__ int16_t s_e[kPermBlock * kMaxK];  // local expert of each slot of the block, or -1
   __shared__ int32_t s_pre[kMaxE][NW];         // set bits of mask[e] in words before w
+  __shared__ int s_dup;                        // some token repeats a local expert
   const int tid = threadIdx.x;
+  if (tid == 0) s_dup = 0;
   const int t0 = blockIdx.x * kPermBlock;
   const int nt = min(kPermBlock, T - t0);
   const int nslot = nt * k;
@@ -58,12 +62,32 @@ __global__ __launch_bounds__(kPermBlock) void hist_rank_kernel(const int32_t* __
   const int word = tid >> 5;
   const uint32_t bit = 1u << (tid & 31);
   if (tid < nt) {
+    bool dup = false;
     for (int j = 0; j < k; ++j) {
       const int e = s_e[tid * k + j];
-      if (e >= 0) atomicOr(&mask[e][word], bit);
+      // only this thread sets this token's bit, so a bit already set means the
+      // token lists expert e in an earlier slot
+      if (e >= 0) dup |= (atomicOr(&mask[e][word], bit) & bit) != 0u;
     }
+    if (dup) s_dup = 1;
   }
   __syncthreads();
+  if (s_dup != 0) {
+    // A token of this block lists one local expert in several slots (top-k
+    // never does; a caller's own lists may).  One bit per (expert, token)
+    // cannot count those slots, so each expert's thread walks the block's
+    // slots in (token, slot) order instead: the slots of one expert get
+    // consecutive ranks in that order, as the plain definition orders them.
+    for (int e = tid; e < E_l; e += kPermBlock) {
+      int c = 0;
+      for (int i = 0; i < nslot; ++i)
+        if (s_e[i] == e) rank[(size_t)t0 * k + i] = c++;
+      block_counts[(size_t)blockIdx.x * E_l + e] = c;
+    }
+    for (int i = tid; i < nslot; i += kPermBlock)
+      if (s_e[i] < 0) rank[(size_t)t0 * k + i] = -1;
+    return;
+  }
   for (int e = tid; e < E_l; e += kPermBlock) {
     int c = 0;
 #pragma unroll

@@ -290,8 +290,8 @@ def pair_values(x, idx, w_gate, w_up, w_down, e_lo: int, e_hi: int,
 # FP8 variant of the expert FFN (forward)
 # --------------------------------------------------------------------------
 # The pages name FP8 as their only kernel-level speed lever (page
-# "Qwen3-MoE-30B-A3B模型EP+FSDP2并行方案", the closing throughput table) and
-# fix no format or scaling.  Readings used here:
+# "TorchTitan FSDP2 完全指南", section "性能表现", H100 benchmark table, row
+# FSDP + compile + FP8) and fix no format or scaling.  Readings used here:
 #   - format OCP FP8 E4M3 ("fn": no infinities, one NaN code per sign, largest
 #     finite 448, smallest subnormal 2^-9);
 #   - every row (a token of the activations, an output channel of a weight

@@ -136,6 +136,34 @@ def test_ffn_fwd_errors():
     assert f(A, A, 16, 0, 128, 64, A, A, A, BF16, N, N, N, A, big, S) == OK            # nothing routed
 
 
+def test_operand_ranges_below_2gib():
+    """The matrix-core kernels address operands with 32-bit byte ranges: shapes whose
+    grouped-row buffers, expert weights or router input reach 2 GiB are refused on
+    the host (MOE_EUNSUPPORTED) instead of wrapping on the device."""
+    f = lambda *a: L.moe_grouped_ffn_fwd(*a)
+    big = 1 << 40
+    # R_cap * H * 2 = 2^19 * 2048 * 2 = 2^31 bytes: refused; one row fewer is accepted
+    assert f(A, A, 16, 1 << 19, 2048, 768, A, A, A, BF16, N, A, A, A, big, S) == EUNSUP
+    assert "2 GiB" in _err() and "grouped-row" in _err()
+    assert f(A, A, 16, (1 << 19) - 1, 2048, 64, A, A, A, BF16, N, A, A, N, 0, S) == EWS
+    # R_cap * 2I * 2 reaches 2^31 through I
+    assert f(A, A, 16, 1 << 16, 128, 8192, A, A, A, BF16, N, A, A, A, big, S) == EUNSUP
+    # one expert's gate + up weights: 2 * I * H * 2 = 2^31
+    assert f(A, A, 1, 64, 16384, 32768, A, A, A, BF16, N, A, A, A, big, S) == EUNSUP
+    assert "gate and up" in _err()
+    # fp32 layers index with 64-bit offsets: no such limit (the call gets as far as
+    # the NULL w_gate, so nothing is launched)
+    assert f(A, A, 16, 1 << 19, 2048, 768, N, A, A, F32, N, A, A, N, 0, S) == EINVAL and "w_gate" in _err()
+    b = lambda *a: L.moe_grouped_ffn_bwd(*a)
+    assert b(A, A, A, A, A, 16, 1 << 19, 2048, 768, A, A, A, BF16, A, A, A, A, 0, A, big, S) == EUNSUP
+    fp8 = L.moe_grouped_ffn_fwd_fp8
+    assert fp8(A, A, A, A, 16, 1 << 20, 2048, 768, A, A, A, A, A, A, A, A, A, A, big, S) == EUNSUP
+    rb = lambda *a: L.moe_route_bwd(*a)
+    # x^T . dz with T * H * 2 = 2^31 bytes of x: refused only when dw_router is asked for
+    assert rb(A, A, A, A, A, 1 << 19, 2048, 128, 8, BF16, A, N, A, A, big, S) == EUNSUP
+    assert "x spans" in _err()
+
+
 def test_fp8_entry_points_errors():
     q = lambda *a: L.moe_quantize_fp8(*a)
     assert q(A, 64, 2040, BF16, N, A, A, S) == EINVAL and "multiple of 16" in _err()

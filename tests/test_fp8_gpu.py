@@ -82,6 +82,11 @@ FP8_CASES = [
     SKEWED.scaled(name="fp8_skewed_t1024_h256_i256_e32_k4", T=1024, H=256, I=256, E=32, k=4, e_lo=0,
                   e_hi=32),
     EP_SHARE.scaled(name="fp8_t2048_h2048_i768_e16_k4_all_local", T=2048, E=16, k=4, e_lo=0, e_hi=16),
+    # more tiles than persistent workgroups: ~870 gate/up tiles (6 N tiles) and ~430
+    # down tiles, so workgroups run later tiles (next-tile scale loads, prologue
+    # during the epilogue)
+    EP_SHARE.scaled(name="fp8_multitile_t8192_h2048_i768_e16_k4_all_local", T=8192, E=16, k=4,
+                    e_lo=0, e_hi=16),
 ]
 
 
@@ -109,11 +114,17 @@ def test_ffn_fwd_fp8_matches_oracle(w):
         assert np.array_equal(_np(wq[n][1]), ref_w[n][1]), n
     # FP8 permute: rows of codes move bit for bit
     perm = moe.moe_permute(xq, torch.from_numpy(idx.astype(np.int32)).to(DEV), w.E, w.e_lo, w.e_hi)
+    R_cap, nan = w.T * w.k, float("nan")
+    guard = {"h_perm": torch.full((R_cap, w.I), nan, dtype=bf, device=DEV),
+             "y_perm": torch.full((R_cap, w.H), nan, dtype=bf, device=DEV),
+             "gu": torch.full((R_cap, 2 * w.I), nan, dtype=bf, device=DEV)}
     out = moe.moe_grouped_ffn_fwd_fp8(perm["x_perm"], sx, perm["src_row"], perm["offsets"],
-                                      wq["w_gate"], wq["w_up"], wq["w_down"], save_gu=True)
+                                      wq["w_gate"], wq["w_up"], wq["w_down"], save_gu=True, out=guard)
     torch.cuda.synchronize()
     offsets = perm["offsets"].cpu().numpy()
     R = int(offsets[-1])
+    for n in guard:
+        assert torch.isnan(out[n][R:].float()).all(), f"{n}: rows >= R were written"
     src_row = perm["src_row"].cpu().numpy()[:R]
     assert np.array_equal(perm["x_perm"][:R].cpu().numpy(), ref_xq[src_row])
     h_got, y_got = _np(out["h_perm"][:R]), _np(out["y_perm"][:R])
@@ -203,6 +214,9 @@ DGRAD_CASES = [
     SKEWED.scaled(name="dgrad_fp8_skewed_t1024_h256_i256_e32_k4", T=1024, H=256, I=256, E=32, k=4,
                   e_lo=0, e_hi=32),
     EP_SHARE.scaled(name="dgrad_fp8_t2048_h2048_i768_e16_k4_all_local", T=2048, E=16, k=4, e_lo=0, e_hi=16),
+    # ~430 dh tiles and ~1150 dx tiles for 256 persistent workgroups
+    EP_SHARE.scaled(name="dgrad_fp8_multitile_t8192_h2048_i768_e16_k4_all_local", T=8192, E=16, k=4,
+                    e_lo=0, e_hi=16),
 ]
 
 
