@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef enum {
   MOE_OK = 0,
@@ -146,6 +146,22 @@ int moe_grouped_ffn_fwd(const void* x_perm, const int32_t* offsets, int E_l, int
                         int I, const void* w_gate, const void* w_up, const void* w_down, int dtype,
                         void* gu_saved, void* h_perm, void* y_perm, void* ws, size_t ws_bytes,
                         void* stream);
+
+/* moe_grouped_ffn_fwd without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Arguments, results and rounding are those of
+ * moe_grouped_ffn_fwd (the same kernels, so the same bits).  The tile schedule
+ * goes to a static scratch array in the library, 64 KiB per GPU, allocated
+ * when the library is loaded and held until the process ends; it serves
+ * R_cap <= 1048576 (2^20) routed-row capacity for any E_l <= 256, and larger
+ * R_cap returns MOE_EUNSUPPORTED before anything is enqueued.  Every call on
+ * one GPU uses that GPU's single array: calls that overlap on one GPU (two
+ * streams, or two host threads, without an order between the calls) race on
+ * it and must not be issued.  The call itself allocates nothing. */
+int moe_grouped_ffn_fwd_noalloc(const void* x_perm, const int32_t* offsets, int E_l, int R_cap,
+                                int H, int I, const void* w_gate, const void* w_up,
+                                const void* w_down, int dtype, void* gu_saved, void* h_perm,
+                                void* y_perm, void* stream);
 
 /* FP8 recipe of the expert FFN.  The pages name FP8 as their only
  * kernel-level speed lever (page "TorchTitan FSDP2 完全指南", section

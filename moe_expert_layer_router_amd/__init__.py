@@ -28,7 +28,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_F32, MOE_BF16, MOE_FP8 = 0, 1, 2
 (MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD, MOE_OP_ROUTE_BWD,
  MOE_OP_COMBINE_DX, MOE_OP_FFN_FWD_FP8, MOE_OP_FFN_DGRAD_FP8) = range(8)
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 class MoEError(RuntimeError):
@@ -49,6 +49,7 @@ def _load():
         "moe_route_from_logits": ([P, I32, I32, I32, P, P, P], I32),
         "moe_permute": ([P, P, I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, SZ, P], I32),
         "moe_grouped_ffn_fwd": ([P, P, I32, I32, I32, I32, P, P, P, I32, P, P, P, P, SZ, P], I32),
+        "moe_grouped_ffn_fwd_noalloc": ([P, P, I32, I32, I32, I32, P, P, P, I32, P, P, P, P], I32),
         "moe_combine": ([P, P, P, P, I32, I32, I32, I32, P, P], I32),
         "moe_combine_bwd": ([P, P, P, P, I32, I32, I32, I32, P, P, P], I32),
         "moe_combine_dx": ([P, P, P, P, P, P, I32, I32, I32, I32, I32, P, P, SZ, P], I32),

@@ -320,6 +320,43 @@ int moe_grouped_ffn_fwd(const void* x_perm, const int32_t* offsets, int E_l, int
   return hip_status(e, fn);
 }
 
+int moe_grouped_ffn_fwd_noalloc(const void* x_perm, const int32_t* offsets, int E_l, int R_cap,
+                                int H, int I, const void* w_gate, const void* w_up,
+                                const void* w_down, int dtype, void* gu_saved, void* h_perm,
+                                void* y_perm, void* stream) {
+  const char* fn = "moe_grouped_ffn_fwd_noalloc";
+  if (int rc = check_dtype(dtype, fn)) return rc;
+  if (int rc = check_ffn_shape(E_l, R_cap, H, I, dtype, fn)) return rc;
+  if (R_cap > kNoAllocMaxRows)
+    return fail(MOE_EUNSUPPORTED, "%s: R_cap=%d exceeds the %d rows the library's static scratch "
+                "holds a tile table for; use moe_grouped_ffn_fwd with a workspace", fn, R_cap,
+                kNoAllocMaxRows);
+  if (int rc = check_ptr(offsets, "offsets", fn)) return rc;
+  if (int rc = check_ptr(w_gate, "w_gate", fn, true)) return rc;
+  if (int rc = check_ptr(w_up, "w_up", fn, true)) return rc;
+  if (int rc = check_ptr(w_down, "w_down", fn, true)) return rc;
+  if (R_cap > 0) {
+    if (int rc = check_ptr(x_perm, "x_perm", fn, true)) return rc;
+    if (int rc = check_ptr(h_perm, "h_perm", fn, true)) return rc;
+    if (int rc = check_ptr(y_perm, "y_perm", fn, true)) return rc;
+  }
+  if (gu_saved != nullptr && !aligned16(gu_saved))
+    return fail(MOE_EINVAL, "%s: gu_saved must be 16-byte aligned", fn);
+  if (R_cap == 0) return MOE_OK;
+  hipStream_t s = begin_launch(stream);
+  hipError_t e;
+  if (dtype == MOE_BF16)
+    e = launch_ffn_fwd_bf16_noalloc((const bf16_t*)x_perm, offsets, E_l, R_cap, H, I,
+                                    (const bf16_t*)w_gate, (const bf16_t*)w_up,
+                                    (const bf16_t*)w_down, (bf16_t*)gu_saved, (bf16_t*)h_perm,
+                                    (bf16_t*)y_perm, s);
+  else  // the fp32 kernels use no scratch
+    e = launch_ffn_fwd_f32((const float*)x_perm, offsets, E_l, R_cap, H, I, (const float*)w_gate,
+                           (const float*)w_up, (const float*)w_down, (float*)gu_saved,
+                           (float*)h_perm, (float*)y_perm, s);
+  return hip_status(e, fn);
+}
+
 int moe_quantize_fp8(const void* src, int rows, int cols, int dtype, const int32_t* nrows,
                      uint8_t* q, float* scale, void* stream) {
   const char* fn = "moe_quantize_fp8";

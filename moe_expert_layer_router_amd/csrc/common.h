@@ -194,6 +194,13 @@ hipError_t launch_ffn_fwd_bf16(const bf16_t* x_perm, const int32_t* offsets, int
                                int H, int I, const bf16_t* w_gate, const bf16_t* w_up,
                                const bf16_t* w_down, bf16_t* gu, bf16_t* h_perm, bf16_t* y_perm,
                                void* ws, hipStream_t s);
+// The same with the tile table in the library's static per-GPU scratch (no
+// workspace argument); R_cap <= kNoAllocMaxRows.
+constexpr int kNoAllocMaxRows = 1 << 20;
+hipError_t launch_ffn_fwd_bf16_noalloc(const bf16_t* x_perm, const int32_t* offsets, int E_l,
+                                       int R_cap, int H, int I, const bf16_t* w_gate,
+                                       const bf16_t* w_up, const bf16_t* w_down, bf16_t* gu,
+                                       bf16_t* h_perm, bf16_t* y_perm, hipStream_t s);
 // FP8 forward (gemm.hip) and E4M3 row quantization (fp8.hip)
 size_t ffn_fwd_fp8_ws_bytes(int R_cap, int E_l, int I);
 hipError_t launch_ffn_fwd_fp8(const uint8_t* x_q, const float* x_scale, const int32_t* src_row,

@@ -57,10 +57,12 @@
 #include "common.h"
 
 #include <algorithm>
+#include <mutex>
 
 namespace moe {
 
 constexpr int BN = 256, BK = 32, NTH = 256;
+constexpr int kMaxDevices = 64;  // per-device objects the launchers keep
 constexpr int kTileCtrs = 4;             // dynamic tile counters in the FFN workspace
 constexpr int WN = 128;                  // wave sub-tile width
 constexpr int NI = WN / 32;              // MFMA blocks per wave along N
@@ -1221,7 +1223,7 @@ __global__ __launch_bounds__(kMaxE) void ffn_sched_kernel(const int32_t* __restr
   }
 }
 
-static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+static constexpr size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 int gemm_tiles(int M, int N) { return ((M + kBmWgrad - 1) / kBmWgrad) * ((N + BN - 1) / BN); }
 
@@ -1289,6 +1291,52 @@ hipError_t launch_ffn_fwd_bf16(const bf16_t* x_perm, const int32_t* offsets, int
   d.c0 = y_perm;
   d.ldc = H;
   return launch_gemm<K_DOWN_FWD, kBmGrouped>(d, mt_upper * d.n_ntiles, MOE_KERNEL_FFN_DOWN, s);
+}
+
+// ---------------------------------------------------------------------------
+// The forward without a workspace (moe_grouped_ffn_fwd_noalloc): its only
+// scratch, the tile table, lives in a static device array of fixed size, one
+// copy per GPU, held until the process ends.  On the host the array's name is
+// not a device address: the launcher uses only the address hipGetSymbolAddress
+// returns, looked up once per device with that device current.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = 64 * 1024;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+static_assert(align256((1 + 3 * ((size_t)kNoAllocMaxRows / kBmGrouped + kMaxE + 1)) * sizeof(int32_t)) <=
+                  kNoAllocScratchBytes,
+              "the tile table of the largest no-workspace forward fits the static scratch");
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static hipError_t noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_ffn_fwd_bf16_noalloc(const bf16_t* x_perm, const int32_t* offsets, int E_l,
+                                       int R_cap, int H, int I, const bf16_t* w_gate,
+                                       const bf16_t* w_up, const bf16_t* w_down, bf16_t* gu,
+                                       bf16_t* h_perm, bf16_t* y_perm, hipStream_t s) {
+  if (R_cap > kNoAllocMaxRows) return hipErrorInvalidValue;  // the ABI refuses these first
+  void* table = nullptr;
+  hipError_t e = noalloc_scratch(&table);
+  if (e != hipSuccess) return e;
+  // the tile-table kernel writes every entry the products read (count first),
+  // so nothing in the array needs clearing
+  return launch_ffn_fwd_bf16(x_perm, offsets, E_l, R_cap, H, I, w_gate, w_up, w_down, gu, h_perm,
+                             y_perm, table, s);
 }
 
 // Row scales of the permuted activations: sxp[r] = sx[src_row[r]] for the
@@ -1458,8 +1506,6 @@ struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, mid = nullptr, join = nullptr;
 };
-
-constexpr int kMaxDevices = 64;
 
 static SideStream* side_stream() {
   thread_local SideStream per_dev[kMaxDevices];
