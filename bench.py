@@ -30,6 +30,10 @@ PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (vector/matrix)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
+METRIC = "MoE layer fwd+bwd TFLOP/s and tokens/s, 128e/H2048/I768 top-8 bf16"
+# the 128-expert full layer whose forward the secondary measurement times
+SECONDARY_WORKLOAD = "full_t16384_h2048_i768_e128_k8"
+
 KERNELS = ["ROUTE", "PERMUTE_HIST", "PERMUTE_SCAN", "PERMUTE_SCATTER", "FFN_GATEUP", "FFN_DOWN",
            "COMBINE", "COMBINE_BWD", "ROUTE_BWD_DZ", "ROUTE_BWD_DW", "FFN_DOWN_DGRAD",
            "FFN_DOWN_WGRAD", "FFN_GATEUP_DGRAD", "FFN_GATEUP_WGRAD", "COMBINE_DX"]
@@ -128,14 +132,25 @@ def roofline_of(name, w, R, avg_us, launches, A=None):
 
 def cpu_baseline(w, inp, target_s=12.0):
     """The CPU oracle as it stands, on the first Ts tokens of the same workload."""
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
     import numpy as np
 
     import oracle as O
+    avail = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = avail
+    cores = min(avail, blas)
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
 
     def run(Ts):
         x = inp["x"][:Ts]
@@ -164,6 +179,7 @@ def cpu_baseline(w, inp, target_s=12.0):
     sub = w.scaled(T=Ts)
     fl = step_flops(sub, R)
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "cores_available": avail, "blas_threads": int(blas), "cpu_model": model,
             "kind": "oracle", "tokens_per_s": round(Ts / dt, 1), "seconds": round(dt * reps, 2),
             "sample": f"first {Ts} of {w.T} tokens of {w.name}, float64 NumPy "
                       f"{'forward+backward' if w.train else 'forward'}, mean of {reps} run(s)"}
@@ -363,6 +379,79 @@ def step_stats(run, n, dev):
     return out
 
 
+def live_kernel_times(moe, torch, step, n):
+    """Live per-kernel durations: events the library records around each launch
+    of one kernel, on the stream it is launched on, over n eager steps."""
+    kt = {}
+    for kid, name in enumerate(KERNELS):
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(4 * n)]
+        stops = [torch.cuda.Event(enable_timing=True) for _ in range(4 * n)]
+        # torch creates the HIP event on first record; the library records it again
+        for e in starts + stops:
+            e.record()
+        torch.cuda.synchronize()
+        arr_s = (ctypes.c_void_p * (4 * n))(*[ctypes.c_void_p(e.cuda_event) for e in starts])
+        arr_e = (ctypes.c_void_p * (4 * n))(*[ctypes.c_void_p(e.cuda_event) for e in stops])
+        moe.lib.moe_profile_kernel(kid, arr_s, arr_e, 4 * n)
+        for _ in range(n):
+            step()
+        torch.cuda.synchronize()
+        cnt = moe.lib.moe_profile_recorded()
+        moe.lib.moe_profile_kernel(-1, None, None, 0)
+        if cnt == 0:
+            continue
+        times = [starts[i].elapsed_time(stops[i]) * 1e3 for i in range(cnt)]
+        kt[name] = {"avg_us": sum(times) / cnt, "launches_per_step": cnt // n,
+                    "us_per_step": sum(times) / n}
+    return kt
+
+
+def secondary_forward(w, args, moe, torch):
+    """The forward of the full 128-expert layer (every expert local, T = 16384):
+    graph-replayed layer time and each forward kernel's live time against its
+    roofline (router, permute and combine against HBM, the grouped products
+    against bf16 MFMA).  "PERMUTE" is the permute's three launches together,
+    priced at the scatter's algorithmic bytes."""
+    from workloads import make_inputs
+    dev = torch.device("cuda:0")
+    inp = make_inputs(w)
+    t = {n: torch.from_numpy(v).to(dev).to(torch.bfloat16).contiguous() for n, v in inp.items()
+         if n != "bias"}
+    layer = moe.MoELayer(w.T, w.H, w.I, w.E, w.k, w.e_lo, w.e_hi, torch.bfloat16, dev, train=False)
+    step = lambda: layer.forward(t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"])
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    R = int(layer.buf["offsets"][-1].item())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    kt = live_kernel_times(moe, torch, step, args.steps)
+    roof = {}
+    for k, v in kt.items():
+        r = roofline_of(k, w, R, v["avg_us"], v["launches_per_step"])
+        roof[k] = {kk: r[kk] for kk in ("bound", "achieved", "unit", "frac", "avg_us")}
+    perm = [k for k in ("PERMUTE_HIST", "PERMUTE_SCAN", "PERMUTE_SCATTER") if k in kt]
+    if perm:
+        us = sum(kt[k]["avg_us"] for k in perm)
+        nb = kernel_work("PERMUTE_SCATTER", w, R, 1)[1]
+        roof["PERMUTE"] = {"bound": "hbm", "achieved": round(nb / (us * 1e-6) / 1e9, 1), "unit": "GB/s",
+                           "frac": round(nb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "avg_us": round(us, 2)}
+    flops = step_flops(w, R)
+    return {"workload": w.name, "pass": "forward", "timing": "hip-graph replay", "steps": args.steps,
+            "ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "tokens_per_s": round(w.T / (ms * 1e-3), 1), "routed_rows": R, "roofline": roof}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -372,6 +461,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-times", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the forward of the full 128-expert layer timed after the main step")
     ap.add_argument("--no-step-stats", action="store_true",
                     help="skip the per-step warm / cold (cache-flushed) timing pass")
     ap.add_argument("--fp8-ffn", action="store_true",
@@ -452,7 +543,7 @@ def main():
 
     flops = step_flops(w, R)
     result = {
-        "metric": "MoE layer fwd+bwd TFLOP/s and tokens/s, 128e/H2048/I768 top-8 bf16",
+        "metric": METRIC if w.train else METRIC.replace("fwd+bwd", "fwd"),
         "value": round(flops / (ms * 1e-3) / 1e12, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -474,31 +565,7 @@ def main():
         result["step_ms"] = step_stats(run, args.steps, dev)
 
     if not args.no_kernel_times:
-        # Live per-kernel durations: events recorded by the library around each
-        # launch of one kernel, on the stream it is launched on (eager steps).
-        kt = {}
-        n = args.steps
-        for kid, name in enumerate(KERNELS):
-            starts = [torch.cuda.Event(enable_timing=True) for _ in range(4 * n)]
-            stops = [torch.cuda.Event(enable_timing=True) for _ in range(4 * n)]
-            # torch creates the HIP event on first record; the library records it again
-            for e in starts + stops:
-                e.record()
-            torch.cuda.synchronize()
-            arr_s = (ctypes.c_void_p * (4 * n))(*[ctypes.c_void_p(e.cuda_event) for e in starts])
-            arr_e = (ctypes.c_void_p * (4 * n))(*[ctypes.c_void_p(e.cuda_event) for e in stops])
-            moe.lib.moe_profile_kernel(kid, arr_s, arr_e, 4 * n)
-            for _ in range(n):
-                step()
-            torch.cuda.synchronize()
-            cnt = moe.lib.moe_profile_recorded()
-            moe.lib.moe_profile_kernel(-1, None, None, 0)
-            if cnt == 0:
-                continue
-            times = [starts[i].elapsed_time(stops[i]) * 1e3 for i in range(cnt)]
-            per_step = cnt // n
-            kt[name] = {"avg_us": sum(times) / cnt, "launches_per_step": per_step,
-                        "us_per_step": sum(times) / n}
+        kt = live_kernel_times(moe, torch, step, args.steps)
         result["kernels_us_per_step"] = {k: round(v["us_per_step"], 2) for k, v in kt.items()}
         dom = max(kt, key=lambda k: kt[k]["us_per_step"])
         result["roofline"] = roofline_of(dom, w, R, kt[dom]["avg_us"], kt[dom]["launches_per_step"], A)
@@ -506,6 +573,11 @@ def main():
                                       roofline_of(k, w, R, v["avg_us"], v["launches_per_step"], A).items()
                                       if kk in ("bound", "achieved", "unit", "frac", "avg_us")}
                                   for k, v in kt.items()}
+
+    if not args.no_secondary and w.name != SECONDARY_WORKLOAD:
+        del layer, graph
+        torch.cuda.empty_cache()
+        result["secondary"] = secondary_forward(WORKLOADS[SECONDARY_WORKLOAD], args, moe, torch)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp)

@@ -88,7 +88,9 @@ struct Cfg {
   // The epilogue stages 16 x 128 fp32 (8 KB) per wave.  256-row tiles keep
   // that area after the ring, so the next tile's first K steps are loaded
   // during the epilogue; 128-row tiles (two workgroups per CU) stage in the
-  // ring and start the next tile's loads after it.
+  // ring and start the next tile's loads after it.  (A fifth ring slot with
+  // the staging area laid over it, four K steps in flight instead of three,
+  // measured no faster on the training step or the 128-expert forward.)
   static constexpr bool kSepStage = BM == 256;
   static constexpr int kStageBytes = 4 * 8192;
   static constexpr int kStageOff = kSepStage ? kRingBytes : 0;
@@ -634,6 +636,48 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
         }
       return;
     }
+    if (p.accumulate == 0) {  // uniform
+      // Overwrite: unconditional buffer stores whose descriptor covers the
+      // output rows of this 16-row pass (rows past M dropped by the range
+      // check, columns past N by the kill offset), so their number is static
+      // (epilogue_vmem_ops) and the next tile's K loop waits for its own DMA,
+      // not for these stores.  Each store instruction writes 256 contiguous
+      // bytes of a row (lane l: columns 4 (l % 16) .. + 3 and 64 more), and the
+      // non-temporal policy keeps the fp32 result out of L2 (read only by the
+      // optimizer).
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          stage_half(st, acc, mi, h, lane);
+          // first output row of the pass; a pass never straddles m_split
+          // (a multiple of 64 rows)
+          const int mb = m0 + wm * WM + mi * 32 + 16 * h;
+          const bool first = mb < p.m_split || p.f1 == nullptr;
+          float* base = (first ? p.f0 : p.f1) + e * p.f_group_stride;
+          const int mrel = first ? mb : mb - p.m_split;
+          const int nrows = (first ? min(p.m_split, p.M) : p.M - p.m_split) - mrel;
+          const out_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+              base + (long)max(mrel, 0) * p.ldc, 0, nrows > 0 ? (int)(nrows * p.ldc * 4) : 0, 0x00020000);
+#pragma unroll
+          for (int it = 0; it < 4; ++it) {
+            const int r = it * 4 + (lane >> 4);
+            const int c = (lane & 15) * 4;
+            const int n = n0 + wn * WN + c;
+            const f32x4_t a = *reinterpret_cast<const f32x4_t*>(&st[stage_idx(r, c)]);
+            const f32x4_t b = *reinterpret_cast<const f32x4_t*>(&st[stage_idx(r, c + 64)]);
+            const uint32_t oa = n < p.N ? (uint32_t)((r * p.ldc + n) * 4) : kOutKill;
+            const uint32_t ob = n + 64 < p.N ? (uint32_t)((r * p.ldc + n + 64) * 4) : kOutKill;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, a), ro, oa, 0, kCpolNT);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, b), ro, ob, 0, kCpolNT);
+          }
+          // the next half reuses the staging area
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+      return;
+    }
+    // Accumulate: read, add, write back (memory operations depend on the
+    // data; the next tile's K loop then waits for them all).
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -651,17 +695,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
           float* dst = (m < p.m_split) ? p.f0 + e * p.f_group_stride + (long)m * p.ldc + n
                                        : p.f1 + e * p.f_group_stride + (long)(m - p.m_split) * p.ldc + n;
           float4* d4 = reinterpret_cast<float4*>(dst);
-          if (p.accumulate) {
-            const float4 o0 = d4[0], o1 = d4[1];
-            d4[0] = make_float4(o0.x + v[0], o0.y + v[1], o0.z + v[2], o0.w + v[3]);
-            d4[1] = make_float4(o1.x + v[4], o1.y + v[5], o1.z + v[6], o1.w + v[7]);
-          } else {
-            // written once per step and read only by the optimizer: streaming
-            // stores, which leave L2 to the operands of the products beside
-            f32x4_t* q4 = reinterpret_cast<f32x4_t*>(dst);
-            __builtin_nontemporal_store(f32x4_t{v[0], v[1], v[2], v[3]}, q4);
-            __builtin_nontemporal_store(f32x4_t{v[4], v[5], v[6], v[7]}, q4 + 1);
-          }
+          const float4 o0 = d4[0], o1 = d4[1];
+          d4[0] = make_float4(o0.x + v[0], o0.y + v[1], o0.z + v[2], o0.w + v[3]);
+          d4[1] = make_float4(o1.x + v[4], o1.y + v[5], o1.z + v[6], o1.w + v[7]);
         }
         // the next half reuses the staging area
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -875,11 +911,12 @@ __device__ __forceinline__ void k_steps_f8(f32x16_t (&acc)[C::MI][NI], Frags8<C>
   }
 }
 
-// Vector memory instructions each lane issues in the epilogue of an M-grouped
-// product (the buffer stores and loads there are unconditional: the range
-// checks drop the ones outside the tile), or -1 where the count depends on the
-// data (WGRAD).  A K loop that starts after the previous tile's epilogue (its
-// first DMAs issued before that epilogue) waits past exactly these.
+// Vector memory instructions each lane issues in the epilogue of a product
+// (the buffer stores and loads there are unconditional: the range checks drop
+// the ones outside the tile; WGRAD: its overwriting epilogue, the accumulating
+// and folding ones depend on the data and take the plain wait).  A K loop that
+// starts after the previous tile's epilogue (its first DMAs issued before that
+// epilogue) waits past exactly these.
 template <int KIND, class C, bool F8 = false>
 __host__ __device__ constexpr int epilogue_vmem_ops() {
   // FP8: the next tile's scale loads follow the epilogue (rows, then columns
@@ -887,7 +924,7 @@ __host__ __device__ constexpr int epilogue_vmem_ops() {
   return (F8 ? Scales<KIND, C>::NR + Scales<KIND, C>::NC / 4 : 0) +
          (KIND == K_GATEUP_FWD   ? 12 * C::MI   // 3 stores x 2 rows x 2 halves per block row
           : KIND == K_DOWN_DGRAD ? 32 * C::MI   // 2 loads + 2 stores x 4 rows x 2 halves
-          : KIND == K_WGRAD      ? -1
+          : KIND == K_WGRAD      ? 16 * C::MI   // overwrite: 2 stores x 4 rows x 2 halves
                                  : 8 * C::MI);  // 1 store x 4 rows x 2 halves
 }
 
@@ -1102,7 +1139,7 @@ void gemm_kernel(const GemmArgs p) {
       constexpr int kFirst = (NST - 2) * ND + ND / 2;
       constexpr int kEpi = epilogue_vmem_ops<KIND, C, F8>();
       constexpr int kAfter = kEpi < 0 ? kFirst : (kFirst + kEpi > 63 ? 63 : kFirst + kEpi);
-      if (C::kSepStage && after_epi)
+      if (C::kSepStage && after_epi && (KIND != K_WGRAD || (p.accumulate == 0 && p.fold == 0)))
         wait_vm<kAfter>();
       else
         wait_vm<kFirst>();
