@@ -755,13 +755,19 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
     out_rsrc_t rg;
     u32x4_t graw[2][4], uraw[2][4];
     if constexpr (KIND == K_DOWN_DGRAD) rg = out_rsrc(p.gu, row0, row1, 2L * p.I);
+    // Columns past N take the kill bit OR'd into distinct offsets: with a
+    // select between an offset and one shared kill offset, the compiler merged
+    // the g and u loads of the killed lanes and branched around them, and the
+    // branch's join waited for every outstanding memory operation (vmcnt(0)),
+    // the next tile's prefetched DMA included.
+    const uint32_t gu_kill = (uint32_t)(!col_ok) << 31;
     auto load_gu = [&](int pq, int b) {
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const int lrow = wm * WM + (pq >> 1) * 32 + 16 * (pq & 1) + it * 4 + (lane >> 4);
-        const uint32_t o = col_ok ? (uint32_t)((lrow * 2 * p.I + n) * 2) : kOutKill;
-        graw[b][it] = __builtin_amdgcn_raw_buffer_load_b128(rg, o, 0, 0);
-        uraw[b][it] = __builtin_amdgcn_raw_buffer_load_b128(rg, o + (col_ok ? p.I * 2 : 0), 0, 0);
+        const uint32_t o = (uint32_t)((lrow * 2 * p.I + n) * 2);
+        graw[b][it] = __builtin_amdgcn_raw_buffer_load_b128(rg, o | gu_kill, 0, 0);
+        uraw[b][it] = __builtin_amdgcn_raw_buffer_load_b128(rg, (o + p.I * 2) | gu_kill, 0, 0);
       }
     };
     if constexpr (KIND == K_DOWN_DGRAD) load_gu(0, 0);
