@@ -18,6 +18,10 @@ FLAGS = [
     # packed fp32 VALU ops are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-variable", "-Wno-pass-failed",
+    # atomics stay as written: the wave-level atomic optimizer rewrites a
+    # single lane's tile-ticket atomicAdd into a form that needs the result at
+    # once, which exposes the atomic's latency at every tile change
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
 ]
 
 

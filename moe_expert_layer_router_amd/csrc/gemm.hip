@@ -1184,7 +1184,10 @@ void gemm_kernel(const GemmArgs p) {
       // hand thread 0's ticket to the workgroup through the first word of
       // the ring (idle here: this tile's K loop is done, the next tile's DMA
       // is not issued yet), and draw the next ticket
-      volatile int* slot0 = reinterpret_cast<volatile int*>(g_lds);
+      // an LDS-address-space pointer: a generic one made this a flat store,
+      // which the compiler follows with a wait for all memory operations
+      typedef __attribute__((address_space(3))) volatile int lds_int_t;
+      lds_int_t* slot0 = reinterpret_cast<lds_int_t*>(lds_ptr(0));
       if (tid == 0) {
         slot0[0] = (int)gridDim.x + ticket;
         ticket = atomicAdd(p.tile_ctr, 1);

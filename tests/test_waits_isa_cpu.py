@@ -22,6 +22,7 @@ the kernels document, and require every wait to be correct and tight:
   stages (one per four steps), with the prologue and refill order of the
   kernel; every wait before a step's fragment reads must cover both stages.
 """
+import importlib.util
 import os
 import re
 import subprocess
@@ -35,10 +36,18 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 VMCNT_MAX = 63
 
 
+def _build_flags():
+    """The library's own compile flags (moe_expert_layer_router_amd/build.py), minus linking."""
+    spec = importlib.util.spec_from_file_location(
+        "_moe_build", os.path.join(ROOT, "moe_expert_layer_router_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return [f for f in mod.FLAGS if f not in ("-shared", "-fPIC")]
+
+
 def _asm(src):
     out = os.path.join(tempfile.mkdtemp(prefix="moe_isa_"), os.path.basename(src) + ".s")
-    cmd = [HIPCC, "-O3", "--offload-arch=gfx950", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "--cuda-device-only", "-S", src, "-o", out]
+    cmd = [HIPCC, *_build_flags(), "--cuda-device-only", "-S", src, "-o", out]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
     return open(out).read().split("\n")
@@ -230,6 +239,23 @@ def test_gemm_ring_waits_are_correct_and_tight(gemm_asm, kind, bm, fp8):
         f.issue("epilogue", k_epi)
         prologue(f, 1)
         k_loop_steps(f, 1, 24, k_first)
+
+
+@pytest.mark.parametrize("kind,bm", [(2, 256), (3, 256), (4, 256), (4, 128)])
+def test_tile_ticket_latency_stays_hidden(gemm_asm, kind, bm):
+    """The products that take tiles from a device counter draw the ticket of the
+    tile after next with one lane's atomic add and hand the previous ticket to
+    the workgroup through LDS.  No wait for all memory operations may follow the
+    atomic directly (its result is used one tile later), and the hand-off goes
+    through LDS, not a flat store."""
+    body = [l.strip() for l in _gemm_body(gemm_asm, kind, bm, False)]
+    code = [l for l in body if l and not l.startswith(";") and not l.startswith(".")]
+    at = [i for i, l in enumerate(code) if l.startswith("global_atomic_add")]
+    assert at, "no ticket atomic"
+    for i in at:
+        nxt = code[i + 1:i + 6]
+        assert not any(l.startswith("s_waitcnt") and "vmcnt(0)" in l for l in nxt), nxt
+    assert not any(l.startswith("flat_store") for l in code)
 
 
 @pytest.mark.parametrize("nb", [1, 2, 4])
