@@ -55,13 +55,14 @@
 // epilogue multiplies each accumulator by its row scale times its column
 // scale (both powers of two: exact) before the SwiGLU.
 #include "common.h"
+#include "lds_layout.h"
 
 #include <algorithm>
 #include <mutex>
 
 namespace moe {
 
-constexpr int BN = 256, BK = 32, NTH = 256;
+constexpr int BN = 256, NTH = 256;  // BK, KCH: lds_layout.h
 constexpr int kMaxDevices = 64;  // per-device objects the launchers keep
 constexpr int kTileCtrs = 4;             // dynamic tile counters in the FFN workspace
 constexpr int WN = 128;                  // wave sub-tile width
@@ -69,7 +70,6 @@ constexpr int NI = WN / 32;              // MFMA blocks per wave along N
 constexpr int KSUB = BK / 16;            // k16 sub-steps per K step
 constexpr int kStageB = BN * BK;         // bf16 elements per B stage
 constexpr int NIB = kStageB * 2 / 1024 / 4;  // DMA instructions (1 KB each) per wave per stage, B
-constexpr int KCH = BK / 8;              // 16-byte chunks per KC row
 constexpr int kSlotB = kStageB * 2;      // bytes
 
 // Block-height dependent parameters.
@@ -152,19 +152,8 @@ template <int KIND> struct Traits {
   static constexpr bool B_KC = KIND == K_GATEUP_FWD || KIND == K_DOWN_FWD;
 };
 
-// ---------------------------------------------------------------------------
-// LDS layouts
-// ---------------------------------------------------------------------------
-// KC tile [rows][32]: rows are 64 bytes, four per 256-byte line of the 64
-// LDS banks.  The 16 lanes of one ds_read_b128 phase read the same logical
-// chunk of 16 consecutive rows; XOR with (r / 4) % 4 puts them on 16 distinct
-// 16-byte bank groups (measured on gfx950: the XOR with (r / 2) % 4 that
-// suits 32 banks loses about 28% of the LDS read rate to conflicts).
-__device__ __forceinline__ int kc_swz(int r) { return (r >> 2) & 3; }
-// first element of logical 16-byte chunk `chunk` of row r
-__device__ __forceinline__ int kc_idx(int r, int chunk) { return r * BK + ((chunk ^ kc_swz(r)) << 3); }
-// MC tile [BK][W]: LDS position of logical 16-byte chunk c of row k (and back).
-__device__ __forceinline__ int mc_chunk(int k, int c) { return c ^ ((k & 3) << 2); }
+// LDS layouts of the tiles (swizzles, DMA placement, fragment offsets):
+// lds_layout.h.
 
 // ---------------------------------------------------------------------------
 // DMA operands (the buffer -> LDS helpers are in common.h)
@@ -178,25 +167,6 @@ struct Operand {
   uint32_t voff[NI];
   uint32_t kstep;    // byte step per unit of k (KC: 2, MC: row pitch in bytes)
 };
-
-// KC operand: DMA instruction u of wave w covers 16-byte LDS chunks
-// p = (w*N + u)*64 + lane, i.e. tile row p/KCH, LDS chunk p%KCH, which holds
-// the logical k chunk (p%KCH) ^ swz(row).
-template <int N>
-__device__ __forceinline__ void kc_rows(int wave, int lane, int u, int& row, int& chunk) {
-  const int p = (wave * N + u) * 64 + lane;
-  row = p / KCH;
-  chunk = (p % KCH) ^ kc_swz(row);
-}
-
-// MC operand of width W: chunk p -> k row p / (W/8), LDS chunk p % (W/8),
-// holding logical chunk mc_chunk(row, p % (W/8)).
-template <int N, int W>
-__device__ __forceinline__ void mc_rows(int wave, int lane, int u, int& row, int& chunk) {
-  const int p = (wave * N + u) * 64 + lane;
-  row = p / (W / 8);
-  chunk = mc_chunk(row, p % (W / 8));
-}
 
 // ---------------------------------------------------------------------------
 // MFMA fragments from LDS
@@ -276,25 +246,15 @@ struct FragLanes {
 
 template <int W, int N>
 __device__ __forceinline__ void mc_lane_offsets(int lane, int mb, uint32_t (&mc)[N], int n) {
-  const int g = lane >> 4, i = lane & 15;
-  const int x = 2 * (g & 1) + ((i & 3) >> 1);
-  const int r = (i >> 2) & 3;
-  const int rowpart = (8 * (g >> 1) + (i >> 2)) * W + 4 * (i & 1);
 #pragma unroll
-  for (int j = 0; j < N; ++j) {
-    const int M = mb + j;
-    const int c = 4 * ((M & ~3) | ((M & 3) ^ r)) + x;
-    mc[j] = j < n ? (uint32_t)(2 * (rowpart + 8 * c)) : 0u;
-  }
+  for (int j = 0; j < N; ++j) mc[j] = j < n ? mc_lane_offset<W>(lane, mb + j) : 0u;
 }
 
 template <class C>
 __device__ __forceinline__ FragLanes frag_lanes(int lane, int wave) {
   FragLanes L;
-  const int r = lane & 31;
 #pragma unroll
-  for (int s = 0; s < KSUB; ++s)
-    L.kc[s] = (uint32_t)(r * BK * 2 + (((2 * s + (lane >> 5)) ^ kc_swz(r)) << 4));
+  for (int s = 0; s < KSUB; ++s) L.kc[s] = kc_lane_offset(lane, s);
   mc_lane_offsets<C::BM>(lane, (wave >> 1) * (C::WM / 32), L.mc_a, C::MI);
   mc_lane_offsets<BN>(lane, (wave & 1) * (WN / 32), L.mc_b, NI);
   return L;
@@ -471,8 +431,6 @@ template <class C>
 __device__ __forceinline__ float* stage_area(int wave) {
   return reinterpret_cast<float*>(reinterpret_cast<char*>(g_lds) + C::kStageOff) + wave * 2048;
 }
-// fp32 element (row r < 16, col c < 128) of a wave's staging area
-__device__ __forceinline__ int stage_idx(int r, int c) { return r * 128 + (c ^ (((r >> 2) & 1) << 5)); }
 
 template <int MI>
 __device__ __forceinline__ void stage_half(float* st, const f32x16_t (&acc)[MI][NI], int mi, int h,
