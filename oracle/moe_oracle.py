@@ -471,6 +471,56 @@ def expert_dgrad_fp8_parts(dyq, sdy, g, u, wdtq, sdt, wgutq, sgut) -> Dict[str, 
 
 
 # --------------------------------------------------------------------------
+# FP8 variant of the expert weight gradients
+# --------------------------------------------------------------------------
+# Readings, on top of the data gradients': a weight gradient sums over one
+# expert's rows (dW_down[e] = sum_r dy[r]^T h[r], dW_gate[e] = sum_r dg[r]^T
+# x[r], dW_up[e] likewise with du), so a scale that is to multiply the whole
+# sum must stay the same along those rows.  Each operand is therefore
+# quantized per (expert, column): the column restricted to the expert's rows
+# gets the row rule above (its transpose is a row).  The operands are the
+# values the bf16 layer holds: the grouped token rows x, the bf16 [dg | du]
+# of the FP8 data gradients, the bf16 h of the forward and the bf16 rows of
+# dy_perm.  The codes' exact products are summed and the two scales multiply
+# the sum; the result is an fp32 tensor like the bf16 weight gradients.
+
+def quantize_group_cols_fp8(a, offsets):
+    """Per-(group, column) codes of the grouped rows a [R, C], group e being
+    rows offsets[e] .. offsets[e + 1] - 1: for every group, quantize_rows_fp8
+    of the transpose of its rows.  Returns a list of code matrices [C, n_e]
+    (one per group) and the scales [E_l, C]."""
+    a = _f64(a)
+    off = np.asarray(offsets, dtype=np.int64)
+    codes, scales = [], []
+    for e in range(len(off) - 1):
+        q, s = quantize_rows_fp8(a[off[e]:off[e + 1]].T)
+        codes.append(q)
+        scales.append(s)
+    return codes, (np.stack(scales) if scales else np.zeros((0, a.shape[1])))
+
+
+def moe_wgrad_fp8(x_perm, dgu, h_perm, dy_perm, offsets) -> Dict[str, np.ndarray]:
+    """FP8 weight gradients of the local experts from their grouped rows:
+    dW_gate[e], dW_up[e] [I, H] = the row-scaled product of the columns of
+    [dg | du] with the columns of x (first I rows of the [2I, H] result for
+    the gate, the rest for up); dW_down[e] [H, I] = that of the columns of dy
+    with the columns of h.  An expert without rows gets zeros."""
+    I = _f64(dgu).shape[1] // 2
+    xq, sx = quantize_group_cols_fp8(x_perm, offsets)
+    gq, sg = quantize_group_cols_fp8(dgu, offsets)
+    hq, sh = quantize_group_cols_fp8(h_perm, offsets)
+    dq, sd = quantize_group_cols_fp8(dy_perm, offsets)
+    E_l = len(xq)
+    H = _f64(x_perm).shape[1]
+    dWg, dWu, dWd = np.zeros((E_l, I, H)), np.zeros((E_l, I, H)), np.zeros((E_l, H, I))
+    for e in range(E_l):
+        gu_w = fp8_matmul_rows(gq[e], sg[e], xq[e], sx[e])     # [2I, H]
+        dWg[e], dWu[e] = gu_w[:I], gu_w[I:]
+        dWd[e] = fp8_matmul_rows(dq[e], sd[e], hq[e], sh[e])    # [H, I]
+    return {"dw_gate": dWg, "dw_up": dWu, "dw_down": dWd}
+
+
+# --------------------------------------------------------------------------
 # Backward
 # --------------------------------------------------------------------------
 

@@ -569,6 +569,86 @@ def check_pair_values_rows():
         assert np.allclose(sub[n], pv[n][[7, 2]], rtol=1e-12, atol=1e-14, equal_nan=True)
 
 
+def check_fp8_group_col_scales_literal():
+    """Per-(group, column) scales of a hand-built grouped matrix, worked out by hand
+    from the rule "smallest power of two 2^e with max|column of the group| <= 448 * 2^e"
+    (e = 0 for an all-zero column or an empty group): group 0 (rows 0-1) has column
+    maxima 448, 449, 0 -> scales 1, 2, 1; group 1 is empty -> 1, 1, 1; group 2 (rows
+    2-4) has maxima 0.875 = 448 * 2^-9, 3584 = 448 * 2^3 and 0.001 -> 2^-9, 8, 2^-18.
+    Each code decodes, times its scale, to within one E4M3 step of its value."""
+    a = np.array([[448.0, -449.0, 0.0],
+                  [-3.0, 100.0, 0.0],
+                  [0.5, 3584.0, -0.001],
+                  [-0.875, 1.0, 0.0005],
+                  [0.25, -7.0, 0.0]])
+    codes, sc = O.quantize_group_cols_fp8(a, [0, 2, 2, 5])
+    want = np.array([[1.0, 2.0, 1.0], [1.0, 1.0, 1.0], [2.0 ** -9, 8.0, 2.0 ** -18]])
+    assert sc.shape == (3, 3) and np.array_equal(sc, want)
+    assert [c.shape for c in codes] == [(3, 2), (3, 0), (3, 3)]
+    for e, (o0, o1) in enumerate(((0, 2), (2, 2), (2, 5))):
+        back = O.fp8_e4m3_decode(codes[e]) * sc[e][:, None]
+        ref = a[o0:o1].T
+        assert np.all(np.abs(back - ref) <= np.maximum(2.0 ** -4 * np.abs(ref), sc[e][:, None] * 2.0 ** -10))
+
+
+def _grid_cols(rng, grid, rows, cols, offsets):
+    """rows x cols values on the E4M3 grid times a power of two per (group, column),
+    each (group, column) reaching 448 times its power exactly (codes then exact)"""
+    a = rng.choice(np.concatenate([grid, -grid]), size=(rows, cols))
+    for e in range(len(offsets) - 1):
+        o0, o1 = offsets[e], offsets[e + 1]
+        if o1 == o0:
+            continue
+        p = np.exp2(rng.integers(-4, 4, size=cols).astype(np.float64))
+        a[o0:o1] *= p
+        a[o0 + rng.integers(0, o1 - o0, size=cols), np.arange(cols)] = 448.0 * p
+    return a
+
+
+def check_fp8_wgrad_exact_on_grid():
+    """On operands whose (group, column) slices lie on the E4M3 grid scaled by a power
+    of two with maximum 448 times it, every code is exact, so the FP8 weight gradients
+    equal the plain per-expert weight gradients (dW_down[e] = dy_e^T h_e, dW_gate[e] =
+    dg_e^T x_e, dW_up[e] = du_e^T x_e over the expert's rows) exactly; an expert with
+    no rows gets zeros."""
+    rng = np.random.default_rng(21)
+    grid = O.fp8_e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    grid = grid[grid >= 2.0 ** -3]           # keep every product and sum exact in float64
+    offsets = [0, 5, 5, 13, 16]
+    R, H, I = 16, 12, 8
+    x = _grid_cols(rng, grid, R, H, offsets)
+    dgu = _grid_cols(rng, grid, R, 2 * I, offsets)
+    h = _grid_cols(rng, grid, R, I, offsets)
+    dy = _grid_cols(rng, grid, R, H, offsets)
+    got = O.moe_wgrad_fp8(x, dgu, h, dy, offsets)
+    for e in range(4):
+        o0, o1 = offsets[e], offsets[e + 1]
+        assert np.array_equal(got["dw_down"][e], dy[o0:o1].T @ h[o0:o1])
+        assert np.array_equal(got["dw_gate"][e], dgu[o0:o1, :I].T @ x[o0:o1])
+        assert np.array_equal(got["dw_up"][e], dgu[o0:o1, I:].T @ x[o0:o1])
+    assert not got["dw_down"][1].any() and not got["dw_gate"][1].any()
+
+
+def check_fp8_wgrad_close_to_exact():
+    """Random operands whose experts differ in magnitude by 2^20: each expert's FP8
+    weight gradients stay within the two operands' E4M3 rounding (each within 2^-4
+    relative: rel-L2 under 10%) of its exact weight gradients.  Scales shared across
+    experts would push the small expert's codes into underflow."""
+    rng = np.random.default_rng(22)
+    offsets = [0, 40, 90]
+    R, H, I = 90, 48, 32
+    mag = np.ones((R, 1))
+    mag[40:] = 2.0 ** 20
+    x, dgu = rng.standard_normal((R, H)) * mag, rng.standard_normal((R, 2 * I)) * mag
+    h, dy = rng.standard_normal((R, I)) * mag, rng.standard_normal((R, H)) * mag
+    got = O.moe_wgrad_fp8(x, dgu, h, dy, offsets)
+    for e in range(2):
+        o0, o1 = offsets[e], offsets[e + 1]
+        assert _rel(got["dw_down"][e], dy[o0:o1].T @ h[o0:o1]) < 0.10
+        assert _rel(got["dw_gate"][e], dgu[o0:o1, :I].T @ x[o0:o1]) < 0.10
+        assert _rel(got["dw_up"][e], dgu[o0:o1, I:].T @ x[o0:o1]) < 0.10
+
+
 ALL_CHECKS = [check_gating_golden, check_topk_brute_force, check_zero_input_routing,
               check_duplicate_router_columns, check_k1_and_kE, check_weights_sum_to_one,
               check_counts_offsets, check_permutation_maps, check_permute_unpermute_identity,
@@ -577,7 +657,9 @@ ALL_CHECKS = [check_gating_golden, check_topk_brute_force, check_zero_input_rout
               check_finite_differences, check_router_grads_vs_autograd, check_fp8_codes_vs_torch,
               check_fp8_row_scale_is_minimal, check_fp8_matmul_brute_force,
               check_fp8_forward_close_to_exact, check_fp8_weight_t_scales_per_input_channel,
-              check_fp8_dgrad_close_to_exact, check_round_bf16_vs_torch, check_pair_values_rows]
+              check_fp8_dgrad_close_to_exact, check_round_bf16_vs_torch, check_pair_values_rows,
+              check_fp8_group_col_scales_literal, check_fp8_wgrad_exact_on_grid,
+              check_fp8_wgrad_close_to_exact]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
@@ -712,10 +794,44 @@ def _mut_pair_values_slot_order(x, idx, w_gate, w_up, w_down, e_lo, e_hi, tokens
     return {n: v[:, ::-1].copy() for n, v in out.items()}
 
 
+def _mut_group_cols_shared_scale(a, offsets):
+    """scales from the column maxima over all rows instead of each group's rows"""
+    a = np.asarray(a, np.float64)
+    s = np.exp2(OM.fp8_row_exponent(np.abs(a).max(axis=0) if len(a) else np.zeros(a.shape[1]))
+                .astype(np.float64))
+    off = np.asarray(offsets, np.int64)
+    codes = [OM.fp8_e4m3_encode(a[off[e]:off[e + 1]].T / s[:, None]) for e in range(len(off) - 1)]
+    return codes, np.broadcast_to(s, (len(off) - 1, a.shape[1])).copy()
+
+
+def _mut_group_cols_one_scale_per_group(a, offsets):
+    """one scale per group (its largest column) instead of one per (group, column)"""
+    a = np.asarray(a, np.float64)
+    off = np.asarray(offsets, np.int64)
+    codes, scales = [], []
+    for e in range(len(off) - 1):
+        blk = a[off[e]:off[e + 1]]
+        s = 2.0 ** float(OM.fp8_row_exponent(np.array([np.abs(blk).max() if blk.size else 0.0]))[0])
+        codes.append(OM.fp8_e4m3_encode(blk.T / s))
+        scales.append(np.full(a.shape[1], s))
+    return codes, np.stack(scales)
+
+
+def _mut_wgrad_gate_up_swapped(x_perm, dgu, h_perm, dy_perm, offsets):
+    out = _ORIG["moe_wgrad_fp8"](x_perm, dgu, h_perm, dy_perm, offsets)
+    return {"dw_gate": out["dw_up"], "dw_up": out["dw_gate"], "dw_down": out["dw_down"]}
+
+
+def _mut_wgrad_down_from_x(x_perm, dgu, h_perm, dy_perm, offsets):
+    """dW_down from the columns of x in place of dy"""
+    return _ORIG["moe_wgrad_fp8"](x_perm, dgu, h_perm, x_perm, offsets)
+
+
 _ORIG = {n: getattr(OM, n) for n in ("silu", "topk_experts", "gate_weights", "permutation_maps",
                                      "moe_backward", "expert_ffn_parts", "fp8_e4m3_encode",
                                      "fp8_row_exponent", "quantize_expert_weights_t_fp8",
-                                     "round_bf16", "pair_values")}
+                                     "round_bf16", "pair_values", "quantize_group_cols_fp8",
+                                     "moe_wgrad_fp8")}
 
 MUTATIONS = [("silu", _mut_silu_is_sigmoid), ("topk_experts", _mut_topk_ties_high),
              ("gate_weights", _mut_no_renorm), ("permutation_maps", _mut_group_tokens_descending),
@@ -731,7 +847,11 @@ MUTATIONS = [("silu", _mut_silu_is_sigmoid), ("topk_experts", _mut_topk_ties_hig
              ("round_bf16", _mut_bf16_truncates), ("round_bf16", _mut_bf16_ties_away),
              ("round_bf16", _mut_bf16_via_float32),
              ("pair_values", _mut_pair_values_global_index),
-             ("pair_values", _mut_pair_values_slot_order)]
+             ("pair_values", _mut_pair_values_slot_order),
+             ("quantize_group_cols_fp8", _mut_group_cols_shared_scale),
+             ("quantize_group_cols_fp8", _mut_group_cols_one_scale_per_group),
+             ("moe_wgrad_fp8", _mut_wgrad_gate_up_swapped),
+             ("moe_wgrad_fp8", _mut_wgrad_down_from_x)]
 
 
 @pytest.mark.parametrize("name,mut", MUTATIONS, ids=[m[1].__name__ for m in MUTATIONS])
