@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 typedef enum {
   MOE_OK = 0,
@@ -75,7 +75,8 @@ typedef enum {
   MOE_OP_ROUTE_BWD = 4,
   MOE_OP_COMBINE_DX = 5,
   MOE_OP_FFN_FWD_FP8 = 6,
-  MOE_OP_FFN_DGRAD_FP8 = 7
+  MOE_OP_FFN_DGRAD_FP8 = 7,
+  MOE_OP_FFN_WGRAD_FP8 = 8
 } moe_op;
 
 /* Returns MOE_ABI_VERSION of the loaded library. */
@@ -216,7 +217,7 @@ int moe_quantize_fp8_t(const void* src0, const void* src1, int batch, int N, int
                        uint8_t* q, float* scale, void* stream);
 
 /* Data gradients of the grouped SwiGLU FFN on E4M3 codes (the weight
- * gradients stay with moe_grouped_ffn_bwd in bf16).  With dy_q / dy_scale the
+ * gradients: moe_grouped_ffn_wgrad_fp8, or moe_grouped_ffn_bwd in bf16).  With dy_q / dy_scale the
  * rows of dy_perm quantized by moe_quantize_fp8, wdt_* the codes of W_down^T
  * and wgut_* those of [W_gate^T | W_up^T] from moe_quantize_fp8_t:
  *   dh[r,i]  = bf16(dy_scale[r] * wdt_scale[e,i] * sum_h code(dy_q[r,h]) code(wdt_q[e,i,h]))
@@ -234,6 +235,47 @@ int moe_grouped_ffn_dgrad_fp8(const uint8_t* dy_q, const float* dy_scale, const 
                               const uint8_t* wdt_q, const float* wdt_scale, const uint8_t* wgut_q,
                               const float* wgut_scale, void* dgu, void* dx_perm, void* ws,
                               size_t ws_bytes, void* stream);
+
+/* Column quantization of grouped rows for the FP8 weight gradients, which
+ * sum over each expert's rows, so a scale must hold along them: for group g
+ * (rows offsets[g] .. offsets[g+1]-1 of the logical matrix, row r being
+ * src[src_row[r]] when src_row is not NULL, else src[r]) and column c,
+ *   scale[g,c] = 2^e, e the smallest integer with max_r |src[r,c]| <= 448 * 2^e
+ *                over the group's rows (e = 0 for an empty group or a zero column),
+ *   q[c, poff[g] + i] = the E4M3 code nearest to src[offsets[g]+i, c] / scale[g,c]
+ *                (ties to even) for i < n_g, and code 0 for n_g <= i < round64(n_g),
+ *   poff[g]  = sum over g' < g of round64(n_g'), poff[E_l] the total (out).
+ * Columns poff[E_l] .. q_pitch-1 of q are not written.
+ *   src [rows,C] bf16 (row pitch C), src_row [R_cap] int32 or NULL, offsets
+ *   [E_l+1] int32 (device), q [C,q_pitch] uint8, scale [E_l,C] fp32, poff
+ *   [E_l+1] int32.  C % 64 == 0 and q_pitch % 64 == 0 with
+ *   q_pitch >= round64(R_cap) + 64 * E_l (else MOE_EINVAL); src and q 16-byte
+ *   aligned.  Reading of the FP8 recipe (page "TorchTitan FSDP2 完全指南",
+ *   section "性能表现", row FSDP + compile + FP8, which fixes no scaling). */
+int moe_quantize_fp8_group_t(const void* src, const int32_t* src_row, int C,
+                             const int32_t* offsets, int E_l, int R_cap, uint8_t* q, int q_pitch,
+                             float* scale, int32_t* poff, void* stream);
+
+/* Weight gradients of the grouped SwiGLU FFN on E4M3 codes (same FP8
+ * reading).  Each operand is column-quantized per expert as
+ * moe_quantize_fp8_group_t does (codes and scales in ws), then, for every
+ * local expert e with rows r in its group (r < R = offsets[E_l]):
+ *   [dW_gate; dW_up][e][i,h] = s_gu[e,i] * s_x[e,h] * sum_r code(dgu[r,i]) code(x_r[h])
+ *   dW_down[e][h,i]          = s_dy[e,h] * s_h[e,i] * sum_r code(dy_perm[r,h]) code(h_perm[r,i])
+ * (rows i < I of the first product are dW_gate, the rest dW_up), with x_r the
+ * grouped token row: x[src_row[r]] if src_row is not NULL, else x[r].
+ * Code products are exact and summed in fp32; accumulate != 0 adds to the
+ * fp32 outputs instead of overwriting them.  An expert without rows gets 0.
+ *   x [T,H] (with src_row [R_cap]) or [R_cap,H] bf16, dgu [R_cap,2I] bf16
+ *   (moe_grouped_ffn_dgrad_fp8's dgu), h_perm [R_cap,I] bf16, dy_perm
+ *   [R_cap,H] bf16, dw_gate / dw_up [E_l,I,H] fp32, dw_down [E_l,H,I] fp32
+ *   ws       MOE_OP_FFN_WGRAD_FP8 workspace (codes, scales, padded offsets)
+ * Needs H % 128 == 0 and I % 128 == 0 (else MOE_EUNSUPPORTED). */
+int moe_grouped_ffn_wgrad_fp8(const void* x, const int32_t* src_row, const void* dgu,
+                              const void* h_perm, const void* dy_perm, const int32_t* offsets,
+                              int E_l, int R_cap, int H, int I, float* dw_gate, float* dw_up,
+                              float* dw_down, int accumulate, void* ws, size_t ws_bytes,
+                              void* stream);
 
 /* Weighted unpermute ("combine"): for every token, in slot order j = 0..k-1,
  *   y[t] = sum_{j: dest_row[t*k+j] >= 0} topk_w[t,j] * y_perm[dest_row[t*k+j]]  (+ addend[t])

@@ -10,7 +10,8 @@ an error.
 Functions keep the C names (moe_route, moe_permute, moe_grouped_ffn_fwd,
 moe_combine, moe_combine_bwd, moe_grouped_ffn_bwd, moe_route_bwd, and the FP8
 forward: moe_quantize_fp8, moe_grouped_ffn_fwd_fp8; data gradients:
-moe_quantize_fp8_t, moe_grouped_ffn_dgrad_fp8) and return
+moe_quantize_fp8_t, moe_grouped_ffn_dgrad_fp8; weight gradients:
+moe_quantize_fp8_group_t, moe_grouped_ffn_wgrad_fp8) and return
 freshly allocated torch tensors; each also accepts preallocated outputs via
 ``out=`` dictionaries so that steady-state loops allocate nothing.
 """
@@ -27,8 +28,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_F32, MOE_BF16, MOE_FP8 = 0, 1, 2
 (MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD, MOE_OP_ROUTE_BWD,
- MOE_OP_COMBINE_DX, MOE_OP_FFN_FWD_FP8, MOE_OP_FFN_DGRAD_FP8) = range(8)
-ABI_VERSION = 5
+ MOE_OP_COMBINE_DX, MOE_OP_FFN_FWD_FP8, MOE_OP_FFN_DGRAD_FP8, MOE_OP_FFN_WGRAD_FP8) = range(9)
+ABI_VERSION = 6
 
 
 class MoEError(RuntimeError):
@@ -65,6 +66,9 @@ def _load():
         "moe_grouped_ffn_dgrad_fp8": ([P, P, P, P, I32, I32, I32, I32, P, P, P, P, P, P, P, SZ, P], I32),
         "moe_grouped_ffn_fwd_fp8": ([P, P, P, P, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, P,
                                      SZ, P], I32),
+        "moe_quantize_fp8_group_t": ([P, P, I32, P, I32, I32, P, I32, P, P, P], I32),
+        "moe_grouped_ffn_wgrad_fp8": ([P, P, P, P, P, P, I32, I32, I32, I32, P, P, P, I32, P, SZ, P],
+                                      I32),
         "moe_profile_kernel": ([I32, ctypes.POINTER(P), ctypes.POINTER(P), I32], I32),
         "moe_profile_recorded": ([], I32),
     }
@@ -425,4 +429,58 @@ def moe_grouped_ffn_dgrad_fp8(dy_q: torch.Tensor, dy_scale: torch.Tensor, gu: to
                                          _ptr(wgut[1]), _ptr(o["dgu"]), _ptr(o["dx_perm"]),
                                          _ptr(ws), _nbytes(ws), _stream()),
            "moe_grouped_ffn_dgrad_fp8")
+    return o
+
+
+def wgrad_fp8_pitch(R_cap: int, E_l: int) -> int:
+    """Row pitch (codes) of the transposed code matrices: room for every group's
+    rows rounded up to 64."""
+    return ((R_cap + 63) // 64) * 64 + 64 * E_l
+
+
+def moe_quantize_fp8_group_t(src: torch.Tensor, offsets: torch.Tensor, E_l: int,
+                             src_row: Optional[torch.Tensor] = None, R_cap: Optional[int] = None,
+                             out: Optional[Dict[str, torch.Tensor]] = None):
+    """Per-(group, column) E4M3 codes of grouped bf16 rows (row r = src[src_row[r]] if
+    src_row is given, else src[r]), transposed: returns dict q uint8 [C, pitch]
+    (group g at columns poff[g] ..), scale fp32 [E_l, C], poff int32 [E_l + 1]."""
+    C = src.shape[1]
+    if R_cap is None:
+        R_cap = src_row.numel() if src_row is not None else src.shape[0]
+    pitch = wgrad_fp8_pitch(R_cap, E_l)
+    dev = src.device
+    o = dict(out or {})
+    o.setdefault("q", torch.empty((C, pitch), dtype=torch.uint8, device=dev))
+    o.setdefault("scale", torch.empty((E_l, C), dtype=torch.float32, device=dev))
+    o.setdefault("poff", torch.empty(E_l + 1, dtype=torch.int32, device=dev))
+    _check(lib.moe_quantize_fp8_group_t(_ptr(src), _ptr(src_row), C, _ptr(offsets), E_l, R_cap,
+                                        _ptr(o["q"]), o["q"].shape[1], _ptr(o["scale"]),
+                                        _ptr(o["poff"]), _stream()), "moe_quantize_fp8_group_t")
+    return o
+
+
+def moe_grouped_ffn_wgrad_fp8(x: torch.Tensor, src_row: Optional[torch.Tensor], dgu: torch.Tensor,
+                              h_perm: torch.Tensor, dy_perm: torch.Tensor, offsets: torch.Tensor,
+                              E_l: int, accumulate: bool = False, ws: Optional[torch.Tensor] = None,
+                              out: Optional[Dict[str, torch.Tensor]] = None):
+    """Weight gradients of the grouped SwiGLU FFN on E4M3 codes (operands quantized per
+    (expert, column)).  x [T, H] with src_row [R_cap] (or the grouped rows [R_cap, H]
+    with src_row None), dgu [R_cap, 2I], h_perm [R_cap, I], dy_perm [R_cap, H], all
+    bf16.  Returns dict dw_gate, dw_up [E_l, I, H] and dw_down [E_l, H, I] (fp32)."""
+    R_cap, H = dy_perm.shape
+    I = h_perm.shape[1]
+    dev = dy_perm.device
+    o = dict(out or {})
+    for n, sh in (("dw_gate", (E_l, I, H)), ("dw_up", (E_l, I, H)), ("dw_down", (E_l, H, I))):
+        o.setdefault(n, torch.empty(sh, dtype=torch.float32, device=dev))
+    nb = lib.moe_workspace_bytes(MOE_OP_FFN_WGRAD_FP8, max(R_cap, 0), H, I, max(E_l, 1), 1, 0, E_l,
+                                 MOE_BF16)
+    if nb < 0:
+        _check(int(nb), "moe_workspace_bytes")
+    ws = _ws(int(nb), dev, ws)
+    _check(lib.moe_grouped_ffn_wgrad_fp8(_ptr(x), _ptr(src_row), _ptr(dgu), _ptr(h_perm),
+                                         _ptr(dy_perm), _ptr(offsets), E_l, R_cap, H, I,
+                                         _ptr(o["dw_gate"]), _ptr(o["dw_up"]), _ptr(o["dw_down"]),
+                                         1 if accumulate else 0, _ptr(ws), _nbytes(ws), _stream()),
+           "moe_grouped_ffn_wgrad_fp8")
     return o

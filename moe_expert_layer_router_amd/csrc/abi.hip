@@ -186,7 +186,8 @@ int64_t moe_workspace_bytes(int op, int T, int H, int I, int E, int k, int e_lo,
                             int dtype) {
   const char* fn = "moe_workspace_bytes";
   if (dtype == MOE_FP8) {
-    if (op != MOE_OP_PERMUTE && op != MOE_OP_FFN_FWD_FP8 && op != MOE_OP_FFN_DGRAD_FP8)
+    if (op != MOE_OP_PERMUTE && op != MOE_OP_FFN_FWD_FP8 && op != MOE_OP_FFN_DGRAD_FP8 &&
+        op != MOE_OP_FFN_WGRAD_FP8)
       return fail(MOE_EINVAL, "%s: MOE_FP8 applies to MOE_OP_PERMUTE and the FP8 FFN ops only", fn);
   } else if (int rc = check_dtype(dtype, fn)) {
     return rc;
@@ -202,12 +203,15 @@ int64_t moe_workspace_bytes(int op, int T, int H, int I, int E, int k, int e_lo,
     case MOE_OP_COMBINE_DX:
       return (int64_t)align256((size_t)E * H * elem_bytes(dtype));
     case MOE_OP_FFN_FWD_FP8:
-    case MOE_OP_FFN_DGRAD_FP8: {
+    case MOE_OP_FFN_DGRAD_FP8:
+    case MOE_OP_FFN_WGRAD_FP8: {
       if (e_lo < 0 || e_hi > E || e_lo >= e_hi)
         return fail(MOE_EINVAL, "%s: need 0 <= e_lo < e_hi <= E", fn);
       if (I <= 0) return fail(MOE_EINVAL, "%s: I must be positive", fn);
-      return (int64_t)(op == MOE_OP_FFN_FWD_FP8 ? ffn_fwd_fp8_ws_bytes(R_cap, e_hi - e_lo, I)
-                                                : ffn_dgrad_fp8_ws_bytes(R_cap, e_hi - e_lo, I));
+      const int E_l = e_hi - e_lo;
+      if (op == MOE_OP_FFN_WGRAD_FP8) return (int64_t)ffn_wgrad_fp8_ws_bytes(R_cap, E_l, H, I);
+      return (int64_t)(op == MOE_OP_FFN_FWD_FP8 ? ffn_fwd_fp8_ws_bytes(R_cap, E_l, I)
+                                                : ffn_dgrad_fp8_ws_bytes(R_cap, E_l, I));
     }
     case MOE_OP_PERMUTE:
     case MOE_OP_FFN_FWD:
@@ -449,6 +453,63 @@ int moe_grouped_ffn_dgrad_fp8(const uint8_t* dy_q, const float* dy_scale, const 
   return hip_status(launch_ffn_dgrad_fp8(dy_q, dy_scale, (const bf16_t*)gu_saved, offsets, E_l,
                                          R_cap, H, I, wdt_q, wdt_scale, wgut_q, wgut_scale,
                                          (bf16_t*)dgu, (bf16_t*)dx_perm, ws, begin_launch(stream)),
+                    fn);
+}
+
+int moe_quantize_fp8_group_t(const void* src, const int32_t* src_row, int C,
+                             const int32_t* offsets, int E_l, int R_cap, uint8_t* q, int q_pitch,
+                             float* scale, int32_t* poff, void* stream) {
+  const char* fn = "moe_quantize_fp8_group_t";
+  if (E_l < 1 || E_l > kMaxE) return fail(MOE_EINVAL, "%s: E_l=%d outside [1, %d]", fn, E_l, kMaxE);
+  if (R_cap < 0) return fail(MOE_EINVAL, "%s: R_cap must be >= 0", fn);
+  if (C <= 0 || C % 64 != 0) return fail(MOE_EINVAL, "%s: C=%d must be a positive multiple of 64", fn, C);
+  const int64_t need = (((int64_t)R_cap + 63) & ~(int64_t)63) + 64 * (int64_t)E_l;
+  if (q_pitch % 64 != 0 || q_pitch < need)
+    return fail(MOE_EINVAL, "%s: q_pitch=%d must be a multiple of 64 and >= %lld", fn, q_pitch,
+                (long long)need);
+  if (int rc = check_ptr(offsets, "offsets", fn)) return rc;
+  if (int rc = check_ptr(q, "q", fn, true)) return rc;
+  if (int rc = check_ptr(scale, "scale", fn)) return rc;
+  if (int rc = check_ptr(poff, "poff", fn)) return rc;
+  if (R_cap > 0)
+    if (int rc = check_ptr(src, "src", fn, true)) return rc;
+  QuantGroupT a{};
+  a.t[0] = {(const bf16_t*)src, src_row, (long)C, C, q, scale};
+  a.nt = 1;
+  a.offsets = offsets;
+  a.E_l = E_l;
+  a.Kp = q_pitch;
+  a.poff = poff;
+  return hip_status(launch_quantize_group_t_fp8(a, begin_launch(stream)), fn);
+}
+
+int moe_grouped_ffn_wgrad_fp8(const void* x, const int32_t* src_row, const void* dgu,
+                              const void* h_perm, const void* dy_perm, const int32_t* offsets,
+                              int E_l, int R_cap, int H, int I, float* dw_gate, float* dw_up,
+                              float* dw_down, int accumulate, void* ws, size_t ws_bytes,
+                              void* stream) {
+  const char* fn = "moe_grouped_ffn_wgrad_fp8";
+  if (int rc = check_ffn_shape(E_l, R_cap, H, I, MOE_FP8, fn)) return rc;
+  if (H % 128 != 0 || I % 128 != 0)
+    return fail(MOE_EUNSUPPORTED, "%s: needs H %% 128 == 0 and I %% 128 == 0 (H=%d, I=%d)", fn, H, I);
+  // the transposed code matrices: max(2I, H) rows of the padded pitch
+  const int64_t pitch = (((int64_t)R_cap + 63) & ~(int64_t)63) + 64 * (int64_t)E_l;
+  if (int rc = check_range(pitch * std::max(2 * I, H), "a transposed code matrix", fn)) return rc;
+  if (int rc = check_ptr(offsets, "offsets", fn)) return rc;
+  if (int rc = check_ptr(dw_gate, "dw_gate", fn, true)) return rc;
+  if (int rc = check_ptr(dw_up, "dw_up", fn, true)) return rc;
+  if (int rc = check_ptr(dw_down, "dw_down", fn, true)) return rc;
+  if (R_cap > 0) {
+    if (int rc = check_ptr(x, "x", fn, true)) return rc;
+    if (int rc = check_ptr(dgu, "dgu", fn, true)) return rc;
+    if (int rc = check_ptr(h_perm, "h_perm", fn, true)) return rc;
+    if (int rc = check_ptr(dy_perm, "dy_perm", fn, true)) return rc;
+  }
+  if (int rc = check_ws(ws, ws_bytes, ffn_wgrad_fp8_ws_bytes(R_cap, E_l, H, I), fn)) return rc;
+  return hip_status(launch_ffn_wgrad_fp8((const bf16_t*)x, src_row, (const bf16_t*)dgu,
+                                         (const bf16_t*)h_perm, (const bf16_t*)dy_perm, offsets,
+                                         E_l, R_cap, H, I, dw_gate, dw_up, dw_down,
+                                         accumulate != 0, ws, begin_launch(stream)),
                     fn);
 }
 

@@ -223,6 +223,36 @@ hipError_t launch_ffn_dgrad_fp8(const uint8_t* dy_q, const float* dy_scale, cons
                                 const uint8_t* wdt_q, const float* wdt_s, const uint8_t* wgut_q,
                                 const float* wgut_s, bf16_t* dgu, bf16_t* dx_perm, void* ws,
                                 hipStream_t s);
+// FP8 weight gradients: columns of grouped rows quantized per (group, column)
+// into transposed code rows, each group at a padded offset (fp8.hip), and the
+// two K-grouped products on them (gemm.hip).
+struct QuantGroupTensor {
+  const bf16_t* src;     // [rows][ld] bf16
+  const int32_t* rows;   // logical row r reads src row rows[r] (null: row r)
+  long ld;
+  int C;                 // columns (multiple of 64)
+  uint8_t* q;            // [C][Kp] codes
+  float* scale;          // [groups][C]
+};
+constexpr int kQuantGroupTensors = 4;
+struct QuantGroupT {
+  QuantGroupTensor t[kQuantGroupTensors];
+  int nt;
+  const int32_t* offsets;  // [groups + 1] row offsets (device)
+  int E_l;
+  int Kp;                  // code row pitch
+  int32_t* poff;           // out: [groups + 1] padded offsets (multiples of 64)
+  int32_t* ctrs;           // counters zeroed for the products that follow, or null
+  int nctrs;
+};
+hipError_t launch_quantize_group_t_fp8(const QuantGroupT& q, hipStream_t s);
+int wgrad_fp8_pitch(int R_cap, int E_l);
+size_t ffn_wgrad_fp8_ws_bytes(int R_cap, int E_l, int H, int I);
+hipError_t launch_ffn_wgrad_fp8(const bf16_t* x, const int32_t* src_row, const bf16_t* dgu,
+                                const bf16_t* h_perm, const bf16_t* dy_perm,
+                                const int32_t* offsets, int E_l, int R_cap, int H, int I,
+                                float* dw_gate, float* dw_up, float* dw_down, bool accumulate,
+                                void* ws, hipStream_t s);
 hipError_t order_after(hipStream_t s, hipStream_t waiter);
 hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, const bf16_t* gu,
                                const bf16_t* h_perm, const int32_t* offsets, int E_l, int R_cap,

@@ -145,6 +145,97 @@ hipError_t launch_quantize_t_fp8(const bf16_t* src0, const bf16_t* src1, int bat
   return hipGetLastError();
 }
 
+// Columns of grouped rows quantized per (group, column) for the FP8 weight
+// gradients, which sum over a group's rows: for group g (rows offsets[g] ..
+// offsets[g + 1] - 1) and column c, scale = 2^e by the row rule above applied
+// to the column restricted to the group, and the codes of that column go to
+// row c of the transposed output, columns poff[g] .. poff[g] + n_g - 1, with
+// zero codes up to the next multiple of 64 (poff[g] = the sum of the earlier
+// groups' row counts rounded up to 64, also written out).  A workgroup takes
+// 64 columns of one tensor for one group: pass 1 the column maxima (each
+// thread 8 columns of every 32nd row, then an LDS reduction), pass 2 the
+// codes, through 64 x 64 tiles in LDS so that each thread writes 16
+// consecutive codes of one output row.  Columns of several tensors share one
+// launch (strips numbered tensor by tensor).
+__global__ __launch_bounds__(256) void quantize_group_t_fp8_kernel(const QuantGroupT a) {
+  __shared__ float s_max[32][65];
+  __shared__ int s_e[64];
+  __shared__ __align__(16) bf16_t s_tile[64][64];
+  __shared__ int s_poff;
+  const int g = blockIdx.y, t = threadIdx.x;
+  int ti = 0, strip = blockIdx.x;
+  while (ti + 1 < a.nt && strip >= a.t[ti].C / 64) {
+    strip -= a.t[ti].C / 64;
+    ++ti;
+  }
+  const QuantGroupTensor T = a.t[ti];
+  const int c0 = strip * 64;
+  const int o0 = a.offsets[g], n = a.offsets[g + 1] - o0;
+  if (t < kWave) {  // padded start of this group
+    int acc = 0;
+    for (int j = t; j < g; j += kWave) acc += (a.offsets[j + 1] - a.offsets[j] + 63) & ~63;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+    if (t == 0) s_poff = acc;
+  }
+  if (a.ctrs != nullptr && blockIdx.x == 0 && g == 0 && t < a.nctrs) a.ctrs[t] = 0;
+  const int cc = t & 7, r0 = t >> 3;
+  float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int r = r0; r < n; r += 32) {
+    const long row = T.rows != nullptr ? T.rows[o0 + r] : o0 + r;
+    float v[8];
+    unpack8(*reinterpret_cast<const uint4*>(T.src + row * T.ld + c0 + 8 * cc), v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf(v[i]));
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s_max[r0][8 * cc + i] = m[i];
+  __syncthreads();
+  const int poff = s_poff;
+  if (blockIdx.x == 0 && t == 0) {
+    a.poff[g] = poff;
+    if (g == a.E_l - 1) a.poff[a.E_l] = poff + ((n + 63) & ~63);
+  }
+  if (t < 64) {
+    float mx = 0.f;
+    for (int r = 0; r < 32; ++r) mx = fmaxf(mx, s_max[r][t]);
+    const int e = fp8_exponent(mx);
+    s_e[t] = e;
+    T.scale[(size_t)g * T.C + c0 + t] = ldexpf(1.f, e);
+  }
+  __syncthreads();
+  const int oc = t & 63, og = t >> 6;  // output row c0 + oc, 16 group rows 16 og .. + 15 of a tile
+  const int e = s_e[oc];
+  uint8_t* qrow = T.q + (size_t)(c0 + oc) * a.Kp + poff;
+  for (int j0 = 0; j0 < n; j0 += 64) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = r0 + 32 * h;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (j0 + r < n) {
+        const long row = T.rows != nullptr ? T.rows[o0 + j0 + r] : o0 + j0 + r;
+        v = *reinterpret_cast<const uint4*>(T.src + row * T.ld + c0 + 8 * cc);
+      }
+      *reinterpret_cast<uint4*>(&s_tile[r][8 * cc]) = v;
+    }
+    __syncthreads();
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = bf2f(s_tile[16 * og + i][oc]);
+    const uint2 lo = fp8_codes8(v, e), hi = fp8_codes8(v + 8, e);
+    *reinterpret_cast<uint4*>(qrow + j0 + 16 * og) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    __syncthreads();
+  }
+}
+
+hipError_t launch_quantize_group_t_fp8(const QuantGroupT& q, hipStream_t s) {
+  int strips = 0;
+  for (int i = 0; i < q.nt; ++i) strips += q.t[i].C / 64;
+  if (strips == 0 || q.E_l <= 0) return hipSuccess;
+  quantize_group_t_fp8_kernel<<<dim3(strips, q.E_l), 256, 0, s>>>(q);
+  return hipGetLastError();
+}
+
 // Gradients of h = SiLU(g) * u for the FP8 gate / up data gradient, one wave
 // per grouped row r < nrows: dg = dh u s (1 + g (1 - s)), du = dh SiLU(g),
 // s = sigmoid(g), in fp32 from the bf16 dh and the saved g, u; [dg | du] is

@@ -106,7 +106,11 @@ constexpr int kBmGrouped = 256;
 constexpr int kBmWgrad = 256;
 constexpr int kBmWgradDown = 128;
 
-enum GemmKind { K_GATEUP_FWD = 0, K_DOWN_FWD = 1, K_DOWN_DGRAD = 2, K_GATEUP_DGRAD = 3, K_WGRAD = 4 };
+enum GemmKind {
+  K_GATEUP_FWD = 0, K_DOWN_FWD = 1, K_DOWN_DGRAD = 2, K_GATEUP_DGRAD = 3, K_WGRAD = 4,
+  K_WGRAD8 = 5  // FP8 weight gradient: K-grouped, both operands K-contiguous codes
+};
+constexpr bool k_grouped(int kind) { return kind == K_WGRAD || kind == K_WGRAD8; }
 
 struct GemmArgs {
   const bf16_t* a;
@@ -116,6 +120,7 @@ struct GemmArgs {
   long ldb;
   long b_group_stride;      // elements between experts in b0 / b1
   const int32_t* offsets;   // group row offsets [groups + 1], or null for even splits
+                            // (WGRAD8: padded code offsets, multiples of 64)
   const int32_t* sched;     // M-grouped tile table: [0] = count, then (expert, row0, row1)
   int groups;               // K-grouped: number of groups
   int split_rows;           // K-grouped with offsets == null: rows per group
@@ -138,6 +143,7 @@ struct GemmArgs {
   const float* sb0;
   const float* sb1;
   long sb_group_stride;
+  long sa_group_stride;     // WGRAD8: per-group row scales of A ([groups][M] floats)
   // Dynamic tile order: null = static (workgroup g takes tiles g, g + grid,
   // ...); else a zeroed counter from which workgroups draw their tiles after
   // the first (tile grid + ticket), so that kernels running side by side
@@ -149,7 +155,7 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 template <int KIND> struct Traits {
   static constexpr bool A_KC = KIND != K_WGRAD;
-  static constexpr bool B_KC = KIND == K_GATEUP_FWD || KIND == K_DOWN_FWD;
+  static constexpr bool B_KC = KIND == K_GATEUP_FWD || KIND == K_DOWN_FWD || KIND == K_WGRAD8;
 };
 
 // LDS layouts of the tiles (swizzles, DMA placement, fragment offsets):
@@ -492,6 +498,35 @@ __device__ __forceinline__ void load_scales(const GemmArgs& p, int e, int nt, in
                                             int row1, int wave, int lane, Scales<KIND, C>& S) {
   constexpr int MI = C::MI, WM = C::WM;
   const int wm = wave >> 1, wn = wave & 1;
+  if constexpr (KIND == K_WGRAD8) {
+    // row0 = the tile's first output row m0: the group's A scales of the rows
+    // the epilogue visits (past M: zero, never stored), and the B scales of
+    // the lane's columns 4 (lane % 16) .. + 3 and 64 more
+    const out_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(p.sa) + (long)e * p.sa_group_stride + row0, 0, (p.M - row0) * 4, 0x00020000);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int lrow = wm * WM + mi * 32 + 16 * h + it * 4 + (lane >> 4);
+          S.row[(mi * 2 + h) * 4 + it] =
+              __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rr, lrow * 4, 0, 0));
+        }
+    const int n = n0 + wn * WN + (lane & 15) * 4;
+    const out_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(p.sb0) + (long)e * p.sb_group_stride, 0, p.N * 4, 0x00020000);
+    const u32x4_t c0 = __builtin_amdgcn_raw_buffer_load_b128(rc, n < p.N ? (uint32_t)n * 4 : kOutKill, 0, 0);
+    const u32x4_t c1 =
+        __builtin_amdgcn_raw_buffer_load_b128(rc, n + 64 < p.N ? (uint32_t)(n + 64) * 4 : kOutKill, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      S.col[i] = __uint_as_float(c0[i]);
+      S.col[4 + i] = __uint_as_float(c1[i]);
+    }
+    return;
+  }
   // rows [row0, row1) of the row scales; the ones past row1 read as zero
   const out_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.sa) + row0, 0,
                                                           (row1 - row0) * 4, 0x00020000);
@@ -656,6 +691,49 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
           const float4 o0 = d4[0], o1 = d4[1];
           d4[0] = make_float4(o0.x + v[0], o0.y + v[1], o0.z + v[2], o0.w + v[3]);
           d4[1] = make_float4(o1.x + v[4], o1.y + v[5], o1.z + v[6], o1.w + v[7]);
+        }
+        // the next half reuses the staging area
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      }
+  } else if constexpr (KIND == K_WGRAD8) {
+    // FP8 weight gradient: the sum of the code products times the group's row
+    // scale of A and column scale of B (powers of two: exact), then the same
+    // stores as the bf16 overwrite above (rows past M dropped by the range
+    // check, columns past N by the kill offset); accumulate reads the old
+    // value through the same descriptor and adds it first.
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        stage_half(st, acc, mi, h, lane);
+        const int mb = m0 + wm * WM + mi * 32 + 16 * h;
+        const bool first = mb < p.m_split || p.f1 == nullptr;
+        float* base = (first ? p.f0 : p.f1) + e * p.f_group_stride;
+        const int mrel = first ? mb : mb - p.m_split;
+        const int nrows = (first ? min(p.m_split, p.M) : p.M - p.m_split) - mrel;
+        const out_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+            base + (long)max(mrel, 0) * p.ldc, 0, nrows > 0 ? (int)(nrows * p.ldc * 4) : 0, 0x00020000);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int r = it * 4 + (lane >> 4);
+          const int c = (lane & 15) * 4;
+          const int n = n0 + wn * WN + c;
+          f32x4_t a = *reinterpret_cast<const f32x4_t*>(&st[stage_idx(r, c)]);
+          f32x4_t b = *reinterpret_cast<const f32x4_t*>(&st[stage_idx(r, c + 64)]);
+          const float sr = S.row[(mi * 2 + h) * 4 + it];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            a[j] *= sr * S.col[j];
+            b[j] *= sr * S.col[4 + j];
+          }
+          const uint32_t oa = n < p.N ? (uint32_t)((r * p.ldc + n) * 4) : kOutKill;
+          const uint32_t ob = n + 64 < p.N ? (uint32_t)((r * p.ldc + n + 64) * 4) : kOutKill;
+          if (p.accumulate != 0) {  // uniform
+            a = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, oa, 0, 0)) + a;
+            b = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, ob, 0, 0)) + b;
+          }
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, a), ro, oa, 0, kCpolNT);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, b), ro, ob, 0, kCpolNT);
         }
         // the next half reuses the staging area
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -883,6 +961,8 @@ __device__ __forceinline__ void k_steps_f8(f32x16_t (&acc)[C::MI][NI], Frags8<C>
 // epilogue) waits past exactly these.
 template <int KIND, class C, bool F8 = false>
 __host__ __device__ constexpr int epilogue_vmem_ops() {
+  // WGRAD8: not counted (the plain wait)
+  if (KIND == K_WGRAD8) return -1;
   // FP8: the next tile's scale loads follow the epilogue (rows, then columns
   // four at a time)
   return (F8 ? Scales<KIND, C>::NR + Scales<KIND, C>::NC / 4 : 0) +
@@ -903,7 +983,17 @@ template <int KIND, class C>
 __device__ __forceinline__ Tile decode_tile(const GemmArgs& p, int work) {
   constexpr int BM = C::BM;
   int e, nt, row0 = 0, row1 = 0, m0 = 0, kbeg = 0, kend = 0;
-  if constexpr (KIND == K_WGRAD) {
+  if constexpr (KIND == K_WGRAD8) {
+    // K = the group's padded code columns [offsets[e], offsets[e + 1]), two
+    // codes per bf16 slot; row0 carries m0 for the scale loads
+    e = work / (p.n_mtiles * p.n_ntiles);
+    const int rem = work - e * p.n_mtiles * p.n_ntiles;
+    m0 = (rem / p.n_ntiles) * BM;
+    nt = rem % p.n_ntiles;
+    kbeg = p.offsets[e] >> 1;
+    kend = p.offsets[e + 1] >> 1;
+    row0 = m0;
+  } else if constexpr (KIND == K_WGRAD) {
     e = work / (p.n_mtiles * p.n_ntiles);
     const int rem = work - e * p.n_mtiles * p.n_ntiles;
     m0 = (rem / p.n_ntiles) * BM;
@@ -954,6 +1044,28 @@ __device__ __forceinline__ void setup_operands(const GemmArgs& p, const Tile& t,
   constexpr int BM = C::BM, NIA = C::NIA;
   const int e = t.e, nt = t.nt, n0 = t.n0, row0 = t.row0, row1 = t.row1, m0 = t.m0;
   const int kbeg = t.kbeg, kend = t.kend;
+  if constexpr (KIND == K_WGRAD8) {
+    // A: code rows m0 .. of [M][lda slots], B: code rows n0 .. of [N][ldb],
+    // both from slot kbeg on (the group's padded columns, zeros past its
+    // rows); rows past M / N lie past the ranges and read as zero
+    opA.rsrc = make_rsrc(p.a + (long)m0 * p.lda + kbeg, (uint32_t)(((long)(p.M - m0) * p.lda - kbeg) * 2));
+    opA.kstep = 2;
+#pragma unroll
+    for (int u = 0; u < NIA; ++u) {
+      int r, c;
+      kc_rows<NIA>(wave, lane, u, r, c);
+      opA.voff[u] = (uint32_t)(r * p.lda * 2 + c * 16);
+    }
+    opB.rsrc = make_rsrc(p.b0 + (long)n0 * p.ldb + kbeg, (uint32_t)(((long)(p.N - n0) * p.ldb - kbeg) * 2));
+    opB.kstep = 2;
+#pragma unroll
+    for (int u = 0; u < NIB; ++u) {
+      int r, c;
+      kc_rows<NIB>(wave, lane, u, r, c);
+      opB.voff[u] = (uint32_t)(r * p.ldb * 2 + c * 16);
+    }
+    return;
+  }
   if constexpr (Tr::A_KC) {
     // the tile's rows [row0, row1) of A; rows past row1 read as zero
     opA.rsrc = make_rsrc(p.a + (long)row0 * p.lda, (uint32_t)((row1 - row0) * p.lda * 2));
@@ -1045,7 +1157,9 @@ template <int KIND, int BM_, bool F8 = false>
 __global__ __launch_bounds__(NTH)
 __attribute__((amdgpu_waves_per_eu(Cfg<BM_>::kWavesPerSimd, Cfg<BM_>::kWavesPerSimd)))
 void gemm_kernel(const GemmArgs p) {
-  static_assert(!F8 || KIND == K_GATEUP_FWD || KIND == K_DOWN_FWD, "FP8: K-contiguous products only");
+  static_assert(!F8 || KIND == K_GATEUP_FWD || KIND == K_DOWN_FWD || KIND == K_WGRAD8,
+                "FP8: K-contiguous products only");
+  static_assert(KIND != K_WGRAD8 || F8, "WGRAD8 runs on E4M3 codes");
   using Tr = Traits<KIND>;
   using C = Cfg<BM_>;
   constexpr int WM = C::WM, MI = C::MI, NST = C::NST, NIA = C::NIA;
@@ -1058,7 +1172,7 @@ void gemm_kernel(const GemmArgs p) {
   const FragLanes L = frag_lanes<C>(lane, wave);
 
   int total;
-  if constexpr (KIND == K_WGRAD)
+  if constexpr (k_grouped(KIND))
     total = p.groups * p.n_mtiles * p.n_ntiles;
   else
     total = p.sched[0] * p.n_ntiles;
@@ -1496,6 +1610,116 @@ hipError_t launch_ffn_dgrad_fp8(const uint8_t* dy_q, const float* dy_scale, cons
   x.sb0 = wgut_s;
   x.sb_group_stride = H;
   return launch_gemm<K_DOWN_FWD, kBmGrouped, true>(x, mt_upper * x.n_ntiles, MOE_KERNEL_FFN_GATEUP_DGRAD, s);
+}
+
+// FP8 weight gradients of the expert FFN: the four operands' columns are
+// quantized per (expert, column) into transposed code matrices whose rows
+// hold each expert's rows at a padded offset (a multiple of 64 codes, zeros
+// past its rows), so that both operands of every product are K-contiguous
+// and each expert's K range is whole 64-code steps:
+//   dW_gate | dW_up  [2I, H] per expert = codes of [dg | du]^T x codes of x^T
+//   dW_down          [H, I]  per expert = codes of dy^T x codes of h^T
+int wgrad_fp8_pitch(int R_cap, int E_l) { return ((R_cap + 63) & ~63) + 64 * E_l; }
+
+static size_t wgrad_fp8_codes_bytes(int R_cap, int E_l, int C) {
+  return align256((size_t)wgrad_fp8_pitch(R_cap, E_l) * C);
+}
+
+size_t ffn_wgrad_fp8_ws_bytes(int R_cap, int E_l, int H, int I) {
+  return wgrad_fp8_codes_bytes(R_cap, E_l, 2 * I) + 2 * wgrad_fp8_codes_bytes(R_cap, E_l, H) +
+         wgrad_fp8_codes_bytes(R_cap, E_l, I) + align256((size_t)E_l * (3 * I + 2 * H) * 4) +
+         align256((size_t)(E_l + 1) * 4) + 256;
+}
+
+hipError_t launch_ffn_wgrad_fp8(const bf16_t* x, const int32_t* src_row, const bf16_t* dgu,
+                                const bf16_t* h_perm, const bf16_t* dy_perm,
+                                const int32_t* offsets, int E_l, int R_cap, int H, int I,
+                                float* dw_gate, float* dw_up, float* dw_down, bool accumulate,
+                                void* ws, hipStream_t s) {
+  const int Kp = wgrad_fp8_pitch(R_cap, E_l);
+  char* w = (char*)ws;
+  uint8_t* q_gu = (uint8_t*)w;
+  w += wgrad_fp8_codes_bytes(R_cap, E_l, 2 * I);
+  uint8_t* q_x = (uint8_t*)w;
+  w += wgrad_fp8_codes_bytes(R_cap, E_l, H);
+  uint8_t* q_dy = (uint8_t*)w;
+  w += wgrad_fp8_codes_bytes(R_cap, E_l, H);
+  uint8_t* q_h = (uint8_t*)w;
+  w += wgrad_fp8_codes_bytes(R_cap, E_l, I);
+  float* s_gu = (float*)w;
+  float* s_x = s_gu + (size_t)E_l * 2 * I;
+  float* s_dy = s_x + (size_t)E_l * H;
+  float* s_h = s_dy + (size_t)E_l * H;
+  w += align256((size_t)E_l * (3 * I + 2 * H) * 4);
+  int32_t* poff = (int32_t*)w;
+  w += align256((size_t)(E_l + 1) * 4);
+  int32_t* ctrs = (int32_t*)w;
+
+  QuantGroupT q{};
+  q.t[0] = {dgu, nullptr, 2L * I, 2 * I, q_gu, s_gu};
+  q.t[1] = {x, src_row, (long)H, H, q_x, s_x};
+  q.t[2] = {dy_perm, nullptr, (long)H, H, q_dy, s_dy};
+  q.t[3] = {h_perm, nullptr, (long)I, I, q_h, s_h};
+  q.nt = 4;
+  q.offsets = offsets;
+  q.E_l = E_l;
+  q.Kp = Kp;
+  q.poff = poff;
+  q.ctrs = ctrs;
+  q.nctrs = 2;
+  hipError_t err = launch_quantize_group_t_fp8(q, s);
+  if (err != hipSuccess) return err;
+
+  // E4M3 rows of Kp codes run through the ring as rows of Kp / 2 bf16 slots.
+  GemmArgs g{};
+  g.a = (const bf16_t*)q_gu;
+  g.lda = Kp / 2;
+  g.b0 = (const bf16_t*)q_x;
+  g.ldb = Kp / 2;
+  g.offsets = poff;
+  g.groups = E_l;
+  g.M = 2 * I;
+  g.N = H;
+  g.n_mtiles = (2 * I + kBmWgrad - 1) / kBmWgrad;
+  g.n_ntiles = (H + BN - 1) / BN;
+  g.f0 = dw_gate;
+  g.f1 = dw_up;
+  g.m_split = I;
+  g.ldc = H;
+  g.f_group_stride = (long)I * H;
+  g.accumulate = accumulate ? 1 : 0;
+  g.sa = s_gu;
+  g.sa_group_stride = 2 * I;
+  g.sb0 = s_x;
+  g.sb_group_stride = H;
+  g.tile_ctr = ctrs;
+  err = launch_gemm<K_WGRAD8, kBmWgrad, true>(g, E_l * g.n_mtiles * g.n_ntiles,
+                                              MOE_KERNEL_FFN_GATEUP_WGRAD, s);
+  if (err != hipSuccess) return err;
+
+  GemmArgs d{};
+  d.a = (const bf16_t*)q_dy;
+  d.lda = Kp / 2;
+  d.b0 = (const bf16_t*)q_h;
+  d.ldb = Kp / 2;
+  d.offsets = poff;
+  d.groups = E_l;
+  d.M = H;
+  d.N = I;
+  d.n_mtiles = (H + kBmWgrad - 1) / kBmWgrad;
+  d.n_ntiles = (I + BN - 1) / BN;
+  d.f0 = dw_down;
+  d.m_split = H;
+  d.ldc = I;
+  d.f_group_stride = (long)H * I;
+  d.accumulate = accumulate ? 1 : 0;
+  d.sa = s_dy;
+  d.sa_group_stride = H;
+  d.sb0 = s_h;
+  d.sb_group_stride = I;
+  d.tile_ctr = ctrs + 1;
+  return launch_gemm<K_WGRAD8, kBmWgrad, true>(d, E_l * d.n_mtiles * d.n_ntiles,
+                                               MOE_KERNEL_FFN_DOWN_WGRAD, s);
 }
 
 // A second stream of the calling device for products that may run beside

@@ -50,7 +50,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_single_hip_runtime():
-    assert L.moe_abi_version() == moe.ABI_VERSION == 5
+    assert L.moe_abi_version() == moe.ABI_VERSION == 6
     libs = moe.hip_runtimes_mapped()
     assert len(libs) <= 1, libs
 
@@ -221,6 +221,44 @@ def test_fp8_dgrad_entry_points_errors():
     assert n >= 8192 * 8 * (768 * 2 + 2 * 768 + 4)                            # dh, codes, scales
     assert ws(moe.MOE_OP_FFN_DGRAD_FP8, 8192, 2048, 768, 128, 8, 0, 16, FP8) == n
 
+
+
+def test_fp8_wgrad_entry_points_errors():
+    """Argument errors of the FP8 weight gradients and their column quantizer (every
+    case fails on the host; none launches)."""
+    q = lambda *a: L.moe_quantize_fp8_group_t(*a)
+    pitch = moe.wgrad_fp8_pitch(4096, 16)
+    qa = lambda C=2048, El=16, R=4096, p=pitch, src=A, off=A, qq=A, sc=A, po=A: (
+        src, N, C, off, El, R, qq, p, sc, po, S)
+    assert q(*qa(C=2000)) == EINVAL and "64" in _err()
+    assert q(*qa(El=0)) == EINVAL
+    assert q(*qa(El=300)) == EINVAL
+    assert q(*qa(R=-1)) == EINVAL
+    assert q(*qa(p=pitch - 64)) == EINVAL and "q_pitch" in _err()
+    assert q(*qa(p=pitch + 1)) == EINVAL and "q_pitch" in _err()
+    assert q(*qa(off=N)) == EINVAL and "offsets" in _err()
+    assert q(*qa(qq=U)) == EINVAL and "q" in _err()
+    assert q(*qa(po=N)) == EINVAL and "poff" in _err()
+    assert q(*qa(src=U)) == EINVAL and "src" in _err()
+    w = lambda *a: L.moe_grouped_ffn_wgrad_fp8(*a)
+    big = 1 << 31
+    wa = lambda H=2048, I=768, El=16, R=4096, ws=big, x=A, dgu=A, dwg=A, dwd=A, off=A: (
+        x, A, dgu, A, A, off, El, R, H, I, dwg, A, dwd, 0, A, ws, S)
+    assert w(*wa(I=704)) == EUNSUP and "128" in _err()
+    assert w(*wa(H=1984)) == EUNSUP
+    assert w(*wa(El=0)) == EINVAL
+    assert w(*wa(off=N)) == EINVAL and "offsets" in _err()
+    assert w(*wa(dwg=N)) == EINVAL and "dw_gate" in _err()
+    assert w(*wa(dwd=U)) == EINVAL and "dw_down" in _err()
+    assert w(*wa(x=N)) == EINVAL and "x" in _err()
+    assert w(*wa(dgu=U)) == EINVAL and "dgu" in _err()
+    assert w(*wa(ws=8)) == EWS
+    # a transposed code matrix of 2 GiB or more is refused
+    assert w(*wa(H=16384, R=131072)) == EUNSUP and "2 GiB" in _err()
+    ws = lambda *a: L.moe_workspace_bytes(*a)
+    n = ws(moe.MOE_OP_FFN_WGRAD_FP8, 4096, 2048, 768, 128, 4, 0, 16, BF16)
+    assert n >= pitch * (2 * 768 + 2 * 2048 + 768) + 16 * (3 * 768 + 2 * 2048) * 4   # codes, scales
+    assert ws(moe.MOE_OP_FFN_WGRAD_FP8, 4096, 2048, 768, 128, 4, 0, 16, FP8) == n
 
 def test_ffn_bwd_split_needs_a_second_stream():
     f = lambda *a: L.moe_grouped_ffn_bwd_split(*a)

@@ -121,14 +121,16 @@ class Fifo:
 
 
 # gemm_kernel<KIND, BM, FP8>: KIND 0 gate/up, 1 down, 2 down data gradient,
-# 3 gate/up data gradient, 4 weight gradient.  Per-lane vector memory
-# instructions of one epilogue, as the kernel counts them (stores per 16-row
-# half pass, times 2 MI passes), and the FP8 scale loads of the next tile.
+# 3 gate/up data gradient, 4 weight gradient, 5 FP8 weight gradient.  Per-lane
+# vector memory instructions of one epilogue, as the kernel counts them (stores
+# per 16-row half pass, times 2 MI passes), and the FP8 scale loads of the next
+# tile.  The FP8 weight gradient does not count its epilogue (None): its first
+# wait after a tile change is the plain one.
 def _design(kind, bm, fp8):
     mi = bm // 64
     nst = 4 if bm == 256 else 3
     nia, nib = bm * 32 * 2 // 4096, 4
-    epi = {0: 12 * mi, 1: 8 * mi, 2: 32 * mi, 3: 8 * mi, 4: 16 * mi}[kind]
+    epi = {0: 12 * mi, 1: 8 * mi, 2: 32 * mi, 3: 8 * mi, 4: 16 * mi, 5: None}[kind]
     scales = 0
     if fp8:
         nr = 4 * mi if kind == 0 else 8 * mi
@@ -139,6 +141,7 @@ def _design(kind, bm, fp8):
 
 GEMM_KERNELS = [(0, 256, False), (1, 256, False), (2, 256, False), (3, 256, False), (4, 256, False),
                 (4, 128, False), (0, 256, True), (1, 256, True)]
+GEMM_KERNELS_ALL = GEMM_KERNELS + [(5, 256, True)]
 
 
 def _gemm_body(gemm_asm, kind, bm, fp8):
@@ -168,7 +171,7 @@ def test_gemm_epilogue_memory_ops_match_the_wait(gemm_asm, kind, bm, fp8):
         assert _events(body).count(0) <= ref, (_events(body).count(0), ref)
 
 
-@pytest.mark.parametrize("kind,bm,fp8", GEMM_KERNELS, ids=lambda v: str(v))
+@pytest.mark.parametrize("kind,bm,fp8", GEMM_KERNELS_ALL, ids=lambda v: str(v))
 def test_gemm_ring_waits_are_correct_and_tight(gemm_asm, kind, bm, fp8):
     """Replays the ring: prologue, K steps, epilogue + next prologue, next K steps,
     with the DMA counts and wait values taken from the compiled kernel."""
@@ -182,7 +185,8 @@ def test_gemm_ring_waits_are_correct_and_tight(gemm_asm, kind, bm, fp8):
     k_first = (nst - 2) * nd + nd // 2
     k_loop = (nst - 2) * nd
     assert k_first in waits and k_loop in waits, (waits, k_first, k_loop)
-    k_epi = d["epi"] + d["scales"]
+    plain_after = d["epi"] is None
+    k_epi = 0 if plain_after else d["epi"] + d["scales"]
     k_after = min(VMCNT_MAX, k_first + k_epi)
     if d["sep"]:
         assert k_after in waits, (waits, k_after)
@@ -225,7 +229,14 @@ def test_gemm_ring_waits_are_correct_and_tight(gemm_asm, kind, bm, fp8):
     probe.wait(k_first + 1)
     assert probe.pending((0, 0)), "first wait not tight"
     # tile change: next prologue, then this tile's epilogue (and FP8 scales)
-    if d["sep"]:
+    if d["sep"] and plain_after:
+        # an uncounted epilogue of any size: the plain wait is still correct
+        for n_epi in (0, 7, 40, 100):
+            g = Fifo()
+            prologue(g, 1)
+            g.issue("epilogue", n_epi)
+            k_loop_steps(g, 1, 24, k_first)
+    elif d["sep"]:
         prologue(f, 1)
         f.issue("epilogue", k_epi)
         before = list(f.q)
@@ -241,14 +252,15 @@ def test_gemm_ring_waits_are_correct_and_tight(gemm_asm, kind, bm, fp8):
         k_loop_steps(f, 1, 24, k_first)
 
 
-@pytest.mark.parametrize("kind,bm", [(2, 256), (3, 256), (4, 256), (4, 128)])
-def test_tile_ticket_latency_stays_hidden(gemm_asm, kind, bm):
+@pytest.mark.parametrize("kind,bm,fp8", [(2, 256, False), (3, 256, False), (4, 256, False),
+                                         (4, 128, False), (5, 256, True)])
+def test_tile_ticket_latency_stays_hidden(gemm_asm, kind, bm, fp8):
     """The products that take tiles from a device counter draw the ticket of the
     tile after next with one lane's atomic add and hand the previous ticket to
     the workgroup through LDS.  No wait for all memory operations may follow the
     atomic directly (its result is used one tile later), and the hand-off goes
     through LDS, not a flat store."""
-    body = [l.strip() for l in _gemm_body(gemm_asm, kind, bm, False)]
+    body = [l.strip() for l in _gemm_body(gemm_asm, kind, bm, fp8)]
     code = [l for l in body if l and not l.startswith(";") and not l.startswith(".")]
     at = [i for i, l in enumerate(code) if l.startswith("global_atomic_add")]
     assert at, "no ticket atomic"
