@@ -452,6 +452,49 @@ def secondary_forward(w, args, moe, torch):
             "tokens_per_s": round(w.T / (ms * 1e-3), 1), "routed_rows": R, "roofline": roof}
 
 
+def fp8_step(w, t, bias, args, moe, torch):
+    """The same training step with the expert FFN in the FP8 recipe (MoELayer with
+    fp8=True: token, weight, dy and [dg | du] quantization included in the step),
+    graph-replayed on the same inputs; checked bit for bit against its eager run."""
+    dev = torch.device("cuda:0")
+    layer = moe.MoELayer(w.T, w.H, w.I, w.E, w.k, w.e_lo, w.e_hi, torch.bfloat16, dev, train=True,
+                         fp8=True)
+
+    def step():
+        layer.forward(t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"], bias=bias)
+        layer.backward(t["dy"], t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"])
+
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    ref = layer.buf["dx"].clone()
+    R = int(layer.buf["offsets"][-1].item())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    g.replay()
+    torch.cuda.synchronize()
+    same = torch.equal(layer.buf["dx"].view(torch.int16), ref.view(torch.int16))
+    run = g.replay if same else step
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = step_flops(w, R)
+    out = {"workload": w.name, "pass": "forward+backward", "ffn": "fp8 e4m3 (per-row / per-channel "
+           "power-of-two scales), router and combine bf16", "timing": "hip-graph replay" if same else
+           "eager launches", "steps": args.steps, "ms_per_step": round(ms, 4),
+           "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "tokens_per_s": round(w.T / (ms * 1e-3), 1),
+           "routed_rows": R}
+    del layer, g
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -465,6 +508,10 @@ def main():
                     help="skip the forward of the full 128-expert layer timed after the main step")
     ap.add_argument("--no-step-stats", action="store_true",
                     help="skip the per-step warm / cold (cache-flushed) timing pass")
+    ap.add_argument("--fp8", action="store_true",
+                    help="run the layer with the FP8 expert FFN (MoELayer(fp8=True)) as the main step")
+    ap.add_argument("--no-fp8-step", action="store_true",
+                    help="skip the training step with the FP8 expert FFN timed after the main step")
     ap.add_argument("--fp8-ffn", action="store_true",
                     help="instead of the layer step: time the grouped FFN forward in bf16 and in the "
                          "FP8 recipe on the same routing (default workload: the full 128-expert layer)")
@@ -496,7 +543,10 @@ def main():
     inp = make_inputs(w)
     t = {n: torch.from_numpy(v).to(dev).to(dt).contiguous() for n, v in inp.items() if n != "bias"}
     bias = torch.from_numpy(inp["bias"]).to(dev) if "bias" in inp else None
-    layer = moe.MoELayer(w.T, w.H, w.I, w.E, w.k, w.e_lo, w.e_hi, dt, dev, train=w.train)
+    if args.fp8 and w.dtype != "bf16":
+        print("--fp8 needs a bf16 workload", file=sys.stderr)
+        sys.exit(2)
+    layer = moe.MoELayer(w.T, w.H, w.I, w.E, w.k, w.e_lo, w.e_hi, dt, dev, train=w.train, fp8=args.fp8)
 
     def step():
         layer.forward(t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"], bias=bias)
@@ -543,13 +593,15 @@ def main():
 
     flops = step_flops(w, R)
     result = {
-        "metric": METRIC if w.train else METRIC.replace("fwd+bwd", "fwd"),
+        "metric": (METRIC if w.train else METRIC.replace("fwd+bwd", "fwd")).replace(
+            "bf16", "FP8 expert FFN" if args.fp8 else "bf16"),
         "value": round(flops / (ms * 1e-3) / 1e12, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "dtype": ("fp8-e4m3 expert FFN, bf16 router/combine" if args.fp8 else "bf16")
+                 if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded normal draws, random-init weights)",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "I": w.I, "E": w.E, "k": w.k,
                    "local_experts": [w.e_lo, w.e_hi], "routed_rows": R,
@@ -577,7 +629,16 @@ def main():
     if not args.no_secondary and w.name != SECONDARY_WORKLOAD:
         del layer, graph
         torch.cuda.empty_cache()
+        layer = graph = None
         result["secondary"] = secondary_forward(WORKLOADS[SECONDARY_WORKLOAD], args, moe, torch)
+
+    if not args.no_fp8_step and not args.fp8 and w.train and w.dtype == "bf16":
+        del layer, graph
+        torch.cuda.empty_cache()
+        layer = graph = None
+        fp = fp8_step(w, t, bias, args, moe, torch)
+        fp["vs_bf16_step"] = round(ms / fp["ms_per_step"], 3)
+        result["fp8_step"] = fp
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp)

@@ -11,6 +11,13 @@ router backward run on a second stream (default priority) beside the data
 gradients and the input-gradient pass; each concurrent call has its own
 workspace, and the current stream waits for the second one before
 backward() returns.
+
+With fp8=True the expert FFN runs the library's FP8 recipe (E4M3 codes with
+power-of-two scales): tokens are quantized per row before the permute (which
+then moves code rows), the weights per output channel (forward) and per input
+channel (data gradients) on every call, the rows of dy_perm per row, and the
+weight gradients quantize their operands per (expert, column).  Routing,
+combine and the router backward stay as in the bf16 layer.
 """
 from __future__ import annotations
 
@@ -19,8 +26,9 @@ from typing import Dict, Optional
 
 import torch
 
-from . import (MOE_BF16, MOE_F32, MOE_OP_FFN_BWD, MOE_OP_FFN_FWD, MOE_OP_PERMUTE,
-               MOE_OP_ROUTE, MOE_OP_ROUTE_BWD, _check, _stream, lib, workspace_bytes)
+from . import (MOE_BF16, MOE_F32, MOE_FP8, MOE_OP_FFN_BWD, MOE_OP_FFN_DGRAD_FP8, MOE_OP_FFN_FWD,
+               MOE_OP_FFN_FWD_FP8, MOE_OP_FFN_WGRAD_FP8, MOE_OP_PERMUTE, MOE_OP_ROUTE,
+               MOE_OP_ROUTE_BWD, _check, _stream, lib, workspace_bytes)
 
 
 def _p(t: Optional[torch.Tensor]):
@@ -29,7 +37,11 @@ def _p(t: Optional[torch.Tensor]):
 
 class MoELayer:
     def __init__(self, T: int, H: int, I: int, E: int, k: int, e_lo: int, e_hi: int,
-                 dtype: torch.dtype, device="cuda", train: bool = True):
+                 dtype: torch.dtype, device="cuda", train: bool = True, fp8: bool = False):
+        if fp8 and (dtype != torch.bfloat16 or H % 128 or I % 128 or I > 2048):
+            raise ValueError("the FP8 layer needs bf16 tensors, H % 128 == 0, I % 128 == 0 "
+                             "and I <= 2048")
+        self.fp8 = fp8
         self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
         self.e_lo, self.e_hi, self.E_l = e_lo, e_hi, e_hi - e_lo
         self.dtype = dtype
@@ -47,7 +59,8 @@ class MoELayer:
         b["offsets"] = torch.empty(E_l + 1, dtype=i32, device=dev)
         b["dest_row"] = torch.empty(T * k, dtype=i32, device=dev)
         b["src_row"] = torch.empty(T * k, dtype=i32, device=dev)
-        b["x_perm"] = torch.empty((R, H), dtype=dtype, device=dev)
+        # (FP8: the permute moves code rows, so bf16 x_perm is not materialised)
+        b["x_perm"] = None if fp8 else torch.empty((R, H), dtype=dtype, device=dev)
         b["h_perm"] = torch.empty((R, I), dtype=dtype, device=dev)
         b["y_perm"] = torch.empty((R, H), dtype=dtype, device=dev)
         b["gu"] = torch.empty((R, 2 * I), dtype=dtype, device=dev) if train else None
@@ -63,10 +76,31 @@ class MoELayer:
             b["dw_down"] = torch.empty((E_l, H, I), dtype=f32, device=dev)
             b["dx"] = torch.empty((T, H), dtype=dtype, device=dev)
             b["w_router_t"] = torch.empty((E, H), dtype=dtype, device=dev)
+        if fp8:
+            u8 = torch.uint8
+            b["x_q"] = torch.empty((T, H), dtype=u8, device=dev)
+            b["x_scale"] = torch.empty(T, dtype=f32, device=dev)
+            b["xq_perm"] = torch.empty((R, H), dtype=u8, device=dev)
+            b["wg_q"] = torch.empty((E_l, I, H), dtype=u8, device=dev)
+            b["wu_q"] = torch.empty((E_l, I, H), dtype=u8, device=dev)
+            b["wd_q"] = torch.empty((E_l, H, I), dtype=u8, device=dev)
+            b["wg_s"] = torch.empty((E_l, I), dtype=f32, device=dev)
+            b["wu_s"] = torch.empty((E_l, I), dtype=f32, device=dev)
+            b["wd_s"] = torch.empty((E_l, H), dtype=f32, device=dev)
+            if train:
+                b["dy_q"] = torch.empty((R, H), dtype=u8, device=dev)
+                b["dy_scale"] = torch.empty(R, dtype=f32, device=dev)
+                b["wdt_q"] = torch.empty((E_l, I, H), dtype=u8, device=dev)
+                b["wdt_s"] = torch.empty((E_l, I), dtype=f32, device=dev)
+                b["wgut_q"] = torch.empty((E_l, H, 2 * I), dtype=u8, device=dev)
+                b["wgut_s"] = torch.empty((E_l, H), dtype=f32, device=dev)
+                b["dgu"] = torch.empty((R, 2 * I), dtype=dtype, device=dev)
         self.buf = b
-        ops = [MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN_FWD]
+        ops = [MOE_OP_ROUTE, MOE_OP_PERMUTE]
+        ops += [MOE_OP_FFN_FWD_FP8] if fp8 else [MOE_OP_FFN_FWD]
         if train:
-            ops += [MOE_OP_FFN_BWD, MOE_OP_ROUTE_BWD]
+            ops += [MOE_OP_FFN_DGRAD_FP8] if fp8 else [MOE_OP_FFN_BWD]
+            ops += [MOE_OP_ROUTE_BWD]
         nb = max(workspace_bytes(op, T, H, I, E, k, e_lo, e_hi, self.dt) for op in ops)
         # one workspace for the calls that run one after another on the current
         # stream; the backward's concurrent calls get their own
@@ -76,6 +110,7 @@ class MoELayer:
             ws = lambda op: torch.empty(max(workspace_bytes(op, T, H, I, E, k, e_lo, e_hi, self.dt), 256),
                                         dtype=torch.uint8, device=dev)
             self.ws_rb = ws(MOE_OP_ROUTE_BWD)
+            self.ws_w8 = ws(MOE_OP_FFN_WGRAD_FP8) if fp8 else None
             self.side = torch.cuda.Stream(device=dev) if dev.type == "cuda" else None
 
     def forward(self, x, w_router, w_gate, w_up, w_down, bias=None, save_logits=True):
@@ -85,16 +120,63 @@ class MoELayer:
         _check(lib.moe_route(_p(x), _p(w_router), _p(bias), T, H, E, k, self.dt,
                              _p(b["logits"]) if save_logits else None, _p(b["topk_idx"]),
                              _p(b["topk_w"]), ws, wsb, s), "moe_route")
-        _check(lib.moe_permute(_p(x), _p(b["topk_idx"]), T, H, E, k, self.e_lo, self.e_hi, self.dt,
-                               _p(b["counts"]), _p(b["offsets"]), _p(b["dest_row"]),
-                               _p(b["src_row"]), _p(b["x_perm"]), ws, wsb, s), "moe_permute")
-        _check(lib.moe_grouped_ffn_fwd(_p(b["x_perm"]), _p(b["offsets"]), self.E_l, self.R_cap, H, I,
-                                       _p(w_gate), _p(w_up), _p(w_down), self.dt, _p(b["gu"]),
-                                       _p(b["h_perm"]), _p(b["y_perm"]), ws, wsb, s),
-               "moe_grouped_ffn_fwd")
+        if self.fp8:
+            self._forward_ffn_fp8(x, w_gate, w_up, w_down, ws, wsb, s)
+        else:
+            _check(lib.moe_permute(_p(x), _p(b["topk_idx"]), T, H, E, k, self.e_lo, self.e_hi,
+                                   self.dt, _p(b["counts"]), _p(b["offsets"]), _p(b["dest_row"]),
+                                   _p(b["src_row"]), _p(b["x_perm"]), ws, wsb, s), "moe_permute")
+            _check(lib.moe_grouped_ffn_fwd(_p(b["x_perm"]), _p(b["offsets"]), self.E_l, self.R_cap,
+                                           H, I, _p(w_gate), _p(w_up), _p(w_down), self.dt, _p(b["gu"]),
+                                           _p(b["h_perm"]), _p(b["y_perm"]), ws, wsb, s),
+                   "moe_grouped_ffn_fwd")
         _check(lib.moe_combine(_p(b["y_perm"]), _p(b["topk_w"]), _p(b["dest_row"]), None, T, H, k,
                                self.dt, _p(b["y"]), s), "moe_combine")
         return b["y"]
+
+    def _quantize_rows(self, src, rows, cols, q, scale, s, nrows=None):
+        _check(lib.moe_quantize_fp8(_p(src), rows, cols, self.dt, _p(nrows), _p(q), _p(scale), s),
+               "moe_quantize_fp8")
+
+    def _forward_ffn_fp8(self, x, w_gate, w_up, w_down, ws, wsb, s):
+        """Token rows quantized, code rows permuted, weights quantized per output
+        channel, then the FP8 grouped FFN (h, g and u kept in bf16)."""
+        b, T, H, I, E, k, E_l = self.buf, self.T, self.H, self.I, self.E, self.k, self.E_l
+        self._quantize_rows(x, T, H, b["x_q"], b["x_scale"], s)
+        _check(lib.moe_permute(_p(b["x_q"]), _p(b["topk_idx"]), T, H, E, k, self.e_lo, self.e_hi,
+                               MOE_FP8, _p(b["counts"]), _p(b["offsets"]), _p(b["dest_row"]),
+                               _p(b["src_row"]), _p(b["xq_perm"]), ws, wsb, s), "moe_permute")
+        self._quantize_rows(w_gate, E_l * I, H, b["wg_q"], b["wg_s"], s)
+        self._quantize_rows(w_up, E_l * I, H, b["wu_q"], b["wu_s"], s)
+        self._quantize_rows(w_down, E_l * H, I, b["wd_q"], b["wd_s"], s)
+        _check(lib.moe_grouped_ffn_fwd_fp8(_p(b["xq_perm"]), _p(b["x_scale"]), _p(b["src_row"]),
+                                           _p(b["offsets"]), E_l, self.R_cap, H, I, _p(b["wg_q"]),
+                                           _p(b["wg_s"]), _p(b["wu_q"]), _p(b["wu_s"]), _p(b["wd_q"]),
+                                           _p(b["wd_s"]), _p(b["gu"]), _p(b["h_perm"]),
+                                           _p(b["y_perm"]), ws, wsb, s), "moe_grouped_ffn_fwd_fp8")
+
+    def _backward_ffn_fp8(self, x, w_gate, w_up, w_down, ws, wsb, s, side):
+        """dy_perm rows and the weights (per input channel) quantized, the FP8 data
+        gradients on this stream, then the FP8 weight gradients on the side stream."""
+        b, H, I, E_l = self.buf, self.H, self.I, self.E_l
+        self._quantize_rows(b["dy_perm"], self.R_cap, H, b["dy_q"], b["dy_scale"], s,
+                            nrows=b["offsets"][E_l:])
+        _check(lib.moe_quantize_fp8_t(_p(w_down), None, E_l, H, I, self.dt, _p(b["wdt_q"]),
+                                      _p(b["wdt_s"]), s), "moe_quantize_fp8_t")
+        _check(lib.moe_quantize_fp8_t(_p(w_gate), _p(w_up), E_l, I, H, self.dt, _p(b["wgut_q"]),
+                                      _p(b["wgut_s"]), s), "moe_quantize_fp8_t")
+        _check(lib.moe_grouped_ffn_dgrad_fp8(_p(b["dy_q"]), _p(b["dy_scale"]), _p(b["gu"]),
+                                             _p(b["offsets"]), E_l, self.R_cap, H, I, _p(b["wdt_q"]),
+                                             _p(b["wdt_s"]), _p(b["wgut_q"]), _p(b["wgut_s"]),
+                                             _p(b["dgu"]), _p(b["dx_perm"]), ws, wsb, s),
+               "moe_grouped_ffn_dgrad_fp8")
+        # the weight gradients need dgu: the side stream waits for this stream
+        self.side.wait_stream(torch.cuda.current_stream())
+        _check(lib.moe_grouped_ffn_wgrad_fp8(_p(x), _p(b["src_row"]), _p(b["dgu"]), _p(b["h_perm"]),
+                                             _p(b["dy_perm"]), _p(b["offsets"]), E_l, self.R_cap, H, I,
+                                             _p(b["dw_gate"]), _p(b["dw_up"]), _p(b["dw_down"]), 0,
+                                             _p(self.ws_w8), self.ws_w8.numel(), side),
+               "moe_grouped_ffn_wgrad_fp8")
 
     def backward(self, dy, x, w_router, w_gate, w_up, w_down) -> Dict[str, torch.Tensor]:
         if not self.train:
@@ -112,20 +194,23 @@ class MoELayer:
                "moe_combine_bwd")
         main = torch.cuda.current_stream()
         side = ctypes.c_void_p(self.side.cuda_stream)
-        # data gradients on this stream; the weight gradients continue on the side stream
-        _check(lib.moe_grouped_ffn_bwd_split(_p(b["dy_perm"]), _p(b["x_perm"]), _p(b["gu"]),
-                                             _p(b["h_perm"]), _p(b["offsets"]), self.E_l, self.R_cap,
-                                             H, I, _p(w_gate), _p(w_up), _p(w_down), self.dt,
-                                             _p(b["dx_perm"]), _p(b["dw_gate"]), _p(b["dw_up"]),
-                                             _p(b["dw_down"]), 0, ws, wsb, s, side),
-               "moe_grouped_ffn_bwd_split")
+        if self.fp8:
+            self._backward_ffn_fp8(x, w_gate, w_up, w_down, ws, wsb, s, side)
+        else:
+            # data gradients on this stream; the weight gradients continue on the side stream
+            _check(lib.moe_grouped_ffn_bwd_split(_p(b["dy_perm"]), _p(b["x_perm"]), _p(b["gu"]),
+                                                 _p(b["h_perm"]), _p(b["offsets"]), self.E_l,
+                                                 self.R_cap, H, I, _p(w_gate), _p(w_up), _p(w_down),
+                                                 self.dt, _p(b["dx_perm"]), _p(b["dw_gate"]),
+                                                 _p(b["dw_up"]), _p(b["dw_down"]), 0, ws, wsb, s, side),
+                   "moe_grouped_ffn_bwd_split")
         # input gradient: the experts' part and the router's part in one pass
         _check(lib.moe_combine_dx_t(_p(b["dx_perm"]), _p(b["dest_row"]), _p(b["d_topk_w"]),
                                     _p(b["topk_w"]), _p(b["topk_idx"]), _p(b["w_router_t"]), T, H,
                                     E, k, self.dt, _p(b["dx"]), s),
                "moe_combine_dx_t")
         # router backward behind the weight gradients (the side stream already
-        # waits for d_topk_w: the FFN call forked it after the combine backward)
+        # waits for d_topk_w: the FFN backward forked it after the combine backward)
         _check(lib.moe_route_bwd(_p(b["d_topk_w"]), _p(b["topk_w"]), _p(b["topk_idx"]), _p(x),
                                  _p(w_router), T, H, E, k, self.dt, _p(b["d_logits"]),
                                  None, _p(b["dw_router"]), _p(self.ws_rb), self.ws_rb.numel(), side),

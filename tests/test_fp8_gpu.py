@@ -27,7 +27,7 @@ import pytest
 import torch
 
 import oracle as O
-from workloads import EP_SHARE, SKEWED, make_inputs
+from workloads import EP_SHARE, SKEWED, TRAIN, make_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -451,3 +451,75 @@ def test_ffn_wgrad_fp8_matches_oracle(w):
                              np.linalg.norm(got["dw_down"][i] - ex_dn) / np.linalg.norm(ex_dn)))
     print(f"  R={R}: worst |d| / bound {worst:.3f}; vs exact rel-L2 max {max(rel_exact):.3e}", flush=True)
     assert max(rel_exact) < 0.10
+
+
+# ----------------------------------------------------------------------------
+# the layer with fp8=True
+# ----------------------------------------------------------------------------
+
+LAYER_FP8_CASES = [
+    TRAIN.scaled(name="layer_fp8_t512_h256_i128_e32_k4_local4to20", T=512, H=256, I=128, E=32, k=4,
+                 e_lo=4, e_hi=20),
+    TRAIN.scaled(name="layer_fp8_t2048_h2048_i768_e128_k8_local0to16", T=2048),
+]
+
+
+@pytest.mark.parametrize("w", LAYER_FP8_CASES, ids=lambda w: w.name)
+def test_layer_fp8_is_the_call_chain_and_tracks_the_exact_layer(w):
+    """MoELayer(fp8=True): forward and backward equal, bit for bit, the FP8 calls
+    chained by hand (every call is checked against the oracle's FP8 recipe above),
+    and stay within the recipe's quantization error of the exact layer (oracle,
+    fp64): each quantized operand carries a relative rounding error of at most
+    2^-4, so y stays under the forward pin's 0.12 rel-L2, and the gradients,
+    which chain through more quantized operands (dy, dh, [dg | du] and the
+    forward's g, u, h), under 0.2."""
+    inp = make_inputs(w)
+    bf = torch.bfloat16
+    print(f"  case {w.name}", flush=True)
+    t = {n: _dev(inp[n], bf) for n in ("x", "w_router", "w_gate", "w_up", "w_down", "dy")}
+    layer = moe.MoELayer(w.T, w.H, w.I, w.E, w.k, w.e_lo, w.e_hi, bf, DEV, train=True, fp8=True)
+    args = (t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"])
+    y = layer.forward(*args).clone()
+    g = {n: v.clone() for n, v in layer.backward(t["dy"], *args).items()}
+    torch.cuda.synchronize()
+    # the same chain, call by call
+    E_l = w.E_l
+    idx, tw, _ = moe.moe_route(t["x"], t["w_router"], w.k)
+    xq, sx = moe.moe_quantize_fp8(t["x"])
+    perm = moe.moe_permute(xq, idx, w.E, w.e_lo, w.e_hi)
+    wq = {}
+    for n in ("w_gate", "w_up", "w_down"):
+        El, N, K = t[n].shape
+        q, s = moe.moe_quantize_fp8(t[n].view(El * N, K))
+        wq[n] = (q.view(El, N, K), s.view(El, N))
+    f = moe.moe_grouped_ffn_fwd_fp8(perm["x_perm"], sx, perm["src_row"], perm["offsets"], wq["w_gate"],
+                                    wq["w_up"], wq["w_down"], save_gu=True)
+    y2 = moe.moe_combine(f["y_perm"], tw, perm["dest_row"], w.T)
+    cb = moe.moe_combine_bwd(t["dy"], f["y_perm"], tw, perm["dest_row"])
+    dyq, sdy = moe.moe_quantize_fp8(cb["dy_perm"], nrows=perm["offsets"][E_l:])
+    d = moe.moe_grouped_ffn_dgrad_fp8(dyq, sdy, f["gu"], perm["offsets"], moe.moe_quantize_fp8_t(t["w_down"]),
+                                      moe.moe_quantize_fp8_t(t["w_gate"], t["w_up"]))
+    wgr = moe.moe_grouped_ffn_wgrad_fp8(t["x"], perm["src_row"], d["dgu"], f["h_perm"], cb["dy_perm"],
+                                        perm["offsets"], E_l)
+    dx2 = moe.moe_combine_dx_t(d["dx_perm"], perm["dest_row"], cb["d_topk_w"], tw, idx,
+                               moe.moe_router_weight_t(t["w_router"]))
+    rb = moe.moe_route_bwd(cb["d_topk_w"], tw, idx, t["x"], t["w_router"], want_dx=False)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    assert torch.equal(g["dx"], dx2)
+    assert torch.equal(g["d_topk_w"], cb["d_topk_w"])
+    for n in ("dw_gate", "dw_up", "dw_down"):
+        assert torch.equal(g[n], wgr[n]), n
+    assert torch.equal(g["d_logits"], rb["d_logits"]) and torch.equal(g["dw_router"], rb["dw_router"])
+    # against the exact layer
+    _, idx_o, gw = O.route(inp["x"], inp["w_router"], w.k)
+    ref_y = O.moe_forward(inp["x"], idx_o, gw, inp["w_gate"], inp["w_up"], inp["w_down"], w.e_lo, w.e_hi)
+    ref = O.moe_backward(inp["x"], inp["w_router"], idx_o, gw, inp["w_gate"], inp["w_up"], inp["w_down"],
+                         inp["dy"], w.e_lo, w.e_hi)
+    rel = lambda a, b: float(np.linalg.norm(_np(a) - b) / max(np.linalg.norm(b), 1e-30))
+    r = {"y": rel(y, ref_y), "dx": rel(g["dx"], ref["dx"]), "dw_gate": rel(g["dw_gate"], ref["dw_gate"]),
+         "dw_up": rel(g["dw_up"], ref["dw_up"]), "dw_down": rel(g["dw_down"], ref["dw_down"]),
+         "d_logits": rel(g["d_logits"], ref["d_logits"]), "dw_router": rel(g["dw_router"], ref["dw_router"])}
+    print("  rel-L2 vs the exact layer: " + ", ".join(f"{n} {v:.3e}" for n, v in r.items()), flush=True)
+    assert r["y"] < 0.12
+    assert all(v < 0.2 for n, v in r.items() if n != "y")
