@@ -76,7 +76,8 @@ typedef enum {
   MOE_OP_COMBINE_DX = 5,
   MOE_OP_FFN_FWD_FP8 = 6,
   MOE_OP_FFN_DGRAD_FP8 = 7,
-  MOE_OP_FFN_WGRAD_FP8 = 8
+  MOE_OP_FFN_WGRAD_FP8 = 8,
+  MOE_OP_QUANTIZE_W_FP8 = 9
 } moe_op;
 
 /* Returns MOE_ABI_VERSION of the loaded library. */
@@ -215,6 +216,22 @@ int moe_grouped_ffn_fwd_fp8(const uint8_t* x_q, const float* x_scale, const int3
  * aligned. */
 int moe_quantize_fp8_t(const void* src0, const void* src1, int batch, int N, int K, int dtype,
                        uint8_t* q, float* scale, void* stream);
+
+/* Both FP8 code layouts of expert weights from one pair of passes: with w0
+ * (and w1, or NULL) [batch,N,K] bf16,
+ *   q0 / s0 (q1 / s1): the rows of w0 (w1) quantized as moe_quantize_fp8 does
+ *                      ([batch,N,K] codes, [batch,N] scales; forward operands),
+ *   qt / st          : the rows of [w0^T | w1^T] quantized as moe_quantize_fp8_t
+ *                      does ([batch,K,n*N] codes, [batch,K] scales; operands of
+ *                      the data gradients), skipped when qt is NULL;
+ * bit for bit the results of those two calls.  ws: MOE_OP_QUANTIZE_W_FP8
+ * workspace (the per-tile maxima), sized for the gate/up pair (batch = E_l,
+ * N = I, K = H, two sources), which also covers W_down alone.
+ * N % 128 == 0 and K % 128 == 0 (else MOE_EUNSUPPORTED); dtype MOE_BF16;
+ * pointers 16-byte aligned. */
+int moe_quantize_fp8_w(const void* w0, const void* w1, int batch, int N, int K, int dtype,
+                       uint8_t* q0, float* s0, uint8_t* q1, float* s1, uint8_t* qt, float* st,
+                       void* ws, size_t ws_bytes, void* stream);
 
 /* Data gradients of the grouped SwiGLU FFN on E4M3 codes (the weight
  * gradients: moe_grouped_ffn_wgrad_fp8, or moe_grouped_ffn_bwd in bf16).  With dy_q / dy_scale the

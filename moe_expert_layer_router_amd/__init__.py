@@ -10,7 +10,8 @@ an error.
 Functions keep the C names (moe_route, moe_permute, moe_grouped_ffn_fwd,
 moe_combine, moe_combine_bwd, moe_grouped_ffn_bwd, moe_route_bwd, and the FP8
 forward: moe_quantize_fp8, moe_grouped_ffn_fwd_fp8; data gradients:
-moe_quantize_fp8_t, moe_grouped_ffn_dgrad_fp8; weight gradients:
+moe_quantize_fp8_t, moe_grouped_ffn_dgrad_fp8; both weight layouts at once:
+moe_quantize_fp8_w; weight gradients:
 moe_quantize_fp8_group_t, moe_grouped_ffn_wgrad_fp8) and return
 freshly allocated torch tensors; each also accepts preallocated outputs via
 ``out=`` dictionaries so that steady-state loops allocate nothing.
@@ -28,7 +29,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_F32, MOE_BF16, MOE_FP8 = 0, 1, 2
 (MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD, MOE_OP_ROUTE_BWD,
- MOE_OP_COMBINE_DX, MOE_OP_FFN_FWD_FP8, MOE_OP_FFN_DGRAD_FP8, MOE_OP_FFN_WGRAD_FP8) = range(9)
+ MOE_OP_COMBINE_DX, MOE_OP_FFN_FWD_FP8, MOE_OP_FFN_DGRAD_FP8, MOE_OP_FFN_WGRAD_FP8,
+ MOE_OP_QUANTIZE_W_FP8) = range(10)
 ABI_VERSION = 6
 
 
@@ -67,6 +69,7 @@ def _load():
         "moe_grouped_ffn_fwd_fp8": ([P, P, P, P, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, P,
                                      SZ, P], I32),
         "moe_quantize_fp8_group_t": ([P, P, I32, P, I32, I32, P, I32, P, P, P], I32),
+        "moe_quantize_fp8_w": ([P, P, I32, I32, I32, I32, P, P, P, P, P, P, P, SZ, P], I32),
         "moe_grouped_ffn_wgrad_fp8": ([P, P, P, P, P, P, I32, I32, I32, I32, P, P, P, I32, P, SZ, P],
                                       I32),
         "moe_profile_kernel": ([I32, ctypes.POINTER(P), ctypes.POINTER(P), I32], I32),
@@ -483,4 +486,36 @@ def moe_grouped_ffn_wgrad_fp8(x: torch.Tensor, src_row: Optional[torch.Tensor], 
                                          _ptr(o["dw_gate"]), _ptr(o["dw_up"]), _ptr(o["dw_down"]),
                                          1 if accumulate else 0, _ptr(ws), _nbytes(ws), _stream()),
            "moe_grouped_ffn_wgrad_fp8")
+    return o
+
+
+def moe_quantize_fp8_w(w0: torch.Tensor, w1: Optional[torch.Tensor] = None, transposed: bool = True,
+                       ws: Optional[torch.Tensor] = None,
+                       out: Optional[Dict[str, torch.Tensor]] = None):
+    """Both E4M3 code layouts of bf16 expert weights w0 (and w1) [B, N, K]: the rows
+    (q0/s0, q1/s1, as moe_quantize_fp8) and, unless transposed is False, the rows of
+    [w0^T | w1^T] (qt [B, K, n N] / st [B, K], as moe_quantize_fp8_t)."""
+    B, N, K = w0.shape
+    n = 1 if w1 is None else 2
+    dev = w0.device
+    o = dict(out or {})
+    o.setdefault("q0", torch.empty((B, N, K), dtype=torch.uint8, device=dev))
+    o.setdefault("s0", torch.empty((B, N), dtype=torch.float32, device=dev))
+    if w1 is not None:
+        o.setdefault("q1", torch.empty((B, N, K), dtype=torch.uint8, device=dev))
+        o.setdefault("s1", torch.empty((B, N), dtype=torch.float32, device=dev))
+    else:
+        o["q1"] = o["s1"] = None
+    if transposed:
+        o.setdefault("qt", torch.empty((B, K, n * N), dtype=torch.uint8, device=dev))
+        o.setdefault("st", torch.empty((B, K), dtype=torch.float32, device=dev))
+    else:
+        o["qt"] = o["st"] = None
+    al = lambda b: (b + 255) // 256 * 256
+    nb = 2 * al(n * B * N * (K // 128) * 4) + al(n * B * N * 4) + al(B * K * 4)
+    ws = _ws(nb, dev, ws)
+    _check(lib.moe_quantize_fp8_w(_ptr(w0), _ptr(w1), B, N, K, _dtype_code(w0), _ptr(o["q0"]),
+                                  _ptr(o["s0"]), _ptr(o["q1"]), _ptr(o["s1"]), _ptr(o["qt"]),
+                                  _ptr(o["st"]), _ptr(ws), _nbytes(ws), _stream()),
+           "moe_quantize_fp8_w")
     return o

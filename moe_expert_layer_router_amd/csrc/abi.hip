@@ -187,7 +187,7 @@ int64_t moe_workspace_bytes(int op, int T, int H, int I, int E, int k, int e_lo,
   const char* fn = "moe_workspace_bytes";
   if (dtype == MOE_FP8) {
     if (op != MOE_OP_PERMUTE && op != MOE_OP_FFN_FWD_FP8 && op != MOE_OP_FFN_DGRAD_FP8 &&
-        op != MOE_OP_FFN_WGRAD_FP8)
+        op != MOE_OP_FFN_WGRAD_FP8 && op != MOE_OP_QUANTIZE_W_FP8)
       return fail(MOE_EINVAL, "%s: MOE_FP8 applies to MOE_OP_PERMUTE and the FP8 FFN ops only", fn);
   } else if (int rc = check_dtype(dtype, fn)) {
     return rc;
@@ -202,6 +202,13 @@ int64_t moe_workspace_bytes(int op, int T, int H, int I, int E, int k, int e_lo,
       return (int64_t)ws_route_bwd(T, H, E, dtype);
     case MOE_OP_COMBINE_DX:
       return (int64_t)align256((size_t)E * H * elem_bytes(dtype));
+    case MOE_OP_QUANTIZE_W_FP8: {
+      if (e_lo < 0 || e_hi > E || e_lo >= e_hi)
+        return fail(MOE_EINVAL, "%s: need 0 <= e_lo < e_hi <= E", fn);
+      if (I <= 0 || I % 128 != 0 || H % 128 != 0)
+        return fail(MOE_EINVAL, "%s: need I > 0 and H, I multiples of 128", fn);
+      return (int64_t)quantize_w_fp8_ws_bytes(e_hi - e_lo, I, H, 2);
+    }
     case MOE_OP_FFN_FWD_FP8:
     case MOE_OP_FFN_DGRAD_FP8:
     case MOE_OP_FFN_WGRAD_FP8: {
@@ -424,6 +431,35 @@ int moe_quantize_fp8_t(const void* src0, const void* src1, int batch, int N, int
   if (int rc = check_ptr(scale, "scale", fn)) return rc;
   return hip_status(launch_quantize_t_fp8((const bf16_t*)src0, (const bf16_t*)src1, batch, N, K, q,
                                           scale, begin_launch(stream)),
+                    fn);
+}
+
+int moe_quantize_fp8_w(const void* w0, const void* w1, int batch, int N, int K, int dtype,
+                       uint8_t* q0, float* s0, uint8_t* q1, float* s1, uint8_t* qt, float* st,
+                       void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "moe_quantize_fp8_w";
+  if (dtype != MOE_BF16) return fail(MOE_EUNSUPPORTED, "%s: needs MOE_BF16 weights", fn);
+  if (batch < 0 || N <= 0 || K <= 0)
+    return fail(MOE_EINVAL, "%s: need batch >= 0, N > 0, K > 0 (batch=%d, N=%d, K=%d)", fn, batch, N, K);
+  if (N % 128 != 0 || K % 128 != 0)
+    return fail(MOE_EUNSUPPORTED, "%s: needs N %% 128 == 0 and K %% 128 == 0 (N=%d, K=%d)", fn, N, K);
+  if (batch == 0) return MOE_OK;
+  if (int rc = check_ptr(w0, "w0", fn, true)) return rc;
+  if (int rc = check_ptr(q0, "q0", fn, true)) return rc;
+  if (int rc = check_ptr(s0, "s0", fn)) return rc;
+  if (w1 != nullptr) {
+    if (int rc = check_ptr(w1, "w1", fn, true)) return rc;
+    if (int rc = check_ptr(q1, "q1", fn, true)) return rc;
+    if (int rc = check_ptr(s1, "s1", fn)) return rc;
+  }
+  if (qt != nullptr) {
+    if (!aligned16(qt)) return fail(MOE_EINVAL, "%s: qt must be 16-byte aligned", fn);
+    if (int rc = check_ptr(st, "st", fn)) return rc;
+  }
+  if (int rc = check_ws(ws, ws_bytes, quantize_w_fp8_ws_bytes(batch, N, K, w1 != nullptr ? 2 : 1), fn))
+    return rc;
+  return hip_status(launch_quantize_w_fp8((const bf16_t*)w0, (const bf16_t*)w1, batch, N, K, q0, s0,
+                                          q1, s1, qt, st, ws, begin_launch(stream)),
                     fn);
 }
 

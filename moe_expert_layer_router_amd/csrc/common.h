@@ -246,6 +246,11 @@ struct QuantGroupT {
   int nctrs;
 };
 hipError_t launch_quantize_group_t_fp8(const QuantGroupT& q, hipStream_t s);
+// both code layouts of expert weights (rows; per input channel, transposed)
+size_t quantize_w_fp8_ws_bytes(int batch, int N, int K, int nsrc);
+hipError_t launch_quantize_w_fp8(const bf16_t* w0, const bf16_t* w1, int batch, int N, int K,
+                                 uint8_t* q0, float* s0, uint8_t* q1, float* s1, uint8_t* qt,
+                                 float* st, void* ws, hipStream_t s);
 int wgrad_fp8_pitch(int R_cap, int E_l);
 size_t ffn_wgrad_fp8_ws_bytes(int R_cap, int E_l, int H, int I);
 hipError_t launch_ffn_wgrad_fp8(const bf16_t* x, const int32_t* src_row, const bf16_t* dgu,

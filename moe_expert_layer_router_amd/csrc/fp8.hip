@@ -145,6 +145,192 @@ hipError_t launch_quantize_t_fp8(const bf16_t* src0, const bf16_t* src1, int bat
   return hipGetLastError();
 }
 
+// Both code layouts of expert weights from the same two reads: the rows of
+// w0 (and w1) [B][N][K] as quantize_rows_fp8 makes them (forward) and the
+// per-input-channel rows of [w0^T | w1^T] as quantize_t_fp8 makes them (data
+// gradients), bit for bit: the same exponent rule and conversion on the same
+// maxima (a maximum is exact in any order).  Three launches over 128 x 128
+// tiles: (1) each tile's row maxima (over its 128 columns) and column maxima
+// (over its 128 rows) to fp32 partials in the workspace; (2) one thread per
+// row and per input channel reduces its partials to the scale exponent (and
+// writes the scale); (3) each tile goes out twice, as rows of codes (two
+// threads per row, 64 consecutive codes each) and, through LDS, as rows of
+// the transposed layout (two threads per input channel), so that every
+// 128-byte line of either output is written by one workgroup.
+// N % 128 == 0, K % 128 == 0.
+constexpr int kQwT = 128;  // tile edge
+struct QuantW {
+  const bf16_t* w[2];
+  uint8_t* q[2];      // row codes [B][N][K] of w0 / w1
+  float* s[2];        // row scales [B][N]
+  uint8_t* qt;        // transposed codes [B][K][nsrc N], or null
+  float* st;          // per-input-channel scales [B][K]
+  float* rowp;        // [nsrc][B][N][K / 128] row partial maxima
+  float* colp;        // [B][K][nsrc N / 128] column partial maxima
+  int* erow;          // [nsrc][B][N] row exponents
+  int* ecol;          // [B][K] input-channel exponents
+  int nsrc, B, N, K;
+};
+
+// Thread t of a tile holds the 16-byte chunk t % 16 (columns 8 (t % 16) ..
+// + 7) of rows t / 16 + 16 i, i < 8: each load instruction of a wave reads
+// four whole 256-byte rows.  The chunks are also copied into the LDS tile.
+__device__ __forceinline__ void load_tile128(const bf16_t* src, int K, int t,
+                                             bf16_t (*tile)[kQwT + 8], uint4 (&raw)[8]) {
+  const int r0 = t >> 4, c = (t & 15) * 8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) raw[i] = *reinterpret_cast<const uint4*>(src + (size_t)(r0 + 16 * i) * K + c);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&tile[r0 + 16 * i][c]) = raw[i];
+}
+
+__global__ __launch_bounds__(256) void quantize_w_max_kernel(const QuantW a) {
+  __shared__ float s_col[4][kQwT];
+  const int kb = blockIdx.x, nb_all = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int nbs = a.N / kQwT, src = nb_all / nbs, nb = nb_all % nbs;
+  const bf16_t* w = a.w[src] + ((size_t)b * a.N + nb * kQwT) * a.K + kb * kQwT;
+  // thread t: columns 8 (t % 16) .. + 7 of rows t / 16 + 16 i (as load_tile128)
+  uint4 raw[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    raw[i] = *reinterpret_cast<const uint4*>(w + (size_t)((t >> 4) + 16 * i) * a.K + (t & 15) * 8);
+  float mc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // rows: maximum over the tile's 128 columns (the 16 lanes of the row)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float v[8];
+    unpack8(raw[i], v);
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      m = fmaxf(m, fabsf(v[j]));
+      mc[j] = fmaxf(mc[j], fabsf(v[j]));
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+    if ((t & 15) == 0)
+      a.rowp[(((size_t)src * a.B + b) * a.N + nb * kQwT + (t >> 4) + 16 * i) * (a.K / kQwT) + kb] = m;
+  }
+  if (a.qt == nullptr) return;
+  // columns: the four lanes of a wave with the same chunk, then the four waves
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    mc[j] = fmaxf(mc[j], __shfl_xor(mc[j], 16, kWave));
+    mc[j] = fmaxf(mc[j], __shfl_xor(mc[j], 32, kWave));
+  }
+  if ((t & 63) < 16)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s_col[t >> 6][(t & 15) * 8 + j] = mc[j];
+  __syncthreads();
+  if (t < kQwT) {
+    const float m = fmaxf(fmaxf(s_col[0][t], s_col[1][t]), fmaxf(s_col[2][t], s_col[3][t]));
+    a.colp[((size_t)b * a.K + kb * kQwT + t) * (a.nsrc * nbs) + nb_all] = m;
+  }
+}
+
+// One thread per row (first nsrc B N threads) and per input channel (next B K).
+__global__ __launch_bounds__(256) void quantize_w_exp_kernel(const QuantW a) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  const long nrow = (long)a.nsrc * a.B * a.N;
+  if (i < nrow) {
+    const float* p = a.rowp + i * (a.K / kQwT);
+    float m = 0.f;
+    for (int j = 0; j < a.K / kQwT; ++j) m = fmaxf(m, p[j]);
+    const int e = fp8_exponent(m);
+    a.erow[i] = e;
+    const long src = i / ((long)a.B * a.N);
+    a.s[src][i - src * a.B * a.N] = ldexpf(1.f, e);
+    return;
+  }
+  const long c = i - nrow;
+  if (a.qt == nullptr || c >= (long)a.B * a.K) return;
+  const int np = a.nsrc * (a.N / kQwT);
+  const float* p = a.colp + c * np;
+  float m = 0.f;
+  for (int j = 0; j < np; ++j) m = fmaxf(m, p[j]);
+  const int e = fp8_exponent(m);
+  a.ecol[c] = e;
+  a.st[c] = ldexpf(1.f, e);
+}
+
+__global__ __launch_bounds__(256) void quantize_w_codes_kernel(const QuantW a) {
+  __shared__ __align__(16) bf16_t tile[kQwT][kQwT + 8];
+  const int kb = blockIdx.x, nb_all = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int nbs = a.N / kQwT, src = nb_all / nbs, nb = nb_all % nbs;
+  const bf16_t* w = a.w[src] + ((size_t)b * a.N + nb * kQwT) * a.K + kb * kQwT;
+  uint4 raw[8];
+  load_tile128(w, a.K, t, tile, raw);
+  // row codes: eight codes of each of the thread's rows (a wave's store
+  // instruction writes four whole 128-byte code rows of the tile)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = (t >> 4) + 16 * i;
+    const int e = a.erow[((size_t)src * a.B + b) * a.N + nb * kQwT + r];
+    float v[8];
+    unpack8(raw[i], v);
+    *reinterpret_cast<uint2*>(a.q[src] + ((size_t)b * a.N + nb * kQwT + r) * a.K + kb * kQwT +
+                              (t & 15) * 8) = fp8_codes8(v, e);
+  }
+  if (a.qt == nullptr) return;
+  __syncthreads();
+  {  // transposed codes: input channel t % 128, 64 consecutive rows from 64 (t / 128)
+    const int c = t & (kQwT - 1), g = t >> 7;
+    const int e = a.ecol[(size_t)b * a.K + kb * kQwT + c];
+    uint8_t* dst = a.qt + ((size_t)b * a.K + kb * kQwT + c) * (size_t)(a.nsrc * a.N) + (size_t)src * a.N +
+                   nb * kQwT + 64 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = bf2f(tile[64 * g + 16 * i + j][c]);
+      const uint2 lo = fp8_codes8(v, e), hi = fp8_codes8(v + 8, e);
+      *reinterpret_cast<uint4*>(dst + 16 * i) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+  }
+}
+
+static size_t qw_align(size_t b) { return (b + 255) & ~(size_t)255; }
+
+size_t quantize_w_fp8_ws_bytes(int batch, int N, int K, int nsrc) {
+  const size_t parts = (size_t)nsrc * batch * N * (K / kQwT);
+  return 2 * qw_align(parts * 4) + qw_align((size_t)nsrc * batch * N * 4) + qw_align((size_t)batch * K * 4);
+}
+
+hipError_t launch_quantize_w_fp8(const bf16_t* w0, const bf16_t* w1, int batch, int N, int K,
+                                 uint8_t* q0, float* s0, uint8_t* q1, float* s1, uint8_t* qt,
+                                 float* st, void* ws, hipStream_t s) {
+  if (batch <= 0) return hipSuccess;
+  QuantW a{};
+  a.nsrc = w1 != nullptr ? 2 : 1;
+  a.w[0] = w0;
+  a.w[1] = w1;
+  a.q[0] = q0;
+  a.q[1] = q1;
+  a.s[0] = s0;
+  a.s[1] = s1;
+  a.qt = qt;
+  a.st = st;
+  a.B = batch;
+  a.N = N;
+  a.K = K;
+  const size_t parts = qw_align((size_t)a.nsrc * batch * N * (K / kQwT) * 4);
+  char* p = (char*)ws;
+  a.rowp = (float*)p;
+  a.colp = (float*)(p + parts);
+  a.erow = (int*)(p + 2 * parts);
+  a.ecol = (int*)(p + 2 * parts + qw_align((size_t)a.nsrc * batch * N * 4));
+  const dim3 grid(K / kQwT, a.nsrc * (N / kQwT), batch);
+  quantize_w_max_kernel<<<grid, 256, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long threads = (long)a.nsrc * batch * N + (qt != nullptr ? (long)batch * K : 0);
+  quantize_w_exp_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  quantize_w_codes_kernel<<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 // Columns of grouped rows quantized per (group, column) for the FP8 weight
 // gradients, which sum over a group's rows: for group g (rows offsets[g] ..
 // offsets[g + 1] - 1) and column c, scale = 2^e by the row rule above applied

@@ -14,10 +14,12 @@ backward() returns.
 
 With fp8=True the expert FFN runs the library's FP8 recipe (E4M3 codes with
 power-of-two scales): tokens are quantized per row before the permute (which
-then moves code rows), the weights per output channel (forward) and per input
-channel (data gradients) on every call, the rows of dy_perm per row, and the
-weight gradients quantize their operands per (expert, column).  Routing,
-combine and the router backward stay as in the bf16 layer.
+then moves code rows); every forward quantizes the weights per output channel
+and, for training, per input channel as well (both layouts in one pass pair;
+the backward uses these codes, so it must be given the forward's weights); the
+backward quantizes the rows of dy_perm, and the weight gradients quantize
+their operands per (expert, column).  Routing, combine and the router backward
+stay as in the bf16 layer.
 """
 from __future__ import annotations
 
@@ -27,8 +29,8 @@ from typing import Dict, Optional
 import torch
 
 from . import (MOE_BF16, MOE_F32, MOE_FP8, MOE_OP_FFN_BWD, MOE_OP_FFN_DGRAD_FP8, MOE_OP_FFN_FWD,
-               MOE_OP_FFN_FWD_FP8, MOE_OP_FFN_WGRAD_FP8, MOE_OP_PERMUTE, MOE_OP_ROUTE,
-               MOE_OP_ROUTE_BWD, _check, _stream, lib, workspace_bytes)
+               MOE_OP_FFN_FWD_FP8, MOE_OP_FFN_WGRAD_FP8, MOE_OP_PERMUTE, MOE_OP_QUANTIZE_W_FP8,
+               MOE_OP_ROUTE, MOE_OP_ROUTE_BWD, _check, _stream, lib, workspace_bytes)
 
 
 def _p(t: Optional[torch.Tensor]):
@@ -97,7 +99,7 @@ class MoELayer:
                 b["dgu"] = torch.empty((R, 2 * I), dtype=dtype, device=dev)
         self.buf = b
         ops = [MOE_OP_ROUTE, MOE_OP_PERMUTE]
-        ops += [MOE_OP_FFN_FWD_FP8] if fp8 else [MOE_OP_FFN_FWD]
+        ops += [MOE_OP_FFN_FWD_FP8, MOE_OP_QUANTIZE_W_FP8] if fp8 else [MOE_OP_FFN_FWD]
         if train:
             ops += [MOE_OP_FFN_DGRAD_FP8] if fp8 else [MOE_OP_FFN_BWD]
             ops += [MOE_OP_ROUTE_BWD]
@@ -146,9 +148,16 @@ class MoELayer:
         _check(lib.moe_permute(_p(b["x_q"]), _p(b["topk_idx"]), T, H, E, k, self.e_lo, self.e_hi,
                                MOE_FP8, _p(b["counts"]), _p(b["offsets"]), _p(b["dest_row"]),
                                _p(b["src_row"]), _p(b["xq_perm"]), ws, wsb, s), "moe_permute")
-        self._quantize_rows(w_gate, E_l * I, H, b["wg_q"], b["wg_s"], s)
-        self._quantize_rows(w_up, E_l * I, H, b["wu_q"], b["wu_s"], s)
-        self._quantize_rows(w_down, E_l * H, I, b["wd_q"], b["wd_s"], s)
+        # weights: rows for these products and, when training, the input
+        # channels for the data gradients, from the same reads
+        tr = self.train
+        _check(lib.moe_quantize_fp8_w(_p(w_gate), _p(w_up), E_l, I, H, self.dt, _p(b["wg_q"]),
+                                      _p(b["wg_s"]), _p(b["wu_q"]), _p(b["wu_s"]),
+                                      _p(b["wgut_q"]) if tr else None, _p(b["wgut_s"]) if tr else None,
+                                      ws, wsb, s), "moe_quantize_fp8_w")
+        _check(lib.moe_quantize_fp8_w(_p(w_down), None, E_l, H, I, self.dt, _p(b["wd_q"]), _p(b["wd_s"]),
+                                      None, None, _p(b["wdt_q"]) if tr else None,
+                                      _p(b["wdt_s"]) if tr else None, ws, wsb, s), "moe_quantize_fp8_w")
         _check(lib.moe_grouped_ffn_fwd_fp8(_p(b["xq_perm"]), _p(b["x_scale"]), _p(b["src_row"]),
                                            _p(b["offsets"]), E_l, self.R_cap, H, I, _p(b["wg_q"]),
                                            _p(b["wg_s"]), _p(b["wu_q"]), _p(b["wu_s"]), _p(b["wd_q"]),
@@ -156,15 +165,12 @@ class MoELayer:
                                            _p(b["y_perm"]), ws, wsb, s), "moe_grouped_ffn_fwd_fp8")
 
     def _backward_ffn_fp8(self, x, w_gate, w_up, w_down, ws, wsb, s, side):
-        """dy_perm rows and the weights (per input channel) quantized, the FP8 data
-        gradients on this stream, then the FP8 weight gradients on the side stream."""
+        """dy_perm rows quantized, the FP8 data gradients on this stream (weight
+        codes per input channel from the forward), then the FP8 weight gradients
+        on the side stream."""
         b, H, I, E_l = self.buf, self.H, self.I, self.E_l
         self._quantize_rows(b["dy_perm"], self.R_cap, H, b["dy_q"], b["dy_scale"], s,
                             nrows=b["offsets"][E_l:])
-        _check(lib.moe_quantize_fp8_t(_p(w_down), None, E_l, H, I, self.dt, _p(b["wdt_q"]),
-                                      _p(b["wdt_s"]), s), "moe_quantize_fp8_t")
-        _check(lib.moe_quantize_fp8_t(_p(w_gate), _p(w_up), E_l, I, H, self.dt, _p(b["wgut_q"]),
-                                      _p(b["wgut_s"]), s), "moe_quantize_fp8_t")
         _check(lib.moe_grouped_ffn_dgrad_fp8(_p(b["dy_q"]), _p(b["dy_scale"]), _p(b["gu"]),
                                              _p(b["offsets"]), E_l, self.R_cap, H, I, _p(b["wdt_q"]),
                                              _p(b["wdt_s"]), _p(b["wgut_q"]), _p(b["wgut_s"]),

@@ -72,7 +72,7 @@ def test_workspace_bytes_and_errors():
     assert ws(moe.MOE_OP_PERMUTE, 16384, 2048, 768, 128, 8, 0, 128, BF16) > 16384 * 8 * 4
     assert ws(moe.MOE_OP_FFN_BWD, 8192, 2048, 768, 128, 8, 0, 16, BF16) >= 8192 * 8 * 2 * 768 * 2
     assert ws(moe.MOE_OP_PERMUTE, 0, 2048, 768, 128, 8, 0, 16, BF16) == 0
-    assert ws(9, 16, 64, 32, 8, 2, 0, 8, F32) == EINVAL and "unknown op" in _err()
+    assert ws(10, 16, 64, 32, 8, 2, 0, 8, F32) == EINVAL and "unknown op" in _err()
     assert ws(moe.MOE_OP_ROUTE, 16, 64, 32, 8, 9, 0, 8, F32) == EINVAL and "k=9" in _err()
     assert ws(moe.MOE_OP_ROUTE, 16, 64, 32, 300, 2, 0, 8, F32) == EINVAL
     assert ws(moe.MOE_OP_ROUTE, 16, 62, 32, 8, 2, 0, 8, BF16) == EINVAL and "multiple of 8" in _err()
@@ -259,6 +259,27 @@ def test_fp8_wgrad_entry_points_errors():
     n = ws(moe.MOE_OP_FFN_WGRAD_FP8, 4096, 2048, 768, 128, 4, 0, 16, BF16)
     assert n >= pitch * (2 * 768 + 2 * 2048 + 768) + 16 * (3 * 768 + 2 * 2048) * 4   # codes, scales
     assert ws(moe.MOE_OP_FFN_WGRAD_FP8, 4096, 2048, 768, 128, 4, 0, 16, FP8) == n
+
+
+def test_fp8_weight_quantizer_errors():
+    """Argument errors of moe_quantize_fp8_w (none launches)."""
+    f = lambda *a: L.moe_quantize_fp8_w(*a)
+    big = 1 << 28
+    a = lambda w0=A, w1=A, B=16, N=768, K=2048, dt=BF16, q0=A, s0=A, q1=A, s1=A, qt=A, st=A, ws=big: (
+        w0, w1, B, N, K, dt, q0, s0, q1, s1, qt, st, A, ws, S)
+    assert f(*a(dt=F32)) == EUNSUP and "BF16" in _err()
+    assert f(*a(N=704)) == EUNSUP and "128" in _err()
+    assert f(*a(K=2000)) == EUNSUP
+    assert f(*a(B=-1)) == EINVAL
+    assert f(*a(w0=U)) == EINVAL and "w0" in _err()
+    assert f(*a(q0=N)) == EINVAL and "q0" in _err()
+    assert f(*a(s1=N)) == EINVAL and "s1" in _err()
+    assert f(*a(qt=U)) == EINVAL and "qt" in _err()
+    assert f(*a(st=N)) == EINVAL and "st" in _err()
+    assert f(*a(ws=8)) == EWS
+    assert f(*a(B=0)) == OK                                   # nothing to do, nothing launched
+    n = L.moe_workspace_bytes(moe.MOE_OP_QUANTIZE_W_FP8, 4096, 2048, 768, 128, 8, 0, 16, BF16)
+    assert n >= 2 * (2 * 16 * 768 * (2048 // 128) * 4) + 2 * 16 * 768 * 4 + 16 * 2048 * 4
 
 def test_ffn_bwd_split_needs_a_second_stream():
     f = lambda *a: L.moe_grouped_ffn_bwd_split(*a)

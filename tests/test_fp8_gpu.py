@@ -220,6 +220,39 @@ def test_quantize_fp8_t_bit_exact(pair, N):
     assert np.array_equal(_np(s), ref_s)
 
 
+@pytest.mark.parametrize("pair,N,K,transposed", [(True, 768, 2048, True), (False, 2048, 768, True),
+                                                  (True, 384, 128, False), (False, 128, 128, True)],
+                         ids=["gate_up_pair", "down", "pair_rows_only", "single_tile"])
+def test_quantize_fp8_w_matches_both_quantizers(pair, N, K, transposed):
+    """moe_quantize_fp8_w gives, bit for bit, the row codes of moe_quantize_fp8 and the
+    per-input-channel codes of moe_quantize_fp8_t (both checked against the oracle
+    above) on weights whose rows and columns span 2^-20 .. 2^20, with a zero row, a
+    zero column and maxima exactly on a scale boundary."""
+    rng = np.random.default_rng(43)
+    B = 3
+    w0 = rng.standard_normal((B, N, K)) * np.exp2(rng.integers(-20, 20, size=(B, N, 1))) \
+        * np.exp2(rng.integers(-4, 4, size=(B, 1, K)))
+    w1 = rng.standard_normal((B, N, K)) * np.exp2(rng.integers(-20, 20, size=(B, N, 1)))
+    w0[0, 3, :] = 0.0
+    w0[1, :, 5] = 0.0
+    w1[1, :, 5] = 0.0
+    w0[2, 7, 9] = 448.0 * 2.0 ** 6
+    t0, t1 = _dev(w0.astype(np.float32), torch.bfloat16), _dev(w1.astype(np.float32), torch.bfloat16)
+    print(f"  quantize_w pair={pair} B={B} N={N} K={K} transposed={transposed}", flush=True)
+    o = moe.moe_quantize_fp8_w(t0, t1 if pair else None, transposed=transposed)
+    r0 = moe.moe_quantize_fp8(t0.view(B * N, K))
+    r1 = moe.moe_quantize_fp8(t1.view(B * N, K)) if pair else None
+    rt = moe.moe_quantize_fp8_t(t0, t1 if pair else None) if transposed else None
+    torch.cuda.synchronize()
+    assert torch.equal(o["q0"].view(B * N, K), r0[0]) and torch.equal(o["s0"].view(-1), r0[1])
+    if pair:
+        assert torch.equal(o["q1"].view(B * N, K), r1[0]) and torch.equal(o["s1"].view(-1), r1[1])
+    if transposed:
+        assert torch.equal(o["qt"], rt[0]) and torch.equal(o["st"], rt[1])
+    else:
+        assert o["qt"] is None
+
+
 DGRAD_CASES = [
     EP_SHARE.scaled(name="dgrad_fp8_t512_h256_i128_e32_k4_local4to20", T=512, H=256, I=128, E=32, k=4,
                     e_lo=4, e_hi=20),
