@@ -408,6 +408,10 @@ WGRAD_CASES = [
                     e_lo=4, e_hi=20),
     SKEWED.scaled(name="wgrad_fp8_skewed_t1024_h256_i256_e32_k4", T=1024, H=256, I=256, E=32, k=4,
                   e_lo=0, e_hi=32),
+    # partial tiles on both sides: dW_down has M = H = 384 (a 128-row second M
+    # tile) and N = I = 128; the gate/up product has N = H = 384
+    EP_SHARE.scaled(name="wgrad_fp8_t512_h384_i128_e8_k2_partial_tiles", T=512, H=384, I=128, E=8, k=2,
+                    e_lo=0, e_hi=8),
     # the expert layer's shapes: 16 experts x (48 gate/up + 24 down) tiles for 256
     # persistent workgroups
     EP_SHARE.scaled(name="wgrad_fp8_multitile_t4096_h2048_i768_e16_k4_all_local", T=4096, E=16, k=4,
@@ -556,3 +560,8 @@ def test_layer_fp8_is_the_call_chain_and_tracks_the_exact_layer(w):
     print("  rel-L2 vs the exact layer: " + ", ".join(f"{n} {v:.3e}" for n, v in r.items()), flush=True)
     assert r["y"] < 0.12
     assert all(v < 0.2 for n, v in r.items() if n != "y")
+    # the forward-only FP8 layer (no per-input-channel weight codes) gives the same y
+    inf = moe.MoELayer(w.T, w.H, w.I, w.E, w.k, w.e_lo, w.e_hi, bf, DEV, train=False, fp8=True)
+    y_inf = inf.forward(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(y_inf, y)
