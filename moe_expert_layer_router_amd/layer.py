@@ -151,6 +151,7 @@ class MoELayer:
         # weights: rows for these products and, when training, the input
         # channels for the data gradients, from the same reads
         tr = self.train
+        self._fp8_weights = (w_gate.data_ptr(), w_up.data_ptr(), w_down.data_ptr())
         _check(lib.moe_quantize_fp8_w(_p(w_gate), _p(w_up), E_l, I, H, self.dt, _p(b["wg_q"]),
                                       _p(b["wg_s"]), _p(b["wu_q"]), _p(b["wu_s"]),
                                       _p(b["wgut_q"]) if tr else None, _p(b["wgut_s"]) if tr else None,
@@ -169,6 +170,9 @@ class MoELayer:
         codes per input channel from the forward), then the FP8 weight gradients
         on the side stream."""
         b, H, I, E_l = self.buf, self.H, self.I, self.E_l
+        if getattr(self, "_fp8_weights", None) != (w_gate.data_ptr(), w_up.data_ptr(), w_down.data_ptr()):
+            raise ValueError("the FP8 backward uses the weight codes of the forward: pass it the "
+                             "forward's weight tensors")
         self._quantize_rows(b["dy_perm"], self.R_cap, H, b["dy_q"], b["dy_scale"], s,
                             nrows=b["offsets"][E_l:])
         _check(lib.moe_grouped_ffn_dgrad_fp8(_p(b["dy_q"]), _p(b["dy_scale"]), _p(b["gu"]),
