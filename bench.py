@@ -343,13 +343,40 @@ def fp8_dgrad_bench(w, args, moe, torch, t, pb, timed, n):
                                      "peak_tflops": peak, "frac": round(ach / peak, 4)}
     us_b = kern["FFN_DOWN_DGRAD_bf16"]["avg_us"] + kern["FFN_GATEUP_DGRAD_bf16"]["avg_us"]
     flops = 6.0 * R * H * I
+    # the whole expert backward: bf16 (moe_grouped_ffn_bwd, data and weight
+    # gradients on two streams) against the FP8 data gradients followed by the
+    # FP8 weight gradients (their operand quantization included)
+    f_bb = lambda: moe.moe_grouped_ffn_bwd(dy, pb["x_perm"], gu, h_perm, offsets, t["w_gate"], t["w_up"],
+                                           t["w_down"], ws=ws, out={"dx_perm": bufs["dx"],
+                                                                    "dw_gate": bufs["dwg"],
+                                                                    "dw_up": bufs["dwu"],
+                                                                    "dw_down": bufs["dwd"]})
+    ow = moe.moe_grouped_ffn_wgrad_fp8(pb["x_perm"], None, o8["dgu"], h_perm, dy, offsets, E_l)
+    nbw = moe.lib.moe_workspace_bytes(moe.MOE_OP_FFN_WGRAD_FP8, R_cap, H, I, max(E_l, 1), 1, 0, E_l,
+                                      moe.MOE_BF16)
+    wsw = torch.empty(int(nbw), dtype=torch.uint8, device=dev)
+    f_w8 = lambda: moe.moe_grouped_ffn_wgrad_fp8(pb["x_perm"], None, o8["dgu"], h_perm, dy, offsets, E_l,
+                                                 ws=wsw, out=ow)
+
+    def f_b8():
+        f_8()
+        f_w8()
+    us_bb, us_w8, us_b8 = timed(f_bb, n), timed(f_w8, n), timed(f_b8, n)
+    backward = {"us": {"bf16": round(us_bb, 2), "fp8": round(us_b8, 2), "fp8_weight_gradients": round(us_w8, 2)},
+                "bf16_tflops": round(2 * flops / (us_bb * 1e-6) / 1e12, 1),
+                "fp8_tflops": round(2 * flops / (us_b8 * 1e-6) / 1e12, 1),
+                "speedup_vs_bf16": round(us_bb / us_b8, 3),
+                "note": "fp8 = data gradients (with the SiLU' pass and [dg|du] codes) + weight gradients "
+                        "(with the per-(expert, column) quantization of their four operands); the dy_perm "
+                        "rows and the transposed weights are quantized outside (timed below)"}
     return {"us": {"fp8": round(us_8, 2), "bf16_products": round(us_b, 2)},
             "fp8_tflops": round(flops / (us_8 * 1e-6) / 1e12, 1),
             "bf16_tflops": round(flops / (us_b * 1e-6) / 1e12, 1),
             "speedup_vs_bf16": round(us_b / us_8, 3),
             "dy_quantize_us": round(timed(f_qdy, n), 2),
             "weight_quantize_t_us": round(timed(f_qw, n), 2),
-            "kernels": kern}
+            "kernels": kern,
+            "backward": backward}
 
 
 def step_stats(run, n, dev):
