@@ -621,13 +621,15 @@ def test_ffn_bwd_split_equals_single_stream():
         assert torch.equal(out2[n], out[n]), n
 
 
-def test_layer_graph_replays_match_eager():
-    """The layer step (forward + backward over three streams) captured in a HIP graph:
-    every replay, with eager work of the program in between, equals the eager result."""
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8_ffn"])
+def test_layer_graph_replays_match_eager(fp8):
+    """The layer step (forward + backward over three streams; with fp8, the FP8
+    expert FFN and its quantization passes) captured in a HIP graph: every replay,
+    with eager work of the program in between, equals the eager result."""
     w = TRAIN.scaled(name="graph", T=1024)
     inp = _inputs(w)
     t = _gpu_tensors(w, inp)
-    layer = moe.MoELayer(w.T, w.H, w.I, w.E, w.k, w.e_lo, w.e_hi, t["x"].dtype, DEV)
+    layer = moe.MoELayer(w.T, w.H, w.I, w.E, w.k, w.e_lo, w.e_hi, t["x"].dtype, DEV, fp8=fp8)
 
     def step():
         layer.forward(t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"])
