@@ -15,26 +15,33 @@
 // and a tile table (built on the device from the offsets) maps M tiles to
 // experts.  "K-grouped": the reduction runs over an expert's rows.
 //
-// Tiling: 256 threads = 4 waves in a 2x2 grid, block tile BM x 256, K step 32,
-// each wave a BM/2 x 128 sub-tile of (BM/64) x 4 MFMA 32x32x16 bf16 blocks with
-// fp32 accumulators.  Two block heights:
+// Tiling: 256 threads = 4 waves in a 2x2 grid, block tile BM x 256, each wave
+// a BM/2 x 128 sub-tile of (BM/64) x 4 MFMA 32x32x16 bf16 blocks with fp32
+// accumulators.  Two block heights:
 //   BM = 256: 128 x 128 wave tiles (256 accumulator registers, one wave per
-//     SIMD), 4-stage ring of 128 KB, one workgroup per CU.  Per k16 sub-step a
-//     wave reads 8 KB of fragments for 16 MFMAs, which keeps the LDS traffic
-//     per MFMA well inside the CU's LDS bandwidth.
+//     SIMD), 128 KB of ring plus a 32 KB staging area, one workgroup per CU.
+//     Per k16 sub-step a wave reads 8 KB of fragments for 16 MFMAs, which
+//     keeps the LDS traffic per MFMA well inside the CU's LDS bandwidth.
 //   BM = 128: 64 x 128 wave tiles (128 accumulators), 3-stage ring of 72 KB,
 //     two workgroups per CU: twice the LDS traffic per MFMA, but half the tile
 //     height (less padding of ragged expert groups, more tiles to spread over
 //     256 CUs) and a second workgroup whose MFMAs fill the gaps of the other's
 //     barriers, prologue and epilogue.
-// Operand tiles stream into the LDS ring by buffer->LDS DMA
+// Two rings (Cfg):
+//   narrow: K steps of 32, NST slots; the DMA of step k + NST - 1 is in
+//     flight while step k computes.
+//   wide (the bf16 M-grouped products): K blocks of 64 in five 32 KB regions
+//     (the fifth doubles as the staging area); blocks j + 1 and j + 2 are in
+//     flight while block j computes.  A K-contiguous row of a block is one
+//     whole 128-byte line, where a narrow step reads half lines: on gfx950 the
+//     buffer->LDS path moves about twice the bytes per cycle for whole lines.
+// Operand tiles stream into the ring by buffer->LDS DMA
 // (buffer_load_dwordx4 ... lds): no staging registers, and the buffer range
 // check turns every row outside the tile's valid range into zeros, which
-// handles ragged expert groups.  The DMA of K step k + NST - 1 is in flight
-// while step k computes; waits are explicit (s_waitcnt vmcnt / lgkmcnt and
-// s_barrier).
+// handles ragged expert groups.  Waits are explicit (s_waitcnt vmcnt /
+// lgkmcnt and s_barrier).
 //   K-contiguous operands ("KC": activations in the forward, A of the data
-//   gradients) are stored as rows of 32 bf16 with the 16-byte chunks
+//   gradients) are stored as rows of 32 or 64 bf16 with the 16-byte chunks
 //   XOR-swizzled by row and read as MFMA fragments with ds_read_b128.
 //   MN-contiguous operands ("MC": weights in the data gradients, both operands
 //   of the weight gradients) are stored untransposed (rows = k) with 16-byte
@@ -67,23 +74,37 @@ constexpr int kMaxDevices = 64;  // per-device objects the launchers keep
 constexpr int kTileCtrs = 4;             // dynamic tile counters in the FFN workspace
 constexpr int WN = 128;                  // wave sub-tile width
 constexpr int NI = WN / 32;              // MFMA blocks per wave along N
-constexpr int KSUB = BK / 16;            // k16 sub-steps per K step
-constexpr int kStageB = BN * BK;         // bf16 elements per B stage
-constexpr int NIB = kStageB * 2 / 1024 / 4;  // DMA instructions (1 KB each) per wave per stage, B
-constexpr int kSlotB = kStageB * 2;      // bytes
 
-// Block-height dependent parameters.
-template <int BM_>
+// Block-height and ring dependent parameters.  Two rings:
+//   narrow (WIDE = false): K steps of BK = 32, NST slots of A then NST slots
+//     of B.  A K-contiguous row of a step is 64 bytes: every DMA instruction
+//     reads 16 half cache lines.
+//   wide (WIDE = true, BM = 256 only): K blocks of 64, five 32 KiB regions;
+//     load i of a tile (A of block j = load 2j, B of block j = load 2j + 1)
+//     goes to region i % 5.  A K-contiguous row of a block is a whole 128-byte
+//     line, and each DMA instruction reads 8 whole lines: the texture path
+//     moves about twice the bytes per cycle (a probe of the two patterns over
+//     L2-resident data: 123 against 66 GB/s per CU).  Region 4 is also the
+//     epilogue's staging area.
+template <int BM_, bool WIDE_ = false>
 struct Cfg {
   static constexpr int BM = BM_;
+  static constexpr bool WIDE = WIDE_;
+  static constexpr int BKX = WIDE ? 64 : BK;           // K per ring stage (bf16)
+  static constexpr int KSUB = BKX / 16;                // k16 sub-steps per stage
   static constexpr int WM = BM / 2;                    // wave sub-tile height
   static constexpr int MI = WM / 32;                   // MFMA blocks per wave along M
-  static constexpr int NST = BM == 256 ? 4 : 3;        // ring stages
-  static constexpr int kStageA = BM * BK;              // bf16 elements per A stage
-  static constexpr int NIA = kStageA * 2 / 1024 / 4;   // DMA instructions per wave per stage, A
+  static constexpr int NST = BM == 256 ? 4 : 3;        // narrow ring: stages
+  static constexpr int kStageA = BM * BKX;             // bf16 elements per A stage
+  static constexpr int kStageB = BN * BKX;             // bf16 elements per B stage
+  static constexpr int NIA = kStageA * 2 / 1024 / 4;   // DMA instructions (1 KB) per wave per stage, A
+  static constexpr int NIB = kStageB * 2 / 1024 / 4;   // and B
   static constexpr int kSlotA = kStageA * 2;           // bytes
-  static constexpr int kOffB = NST * kSlotA;           // B slots start here
-  static constexpr int kRingBytes = NST * (kSlotA + kSlotB);
+  static constexpr int kSlotB = kStageB * 2;
+  static constexpr int kRegion = 32768;                // wide ring: region bytes
+  static constexpr int kOffB = WIDE ? 0 : NST * kSlotA;  // narrow: B slots start here
+  // wide: regions 0..3 (region 4 is the staging area below)
+  static constexpr int kRingBytes = WIDE ? 4 * kRegion : NST * (kSlotA + kSlotB);
   static constexpr int kWavesPerSimd = BM == 256 ? 1 : 2;  // = workgroups per CU
   // The epilogue stages 16 x 128 fp32 (8 KB) per wave.  256-row tiles keep
   // that area after the ring, so the next tile's first K steps are loaded
@@ -97,12 +118,20 @@ struct Cfg {
   static constexpr int kLdsBytes = kSepStage ? kRingBytes + kStageBytes : kRingBytes;
   static_assert(kLdsBytes * kWavesPerSimd <= 160 * 1024, "LDS per CU");
   static_assert(kSepStage || kRingBytes >= kStageBytes, "staging area inside the ring");
+  static_assert(!WIDE || (BM == 256 && kSlotA == kRegion && kSlotB == kRegion && kStageBytes == kRegion &&
+                          kStageOff == 4 * kRegion),
+                "wide ring: five equal regions, the fifth is the staging area");
 };
 // Tile heights in use (chosen per product by measurement on the 128-expert
 // layer: 256 wherever the larger tile's lower L2 and LDS traffic per MFMA wins
 // over the finer tiling of 128; the down-projection weight gradient, whose
 // K = expert rows is short, runs faster with 128).
 constexpr int kBmGrouped = 256;
+// The bf16 M-grouped products run on the wide ring (K blocks of 64; their K,
+// H or I or 2I, is a multiple of 64); the weight gradients, whose operands are
+// MN-contiguous rows of 512 bytes already, and the FP8 products keep the
+// narrow one.
+constexpr bool kWideGrouped = true;
 constexpr int kBmWgrad = 256;
 constexpr int kBmWgradDown = 128;
 
@@ -178,9 +207,11 @@ struct Operand {
 // MFMA fragments from LDS
 // ---------------------------------------------------------------------------
 // GATEUP_FWD B tile rows interleave 32 gate rows and 32 up rows; DMA
-// instruction u of a wave fills tile rows 16 (w NIB + u) .. + 15 (w NIB even),
-// so whether it carries up rows depends on u alone.
-__device__ __forceinline__ bool gateup_is_up(int u) { return ((u * 64 / KCH) >> 5) & 1; }
+// instruction u of a wave fills tile rows R (w NIB + u) .. + R - 1, R = 512 /
+// BKX rows per instruction (w NIB R a multiple of 64), so whether it carries
+// up rows depends on u alone.
+template <class C>
+__device__ __forceinline__ bool gateup_is_up(int u) { return ((u * (512 / C::BKX)) >> 5) & 1; }
 
 // DMA of one K step (k0 = first k) into the wave's part of a ring slot
 // (la, lb: LDS byte addresses).
@@ -195,7 +226,7 @@ __device__ __forceinline__ bool gateup_is_up(int u) { return ((u * 64 / KCH) >> 
 
 template <int KIND, class C>
 __device__ __forceinline__ void dma_piece(const GemmArgs& p, const Operand<C::NIA>& opA,
-                                          const Operand<NIB>& opB, uint32_t la, uint32_t lb,
+                                          const Operand<C::NIB>& opB, uint32_t la, uint32_t lb,
                                           int k0, uint32_t kill, int u) {
   constexpr int NIA = C::NIA;
   if (u < NIA) {
@@ -205,7 +236,7 @@ __device__ __forceinline__ void dma_piece(const GemmArgs& p, const Operand<C::NI
   const int v = u - NIA;
   if constexpr (KIND == K_GATEUP_FWD) {
     // each instruction fills 16 rows of one gate or up block
-    dma16(gateup_is_up(v) ? opB.rsrc2 : opB.rsrc, (opB.voff[v] + (uint32_t)k0 * 2) | kill, lb + v * 1024);
+    dma16(gateup_is_up<C>(v) ? opB.rsrc2 : opB.rsrc, (opB.voff[v] + (uint32_t)k0 * 2) | kill, lb + v * 1024);
   } else if constexpr (KIND == K_GATEUP_DGRAD) {
     const bool up = k0 >= p.I;
     const uint32_t kk = (uint32_t)(up ? k0 - p.I : k0);
@@ -233,7 +264,7 @@ __device__ __forceinline__ lds_char_t* lds_ptr(uint32_t byte) {
 // Per-lane byte offsets of the MFMA fragments inside a tile slot, fixed for the
 // kernel's life; everything else in a fragment address is wave-uniform or a
 // compile-time constant.
-//   KC (rows of BK bf16): lane l reads row l % 32 of a 32-row block, logical
+//   KC (rows of BKX bf16): lane l reads row l % 32 of a 32-row block, logical
 //   chunk 2 s + l / 32; the block's first row (a multiple of 16) does not
 //   change the swizzle, so kc[s] is the offset for block row 0.
 //   MC (transposing reads, width W): with g = l / 16, i = l % 16 the lane reads
@@ -244,8 +275,9 @@ __device__ __forceinline__ lds_char_t* lds_ptr(uint32_t byte) {
 //   0..3) thus fall in four different 64-byte quarters of the 256-byte bank
 //   line: the 32 lanes cover all 64 banks once.  mc[j] is the whole offset of
 //   fragment j (wave base included; the k sub-step is added per read).
+template <class C>
 struct FragLanes {
-  uint32_t kc[KSUB];
+  uint32_t kc[C::KSUB];
   uint32_t mc_a[4];
   uint32_t mc_b[NI];
 };
@@ -257,10 +289,10 @@ __device__ __forceinline__ void mc_lane_offsets(int lane, int mb, uint32_t (&mc)
 }
 
 template <class C>
-__device__ __forceinline__ FragLanes frag_lanes(int lane, int wave) {
-  FragLanes L;
+__device__ __forceinline__ FragLanes<C> frag_lanes(int lane, int wave) {
+  FragLanes<C> L;
 #pragma unroll
-  for (int s = 0; s < KSUB; ++s) L.kc[s] = kc_lane_offset(lane, s);
+  for (int s = 0; s < C::KSUB; ++s) L.kc[s] = kc_lane_offset<C::BKX>(lane, s);
   mc_lane_offsets<C::BM>(lane, (wave >> 1) * (C::WM / 32), L.mc_a, C::MI);
   mc_lane_offsets<BN>(lane, (wave & 1) * (WN / 32), L.mc_b, NI);
   return L;
@@ -290,7 +322,7 @@ struct Frags {
 };
 
 // sa / sb: byte offsets of the A / B slot plus the wave's block base
-// (KC: first row * BK * 2; MC: first column * 2).
+// (KC: first row * BKX * 2; MC: first column * 2).
 // Fragment j of a sub-step, in the order the MFMAs of the next sub-step need
 // them: A0, B0, B1, B2, B3, A1, A2, ... (MFMAs run mi-major).
 template <class C>
@@ -300,20 +332,20 @@ __host__ __device__ constexpr int frag_order(int j) {
 
 template <int KIND, class C>
 __device__ __forceinline__ void load_frag(Frags<C>& f, int j, int s, uint32_t sa, uint32_t sb,
-                                          const FragLanes& L) {
+                                          const FragLanes<C>& L) {
   using Tr = Traits<KIND>;
   constexpr int MI = C::MI, BM = C::BM;
   const int q = frag_order<C>(j);
   if (q < MI) {
     const int mi = q;
     if constexpr (Tr::A_KC)
-      f.a[mi] = frag_kc(sa, L.kc[s], mi * 32 * BK * 2);
+      f.a[mi] = frag_kc(sa, L.kc[s], mi * 32 * C::BKX * 2);
     else
       f.a[mi] = frag_mc<BM>(sa, L.mc_a[mi], 2 * (16 * s * BM));
   } else {
     const int ni = q - MI;
     if constexpr (Tr::B_KC)
-      f.b[ni] = frag_kc(sb, L.kc[s], ni * 32 * BK * 2);
+      f.b[ni] = frag_kc(sb, L.kc[s], ni * 32 * C::BKX * 2);
     else
       f.b[ni] = frag_mc<BN>(sb, L.mc_b[ni], 2 * (16 * s * BN));
   }
@@ -321,7 +353,7 @@ __device__ __forceinline__ void load_frag(Frags<C>& f, int j, int s, uint32_t sa
 
 template <int KIND, class C>
 __device__ __forceinline__ void load_frags(Frags<C>& f, int s, uint32_t sa, uint32_t sb,
-                                           const FragLanes& L) {
+                                           const FragLanes<C>& L) {
 #pragma unroll
   for (int j = 0; j < C::MI + NI; ++j) load_frag<KIND, C>(f, j, s, sa, sb, L);
 }
@@ -355,13 +387,13 @@ __device__ __forceinline__ void mfma_f8(f32x16_t& acc, const i32x8_t& a, const i
 }
 
 template <class C>
-__device__ __forceinline__ void read_a8(Frags8<C>& f, int mi, int s, uint32_t sa, const FragLanes& L) {
-  const i32x4_t v = __builtin_bit_cast(i32x4_t, frag_kc(sa, L.kc[s], mi * 32 * BK * 2));
+__device__ __forceinline__ void read_a8(Frags8<C>& f, int mi, int s, uint32_t sa, const FragLanes<C>& L) {
+  const i32x4_t v = __builtin_bit_cast(i32x4_t, frag_kc(sa, L.kc[s], mi * 32 * C::BKX * 2));
   if (s == 0) f.a[mi].lo = v; else f.a[mi].hi = v;
 }
 template <class C>
-__device__ __forceinline__ void read_b8(Frags8<C>& f, int ni, int s, uint32_t sb, const FragLanes& L) {
-  const i32x4_t v = __builtin_bit_cast(i32x4_t, frag_kc(sb, L.kc[s], ni * 32 * BK * 2));
+__device__ __forceinline__ void read_b8(Frags8<C>& f, int ni, int s, uint32_t sb, const FragLanes<C>& L) {
+  const i32x4_t v = __builtin_bit_cast(i32x4_t, frag_kc(sb, L.kc[s], ni * 32 * C::BKX * 2));
   if (s == 0) f.b[ni].lo = v; else f.b[ni].hi = v;
 }
 
@@ -381,7 +413,7 @@ __device__ __forceinline__ void read_b8(Frags8<C>& f, int ni, int s, uint32_t sb
 //               (the reads end with the last MFMA).
 template <class C>
 struct DmaSplit {
-  static constexpr int ND = C::NIA + NIB;  // DMA instructions per wave per step
+  static constexpr int ND = C::NIA + C::NIB;  // DMA instructions per wave per step
   static constexpr int NH = ND / 2;        // per half
   static constexpr int DSTR = C::MI * NI / NH;
   static_assert(ND % 2 == 0 && DSTR >= 1, "DMA halves");
@@ -390,8 +422,8 @@ struct DmaSplit {
 template <int KIND, class C>
 __device__ __forceinline__ void mma_read_next(f32x16_t (&acc)[C::MI][NI], const Frags<C>& cur,
                                               Frags<C>& nxt, int s_next, uint32_t sa, uint32_t sb,
-                                              const FragLanes& L, const GemmArgs& p,
-                                              const Operand<C::NIA>& opA, const Operand<NIB>& opB,
+                                              const FragLanes<C>& L, const GemmArgs& p,
+                                              const Operand<C::NIA>& opA, const Operand<C::NIB>& opB,
                                               uint32_t la, uint32_t lb, int k0, uint32_t kill) {
   constexpr int NM = C::MI * NI, NR = C::MI + NI;
   using D = DmaSplit<C>;
@@ -409,8 +441,8 @@ __device__ __forceinline__ void mma_read_next(f32x16_t (&acc)[C::MI][NI], const 
 template <int KIND, class C>
 __device__ __forceinline__ void mma_dma_read(f32x16_t (&acc)[C::MI][NI], const Frags<C>& cur,
                                              Frags<C>& nxt, uint32_t sa, uint32_t sb,
-                                             const FragLanes& L, const GemmArgs& p,
-                                             const Operand<C::NIA>& opA, const Operand<NIB>& opB,
+                                             const FragLanes<C>& L, const GemmArgs& p,
+                                             const Operand<C::NIA>& opA, const Operand<C::NIB>& opB,
                                              uint32_t la, uint32_t lb, int k0, uint32_t kill) {
   constexpr int NM = C::MI * NI, NR = C::MI + NI;
   using D = DmaSplit<C>;
@@ -870,11 +902,13 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
 // next step's sub-step 0 fragments.
 template <int KIND, class C>
 __device__ __forceinline__ void k_steps(f32x16_t (&acc)[C::MI][NI], Frags<C>& f0, Frags<C>& f1,
-                                        const FragLanes& L, const GemmArgs& p,
-                                        const Operand<C::NIA>& opA, const Operand<NIB>& opB,
+                                        const FragLanes<C>& L, const GemmArgs& p,
+                                        const Operand<C::NIA>& opA, const Operand<C::NIB>& opB,
                                         uint32_t dma_a, uint32_t dma_b, uint32_t wa, uint32_t wb,
                                         int nk) {
-  constexpr int NST = C::NST, NIA = C::NIA, kSlotA = C::kSlotA, kOffB = C::kOffB;
+  constexpr int NST = C::NST, NIA = C::NIA, NIB = C::NIB, kSlotA = C::kSlotA, kSlotB = C::kSlotB;
+  constexpr int kOffB = C::kOffB, BK = C::BKX;
+  static_assert(!C::WIDE, "narrow ring");
   int slot = 0;
   for (int kt = 0; kt < nk; ++kt) {
     const uint32_t sa = slot * kSlotA + wa, sb = kOffB + slot * kSlotB + wb;
@@ -894,6 +928,71 @@ __device__ __forceinline__ void k_steps(f32x16_t (&acc)[C::MI][NI], Frags<C>& f0
   }
 }
 
+// The K blocks of one tile on the wide ring.  Block j sits in regions
+// (2j) % 5 (A) and (2j + 1) % 5 (B); on entry the regions hold blocks 0 and 1
+// (landed or in flight) and f0 holds block 0's sub-step 0 fragments.
+//   s0: MFMAs of sub-step 0 (f0), sub-step 1's fragments into f1;
+//   s1, s2: MFMAs (f1, then f0), the next sub-step's fragments, and spread
+//       between the MFMAs the DMA of block j + 2's A (load 2j + 4, region
+//       (2j + 4) % 5 = block j - 1's B, read before the previous barrier);
+//   wait until block j + 1 has landed (only block j + 2's A may remain in
+//       flight), barrier: every wave has also finished reading block j;
+//   s3: MFMAs (f1), the DMA of block j + 2's B (load 2j + 5, region (2j) % 5 =
+//       block j's A) and block j + 1's sub-step 0 fragments into f0.
+// Block j + 2's B thus has three sub-steps to land, its A about one block.
+template <int KIND, class C>
+__device__ __forceinline__ void k_blocks(f32x16_t (&acc)[C::MI][NI], Frags<C>& f0, Frags<C>& f1,
+                                         const FragLanes<C>& L, const GemmArgs& p,
+                                         const Operand<C::NIA>& opA, const Operand<C::NIB>& opB,
+                                         uint32_t dma_w, uint32_t wa, uint32_t wb, int nk) {
+  constexpr int R = C::kRegion, NIA = C::NIA, NIB = C::NIB, MI = C::MI;
+  constexpr int NM = MI * NI, NR = MI + NI;
+  static_assert(C::WIDE && C::KSUB == 4, "wide ring");
+  static_assert(NR <= NM && NIA % 2 == 0 && NM % (NIA / 2) == 0 && NM % NIB == 0, "interleave pattern");
+  constexpr int SA = NM / (NIA / 2);  // one A piece every SA MFMAs of s1 and s2
+  constexpr int SB = NM / NIB;        // one B piece every SB MFMAs of s3
+  int ra = 0;                         // (2j) % 5
+  for (int j = 0; j < nk; ++j) {
+    const int rb = ra == 4 ? 0 : ra + 1;    // (2j + 1) % 5
+    const int rn = rb == 4 ? 0 : rb + 1;    // (2j + 2) % 5: block j + 1's A
+    const int rnb = rn == 4 ? 0 : rn + 1;   // (2j + 3) % 5: block j + 1's B
+    const int rq = rnb == 4 ? 0 : rnb + 1;  // (2j + 4) % 5: block j + 2's A
+    const uint32_t sa = ra * R + wa, sb = rb * R + wb;
+    const uint32_t kill = j + 2 < nk ? 0u : kDmaKill;
+    const int k2 = (j + 2) * C::BKX;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      mfma1(acc[m / NI][m % NI], f0.a[m / NI], f0.b[m % NI]);
+      if (m < NR) load_frag<KIND, C>(f1, m, 1, sa, sb, L);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      mfma1(acc[m / NI][m % NI], f1.a[m / NI], f1.b[m % NI]);
+      if (m < NR) load_frag<KIND, C>(f0, m, 2, sa, sb, L);
+      if (m % SA == 0) dma_piece<KIND, C>(p, opA, opB, dma_w + rq * R, 0u, k2, kill, m / SA);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      mfma1(acc[m / NI][m % NI], f0.a[m / NI], f0.b[m % NI]);
+      if (m < NR) load_frag<KIND, C>(f1, m, 3, sa, sb, L);
+      if (m % SA == 0) dma_piece<KIND, C>(p, opA, opB, dma_w + rq * R, 0u, k2, kill, NIA / 2 + m / SA);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vm<NIA>();
+    lds_barrier();  // every wave: block j + 1 landed, block j fully read
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      mfma1(acc[m / NI][m % NI], f1.a[m / NI], f1.b[m % NI]);
+      if (m % SB == 0) dma_piece<KIND, C>(p, opA, opB, 0u, dma_w + ra * R, k2, kill, NIA + m / SB);
+      if (m >= NM - NR) load_frag<KIND, C>(f0, m - (NM - NR), 0, rn * R + wa, rnb * R + wb, L);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    ra = rn;
+  }
+}
+
 // FP8 K loop, on the same ring and DMA schedule as k_steps.  On entry f holds
 // the A blocks mi < MI / 2 and every B block of step 0.  Per step:
 //   phase 1: MFMAs of the blocks mi < MI / 2; between them the A blocks
@@ -906,11 +1005,13 @@ __device__ __forceinline__ void k_steps(f32x16_t (&acc)[C::MI][NI], Frags<C>& f0
 //            half of the DMA of step kt + NST is issued.
 template <int KIND, class C>
 __device__ __forceinline__ void k_steps_f8(f32x16_t (&acc)[C::MI][NI], Frags8<C>& f,
-                                           const FragLanes& L, const GemmArgs& p,
-                                           const Operand<C::NIA>& opA, const Operand<NIB>& opB,
+                                           const FragLanes<C>& L, const GemmArgs& p,
+                                           const Operand<C::NIA>& opA, const Operand<C::NIB>& opB,
                                            uint32_t dma_a, uint32_t dma_b, uint32_t wa, uint32_t wb,
                                            int nk) {
-  constexpr int NST = C::NST, NIA = C::NIA, kSlotA = C::kSlotA, kOffB = C::kOffB, MI = C::MI;
+  constexpr int NST = C::NST, NIA = C::NIA, NIB = C::NIB, kSlotA = C::kSlotA, kSlotB = C::kSlotB;
+  constexpr int kOffB = C::kOffB, MI = C::MI, BK = C::BKX;
+  static_assert(!C::WIDE, "narrow ring");
   constexpr int MH = MI / 2, NP = MH * NI;  // MFMAs per phase
   using D = DmaSplit<C>;
   constexpr int STR = NP / D::NH;           // one DMA piece every STR MFMAs
@@ -1032,16 +1133,16 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p, int work) {
   t.m0 = m0;
   t.kbeg = kbeg;
   t.kend = kend;
-  t.nk = (kend - kbeg + BK - 1) / BK;
+  t.nk = (kend - kbeg + C::BKX - 1) / C::BKX;
   return t;
 }
 
 // Buffer descriptors and per-lane DMA offsets of a tile's operands.
 template <int KIND, class C>
 __device__ __forceinline__ void setup_operands(const GemmArgs& p, const Tile& t, int wave, int lane,
-                                               Operand<C::NIA>& opA, Operand<NIB>& opB) {
+                                               Operand<C::NIA>& opA, Operand<C::NIB>& opB) {
   using Tr = Traits<KIND>;
-  constexpr int BM = C::BM, NIA = C::NIA;
+  constexpr int BM = C::BM, NIA = C::NIA, NIB = C::NIB, BKX = C::BKX;
   const int e = t.e, nt = t.nt, n0 = t.n0, row0 = t.row0, row1 = t.row1, m0 = t.m0;
   const int kbeg = t.kbeg, kend = t.kend;
   if constexpr (KIND == K_WGRAD8) {
@@ -1053,7 +1154,7 @@ __device__ __forceinline__ void setup_operands(const GemmArgs& p, const Tile& t,
 #pragma unroll
     for (int u = 0; u < NIA; ++u) {
       int r, c;
-      kc_rows<NIA>(wave, lane, u, r, c);
+      kc_rows<NIA, BKX>(wave, lane, u, r, c);
       opA.voff[u] = (uint32_t)(r * p.lda * 2 + c * 16);
     }
     opB.rsrc = make_rsrc(p.b0 + (long)n0 * p.ldb + kbeg, (uint32_t)(((long)(p.N - n0) * p.ldb - kbeg) * 2));
@@ -1061,7 +1162,7 @@ __device__ __forceinline__ void setup_operands(const GemmArgs& p, const Tile& t,
 #pragma unroll
     for (int u = 0; u < NIB; ++u) {
       int r, c;
-      kc_rows<NIB>(wave, lane, u, r, c);
+      kc_rows<NIB, BKX>(wave, lane, u, r, c);
       opB.voff[u] = (uint32_t)(r * p.ldb * 2 + c * 16);
     }
     return;
@@ -1073,7 +1174,7 @@ __device__ __forceinline__ void setup_operands(const GemmArgs& p, const Tile& t,
 #pragma unroll
     for (int u = 0; u < NIA; ++u) {
       int r, c;
-      kc_rows<NIA>(wave, lane, u, r, c);
+      kc_rows<NIA, BKX>(wave, lane, u, r, c);
       opA.voff[u] = (uint32_t)(r * p.lda * 2 + c * 16);
     }
   } else {  // WGRAD: A[k = row of the group][m]; rows past the group read as zero
@@ -1097,7 +1198,7 @@ __device__ __forceinline__ void setup_operands(const GemmArgs& p, const Tile& t,
 #pragma unroll
     for (int u = 0; u < NIB; ++u) {
       int r, c;
-      kc_rows<NIB>(wave, lane, u, r, c);
+      kc_rows<NIB, BKX>(wave, lane, u, r, c);
       const int col = nt * 128 + (r >> 6) * 32 + (r & 31);
       opB.voff[u] = (uint32_t)(col * p.ldb * 2 + c * 16);
     }
@@ -1107,7 +1208,7 @@ __device__ __forceinline__ void setup_operands(const GemmArgs& p, const Tile& t,
 #pragma unroll
     for (int u = 0; u < NIB; ++u) {
       int r, c;
-      kc_rows<NIB>(wave, lane, u, r, c);
+      kc_rows<NIB, BKX>(wave, lane, u, r, c);
       opB.voff[u] = (uint32_t)((n0 + r) * p.ldb * 2 + c * 16);
     }
   } else if constexpr (KIND == K_DOWN_DGRAD || KIND == K_GATEUP_DGRAD) {
@@ -1137,39 +1238,55 @@ __device__ __forceinline__ void setup_operands(const GemmArgs& p, const Tile& t,
   }
 }
 
-// Steps 0 .. NST - 2 and the first half of step NST - 1 of a tile into the
-// ring (the ones past K dropped).
+// Narrow ring: steps 0 .. NST - 2 and the first half of step NST - 1 of a
+// tile.  Wide ring: loads 0 .. 3 (A and B of blocks 0 and 1) into regions
+// 0 .. 3.  The ones past K are dropped.
 template <int KIND, class C>
 __device__ __forceinline__ void issue_prologue(const GemmArgs& p, const Operand<C::NIA>& opA,
-                                               const Operand<NIB>& opB, uint32_t dma_a,
+                                               const Operand<C::NIB>& opB, uint32_t dma_a,
                                                uint32_t dma_b, int nk) {
-  constexpr int NST = C::NST, ND = C::NIA + NIB;
+  constexpr int NIA = C::NIA, ND = C::NIA + C::NIB;
+  if constexpr (C::WIDE) {
 #pragma unroll
-  for (int st = 0; st < NST; ++st) {
-    const uint32_t kill = st < nk ? 0u : kDmaKill;
+    for (int blk = 0; blk < 2; ++blk) {
+      const uint32_t kill = blk < nk ? 0u : kDmaKill;
 #pragma unroll
-    for (int u = 0; u < (st < NST - 1 ? ND : ND / 2); ++u)
-      dma_piece<KIND, C>(p, opA, opB, dma_a + st * C::kSlotA, dma_b + st * kSlotB, st * BK, kill, u);
+      for (int u = 0; u < ND; ++u)
+        dma_piece<KIND, C>(p, opA, opB, dma_a + 2 * blk * C::kRegion, dma_b + (2 * blk + 1) * C::kRegion,
+                           blk * C::BKX, kill, u);
+    }
+  } else {
+    constexpr int NST = C::NST;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const uint32_t kill = st < nk ? 0u : kDmaKill;
+#pragma unroll
+      for (int u = 0; u < (st < NST - 1 ? ND : ND / 2); ++u)
+        dma_piece<KIND, C>(p, opA, opB, dma_a + st * C::kSlotA, dma_b + st * C::kSlotB, st * C::BKX, kill,
+                           u);
+    }
   }
 }
 
-template <int KIND, int BM_, bool F8 = false>
+template <int KIND, int BM_, bool F8 = false, bool WIDE = false>
 __global__ __launch_bounds__(NTH)
-__attribute__((amdgpu_waves_per_eu(Cfg<BM_>::kWavesPerSimd, Cfg<BM_>::kWavesPerSimd)))
+__attribute__((amdgpu_waves_per_eu(Cfg<BM_, WIDE>::kWavesPerSimd, Cfg<BM_, WIDE>::kWavesPerSimd)))
 void gemm_kernel(const GemmArgs p) {
   static_assert(!F8 || KIND == K_GATEUP_FWD || KIND == K_DOWN_FWD || KIND == K_WGRAD8,
                 "FP8: K-contiguous products only");
   static_assert(KIND != K_WGRAD8 || F8, "WGRAD8 runs on E4M3 codes");
+  static_assert(!(F8 && WIDE), "the FP8 K loop runs on the narrow ring");
+  static_assert(!(WIDE && k_grouped(KIND)), "wide ring: M-grouped products (K a multiple of 64)");
   using Tr = Traits<KIND>;
-  using C = Cfg<BM_>;
-  constexpr int WM = C::WM, MI = C::MI, NST = C::NST, NIA = C::NIA;
+  using C = Cfg<BM_, WIDE>;
+  constexpr int WM = C::WM, MI = C::MI, NST = C::NST, NIA = C::NIA, NIB = C::NIB;
   constexpr int kOffB = C::kOffB;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const FragLanes L = frag_lanes<C>(lane, wave);
+  const FragLanes<C> L = frag_lanes<C>(lane, wave);
 
   int total;
   if constexpr (k_grouped(KIND))
@@ -1185,10 +1302,10 @@ void gemm_kernel(const GemmArgs p) {
   if (p.tile_ctr != nullptr && tid == 0) ticket = atomicAdd(p.tile_ctr, 1);
   const uint32_t dma_a = lds_addr(g_lds) + wave * NIA * 1024;  // this wave's DMA area
   const uint32_t dma_b = lds_addr(g_lds) + kOffB + wave * NIB * 1024;
-  // wave block bases inside a slot
+  // wave block bases inside a slot or region
   // (MC fragment offsets hold the wave's columns themselves)
-  const uint32_t wa = Tr::A_KC ? (uint32_t)(wm * WM * BK * 2) : 0u;
-  const uint32_t wb = Tr::B_KC ? (uint32_t)(wn * WN * BK * 2) : 0u;
+  const uint32_t wa = Tr::A_KC ? (uint32_t)(wm * WM * C::BKX * 2) : 0u;
+  const uint32_t wb = Tr::B_KC ? (uint32_t)(wn * WN * C::BKX * 2) : 0u;
   constexpr int ND = NIA + NIB;
 
   Tile t = decode_tile<KIND, C>(p, work);
@@ -1210,11 +1327,12 @@ void gemm_kernel(const GemmArgs p) {
       for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16_t{};
 
     if (t.nk > 0) {
-      // Step 0 has landed when only the newer DMAs remain (memory operations
-      // retire in order).  After an epilogue of a known size the wait also
-      // lets those newer operations stay in flight (up to the counter's 63);
-      // otherwise the epilogue's operations only make the wait stronger.
-      constexpr int kFirst = (NST - 2) * ND + ND / 2;
+      // Step (block) 0 has landed when only the newer DMAs remain (memory
+      // operations retire in order).  After an epilogue of a known size the
+      // wait also lets those newer operations stay in flight (up to the
+      // counter's 63); otherwise the epilogue's operations only make the wait
+      // stronger.
+      constexpr int kFirst = C::WIDE ? ND : (NST - 2) * ND + ND / 2;
       constexpr int kEpi = epilogue_vmem_ops<KIND, C, F8>();
       constexpr int kAfter = kEpi < 0 ? kFirst : (kFirst + kEpi > 63 ? 63 : kFirst + kEpi);
       if (C::kSepStage && after_epi && (KIND != K_WGRAD || (p.accumulate == 0 && p.fold == 0)))
@@ -1223,9 +1341,14 @@ void gemm_kernel(const GemmArgs p) {
         wait_vm<kFirst>();
       lds_barrier();
       // Two fragment sets, no copies between them: f0 holds sub-step 0 (read
-      // at the end of the previous step), f1 sub-step 1.
-      static_assert(KSUB == 2, "the fragment pipeline below assumes two k16 sub-steps");
-      if constexpr (F8) {
+      // at the end of the previous step), f1 sub-step 1 (wide ring: f0 and f1
+      // alternate over the four sub-steps).
+      if constexpr (C::WIDE) {
+        Frags<C> f0, f1;
+        load_frags<KIND, C>(f0, 0, wa, C::kRegion + wb, L);
+        k_blocks<KIND, C>(acc, f0, f1, L, p, opA, opB, dma_a, wa, wb, t.nk);
+      } else if constexpr (F8) {
+        static_assert(C::KSUB == 2, "the FP8 pipeline reads two 16-byte halves per K step");
         Frags8<C> f;
 #pragma unroll
         for (int mi = 0; mi < MI / 2; ++mi) {
@@ -1239,6 +1362,7 @@ void gemm_kernel(const GemmArgs p) {
         }
         k_steps_f8<KIND, C>(acc, f, L, p, opA, opB, dma_a, dma_b, wa, wb, t.nk);
       } else {
+        static_assert(C::KSUB == 2, "the fragment pipeline below assumes two k16 sub-steps");
         Frags<C> f0, f1;
         load_frags<KIND, C>(f0, 0, wa, kOffB + wb, L);
         k_steps<KIND, C>(acc, f0, f1, L, p, opA, opB, dma_a, dma_b, wa, wb, t.nk);
@@ -1357,13 +1481,13 @@ static int32_t* ffn_tile_ctrs(void* ws, int R_cap, int E_l) {
   return (int32_t*)((char*)ws + ffn_sched_table_bytes(R_cap, E_l));
 }
 
-template <int KIND, int BM_, bool F8 = false>
+template <int KIND, int BM_, bool F8 = false, bool WIDE = false>
 static hipError_t launch_gemm(const GemmArgs& a, int work_upper, int kernel_id, hipStream_t s) {
-  using C = Cfg<BM_>;
+  using C = Cfg<BM_, WIDE>;
   if (work_upper <= 0) return hipSuccess;
   const int grid = std::min(work_upper, kCUs * C::kWavesPerSimd);  // persistent
   ProfScope ps(kernel_id, s);
-  gemm_kernel<KIND, BM_, F8><<<grid, NTH, C::kLdsBytes, s>>>(a);
+  gemm_kernel<KIND, BM_, F8, WIDE><<<grid, NTH, C::kLdsBytes, s>>>(a);
   return hipGetLastError();
 }
 
@@ -1392,7 +1516,7 @@ hipError_t launch_ffn_fwd_bf16(const bf16_t* x_perm, const int32_t* offsets, int
   g.c0 = h_perm;
   g.ldc = I;
   g.c1 = gu;
-  err = launch_gemm<K_GATEUP_FWD, kBmGrouped>(g, mt_upper * g.n_ntiles, MOE_KERNEL_FFN_GATEUP, s);
+  err = launch_gemm<K_GATEUP_FWD, kBmGrouped, false, kWideGrouped>(g, mt_upper * g.n_ntiles, MOE_KERNEL_FFN_GATEUP, s);
   if (err != hipSuccess) return err;
 
   GemmArgs d{};
@@ -1408,7 +1532,7 @@ hipError_t launch_ffn_fwd_bf16(const bf16_t* x_perm, const int32_t* offsets, int
   d.n_ntiles = (H + BN - 1) / BN;
   d.c0 = y_perm;
   d.ldc = H;
-  return launch_gemm<K_DOWN_FWD, kBmGrouped>(d, mt_upper * d.n_ntiles, MOE_KERNEL_FFN_DOWN, s);
+  return launch_gemm<K_DOWN_FWD, kBmGrouped, false, kWideGrouped>(d, mt_upper * d.n_ntiles, MOE_KERNEL_FFN_DOWN, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -1805,7 +1929,7 @@ hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, cons
   a.gu = gu;
   a.c0 = dgu;
   a.tile_ctr = ctrs + 0;
-  err = launch_gemm<K_DOWN_DGRAD, kBmGrouped>(a, mt_upper * a.n_ntiles, MOE_KERNEL_FFN_DOWN_DGRAD, s);
+  err = launch_gemm<K_DOWN_DGRAD, kBmGrouped, false, kWideGrouped>(a, mt_upper * a.n_ntiles, MOE_KERNEL_FFN_DOWN_DGRAD, s);
   if (err != hipSuccess) return err;
   if (side != nullptr && (err = hipEventRecord(side->mid, s)) != hipSuccess) return err;
 
@@ -1846,7 +1970,7 @@ hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, cons
   c.c0 = dx_perm;
   c.ldc = H;
   c.tile_ctr = ctrs + 2;
-  err = launch_gemm<K_GATEUP_DGRAD, kBmGrouped>(c, mt_upper * c.n_ntiles, MOE_KERNEL_FFN_GATEUP_DGRAD, s);
+  err = launch_gemm<K_GATEUP_DGRAD, kBmGrouped, false, kWideGrouped>(c, mt_upper * c.n_ntiles, MOE_KERNEL_FFN_GATEUP_DGRAD, s);
   if (err != hipSuccess) return err;
 
   // dW_gate[e] = dG_e^T X_e, dW_up[e] = dU_e^T X_e (one product with M = 2I).

@@ -8,30 +8,41 @@
 
 namespace moe {
 
-constexpr int BK = 32;        // K step of a tile (bf16 elements)
-constexpr int KCH = BK / 8;   // 16-byte chunks per K-contiguous row
+constexpr int BK = 32;        // K step of the 4-slot ring (bf16 elements)
+constexpr int KCH = BK / 8;   // 16-byte chunks per K-contiguous row of that ring
 
-// KC tile [rows][32]: rows are 64 bytes, four per 256-byte line of the 64
-// LDS banks.  The 16 lanes of one ds_read_b128 phase read the same logical
-// chunk of 16 consecutive rows; XOR with (r / 4) % 4 puts them on 16 distinct
-// 16-byte bank groups (measured on gfx950: the XOR with (r / 2) % 4 that
-// suits 32 banks loses about 28% of the LDS read rate to conflicts).
-__host__ __device__ __forceinline__ int kc_swz(int r) { return (r >> 2) & 3; }
-// first element of logical 16-byte chunk `chunk` of row r
-__host__ __device__ __forceinline__ int kc_idx(int r, int chunk) {
-  return r * BK + ((chunk ^ kc_swz(r)) << 3);
+// K-contiguous tiles hold rows of BKX bf16: BKX = 32 (64-byte rows, the K step
+// of the 4-slot ring) or BKX = 64 (128-byte rows, the K block of the 5-region
+// ring: each DMA row is one whole 128-byte cache line).
+//   BKX = 32: four rows per 256-byte line of the 64 LDS banks.  The 16 lanes
+//   of one ds_read_b128 phase read the same logical chunk of 16 consecutive
+//   rows; XOR with (r / 4) % 4 puts them on 16 distinct 16-byte bank groups
+//   (measured on gfx950: the XOR with (r / 2) % 4 that suits 32 banks loses
+//   about 28% of the LDS read rate to conflicts).
+//   BKX = 64: two rows per bank line; XOR with (r / 2) % 8 gives the 16 rows
+//   of a phase the 16 pairs (r % 2, chunk position).
+template <int BKX = BK>
+__host__ __device__ __forceinline__ int kc_swz(int r) {
+  static_assert(BKX == 32 || BKX == 64, "K-contiguous row length");
+  return BKX == 32 ? (r >> 2) & 3 : (r >> 1) & 7;
 }
-// MC tile [BK][W]: LDS position of logical 16-byte chunk c of row k (and back).
+// first element of logical 16-byte chunk `chunk` of row r
+template <int BKX = BK>
+__host__ __device__ __forceinline__ int kc_idx(int r, int chunk) {
+  return r * BKX + ((chunk ^ kc_swz<BKX>(r)) << 3);
+}
+// MC tile [BKX][W] (rows = k): LDS position of logical 16-byte chunk c of row k (and back).
 __host__ __device__ __forceinline__ int mc_chunk(int k, int c) { return c ^ ((k & 3) << 2); }
 
 // KC operand: DMA instruction u of wave w covers 16-byte LDS chunks
-// p = (w*N + u)*64 + lane, i.e. tile row p/KCH, LDS chunk p%KCH, which holds
-// the logical k chunk (p%KCH) ^ swz(row).
-template <int N>
+// p = (w*N + u)*64 + lane, i.e. tile row p/(BKX/8), LDS chunk p%(BKX/8), which
+// holds the logical k chunk (p%(BKX/8)) ^ swz(row).
+template <int N, int BKX = BK>
 __host__ __device__ __forceinline__ void kc_rows(int wave, int lane, int u, int& row, int& chunk) {
+  constexpr int ch = BKX / 8;
   const int p = (wave * N + u) * 64 + lane;
-  row = p / KCH;
-  chunk = (p % KCH) ^ kc_swz(row);
+  row = p / ch;
+  chunk = (p % ch) ^ kc_swz<BKX>(row);
 }
 
 // MC operand of width W: chunk p -> k row p / (W/8), LDS chunk p % (W/8),
@@ -46,9 +57,10 @@ __host__ __device__ __forceinline__ void mc_rows(int wave, int lane, int u, int&
 // Byte offset of a lane's KC fragment for k16 sub-step s inside a 32-row
 // block: lane l reads row l % 32, logical chunk 2 s + l / 32; the block's
 // first row (a multiple of 16) does not change the swizzle.
+template <int BKX = BK>
 __host__ __device__ __forceinline__ uint32_t kc_lane_offset(int lane, int s) {
   const int r = lane & 31;
-  return (uint32_t)(r * BK * 2 + (((2 * s + (lane >> 5)) ^ kc_swz(r)) << 4));
+  return (uint32_t)(r * BKX * 2 + (((2 * s + (lane >> 5)) ^ kc_swz<BKX>(r)) << 4));
 }
 
 // Byte offset of a lane's first transposing read (ds_read_b64_tr_b16) of the

@@ -6,9 +6,11 @@
 //
 // What the reads must deliver (the 32x32x16 bf16 MFMA operand layout): lane l
 // of a 32-row (or 32-column) block holds row (column) l % 32 and the eight
-// consecutive k values 8 (l / 32) .. + 7 of the k16 sub-step.
-//   K-contiguous tiles ([rows][32] bf16): one ds_read_b128 per fragment.
-//   MN-contiguous tiles ([32 k][W] bf16): two ds_read_b64_tr_b16, k and k + 4;
+// consecutive k values 8 (l / 32) .. + 7 of the k16 sub-step.  Both ring
+// depths are checked: K steps of 32 (64-byte K-contiguous rows, 32-row MN
+// tiles) and K blocks of 64 (128-byte rows, 64-row MN tiles).
+//   K-contiguous tiles ([rows][BKX] bf16): one ds_read_b128 per fragment.
+//   MN-contiguous tiles ([BKX k][W] bf16): two ds_read_b64_tr_b16, k and k + 4;
 //   within each 16-lane group lane i supplies the address of row kb + i / 4,
 //   columns c0 + 4 (i % 4) .. + 3, and lane j of the group receives the four k
 //   values of column c0 + j.
@@ -38,33 +40,42 @@ static int failures = 0;
   } while (0)
 
 // ---------------------------------------------------------------- KC tiles
-// rows: tile rows (BM or BN); N: DMA instructions per wave; wave_rows: rows of
-// one wave's sub-tile, waves_along: which wave index selects the row block.
-template <int N>
+// rows: tile rows (BM or BN); N: DMA instructions per wave; BKX: row length.
+template <int N, int BKX>
 static void check_kc(int rows, const char* what) {
-  const int chunks = rows * KCH;
+  constexpr int ch = BKX / 8;  // 16-byte chunks per row
+  const int chunks = rows * ch;
   CHECK(4 * N * 64 == chunks, "%s: 4 waves x %d DMA x 64 lanes != %d chunks", what, N, chunks);
   std::vector<std::pair<int, int>> content(chunks, {-1, -1});  // LDS chunk -> (row, logical chunk)
   std::set<std::pair<int, int>> seen;
   for (int w = 0; w < 4; ++w)
-    for (int u = 0; u < N; ++u)
+    for (int u = 0; u < N; ++u) {
+      std::set<int> lines;  // rows (global 128-byte lines) one instruction touches
       for (int l = 0; l < 64; ++l) {
         int r, c;
-        kc_rows<N>(w, l, u, r, c);
+        kc_rows<N, BKX>(w, l, u, r, c);
         const int p = (w * N + u) * 64 + l;  // the DMA writes lds + 16 * lane
-        CHECK(r >= 0 && r < rows && c >= 0 && c < KCH, "%s: DMA chunk %d -> (%d, %d) outside", what, p, r, c);
+        CHECK(r >= 0 && r < rows && c >= 0 && c < ch, "%s: DMA chunk %d -> (%d, %d) outside", what, p, r, c);
         content[p] = {r, c};
         CHECK(seen.insert({r, c}).second, "%s: logical chunk (%d, %d) loaded twice", what, r, c);
         // the element index kc_idx names is where that logical chunk sits
-        CHECK(kc_idx(r, c) == p * 8, "%s: kc_idx(%d, %d) = %d, DMA put it at %d", what, r, c, kc_idx(r, c), p * 8);
+        CHECK(kc_idx<BKX>(r, c) == p * 8, "%s: kc_idx(%d, %d) = %d, DMA put it at %d", what, r, c,
+              kc_idx<BKX>(r, c), p * 8);
+        // a row's BKX * 2 bytes of one step start at a multiple of BKX * 2
+        // (<= 128) in memory, so they lie in one 128-byte line
+        lines.insert(r);
       }
+      // 1 KiB per instruction: 16 half lines (BKX = 32) or 8 whole lines (64)
+      CHECK((int)lines.size() == 1024 / (BKX * 2), "%s: instruction %d of wave %d touches %zu rows", what, u, w,
+            lines.size());
+    }
   CHECK((int)seen.size() == chunks, "%s: %zu of %d chunks loaded", what, seen.size(), chunks);
-  // fragment reads: every 32-row block, both sub-steps
+  // fragment reads: every 32-row block, every k16 sub-step
   for (int blk = 0; blk < rows / 32; ++blk)
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < BKX / 16; ++s) {
       std::vector<int> addr(64);
       for (int l = 0; l < 64; ++l) {
-        const uint32_t a = (uint32_t)(blk * 32 * BK * 2) + kc_lane_offset(l, s);
+        const uint32_t a = (uint32_t)(blk * 32 * BKX * 2) + kc_lane_offset<BKX>(l, s);
         addr[l] = (int)a;
         CHECK(a % 16 == 0, "%s: unaligned fragment read", what);
         const std::pair<int, int> want = {blk * 32 + (l & 31), 2 * s + (l >> 5)};
@@ -81,10 +92,10 @@ static void check_kc(int rows, const char* what) {
 }
 
 // ---------------------------------------------------------------- MC tiles
-template <int N, int W>
+template <int N, int W, int BKX>
 static void check_mc(const char* what) {
   constexpr int cpr = W / 8;  // 16-byte chunks per k row
-  const int chunks = BK * cpr;
+  const int chunks = BKX * cpr;
   CHECK(4 * N * 64 == chunks, "%s: 4 waves x %d DMA x 64 lanes != %d chunks", what, N, chunks);
   std::vector<std::pair<int, int>> content(chunks, {-1, -1});  // LDS chunk -> (k, logical chunk)
   std::set<std::pair<int, int>> seen;
@@ -94,7 +105,7 @@ static void check_mc(const char* what) {
         int k, c;
         mc_rows<N, W>(w, l, u, k, c);
         const int p = (w * N + u) * 64 + l;
-        CHECK(k >= 0 && k < BK && c >= 0 && c < cpr, "%s: DMA chunk %d -> (%d, %d) outside", what, p, k, c);
+        CHECK(k >= 0 && k < BKX && c >= 0 && c < cpr, "%s: DMA chunk %d -> (%d, %d) outside", what, p, k, c);
         CHECK(p / cpr == k, "%s: chunk %d is not in row %d", what, p, k);
         content[p] = {k, c};
         CHECK(seen.insert({k, c}).second, "%s: logical chunk (%d, %d) loaded twice", what, k, c);
@@ -109,7 +120,7 @@ static void check_mc(const char* what) {
     CHECK(content[k * cpr + lds_chunk].first == k, "%s: chunk holds another row", what);
   };
   for (int M = 0; M < W / 32; ++M)
-    for (int s = 0; s < 2; ++s)
+    for (int s = 0; s < BKX / 16; ++s)
       for (int half = 0; half < 2; ++half) {  // the read of k .. k+3, then k+4 .. k+7
         std::vector<uint32_t> addr(64);
         for (int l = 0; l < 64; ++l) {
@@ -163,13 +174,17 @@ static void check_stage() {
 }
 
 int main() {
-  // K-contiguous: A of the 256-row and 128-row tiles (4 and 2 DMA per wave),
-  // B of 256 columns (4 DMA per wave)
-  check_kc<4>(256, "KC 256 rows");
-  check_kc<2>(128, "KC 128 rows");
+  // K-contiguous, K step 32: A of the 256-row and 128-row tiles (4 and 2 DMA
+  // per wave), B of 256 columns (4 DMA per wave)
+  check_kc<4, 32>(256, "KC 256 rows");
+  check_kc<2, 32>(128, "KC 128 rows");
+  // K-contiguous, K block 64: 256 rows or columns (8 DMA per wave)
+  check_kc<8, 64>(256, "KC2 256 rows");
   // MN-contiguous: the 256-wide B tile and the weight gradients' A tiles
-  check_mc<4, 256>("MC width 256");
-  check_mc<2, 128>("MC width 128");
+  check_mc<4, 256, 32>("MC width 256");
+  check_mc<2, 128, 32>("MC width 128");
+  // MN-contiguous, K block 64: the data gradients' 256-wide B tile
+  check_mc<8, 256, 64>("MC2 width 256");
   check_stage();
   if (failures) {
     printf("%d failed checks\n", failures);

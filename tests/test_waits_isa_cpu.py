@@ -10,9 +10,13 @@ assembly on the CPU (hipcc, no GPU), read the DMA and wait sequence the
 compiler actually emitted, replay it against a FIFO model of the issue order
 the kernels document, and require every wait to be correct and tight:
 
-* grouped GEMM, steady state: each K step issues one step's DMA (ND instructions,
-  half before and half after the wait); the wait before the barrier leaves only
-  the steps newer than the one about to be read in flight;
+* grouped GEMM, narrow ring (K steps of 32), steady state: each K step issues
+  one step's DMA (ND instructions, half before and half after the wait); the
+  wait before the barrier leaves only the steps newer than the one about to be
+  read in flight;
+* grouped GEMM, wide ring (K blocks of 64, five regions): the prologue loads
+  A and B of blocks 0 and 1; block j issues block j + 2's A before its wait
+  and block j + 2's B after it, and the wait must leave only that A in flight;
 * grouped GEMM, tile change: the next tile's prologue is issued before the
   current tile's epilogue, so the first wait of the next K loop counts the
   epilogue's vector memory instructions too.  Their number in the compiled
@@ -120,23 +124,27 @@ class Fifo:
         return label in self.q
 
 
-# gemm_kernel<KIND, BM, FP8>: KIND 0 gate/up, 1 down, 2 down data gradient,
-# 3 gate/up data gradient, 4 weight gradient, 5 FP8 weight gradient.  Per-lane
+# gemm_kernel<KIND, BM, FP8, WIDE>: KIND 0 gate/up, 1 down, 2 down data gradient,
+# 3 gate/up data gradient, 4 weight gradient, 5 FP8 weight gradient; the bf16
+# M-grouped products (KIND 0-3) run on the wide ring.  Per-lane
 # vector memory instructions of one epilogue, as the kernel counts them (stores
 # per 16-row half pass, times 2 MI passes), and the FP8 scale loads of the next
 # tile.  The FP8 weight gradient does not count its epilogue (None): its first
 # wait after a tile change is the plain one.
 def _design(kind, bm, fp8):
     mi = bm // 64
+    wide = kind <= 3 and bm == 256 and not fp8
     nst = 4 if bm == 256 else 3
-    nia, nib = bm * 32 * 2 // 4096, 4
+    bkx = 64 if wide else 32
+    nia, nib = bm * bkx * 2 // 4096, 256 * bkx * 2 // 4096
     epi = {0: 12 * mi, 1: 8 * mi, 2: 32 * mi, 3: 8 * mi, 4: 16 * mi, 5: None}[kind]
     scales = 0
     if fp8:
         nr = 4 * mi if kind == 0 else 8 * mi
         nc = 16 if kind == 0 else 8
         scales = nr + nc // 4
-    return {"nst": nst, "nd": nia + nib, "epi": epi, "scales": scales, "sep": bm == 256}
+    return {"nst": nst, "nd": nia + nib, "nia": nia, "epi": epi, "scales": scales, "sep": bm == 256,
+            "wide": wide}
 
 
 GEMM_KERNELS = [(0, 256, False), (1, 256, False), (2, 256, False), (3, 256, False), (4, 256, False),
@@ -145,7 +153,8 @@ GEMM_KERNELS_ALL = GEMM_KERNELS + [(5, 256, True)]
 
 
 def _gemm_body(gemm_asm, kind, bm, fp8):
-    pat = r"gemm_kernelILi%dELi%dELb%dE" % (kind, bm, int(fp8))
+    wide = _design(kind, bm, fp8)["wide"]
+    pat = r"gemm_kernelILi%dELi%dELb%dELb%dE" % (kind, bm, int(fp8), int(wide))
     f = _functions(gemm_asm, pat)
     assert len(f) == 1, (pat, list(f))
     return next(iter(f.values()))
@@ -177,6 +186,9 @@ def test_gemm_ring_waits_are_correct_and_tight(gemm_asm, kind, bm, fp8):
     with the DMA counts and wait values taken from the compiled kernel."""
     d = _design(kind, bm, fp8)
     ev = _events(_gemm_body(gemm_asm, kind, bm, fp8))
+    if d["wide"]:
+        _check_wide_ring(ev, d)
+        return
     nst, nd = d["nst"], d["nd"]
     dmas = [e for e in ev if e == "D"]
     # prologue (steps 0 .. NST-2 and half of NST-1) twice, one K step's DMA in the loop
@@ -250,6 +262,79 @@ def test_gemm_ring_waits_are_correct_and_tight(gemm_asm, kind, bm, fp8):
         f.issue("epilogue", k_epi)
         prologue(f, 1)
         k_loop_steps(f, 1, 24, k_first)
+
+
+def _check_wide_ring(ev, d):
+    """The wide ring: loads are labelled (tile, block, operand).  The prologue
+    issues A and B of blocks 0 and 1 (NIA + NIB instructions each pair); in
+    block j the kernel issues block j + 2's A (NIA), waits, and issues block
+    j + 2's B (NIB).  The wait before block j + 1's fragments are read must
+    leave block j + 1 landed and be tight; the first wait of a tile (plain, or
+    after the previous epilogue's counted operations) must cover block 0."""
+    nd, nia = d["nd"], d["nia"]
+    nib = nd - nia
+    dmas = [e for e in ev if e == "D"]
+    # prologue twice (first tile, next tile), one block's two DMA groups in the loop
+    assert len(dmas) == 2 * 2 * nd + nd, (len(dmas), d)
+    waits = [e for e in ev if isinstance(e, int) and e > 0]
+    k_first, k_loop = nd, nia
+    assert k_first in waits and k_loop in waits, (waits, k_first, k_loop)
+    k_epi = d["epi"] + d["scales"]
+    k_after = min(VMCNT_MAX, k_first + k_epi)
+    assert k_after in waits, (waits, k_after)
+    # inside the loop exactly one wait, between the two DMA groups
+    # (the innermost loop header: the tile loop's comes first)
+    hdr = max(i for i, e in enumerate(ev) if e == "L")
+    end = next(i for i in range(hdr, len(ev)) if ev[i] == 0)
+    body = ev[hdr + 1:end]
+    assert body == ["D"] * nia + [k_loop] + ["D"] * nib, body
+
+    def prologue(f, tile):
+        for blk in range(2):
+            f.issue((tile, blk, "A"), nia)
+            f.issue((tile, blk, "B"), nib)
+
+    def landed(f, tile, blk):
+        return not f.pending((tile, blk, "A")) and not f.pending((tile, blk, "B"))
+
+    def k_blocks(f, tile, nk, first_wait):
+        f.wait(first_wait)
+        assert landed(f, tile, 0)
+        for j in range(nk):
+            f.issue((tile, j + 2, "A"), nia)
+            before = list(f.q)
+            f.wait(k_loop)
+            if j + 1 < nk:
+                assert landed(f, tile, j + 1), (j, f.q)
+                if "epilogue" not in before:
+                    probe = Fifo()
+                    probe.q = before
+                    probe.wait(k_loop + 1)
+                    assert not landed(probe, tile, j + 1), "wait not tight"
+            f.issue((tile, j + 2, "B"), nib)
+        f.wait(0)
+
+    f = Fifo()
+    prologue(f, 0)
+    before = list(f.q)
+    k_blocks(f, 0, 12, k_first)
+    probe = Fifo()
+    probe.q = before
+    probe.wait(k_first + 1)
+    assert not landed(probe, 0, 0), "first wait not tight"
+    prologue(f, 1)
+    f.issue("epilogue", k_epi)
+    before = list(f.q)
+    k_blocks(f, 1, 12, k_after)
+    if k_first + k_epi <= VMCNT_MAX:
+        probe = Fifo()
+        probe.q = before
+        probe.wait(k_after + 1)
+        assert not landed(probe, 1, 0), "wait after the epilogue not tight"
+    for nk in (1, 2, 3):  # short tiles: the killed loads past K still count
+        g = Fifo()
+        prologue(g, 2)
+        k_blocks(g, 2, nk, k_first)
 
 
 @pytest.mark.parametrize("kind,bm,fp8", [(2, 256, False), (3, 256, False), (4, 256, False),
