@@ -36,7 +36,8 @@ SECONDARY_WORKLOAD = "full_t16384_h2048_i768_e128_k8"
 
 KERNELS = ["ROUTE", "PERMUTE_HIST", "PERMUTE_SCAN", "PERMUTE_SCATTER", "FFN_GATEUP", "FFN_DOWN",
            "COMBINE", "COMBINE_BWD", "ROUTE_BWD_DZ", "ROUTE_BWD_DW", "FFN_DOWN_DGRAD",
-           "FFN_DOWN_WGRAD", "FFN_GATEUP_DGRAD", "FFN_GATEUP_WGRAD", "COMBINE_DX"]
+           "FFN_DOWN_WGRAD", "FFN_GATEUP_DGRAD", "FFN_GATEUP_WGRAD", "COMBINE_DX", "ROUTE_BWD_DX",
+           "COMBINE_ADD"]
 
 
 def step_flops(w, R):
@@ -64,6 +65,10 @@ def kernel_work(name, w, R, launches, A=None):
         "COMBINE_BWD": (0, A * H * b + 2 * R * H * b + T * k * 12),
         "ROUTE_BWD_DZ": (0, T * k * 12 + T * E * 4 + T * 2 * E * 2),
         "COMBINE_DX": (2.0 * T * k * H, R * H * b + E * H * b + T * k * 16 + T * H * b),
+        # dense product over all E columns (the method's work is the k kept ones)
+        "ROUTE_BWD_DX": (2.0 * T * k * H, T * 2 * E * 2 + H * E * b + T * H * 4),
+        # unweighted unpermute-reduce plus an fp32 addend row per token
+        "COMBINE_ADD": (0, R * H * b + T * k * 4 + T * H * 4 + T * H * b),
         "ROUTE_BWD_DW": (2.0 * T * H * E, T * H * b + T * 2 * E * 2 + H * E * 4),
         "FFN_DOWN_DGRAD": (2.0 * R * H * I, R * H * b + El * H * I * b + 2 * R * 2 * I * b),
         "FFN_DOWN_WGRAD": (2.0 * R * H * I, R * H * b + R * I * b + El * H * I * 4),

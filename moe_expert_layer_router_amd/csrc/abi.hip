@@ -758,10 +758,17 @@ int moe_route_bwd(const float* d_topk_w, const float* topk_w, const int32_t* top
     partials = (float*)w;
   }
   hipError_t e = hipSuccess;
-  if (T > 0 && dx_router != nullptr) e = launch_transpose(w_router, wt, H, E, elem_bytes(dtype), s);
+  // bf16 with E % 64 == 0: dx_router as an MFMA product of the split logit
+  // gradient with W_r itself (no transpose, no per-token gather)
+  const bool dx_mfma = bf16 && dx_router != nullptr && router_dx_mfma_ok(H, E);
+  if (T > 0 && dx_router != nullptr && !dx_mfma)
+    e = launch_transpose(w_router, wt, H, E, elem_bytes(dtype), s);
   if (e == hipSuccess && T > 0)
-    e = launch_route_bwd_dz(d_topk_w, topk_w, topk_idx, wt, T, H, E, k, bf16, d_logits, dx_router,
-                            (bf16 && dw_router != nullptr) ? dz_hilo : nullptr, s);
+    e = launch_route_bwd_dz(d_topk_w, topk_w, topk_idx, wt, T, H, E, k, bf16, d_logits,
+                            dx_mfma ? nullptr : dx_router,
+                            (bf16 && (dw_router != nullptr || dx_mfma)) ? dz_hilo : nullptr, s);
+  if (e == hipSuccess && T > 0 && dx_mfma)
+    e = launch_router_dx(dz_hilo, (const bf16_t*)w_router, T, H, E, dx_router, s);
   if (e == hipSuccess && dw_router != nullptr) {
     if (bf16) {
       if (T > 0) {

@@ -411,7 +411,7 @@ hipError_t launch_combine(const void* y_perm, const float* topk_w, const int32_t
                           const float* addend, int T, int H, int k, bool bf16, void* y,
                           hipStream_t s) {
   const int blocks = (T + 3) / 4;
-  ProfScope ps(MOE_KERNEL_COMBINE, s);
+  ProfScope ps(addend != nullptr ? MOE_KERNEL_COMBINE_ADD : MOE_KERNEL_COMBINE, s);
   if (bf16)
     combine_kernel<true><<<blocks, 256, 0, s>>>(y_perm, topk_w, dest_row, addend, T, H, k, y);
   else

@@ -270,6 +270,11 @@ hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, cons
 hipError_t launch_dw_router_bf16(const bf16_t* x, const bf16_t* dz_hilo, int T, int H, int E,
                                  int nsplit, int32_t* split_offsets, float* partials,
                                  hipStream_t s);
+// dx_router [T][H] fp32 = [dz_hi | dz_lo] . [W_r | W_r]^T on the matrix cores
+// (dz_hilo [T][2E], W_r [H][E] bf16); needs router_dx_mfma_ok(H, E).
+bool router_dx_mfma_ok(int H, int E);
+hipError_t launch_router_dx(const bf16_t* dz_hilo, const bf16_t* w_router, int T, int H, int E,
+                            float* dx_router, hipStream_t s);
 
 // gemm_f32.hip (plain fp32 kernels for the fp32 path)
 hipError_t launch_ffn_fwd_f32(const float* x_perm, const int32_t* offsets, int E_l, int R_cap,

@@ -10,6 +10,7 @@
 //   DOWN_DGRAD   [dG dU] = SiLU'(dY_e W_down)               M-grouped, fused SiLU' epilogue
 //   GATEUP_DGRAD dX_e = dG W_gate + dU W_up                 M-grouped
 //   WGRAD        dW_e = A_e^T B_e over the expert's rows    K-grouped, fp32 out
+//   ROUTER_DX    dx_router = [dz_hi dz_lo] [W_r W_r]^T      one group of T rows, fp32 out
 // and, with FP8 = true, the two forward products on E4M3 codes (below).
 // "M-grouped": each expert owns a contiguous row range of the grouped buffer
 // and a tile table (built on the device from the offsets) maps M tiles to
@@ -137,7 +138,8 @@ constexpr int kBmWgradDown = 128;
 
 enum GemmKind {
   K_GATEUP_FWD = 0, K_DOWN_FWD = 1, K_DOWN_DGRAD = 2, K_GATEUP_DGRAD = 3, K_WGRAD = 4,
-  K_WGRAD8 = 5  // FP8 weight gradient: K-grouped, both operands K-contiguous codes
+  K_WGRAD8 = 5,   // FP8 weight gradient: K-grouped, both operands K-contiguous codes
+  K_ROUTER_DX = 6  // router input gradient: T token rows, K = 2E, B = W_r read twice
 };
 constexpr bool k_grouped(int kind) { return kind == K_WGRAD || kind == K_WGRAD8; }
 
@@ -184,7 +186,8 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 template <int KIND> struct Traits {
   static constexpr bool A_KC = KIND != K_WGRAD;
-  static constexpr bool B_KC = KIND == K_GATEUP_FWD || KIND == K_DOWN_FWD || KIND == K_WGRAD8;
+  static constexpr bool B_KC =
+      KIND == K_GATEUP_FWD || KIND == K_DOWN_FWD || KIND == K_WGRAD8 || KIND == K_ROUTER_DX;
 };
 
 // LDS layouts of the tiles (swizzles, DMA placement, fragment offsets):
@@ -241,6 +244,10 @@ __device__ __forceinline__ void dma_piece(const GemmArgs& p, const Operand<C::NI
     const bool up = k0 >= p.I;
     const uint32_t kk = (uint32_t)(up ? k0 - p.I : k0);
     dma16(up ? opB.rsrc2 : opB.rsrc, (opB.voff[v] + kk * opB.kstep) | kill, lb + v * 1024);
+  } else if constexpr (KIND == K_ROUTER_DX) {
+    // columns k and E + k of the product both read W_r's column k (p.I = E)
+    const uint32_t kk = (uint32_t)(k0 >= p.I ? k0 - p.I : k0);
+    dma16(opB.rsrc, (opB.voff[v] + kk * 2) | kill, lb + v * 1024);
   } else {
     dma16(opB.rsrc, (opB.voff[v] + (uint32_t)k0 * opB.kstep) | kill, lb + v * 1024);
   }
@@ -770,6 +777,33 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
         // the next half reuses the staging area
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
+  } else if constexpr (KIND == K_ROUTER_DX) {
+    // fp32 rows [row0, row1) of dx_router: as the weight gradients' overwriting
+    // epilogue, each store instruction writes 256 contiguous bytes of a row
+    // (lane l: columns 4 (l % 16) .. + 3 and 64 more); rows past the tile fall
+    // outside the descriptor's range, columns past N take the kill offset.
+    const out_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(p.f0 + (long)row0 * p.ldc, 0,
+                                                            (int)((row1 - row0) * p.ldc * 4), 0x00020000);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        stage_half(st, acc, mi, h, lane);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int r = it * 4 + (lane >> 4);
+          const int lrow = wm * WM + mi * 32 + 16 * h + r;
+          const int c = (lane & 15) * 4;
+          const int n = n0 + wn * WN + c;
+          const f32x4_t a = *reinterpret_cast<const f32x4_t*>(&st[stage_idx(r, c)]);
+          const f32x4_t b = *reinterpret_cast<const f32x4_t*>(&st[stage_idx(r, c + 64)]);
+          const uint32_t oa = n < p.N ? (uint32_t)((lrow * p.ldc + n) * 4) : kOutKill;
+          const uint32_t ob = n + 64 < p.N ? (uint32_t)((lrow * p.ldc + n + 64) * 4) : kOutKill;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, a), ro, oa, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, b), ro, ob, 0, 0);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      }
   } else if constexpr (KIND == K_GATEUP_FWD) {
     // staged columns: [g 32 | u 32 | g 32 | u 32] for h columns nt*128 + wn*64 + 0..63
     const out_rsrc_t rh = out_rsrc(p.c0, row0, row1, p.ldc);
@@ -1070,6 +1104,7 @@ __host__ __device__ constexpr int epilogue_vmem_ops() {
          (KIND == K_GATEUP_FWD   ? 12 * C::MI   // 3 stores x 2 rows x 2 halves per block row
           : KIND == K_DOWN_DGRAD ? 32 * C::MI   // 2 loads + 2 stores x 4 rows x 2 halves
           : KIND == K_WGRAD      ? 16 * C::MI   // overwrite: 2 stores x 4 rows x 2 halves
+          : KIND == K_ROUTER_DX  ? 16 * C::MI   // 2 stores x 4 rows x 2 halves
                                  : 8 * C::MI);  // 1 store x 4 rows x 2 halves
 }
 
@@ -1106,6 +1141,14 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p, int work) {
       kbeg = min(e * p.split_rows, p.ktot);
       kend = min(kbeg + p.split_rows, p.ktot);
     }
+  } else if constexpr (KIND == K_ROUTER_DX) {
+    // one group: tiles of BM consecutive rows
+    const int mt = work / p.n_ntiles;
+    nt = work - mt * p.n_ntiles;
+    e = 0;
+    row0 = mt * BM;
+    row1 = min(row0 + BM, p.M);
+    kend = p.K;
   } else {
     const int mt = work / p.n_ntiles;
     nt = work - mt * p.n_ntiles;
@@ -1225,6 +1268,16 @@ __device__ __forceinline__ void setup_operands(const GemmArgs& p, const Tile& t,
       const int col = min(n0 + c * 8, p.N - 8);
       opB.voff[u] = (uint32_t)(r * p.ldb * 2 + col * 2);
     }
+  } else if constexpr (KIND == K_ROUTER_DX) {
+    // B[n][k] = W_r[n][k mod E]: rows of W_r [N][E], K-contiguous
+    opB.rsrc = make_rsrc(p.b0, (uint32_t)(p.N * p.ldb * 2));
+    opB.kstep = 2;
+#pragma unroll
+    for (int u = 0; u < NIB; ++u) {
+      int r, c;
+      kc_rows<NIB, BKX>(wave, lane, u, r, c);
+      opB.voff[u] = (uint32_t)((n0 + r) * p.ldb * 2 + c * 16);
+    }
   } else {  // WGRAD B
     opB.rsrc = make_rsrc(p.b0 + (long)kbeg * p.ldb, (uint32_t)((kend - kbeg) * p.ldb * 2));
     opB.kstep = (uint32_t)(p.ldb * 2);
@@ -1277,6 +1330,7 @@ void gemm_kernel(const GemmArgs p) {
   static_assert(KIND != K_WGRAD8 || F8, "WGRAD8 runs on E4M3 codes");
   static_assert(!(F8 && WIDE), "the FP8 K loop runs on the narrow ring");
   static_assert(!(WIDE && k_grouped(KIND)), "wide ring: M-grouped products (K a multiple of 64)");
+  static_assert(KIND != K_ROUTER_DX || (WIDE && !F8), "the router product runs on the wide ring");
   using Tr = Traits<KIND>;
   using C = Cfg<BM_, WIDE>;
   constexpr int WM = C::WM, MI = C::MI, NST = C::NST, NIA = C::NIA, NIB = C::NIB;
@@ -1291,6 +1345,8 @@ void gemm_kernel(const GemmArgs p) {
   int total;
   if constexpr (k_grouped(KIND))
     total = p.groups * p.n_mtiles * p.n_ntiles;
+  else if constexpr (KIND == K_ROUTER_DX)
+    total = p.n_mtiles * p.n_ntiles;
   else
     total = p.sched[0] * p.n_ntiles;
 
@@ -2026,6 +2082,30 @@ hipError_t launch_dw_router_bf16(const bf16_t* x, const bf16_t* dz_hilo, int T, 
   w.f_group_stride = (long)H * w.ldc;
   w.accumulate = 0;
   return launch_gemm<K_WGRAD, kBmWgrad>(w, nsplit * w.n_mtiles * w.n_ntiles, MOE_KERNEL_ROUTE_BWD_DW, s);
+}
+
+bool router_dx_mfma_ok(int H, int E) { return H % 64 == 0 && E > 0 && E % 64 == 0; }
+
+hipError_t launch_router_dx(const bf16_t* dz_hilo, const bf16_t* w_router, int T, int H, int E,
+                            float* dx_router, hipStream_t s) {
+  if (!router_dx_mfma_ok(H, E)) return hipErrorInvalidValue;
+  GemmArgs a{};
+  a.a = dz_hilo;     // [T][2E]: high halves, then low halves
+  a.lda = 2 * E;
+  a.b0 = w_router;   // [H][E]
+  a.b1 = w_router;
+  a.ldb = E;
+  a.M = T;
+  a.N = H;
+  a.K = 2 * E;       // a multiple of 64, and a K block never straddles E
+  a.I = E;
+  a.n_mtiles = (T + kBmGrouped - 1) / kBmGrouped;
+  a.n_ntiles = (H + BN - 1) / BN;
+  a.f0 = dx_router;  // [T][H]
+  a.ldc = H;
+  a.tile_ctr = nullptr;
+  return launch_gemm<K_ROUTER_DX, kBmGrouped, false, true>(a, a.n_mtiles * a.n_ntiles,
+                                                           MOE_KERNEL_ROUTE_BWD_DX, s);
 }
 
 }  // namespace moe

@@ -457,11 +457,15 @@ def test_backward_matches_oracle(w):
 
 @pytest.mark.parametrize("w", [TINY.scaled(name="tiny_fp32_train", train=True),
                                TRAIN.scaled(name="ragged_bf16_train_t1000_h192_i128_e24_k3", T=1000,
-                                            H=192, I=128, E=24, k=3, e_lo=5, e_hi=21)],
+                                            H=192, I=128, E=24, k=3, e_lo=5, e_hi=21),
+                               TRAIN.scaled(name="bf16_train_t700_h256_i128_e64_k4", T=700, H=256,
+                                            I=128, E=64, k=4, e_lo=8, e_hi=24)],
                          ids=lambda w: w.name)
 def test_combine_dx_equals_unfused(w):
     """moe_combine_dx == moe_combine(dx_perm, addend = dx_router of moe_route_bwd), up to
-    the one rounding of the output (the fp32 sums run in a different order)."""
+    the one rounding of the output (the fp32 sums run in a different order; with
+    E = 64 in bf16, dx_router is the MFMA product), and the layer's dx is the fused
+    form bit for bit."""
     inp = _inputs(w)
     t = _gpu_tensors(w, inp)
     layer, _, g = run_layer(w, t)
@@ -559,6 +563,42 @@ def test_combine_dx_matches_oracle(case):
         assert (np.abs(_np(rb["dx_router"]) - O.router_input_grad(dz, wr64)) <= dxr_bound).all()
         dwr_bound = 2.0 ** -12 * (np.abs(x64).T @ np.abs(dz)) + 1e-30
         assert (np.abs(_np(rb["dw_router"]) - x64.T @ dz) <= dwr_bound).all()
+
+
+# (T, H, E, k) of the router's input-gradient product (bf16, E % 64 == 0): one
+# token; ragged T; T = 9000 = 36 row tiles x 8 column tiles, more than one round
+# of the persistent grid; H = 320 and 192 leave partial column tiles; E = 192
+# puts the boundary between the high and low halves of the split logit
+# gradient in the middle of the K range.
+ROUTER_DX_CASES = [(1, 256, 64, 2), (300, 320, 64, 4), (1000, 192, 192, 6), (777, 2048, 128, 8),
+                   (9000, 2048, 128, 8)]
+
+
+@pytest.mark.parametrize("T,H,E,k", ROUTER_DX_CASES, ids=lambda v: str(v))
+def test_router_input_grad_product_matches_oracle(T, H, E, k):
+    """moe_route_bwd's dx_router where it is an MFMA product ([dz_hi | dz_lo] . [W_r |
+    W_r]^T over all E columns) against the oracle's router input gradient: within
+    2^-14 of the sum of absolute terms (dz enters as two bf16 halves, about 16
+    bits; K = 2E fp32 products), and zero work for dw_router."""
+    rng = np.random.default_rng(T * 7919 + H * 31 + E)
+    idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    tw = rng.random((T, k)) + 0.1
+    tw /= tw.sum(1, keepdims=True)
+    dtw = rng.standard_normal((T, k))
+    g_tw, g_dtw = _dev(tw, torch.float32), _dev(dtw, torch.float32)
+    g_idx = torch.from_numpy(idx).to(DEV)
+    wr = _dev(rng.standard_normal((H, E)) / np.sqrt(H), torch.bfloat16)
+    x = torch.zeros((T, H), dtype=torch.bfloat16, device=DEV)  # shapes only (no dw_router)
+    print(f"  router dx product: T={T} H={H} E={E} k={k}", flush=True)
+    rb = moe.moe_route_bwd(g_dtw, g_tw, g_idx, x, wr, want_dx=True, want_dw=False)
+    torch.cuda.synchronize()
+    dz = O.router_logit_grad(_np(g_tw), _np(g_dtw), idx, E)
+    wr64 = _np(wr)
+    ref = O.router_input_grad(dz, wr64)
+    bound = 2.0 ** -14 * O.router_input_grad(np.abs(dz), np.abs(wr64)) + 1e-30
+    err = np.abs(_np(rb["dx_router"]) - ref)
+    print(f"  max err / bound {(err / bound).max():.3g}", flush=True)
+    assert (err <= bound).all()
 
 
 def test_weight_grad_accumulate():

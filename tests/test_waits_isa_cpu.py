@@ -125,19 +125,20 @@ class Fifo:
 
 
 # gemm_kernel<KIND, BM, FP8, WIDE>: KIND 0 gate/up, 1 down, 2 down data gradient,
-# 3 gate/up data gradient, 4 weight gradient, 5 FP8 weight gradient; the bf16
-# M-grouped products (KIND 0-3) run on the wide ring.  Per-lane
+# 3 gate/up data gradient, 4 weight gradient, 5 FP8 weight gradient, 6 router
+# input gradient; the bf16 M-grouped products (KIND 0-3) and the router
+# product run on the wide ring.  Per-lane
 # vector memory instructions of one epilogue, as the kernel counts them (stores
 # per 16-row half pass, times 2 MI passes), and the FP8 scale loads of the next
 # tile.  The FP8 weight gradient does not count its epilogue (None): its first
 # wait after a tile change is the plain one.
 def _design(kind, bm, fp8):
     mi = bm // 64
-    wide = kind <= 3 and bm == 256 and not fp8
+    wide = kind in (0, 1, 2, 3, 6) and bm == 256 and not fp8
     nst = 4 if bm == 256 else 3
     bkx = 64 if wide else 32
     nia, nib = bm * bkx * 2 // 4096, 256 * bkx * 2 // 4096
-    epi = {0: 12 * mi, 1: 8 * mi, 2: 32 * mi, 3: 8 * mi, 4: 16 * mi, 5: None}[kind]
+    epi = {0: 12 * mi, 1: 8 * mi, 2: 32 * mi, 3: 8 * mi, 4: 16 * mi, 5: None, 6: 16 * mi}[kind]
     scales = 0
     if fp8:
         nr = 4 * mi if kind == 0 else 8 * mi
@@ -148,7 +149,7 @@ def _design(kind, bm, fp8):
 
 
 GEMM_KERNELS = [(0, 256, False), (1, 256, False), (2, 256, False), (3, 256, False), (4, 256, False),
-                (4, 128, False), (0, 256, True), (1, 256, True)]
+                (4, 128, False), (0, 256, True), (1, 256, True), (6, 256, False)]
 GEMM_KERNELS_ALL = GEMM_KERNELS + [(5, 256, True)]
 
 
