@@ -128,11 +128,15 @@ struct Cfg {
 // over the finer tiling of 128; the down-projection weight gradient, whose
 // K = expert rows is short, runs faster with 128).
 constexpr int kBmGrouped = 256;
-// The bf16 M-grouped products run on the wide ring (K blocks of 64; their K,
-// H or I or 2I, is a multiple of 64); the weight gradients, whose operands are
-// MN-contiguous rows of 512 bytes already, and the FP8 products keep the
-// narrow one.
+// The bf16 products with 256-row tiles run on the wide ring: the M-grouped
+// ones (their K, H or I or 2I, is a multiple of 64, so no K block straddles a
+// row's end) and the weight gradients with 256-row tiles (their K tail is a
+// row range, dropped by the descriptors like any ragged group; their
+// MN-contiguous 512-byte rows read whole lines either way, and the wide ring
+// measured even with the narrow one there).  dW_down (128-row tiles) and the
+// FP8 products keep the narrow ring.
 constexpr bool kWideGrouped = true;
+constexpr bool kWideWgrad = true;
 constexpr int kBmWgrad = 256;
 constexpr int kBmWgradDown = 128;
 
@@ -1329,7 +1333,7 @@ void gemm_kernel(const GemmArgs p) {
                 "FP8: K-contiguous products only");
   static_assert(KIND != K_WGRAD8 || F8, "WGRAD8 runs on E4M3 codes");
   static_assert(!(F8 && WIDE), "the FP8 K loop runs on the narrow ring");
-  static_assert(!(WIDE && k_grouped(KIND)), "wide ring: M-grouped products (K a multiple of 64)");
+  static_assert(!(WIDE && KIND == K_WGRAD8), "the FP8 products run on the narrow ring");
   static_assert(KIND != K_ROUTER_DX || (WIDE && !F8), "the router product runs on the wide ring");
   using Tr = Traits<KIND>;
   using C = Cfg<BM_, WIDE>;
@@ -2049,7 +2053,8 @@ hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, cons
   w.accumulate = accumulate ? 1 : 0;
   w.tile_ctr = ctrs + 3;
   if (side != nullptr && (err = hipStreamWaitEvent(s2, side->mid, 0)) != hipSuccess) return err;
-  err = launch_gemm<K_WGRAD, kBmWgrad>(w, E_l * w.n_mtiles * w.n_ntiles, MOE_KERNEL_FFN_GATEUP_WGRAD, s2);
+  err = launch_gemm<K_WGRAD, kBmWgrad, false, kWideWgrad>(w, E_l * w.n_mtiles * w.n_ntiles,
+                                                         MOE_KERNEL_FFN_GATEUP_WGRAD, s2);
   if (err != hipSuccess) return err;
   if (side != nullptr && wgrad_stream == nullptr) {
     if ((err = hipEventRecord(side->join, s2)) != hipSuccess) return err;
@@ -2081,7 +2086,8 @@ hipError_t launch_dw_router_bf16(const bf16_t* x, const bf16_t* dz_hilo, int T, 
   w.ldc = F > 0 ? E : 2 * E;
   w.f_group_stride = (long)H * w.ldc;
   w.accumulate = 0;
-  return launch_gemm<K_WGRAD, kBmWgrad>(w, nsplit * w.n_mtiles * w.n_ntiles, MOE_KERNEL_ROUTE_BWD_DW, s);
+  return launch_gemm<K_WGRAD, kBmWgrad, false, kWideWgrad>(w, nsplit * w.n_mtiles * w.n_ntiles,
+                                                           MOE_KERNEL_ROUTE_BWD_DW, s);
 }
 
 bool router_dx_mfma_ok(int H, int E) { return H % 64 == 0 && E > 0 && E % 64 == 0; }

@@ -134,7 +134,7 @@ class Fifo:
 # wait after a tile change is the plain one.
 def _design(kind, bm, fp8):
     mi = bm // 64
-    wide = kind in (0, 1, 2, 3, 6) and bm == 256 and not fp8
+    wide = kind in (0, 1, 2, 3, 4, 6) and bm == 256 and not fp8
     nst = 4 if bm == 256 else 3
     bkx = 64 if wide else 32
     nia, nib = bm * bkx * 2 // 4096, 256 * bkx * 2 // 4096
@@ -284,8 +284,11 @@ def _check_wide_ring(ev, d):
     k_after = min(VMCNT_MAX, k_first + k_epi)
     assert k_after in waits, (waits, k_after)
     # inside the loop exactly one wait, between the two DMA groups
-    # (the innermost loop header: the tile loop's comes first)
-    hdr = max(i for i, e in enumerate(ev) if e == "L")
+    # (the K loop's header: the one directly followed by a DMA; the tile loop's
+    # comes first, epilogue loops come later)
+    hdrs = [i for i, e in enumerate(ev[:-1]) if e == "L" and ev[i + 1] == "D"]
+    assert len(hdrs) == 1, hdrs
+    hdr = hdrs[0]
     end = next(i for i in range(hdr, len(ev)) if ev[i] == 0)
     body = ev[hdr + 1:end]
     assert body == ["D"] * nia + [k_loop] + ["D"] * nib, body
