@@ -59,9 +59,10 @@
 // codes.  Per K step each (mi, ni) block takes one v_mfma_scale_f32_32x32x64
 // _f8f6f4 (unit block scales) whose 32 operand bytes per lane are the two
 // 16-byte fragments the bf16 path reads for its two k16 sub-steps (a
-// permutation of K applied to both operands, so the sum is the same).  The
-// epilogue multiplies each accumulator by its row scale times its column
-// scale (both powers of two: exact) before the SwiGLU.
+// permutation of K applied to both operands, so the sum is the same); on the
+// wide ring a 128-code block is two such steps.  The epilogue multiplies each
+// accumulator by its row scale times its column scale (both powers of two:
+// exact) before the SwiGLU.
 #include "common.h"
 #include "lds_layout.h"
 
@@ -137,6 +138,10 @@ constexpr int kBmGrouped = 256;
 // FP8 products keep the narrow ring.
 constexpr bool kWideGrouped = true;
 constexpr bool kWideWgrad = true;
+// The FP8 M-grouped products (the forward and both data gradients; their K in
+// 16-bit slots, H / 2, I / 2 or I, is a multiple of 64 since the FP8 entry
+// points need H and I multiples of 128) run on it too.
+constexpr bool kWideF8 = true;
 constexpr int kBmWgrad = 256;
 constexpr int kBmWgradDown = 128;
 
@@ -383,7 +388,8 @@ __device__ __forceinline__ void mma(f32x16_t (&acc)[C::MI][NI], const Frags<C>& 
 
 // FP8: a (mi, ni) block's operands for one 64-code K step: bytes 0..15 of the
 // lane's 32 are the fragment of bf16 sub-step 0, bytes 16..31 that of
-// sub-step 1.
+// sub-step 1 (on the wide ring the block's second step takes sub-steps 2
+// and 3).
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 template <class C>
@@ -400,12 +406,12 @@ __device__ __forceinline__ void mfma_f8(f32x16_t& acc, const i32x8_t& a, const i
 template <class C>
 __device__ __forceinline__ void read_a8(Frags8<C>& f, int mi, int s, uint32_t sa, const FragLanes<C>& L) {
   const i32x4_t v = __builtin_bit_cast(i32x4_t, frag_kc(sa, L.kc[s], mi * 32 * C::BKX * 2));
-  if (s == 0) f.a[mi].lo = v; else f.a[mi].hi = v;
+  if ((s & 1) == 0) f.a[mi].lo = v; else f.a[mi].hi = v;
 }
 template <class C>
 __device__ __forceinline__ void read_b8(Frags8<C>& f, int ni, int s, uint32_t sb, const FragLanes<C>& L) {
   const i32x4_t v = __builtin_bit_cast(i32x4_t, frag_kc(sb, L.kc[s], ni * 32 * C::BKX * 2));
-  if (s == 0) f.b[ni].lo = v; else f.b[ni].hi = v;
+  if ((s & 1) == 0) f.b[ni].lo = v; else f.b[ni].hi = v;
 }
 
 // A stall in a wave's instruction stream idles its matrix core unless another
@@ -1092,6 +1098,87 @@ __device__ __forceinline__ void k_steps_f8(f32x16_t (&acc)[C::MI][NI], Frags8<C>
   }
 }
 
+// FP8 K blocks on the wide ring: a block holds 128 codes per row, two E4M3
+// MFMA steps (step 0 on the fragments of bf16 sub-steps 0 and 1, step 1 on
+// sub-steps 2 and 3).  One fragment set, as in k_steps_f8: on entry f holds
+// step 0's A blocks mi < MI / 2 and all its B blocks.  Per block j:
+//   1a: MFMAs of step 0, blocks mi < MI / 2; step 0's A blocks mi >= MI / 2
+//       are read;
+//   2a: MFMAs of step 0, mi >= MI / 2 (ni-major); B block ni of step 1 is
+//       read after its last use in step 0, step 1's A blocks mi < MI / 2 in
+//       between, and half of block j + 2's A DMA is issued;
+//   1b: MFMAs of step 1, mi < MI / 2; step 1's A blocks mi >= MI / 2 read and
+//       the other half of block j + 2's A DMA issued;
+//   wait until block j + 1 has landed (only block j + 2's A in flight),
+//       barrier: every wave has also finished reading block j;
+//   2b: MFMAs of step 1, mi >= MI / 2; block j + 1's step-0 B blocks read
+//       after their last use and its A blocks mi < MI / 2 in between; block
+//       j + 2's B DMA issued into block j's A region.
+// Regions as in k_blocks: block j in (2j) % 5 (A) and (2j + 1) % 5 (B).
+template <int KIND, class C>
+__device__ __forceinline__ void k_blocks_f8(f32x16_t (&acc)[C::MI][NI], Frags8<C>& f,
+                                            const FragLanes<C>& L, const GemmArgs& p,
+                                            const Operand<C::NIA>& opA, const Operand<C::NIB>& opB,
+                                            uint32_t dma_w, uint32_t wa, uint32_t wb, int nk) {
+  constexpr int R = C::kRegion, NIA = C::NIA, NIB = C::NIB, MI = C::MI;
+  constexpr int MH = MI / 2, NP = MH * NI;  // MFMAs per phase
+  static_assert(C::WIDE && C::KSUB == 4 && MI % 2 == 0 && 2 * MH <= NP, "wide FP8 ring");
+  static_assert(NIA % 2 == 0 && NP % (NIA / 2) == 0 && NP % NIB == 0, "DMA spread");
+  constexpr int SA = NP / (NIA / 2);  // one A piece every SA MFMAs of phases 2a and 1b
+  constexpr int SB = NP / NIB;        // one B piece every SB MFMAs of phase 2b
+  int ra = 0;                         // (2j) % 5
+  for (int j = 0; j < nk; ++j) {
+    const int rb = ra == 4 ? 0 : ra + 1;    // (2j + 1) % 5
+    const int rn = rb == 4 ? 0 : rb + 1;    // (2j + 2) % 5: block j + 1's A
+    const int rnb = rn == 4 ? 0 : rn + 1;   // (2j + 3) % 5: block j + 1's B
+    const int rq = rnb == 4 ? 0 : rnb + 1;  // (2j + 4) % 5: block j + 2's A
+    const uint32_t sa = ra * R + wa, sb = rb * R + wb;
+    const uint32_t kill = j + 2 < nk ? 0u : kDmaKill;
+    const int k2 = (j + 2) * C::BKX;
+#pragma unroll
+    for (int m = 0; m < NP; ++m) {  // 1a
+      mfma_f8(acc[m / NI][m % NI], f.a[m / NI], f.b[m % NI]);
+      if (m < 2 * MH) read_a8<C>(f, MH + m / 2, m % 2, sa, L);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int m = 0; m < NP; ++m) {  // 2a
+      const int ni = m / MH, mi = MH + m % MH;
+      mfma_f8(acc[mi][ni], f.a[mi], f.b[ni]);
+      if (m % MH == MH - 1) {
+        read_b8<C>(f, ni, 2, sb, L);
+        read_b8<C>(f, ni, 3, sb, L);
+      }
+      if (m < 2 * MH) read_a8<C>(f, m / 2, 2 + m % 2, sa, L);
+      if (m % SA == 0) dma_piece<KIND, C>(p, opA, opB, dma_w + rq * R, 0u, k2, kill, m / SA);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int m = 0; m < NP; ++m) {  // 1b
+      mfma_f8(acc[m / NI][m % NI], f.a[m / NI], f.b[m % NI]);
+      if (m < 2 * MH) read_a8<C>(f, MH + m / 2, 2 + m % 2, sa, L);
+      if (m % SA == 0) dma_piece<KIND, C>(p, opA, opB, dma_w + rq * R, 0u, k2, kill, NIA / 2 + m / SA);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vm<NIA>();
+    lds_barrier();  // every wave: block j + 1 landed, block j fully read
+    const uint32_t na = rn * R + wa, nb = rnb * R + wb;
+#pragma unroll
+    for (int m = 0; m < NP; ++m) {  // 2b
+      const int ni = m / MH, mi = MH + m % MH;
+      mfma_f8(acc[mi][ni], f.a[mi], f.b[ni]);
+      if (m % MH == MH - 1) {
+        read_b8<C>(f, ni, 0, nb, L);
+        read_b8<C>(f, ni, 1, nb, L);
+      }
+      if (m < 2 * MH) read_a8<C>(f, m / 2, m % 2, na, L);
+      if (m % SB == 0) dma_piece<KIND, C>(p, opA, opB, 0u, dma_w + ra * R, k2, kill, NIA + m / SB);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    ra = rn;
+  }
+}
+
 // Vector memory instructions each lane issues in the epilogue of a product
 // (the buffer stores and loads there are unconditional: the range checks drop
 // the ones outside the tile; WGRAD: its overwriting epilogue, the accumulating
@@ -1332,8 +1419,8 @@ void gemm_kernel(const GemmArgs p) {
   static_assert(!F8 || KIND == K_GATEUP_FWD || KIND == K_DOWN_FWD || KIND == K_WGRAD8,
                 "FP8: K-contiguous products only");
   static_assert(KIND != K_WGRAD8 || F8, "WGRAD8 runs on E4M3 codes");
-  static_assert(!(F8 && WIDE), "the FP8 K loop runs on the narrow ring");
-  static_assert(!(WIDE && KIND == K_WGRAD8), "the FP8 products run on the narrow ring");
+  // (the FP8 weight gradient's groups are padded to 64 codes, half a wide block)
+  static_assert(!(WIDE && KIND == K_WGRAD8), "the FP8 weight gradient runs on the narrow ring");
   static_assert(KIND != K_ROUTER_DX || (WIDE && !F8), "the router product runs on the wide ring");
   using Tr = Traits<KIND>;
   using C = Cfg<BM_, WIDE>;
@@ -1403,12 +1490,10 @@ void gemm_kernel(const GemmArgs p) {
       // Two fragment sets, no copies between them: f0 holds sub-step 0 (read
       // at the end of the previous step), f1 sub-step 1 (wide ring: f0 and f1
       // alternate over the four sub-steps).
-      if constexpr (C::WIDE) {
-        Frags<C> f0, f1;
-        load_frags<KIND, C>(f0, 0, wa, C::kRegion + wb, L);
-        k_blocks<KIND, C>(acc, f0, f1, L, p, opA, opB, dma_a, wa, wb, t.nk);
-      } else if constexpr (F8) {
-        static_assert(C::KSUB == 2, "the FP8 pipeline reads two 16-byte halves per K step");
+      if constexpr (F8) {
+        // step 0's A blocks mi < MI / 2 and B blocks (B: narrow ring slot 0,
+        // wide ring region 1)
+        const uint32_t b0 = C::WIDE ? C::kRegion + wb : kOffB + wb;
         Frags8<C> f;
 #pragma unroll
         for (int mi = 0; mi < MI / 2; ++mi) {
@@ -1417,10 +1502,19 @@ void gemm_kernel(const GemmArgs p) {
         }
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
-          read_b8<C>(f, ni, 0, kOffB + wb, L);
-          read_b8<C>(f, ni, 1, kOffB + wb, L);
+          read_b8<C>(f, ni, 0, b0, L);
+          read_b8<C>(f, ni, 1, b0, L);
         }
-        k_steps_f8<KIND, C>(acc, f, L, p, opA, opB, dma_a, dma_b, wa, wb, t.nk);
+        if constexpr (C::WIDE) {
+          k_blocks_f8<KIND, C>(acc, f, L, p, opA, opB, dma_a, wa, wb, t.nk);
+        } else {
+          static_assert(C::KSUB == 2, "the narrow FP8 pipeline reads two 16-byte halves per K step");
+          k_steps_f8<KIND, C>(acc, f, L, p, opA, opB, dma_a, dma_b, wa, wb, t.nk);
+        }
+      } else if constexpr (C::WIDE) {
+        Frags<C> f0, f1;
+        load_frags<KIND, C>(f0, 0, wa, C::kRegion + wb, L);
+        k_blocks<KIND, C>(acc, f0, f1, L, p, opA, opB, dma_a, wa, wb, t.nk);
       } else {
         static_assert(C::KSUB == 2, "the fragment pipeline below assumes two k16 sub-steps");
         Frags<C> f0, f1;
@@ -1701,7 +1795,7 @@ hipError_t launch_ffn_fwd_fp8(const uint8_t* x_q, const float* x_scale, const in
   g.sb0 = wg_s;
   g.sb1 = wu_s;
   g.sb_group_stride = I;
-  err = launch_gemm<K_GATEUP_FWD, kBmGrouped, true>(g, mt_upper * g.n_ntiles, MOE_KERNEL_FFN_GATEUP, s);
+  err = launch_gemm<K_GATEUP_FWD, kBmGrouped, true, kWideF8>(g, mt_upper * g.n_ntiles, MOE_KERNEL_FFN_GATEUP, s);
   if (err != hipSuccess) return err;
 
   err = launch_quantize_fp8(h_perm, R_cap, I, true, offsets + E_l, hq, sh, s);
@@ -1723,7 +1817,7 @@ hipError_t launch_ffn_fwd_fp8(const uint8_t* x_q, const float* x_scale, const in
   d.sa = sh;
   d.sb0 = wd_s;
   d.sb_group_stride = H;
-  return launch_gemm<K_DOWN_FWD, kBmGrouped, true>(d, mt_upper * d.n_ntiles, MOE_KERNEL_FFN_DOWN, s);
+  return launch_gemm<K_DOWN_FWD, kBmGrouped, true, kWideF8>(d, mt_upper * d.n_ntiles, MOE_KERNEL_FFN_DOWN, s);
 }
 
 // FP8 data gradients of the expert FFN.  Both products are the FP8 down
@@ -1771,7 +1865,7 @@ hipError_t launch_ffn_dgrad_fp8(const uint8_t* dy_q, const float* dy_scale, cons
   d.sa = dy_scale;
   d.sb0 = wdt_s;
   d.sb_group_stride = I;
-  err = launch_gemm<K_DOWN_FWD, kBmGrouped, true>(d, mt_upper * d.n_ntiles, MOE_KERNEL_FFN_DOWN_DGRAD, s);
+  err = launch_gemm<K_DOWN_FWD, kBmGrouped, true, kWideF8>(d, mt_upper * d.n_ntiles, MOE_KERNEL_FFN_DOWN_DGRAD, s);
   if (err != hipSuccess) return err;
 
   err = launch_swiglu_bwd_fp8(dh, gu, R_cap, I, offsets + E_l, dgu, dguq, sdgu, s);
@@ -1793,7 +1887,7 @@ hipError_t launch_ffn_dgrad_fp8(const uint8_t* dy_q, const float* dy_scale, cons
   x.sa = sdgu;
   x.sb0 = wgut_s;
   x.sb_group_stride = H;
-  return launch_gemm<K_DOWN_FWD, kBmGrouped, true>(x, mt_upper * x.n_ntiles, MOE_KERNEL_FFN_GATEUP_DGRAD, s);
+  return launch_gemm<K_DOWN_FWD, kBmGrouped, true, kWideF8>(x, mt_upper * x.n_ntiles, MOE_KERNEL_FFN_GATEUP_DGRAD, s);
 }
 
 // FP8 weight gradients of the expert FFN: the four operands' columns are

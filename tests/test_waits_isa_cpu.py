@@ -134,7 +134,9 @@ class Fifo:
 # wait after a tile change is the plain one.
 def _design(kind, bm, fp8):
     mi = bm // 64
-    wide = kind in (0, 1, 2, 3, 4, 6) and bm == 256 and not fp8
+    # (FP8: the forward and data-gradient products, kinds 0 and 1; the FP8
+    # weight gradient, kind 5, stays on the narrow ring)
+    wide = bm == 256 and (kind in (0, 1, 2, 3, 4, 6) if not fp8 else kind in (0, 1))
     nst = 4 if bm == 256 else 3
     bkx = 64 if wide else 32
     nia, nib = bm * bkx * 2 // 4096, 256 * bkx * 2 // 4096
