@@ -124,18 +124,20 @@ struct Cfg {
                           kStageOff == 4 * kRegion),
                 "wide ring: five equal regions, the fifth is the staging area");
 };
-// Tile heights in use (chosen per product by measurement on the 128-expert
-// layer: 256 wherever the larger tile's lower L2 and LDS traffic per MFMA wins
-// over the finer tiling of 128; the down-projection weight gradient, whose
-// K = expert rows is short, runs faster with 128).
+// Tile heights in use: 256 for every product (chosen by measurement: the
+// larger tile's lower L2 and LDS traffic per MFMA wins over the finer tiling
+// of 128; the down-projection weight gradient, whose K = expert rows is
+// short, ran faster with 128 on the narrow ring and about even, slightly
+// ahead, with 256 on the wide one).  The 128-row configuration stays
+// available.
 constexpr int kBmGrouped = 256;
 // The bf16 products with 256-row tiles run on the wide ring: the M-grouped
 // ones (their K, H or I or 2I, is a multiple of 64, so no K block straddles a
 // row's end) and the weight gradients with 256-row tiles (their K tail is a
 // row range, dropped by the descriptors like any ragged group; their
 // MN-contiguous 512-byte rows read whole lines either way, and the wide ring
-// measured even with the narrow one there).  dW_down (128-row tiles) and the
-// FP8 products keep the narrow ring.
+// measured even with the narrow one there).  The FP8 weight gradient keeps
+// the narrow ring.
 constexpr bool kWideGrouped = true;
 constexpr bool kWideWgrad = true;
 // The FP8 M-grouped products (the forward and both data gradients; their K in
@@ -143,7 +145,7 @@ constexpr bool kWideWgrad = true;
 // points need H and I multiples of 128) run on it too.
 constexpr bool kWideF8 = true;
 constexpr int kBmWgrad = 256;
-constexpr int kBmWgradDown = 128;
+constexpr int kBmWgradDown = 256;
 
 enum GemmKind {
   K_GATEUP_FWD = 0, K_DOWN_FWD = 1, K_DOWN_DGRAD = 2, K_GATEUP_DGRAD = 3, K_WGRAD = 4,
@@ -2105,7 +2107,8 @@ hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, cons
   b.f_group_stride = (long)H * I;
   b.accumulate = accumulate ? 1 : 0;
   b.tile_ctr = ctrs + 1;
-  err = launch_gemm<K_WGRAD, kBmWgradDown>(b, E_l * b.n_mtiles * b.n_ntiles, MOE_KERNEL_FFN_DOWN_WGRAD, s2);
+  err = launch_gemm<K_WGRAD, kBmWgradDown, false, kWideWgrad>(b, E_l * b.n_mtiles * b.n_ntiles,
+                                                             MOE_KERNEL_FFN_DOWN_WGRAD, s2);
   if (err != hipSuccess) return err;
 
   // dX_e = dG W_gate[e] + dU W_up[e]
