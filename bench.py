@@ -37,7 +37,7 @@ SECONDARY_WORKLOAD = "full_t16384_h2048_i768_e128_k8"
 KERNELS = ["ROUTE", "PERMUTE_HIST", "PERMUTE_SCAN", "PERMUTE_SCATTER", "FFN_GATEUP", "FFN_DOWN",
            "COMBINE", "COMBINE_BWD", "ROUTE_BWD_DZ", "ROUTE_BWD_DW", "FFN_DOWN_DGRAD",
            "FFN_DOWN_WGRAD", "FFN_GATEUP_DGRAD", "FFN_GATEUP_WGRAD", "COMBINE_DX", "ROUTE_BWD_DX",
-           "COMBINE_ADD"]
+           "COMBINE_ADD", "FFN_WGRAD_REDUCE"]
 
 
 def step_flops(w, R):
@@ -69,6 +69,8 @@ def kernel_work(name, w, R, launches, A=None):
         "ROUTE_BWD_DX": (2.0 * T * k * H, T * 2 * E * 2 + H * E * b + T * H * 4),
         # unweighted unpermute-reduce plus an fp32 addend row per token
         "COMBINE_ADD": (0, R * H * b + T * k * 4 + T * H * 4 + T * H * b),
+        # split experts' partial slots (none on balanced loads): priced at zero
+        "FFN_WGRAD_REDUCE": (0, 0),
         "ROUTE_BWD_DW": (2.0 * T * H * E, T * H * b + T * 2 * E * 2 + H * E * 4),
         "FFN_DOWN_DGRAD": (2.0 * R * H * I, R * H * b + El * H * I * b + 2 * R * 2 * I * b),
         "FFN_DOWN_WGRAD": (2.0 * R * H * I, R * H * b + R * I * b + El * H * I * 4),

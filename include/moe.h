@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 7
+#define MOE_ABI_VERSION 8
 
 typedef enum {
   MOE_OK = 0,
@@ -416,7 +416,8 @@ typedef enum {
   MOE_KERNEL_COMBINE_DX = 14,     /* fused input gradient (moe_combine_dx) */
   MOE_KERNEL_ROUTE_BWD_DX = 15,   /* router input gradient as an MFMA product (moe_route_bwd) */
   MOE_KERNEL_COMBINE_ADD = 16,    /* moe_combine with an addend (an input gradient's unpermute-reduce) */
-  MOE_KERNEL_COUNT = 17
+  MOE_KERNEL_FFN_WGRAD_REDUCE = 17, /* split experts' weight-gradient partials added (moe_grouped_ffn_bwd) */
+  MOE_KERNEL_COUNT = 18
 } moe_kernel;
 
 int moe_profile_kernel(int kernel_id, void** start_events, void** stop_events, int n);

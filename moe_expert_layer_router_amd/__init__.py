@@ -31,7 +31,7 @@ MOE_F32, MOE_BF16, MOE_FP8 = 0, 1, 2
 (MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD, MOE_OP_ROUTE_BWD,
  MOE_OP_COMBINE_DX, MOE_OP_FFN_FWD_FP8, MOE_OP_FFN_DGRAD_FP8, MOE_OP_FFN_WGRAD_FP8,
  MOE_OP_QUANTIZE_W_FP8) = range(10)
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 
 class MoEError(RuntimeError):

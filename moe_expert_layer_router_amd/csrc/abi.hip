@@ -93,8 +93,9 @@ size_t ws_route(int T, int H, int E, int dtype) {
 size_t ws_ffn_fwd(int R_cap, int E_l, int dtype) {
   return dtype == MOE_BF16 ? ffn_sched_bytes(R_cap, E_l) : 0;
 }
-size_t ws_ffn_bwd(int R_cap, int E_l, int I, int dtype) {
-  if (dtype == MOE_BF16) return ffn_sched_bytes(R_cap, E_l) + align256((size_t)R_cap * 2 * I * 2);
+size_t ws_ffn_bwd(int R_cap, int E_l, int H, int I, int dtype) {
+  if (dtype == MOE_BF16)
+    return ffn_sched_bytes(R_cap, E_l) + align256((size_t)R_cap * 2 * I * 2) + ffn_wgrad_split_bytes(E_l, H, I);
   return align256((size_t)R_cap * 2 * I * 4);
 }
 size_t ws_route_bwd(int T, int H, int E, int dtype) {
@@ -229,7 +230,7 @@ int64_t moe_workspace_bytes(int op, int T, int H, int I, int E, int k, int e_lo,
       if (op == MOE_OP_PERMUTE) return (int64_t)permute_ws_bytes(T, k, E_l);
       if (I <= 0) return fail(MOE_EINVAL, "%s: I must be positive", fn);
       if (op == MOE_OP_FFN_FWD) return (int64_t)ws_ffn_fwd(R_cap, E_l, dtype);
-      return (int64_t)ws_ffn_bwd(R_cap, E_l, I, dtype);
+      return (int64_t)ws_ffn_bwd(R_cap, E_l, H, I, dtype);
     }
     default:
       return fail(MOE_EINVAL, "%s: unknown op %d", fn, op);
@@ -674,7 +675,7 @@ int ffn_bwd(const char* fn, const void* dy_perm, const void* x_perm, const void*
     if (int rc = check_ptr(h_perm, "h_perm", fn, true)) return rc;
     if (int rc = check_ptr(dx_perm, "dx_perm", fn, true)) return rc;
   }
-  if (int rc = check_ws(ws, ws_bytes, ws_ffn_bwd(R_cap, E_l, I, dtype), fn)) return rc;
+  if (int rc = check_ws(ws, ws_bytes, ws_ffn_bwd(R_cap, E_l, H, I, dtype), fn)) return rc;
   hipStream_t s = begin_launch(stream);
   hipError_t e;
   if (dtype == MOE_BF16)

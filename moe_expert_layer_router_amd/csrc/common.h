@@ -190,6 +190,8 @@ int gemm_tiles(int M, int N);  // output tiles of one M x N product
 // halves before storing ([nsplit, H, E] partials instead of [nsplit, H, 2E]).
 bool dw_router_folds(int E);
 size_t ffn_sched_bytes(int R_cap, int E_l);
+// The weight gradients' split plans and partial slots (FFN backward workspace).
+size_t ffn_wgrad_split_bytes(int E_l, int H, int I);
 hipError_t launch_ffn_fwd_bf16(const bf16_t* x_perm, const int32_t* offsets, int E_l, int R_cap,
                                int H, int I, const bf16_t* w_gate, const bf16_t* w_up,
                                const bf16_t* w_down, bf16_t* gu, bf16_t* h_perm, bf16_t* y_perm,

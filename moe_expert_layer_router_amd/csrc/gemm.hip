@@ -191,7 +191,39 @@ struct GemmArgs {
   // the first (tile grid + ticket), so that kernels running side by side
   // share CUs as they free up.
   int* tile_ctr;
+  // K-grouped FFN weight gradients: the K-chunk plan (null: one chunk per
+  // group, the offsets' row ranges) and the fp32 partial slots [slots][M][N]
+  // of the chunks after a split group's first
+  const int32_t* kplan;
+  float* fpart;
 };
+
+// Load balance of the K-grouped weight gradients.  Their reduction runs over an
+// expert's rows, so one hot expert makes n_mtiles x n_ntiles tiles whose K
+// loops are as long as its row count, while the rest of the chip idles.  An
+// expert whose rows exceed W = max(kSplitMinRows, ceil(R tiles / CUs)) (R the
+// routed rows, tiles its tiles per expert: beyond W one of its tiles alone is
+// more than a CU's average share) is cut into S = min(kSplitMaxChunks,
+// ceil(rows / W)) chunks of a multiple of 64 rows.  Chunk 0 writes the
+// expert's weight gradient as an unsplit expert would (overwriting or adding);
+// chunks 1 .. S - 1 write fp32 partial slots, which wgrad_split_reduce_kernel
+// then adds in chunk order (a fixed order: the result does not depend on
+// timing).  Since S - 1 < rows / W for a split expert, the slots of one
+// product never exceed R / W <= kCUs / tiles.
+constexpr int kSplitMaxChunks = 8;
+constexpr int kSplitMinRows = 1024;
+// Plan of one product (int32): [0] chunks, [1] split experts, then per chunk
+// (expert, first row, end row, partial slot or -1), in the order the tiles are
+// handed out (largest experts first), then per split expert (expert, chunks,
+// first slot) from word 2 + 4 (E_l + slots).
+struct WgradPlan {
+  int32_t* t[2];  // gate/up product, down product (null: no plans)
+  int tiles[2];   // tiles per expert
+  int slots[2];   // partial slots available
+};
+__host__ __device__ constexpr int wgrad_plan_ints(int E_l, int slots) {
+  return 2 + 4 * (E_l + slots) + 3 * (E_l < slots ? E_l : slots);
+}
 
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
@@ -645,7 +677,7 @@ template <int KIND, class C, bool F8 = false>
 __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc)[C::MI][NI], int e,
                                          int nt, int n0, int m0, int row0, int row1, int wave,
                                          int lane,
-                                         const Scales<KIND, C>& S) {
+                                         const Scales<KIND, C>& S, int slot = -1) {
   constexpr int MI = C::MI, WM = C::WM;
   const int wm = wave >> 1, wn = wave & 1;
   float* st = stage_area<C>(wave);
@@ -680,7 +712,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
         }
       return;
     }
-    if (p.accumulate == 0) {  // uniform
+    if (p.accumulate == 0 || slot >= 0) {  // uniform
       // Overwrite: unconditional buffer stores whose descriptor covers the
       // output rows of this 16-row pass (rows past M dropped by the range
       // check, columns past N by the kill offset), so their number is static
@@ -697,10 +729,13 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
           // first output row of the pass; a pass never straddles m_split
           // (a multiple of 64 rows)
           const int mb = m0 + wm * WM + mi * 32 + 16 * h;
-          const bool first = mb < p.m_split || p.f1 == nullptr;
-          float* base = (first ? p.f0 : p.f1) + e * p.f_group_stride;
-          const int mrel = first ? mb : mb - p.m_split;
-          const int nrows = (first ? min(p.m_split, p.M) : p.M - p.m_split) - mrel;
+          // a split chunk's partial slot is one [M][N] block (no gate/up split)
+          const bool part = slot >= 0;
+          const bool first = part || mb < p.m_split || p.f1 == nullptr;
+          float* base = part ? p.fpart + (long)slot * p.M * p.ldc
+                             : (first ? p.f0 : p.f1) + e * p.f_group_stride;
+          const int mrel = (part || first) ? mb : mb - p.m_split;
+          const int nrows = (part ? p.M : first ? min(p.m_split, p.M) : p.M - p.m_split) - mrel;
           const out_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
               base + (long)max(mrel, 0) * p.ldc, 0, nrows > 0 ? (int)(nrows * p.ldc * 4) : 0, 0x00020000);
 #pragma unroll
@@ -1206,12 +1241,13 @@ __host__ __device__ constexpr int epilogue_vmem_ops() {
 // row m0 and rows [kbeg, kend) of the reduction; nk K steps.
 struct Tile {
   int e, nt, n0, row0, row1, m0, kbeg, kend, nk;
+  int slot;  // K-grouped with a plan: the chunk's partial slot, or -1 (the weight gradient itself)
 };
 
 template <int KIND, class C>
 __device__ __forceinline__ Tile decode_tile(const GemmArgs& p, int work) {
   constexpr int BM = C::BM;
-  int e, nt, row0 = 0, row1 = 0, m0 = 0, kbeg = 0, kend = 0;
+  int e, nt, row0 = 0, row1 = 0, m0 = 0, kbeg = 0, kend = 0, slot = -1;
   if constexpr (KIND == K_WGRAD8) {
     // K = the group's padded code columns [offsets[e], offsets[e + 1]), two
     // codes per bf16 slot; row0 carries m0 for the scale loads
@@ -1227,7 +1263,13 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p, int work) {
     const int rem = work - e * p.n_mtiles * p.n_ntiles;
     m0 = (rem / p.n_ntiles) * BM;
     nt = rem % p.n_ntiles;
-    if (p.offsets != nullptr) {
+    if (p.kplan != nullptr) {  // chunk `e` of the plan
+      const int32_t* c = p.kplan + 2 + 4 * e;
+      slot = c[3];
+      kbeg = c[1];
+      kend = c[2];
+      e = c[0];
+    } else if (p.offsets != nullptr) {
       kbeg = p.offsets[e];
       kend = p.offsets[e + 1];
     } else {
@@ -1259,6 +1301,7 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p, int work) {
   m0 = __builtin_amdgcn_readfirstlane(m0);
   kbeg = __builtin_amdgcn_readfirstlane(kbeg);
   kend = __builtin_amdgcn_readfirstlane(kend);
+  slot = __builtin_amdgcn_readfirstlane(slot);
 
   Tile t;
   t.e = e;
@@ -1270,6 +1313,7 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p, int work) {
   t.kbeg = kbeg;
   t.kend = kend;
   t.nk = (kend - kbeg + C::BKX - 1) / C::BKX;
+  t.slot = slot;
   return t;
 }
 
@@ -1436,7 +1480,9 @@ void gemm_kernel(const GemmArgs p) {
   const FragLanes<C> L = frag_lanes<C>(lane, wave);
 
   int total;
-  if constexpr (k_grouped(KIND))
+  if constexpr (KIND == K_WGRAD)
+    total = (p.kplan != nullptr ? p.kplan[0] : p.groups) * p.n_mtiles * p.n_ntiles;
+  else if constexpr (k_grouped(KIND))
     total = p.groups * p.n_mtiles * p.n_ntiles;
   else if constexpr (KIND == K_ROUTER_DX)
     total = p.n_mtiles * p.n_ntiles;
@@ -1559,7 +1605,7 @@ void gemm_kernel(const GemmArgs p) {
       }
     }
     after_epi = C::kSepStage;
-    epilogue<KIND, C, F8>(p, acc, t.e, t.nt, t.n0, t.m0, t.row0, t.row1, wave, lane, S);
+    epilogue<KIND, C, F8>(p, acc, t.e, t.nt, t.n0, t.m0, t.row0, t.row1, wave, lane, S, t.slot);
     // The staging area is reused by the next epilogue (and, for tiles staged
     // in the ring, overwritten by the next tile's first DMA).
     lds_barrier();
@@ -1580,7 +1626,8 @@ void gemm_kernel(const GemmArgs p) {
 __global__ __launch_bounds__(kMaxE) void ffn_sched_kernel(const int32_t* __restrict__ offsets,
                                                           int E_l, int rows,
                                                           int32_t* __restrict__ sched,
-                                                          int32_t* __restrict__ ctrs) {
+                                                          int32_t* __restrict__ ctrs,
+                                                          WgradPlan plan = WgradPlan{}) {
   // the dynamic tile counters of the products that follow start at zero
   if (ctrs != nullptr && threadIdx.x < kTileCtrs) ctrs[threadIdx.x] = 0;
   __shared__ int s[kMaxE + 1];      // s[g] = tiles of experts < g
@@ -1619,6 +1666,181 @@ __global__ __launch_bounds__(kMaxE) void ffn_sched_kernel(const int32_t* __restr
     sched[2 + 3 * i] = r0;
     sched[3 + 3 * i] = min(r0 + rows, s_off[lo + 1]);
   }
+  if (plan.t[0] == nullptr) return;
+  // The weight gradients' K-chunk plans.  When no expert exceeds its product's
+  // split threshold (balanced loads), each expert is one chunk in expert
+  // order, written by its own thread.  Otherwise experts go in order of rows,
+  // largest first (ties: lower id first); each thread sizes its own expert's
+  // chunks, and scans over the ranking give its first chunk and first slot.
+  const long R = (long)s_off[E_l] - s_off[0];
+  bool any = false;
+  for (int q = 0; q < 2; ++q) {
+    const long Wl = (R * plan.tiles[q] + kCUs - 1) / kCUs;
+    const int W = (int)(Wl > kSplitMinRows ? Wl : kSplitMinRows);
+    any = any || (e < E_l && o1 - o0 > W && plan.slots[q] > 0);
+  }
+  if (!__syncthreads_or(any)) {
+    for (int q = 0; q < 2; ++q) {
+      int32_t* t = plan.t[q];
+      if (e < E_l) {
+        t[2 + 4 * e] = e;
+        t[3 + 4 * e] = o0;
+        t[4 + 4 * e] = o1;
+        t[5 + 4 * e] = -1;
+      }
+      if (e == 0) {
+        t[0] = E_l;
+        t[1] = 0;
+      }
+    }
+    return;
+  }
+  int rank = 0;
+  if (e < E_l) {
+    const int re = o1 - o0;
+    for (int q = 0; q < E_l; ++q) {
+      const int rq = s_off[q + 1] - s_off[q];
+      rank += (rq > re || (rq == re && q < e)) ? 1 : 0;
+    }
+  }
+  __shared__ int s_scan[kMaxE];
+  for (int q = 0; q < 2; ++q) {
+    int32_t* t = plan.t[q];
+    const int P = plan.slots[q];
+    const long Wl = (R * plan.tiles[q] + kCUs - 1) / kCUs;
+    const int W = (int)(Wl > kSplitMinRows ? Wl : kSplitMinRows);
+    const int n = o1 - o0;
+    int S = 1, len = n;
+    if (e < E_l && n > W && P > 0) {
+      S = min(kSplitMaxChunks, (n + W - 1) / W);
+      len = (((n + S - 1) / S) + 63) & ~63;  // rows per chunk, a multiple of 64
+      S = (n + len - 1) / len;
+    }
+    if (e >= E_l) S = 0;
+    // exclusive scans in rank order of the chunk counts (low 16 bits) and the
+    // partial slots (high 16 bits; both below 2^15 here)
+    __syncthreads();
+    if (e < E_l) s_scan[rank] = S + ((S > 1 ? S - 1 : 0) << 16);
+    if (e >= E_l && e < kMaxE) s_scan[e] = 0;
+    __syncthreads();
+    int v = s_scan[e];
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int u = __shfl_up(v, d, kWave);
+      if (lane >= d) v += u;
+    }
+    if (lane == kWave - 1) s_wave[w] = v;
+    __syncthreads();
+    for (int qq = 0; qq < w; ++qq) v += s_wave[qq];
+    const int incl = v;  // inclusive, at position e of the rank order
+    __syncthreads();
+    s_scan[e] = incl;
+    __syncthreads();
+    const int total = s_scan[kMaxE - 1];
+    const int chunks = total & 0xffff, slots = total >> 16;
+    // the slot bound holds by construction (S - 1 < rows / W); should it ever
+    // fail, no expert is split
+    const bool ok = slots <= P;
+    int c0 = 0, slot0 = 0, nsplit_before = 0;
+    if (e < E_l) {
+      const int ex = rank > 0 ? s_scan[rank - 1] : 0;
+      c0 = ex & 0xffff;
+      slot0 = ex >> 16;
+    }
+    // split experts before this one in rank order: a third scan, over (S > 1)
+    __syncthreads();
+    if (e < E_l) s_scan[rank] = (ok && S > 1) ? 1 : 0;
+    if (e >= E_l) s_scan[e] = 0;
+    __syncthreads();
+    v = s_scan[e];
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int u = __shfl_up(v, d, kWave);
+      if (lane >= d) v += u;
+    }
+    if (lane == kWave - 1) s_wave[w] = v;
+    __syncthreads();
+    for (int qq = 0; qq < w; ++qq) v += s_wave[qq];
+    __syncthreads();
+    s_scan[e] = v;
+    __syncthreads();
+    const int nsplit = s_scan[kMaxE - 1];
+    if (e < E_l) nsplit_before = rank > 0 ? s_scan[rank - 1] : 0;
+    if (e < E_l) {
+      if (ok) {
+        for (int j = 0; j < S; ++j) {
+          const int kb = o0 + j * len, c = c0 + j;
+          t[2 + 4 * c] = e;
+          t[3 + 4 * c] = kb;
+          t[4 + 4 * c] = min(kb + len, o1);
+          t[5 + 4 * c] = j == 0 ? -1 : slot0 + j - 1;
+        }
+        if (S > 1) {
+          int32_t* split = t + 2 + 4 * (E_l + P) + 3 * nsplit_before;
+          split[0] = e;
+          split[1] = S;
+          split[2] = slot0;
+        }
+      } else {  // one chunk per expert, in rank order
+        t[2 + 4 * rank] = e;
+        t[3 + 4 * rank] = o0;
+        t[4 + 4 * rank] = o1;
+        t[5 + 4 * rank] = -1;
+      }
+    }
+    if (e == 0) {
+      t[0] = ok ? chunks : E_l;
+      t[1] = ok ? nsplit : 0;
+    }
+  }
+}
+
+// The split experts' partial slots added to their weight gradients in chunk
+// order: out += part[slot0] + ... (chunk 0 wrote out itself).  Both products in
+// one launch; elements in float4s, grid-strided.  Nothing to do (the usual
+// case) returns at once.
+struct WgradReduce {
+  const int32_t* plan[2];
+  const float* part[2];
+  float* out0[2];   // rows below m_split (gate; down: all rows)
+  float* out1[2];   // rows from m_split on (up), or null
+  int M[2], N[2], m_split[2];
+  long group_stride[2];
+  int E_l, slots[2];
+};
+
+__global__ __launch_bounds__(256) void wgrad_split_reduce_kernel(const WgradReduce a) {
+  const int tid = blockIdx.x * blockDim.x + threadIdx.x;
+  const int stride = gridDim.x * blockDim.x;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int32_t* pl = a.plan[q];
+    const int ns = pl[1];
+    const int32_t* split = pl + 2 + 4 * (a.E_l + a.slots[q]);
+    const int N = a.N[q], mn4 = a.M[q] * N / 4;  // M N < 2^31 (checked by the entry point)
+    for (int i = 0; i < ns; ++i) {
+      const int g = split[3 * i], S = split[3 * i + 1], slot0 = split[3 * i + 2];
+      const float* part = a.part[q] + (long)slot0 * a.M[q] * N;
+      for (int x = tid; x < mn4; x += stride) {
+        const int el = 4 * x;
+        const int m = el / N, n = el - m * N;
+        const bool up = a.out1[q] != nullptr && m >= a.m_split[q];
+        float* dst = (up ? a.out1[q] : a.out0[q]) + g * a.group_stride[q] +
+                     (long)(up ? m - a.m_split[q] : m) * N + n;
+        // every partial loaded first, then added in chunk order
+        f32x4_t pv[kSplitMaxChunks - 1];
+#pragma unroll
+        for (int j = 0; j < kSplitMaxChunks - 1; ++j)
+          pv[j] = j < S - 1 ? *reinterpret_cast<const f32x4_t*>(part + (long)j * a.M[q] * N + el)
+                            : f32x4_t{};
+        f32x4_t v = *reinterpret_cast<const f32x4_t*>(dst);
+#pragma unroll
+        for (int j = 0; j < kSplitMaxChunks - 1; ++j)
+          if (j < S - 1) v += pv[j];
+        *reinterpret_cast<f32x4_t*>(dst) = v;
+      }
+    }
+  }
 }
 
 static constexpr size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -1633,6 +1855,35 @@ static size_t ffn_sched_table_bytes(int R_cap, int E_l) {
   return align256((1 + 3 * entries) * sizeof(int32_t));
 }
 size_t ffn_sched_bytes(int R_cap, int E_l) { return ffn_sched_table_bytes(R_cap, E_l) + 256; }
+
+// The weight gradients' split plans and partial slots (after dgu in the FFN
+// backward workspace): gate/up product (M = 2I, N = H), then down (M = H, N = I).
+static int wgrad_split_slots(int E_l, int tiles) {
+  return std::min(E_l * (kSplitMaxChunks - 1), kCUs / tiles);
+}
+struct WgradSplitLayout {
+  int tiles[2], slots[2];
+  size_t plan_off[2], part_off[2], bytes;
+};
+static WgradSplitLayout wgrad_split_layout(int E_l, int H, int I) {
+  WgradSplitLayout L{};
+  L.tiles[0] = gemm_tiles(2 * I, H);
+  L.tiles[1] = gemm_tiles(H, I);
+  size_t o = 0;
+  for (int q = 0; q < 2; ++q) {
+    L.slots[q] = wgrad_split_slots(E_l, L.tiles[q]);
+    L.plan_off[q] = o;
+    o += align256((size_t)wgrad_plan_ints(E_l, L.slots[q]) * sizeof(int32_t));
+  }
+  const size_t mn[2] = {(size_t)2 * I * H, (size_t)H * I};
+  for (int q = 0; q < 2; ++q) {
+    L.part_off[q] = o;
+    o += align256((size_t)L.slots[q] * mn[q] * sizeof(float));
+  }
+  L.bytes = o;
+  return L;
+}
+size_t ffn_wgrad_split_bytes(int E_l, int H, int I) { return wgrad_split_layout(E_l, H, I).bytes; }
 static int32_t* ffn_tile_ctrs(void* ws, int R_cap, int E_l) {
   return (int32_t*)((char*)ws + ffn_sched_table_bytes(R_cap, E_l));
 }
@@ -2051,7 +2302,18 @@ hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, cons
   int32_t* sched = (int32_t*)ws;
   bf16_t* dgu = (bf16_t*)((char*)ws + ffn_sched_bytes(R_cap, E_l));
   int32_t* ctrs = ffn_tile_ctrs(ws, R_cap, E_l);
-  ffn_sched_kernel<<<1, kMaxE, 0, s>>>(offsets, E_l, kBmGrouped, sched, ctrs);
+  // the weight gradients' K-chunk plans and partial slots, after dgu
+  char* split_base = (char*)dgu + align256((size_t)R_cap * 2 * I * 2);
+  const WgradSplitLayout SL = wgrad_split_layout(E_l, H, I);
+  WgradPlan plan{};
+  float* part[2];
+  for (int q = 0; q < 2; ++q) {
+    plan.t[q] = (int32_t*)(split_base + SL.plan_off[q]);
+    plan.tiles[q] = SL.tiles[q];
+    plan.slots[q] = SL.slots[q];
+    part[q] = (float*)(split_base + SL.part_off[q]);
+  }
+  ffn_sched_kernel<<<1, kMaxE, 0, s>>>(offsets, E_l, kBmGrouped, sched, ctrs, plan);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int mt_upper = R_cap / kBmGrouped + E_l;
@@ -2107,7 +2369,9 @@ hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, cons
   b.f_group_stride = (long)H * I;
   b.accumulate = accumulate ? 1 : 0;
   b.tile_ctr = ctrs + 1;
-  err = launch_gemm<K_WGRAD, kBmWgradDown, false, kWideWgrad>(b, E_l * b.n_mtiles * b.n_ntiles,
+  b.kplan = plan.t[1];
+  b.fpart = part[1];
+  err = launch_gemm<K_WGRAD, kBmWgradDown, false, kWideWgrad>(b, (E_l + SL.slots[1]) * b.n_mtiles * b.n_ntiles,
                                                              MOE_KERNEL_FFN_DOWN_WGRAD, s2);
   if (err != hipSuccess) return err;
 
@@ -2149,10 +2413,38 @@ hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, cons
   w.f_group_stride = (long)I * H;
   w.accumulate = accumulate ? 1 : 0;
   w.tile_ctr = ctrs + 3;
+  w.kplan = plan.t[0];
+  w.fpart = part[0];
   if (side != nullptr && (err = hipStreamWaitEvent(s2, side->mid, 0)) != hipSuccess) return err;
-  err = launch_gemm<K_WGRAD, kBmWgrad, false, kWideWgrad>(w, E_l * w.n_mtiles * w.n_ntiles,
+  err = launch_gemm<K_WGRAD, kBmWgrad, false, kWideWgrad>(w, (E_l + SL.slots[0]) * w.n_mtiles * w.n_ntiles,
                                                          MOE_KERNEL_FFN_GATEUP_WGRAD, s2);
   if (err != hipSuccess) return err;
+  // the split experts' partial slots, added in chunk order (both products)
+  {
+    WgradReduce r{};
+    r.plan[0] = plan.t[0];
+    r.plan[1] = plan.t[1];
+    r.part[0] = part[0];
+    r.part[1] = part[1];
+    r.out0[0] = dw_gate;
+    r.out1[0] = dw_up;
+    r.M[0] = 2 * I;
+    r.N[0] = H;
+    r.m_split[0] = I;
+    r.group_stride[0] = (long)I * H;
+    r.out0[1] = dw_down;
+    r.out1[1] = nullptr;
+    r.M[1] = H;
+    r.N[1] = I;
+    r.m_split[1] = H;
+    r.group_stride[1] = (long)H * I;
+    r.E_l = E_l;
+    r.slots[0] = SL.slots[0];
+    r.slots[1] = SL.slots[1];
+    ProfScope ps(MOE_KERNEL_FFN_WGRAD_REDUCE, s2);
+    wgrad_split_reduce_kernel<<<kCUs * 2, 256, 0, s2>>>(r);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   if (side != nullptr && wgrad_stream == nullptr) {
     if ((err = hipEventRecord(side->join, s2)) != hipSuccess) return err;
     if ((err = hipStreamWaitEvent(s, side->join, 0)) != hipSuccess) return err;

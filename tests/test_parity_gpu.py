@@ -27,7 +27,7 @@ import torch
 
 import oracle as O
 from mag_bounds import BETA, expert_forward_magnitudes, layer_magnitudes
-from workloads import EP_SHARE, FULL, SKEWED, TINY, TRAIN, Workload, make_inputs
+from workloads import EP_SHARE, FULL, SKEWED, TINY, TRAIN, TRAIN_SKEWED, Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -407,9 +407,15 @@ BWD_CASES = [TINY.scaled(name="tiny_fp32_train", train=True),
              TRAIN.scaled(name="multitile_bf16_train_t4096_h2048_i768_e16_k8_all_local", T=4096, E=16,
                           k=8, e_lo=0, e_hi=16),
              # long K-grouped weight gradients (4096 rows per expert) and ~540
-             # down data-gradient tiles on a narrow layer
+             # down data-gradient tiles on a narrow layer; every expert's rows
+             # exceed one CU's share of the weight gradients, so each is cut in
+             # four K chunks (three partial slots) for both products
              TRAIN.scaled(name="multitile_bf16_train_t8192_h256_i512_e16_k8_all_local", T=8192, H=256,
-                          I=512, E=16, k=8, e_lo=0, e_hi=16)]
+                          I=512, E=16, k=8, e_lo=0, e_hi=16),
+             # the training step under the skewed load, at full size: one local
+             # expert takes 8191 of 8747 rows (its weight gradients in 5 and 8
+             # chunks), ten get none
+             TRAIN_SKEWED]
 
 GUARDED = ("x_perm", "h_perm", "y_perm", "gu", "dy_perm", "dx_perm")
 
@@ -601,8 +607,13 @@ def test_router_input_grad_product_matches_oracle(T, H, E, k):
     assert (err <= bound).all()
 
 
-def test_weight_grad_accumulate():
-    w = TRAIN.scaled(name="acc", T=512, H=256, I=128, E=16, k=4, e_lo=0, e_hi=8)
+@pytest.mark.parametrize("w", [TRAIN.scaled(name="acc", T=512, H=256, I=128, E=16, k=4, e_lo=0, e_hi=8),
+                               # 2048 rows per expert: every expert's weight gradients in two K
+                               # chunks, chunk 0 adding to the prior values, then the partial
+                               TRAIN.scaled(name="acc_split", T=8192, H=256, I=128, E=16, k=4, e_lo=0,
+                                            e_hi=16)],
+                         ids=lambda w: w.name)
+def test_weight_grad_accumulate(w):
     inp = _inputs(w)
     t = _gpu_tensors(w, inp)
     layer, _, g = run_layer(w, t)
@@ -613,12 +624,30 @@ def test_weight_grad_accumulate():
     moe.moe_grouped_ffn_bwd(b["dy_perm"], b["x_perm"], b["gu"], b["h_perm"], b["offsets"], t["w_gate"],
                             t["w_up"], t["w_down"], accumulate=True, out=out)
     torch.cuda.synchronize()
-    for n in base:
-        torch.testing.assert_close(out[n], prior[n] + base[n], rtol=0, atol=1e-6)
+    if w.name == "acc_split":
+        # ((prior + chunk 0) + chunk 1) against prior + (chunk 0 + chunk 1): the
+        # same fp32 sums associated differently, within a few roundings of the
+        # prior plus the chunks' absolute sums (bounded by the gradient's
+        # first-order magnitude)
+        idx = layer.buf["topk_idx"].cpu().numpy()
+        mag = layer_magnitudes(inp["x"], inp["w_router"], idx, _oracle_weights(inp, idx), inp["w_gate"],
+                               inp["w_up"], inp["w_down"], w.e_lo, w.e_hi, inp["dy"])
+        for n in base:
+            bound = 2.0 ** -21 * (prior[n].abs().double().cpu().numpy() + mag[n]) + 1e-30
+            err = (out[n].double() - (prior[n].double() + base[n].double())).abs().cpu().numpy()
+            print(f"  {n}: max err / bound {(err / bound).max():.3g}", flush=True)
+            assert (err <= bound).all(), n
+    else:
+        for n in base:
+            torch.testing.assert_close(out[n], prior[n] + base[n], rtol=0, atol=1e-6)
 
 
-def test_layer_is_deterministic():
-    w = TRAIN.scaled(name="det", T=2048)
+@pytest.mark.parametrize("w", [TRAIN.scaled(name="det", T=2048),
+                               # weight gradients of split experts: partial slots added in chunk order
+                               TRAIN.scaled(name="det_split", T=8192, H=256, I=512, E=16, k=8, e_lo=0,
+                                            e_hi=16)],
+                         ids=lambda w: w.name)
+def test_layer_is_deterministic(w):
     inp = _inputs(w)
     t = _gpu_tensors(w, inp)
     _, y1, g1 = run_layer(w, t)

@@ -56,9 +56,10 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads: a tiny fp32 correctness case, one EP rank's share of
-# the 128-expert layer (forward), the full single-GPU layer, a skewed-load
-# variant and the EP rank's training step (forward + backward).
+# The workloads: a tiny fp32 correctness case, one EP rank's share of the
+# 128-expert layer (forward), the full single-GPU layer, a skewed-load
+# variant, the EP rank's training step (forward + backward) and that step
+# under the skewed load.
 WORKLOADS: Dict[str, Workload] = {
     w.name: w for w in [
         Workload("tiny_fp32_t256_h64_i32_e8_k2", 256, 64, 32, 8, 2, 0, 8, "f32"),
@@ -68,6 +69,11 @@ WORKLOADS: Dict[str, Workload] = {
                  skew=True),
         Workload("ep16_train_t8192_h2048_i768_e128_k8", 8192, 2048, 768, 128, 8, 0, 16, "bf16",
                  train=True),
+        # the training step under the skewed router bias, on the EP rank whose
+        # 16 local experts [80, 96) hold the hottest expert of this seed's
+        # ranking (8191 of its 8747 routed rows; 10 local experts get none)
+        Workload("ep16_train_skewed_t8192_h2048_i768_e128_k8", 8192, 2048, 768, 128, 8, 80, 96,
+                 "bf16", skew=True, train=True),
     ]
 }
 
@@ -76,6 +82,7 @@ EP_SHARE = WORKLOADS["ep16_share_t4096_h2048_i768_e128_k8"]
 FULL = WORKLOADS["full_t16384_h2048_i768_e128_k8"]
 SKEWED = WORKLOADS["skewed_t32768_h2048_i768_e128_k8"]
 TRAIN = WORKLOADS["ep16_train_t8192_h2048_i768_e128_k8"]
+TRAIN_SKEWED = WORKLOADS["ep16_train_skewed_t8192_h2048_i768_e128_k8"]
 
 SKEW_BIAS_SCALE = 2.0
 
