@@ -352,9 +352,13 @@ int moe_router_weight_t(const void* w_router, int H, int E, int dtype, void* w_r
  *   dx_perm [R_cap,H] dtype   gradient wrt x_perm
  *   dw_gate, dw_up [E_l,I,H] fp32, dw_down [E_l,H,I] fp32: overwritten
  *   (accumulate == 0) or added to (accumulate == 1); an expert with no rows
- *   gets exact zeros (or is left unchanged when accumulating).
- *   ws       MOE_OP_FFN_BWD workspace (schedule and the [R_cap,2I] gradient
- *            of g and u) */
+ *   gets exact zeros (or is left unchanged when accumulating).  In bf16 an
+ *   expert with far more rows than the rest (more than max(1024, R*tiles/256),
+ *   tiles = its weight-gradient tiles) has its row range cut into up to 8
+ *   chunks whose fp32 sums are added in chunk order: the result is the same
+ *   for every run, but its summation order differs from an unsplit one.
+ *   ws       MOE_OP_FFN_BWD workspace (schedule, the [R_cap,2I] gradient of
+ *            g and u, the weight gradients' chunk plans and partial sums) */
 int moe_grouped_ffn_bwd(const void* dy_perm, const void* x_perm, const void* gu_saved,
                         const void* h_perm, const int32_t* offsets, int E_l, int R_cap, int H,
                         int I, const void* w_gate, const void* w_up, const void* w_down,
