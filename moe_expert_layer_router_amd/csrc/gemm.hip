@@ -793,10 +793,13 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
       for (int h = 0; h < 2; ++h) {
         stage_half(st, acc, mi, h, lane);
         const int mb = m0 + wm * WM + mi * 32 + 16 * h;
-        const bool first = mb < p.m_split || p.f1 == nullptr;
-        float* base = (first ? p.f0 : p.f1) + e * p.f_group_stride;
-        const int mrel = first ? mb : mb - p.m_split;
-        const int nrows = (first ? min(p.m_split, p.M) : p.M - p.m_split) - mrel;
+        // a split chunk's partial slot is one [M][N] block, overwritten
+        const bool part = slot >= 0;
+        const bool first = part || mb < p.m_split || p.f1 == nullptr;
+        float* base = part ? p.fpart + (long)slot * p.M * p.ldc
+                           : (first ? p.f0 : p.f1) + e * p.f_group_stride;
+        const int mrel = (part || first) ? mb : mb - p.m_split;
+        const int nrows = (part ? p.M : first ? min(p.m_split, p.M) : p.M - p.m_split) - mrel;
         const out_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
             base + (long)max(mrel, 0) * p.ldc, 0, nrows > 0 ? (int)(nrows * p.ldc * 4) : 0, 0x00020000);
 #pragma unroll
@@ -814,7 +817,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16_t (&acc
           }
           const uint32_t oa = n < p.N ? (uint32_t)((r * p.ldc + n) * 4) : kOutKill;
           const uint32_t ob = n + 64 < p.N ? (uint32_t)((r * p.ldc + n + 64) * 4) : kOutKill;
-          if (p.accumulate != 0) {  // uniform
+          if (p.accumulate != 0 && !part) {  // uniform
             a = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, oa, 0, 0)) + a;
             b = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, ob, 0, 0)) + b;
           }
@@ -1255,8 +1258,16 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p, int work) {
     const int rem = work - e * p.n_mtiles * p.n_ntiles;
     m0 = (rem / p.n_ntiles) * BM;
     nt = rem % p.n_ntiles;
-    kbeg = p.offsets[e] >> 1;
-    kend = p.offsets[e + 1] >> 1;
+    if (p.kplan != nullptr) {  // chunk `e` of the plan (code columns, multiples of 64)
+      const int32_t* c = p.kplan + 2 + 4 * e;
+      slot = c[3];
+      kbeg = c[1] >> 1;
+      kend = c[2] >> 1;
+      e = c[0];
+    } else {
+      kbeg = p.offsets[e] >> 1;
+      kend = p.offsets[e + 1] >> 1;
+    }
     row0 = m0;
   } else if constexpr (KIND == K_WGRAD) {
     e = work / (p.n_mtiles * p.n_ntiles);
@@ -1480,7 +1491,7 @@ void gemm_kernel(const GemmArgs p) {
   const FragLanes<C> L = frag_lanes<C>(lane, wave);
 
   int total;
-  if constexpr (KIND == K_WGRAD)
+  if constexpr (KIND == K_WGRAD || KIND == K_WGRAD8)
     total = (p.kplan != nullptr ? p.kplan[0] : p.groups) * p.n_mtiles * p.n_ntiles;
   else if constexpr (k_grouped(KIND))
     total = p.groups * p.n_mtiles * p.n_ntiles;
@@ -1621,57 +1632,15 @@ void gemm_kernel(const GemmArgs p) {
   }
 }
 
-// Tile table of the M-grouped products: for every expert with rows, one entry
-// (expert, first row, end row) per `rows` rows.  sched[0] = number of entries.
-__global__ __launch_bounds__(kMaxE) void ffn_sched_kernel(const int32_t* __restrict__ offsets,
-                                                          int E_l, int rows,
-                                                          int32_t* __restrict__ sched,
-                                                          int32_t* __restrict__ ctrs,
-                                                          WgradPlan plan = WgradPlan{}) {
-  // the dynamic tile counters of the products that follow start at zero
-  if (ctrs != nullptr && threadIdx.x < kTileCtrs) ctrs[threadIdx.x] = 0;
-  __shared__ int s[kMaxE + 1];      // s[g] = tiles of experts < g
-  __shared__ int s_off[kMaxE + 1];  // the offsets, in LDS for the tile loop
-  __shared__ int s_wave[kMaxE / kWave];
-  const int e = threadIdx.x, lane = e & (kWave - 1), w = e / kWave;
-  const int o0 = (e < E_l) ? offsets[e] : 0;
-  const int o1 = (e < E_l) ? offsets[e + 1] : 0;
-  // Only the owners write: s_off[E_l] comes from thread E_l - 1 alone (thread
-  // E_l, in another wave when E_l % 64 == 0, must not store its zero there).
-  if (e < E_l) s_off[e] = o0;
-  if (e == E_l - 1) s_off[E_l] = o1;
-  int v = (o1 - o0 + rows - 1) / rows;  // this expert's tiles
-  // inclusive scan: within each wave by shuffles, then the waves' totals
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int t = __shfl_up(v, d, kWave);
-    if (lane >= d) v += t;
-  }
-  if (lane == kWave - 1) s_wave[w] = v;
-  __syncthreads();
-  for (int q = 0; q < w; ++q) v += s_wave[q];
-  s[e + 1] = v;
-  if (e == 0) s[0] = 0;
-  __syncthreads();
-  const int count = s[E_l];
-  if (e == 0) sched[0] = count;
-  for (int i = e; i < count; i += kMaxE) {
-    int lo = 0, hi = E_l - 1;  // largest g with s[g] <= i
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s[mid] <= i) lo = mid; else hi = mid - 1;
-    }
-    const int r0 = s_off[lo] + (i - s[lo]) * rows;
-    sched[1 + 3 * i] = lo;
-    sched[2 + 3 * i] = r0;
-    sched[3 + 3 * i] = min(r0 + rows, s_off[lo + 1]);
-  }
-  if (plan.t[0] == nullptr) return;
-  // The weight gradients' K-chunk plans.  When no expert exceeds its product's
-  // split threshold (balanced loads), each expert is one chunk in expert
-  // order, written by its own thread.  Otherwise experts go in order of rows,
-  // largest first (ties: lower id first); each thread sizes its own expert's
-  // chunks, and scans over the ranking give its first chunk and first slot.
+// The weight gradients' K-chunk plans (one workgroup of kMaxE threads; thread
+// e holds expert e's offsets o0, o1; s_off the offsets in LDS, complete).
+// When no expert exceeds its product's split threshold (balanced loads), each
+// expert is one chunk in expert order, written by its own thread.  Otherwise
+// experts go in order of rows, largest first (ties: lower id first); each
+// thread sizes its own expert's chunks, and scans over the ranking give its
+// first chunk and first slot.
+__device__ void build_wgrad_plans(const int* s_off, int E_l, int o0, int o1, int e, int lane, int w,
+                                  int* s_wave, const WgradPlan& plan) {
   const long R = (long)s_off[E_l] - s_off[0];
   bool any = false;
   for (int q = 0; q < 2; ++q) {
@@ -1795,6 +1764,71 @@ __global__ __launch_bounds__(kMaxE) void ffn_sched_kernel(const int32_t* __restr
   }
 }
 
+// Tile table of the M-grouped products: for every expert with rows, one entry
+// (expert, first row, end row) per `rows` rows.  sched[0] = number of entries.
+__global__ __launch_bounds__(kMaxE) void ffn_sched_kernel(const int32_t* __restrict__ offsets,
+                                                          int E_l, int rows,
+                                                          int32_t* __restrict__ sched,
+                                                          int32_t* __restrict__ ctrs,
+                                                          WgradPlan plan = WgradPlan{}) {
+  // the dynamic tile counters of the products that follow start at zero
+  if (ctrs != nullptr && threadIdx.x < kTileCtrs) ctrs[threadIdx.x] = 0;
+  __shared__ int s[kMaxE + 1];      // s[g] = tiles of experts < g
+  __shared__ int s_off[kMaxE + 1];  // the offsets, in LDS for the tile loop
+  __shared__ int s_wave[kMaxE / kWave];
+  const int e = threadIdx.x, lane = e & (kWave - 1), w = e / kWave;
+  const int o0 = (e < E_l) ? offsets[e] : 0;
+  const int o1 = (e < E_l) ? offsets[e + 1] : 0;
+  // Only the owners write: s_off[E_l] comes from thread E_l - 1 alone (thread
+  // E_l, in another wave when E_l % 64 == 0, must not store its zero there).
+  if (e < E_l) s_off[e] = o0;
+  if (e == E_l - 1) s_off[E_l] = o1;
+  int v = (o1 - o0 + rows - 1) / rows;  // this expert's tiles
+  // inclusive scan: within each wave by shuffles, then the waves' totals
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int t = __shfl_up(v, d, kWave);
+    if (lane >= d) v += t;
+  }
+  if (lane == kWave - 1) s_wave[w] = v;
+  __syncthreads();
+  for (int q = 0; q < w; ++q) v += s_wave[q];
+  s[e + 1] = v;
+  if (e == 0) s[0] = 0;
+  __syncthreads();
+  const int count = s[E_l];
+  if (e == 0) sched[0] = count;
+  for (int i = e; i < count; i += kMaxE) {
+    int lo = 0, hi = E_l - 1;  // largest g with s[g] <= i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    const int r0 = s_off[lo] + (i - s[lo]) * rows;
+    sched[1 + 3 * i] = lo;
+    sched[2 + 3 * i] = r0;
+    sched[3 + 3 * i] = min(r0 + rows, s_off[lo + 1]);
+  }
+  if (plan.t[0] == nullptr) return;
+  __syncthreads();
+  build_wgrad_plans(s_off, E_l, o0, o1, e, lane, w, s_wave, plan);
+}
+
+// The plans alone, from a given offsets array (the FP8 weight gradient's
+// padded code offsets).
+__global__ __launch_bounds__(kMaxE) void wgrad_plan_kernel(const int32_t* __restrict__ offsets, int E_l,
+                                                           WgradPlan plan) {
+  __shared__ int s_off[kMaxE + 1];
+  __shared__ int s_wave[kMaxE / kWave];
+  const int e = threadIdx.x, lane = e & (kWave - 1), w = e / kWave;
+  const int o0 = (e < E_l) ? offsets[e] : 0;
+  const int o1 = (e < E_l) ? offsets[e + 1] : 0;
+  if (e < E_l) s_off[e] = o0;
+  if (e == E_l - 1) s_off[E_l] = o1;
+  __syncthreads();
+  build_wgrad_plans(s_off, E_l, o0, o1, e, lane, w, s_wave, plan);
+}
+
 // The split experts' partial slots added to their weight gradients in chunk
 // order: out += part[slot0] + ... (chunk 0 wrote out itself).  Both products in
 // one launch; elements in float4s, grid-strided.  Nothing to do (the usual
@@ -1884,6 +1918,34 @@ static WgradSplitLayout wgrad_split_layout(int E_l, int H, int I) {
   return L;
 }
 size_t ffn_wgrad_split_bytes(int E_l, int H, int I) { return wgrad_split_layout(E_l, H, I).bytes; }
+
+// The split experts' partial slots added in chunk order, for both products.
+static hipError_t launch_wgrad_split_reduce(const WgradPlan& plan, float* const (&part)[2],
+                                            const WgradSplitLayout& SL, int E_l, int H, int I,
+                                            float* dw_gate, float* dw_up, float* dw_down, hipStream_t s) {
+  WgradReduce r{};
+  for (int q = 0; q < 2; ++q) {
+    r.plan[q] = plan.t[q];
+    r.part[q] = part[q];
+    r.slots[q] = SL.slots[q];
+  }
+  r.out0[0] = dw_gate;
+  r.out1[0] = dw_up;
+  r.M[0] = 2 * I;
+  r.N[0] = H;
+  r.m_split[0] = I;
+  r.group_stride[0] = (long)I * H;
+  r.out0[1] = dw_down;
+  r.out1[1] = nullptr;
+  r.M[1] = H;
+  r.N[1] = I;
+  r.m_split[1] = H;
+  r.group_stride[1] = (long)H * I;
+  r.E_l = E_l;
+  ProfScope ps(MOE_KERNEL_FFN_WGRAD_REDUCE, s);
+  wgrad_split_reduce_kernel<<<kCUs * 2, 256, 0, s>>>(r);
+  return hipGetLastError();
+}
 static int32_t* ffn_tile_ctrs(void* ws, int R_cap, int E_l) {
   return (int32_t*)((char*)ws + ffn_sched_table_bytes(R_cap, E_l));
 }
@@ -2159,7 +2221,7 @@ static size_t wgrad_fp8_codes_bytes(int R_cap, int E_l, int C) {
 size_t ffn_wgrad_fp8_ws_bytes(int R_cap, int E_l, int H, int I) {
   return wgrad_fp8_codes_bytes(R_cap, E_l, 2 * I) + 2 * wgrad_fp8_codes_bytes(R_cap, E_l, H) +
          wgrad_fp8_codes_bytes(R_cap, E_l, I) + align256((size_t)E_l * (3 * I + 2 * H) * 4) +
-         align256((size_t)(E_l + 1) * 4) + 256;
+         align256((size_t)(E_l + 1) * 4) + 256 + ffn_wgrad_split_bytes(E_l, H, I);
 }
 
 hipError_t launch_ffn_wgrad_fp8(const bf16_t* x, const int32_t* src_row, const bf16_t* dgu,
@@ -2185,6 +2247,17 @@ hipError_t launch_ffn_wgrad_fp8(const bf16_t* x, const int32_t* src_row, const b
   int32_t* poff = (int32_t*)w;
   w += align256((size_t)(E_l + 1) * 4);
   int32_t* ctrs = (int32_t*)w;
+  w += 256;
+  // the K-chunk plans over the padded code columns and the partial slots
+  const WgradSplitLayout SL = wgrad_split_layout(E_l, H, I);
+  WgradPlan plan{};
+  float* part[2];
+  for (int q = 0; q < 2; ++q) {
+    plan.t[q] = (int32_t*)(w + SL.plan_off[q]);
+    plan.tiles[q] = SL.tiles[q];
+    plan.slots[q] = SL.slots[q];
+    part[q] = (float*)(w + SL.part_off[q]);
+  }
 
   QuantGroupT q{};
   q.t[0] = {dgu, nullptr, 2L * I, 2 * I, q_gu, s_gu};
@@ -2200,6 +2273,8 @@ hipError_t launch_ffn_wgrad_fp8(const bf16_t* x, const int32_t* src_row, const b
   q.nctrs = 2;
   hipError_t err = launch_quantize_group_t_fp8(q, s);
   if (err != hipSuccess) return err;
+  wgrad_plan_kernel<<<1, kMaxE, 0, s>>>(poff, E_l, plan);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
 
   // E4M3 rows of Kp codes run through the ring as rows of Kp / 2 bf16 slots.
   GemmArgs g{};
@@ -2224,7 +2299,9 @@ hipError_t launch_ffn_wgrad_fp8(const bf16_t* x, const int32_t* src_row, const b
   g.sb0 = s_x;
   g.sb_group_stride = H;
   g.tile_ctr = ctrs;
-  err = launch_gemm<K_WGRAD8, kBmWgrad, true>(g, E_l * g.n_mtiles * g.n_ntiles,
+  g.kplan = plan.t[0];
+  g.fpart = part[0];
+  err = launch_gemm<K_WGRAD8, kBmWgrad, true>(g, (E_l + SL.slots[0]) * g.n_mtiles * g.n_ntiles,
                                               MOE_KERNEL_FFN_GATEUP_WGRAD, s);
   if (err != hipSuccess) return err;
 
@@ -2249,8 +2326,12 @@ hipError_t launch_ffn_wgrad_fp8(const bf16_t* x, const int32_t* src_row, const b
   d.sb0 = s_h;
   d.sb_group_stride = I;
   d.tile_ctr = ctrs + 1;
-  return launch_gemm<K_WGRAD8, kBmWgrad, true>(d, E_l * d.n_mtiles * d.n_ntiles,
-                                               MOE_KERNEL_FFN_DOWN_WGRAD, s);
+  d.kplan = plan.t[1];
+  d.fpart = part[1];
+  err = launch_gemm<K_WGRAD8, kBmWgrad, true>(d, (E_l + SL.slots[1]) * d.n_mtiles * d.n_ntiles,
+                                              MOE_KERNEL_FFN_DOWN_WGRAD, s);
+  if (err != hipSuccess) return err;
+  return launch_wgrad_split_reduce(plan, part, SL, E_l, H, I, dw_gate, dw_up, dw_down, s);
 }
 
 // A second stream of the calling device for products that may run beside
@@ -2420,31 +2501,8 @@ hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, cons
                                                          MOE_KERNEL_FFN_GATEUP_WGRAD, s2);
   if (err != hipSuccess) return err;
   // the split experts' partial slots, added in chunk order (both products)
-  {
-    WgradReduce r{};
-    r.plan[0] = plan.t[0];
-    r.plan[1] = plan.t[1];
-    r.part[0] = part[0];
-    r.part[1] = part[1];
-    r.out0[0] = dw_gate;
-    r.out1[0] = dw_up;
-    r.M[0] = 2 * I;
-    r.N[0] = H;
-    r.m_split[0] = I;
-    r.group_stride[0] = (long)I * H;
-    r.out0[1] = dw_down;
-    r.out1[1] = nullptr;
-    r.M[1] = H;
-    r.N[1] = I;
-    r.m_split[1] = H;
-    r.group_stride[1] = (long)H * I;
-    r.E_l = E_l;
-    r.slots[0] = SL.slots[0];
-    r.slots[1] = SL.slots[1];
-    ProfScope ps(MOE_KERNEL_FFN_WGRAD_REDUCE, s2);
-    wgrad_split_reduce_kernel<<<kCUs * 2, 256, 0, s2>>>(r);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-  }
+  if ((err = launch_wgrad_split_reduce(plan, part, SL, E_l, H, I, dw_gate, dw_up, dw_down, s2)) != hipSuccess)
+    return err;
   if (side != nullptr && wgrad_stream == nullptr) {
     if ((err = hipEventRecord(side->join, s2)) != hipSuccess) return err;
     if ((err = hipStreamWaitEvent(s, side->join, 0)) != hipSuccess) return err;
