@@ -515,6 +515,7 @@ int moe_quantize_fp8_group_t(const void* src, const int32_t* src_row, int C,
   a.nt = 1;
   a.offsets = offsets;
   a.E_l = E_l;
+  a.max_rows = R_cap;
   a.Kp = q_pitch;
   a.poff = poff;
   return hip_status(launch_quantize_group_t_fp8(a, begin_launch(stream)), fn);

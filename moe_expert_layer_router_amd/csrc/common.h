@@ -242,6 +242,7 @@ struct QuantGroupT {
   int nt;
   const int32_t* offsets;  // [groups + 1] row offsets (device)
   int E_l;
+  int max_rows;            // bound on offsets[E_l] (sizes the grid)
   int Kp;                  // code row pitch
   int32_t* poff;           // out: [groups + 1] padded offsets (multiples of 64)
   int32_t* ctrs;           // counters zeroed for the products that follow, or null

@@ -337,79 +337,192 @@ hipError_t launch_quantize_w_fp8(const bf16_t* w0, const bf16_t* w1, int batch, 
 // to the column restricted to the group, and the codes of that column go to
 // row c of the transposed output, columns poff[g] .. poff[g] + n_g - 1, with
 // zero codes up to the next multiple of 64 (poff[g] = the sum of the earlier
-// groups' row counts rounded up to 64, also written out).  A workgroup takes
-// 64 columns of one tensor for one group: pass 1 the column maxima (each
-// thread 8 columns of every 32nd row, then an LDS reduction), pass 2 the
-// codes, through 64 x 64 tiles in LDS so that each thread writes 16
-// consecutive codes of one output row.  Columns of several tensors share one
-// launch (strips numbered tensor by tensor).
-__global__ __launch_bounds__(256) void quantize_group_t_fp8_kernel(const QuantGroupT a) {
-  __shared__ float s_max[32][65];
-  __shared__ int s_e[64];
-  __shared__ __align__(16) bf16_t s_tile[64][64];
-  __shared__ int s_poff;
-  const int g = blockIdx.y, t = threadIdx.x;
+// groups' row counts rounded up to 64, also written out).
+//
+// A group's rows are cut into chunks of kGtChunk rows (an empty group is one
+// empty chunk), so that a hot group spreads over as many workgroups as its
+// rows need.  Three launches:
+//   1. zero the scales (and the caller's tile counters);
+//   2. per (64 columns, chunk): the chunk's column maxima, and the scale 2^e
+//      they call for merged into the scale by an atomic max on its bits.  e
+//      never falls as the maximum grows and 2^e (down to 2^-141 for the
+//      smallest bf16, a float subnormal) orders like its bit pattern, so the
+//      merge of the chunks' scales is the scale of the group's maximum, in any
+//      order.  A zero column leaves 0;
+//   3. per (64 columns, chunk): e read back from the scale (0 -> e = 0, and the
+//      chunk at the group's start stores 1), the chunk's codes through a
+//      256 x 64 tile in LDS, each thread writing 64 consecutive codes of one
+//      output row.
+// Columns of several tensors share each launch (strips numbered tensor by
+// tensor); the grid's second dimension strides over the chunks.
+constexpr int kGtChunk = 256;
+constexpr int kGtMaxGridY = 64;
+
+struct GtChunk {
+  int g;     // group, -1 past the last chunk
+  int rbeg;  // first row of the chunk within the group
+  int n;     // rows in the chunk
+  int o0;    // offsets[g]
+  int poff;  // padded start of the group
+  int ng;    // rows in the group
+};
+
+// Chunk c of the list (group 0's chunks, then group 1's, ...), found by wave 0
+// with scans over 64 groups at a time; the result goes through LDS to the
+// whole workgroup.
+__device__ GtChunk gt_find_chunk(const int32_t* offsets, int E_l, int c, int t, GtChunk* s_c) {
+  if (t < kWave) {
+    int base_c = 0, base_p = 0;
+    bool found = false;
+    for (int j0 = 0; j0 < E_l && !found; j0 += kWave) {
+      const int j = j0 + t;
+      const int n = j < E_l ? offsets[j + 1] - offsets[j] : 0;
+      const int nc = j < E_l ? max(1, (n + kGtChunk - 1) / kGtChunk) : 0;
+      const int pd = (n + 63) & ~63;
+      int ic = nc, ip = pd;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int xc = __shfl_up(ic, o, kWave), xp = __shfl_up(ip, o, kWave);
+        if (t >= o) {
+          ic += xc;
+          ip += xp;
+        }
+      }
+      const int ec = base_c + ic - nc;
+      if (nc > 0 && c >= ec && c < ec + nc) {
+        const int k = c - ec;
+        *s_c = GtChunk{j, k * kGtChunk, min(n - k * kGtChunk, kGtChunk), offsets[j],
+                       base_p + ip - pd, n};
+      }
+      const int tc = __shfl(ic, kWave - 1, kWave), tp = __shfl(ip, kWave - 1, kWave);
+      found = c < base_c + tc;
+      base_c += tc;
+      base_p += tp;
+    }
+    if (!found && t == 0) s_c->g = -1;
+  }
+  __syncthreads();
+  const GtChunk r = *s_c;
+  __syncthreads();  // s_c is rewritten by the next lookup
+  return r;
+}
+
+// the tensor and 64-column strip of blockIdx.x
+__device__ __forceinline__ const QuantGroupTensor& gt_tensor(const QuantGroupT& a, int& c0) {
   int ti = 0, strip = blockIdx.x;
   while (ti + 1 < a.nt && strip >= a.t[ti].C / 64) {
     strip -= a.t[ti].C / 64;
     ++ti;
   }
-  const QuantGroupTensor T = a.t[ti];
-  const int c0 = strip * 64;
-  const int o0 = a.offsets[g], n = a.offsets[g + 1] - o0;
-  if (t < kWave) {  // padded start of this group
-    int acc = 0;
-    for (int j = t; j < g; j += kWave) acc += (a.offsets[j + 1] - a.offsets[j] + 63) & ~63;
+  c0 = strip * 64;
+  return a.t[ti];
+}
+
+__global__ __launch_bounds__(256) void quantize_group_t_zero_kernel(const QuantGroupT a) {
+  const QuantGroupTensor& T = a.t[blockIdx.y];
+  const long n = (long)a.E_l * T.C;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256)
+    T.scale[i] = 0.f;
+  if (a.ctrs != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && (int)threadIdx.x < a.nctrs)
+    a.ctrs[threadIdx.x] = 0;
+}
+
+__global__ __launch_bounds__(256) void quantize_group_t_max_kernel(const QuantGroupT a) {
+  __shared__ float s_max[32][65];
+  __shared__ GtChunk s_c;
+  const int t = threadIdx.x, cc = t & 7, r0 = t >> 3;
+  int c0;
+  const QuantGroupTensor& T = gt_tensor(a, c0);
+  for (int c = blockIdx.y;; c += gridDim.y) {
+    const GtChunk k = gt_find_chunk(a.offsets, a.E_l, c, t, &s_c);
+    if (k.g < 0) break;
+    uint4 v[kGtChunk / 32];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
-    if (t == 0) s_poff = acc;
-  }
-  if (a.ctrs != nullptr && blockIdx.x == 0 && g == 0 && t < a.nctrs) a.ctrs[t] = 0;
-  const int cc = t & 7, r0 = t >> 3;
-  float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int r = r0; r < n; r += 32) {
-    const long row = T.rows != nullptr ? T.rows[o0 + r] : o0 + r;
-    float v[8];
-    unpack8(*reinterpret_cast<const uint4*>(T.src + row * T.ld + c0 + 8 * cc), v);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf(v[i]));
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) s_max[r0][8 * cc + i] = m[i];
-  __syncthreads();
-  const int poff = s_poff;
-  if (blockIdx.x == 0 && t == 0) {
-    a.poff[g] = poff;
-    if (g == a.E_l - 1) a.poff[a.E_l] = poff + ((n + 63) & ~63);
-  }
-  if (t < 64) {
-    float mx = 0.f;
-    for (int r = 0; r < 32; ++r) mx = fmaxf(mx, s_max[r][t]);
-    const int e = fp8_exponent(mx);
-    s_e[t] = e;
-    T.scale[(size_t)g * T.C + c0 + t] = ldexpf(1.f, e);
-  }
-  __syncthreads();
-  const int oc = t & 63, og = t >> 6;  // output row c0 + oc, 16 group rows 16 og .. + 15 of a tile
-  const int e = s_e[oc];
-  uint8_t* qrow = T.q + (size_t)(c0 + oc) * a.Kp + poff;
-  for (int j0 = 0; j0 < n; j0 += 64) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = r0 + 32 * h;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (j0 + r < n) {
-        const long row = T.rows != nullptr ? T.rows[o0 + j0 + r] : o0 + j0 + r;
-        v = *reinterpret_cast<const uint4*>(T.src + row * T.ld + c0 + 8 * cc);
+    for (int i = 0; i < kGtChunk / 32; ++i) {
+      const int r = k.rbeg + r0 + 32 * i;
+      v[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (r0 + 32 * i < k.n) {
+        const long row = T.rows != nullptr ? T.rows[k.o0 + r] : k.o0 + r;
+        v[i] = *reinterpret_cast<const uint4*>(T.src + row * T.ld + c0 + 8 * cc);
       }
-      *reinterpret_cast<uint4*>(&s_tile[r][8 * cc]) = v;
+    }
+    float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kGtChunk / 32; ++i) {
+      float f[8];
+      unpack8(v[i], f);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m[j] = fmaxf(m[j], fabsf(f[j]));
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s_max[r0][8 * cc + j] = m[j];
+    __syncthreads();
+    if (t < 64) {
+      float mx = 0.f;
+      for (int r = 0; r < 32; ++r) mx = fmaxf(mx, s_max[r][t]);
+      if (mx > 0.f)
+        atomicMax(reinterpret_cast<unsigned int*>(T.scale + (size_t)k.g * T.C + c0 + t),
+                  __float_as_uint(ldexpf(1.f, fp8_exponent(mx))));
     }
     __syncthreads();
-    float v[16];
+  }
+}
+
+// e of a scale 2^e from its bits (normal or subnormal); 0 for a zero scale
+__device__ __forceinline__ int gt_scale_exponent(uint32_t b) {
+  if (b == 0u) return 0;
+  if (b >= 0x00800000u) return (int)(b >> 23) - 127;
+  return (31 - __clz(b)) - 149;
+}
+
+__global__ __launch_bounds__(256) void quantize_group_t_codes_kernel(const QuantGroupT a) {
+  __shared__ __align__(16) bf16_t s_tile[kGtChunk][64];
+  __shared__ int s_e[64];
+  __shared__ GtChunk s_c;
+  const int t = threadIdx.x, cc = t & 7, r0 = t >> 3;
+  const int oc = t & 63, og = t >> 6;  // output row c0 + oc, chunk rows 64 og .. 64 og + 63
+  int c0;
+  const QuantGroupTensor& T = gt_tensor(a, c0);
+  for (int c = blockIdx.y;; c += gridDim.y) {
+    const GtChunk k = gt_find_chunk(a.offsets, a.E_l, c, t, &s_c);
+    if (k.g < 0) break;
+    if (t < 64) {
+      float* sp = T.scale + (size_t)k.g * T.C + c0 + t;
+      const uint32_t b = __float_as_uint(*sp);
+      s_e[t] = gt_scale_exponent(b);
+      if (b == 0u && k.rbeg == 0) *sp = 1.f;
+    }
+    if (blockIdx.x == 0 && k.rbeg == 0 && t == 0) {
+      a.poff[k.g] = k.poff;
+      if (k.g == a.E_l - 1) a.poff[a.E_l] = k.poff + ((k.ng + 63) & ~63);
+    }
+    const int rows64 = (k.n + 63) & ~63;  // the chunk's rows with the group's zero padding
+    uint4 v[kGtChunk / 32];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = bf2f(s_tile[16 * og + i][oc]);
-    const uint2 lo = fp8_codes8(v, e), hi = fp8_codes8(v + 8, e);
-    *reinterpret_cast<uint4*>(qrow + j0 + 16 * og) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    for (int i = 0; i < kGtChunk / 32; ++i) {
+      const int r = r0 + 32 * i;
+      v[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (r < k.n) {
+        const long row = T.rows != nullptr ? T.rows[k.o0 + k.rbeg + r] : k.o0 + k.rbeg + r;
+        v[i] = *reinterpret_cast<const uint4*>(T.src + row * T.ld + c0 + 8 * cc);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kGtChunk / 32; ++i)
+      if (r0 + 32 * i < rows64) *reinterpret_cast<uint4*>(&s_tile[r0 + 32 * i][8 * cc]) = v[i];
+    __syncthreads();
+    if (64 * og < rows64) {
+      const int e = s_e[oc];
+      uint8_t* qrow = T.q + (size_t)(c0 + oc) * a.Kp + k.poff + k.rbeg + 64 * og;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        float f[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) f[i] = bf2f(s_tile[64 * og + 16 * h + i][oc]);
+        const uint2 lo = fp8_codes8(f, e), hi = fp8_codes8(f + 8, e);
+        *reinterpret_cast<uint4*>(qrow + 16 * h) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+    }
     __syncthreads();
   }
 }
@@ -418,7 +531,18 @@ hipError_t launch_quantize_group_t_fp8(const QuantGroupT& q, hipStream_t s) {
   int strips = 0;
   for (int i = 0; i < q.nt; ++i) strips += q.t[i].C / 64;
   if (strips == 0 || q.E_l <= 0) return hipSuccess;
-  quantize_group_t_fp8_kernel<<<dim3(strips, q.E_l), 256, 0, s>>>(q);
+  long zero_max = 0;
+  for (int i = 0; i < q.nt; ++i) zero_max = std::max(zero_max, (long)q.E_l * q.t[i].C);
+  const unsigned zero_x = (unsigned)std::min<long>((zero_max + 4095) / 4096, 256);
+  quantize_group_t_zero_kernel<<<dim3(zero_x, q.nt), 256, 0, s>>>(q);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // at most ceil(rows / kGtChunk) + E_l chunks
+  const long chunks = ((long)q.max_rows + kGtChunk - 1) / kGtChunk + q.E_l;
+  const dim3 grid(strips, (unsigned)std::min<long>(chunks, kGtMaxGridY));
+  quantize_group_t_max_kernel<<<grid, 256, 0, s>>>(q);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  quantize_group_t_codes_kernel<<<grid, 256, 0, s>>>(q);
   return hipGetLastError();
 }
 

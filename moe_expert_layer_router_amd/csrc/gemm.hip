@@ -2267,6 +2267,7 @@ hipError_t launch_ffn_wgrad_fp8(const bf16_t* x, const int32_t* src_row, const b
   q.nt = 4;
   q.offsets = offsets;
   q.E_l = E_l;
+  q.max_rows = R_cap;
   q.Kp = Kp;
   q.poff = poff;
   q.ctrs = ctrs;
