@@ -355,22 +355,43 @@ def _round64(n):
     return (n + 63) // 64 * 64
 
 
+@pytest.mark.parametrize("layout", ["small", "chunked"])
 @pytest.mark.parametrize("mapped", [False, True], ids=["grouped_rows", "token_rows_via_src_row"])
-def test_quantize_fp8_group_t_bit_exact(mapped):
+def test_quantize_fp8_group_t_bit_exact(mapped, layout):
     """Per-(group, column) codes of grouped rows, transposed: codes, scales and padded
     offsets bit for bit against the oracle, zero codes in each group's padding, and
-    nothing written past the last group.  Groups: one of 0 rows, one of 1, one of
-    exactly 64, one of 130; columns with a zero group column, a maximum exactly on a
-    scale boundary and values deep in the subnormal codes."""
+    nothing written past the last group.  small: groups of 37, 0, 1, exactly 64 and
+    130 rows; columns with a zero group column, a maximum exactly on a scale boundary
+    and values deep in the subnormal codes.  chunked: groups past the quantizer's
+    256-row chunks (700 rows, exactly 256, 257 and 512) among 100 groups (0..40
+    rows, some empty), so that a group's maxima come from several chunks and the
+    chunk list is longer than the grid; in the 700-row group one column's maximum
+    sits in its last chunk only, one column is zero except for tiny values in the
+    first chunk, one is zero throughout, and one has a scale below the smallest
+    normal float (2^-129)."""
     rng = np.random.default_rng(51)
-    counts = [37, 0, 1, 64, 130]
+    if layout == "small":
+        counts = [37, 0, 1, 64, 130]
+    else:
+        counts = [700, 0, 256, 257, 512, 1] + [int(v) * (v % 5 != 0) for v in rng.integers(0, 41, 94)]
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     R, C, E_l = int(off[-1]), 192, len(counts)
     a = rng.standard_normal((R, C)) * np.exp2(rng.integers(-30, 30, size=(1, C)))
-    a[off[0]:off[1], 5] = 0.0
-    a[off[3] + 7, 9] = 448.0 * 2.0 ** 4
-    a[off[4]:off[5], 11] = rng.standard_normal(counts[4]) * 2.0 ** -30
-    a[off[4], 11] = 1.0
+    if layout == "small":
+        a[off[0]:off[1], 5] = 0.0
+        a[off[3] + 7, 9] = 448.0 * 2.0 ** 4
+        a[off[4]:off[5], 11] = rng.standard_normal(counts[4]) * 2.0 ** -30
+        a[off[4], 11] = 1.0
+    else:
+        a[:, 3] = rng.standard_normal(R)
+        a[690, 3] = 448.0 * 2.0 ** 6          # group 0's maximum in its third chunk
+        a[:, 4] = 0.0
+        a[:100, 4] = rng.standard_normal(100) * 2.0 ** -40
+        a[:700, 5] = 0.0
+        a[:700, 6] = rng.choice([-1.0, 1.0], 700) * rng.uniform(1.0, 6.0, 700) * 2.0 ** -124  # normal floats
+        a[300, 6] = 448.0 * 2.0 ** -129       # scale 2^-129: a float subnormal
+        a[off[2] + 255, 7] = 448.0 * 2.0 ** 3  # last row of a 256-row group
+        a[off[3] + 256, 7] = -448.0 * 2.0 ** 5  # the one row of a 257-row group's second chunk
     a32 = a.astype(np.float32)
     if mapped:     # token rows in another order, gathered through src_row
         perm = rng.permutation(R)
