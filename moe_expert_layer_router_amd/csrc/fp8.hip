@@ -11,6 +11,8 @@
 // v / s is exact (a power-of-two scaling), so the codes are those of an exact
 // rounding.  One wave per row: a pass for the maximum, a pass (from cache)
 // for the codes.
+#include <algorithm>
+
 #include "common.h"
 
 namespace moe {
@@ -339,24 +341,31 @@ hipError_t launch_quantize_w_fp8(const bf16_t* w0, const bf16_t* w1, int batch, 
 // zero codes up to the next multiple of 64 (poff[g] = the sum of the earlier
 // groups' row counts rounded up to 64, also written out).
 //
-// A group's rows are cut into chunks of kGtChunk rows (an empty group is one
-// empty chunk), so that a hot group spreads over as many workgroups as its
-// rows need.  Three launches:
+// Three launches, each over column strips of 64 (the tensors' strips numbered
+// one after the other) and, in the grid's second dimension, a stride over a
+// list of row chunks (every group's rows cut into chunks; an empty group is
+// one empty chunk), so that a hot group spreads over as many workgroups as its
+// rows need:
 //   1. zero the scales (and the caller's tile counters);
-//   2. per (64 columns, chunk): the chunk's column maxima, and the scale 2^e
-//      they call for merged into the scale by an atomic max on its bits.  e
-//      never falls as the maximum grows and 2^e (down to 2^-141 for the
-//      smallest bf16, a float subnormal) orders like its bit pattern, so the
-//      merge of the chunks' scales is the scale of the group's maximum, in any
-//      order.  A zero column leaves 0;
-//   3. per (64 columns, chunk): e read back from the scale (0 -> e = 0, and the
-//      chunk at the group's start stores 1), the chunk's codes through a
-//      256 x 64 tile in LDS, each thread writing 64 consecutive codes of one
-//      output row.
-// Columns of several tensors share each launch (strips numbered tensor by
-// tensor); the grid's second dimension strides over the chunks.
-constexpr int kGtChunk = 256;
-constexpr int kGtMaxGridY = 64;
+//   2. per (64 columns, chunk of kGtMaxRows rows): the chunk's column maxima,
+//      and the scale 2^e they call for merged into the group's scale by an
+//      atomic max on its bits: e never falls as the maximum grows, and 2^e
+//      (down to 2^-141 for the smallest bf16, a float subnormal) orders like
+//      its bit pattern, so the merge is the scale of the group's maximum, bit
+//      for bit, in any order (0 for a zero column);
+//   3. per (64 columns, chunk of kGtCodesRows rows): e read back from the
+//      scale (0: e = 0, and the group's first chunk stores the scale 1), and
+//      the codes.  Thread (cg, rg) holds 8 columns (c0 + 8 cg ..) of 16
+//      consecutive chunk rows (16 rg ..) and writes per column one 16-byte
+//      piece of that column's output row, so that eight threads of a wave
+//      write a whole 128-byte line, with no LDS transposition.  A thread's 16
+//      rows lie wholly inside or wholly past the group's padded rows.
+// (Holding a group's rows in registers from the maxima to the codes, one read
+// instead of two, needs chunks as long as the groups: at 1024 rows half of
+// each workgroup idled on this layer's ~512-row groups and the pass was
+// slower.)
+constexpr int kGtMaxRows = 256;    // rows per chunk of the maxima pass
+constexpr int kGtCodesRows = 512;  // rows per chunk of the codes pass
 
 struct GtChunk {
   int g;     // group, -1 past the last chunk
@@ -367,9 +376,11 @@ struct GtChunk {
   int ng;    // rows in the group
 };
 
-// Chunk c of the list (group 0's chunks, then group 1's, ...), found by wave 0
-// with scans over 64 groups at a time; the result goes through LDS to the
-// whole workgroup.
+// Chunk c of the list of CH-row chunks of the groups with more than MIN_N rows
+// (group order; an empty group, when counted, is one empty chunk), found by
+// wave 0 with scans over 64 groups at a time; the result reaches the whole
+// workgroup through LDS.
+template <int CH, int MIN_N>
 __device__ GtChunk gt_find_chunk(const int32_t* offsets, int E_l, int c, int t, GtChunk* s_c) {
   if (t < kWave) {
     int base_c = 0, base_p = 0;
@@ -377,7 +388,7 @@ __device__ GtChunk gt_find_chunk(const int32_t* offsets, int E_l, int c, int t, 
     for (int j0 = 0; j0 < E_l && !found; j0 += kWave) {
       const int j = j0 + t;
       const int n = j < E_l ? offsets[j + 1] - offsets[j] : 0;
-      const int nc = j < E_l ? max(1, (n + kGtChunk - 1) / kGtChunk) : 0;
+      const int nc = j < E_l && n > MIN_N ? max(1, (n + CH - 1) / CH) : 0;
       const int pd = (n + 63) & ~63;
       int ic = nc, ip = pd;
 #pragma unroll
@@ -391,8 +402,7 @@ __device__ GtChunk gt_find_chunk(const int32_t* offsets, int E_l, int c, int t, 
       const int ec = base_c + ic - nc;
       if (nc > 0 && c >= ec && c < ec + nc) {
         const int k = c - ec;
-        *s_c = GtChunk{j, k * kGtChunk, min(n - k * kGtChunk, kGtChunk), offsets[j],
-                       base_p + ip - pd, n};
+        *s_c = GtChunk{j, k * CH, min(n - k * CH, CH), offsets[j], base_p + ip - pd, n};
       }
       const int tc = __shfl(ic, kWave - 1, kWave), tp = __shfl(ip, kWave - 1, kWave);
       found = c < base_c + tc;
@@ -418,6 +428,39 @@ __device__ __forceinline__ const QuantGroupTensor& gt_tensor(const QuantGroupT& 
   return a.t[ti];
 }
 
+// 16 rows of 8 columns of a chunk (zeros past its n rows)
+__device__ __forceinline__ void gt_load16(const QuantGroupTensor& T, const GtChunk& k, int r0, int col,
+                                          uint4* v) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = r0 + i;
+    v[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (r < k.n) {
+      const long row = T.rows != nullptr ? T.rows[k.o0 + k.rbeg + r] : k.o0 + k.rbeg + r;
+      v[i] = *reinterpret_cast<const uint4*>(T.src + row * T.ld + col);
+    }
+  }
+}
+
+// the codes of column j (0..7) of 16 rows, as one 16-byte piece
+__device__ __forceinline__ uint4 gt_codes16(const uint4* v, int j, int e) {
+  float f[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t w = (&v[i].x)[j >> 1];
+    f[i] = __uint_as_float((j & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+  const uint2 lo = fp8_codes8(f, e), hi = fp8_codes8(f + 8, e);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+// e of a scale 2^e from its bits (normal or subnormal); 0 for a zero scale
+__device__ __forceinline__ int gt_scale_exponent(uint32_t b) {
+  if (b == 0u) return 0;
+  if (b >= 0x00800000u) return (int)(b >> 23) - 127;
+  return (31 - __clz(b)) - 149;
+}
+
 __global__ __launch_bounds__(256) void quantize_group_t_zero_kernel(const QuantGroupT a) {
   const QuantGroupTensor& T = a.t[blockIdx.y];
   const long n = (long)a.E_l * T.C;
@@ -434,11 +477,11 @@ __global__ __launch_bounds__(256) void quantize_group_t_max_kernel(const QuantGr
   int c0;
   const QuantGroupTensor& T = gt_tensor(a, c0);
   for (int c = blockIdx.y;; c += gridDim.y) {
-    const GtChunk k = gt_find_chunk(a.offsets, a.E_l, c, t, &s_c);
+    const GtChunk k = gt_find_chunk<kGtMaxRows, -1>(a.offsets, a.E_l, c, t, &s_c);
     if (k.g < 0) break;
-    uint4 v[kGtChunk / 32];
+    uint4 v[kGtMaxRows / 32];
 #pragma unroll
-    for (int i = 0; i < kGtChunk / 32; ++i) {
+    for (int i = 0; i < kGtMaxRows / 32; ++i) {
       const int r = k.rbeg + r0 + 32 * i;
       v[i] = make_uint4(0u, 0u, 0u, 0u);
       if (r0 + 32 * i < k.n) {
@@ -446,16 +489,23 @@ __global__ __launch_bounds__(256) void quantize_group_t_max_kernel(const QuantGr
         v[i] = *reinterpret_cast<const uint4*>(T.src + row * T.ld + c0 + 8 * cc);
       }
     }
-    float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // |x| of a bf16 orders like its bits with the sign cleared: the maxima on
+    // the packed words (column 2w in the low half of word w, 2w + 1 in the high;
+    // a NaN, above inf in these bits, wins)
+    uint32_t m[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < kGtChunk / 32; ++i) {
-      float f[8];
-      unpack8(v[i], f);
+    for (int i = 0; i < kGtMaxRows / 32; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) m[j] = fmaxf(m[j], fabsf(f[j]));
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x = (&v[i].x)[w];
+        m[2 * w] = max(m[2 * w], x & 0x7fffu);
+        m[2 * w + 1] = max(m[2 * w + 1], x & 0x7fff0000u);
+      }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      s_max[r0][8 * cc + 2 * w] = __uint_as_float(m[2 * w] << 16);
+      s_max[r0][8 * cc + 2 * w + 1] = __uint_as_float(m[2 * w + 1]);
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) s_max[r0][8 * cc + j] = m[j];
     __syncthreads();
     if (t < 64) {
       float mx = 0.f;
@@ -468,62 +518,39 @@ __global__ __launch_bounds__(256) void quantize_group_t_max_kernel(const QuantGr
   }
 }
 
-// e of a scale 2^e from its bits (normal or subnormal); 0 for a zero scale
-__device__ __forceinline__ int gt_scale_exponent(uint32_t b) {
-  if (b == 0u) return 0;
-  if (b >= 0x00800000u) return (int)(b >> 23) - 127;
-  return (31 - __clz(b)) - 149;
-}
-
 __global__ __launch_bounds__(256) void quantize_group_t_codes_kernel(const QuantGroupT a) {
-  __shared__ __align__(16) bf16_t s_tile[kGtChunk][64];
-  __shared__ int s_e[64];
   __shared__ GtChunk s_c;
-  const int t = threadIdx.x, cc = t & 7, r0 = t >> 3;
-  const int oc = t & 63, og = t >> 6;  // output row c0 + oc, chunk rows 64 og .. 64 og + 63
+  const int t = threadIdx.x, cg = t & 7, rg = t >> 3, r0 = 16 * rg;
   int c0;
   const QuantGroupTensor& T = gt_tensor(a, c0);
   for (int c = blockIdx.y;; c += gridDim.y) {
-    const GtChunk k = gt_find_chunk(a.offsets, a.E_l, c, t, &s_c);
+    const GtChunk k = gt_find_chunk<kGtCodesRows, -1>(a.offsets, a.E_l, c, t, &s_c);
     if (k.g < 0) break;
-    if (t < 64) {
-      float* sp = T.scale + (size_t)k.g * T.C + c0 + t;
-      const uint32_t b = __float_as_uint(*sp);
-      s_e[t] = gt_scale_exponent(b);
-      if (b == 0u && k.rbeg == 0) *sp = 1.f;
-    }
     if (blockIdx.x == 0 && k.rbeg == 0 && t == 0) {
       a.poff[k.g] = k.poff;
       if (k.g == a.E_l - 1) a.poff[a.E_l] = k.poff + ((k.ng + 63) & ~63);
     }
-    const int rows64 = (k.n + 63) & ~63;  // the chunk's rows with the group's zero padding
-    uint4 v[kGtChunk / 32];
+    float* sp = T.scale + (size_t)k.g * T.C + c0 + 8 * cg;
+    if (k.n == 0) {  // an empty group: every column is a zero column
+      if (rg == 0)
 #pragma unroll
-    for (int i = 0; i < kGtChunk / 32; ++i) {
-      const int r = r0 + 32 * i;
-      v[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (r < k.n) {
-        const long row = T.rows != nullptr ? T.rows[k.o0 + k.rbeg + r] : k.o0 + k.rbeg + r;
-        v[i] = *reinterpret_cast<const uint4*>(T.src + row * T.ld + c0 + 8 * cc);
-      }
+        for (int j = 0; j < 8; ++j) sp[j] = 1.f;
+      continue;
     }
+    if (r0 >= ((k.n + 63) & ~63)) continue;
+    uint4 v[16];
+    gt_load16(T, k, r0, c0 + 8 * cg, v);
+    int e[8];
 #pragma unroll
-    for (int i = 0; i < kGtChunk / 32; ++i)
-      if (r0 + 32 * i < rows64) *reinterpret_cast<uint4*>(&s_tile[r0 + 32 * i][8 * cc]) = v[i];
-    __syncthreads();
-    if (64 * og < rows64) {
-      const int e = s_e[oc];
-      uint8_t* qrow = T.q + (size_t)(c0 + oc) * a.Kp + k.poff + k.rbeg + 64 * og;
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        float f[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) f[i] = bf2f(s_tile[64 * og + 16 * h + i][oc]);
-        const uint2 lo = fp8_codes8(f, e), hi = fp8_codes8(f + 8, e);
-        *reinterpret_cast<uint4*>(qrow + 16 * h) = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      }
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t b = __float_as_uint(sp[j]);
+      e[j] = gt_scale_exponent(b);
+      if (b == 0u && k.rbeg == 0 && rg == 0) sp[j] = 1.f;  // a zero column
     }
-    __syncthreads();
+    uint8_t* q = T.q + (size_t)(c0 + 8 * cg) * a.Kp + k.poff + k.rbeg + r0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<uint4*>(q + (size_t)j * a.Kp) = gt_codes16(v, j, e[j]);
   }
 }
 
@@ -537,12 +564,16 @@ hipError_t launch_quantize_group_t_fp8(const QuantGroupT& q, hipStream_t s) {
   quantize_group_t_zero_kernel<<<dim3(zero_x, q.nt), 256, 0, s>>>(q);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // at most ceil(rows / kGtChunk) + E_l chunks
-  const long chunks = ((long)q.max_rows + kGtChunk - 1) / kGtChunk + q.E_l;
-  const dim3 grid(strips, (unsigned)std::min<long>(chunks, kGtMaxGridY));
-  quantize_group_t_max_kernel<<<grid, 256, 0, s>>>(q);
+  // the grids' second dimension: at most the chunk list's length (one chunk
+  // per group plus one per ch rows), at most 64 (the workgroups stride over
+  // the list)
+  const auto grid = [&](int ch) {
+    const long chunks = ((long)q.max_rows + ch - 1) / ch + q.E_l;
+    return dim3(strips, (unsigned)std::min<long>(chunks, 64));
+  };
+  quantize_group_t_max_kernel<<<grid(kGtMaxRows), 256, 0, s>>>(q);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  quantize_group_t_codes_kernel<<<grid, 256, 0, s>>>(q);
+  quantize_group_t_codes_kernel<<<grid(kGtCodesRows), 256, 0, s>>>(q);
   return hipGetLastError();
 }
 
