@@ -15,8 +15,9 @@ backward() returns.
 With fp8=True the expert FFN runs the library's FP8 recipe (E4M3 codes with
 power-of-two scales): tokens are quantized per row before the permute (which
 then moves code rows); every forward quantizes the weights per output channel
-and, for training, per input channel as well (both layouts in one pass pair;
-the backward uses these codes, so it must be given the forward's weights); the
+and, for training, per input channel as well (both layouts in one pass pair,
+on the second stream beside routing and permute; the backward uses these
+codes, so it must be given the forward's weights); the
 backward quantizes the rows of dy_perm, and the weight gradients quantize
 their operands per (expert, column).  Routing, combine and the router backward
 stay as in the bf16 layer.
@@ -108,17 +109,23 @@ class MoELayer:
         # stream; the backward's concurrent calls get their own
         self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
         self.ws_bytes = self.ws.numel()
+        ws = lambda op: torch.empty(max(workspace_bytes(op, T, H, I, E, k, e_lo, e_hi, self.dt), 256),
+                                    dtype=torch.uint8, device=dev)
         if train:
-            ws = lambda op: torch.empty(max(workspace_bytes(op, T, H, I, E, k, e_lo, e_hi, self.dt), 256),
-                                        dtype=torch.uint8, device=dev)
             self.ws_rb = ws(MOE_OP_ROUTE_BWD)
             self.ws_w8 = ws(MOE_OP_FFN_WGRAD_FP8) if fp8 else None
+        # FP8: the weight quantization runs on the side stream beside routing
+        # and permute, with a workspace of its own
+        self.ws_qw = ws(MOE_OP_QUANTIZE_W_FP8) if fp8 else None
+        if train or fp8:
             self.side = torch.cuda.Stream(device=dev) if dev.type == "cuda" else None
 
     def forward(self, x, w_router, w_gate, w_up, w_down, bias=None, save_logits=True):
         b, T, H, I, E, k = self.buf, self.T, self.H, self.I, self.E, self.k
         s = _stream()
         ws, wsb = _p(self.ws), self.ws_bytes
+        if self.fp8:
+            self._quantize_weights_fp8(w_gate, w_up, w_down)
         _check(lib.moe_route(_p(x), _p(w_router), _p(bias), T, H, E, k, self.dt,
                              _p(b["logits"]) if save_logits else None, _p(b["topk_idx"]),
                              _p(b["topk_w"]), ws, wsb, s), "moe_route")
@@ -140,25 +147,34 @@ class MoELayer:
         _check(lib.moe_quantize_fp8(_p(src), rows, cols, self.dt, _p(nrows), _p(q), _p(scale), s),
                "moe_quantize_fp8")
 
+    def _quantize_weights_fp8(self, w_gate, w_up, w_down):
+        """Both code layouts of the expert weights (rows for the forward products
+        and, when training, the input channels for the data gradients, from the
+        same reads) on the side stream: they need only the weights, so they run
+        beside routing and permute; the FP8 FFN waits for them."""
+        b, H, I, E_l, tr = self.buf, self.H, self.I, self.E_l, self.train
+        self._fp8_weights = (w_gate.data_ptr(), w_up.data_ptr(), w_down.data_ptr())
+        self.side.wait_stream(torch.cuda.current_stream())
+        side = ctypes.c_void_p(self.side.cuda_stream)
+        ws, wsb = _p(self.ws_qw), self.ws_qw.numel()
+        _check(lib.moe_quantize_fp8_w(_p(w_gate), _p(w_up), E_l, I, H, self.dt, _p(b["wg_q"]),
+                                      _p(b["wg_s"]), _p(b["wu_q"]), _p(b["wu_s"]),
+                                      _p(b["wgut_q"]) if tr else None, _p(b["wgut_s"]) if tr else None,
+                                      ws, wsb, side), "moe_quantize_fp8_w")
+        _check(lib.moe_quantize_fp8_w(_p(w_down), None, E_l, H, I, self.dt, _p(b["wd_q"]), _p(b["wd_s"]),
+                                      None, None, _p(b["wdt_q"]) if tr else None,
+                                      _p(b["wdt_s"]) if tr else None, ws, wsb, side), "moe_quantize_fp8_w")
+
     def _forward_ffn_fp8(self, x, w_gate, w_up, w_down, ws, wsb, s):
-        """Token rows quantized, code rows permuted, weights quantized per output
-        channel, then the FP8 grouped FFN (h, g and u kept in bf16)."""
+        """Token rows quantized, code rows permuted, then (once the side
+        stream's weight codes are there) the FP8 grouped FFN (h, g and u kept in
+        bf16)."""
         b, T, H, I, E, k, E_l = self.buf, self.T, self.H, self.I, self.E, self.k, self.E_l
         self._quantize_rows(x, T, H, b["x_q"], b["x_scale"], s)
         _check(lib.moe_permute(_p(b["x_q"]), _p(b["topk_idx"]), T, H, E, k, self.e_lo, self.e_hi,
                                MOE_FP8, _p(b["counts"]), _p(b["offsets"]), _p(b["dest_row"]),
                                _p(b["src_row"]), _p(b["xq_perm"]), ws, wsb, s), "moe_permute")
-        # weights: rows for these products and, when training, the input
-        # channels for the data gradients, from the same reads
-        tr = self.train
-        self._fp8_weights = (w_gate.data_ptr(), w_up.data_ptr(), w_down.data_ptr())
-        _check(lib.moe_quantize_fp8_w(_p(w_gate), _p(w_up), E_l, I, H, self.dt, _p(b["wg_q"]),
-                                      _p(b["wg_s"]), _p(b["wu_q"]), _p(b["wu_s"]),
-                                      _p(b["wgut_q"]) if tr else None, _p(b["wgut_s"]) if tr else None,
-                                      ws, wsb, s), "moe_quantize_fp8_w")
-        _check(lib.moe_quantize_fp8_w(_p(w_down), None, E_l, H, I, self.dt, _p(b["wd_q"]), _p(b["wd_s"]),
-                                      None, None, _p(b["wdt_q"]) if tr else None,
-                                      _p(b["wdt_s"]) if tr else None, ws, wsb, s), "moe_quantize_fp8_w")
+        torch.cuda.current_stream().wait_stream(self.side)
         _check(lib.moe_grouped_ffn_fwd_fp8(_p(b["xq_perm"]), _p(b["x_scale"]), _p(b["src_row"]),
                                            _p(b["offsets"]), E_l, self.R_cap, H, I, _p(b["wg_q"]),
                                            _p(b["wg_s"]), _p(b["wu_q"]), _p(b["wu_s"]), _p(b["wd_q"]),
