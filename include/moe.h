@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 8
+#define MOE_ABI_VERSION 9
 
 typedef enum {
   MOE_OK = 0,
@@ -293,6 +293,31 @@ int moe_grouped_ffn_wgrad_fp8(const void* x, const int32_t* src_row, const void*
                               int E_l, int R_cap, int H, int I, float* dw_gate, float* dw_up,
                               float* dw_down, int accumulate, void* ws, size_t ws_bytes,
                               void* stream);
+
+/* moe_grouped_ffn_wgrad_fp8 in two halves, so that a caller can start the
+ * part that does not need dgu (the output of the SiLU' pass of the data
+ * gradients) as soon as x, h_perm and dy_perm exist, e.g. on a second stream
+ * beside the data gradients.  Same FP8 reading and arguments as
+ * moe_grouped_ffn_wgrad_fp8; begin then end on one workspace compute exactly
+ * (bit for bit) what that call computes.
+ *   begin: quantizes the columns of x (through src_row), dy_perm and h_perm
+ *          per expert into ws, builds the K-chunk plans and writes dW_down
+ *          (overwrite, or added to with accumulate != 0).  An expert whose
+ *          rows are split into K chunks gets its chunks after the first as
+ *          fp32 partials in ws: dw_down is complete only after end.
+ *   end:   quantizes the columns of dgu, writes dW_gate and dW_up, then adds
+ *          the partials of both products' split experts in chunk order.
+ * end must run after begin (same stream, or ordered after it by an event),
+ * with the same ws, offsets, E_l, R_cap, H, I and accumulate, and dw_down the
+ * pointer begin wrote; nothing else may use ws in between.  Errors as
+ * moe_grouped_ffn_wgrad_fp8. */
+int moe_grouped_ffn_wgrad_fp8_begin(const void* x, const int32_t* src_row, const void* h_perm,
+                                    const void* dy_perm, const int32_t* offsets, int E_l,
+                                    int R_cap, int H, int I, float* dw_down, int accumulate,
+                                    void* ws, size_t ws_bytes, void* stream);
+int moe_grouped_ffn_wgrad_fp8_end(const void* dgu, const int32_t* offsets, int E_l, int R_cap,
+                                  int H, int I, float* dw_gate, float* dw_up, float* dw_down,
+                                  int accumulate, void* ws, size_t ws_bytes, void* stream);
 
 /* Weighted unpermute ("combine"): for every token, in slot order j = 0..k-1,
  *   y[t] = sum_{j: dest_row[t*k+j] >= 0} topk_w[t,j] * y_perm[dest_row[t*k+j]]  (+ addend[t])

@@ -12,7 +12,8 @@ moe_combine, moe_combine_bwd, moe_grouped_ffn_bwd, moe_route_bwd, and the FP8
 forward: moe_quantize_fp8, moe_grouped_ffn_fwd_fp8; data gradients:
 moe_quantize_fp8_t, moe_grouped_ffn_dgrad_fp8; both weight layouts at once:
 moe_quantize_fp8_w; weight gradients:
-moe_quantize_fp8_group_t, moe_grouped_ffn_wgrad_fp8) and return
+moe_quantize_fp8_group_t, moe_grouped_ffn_wgrad_fp8, and its two halves
+moe_grouped_ffn_wgrad_fp8_begin / _end) and return
 freshly allocated torch tensors; each also accepts preallocated outputs via
 ``out=`` dictionaries so that steady-state loops allocate nothing.
 """
@@ -31,7 +32,7 @@ MOE_F32, MOE_BF16, MOE_FP8 = 0, 1, 2
 (MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD, MOE_OP_ROUTE_BWD,
  MOE_OP_COMBINE_DX, MOE_OP_FFN_FWD_FP8, MOE_OP_FFN_DGRAD_FP8, MOE_OP_FFN_WGRAD_FP8,
  MOE_OP_QUANTIZE_W_FP8) = range(10)
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 
 class MoEError(RuntimeError):
@@ -72,6 +73,8 @@ def _load():
         "moe_quantize_fp8_w": ([P, P, I32, I32, I32, I32, P, P, P, P, P, P, P, SZ, P], I32),
         "moe_grouped_ffn_wgrad_fp8": ([P, P, P, P, P, P, I32, I32, I32, I32, P, P, P, I32, P, SZ, P],
                                       I32),
+        "moe_grouped_ffn_wgrad_fp8_begin": ([P, P, P, P, P, I32, I32, I32, I32, P, I32, P, SZ, P], I32),
+        "moe_grouped_ffn_wgrad_fp8_end": ([P, P, I32, I32, I32, I32, P, P, P, I32, P, SZ, P], I32),
         "moe_profile_kernel": ([I32, ctypes.POINTER(P), ctypes.POINTER(P), I32], I32),
         "moe_profile_recorded": ([], I32),
     }
@@ -487,6 +490,50 @@ def moe_grouped_ffn_wgrad_fp8(x: torch.Tensor, src_row: Optional[torch.Tensor], 
                                          1 if accumulate else 0, _ptr(ws), _nbytes(ws), _stream()),
            "moe_grouped_ffn_wgrad_fp8")
     return o
+
+
+def _wgrad_fp8_ws(R_cap, H, I, E_l, dev, ws):
+    nb = lib.moe_workspace_bytes(MOE_OP_FFN_WGRAD_FP8, max(R_cap, 0), H, I, max(E_l, 1), 1, 0, E_l,
+                                 MOE_BF16)
+    if nb < 0:
+        _check(int(nb), "moe_workspace_bytes")
+    return _ws(int(nb), dev, ws)
+
+
+def moe_grouped_ffn_wgrad_fp8_begin(x: torch.Tensor, src_row: Optional[torch.Tensor],
+                                    h_perm: torch.Tensor, dy_perm: torch.Tensor,
+                                    offsets: torch.Tensor, E_l: int, ws: torch.Tensor,
+                                    dw_down: torch.Tensor, accumulate: bool = False, stream=None):
+    """First half of moe_grouped_ffn_wgrad_fp8: the columns of x (through src_row),
+    dy_perm and h_perm quantized into ws, the K-chunk plans, dW_down (complete only
+    after moe_grouped_ffn_wgrad_fp8_end on the same ws).  stream: a torch stream
+    (default: the current one)."""
+    R_cap, H = dy_perm.shape
+    I = h_perm.shape[1]
+    ws = _wgrad_fp8_ws(R_cap, H, I, E_l, dy_perm.device, ws)
+    st = (stream or torch.cuda.current_stream()).cuda_stream
+    _check(lib.moe_grouped_ffn_wgrad_fp8_begin(_ptr(x), _ptr(src_row), _ptr(h_perm), _ptr(dy_perm),
+                                               _ptr(offsets), E_l, R_cap, H, I, _ptr(dw_down),
+                                               1 if accumulate else 0, _ptr(ws), _nbytes(ws),
+                                               ctypes.c_void_p(st)),
+           "moe_grouped_ffn_wgrad_fp8_begin")
+
+
+def moe_grouped_ffn_wgrad_fp8_end(dgu: torch.Tensor, offsets: torch.Tensor, E_l: int, H: int,
+                                  ws: torch.Tensor, out: Dict[str, torch.Tensor],
+                                  accumulate: bool = False, stream=None):
+    """Second half: the columns of dgu [R_cap, 2I] quantized, dW_gate and dW_up, and
+    the split experts' partial sums of both products (out: dw_gate, dw_up, and the
+    dw_down that begin wrote)."""
+    R_cap, I2 = dgu.shape
+    I = I2 // 2
+    ws = _wgrad_fp8_ws(R_cap, H, I, E_l, dgu.device, ws)
+    st = (stream or torch.cuda.current_stream()).cuda_stream
+    _check(lib.moe_grouped_ffn_wgrad_fp8_end(_ptr(dgu), _ptr(offsets), E_l, R_cap, H, I,
+                                             _ptr(out["dw_gate"]), _ptr(out["dw_up"]),
+                                             _ptr(out["dw_down"]), 1 if accumulate else 0, _ptr(ws),
+                                             _nbytes(ws), ctypes.c_void_p(st)),
+           "moe_grouped_ffn_wgrad_fp8_end")
 
 
 def moe_quantize_fp8_w(w0: torch.Tensor, w1: Optional[torch.Tensor] = None, transposed: bool = True,

@@ -521,12 +521,9 @@ int moe_quantize_fp8_group_t(const void* src, const int32_t* src_row, int C,
   return hip_status(launch_quantize_group_t_fp8(a, begin_launch(stream)), fn);
 }
 
-int moe_grouped_ffn_wgrad_fp8(const void* x, const int32_t* src_row, const void* dgu,
-                              const void* h_perm, const void* dy_perm, const int32_t* offsets,
-                              int E_l, int R_cap, int H, int I, float* dw_gate, float* dw_up,
-                              float* dw_down, int accumulate, void* ws, size_t ws_bytes,
-                              void* stream) {
-  const char* fn = "moe_grouped_ffn_wgrad_fp8";
+// the shape, workspace and pointer checks of the FP8 weight gradients
+static int check_wgrad_fp8(int E_l, int R_cap, int H, int I, const int32_t* offsets,
+                           const void* ws, size_t ws_bytes, const char* fn) {
   if (int rc = check_ffn_shape(E_l, R_cap, H, I, MOE_FP8, fn)) return rc;
   if (H % 128 != 0 || I % 128 != 0)
     return fail(MOE_EUNSUPPORTED, "%s: needs H %% 128 == 0 and I %% 128 == 0 (H=%d, I=%d)", fn, H, I);
@@ -534,6 +531,50 @@ int moe_grouped_ffn_wgrad_fp8(const void* x, const int32_t* src_row, const void*
   const int64_t pitch = (((int64_t)R_cap + 63) & ~(int64_t)63) + 64 * (int64_t)E_l;
   if (int rc = check_range(pitch * std::max(2 * I, H), "a transposed code matrix", fn)) return rc;
   if (int rc = check_ptr(offsets, "offsets", fn)) return rc;
+  return check_ws(ws, ws_bytes, ffn_wgrad_fp8_ws_bytes(R_cap, E_l, H, I), fn);
+}
+
+int moe_grouped_ffn_wgrad_fp8_begin(const void* x, const int32_t* src_row, const void* h_perm,
+                                    const void* dy_perm, const int32_t* offsets, int E_l,
+                                    int R_cap, int H, int I, float* dw_down, int accumulate,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "moe_grouped_ffn_wgrad_fp8_begin";
+  if (int rc = check_wgrad_fp8(E_l, R_cap, H, I, offsets, ws, ws_bytes, fn)) return rc;
+  if (int rc = check_ptr(dw_down, "dw_down", fn, true)) return rc;
+  if (R_cap > 0) {
+    if (int rc = check_ptr(x, "x", fn, true)) return rc;
+    if (int rc = check_ptr(h_perm, "h_perm", fn, true)) return rc;
+    if (int rc = check_ptr(dy_perm, "dy_perm", fn, true)) return rc;
+  }
+  return hip_status(launch_ffn_wgrad_fp8_begin((const bf16_t*)x, src_row, (const bf16_t*)h_perm,
+                                               (const bf16_t*)dy_perm, offsets, E_l, R_cap, H, I,
+                                               dw_down, accumulate != 0, ws, begin_launch(stream)),
+                    fn);
+}
+
+int moe_grouped_ffn_wgrad_fp8_end(const void* dgu, const int32_t* offsets, int E_l, int R_cap,
+                                  int H, int I, float* dw_gate, float* dw_up, float* dw_down,
+                                  int accumulate, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "moe_grouped_ffn_wgrad_fp8_end";
+  if (int rc = check_wgrad_fp8(E_l, R_cap, H, I, offsets, ws, ws_bytes, fn)) return rc;
+  if (int rc = check_ptr(dw_gate, "dw_gate", fn, true)) return rc;
+  if (int rc = check_ptr(dw_up, "dw_up", fn, true)) return rc;
+  if (int rc = check_ptr(dw_down, "dw_down", fn, true)) return rc;
+  if (R_cap > 0)
+    if (int rc = check_ptr(dgu, "dgu", fn, true)) return rc;
+  return hip_status(launch_ffn_wgrad_fp8_end((const bf16_t*)dgu, offsets, E_l, R_cap, H, I,
+                                             dw_gate, dw_up, dw_down, accumulate != 0, ws,
+                                             begin_launch(stream)),
+                    fn);
+}
+
+int moe_grouped_ffn_wgrad_fp8(const void* x, const int32_t* src_row, const void* dgu,
+                              const void* h_perm, const void* dy_perm, const int32_t* offsets,
+                              int E_l, int R_cap, int H, int I, float* dw_gate, float* dw_up,
+                              float* dw_down, int accumulate, void* ws, size_t ws_bytes,
+                              void* stream) {
+  const char* fn = "moe_grouped_ffn_wgrad_fp8";
+  if (int rc = check_wgrad_fp8(E_l, R_cap, H, I, offsets, ws, ws_bytes, fn)) return rc;
   if (int rc = check_ptr(dw_gate, "dw_gate", fn, true)) return rc;
   if (int rc = check_ptr(dw_up, "dw_up", fn, true)) return rc;
   if (int rc = check_ptr(dw_down, "dw_down", fn, true)) return rc;
@@ -543,7 +584,6 @@ int moe_grouped_ffn_wgrad_fp8(const void* x, const int32_t* src_row, const void*
     if (int rc = check_ptr(h_perm, "h_perm", fn, true)) return rc;
     if (int rc = check_ptr(dy_perm, "dy_perm", fn, true)) return rc;
   }
-  if (int rc = check_ws(ws, ws_bytes, ffn_wgrad_fp8_ws_bytes(R_cap, E_l, H, I), fn)) return rc;
   return hip_status(launch_ffn_wgrad_fp8((const bf16_t*)x, src_row, (const bf16_t*)dgu,
                                          (const bf16_t*)h_perm, (const bf16_t*)dy_perm, offsets,
                                          E_l, R_cap, H, I, dw_gate, dw_up, dw_down,

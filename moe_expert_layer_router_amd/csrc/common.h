@@ -261,6 +261,13 @@ hipError_t launch_ffn_wgrad_fp8(const bf16_t* x, const int32_t* src_row, const b
                                 const int32_t* offsets, int E_l, int R_cap, int H, int I,
                                 float* dw_gate, float* dw_up, float* dw_down, bool accumulate,
                                 void* ws, hipStream_t s);
+hipError_t launch_ffn_wgrad_fp8_begin(const bf16_t* x, const int32_t* src_row,
+                                      const bf16_t* h_perm, const bf16_t* dy_perm,
+                                      const int32_t* offsets, int E_l, int R_cap, int H, int I,
+                                      float* dw_down, bool accumulate, void* ws, hipStream_t s);
+hipError_t launch_ffn_wgrad_fp8_end(const bf16_t* dgu, const int32_t* offsets, int E_l, int R_cap,
+                                    int H, int I, float* dw_gate, float* dw_up, float* dw_down,
+                                    bool accumulate, void* ws, hipStream_t s);
 hipError_t order_after(hipStream_t s, hipStream_t waiter);
 hipError_t launch_ffn_bwd_bf16(const bf16_t* dy_perm, const bf16_t* x_perm, const bf16_t* gu,
                                const bf16_t* h_perm, const int32_t* offsets, int E_l, int R_cap,

@@ -2224,66 +2224,129 @@ size_t ffn_wgrad_fp8_ws_bytes(int R_cap, int E_l, int H, int I) {
          align256((size_t)(E_l + 1) * 4) + 256 + ffn_wgrad_split_bytes(E_l, H, I);
 }
 
-hipError_t launch_ffn_wgrad_fp8(const bf16_t* x, const int32_t* src_row, const bf16_t* dgu,
-                                const bf16_t* h_perm, const bf16_t* dy_perm,
-                                const int32_t* offsets, int E_l, int R_cap, int H, int I,
-                                float* dw_gate, float* dw_up, float* dw_down, bool accumulate,
-                                void* ws, hipStream_t s) {
-  const int Kp = wgrad_fp8_pitch(R_cap, E_l);
+// The FP8 weight-gradient workspace: the four operands' transposed codes and
+// per-(expert, column) scales, the padded offsets, the two products' tile
+// counters, the K-chunk plans and the partial slots.
+struct Wgrad8Ws {
+  int Kp;
+  uint8_t *q_gu, *q_x, *q_dy, *q_h;
+  float *s_gu, *s_x, *s_dy, *s_h;
+  int32_t* poff;
+  int32_t* ctrs;
+  WgradSplitLayout SL;
+  WgradPlan plan;
+  float* part[2];
+};
+
+static Wgrad8Ws wgrad8_ws(void* ws, int R_cap, int E_l, int H, int I) {
+  Wgrad8Ws L{};
+  L.Kp = wgrad_fp8_pitch(R_cap, E_l);
   char* w = (char*)ws;
-  uint8_t* q_gu = (uint8_t*)w;
+  L.q_gu = (uint8_t*)w;
   w += wgrad_fp8_codes_bytes(R_cap, E_l, 2 * I);
-  uint8_t* q_x = (uint8_t*)w;
+  L.q_x = (uint8_t*)w;
   w += wgrad_fp8_codes_bytes(R_cap, E_l, H);
-  uint8_t* q_dy = (uint8_t*)w;
+  L.q_dy = (uint8_t*)w;
   w += wgrad_fp8_codes_bytes(R_cap, E_l, H);
-  uint8_t* q_h = (uint8_t*)w;
+  L.q_h = (uint8_t*)w;
   w += wgrad_fp8_codes_bytes(R_cap, E_l, I);
-  float* s_gu = (float*)w;
-  float* s_x = s_gu + (size_t)E_l * 2 * I;
-  float* s_dy = s_x + (size_t)E_l * H;
-  float* s_h = s_dy + (size_t)E_l * H;
+  L.s_gu = (float*)w;
+  L.s_x = L.s_gu + (size_t)E_l * 2 * I;
+  L.s_dy = L.s_x + (size_t)E_l * H;
+  L.s_h = L.s_dy + (size_t)E_l * H;
   w += align256((size_t)E_l * (3 * I + 2 * H) * 4);
-  int32_t* poff = (int32_t*)w;
+  L.poff = (int32_t*)w;
   w += align256((size_t)(E_l + 1) * 4);
-  int32_t* ctrs = (int32_t*)w;
+  L.ctrs = (int32_t*)w;
   w += 256;
   // the K-chunk plans over the padded code columns and the partial slots
-  const WgradSplitLayout SL = wgrad_split_layout(E_l, H, I);
-  WgradPlan plan{};
-  float* part[2];
+  L.SL = wgrad_split_layout(E_l, H, I);
   for (int q = 0; q < 2; ++q) {
-    plan.t[q] = (int32_t*)(w + SL.plan_off[q]);
-    plan.tiles[q] = SL.tiles[q];
-    plan.slots[q] = SL.slots[q];
-    part[q] = (float*)(w + SL.part_off[q]);
+    L.plan.t[q] = (int32_t*)(w + L.SL.plan_off[q]);
+    L.plan.tiles[q] = L.SL.tiles[q];
+    L.plan.slots[q] = L.SL.slots[q];
+    L.part[q] = (float*)(w + L.SL.part_off[q]);
   }
+  return L;
+}
 
+// First half: the columns of x (through src_row), dy_perm and h quantized,
+// both products' tile counters zeroed, the K-chunk plans built, then dW_down
+// (its split experts' partial sums are added by the second half).
+hipError_t launch_ffn_wgrad_fp8_begin(const bf16_t* x, const int32_t* src_row,
+                                      const bf16_t* h_perm, const bf16_t* dy_perm,
+                                      const int32_t* offsets, int E_l, int R_cap, int H, int I,
+                                      float* dw_down, bool accumulate, void* ws, hipStream_t s) {
+  const Wgrad8Ws L = wgrad8_ws(ws, R_cap, E_l, H, I);
   QuantGroupT q{};
-  q.t[0] = {dgu, nullptr, 2L * I, 2 * I, q_gu, s_gu};
-  q.t[1] = {x, src_row, (long)H, H, q_x, s_x};
-  q.t[2] = {dy_perm, nullptr, (long)H, H, q_dy, s_dy};
-  q.t[3] = {h_perm, nullptr, (long)I, I, q_h, s_h};
-  q.nt = 4;
+  q.t[0] = {x, src_row, (long)H, H, L.q_x, L.s_x};
+  q.t[1] = {dy_perm, nullptr, (long)H, H, L.q_dy, L.s_dy};
+  q.t[2] = {h_perm, nullptr, (long)I, I, L.q_h, L.s_h};
+  q.nt = 3;
   q.offsets = offsets;
   q.E_l = E_l;
   q.max_rows = R_cap;
-  q.Kp = Kp;
-  q.poff = poff;
-  q.ctrs = ctrs;
+  q.Kp = L.Kp;
+  q.poff = L.poff;
+  q.ctrs = L.ctrs;
   q.nctrs = 2;
   hipError_t err = launch_quantize_group_t_fp8(q, s);
   if (err != hipSuccess) return err;
-  wgrad_plan_kernel<<<1, kMaxE, 0, s>>>(poff, E_l, plan);
+  wgrad_plan_kernel<<<1, kMaxE, 0, s>>>(L.poff, E_l, L.plan);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   // E4M3 rows of Kp codes run through the ring as rows of Kp / 2 bf16 slots.
+  GemmArgs d{};
+  d.a = (const bf16_t*)L.q_dy;
+  d.lda = L.Kp / 2;
+  d.b0 = (const bf16_t*)L.q_h;
+  d.ldb = L.Kp / 2;
+  d.offsets = L.poff;
+  d.groups = E_l;
+  d.M = H;
+  d.N = I;
+  d.n_mtiles = (H + kBmWgrad - 1) / kBmWgrad;
+  d.n_ntiles = (I + BN - 1) / BN;
+  d.f0 = dw_down;
+  d.m_split = H;
+  d.ldc = I;
+  d.f_group_stride = (long)H * I;
+  d.accumulate = accumulate ? 1 : 0;
+  d.sa = L.s_dy;
+  d.sa_group_stride = H;
+  d.sb0 = L.s_h;
+  d.sb_group_stride = I;
+  d.tile_ctr = L.ctrs + 1;
+  d.kplan = L.plan.t[1];
+  d.fpart = L.part[1];
+  return launch_gemm<K_WGRAD8, kBmWgrad, true>(d, (E_l + L.SL.slots[1]) * d.n_mtiles * d.n_ntiles,
+                                               MOE_KERNEL_FFN_DOWN_WGRAD, s);
+}
+
+// Second half, after the first on the same workspace: the columns of
+// [dg | du] quantized, [dW_gate; dW_up], then the ordered sums of both
+// products' split experts.
+hipError_t launch_ffn_wgrad_fp8_end(const bf16_t* dgu, const int32_t* offsets, int E_l, int R_cap,
+                                    int H, int I, float* dw_gate, float* dw_up, float* dw_down,
+                                    bool accumulate, void* ws, hipStream_t s) {
+  const Wgrad8Ws L = wgrad8_ws(ws, R_cap, E_l, H, I);
+  QuantGroupT q{};
+  q.t[0] = {dgu, nullptr, 2L * I, 2 * I, L.q_gu, L.s_gu};
+  q.nt = 1;
+  q.offsets = offsets;
+  q.E_l = E_l;
+  q.max_rows = R_cap;
+  q.Kp = L.Kp;
+  q.poff = L.poff;  // rewritten with the values the first half wrote
+  hipError_t err = launch_quantize_group_t_fp8(q, s);
+  if (err != hipSuccess) return err;
+
   GemmArgs g{};
-  g.a = (const bf16_t*)q_gu;
-  g.lda = Kp / 2;
-  g.b0 = (const bf16_t*)q_x;
-  g.ldb = Kp / 2;
-  g.offsets = poff;
+  g.a = (const bf16_t*)L.q_gu;
+  g.lda = L.Kp / 2;
+  g.b0 = (const bf16_t*)L.q_x;
+  g.ldb = L.Kp / 2;
+  g.offsets = L.poff;
   g.groups = E_l;
   g.M = 2 * I;
   g.N = H;
@@ -2295,44 +2358,31 @@ hipError_t launch_ffn_wgrad_fp8(const bf16_t* x, const int32_t* src_row, const b
   g.ldc = H;
   g.f_group_stride = (long)I * H;
   g.accumulate = accumulate ? 1 : 0;
-  g.sa = s_gu;
+  g.sa = L.s_gu;
   g.sa_group_stride = 2 * I;
-  g.sb0 = s_x;
+  g.sb0 = L.s_x;
   g.sb_group_stride = H;
-  g.tile_ctr = ctrs;
-  g.kplan = plan.t[0];
-  g.fpart = part[0];
-  err = launch_gemm<K_WGRAD8, kBmWgrad, true>(g, (E_l + SL.slots[0]) * g.n_mtiles * g.n_ntiles,
+  g.tile_ctr = L.ctrs;
+  g.kplan = L.plan.t[0];
+  g.fpart = L.part[0];
+  err = launch_gemm<K_WGRAD8, kBmWgrad, true>(g, (E_l + L.SL.slots[0]) * g.n_mtiles * g.n_ntiles,
                                               MOE_KERNEL_FFN_GATEUP_WGRAD, s);
   if (err != hipSuccess) return err;
+  WgradPlan plan = L.plan;
+  float* part[2] = {L.part[0], L.part[1]};
+  return launch_wgrad_split_reduce(plan, part, L.SL, E_l, H, I, dw_gate, dw_up, dw_down, s);
+}
 
-  GemmArgs d{};
-  d.a = (const bf16_t*)q_dy;
-  d.lda = Kp / 2;
-  d.b0 = (const bf16_t*)q_h;
-  d.ldb = Kp / 2;
-  d.offsets = poff;
-  d.groups = E_l;
-  d.M = H;
-  d.N = I;
-  d.n_mtiles = (H + kBmWgrad - 1) / kBmWgrad;
-  d.n_ntiles = (I + BN - 1) / BN;
-  d.f0 = dw_down;
-  d.m_split = H;
-  d.ldc = I;
-  d.f_group_stride = (long)H * I;
-  d.accumulate = accumulate ? 1 : 0;
-  d.sa = s_dy;
-  d.sa_group_stride = H;
-  d.sb0 = s_h;
-  d.sb_group_stride = I;
-  d.tile_ctr = ctrs + 1;
-  d.kplan = plan.t[1];
-  d.fpart = part[1];
-  err = launch_gemm<K_WGRAD8, kBmWgrad, true>(d, (E_l + SL.slots[1]) * d.n_mtiles * d.n_ntiles,
-                                              MOE_KERNEL_FFN_DOWN_WGRAD, s);
+hipError_t launch_ffn_wgrad_fp8(const bf16_t* x, const int32_t* src_row, const bf16_t* dgu,
+                                const bf16_t* h_perm, const bf16_t* dy_perm,
+                                const int32_t* offsets, int E_l, int R_cap, int H, int I,
+                                float* dw_gate, float* dw_up, float* dw_down, bool accumulate,
+                                void* ws, hipStream_t s) {
+  hipError_t err = launch_ffn_wgrad_fp8_begin(x, src_row, h_perm, dy_perm, offsets, E_l, R_cap, H,
+                                              I, dw_down, accumulate, ws, s);
   if (err != hipSuccess) return err;
-  return launch_wgrad_split_reduce(plan, part, SL, E_l, H, I, dw_gate, dw_up, dw_down, s);
+  return launch_ffn_wgrad_fp8_end(dgu, offsets, E_l, R_cap, H, I, dw_gate, dw_up, dw_down,
+                                  accumulate, ws, s);
 }
 
 // A second stream of the calling device for products that may run beside

@@ -19,8 +19,10 @@ and, for training, per input channel as well (both layouts in one pass pair,
 on the second stream beside routing and permute; the backward uses these
 codes, so it must be given the forward's weights); the
 backward quantizes the rows of dy_perm, and the weight gradients quantize
-their operands per (expert, column).  Routing, combine and the router backward
-stay as in the bf16 layer.
+their operands per (expert, column): x, dy_perm and h (with dW_down) on the
+second stream from the start of the backward, [dg | du] (with dW_gate and
+dW_up) once the data gradients have produced it.  Routing, combine and the
+router backward stay as in the bf16 layer.
 """
 from __future__ import annotations
 
@@ -182,13 +184,24 @@ class MoELayer:
                                            _p(b["y_perm"]), ws, wsb, s), "moe_grouped_ffn_fwd_fp8")
 
     def _backward_ffn_fp8(self, x, w_gate, w_up, w_down, ws, wsb, s, side):
-        """dy_perm rows quantized, the FP8 data gradients on this stream (weight
-        codes per input channel from the forward), then the FP8 weight gradients
-        on the side stream."""
+        """The first half of the FP8 weight gradients (x, dy_perm and h quantized
+        per (expert, column), dW_down) on the side stream from the start; dy_perm
+        rows quantized and the FP8 data gradients on this stream (weight codes per
+        input channel from the forward); then the second half ([dg | du]
+        quantized, dW_gate and dW_up, the split experts' sums) on the side
+        stream once the data gradients have written [dg | du]."""
         b, H, I, E_l = self.buf, self.H, self.I, self.E_l
         if getattr(self, "_fp8_weights", None) != (w_gate.data_ptr(), w_up.data_ptr(), w_down.data_ptr()):
             raise ValueError("the FP8 backward uses the weight codes of the forward: pass it the "
                              "forward's weight tensors")
+        main = torch.cuda.current_stream()
+        w8, w8b = _p(self.ws_w8), self.ws_w8.numel()
+        # dy_perm (the combine backward's output) exists: the side stream starts
+        self.side.wait_stream(main)
+        _check(lib.moe_grouped_ffn_wgrad_fp8_begin(_p(x), _p(b["src_row"]), _p(b["h_perm"]),
+                                                   _p(b["dy_perm"]), _p(b["offsets"]), E_l, self.R_cap,
+                                                   H, I, _p(b["dw_down"]), 0, w8, w8b, side),
+               "moe_grouped_ffn_wgrad_fp8_begin")
         self._quantize_rows(b["dy_perm"], self.R_cap, H, b["dy_q"], b["dy_scale"], s,
                             nrows=b["offsets"][E_l:])
         _check(lib.moe_grouped_ffn_dgrad_fp8(_p(b["dy_q"]), _p(b["dy_scale"]), _p(b["gu"]),
@@ -196,13 +209,12 @@ class MoELayer:
                                              _p(b["wdt_s"]), _p(b["wgut_q"]), _p(b["wgut_s"]),
                                              _p(b["dgu"]), _p(b["dx_perm"]), ws, wsb, s),
                "moe_grouped_ffn_dgrad_fp8")
-        # the weight gradients need dgu: the side stream waits for this stream
-        self.side.wait_stream(torch.cuda.current_stream())
-        _check(lib.moe_grouped_ffn_wgrad_fp8(_p(x), _p(b["src_row"]), _p(b["dgu"]), _p(b["h_perm"]),
-                                             _p(b["dy_perm"]), _p(b["offsets"]), E_l, self.R_cap, H, I,
-                                             _p(b["dw_gate"]), _p(b["dw_up"]), _p(b["dw_down"]), 0,
-                                             _p(self.ws_w8), self.ws_w8.numel(), side),
-               "moe_grouped_ffn_wgrad_fp8")
+        # the second half needs dgu: the side stream waits for this stream
+        self.side.wait_stream(main)
+        _check(lib.moe_grouped_ffn_wgrad_fp8_end(_p(b["dgu"]), _p(b["offsets"]), E_l, self.R_cap, H, I,
+                                                 _p(b["dw_gate"]), _p(b["dw_up"]), _p(b["dw_down"]), 0,
+                                                 w8, w8b, side),
+               "moe_grouped_ffn_wgrad_fp8_end")
 
     def backward(self, dy, x, w_router, w_gate, w_up, w_down) -> Dict[str, torch.Tensor]:
         if not self.train:

@@ -50,7 +50,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_single_hip_runtime():
-    assert L.moe_abi_version() == moe.ABI_VERSION == 8
+    assert L.moe_abi_version() == moe.ABI_VERSION == 9
     libs = moe.hip_runtimes_mapped()
     assert len(libs) <= 1, libs
 

@@ -527,6 +527,56 @@ def test_ffn_wgrad_fp8_matches_oracle(w):
     assert max(rel_exact) < 0.10
 
 
+@pytest.mark.parametrize("acc", [False, True], ids=["overwrite", "accumulate"])
+@pytest.mark.parametrize("w", [WGRAD_CASES[3], WGRAD_CASES[4]], ids=lambda w: w.name)
+def test_ffn_wgrad_fp8_halves_equal_the_whole(w, acc):
+    """moe_grouped_ffn_wgrad_fp8_begin on one stream, then _end on another stream
+    ordered after it by an event (begin started before dgu is written, as the layer
+    runs it), equals moe_grouped_ffn_wgrad_fp8 bit for bit, overwriting and
+    accumulating into the same prior values; one case splits hot experts into K
+    chunks (dW_down is complete only after end)."""
+    inp = make_inputs(w)
+    _, idx, _ = O.route(inp["x"], inp["w_router"], w.k, inp.get("bias"))
+    print(f"  case {w.name} accumulate={acc}", flush=True)
+    bf = torch.bfloat16
+    x = _dev(inp["x"], bf)
+    perm = moe.moe_permute(x, torch.from_numpy(idx.astype(np.int32)).to(DEV), w.E, w.e_lo, w.e_hi)
+    offsets, src_row = perm["offsets"], perm["src_row"]
+    R_cap, E_l = w.T * w.k, w.e_hi - w.e_lo
+    rng = np.random.default_rng(zlib.crc32(w.name.encode()) + 1)
+    dgu_src = _dev((rng.standard_normal((R_cap, 2 * w.I)) * 0.3).astype(np.float32), bf)
+    h = _dev(rng.standard_normal((R_cap, w.I)).astype(np.float32), bf)
+    dy = _dev((rng.standard_normal((R_cap, w.H)) * 0.05).astype(np.float32), bf)
+    prior = {"dw_gate": torch.randn((E_l, w.I, w.H), device=DEV),
+             "dw_up": torch.randn((E_l, w.I, w.H), device=DEV),
+             "dw_down": torch.randn((E_l, w.H, w.I), device=DEV)}
+    whole = {n: t.clone() for n, t in prior.items()}
+    moe.moe_grouped_ffn_wgrad_fp8(x, src_row, dgu_src, h, dy, offsets, E_l, accumulate=acc, out=whole)
+    torch.cuda.synchronize()
+    halves = {n: t.clone() for n, t in prior.items()}
+    nb = moe.lib.moe_workspace_bytes(moe.MOE_OP_FFN_WGRAD_FP8, R_cap, w.H, w.I, E_l, 1, 0, E_l,
+                                     moe.MOE_BF16)
+    ws = torch.full((int(nb),), 0x5A, dtype=torch.uint8, device=DEV)  # stale bytes
+    dgu = torch.full_like(dgu_src, float("nan"))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    moe.moe_grouped_ffn_wgrad_fp8_begin(x, src_row, h, dy, offsets, E_l, ws, halves["dw_down"],
+                                        accumulate=acc, stream=s1)
+    # dgu written on the current stream while begin runs on s1
+    dgu.copy_(dgu_src)
+    ready = torch.cuda.Event()
+    ready.record(torch.cuda.current_stream())
+    done = torch.cuda.Event()
+    done.record(s1)
+    s2.wait_event(ready)
+    s2.wait_event(done)
+    moe.moe_grouped_ffn_wgrad_fp8_end(dgu, offsets, E_l, w.H, ws, halves, accumulate=acc, stream=s2)
+    torch.cuda.current_stream().wait_stream(s2)
+    torch.cuda.synchronize()
+    for n in whole:
+        assert torch.equal(halves[n], whole[n]), f"{n}: halves differ from the whole call"
+
+
 # ----------------------------------------------------------------------------
 # the layer with fp8=True
 # ----------------------------------------------------------------------------
