@@ -183,13 +183,22 @@ class MoELayer:
                                            _p(b["wd_s"]), _p(b["gu"]), _p(b["h_perm"]),
                                            _p(b["y_perm"]), ws, wsb, s), "moe_grouped_ffn_fwd_fp8")
 
-    def _backward_ffn_fp8(self, x, w_gate, w_up, w_down, ws, wsb, s, side):
+    def _route_bwd(self, x, w_router, stream):
+        b, T, H, E, k = self.buf, self.T, self.H, self.E, self.k
+        _check(lib.moe_route_bwd(_p(b["d_topk_w"]), _p(b["topk_w"]), _p(b["topk_idx"]), _p(x),
+                                 _p(w_router), T, H, E, k, self.dt, _p(b["d_logits"]),
+                                 None, _p(b["dw_router"]), _p(self.ws_rb), self.ws_rb.numel(), stream),
+               "moe_route_bwd")
+
+    def _backward_ffn_fp8(self, x, w_router, w_gate, w_up, w_down, ws, wsb, s, side):
         """The first half of the FP8 weight gradients (x, dy_perm and h quantized
-        per (expert, column), dW_down) on the side stream from the start; dy_perm
-        rows quantized and the FP8 data gradients on this stream (weight codes per
-        input channel from the forward); then the second half ([dg | du]
-        quantized, dW_gate and dW_up, the split experts' sums) on the side
-        stream once the data gradients have written [dg | du]."""
+        per (expert, column), dW_down) and then the router backward on the side
+        stream from the start; dy_perm rows quantized and the FP8 data gradients
+        on this stream (weight codes per input channel from the forward); then
+        the second half ([dg | du] quantized, dW_gate and dW_up, the split
+        experts' sums) on the side stream once the data gradients have written
+        [dg | du].  (The router backward needs only d_topk_w and x: it fills the
+        side stream's wait for [dg | du] instead of trailing the step.)"""
         b, H, I, E_l = self.buf, self.H, self.I, self.E_l
         if getattr(self, "_fp8_weights", None) != (w_gate.data_ptr(), w_up.data_ptr(), w_down.data_ptr()):
             raise ValueError("the FP8 backward uses the weight codes of the forward: pass it the "
@@ -202,6 +211,7 @@ class MoELayer:
                                                    _p(b["dy_perm"]), _p(b["offsets"]), E_l, self.R_cap,
                                                    H, I, _p(b["dw_down"]), 0, w8, w8b, side),
                "moe_grouped_ffn_wgrad_fp8_begin")
+        self._route_bwd(x, w_router, side)
         self._quantize_rows(b["dy_perm"], self.R_cap, H, b["dy_q"], b["dy_scale"], s,
                             nrows=b["offsets"][E_l:])
         _check(lib.moe_grouped_ffn_dgrad_fp8(_p(b["dy_q"]), _p(b["dy_scale"]), _p(b["gu"]),
@@ -233,7 +243,7 @@ class MoELayer:
         main = torch.cuda.current_stream()
         side = ctypes.c_void_p(self.side.cuda_stream)
         if self.fp8:
-            self._backward_ffn_fp8(x, w_gate, w_up, w_down, ws, wsb, s, side)
+            self._backward_ffn_fp8(x, w_router, w_gate, w_up, w_down, ws, wsb, s, side)
         else:
             # data gradients on this stream; the weight gradients continue on the side stream
             _check(lib.moe_grouped_ffn_bwd_split(_p(b["dy_perm"]), _p(b["x_perm"]), _p(b["gu"]),
@@ -247,12 +257,10 @@ class MoELayer:
                                     _p(b["topk_w"]), _p(b["topk_idx"]), _p(b["w_router_t"]), T, H,
                                     E, k, self.dt, _p(b["dx"]), s),
                "moe_combine_dx_t")
-        # router backward behind the weight gradients (the side stream already
-        # waits for d_topk_w: the FFN backward forked it after the combine backward)
-        _check(lib.moe_route_bwd(_p(b["d_topk_w"]), _p(b["topk_w"]), _p(b["topk_idx"]), _p(x),
-                                 _p(w_router), T, H, E, k, self.dt, _p(b["d_logits"]),
-                                 None, _p(b["dw_router"]), _p(self.ws_rb), self.ws_rb.numel(), side),
-               "moe_route_bwd")
+        if not self.fp8:
+            # router backward behind the weight gradients (the side stream already
+            # waits for d_topk_w: the FFN backward forked it after the combine backward)
+            self._route_bwd(x, w_router, side)
         main.wait_stream(self.side)
         return {n: b[n] for n in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "d_logits",
                                   "d_topk_w")}
