@@ -588,6 +588,26 @@ LAYER_FP8_CASES = [
 ]
 
 
+def test_layer_fp8_inference_equals_the_training_forward():
+    """MoELayer(fp8=True, train=False) (no backward buffers; the weight codes of one
+    layout, still quantized on the layer's second stream beside routing) gives the
+    training layer's forward bit for bit, on two calls in a row with different
+    weights (the second call must wait for its own weight codes)."""
+    w = LAYER_FP8_CASES[0]
+    inp = make_inputs(w)
+    bf = torch.bfloat16
+    t = {n: _dev(inp[n], bf) for n in ("x", "w_router", "w_gate", "w_up", "w_down")}
+    inf = moe.MoELayer(w.T, w.H, w.I, w.E, w.k, w.e_lo, w.e_hi, bf, DEV, train=False, fp8=True)
+    tr = moe.MoELayer(w.T, w.H, w.I, w.E, w.k, w.e_lo, w.e_hi, bf, DEV, train=True, fp8=True)
+    for scale in (1.0, 0.5):
+        ws = {n: (t[n] * scale).contiguous() for n in ("w_gate", "w_up", "w_down")}
+        args = (t["x"], t["w_router"], ws["w_gate"], ws["w_up"], ws["w_down"])
+        y_inf = inf.forward(*args).clone()
+        y_tr = tr.forward(*args).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(y_inf, y_tr), f"weights x{scale}: inference forward differs"
+
+
 @pytest.mark.parametrize("w", LAYER_FP8_CASES, ids=lambda w: w.name)
 def test_layer_fp8_is_the_call_chain_and_tracks_the_exact_layer(w):
     """MoELayer(fp8=True): forward and backward equal, bit for bit, the FP8 calls
