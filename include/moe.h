@@ -59,7 +59,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_EINVAL = -1,        /* bad argument: null pointer, shape or range */
-  MOE_EUNSUPPORTED = -2,  /* legal request this build does not implement */
+  MOE_EUNSUPPORTED = -2,  /* legal request the library does not implement */
   MOE_EWORKSPACE = -3,    /* ws_bytes smaller than moe_workspace_bytes() */
   MOE_EHIP = -4           /* a HIP launch failed; see moe_last_error() */
 } moe_status;
