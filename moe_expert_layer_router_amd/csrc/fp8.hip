@@ -376,11 +376,10 @@ struct GtChunk {
   int ng;    // rows in the group
 };
 
-// Chunk c of the list of CH-row chunks of the groups with more than MIN_N rows
-// (group order; an empty group, when counted, is one empty chunk), found by
-// wave 0 with scans over 64 groups at a time; the result reaches the whole
-// workgroup through LDS.
-template <int CH, int MIN_N>
+// Chunk c of the list of CH-row chunks of the groups (group order; an empty
+// group is one empty chunk), found by wave 0 with scans over 64 groups at a
+// time; the result reaches the whole workgroup through LDS.
+template <int CH>
 __device__ GtChunk gt_find_chunk(const int32_t* offsets, int E_l, int c, int t, GtChunk* s_c) {
   if (t < kWave) {
     int base_c = 0, base_p = 0;
@@ -388,7 +387,7 @@ __device__ GtChunk gt_find_chunk(const int32_t* offsets, int E_l, int c, int t, 
     for (int j0 = 0; j0 < E_l && !found; j0 += kWave) {
       const int j = j0 + t;
       const int n = j < E_l ? offsets[j + 1] - offsets[j] : 0;
-      const int nc = j < E_l && n > MIN_N ? max(1, (n + CH - 1) / CH) : 0;
+      const int nc = j < E_l ? max(1, (n + CH - 1) / CH) : 0;
       const int pd = (n + 63) & ~63;
       int ic = nc, ip = pd;
 #pragma unroll
@@ -477,7 +476,7 @@ __global__ __launch_bounds__(256) void quantize_group_t_max_kernel(const QuantGr
   int c0;
   const QuantGroupTensor& T = gt_tensor(a, c0);
   for (int c = blockIdx.y;; c += gridDim.y) {
-    const GtChunk k = gt_find_chunk<kGtMaxRows, -1>(a.offsets, a.E_l, c, t, &s_c);
+    const GtChunk k = gt_find_chunk<kGtMaxRows>(a.offsets, a.E_l, c, t, &s_c);
     if (k.g < 0) break;
     uint4 v[kGtMaxRows / 32];
 #pragma unroll
@@ -524,7 +523,7 @@ __global__ __launch_bounds__(256) void quantize_group_t_codes_kernel(const Quant
   int c0;
   const QuantGroupTensor& T = gt_tensor(a, c0);
   for (int c = blockIdx.y;; c += gridDim.y) {
-    const GtChunk k = gt_find_chunk<kGtCodesRows, -1>(a.offsets, a.E_l, c, t, &s_c);
+    const GtChunk k = gt_find_chunk<kGtCodesRows>(a.offsets, a.E_l, c, t, &s_c);
     if (k.g < 0) break;
     if (blockIdx.x == 0 && k.rbeg == 0 && t == 0) {
       a.poff[k.g] = k.poff;
