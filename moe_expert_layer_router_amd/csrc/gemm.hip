@@ -1024,7 +1024,10 @@ __device__ __forceinline__ void k_steps(f32x16_t (&acc)[C::MI][NI], Frags<C>& f0
 //   s3: MFMAs (f1), the DMA of block j + 2's B (load 2j + 5, region (2j) % 5 =
 //       block j's A) and block j + 1's sub-step 0 fragments into f0.
 // Block j + 2's B thus has three sub-steps to land, its A about one block.
-template <int KIND, class C>
+// MIA < MI: the wave's rows end inside the tile, and only its first MIA
+// 32-row blocks are multiplied (the accumulators of the others stay zero; the
+// loads, waits and barriers are those of the full form).
+template <int KIND, class C, int MIA = C::MI>
 __device__ __forceinline__ void k_blocks(f32x16_t (&acc)[C::MI][NI], Frags<C>& f0, Frags<C>& f1,
                                          const FragLanes<C>& L, const GemmArgs& p,
                                          const Operand<C::NIA>& opA, const Operand<C::NIB>& opB,
@@ -1046,20 +1049,20 @@ __device__ __forceinline__ void k_blocks(f32x16_t (&acc)[C::MI][NI], Frags<C>& f
     const int k2 = (j + 2) * C::BKX;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      mfma1(acc[m / NI][m % NI], f0.a[m / NI], f0.b[m % NI]);
+      if (m / NI < MIA) mfma1(acc[m / NI][m % NI], f0.a[m / NI], f0.b[m % NI]);
       if (m < NR) load_frag<KIND, C>(f1, m, 1, sa, sb, L);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      mfma1(acc[m / NI][m % NI], f1.a[m / NI], f1.b[m % NI]);
+      if (m / NI < MIA) mfma1(acc[m / NI][m % NI], f1.a[m / NI], f1.b[m % NI]);
       if (m < NR) load_frag<KIND, C>(f0, m, 2, sa, sb, L);
       if (m % SA == 0) dma_piece<KIND, C>(p, opA, opB, dma_w + rq * R, 0u, k2, kill, m / SA);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      mfma1(acc[m / NI][m % NI], f0.a[m / NI], f0.b[m % NI]);
+      if (m / NI < MIA) mfma1(acc[m / NI][m % NI], f0.a[m / NI], f0.b[m % NI]);
       if (m < NR) load_frag<KIND, C>(f1, m, 3, sa, sb, L);
       if (m % SA == 0) dma_piece<KIND, C>(p, opA, opB, dma_w + rq * R, 0u, k2, kill, NIA / 2 + m / SA);
       __builtin_amdgcn_sched_barrier(0);
@@ -1068,7 +1071,7 @@ __device__ __forceinline__ void k_blocks(f32x16_t (&acc)[C::MI][NI], Frags<C>& f
     lds_barrier();  // every wave: block j + 1 landed, block j fully read
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      mfma1(acc[m / NI][m % NI], f1.a[m / NI], f1.b[m % NI]);
+      if (m / NI < MIA) mfma1(acc[m / NI][m % NI], f1.a[m / NI], f1.b[m % NI]);
       if (m % SB == 0) dma_piece<KIND, C>(p, opA, opB, 0u, dma_w + ra * R, k2, kill, NIA + m / SB);
       if (m >= NM - NR) load_frag<KIND, C>(f0, m - (NM - NR), 0, rn * R + wa, rnb * R + wb, L);
       __builtin_amdgcn_sched_barrier(0);
@@ -1573,7 +1576,22 @@ void gemm_kernel(const GemmArgs p) {
       } else if constexpr (C::WIDE) {
         Frags<C> f0, f1;
         load_frags<KIND, C>(f0, 0, wa, C::kRegion + wb, L);
-        k_blocks<KIND, C>(acc, f0, f1, L, p, opA, opB, dma_a, wa, wb, t.nk);
+        if constexpr (!k_grouped(KIND)) {
+          // an expert's last row tile (or the router product's last token
+          // tile) may end inside this wave's rows: MFMAs only for its 32-row
+          // blocks that hold rows
+          const int mi_act = __builtin_amdgcn_readfirstlane(
+              min(MI, max(0, (t.row1 - t.row0 - wm * WM + 31) / 32)));
+          static_assert(MI == 4, "the short forms below assume four 32-row blocks per wave");
+          if (mi_act > 2)
+            k_blocks<KIND, C>(acc, f0, f1, L, p, opA, opB, dma_a, wa, wb, t.nk);
+          else if (mi_act > 0)
+            k_blocks<KIND, C, 2>(acc, f0, f1, L, p, opA, opB, dma_a, wa, wb, t.nk);
+          else
+            k_blocks<KIND, C, 0>(acc, f0, f1, L, p, opA, opB, dma_a, wa, wb, t.nk);
+        } else {
+          k_blocks<KIND, C>(acc, f0, f1, L, p, opA, opB, dma_a, wa, wb, t.nk);
+        }
       } else {
         static_assert(C::KSUB == 2, "the fragment pipeline below assumes two k16 sub-steps");
         Frags<C> f0, f1;

@@ -146,8 +146,12 @@ def _design(kind, bm, fp8):
         nr = 4 * mi if kind == 0 else 8 * mi
         nc = 16 if kind == 0 else 8
         scales = nr + nc // 4
+    # the bf16 M-grouped products and the router product compile the wide K loop
+    # three times (all four 32-row blocks of a wave multiplied, the first two,
+    # none: an expert's last row tile may end inside a wave's rows)
+    forms = 3 if wide and not fp8 and kind in (0, 1, 2, 3, 6) else 1
     return {"nst": nst, "nd": nia + nib, "nia": nia, "epi": epi, "scales": scales, "sep": bm == 256,
-            "wide": wide}
+            "wide": wide, "forms": forms}
 
 
 GEMM_KERNELS = [(0, 256, False), (1, 256, False), (2, 256, False), (3, 256, False), (4, 256, False),
@@ -277,23 +281,25 @@ def _check_wide_ring(ev, d):
     nd, nia = d["nd"], d["nia"]
     nib = nd - nia
     dmas = [e for e in ev if e == "D"]
-    # prologue twice (first tile, next tile), one block's two DMA groups in the loop
-    assert len(dmas) == 2 * 2 * nd + nd, (len(dmas), d)
+    # prologue twice (first tile, next tile), one block's two DMA groups in
+    # each form of the loop
+    assert len(dmas) == 2 * 2 * nd + d["forms"] * nd, (len(dmas), d)
     waits = [e for e in ev if isinstance(e, int) and e > 0]
     k_first, k_loop = nd, nia
     assert k_first in waits and k_loop in waits, (waits, k_first, k_loop)
     k_epi = d["epi"] + d["scales"]
     k_after = min(VMCNT_MAX, k_first + k_epi)
     assert k_after in waits, (waits, k_after)
-    # inside the loop exactly one wait, between the two DMA groups
-    # (the K loop's header: the one directly followed by a DMA; the tile loop's
-    # comes first, epilogue loops come later)
+    # inside each form of the loop exactly one wait, between the two DMA groups
+    # (a K loop's header: one directly followed by a DMA; the tile loop's comes
+    # first, epilogue loops come later); a body ends at the next loop header or
+    # the drain after the loop
     hdrs = [i for i, e in enumerate(ev[:-1]) if e == "L" and ev[i + 1] == "D"]
-    assert len(hdrs) == 1, hdrs
-    hdr = hdrs[0]
-    end = next(i for i in range(hdr, len(ev)) if ev[i] == 0)
-    body = ev[hdr + 1:end]
-    assert body == ["D"] * nia + [k_loop] + ["D"] * nib, body
+    assert len(hdrs) == d["forms"], hdrs
+    for hdr in hdrs:
+        end = next(i for i in range(hdr + 1, len(ev)) if ev[i] == 0 or ev[i] == "L")
+        body = ev[hdr + 1:end]
+        assert body == ["D"] * nia + [k_loop] + ["D"] * nib, body
 
     def prologue(f, tile):
         for blk in range(2):
