@@ -196,8 +196,12 @@ ROUTE_CASES = [TINY, EP_SHARE, FULL, SKEWED,
                                e_lo=0, e_hi=256),
                EP_SHARE.scaled(name="route_bf16_t301_h320_e40_k5", T=301, H=320, E=40, k=5,
                                e_lo=0, e_hi=40),
-               # two 32-token tiles per workgroup, ragged last workgroup
+               # 513 workgroups of 32 tokens (more than two per CU), ragged last workgroup
                EP_SHARE.scaled(name="route_bf16_t16411_h256_e128_k8", T=16411, H=256),
+               # five 64-column x stages over eight waves (three waves take none),
+               # many workgroups, k = 32 (slots 16.. from the second kept round)
+               EP_SHARE.scaled(name="route_bf16_t16400_h320_e128_k32", T=16400, H=320, E=128, k=32,
+                               e_lo=0, e_hi=128),
                # 4 K steps over 8 waves (some waves have none), one 8-expert chunk
                EP_SHARE.scaled(name="route_bf16_t1000_h64_e8_k2", T=1000, H=64, E=8, k=2, e_lo=0,
                                e_hi=8),
@@ -234,9 +238,11 @@ def test_route_from_logits_ties_exact(T, E, k):
     np.testing.assert_allclose(gw.cpu().numpy(), O.gate_weights(z, idx_ref), rtol=1e-6, atol=1e-7)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_route_degenerate_cases(dtype):
-    w = Workload("t", 300, 128, 64, 16, 3, 0, 16, dtype)
+@pytest.mark.parametrize("dtype,T,E", [("bf16", 300, 16), ("f32", 300, 16),
+                                        # 128 experts (four 32-expert MFMA blocks), 513 workgroups
+                                        ("bf16", 16400, 128)])
+def test_route_degenerate_cases(dtype, T, E):
+    w = Workload("t", T, 128, 64, E, 3, 0, E, dtype)
     inp = make_inputs(w)
     tdt = _tdtype(w)
     # x = 0: every logit is 0, so slots take ids 0..k-1 with weight 1/k
@@ -260,9 +266,11 @@ def test_route_degenerate_cases(dtype):
                 assert 3 in r and r.index(3) < r.index(d)
                 hit += 1
     assert hit > 0
-    # k = 1 gives weight 1; k = E gives the full softmax
+    # k = 1 gives weight 1; k = E (k is at most 32) gives the full softmax
     _, g1, _ = moe.moe_route(_dev(inp["x"], tdt), _dev(inp["w_router"], tdt), 1)
     assert (g1.cpu().numpy() == 1.0).all()
+    if w.E > 32:
+        return
     idxE, gE, lE = moe.moe_route(_dev(inp["x"], tdt), _dev(inp["w_router"], tdt), w.E, want_logits=True)
     lE = lE.cpu().numpy().astype(np.float64)
     ref = O.softmax(lE)
