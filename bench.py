@@ -47,10 +47,12 @@ def step_flops(w, R):
     return f
 
 
-def kernel_work(name, w, R, launches, A=None):
+def kernel_work(name, w, R, launches, A=None, gather=False):
     """Algorithmic (flops, HBM bytes) of ONE launch of a kernel.  R = routed rows
     kept on this GPU, A = tokens with at least one of them (rows of x, dy that
-    the scatter and the combine backward must read; all T when not given)."""
+    the scatter and the combine backward must read; all T when not given).
+    gather: the layer's permute writes the maps alone and the gate/up product
+    reads the token rows through src_row (each row once from HBM)."""
     T, H, I, E, k, El = w.T, w.H, w.I, w.E, w.k, w.E_l
     A = T if A is None else A
     b = 2 if w.dtype == "bf16" else 4
@@ -77,6 +79,9 @@ def kernel_work(name, w, R, launches, A=None):
         "FFN_GATEUP_DGRAD": (4.0 * R * H * I, R * 2 * I * b + 2 * El * I * H * b + R * H * b),
         "FFN_GATEUP_WGRAD": (4.0 * R * H * I, R * 2 * I * b + R * H * b + 2 * El * I * H * 4),
     }
+    if gather:
+        tab["PERMUTE_SCATTER"] = (0, T * k * 12 + R * 4)
+        tab["FFN_GATEUP"] = (4.0 * R * H * I, A * H * b + 2 * El * I * H * b + R * I * b + gu)
     if name == "COMBINE":
         return 0.0, R * H * b + T * k * 8 + T * H * b
     return tab[name]
@@ -118,8 +123,8 @@ def measured_traffic(kernel, workload):
     return None
 
 
-def roofline_of(name, w, R, avg_us, launches, A=None):
-    flops, nbytes = kernel_work(name, w, R, launches, A)
+def roofline_of(name, w, R, avg_us, launches, A=None, gather=False):
+    flops, nbytes = kernel_work(name, w, R, launches, A, gather)
     peak_f = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     t_f = flops / (peak_f * 1e12)
     t_b = nbytes / (PEAK_HBM_GBS * 1e9)
@@ -444,46 +449,67 @@ def secondary_forward(w, args, moe, torch):
     """The forward of the full 128-expert layer (every expert local, T = 16384):
     graph-replayed layer time and each forward kernel's live time against its
     roofline (router, permute and combine against HBM, the grouped products
-    against bf16 MFMA).  "PERMUTE" is the permute's three launches together,
-    priced at the scatter's algorithmic bytes."""
+    against bf16 MFMA).  The layer's permute writes the maps alone and its
+    gate/up product reads the token rows through src_row.  The same forward on
+    the materialized grouped copy is timed beside it ("ms_per_step_grouped_copy"),
+    and its permute launches in it ("permute_copy": the scatter, and the three
+    launches together, "PERMUTE", priced at the copy's algorithmic bytes)."""
     from workloads import make_inputs
     dev = torch.device("cuda:0")
     inp = make_inputs(w)
     t = {n: torch.from_numpy(v).to(dev).to(torch.bfloat16).contiguous() for n, v in inp.items()
          if n != "bias"}
-    layer = moe.MoELayer(w.T, w.H, w.I, w.E, w.k, w.e_lo, w.e_hi, torch.bfloat16, dev, train=False)
-    step = lambda: layer.forward(t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"])
-    for _ in range(max(args.warmup, 1)):
-        step()
-    torch.cuda.synchronize()
-    R = int(layer.buf["offsets"][-1].item())
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        step()
-    g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
+
+    def graph_ms(layer):
+        step = lambda: layer.forward(t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"])
+        for _ in range(max(args.warmup, 1)):
+            step()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
         g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps, step
+
+    layer = moe.MoELayer(w.T, w.H, w.I, w.E, w.k, w.e_lo, w.e_hi, torch.bfloat16, dev, train=False)
+    gather = layer.gather
+    ms, step = graph_ms(layer)
+    R = int(layer.buf["offsets"][-1].item())
     kt = live_kernel_times(moe, torch, step, args.steps)
     roof = {}
     for k, v in kt.items():
-        r = roofline_of(k, w, R, v["avg_us"], v["launches_per_step"])
+        r = roofline_of(k, w, R, v["avg_us"], v["launches_per_step"], gather=gather)
         roof[k] = {kk: r[kk] for kk in ("bound", "achieved", "unit", "frac", "avg_us")}
-    perm = [k for k in ("PERMUTE_HIST", "PERMUTE_SCAN", "PERMUTE_SCATTER") if k in kt]
-    if perm:
-        us = sum(kt[k]["avg_us"] for k in perm)
+    del layer
+    # the permute that writes the grouped copy, alone, and the forward on it
+    ref = moe.MoELayer(w.T, w.H, w.I, w.E, w.k, w.e_lo, w.e_hi, torch.bfloat16, dev, train=False,
+                       gather=False)
+    ms_copy, step_copy = graph_ms(ref)
+    kp = live_kernel_times(moe, torch, step_copy, args.steps)
+    pc = {}
+    for k in ("PERMUTE_HIST", "PERMUTE_SCAN", "PERMUTE_SCATTER"):
+        if k in kp:
+            r = roofline_of(k, w, R, kp[k]["avg_us"], kp[k]["launches_per_step"])
+            pc[k] = {kk: r[kk] for kk in ("bound", "achieved", "unit", "frac", "avg_us")}
+    if pc:
+        us = sum(v["avg_us"] for v in pc.values())
         nb = kernel_work("PERMUTE_SCATTER", w, R, 1)[1]
-        roof["PERMUTE"] = {"bound": "hbm", "achieved": round(nb / (us * 1e-6) / 1e9, 1), "unit": "GB/s",
-                           "frac": round(nb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "avg_us": round(us, 2)}
+        pc["PERMUTE"] = {"bound": "hbm", "achieved": round(nb / (us * 1e-6) / 1e9, 1), "unit": "GB/s",
+                         "frac": round(nb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "avg_us": round(us, 2)}
+    del ref
     flops = step_flops(w, R)
     return {"workload": w.name, "pass": "forward", "timing": "hip-graph replay", "steps": args.steps,
             "ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
-            "tokens_per_s": round(w.T / (ms * 1e-3), 1), "routed_rows": R, "roofline": roof}
+            "tokens_per_s": round(w.T / (ms * 1e-3), 1), "routed_rows": R,
+            "permute": "maps only, gate/up gathers x through src_row" if gather else "grouped copy",
+            "roofline": roof, "ms_per_step_grouped_copy": round(ms_copy, 4), "permute_copy": pc}
 
 
 def fp8_step(w, t, bias, args, moe, torch):

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 9
+#define MOE_ABI_VERSION 10
 
 typedef enum {
   MOE_OK = 0,
@@ -125,7 +125,9 @@ int moe_route_from_logits(const float* logits, int T, int E, int k, int32_t* top
  *   offsets  [E_l+1] int32: exclusive prefix sum, offsets[E_l] = R
  *   dest_row [T*k]   int32: grouped row of slot (t,j), or -1 if not local
  *   src_row  [T*k]   int32: token of grouped row r, for r < R
- *   x_perm   [T*k,H] dtype: x_perm[dest_row[t*k+j]] = x[t], bitwise
+ *   x_perm   [T*k,H] dtype: x_perm[dest_row[t*k+j]] = x[t], bitwise; or NULL:
+ *            the maps alone (for moe_grouped_ffn_fwd_gather, which reads the
+ *            token rows through src_row); x may then be NULL too
  *   ws       MOE_OP_PERMUTE workspace
  * dtype MOE_FP8 moves rows of H one-byte codes (H % 16 == 0).
  * A row of topk_idx may name one expert in several slots (moe_route never
@@ -148,6 +150,21 @@ int moe_grouped_ffn_fwd(const void* x_perm, const int32_t* offsets, int E_l, int
                         int I, const void* w_gate, const void* w_up, const void* w_down, int dtype,
                         void* gu_saved, void* h_perm, void* y_perm, void* ws, size_t ws_bytes,
                         void* stream);
+
+/* moe_grouped_ffn_fwd with the permutation folded into the first product:
+ * grouped row r is token row x[src_row[r]] (src_row from moe_permute, which
+ * then needs no x_perm), read by the gate/up product's operand loads in place
+ * of a permuted copy; everything else, results and rounding included, is
+ * moe_grouped_ffn_fwd's (the same products over the same rows: the same
+ * bits).  The permute then moves no rows, and the product reads the T token
+ * rows instead of T*k routed copies.
+ *   x [T,H] bf16, src_row [R_cap] int32 (entries below offsets[E_l] in [0,T))
+ *   other arguments as in moe_grouped_ffn_fwd (ws: MOE_OP_FFN_FWD)
+ * bf16 only (MOE_EUNSUPPORTED otherwise); T*H*2 < 2^31. */
+int moe_grouped_ffn_fwd_gather(const void* x, const int32_t* src_row, const int32_t* offsets,
+                               int E_l, int R_cap, int T, int H, int I, const void* w_gate,
+                               const void* w_up, const void* w_down, int dtype, void* gu_saved,
+                               void* h_perm, void* y_perm, void* ws, size_t ws_bytes, void* stream);
 
 /* moe_grouped_ffn_fwd without a workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses

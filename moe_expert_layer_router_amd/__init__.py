@@ -7,8 +7,8 @@ stream).  There is no fallback: importing this package fails when the built
 library is missing, and every call raises MoEError when the library reports
 an error.
 
-Functions keep the C names (moe_route, moe_permute, moe_grouped_ffn_fwd,
-moe_combine, moe_combine_bwd, moe_grouped_ffn_bwd, moe_route_bwd, and the FP8
+Functions keep the C names (moe_route, moe_permute, moe_grouped_ffn_fwd and its
+gathering form moe_grouped_ffn_fwd_gather, moe_combine, moe_combine_bwd, moe_grouped_ffn_bwd, moe_route_bwd, and the FP8
 forward: moe_quantize_fp8, moe_grouped_ffn_fwd_fp8; data gradients:
 moe_quantize_fp8_t, moe_grouped_ffn_dgrad_fp8; both weight layouts at once:
 moe_quantize_fp8_w; weight gradients:
@@ -32,7 +32,7 @@ MOE_F32, MOE_BF16, MOE_FP8 = 0, 1, 2
 (MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN_FWD, MOE_OP_FFN_BWD, MOE_OP_ROUTE_BWD,
  MOE_OP_COMBINE_DX, MOE_OP_FFN_FWD_FP8, MOE_OP_FFN_DGRAD_FP8, MOE_OP_FFN_WGRAD_FP8,
  MOE_OP_QUANTIZE_W_FP8) = range(10)
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 
 class MoEError(RuntimeError):
@@ -54,6 +54,8 @@ def _load():
         "moe_permute": ([P, P, I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, SZ, P], I32),
         "moe_grouped_ffn_fwd": ([P, P, I32, I32, I32, I32, P, P, P, I32, P, P, P, P, SZ, P], I32),
         "moe_grouped_ffn_fwd_noalloc": ([P, P, I32, I32, I32, I32, P, P, P, I32, P, P, P, P], I32),
+        "moe_grouped_ffn_fwd_gather": ([P, P, P, I32, I32, I32, I32, I32, P, P, P, I32, P, P, P, P, SZ,
+                                        P], I32),
         "moe_combine": ([P, P, P, P, I32, I32, I32, I32, P, P], I32),
         "moe_combine_bwd": ([P, P, P, P, I32, I32, I32, I32, P, P, P], I32),
         "moe_combine_dx": ([P, P, P, P, P, P, I32, I32, I32, I32, I32, P, P, SZ, P], I32),
@@ -185,8 +187,10 @@ def moe_route_from_logits(logits: torch.Tensor, k: int):
 
 
 def moe_permute(x: torch.Tensor, topk_idx: torch.Tensor, E: int, e_lo: int, e_hi: int,
-                ws: Optional[torch.Tensor] = None, out: Optional[Dict[str, torch.Tensor]] = None):
-    """Group routed rows by expert.  Returns dict counts, offsets, dest_row, src_row, x_perm."""
+                ws: Optional[torch.Tensor] = None, out: Optional[Dict[str, torch.Tensor]] = None,
+                copy_rows: bool = True):
+    """Group routed rows by expert.  Returns dict counts, offsets, dest_row, src_row, x_perm
+    (x_perm None with copy_rows=False: the maps alone, for moe_grouped_ffn_fwd_gather)."""
     T, H = x.shape
     k = topk_idx.shape[1]
     dt = _dtype_code(x)
@@ -197,7 +201,10 @@ def moe_permute(x: torch.Tensor, topk_idx: torch.Tensor, E: int, e_lo: int, e_hi
     o.setdefault("offsets", torch.empty(E_l + 1, dtype=torch.int32, device=dev))
     o.setdefault("dest_row", torch.empty(T * k, dtype=torch.int32, device=dev))
     o.setdefault("src_row", torch.empty(T * k, dtype=torch.int32, device=dev))
-    o.setdefault("x_perm", torch.empty((T * k, H), dtype=x.dtype, device=dev))
+    if copy_rows:
+        o.setdefault("x_perm", torch.empty((T * k, H), dtype=x.dtype, device=dev))
+    else:
+        o["x_perm"] = None
     ws = _ws(workspace_bytes(MOE_OP_PERMUTE, T, H, 1, E, k, e_lo, e_hi, dt), dev, ws)
     _check(lib.moe_permute(_ptr(x), _ptr(topk_idx), T, H, E, k, e_lo, e_hi, dt, _ptr(o["counts"]),
                            _ptr(o["offsets"]), _ptr(o["dest_row"]), _ptr(o["src_row"]),
@@ -229,6 +236,31 @@ def moe_grouped_ffn_fwd(x_perm: torch.Tensor, offsets: torch.Tensor, w_gate: tor
                                    _ptr(w_up), _ptr(w_down), dt, _ptr(o["gu"]), _ptr(o["h_perm"]),
                                    _ptr(o["y_perm"]), _ptr(ws), _nbytes(ws), _stream()),
            "moe_grouped_ffn_fwd")
+    return o
+
+
+def moe_grouped_ffn_fwd_gather(x: torch.Tensor, src_row: torch.Tensor, offsets: torch.Tensor,
+                               w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
+                               R_cap: int, save_gu: bool = True, ws: Optional[torch.Tensor] = None,
+                               out: Optional[Dict[str, torch.Tensor]] = None):
+    """moe_grouped_ffn_fwd on the token rows x [T,H], grouped row r = x[src_row[r]]
+    (moe_permute's src_row).  Returns dict h_perm, y_perm, gu (or None)."""
+    T, H = x.shape
+    E_l, I, _ = w_gate.shape
+    dt = _dtype_code(x)
+    dev = x.device
+    o = dict(out or {})
+    o.setdefault("h_perm", torch.empty((R_cap, I), dtype=x.dtype, device=dev))
+    o.setdefault("y_perm", torch.empty((R_cap, H), dtype=x.dtype, device=dev))
+    if save_gu:
+        o.setdefault("gu", torch.empty((R_cap, 2 * I), dtype=x.dtype, device=dev))
+    else:
+        o["gu"] = None
+    ws = _ws(workspace_bytes(MOE_OP_FFN_FWD, max(R_cap, 0), H, I, max(E_l, 1), 1, 0, E_l, dt), dev, ws)
+    _check(lib.moe_grouped_ffn_fwd_gather(_ptr(x), _ptr(src_row), _ptr(offsets), E_l, R_cap, T, H, I,
+                                          _ptr(w_gate), _ptr(w_up), _ptr(w_down), dt, _ptr(o["gu"]),
+                                          _ptr(o["h_perm"]), _ptr(o["y_perm"]), _ptr(ws), _nbytes(ws),
+                                          _stream()), "moe_grouped_ffn_fwd_gather")
     return o
 
 

@@ -288,11 +288,13 @@ int moe_permute(const void* x, const int32_t* topk_idx, int T, int H, int E, int
   if (int rc = check_ptr(counts, "counts", fn)) return rc;
   if (int rc = check_ptr(offsets, "offsets", fn)) return rc;
   if (T > 0) {
-    if (int rc = check_ptr(x, "x", fn, true)) return rc;
     if (int rc = check_ptr(topk_idx, "topk_idx", fn)) return rc;
     if (int rc = check_ptr(dest_row, "dest_row", fn)) return rc;
     if (int rc = check_ptr(src_row, "src_row", fn)) return rc;
-    if (int rc = check_ptr(x_perm, "x_perm", fn, true)) return rc;
+    if (x_perm != nullptr) {  // NULL: the maps alone
+      if (int rc = check_ptr(x, "x", fn, true)) return rc;
+      if (int rc = check_ptr(x_perm, "x_perm", fn, true)) return rc;
+    }
   }
   const int E_l = e_hi - e_lo;
   if (int rc = check_ws(ws, ws_bytes, permute_ws_bytes(T, k, E_l), fn)) return rc;
@@ -330,6 +332,35 @@ int moe_grouped_ffn_fwd(const void* x_perm, const int32_t* offsets, int E_l, int
                            (const float*)w_up, (const float*)w_down, (float*)gu_saved,
                            (float*)h_perm, (float*)y_perm, s);
   return hip_status(e, fn);
+}
+
+int moe_grouped_ffn_fwd_gather(const void* x, const int32_t* src_row, const int32_t* offsets,
+                               int E_l, int R_cap, int T, int H, int I, const void* w_gate,
+                               const void* w_up, const void* w_down, int dtype, void* gu_saved,
+                               void* h_perm, void* y_perm, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "moe_grouped_ffn_fwd_gather";
+  if (int rc = check_dtype(dtype, fn)) return rc;
+  if (dtype != MOE_BF16) return fail(MOE_EUNSUPPORTED, "%s: bf16 only", fn);
+  if (int rc = check_ffn_shape(E_l, R_cap, H, I, dtype, fn)) return rc;
+  if (T < 0) return fail(MOE_EINVAL, "%s: T must be >= 0 (got %d)", fn, T);
+  if (int rc = check_range((int64_t)T * H * 2, "x", fn)) return rc;
+  if (int rc = check_ptr(offsets, "offsets", fn)) return rc;
+  if (int rc = check_ptr(w_gate, "w_gate", fn, true)) return rc;
+  if (int rc = check_ptr(w_up, "w_up", fn, true)) return rc;
+  if (int rc = check_ptr(w_down, "w_down", fn, true)) return rc;
+  if (R_cap > 0) {
+    if (int rc = check_ptr(x, "x", fn, true)) return rc;
+    if (int rc = check_ptr(src_row, "src_row", fn)) return rc;
+    if (int rc = check_ptr(h_perm, "h_perm", fn, true)) return rc;
+    if (int rc = check_ptr(y_perm, "y_perm", fn, true)) return rc;
+  }
+  if (int rc = check_ws(ws, ws_bytes, ws_ffn_fwd(R_cap, E_l, dtype), fn)) return rc;
+  if (R_cap == 0) return MOE_OK;
+  return hip_status(launch_ffn_fwd_bf16((const bf16_t*)x, offsets, E_l, R_cap, H, I,
+                                        (const bf16_t*)w_gate, (const bf16_t*)w_up,
+                                        (const bf16_t*)w_down, (bf16_t*)gu_saved, (bf16_t*)h_perm,
+                                        (bf16_t*)y_perm, ws, begin_launch(stream), src_row, T),
+                    fn);
 }
 
 int moe_grouped_ffn_fwd_noalloc(const void* x_perm, const int32_t* offsets, int E_l, int R_cap,

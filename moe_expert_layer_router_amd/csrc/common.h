@@ -192,10 +192,12 @@ bool dw_router_folds(int E);
 size_t ffn_sched_bytes(int R_cap, int E_l);
 // The weight gradients' split plans and partial slots (FFN backward workspace).
 size_t ffn_wgrad_split_bytes(int E_l, int H, int I);
+// x_rows null: x_perm holds the grouped rows; else x_perm is the token matrix
+// x [T, H] and grouped row r is its row x_rows[r] (the permutation's src_row)
 hipError_t launch_ffn_fwd_bf16(const bf16_t* x_perm, const int32_t* offsets, int E_l, int R_cap,
                                int H, int I, const bf16_t* w_gate, const bf16_t* w_up,
                                const bf16_t* w_down, bf16_t* gu, bf16_t* h_perm, bf16_t* y_perm,
-                               void* ws, hipStream_t s);
+                               void* ws, hipStream_t s, const int32_t* x_rows = nullptr, int T = 0);
 // The same with the tile table in the library's static per-GPU scratch (no
 // workspace argument); R_cap <= kNoAllocMaxRows.
 constexpr int kNoAllocMaxRows = 1 << 20;

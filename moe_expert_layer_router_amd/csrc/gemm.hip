@@ -157,6 +157,11 @@ constexpr bool k_grouped(int kind) { return kind == K_WGRAD || kind == K_WGRAD8;
 struct GemmArgs {
   const bf16_t* a;
   long lda;
+  // M-grouped products with a K-contiguous A: null = A row r is row r of a;
+  // else A row r is row a_rows[r] of a, which has a_nrows rows (the grouped
+  // FFN forward reading the token rows in place of their permuted copy)
+  const int32_t* a_rows;
+  int a_nrows;
   const bf16_t* b0;  // B operand (gate / the only one)
   const bf16_t* b1;  // second B tensor (up), or null
   long ldb;
@@ -1362,14 +1367,30 @@ __device__ __forceinline__ void setup_operands(const GemmArgs& p, const Tile& t,
     return;
   }
   if constexpr (Tr::A_KC) {
-    // the tile's rows [row0, row1) of A; rows past row1 read as zero
-    opA.rsrc = make_rsrc(p.a + (long)row0 * p.lda, (uint32_t)((row1 - row0) * p.lda * 2));
     opA.kstep = 2;
+    if (!k_grouped(KIND) && p.a_rows != nullptr) {  // uniform
+      // the tile's rows gathered: DMA row r reads row a_rows[row0 + r] of a;
+      // rows past row1 take the kill offset and read as zero.  (The K loop
+      // of the previous tile has drained the memory counter, so these index
+      // loads are the only memory operations in flight here.)
+      opA.rsrc = make_rsrc(p.a, (uint32_t)((long)p.a_nrows * p.lda * 2));
 #pragma unroll
-    for (int u = 0; u < NIA; ++u) {
-      int r, c;
-      kc_rows<NIA, BKX>(wave, lane, u, r, c);
-      opA.voff[u] = (uint32_t)(r * p.lda * 2 + c * 16);
+      for (int u = 0; u < NIA; ++u) {
+        int r, c;
+        kc_rows<NIA, BKX>(wave, lane, u, r, c);
+        const bool in = row0 + r < row1;
+        const int g = p.a_rows[in ? row0 + r : row0];
+        opA.voff[u] = in ? (uint32_t)((long)g * p.lda * 2 + c * 16) : kDmaKill;
+      }
+    } else {
+      // the tile's rows [row0, row1) of A; rows past row1 read as zero
+      opA.rsrc = make_rsrc(p.a + (long)row0 * p.lda, (uint32_t)((row1 - row0) * p.lda * 2));
+#pragma unroll
+      for (int u = 0; u < NIA; ++u) {
+        int r, c;
+        kc_rows<NIA, BKX>(wave, lane, u, r, c);
+        opA.voff[u] = (uint32_t)(r * p.lda * 2 + c * 16);
+      }
     }
   } else {  // WGRAD: A[k = row of the group][m]; rows past the group read as zero
     opA.rsrc = make_rsrc(p.a + (long)kbeg * p.lda, (uint32_t)((kend - kbeg) * p.lda * 2));
@@ -1981,7 +2002,7 @@ static hipError_t launch_gemm(const GemmArgs& a, int work_upper, int kernel_id, 
 hipError_t launch_ffn_fwd_bf16(const bf16_t* x_perm, const int32_t* offsets, int E_l, int R_cap,
                                int H, int I, const bf16_t* w_gate, const bf16_t* w_up,
                                const bf16_t* w_down, bf16_t* gu, bf16_t* h_perm, bf16_t* y_perm,
-                               void* ws, hipStream_t s) {
+                               void* ws, hipStream_t s, const int32_t* x_rows, int T) {
   int32_t* sched = (int32_t*)ws;
   ffn_sched_kernel<<<1, kMaxE, 0, s>>>(offsets, E_l, kBmGrouped, sched, nullptr);
   hipError_t err = hipGetLastError();
@@ -1991,6 +2012,8 @@ hipError_t launch_ffn_fwd_bf16(const bf16_t* x_perm, const int32_t* offsets, int
   GemmArgs g{};
   g.a = x_perm;
   g.lda = H;
+  g.a_rows = x_rows;  // null: x_perm holds the grouped rows; else x = the token rows
+  g.a_nrows = T;
   g.b0 = w_gate;
   g.b1 = w_up;
   g.ldb = H;

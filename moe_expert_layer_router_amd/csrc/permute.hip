@@ -15,7 +15,8 @@
 //     row of every (block, expert) pair.
 //  3. scatter: one wave per token computes its k destination rows and, if
 //     any slot is local, copies the token row once from HBM into its grouped
-//     rows with 16-byte vectors.
+//     rows with 16-byte vectors (or, without a grouped buffer, writes the
+//     maps alone).
 #include "common.h"
 
 namespace moe {
@@ -161,7 +162,9 @@ __global__ __launch_bounds__(kMaxE) void scan_kernel(const int32_t* __restrict__
 
 // One wave per token: destination rows, inverse map, and the row copy.  The
 // token row is read only when at least one of its slots is local, together
-// with the slots' ranks and block bases.
+// with the slots' ranks and block bases.  COPY = false writes the two maps
+// only (a caller whose grouped FFN reads the token rows through src_row).
+template <bool COPY>
 __global__ __launch_bounds__(256) void scatter_kernel(const u32x4_t* __restrict__ x,
                                                       const int32_t* __restrict__ idx,
                                                       const int32_t* __restrict__ rank,
@@ -187,6 +190,13 @@ __global__ __launch_bounds__(256) void scatter_kernel(const u32x4_t* __restrict_
   }
   int dest = -1;
   if (e >= 0) dest = base[(size_t)b * E_l + e] + rank[(size_t)t * k + lane];
+  if constexpr (!COPY) {
+    if (lane < k) {
+      dest_row[(size_t)t * k + lane] = dest;
+      if (dest >= 0) src_row[dest] = t;
+    }
+    return;
+  }
   const u32x4_t* xs = x + (size_t)t * nvec;
   u32x4_t r[CU];
   int v0 = lane;
@@ -242,9 +252,13 @@ hipError_t launch_permute(const void* x, const int32_t* topk_idx, int T, int H, 
   if (T == 0) return hipSuccess;
   const int nvec = H * elem_bytes / 16;
   ProfScope ps(MOE_KERNEL_PERMUTE_SCATTER, s);
-  scatter_kernel<<<(T + 3) / 4, 256, 0, s>>>((const u32x4_t*)x, topk_idx, rank, base, T, k,
-                                              e_lo, E_l, nvec, dest_row, src_row,
-                                              (u32x4_t*)x_perm);
+  if (x_perm != nullptr)
+    scatter_kernel<true><<<(T + 3) / 4, 256, 0, s>>>((const u32x4_t*)x, topk_idx, rank, base, T, k,
+                                                    e_lo, E_l, nvec, dest_row, src_row,
+                                                    (u32x4_t*)x_perm);
+  else
+    scatter_kernel<false><<<(T + 3) / 4, 256, 0, s>>>(nullptr, topk_idx, rank, base, T, k, e_lo, E_l,
+                                                     nvec, dest_row, src_row, nullptr);
   return hipGetLastError();
 }
 

@@ -1,7 +1,9 @@
 """A whole MoE expert layer (forward and backward) over preallocated buffers.
 
 Chains the C-ABI calls in the order of the layer: route -> permute ->
-grouped FFN -> combine, and for the backward the router weight's transpose ->
+grouped FFN -> combine (a bf16 layer built for the forward alone permutes the
+maps only and its FFN reads the token rows through src_row), and for the
+backward the router weight's transpose ->
 combine_bwd -> grouped FFN backward -> unweighted combine of dx_perm plus the
 router's dx (on that transpose) -> route_bwd.
 All buffers and workspaces are allocated once in the constructor, so
@@ -42,7 +44,8 @@ def _p(t: Optional[torch.Tensor]):
 
 class MoELayer:
     def __init__(self, T: int, H: int, I: int, E: int, k: int, e_lo: int, e_hi: int,
-                 dtype: torch.dtype, device="cuda", train: bool = True, fp8: bool = False):
+                 dtype: torch.dtype, device="cuda", train: bool = True, fp8: bool = False,
+                 gather: Optional[bool] = None):
         if fp8 and (dtype != torch.bfloat16 or H % 128 or I % 128 or I > 2048):
             raise ValueError("the FP8 layer needs bf16 tensors, H % 128 == 0, I % 128 == 0 "
                              "and I <= 2048")
@@ -64,8 +67,15 @@ class MoELayer:
         b["offsets"] = torch.empty(E_l + 1, dtype=i32, device=dev)
         b["dest_row"] = torch.empty(T * k, dtype=i32, device=dev)
         b["src_row"] = torch.empty(T * k, dtype=i32, device=dev)
-        # (FP8: the permute moves code rows, so bf16 x_perm is not materialised)
-        b["x_perm"] = None if fp8 else torch.empty((R, H), dtype=dtype, device=dev)
+        # A bf16 layer built for the forward alone reads the token rows through
+        # src_row in its first product (moe_grouped_ffn_fwd_gather): no grouped
+        # copy.  (FP8: the permute moves code rows; training keeps x_perm for
+        # the weight gradients.)
+        can_gather = not train and not fp8 and dtype == torch.bfloat16
+        if gather and not can_gather:
+            raise ValueError("gather=True needs a bf16 layer built for the forward alone (not fp8)")
+        self.gather = can_gather if gather is None else bool(gather)
+        b["x_perm"] = None if (fp8 or self.gather) else torch.empty((R, H), dtype=dtype, device=dev)
         b["h_perm"] = torch.empty((R, I), dtype=dtype, device=dev)
         b["y_perm"] = torch.empty((R, H), dtype=dtype, device=dev)
         b["gu"] = torch.empty((R, 2 * I), dtype=dtype, device=dev) if train else None
@@ -133,6 +143,16 @@ class MoELayer:
                              _p(b["topk_w"]), ws, wsb, s), "moe_route")
         if self.fp8:
             self._forward_ffn_fp8(x, w_gate, w_up, w_down, ws, wsb, s)
+        elif self.gather:
+            # the maps alone, then the FFN reads x through src_row
+            _check(lib.moe_permute(_p(x), _p(b["topk_idx"]), T, H, E, k, self.e_lo, self.e_hi,
+                                   self.dt, _p(b["counts"]), _p(b["offsets"]), _p(b["dest_row"]),
+                                   _p(b["src_row"]), None, ws, wsb, s), "moe_permute")
+            _check(lib.moe_grouped_ffn_fwd_gather(_p(x), _p(b["src_row"]), _p(b["offsets"]), self.E_l,
+                                                  self.R_cap, T, H, I, _p(w_gate), _p(w_up),
+                                                  _p(w_down), self.dt, _p(b["gu"]), _p(b["h_perm"]),
+                                                  _p(b["y_perm"]), ws, wsb, s),
+                   "moe_grouped_ffn_fwd_gather")
         else:
             _check(lib.moe_permute(_p(x), _p(b["topk_idx"]), T, H, E, k, self.e_lo, self.e_hi,
                                    self.dt, _p(b["counts"]), _p(b["offsets"]), _p(b["dest_row"]),

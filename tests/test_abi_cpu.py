@@ -50,7 +50,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_single_hip_runtime():
-    assert L.moe_abi_version() == moe.ABI_VERSION == 9
+    assert L.moe_abi_version() == moe.ABI_VERSION == 10
     libs = moe.hip_runtimes_mapped()
     assert len(libs) <= 1, libs
 
@@ -134,6 +134,23 @@ def test_ffn_fwd_errors():
     assert f(A, A, 16, 512, 128, 64, A, A, A, BF16, N, N, A, A, big, S) == EINVAL and "h_perm" in _err()
     assert f(A, A, 16, 512, 128, 64, A, A, A, BF16, N, A, A, A, 4, S) == EWS
     assert f(A, A, 16, 0, 128, 64, A, A, A, BF16, N, N, N, A, big, S) == OK            # nothing routed
+
+
+def test_ffn_fwd_gather_errors():
+    """The gathering forward: bf16 only, a src_row map when rows are routed, the
+    token matrix below 2 GiB, and the forward's own shape and workspace checks."""
+    g = lambda *a: L.moe_grouped_ffn_fwd_gather(*a)
+    big = 1 << 30
+    # (x, src_row, offsets, E_l, R_cap, T, H, I, w_gate, w_up, w_down, dtype, gu, h, y, ws, ws_bytes, s)
+    assert g(A, A, A, 16, 512, 64, 128, 64, A, A, A, F32, N, A, A, A, big, S) == EUNSUP and "bf16" in _err()
+    assert g(A, N, A, 16, 512, 64, 128, 64, A, A, A, BF16, N, A, A, A, big, S) == EINVAL and "src_row" in _err()
+    assert g(N, A, A, 16, 512, 64, 128, 64, A, A, A, BF16, N, A, A, A, big, S) == EINVAL and "x" in _err()
+    assert g(A, A, A, 16, 512, -1, 128, 64, A, A, A, BF16, N, A, A, A, big, S) == EINVAL
+    assert g(A, A, A, 16, 512, 1 << 19, 2048, 64, A, A, A, BF16, N, A, A, A, big, S) == EUNSUP
+    assert "x spans" in _err()
+    assert g(A, A, A, 16, 512, 64, 128, 96, A, A, A, BF16, N, A, A, A, big, S) == EUNSUP     # I % 64
+    assert g(A, A, A, 16, 512, 64, 128, 64, A, A, A, BF16, N, A, A, A, 4, S) == EWS
+    assert g(N, N, A, 16, 0, 0, 128, 64, A, A, A, BF16, N, N, N, A, big, S) == OK            # nothing routed
 
 
 def test_operand_ranges_below_2gib():

@@ -398,6 +398,59 @@ def test_forward_matches_oracle(w):
     chk.done()
 
 
+GATHER_CASES = [EP_SHARE, FULL, SKEWED,
+                EP_SHARE.scaled(name="ragged_bf16_t1000_h192_i128_e24_k3", T=1000, H=192, I=128, E=24,
+                                k=3, e_lo=5, e_hi=21),
+                # more gate/up tiles than persistent workgroups (second and later
+                # tiles gather their rows during the previous tile's epilogue)
+                EP_SHARE.scaled(name="gather_multitile_t4096_e16_all_local", T=4096, E=16, k=8,
+                                e_lo=0, e_hi=16)]
+
+
+@pytest.mark.parametrize("w", GATHER_CASES, ids=lambda w: w.name)
+def test_forward_gather_equals_permuted_forward(w):
+    """moe_permute without x_perm writes the same maps, and the grouped FFN
+    reading the token rows through src_row gives the same bits as the forward
+    on the permuted copy (the same products over the same rows), rows >= R
+    untouched."""
+    inp = _inputs(w)
+    t = _gpu_tensors(w, inp)
+    idx_t, gw_t, lg_t, p, f, y = run_forward(w, t)
+    q = moe.moe_permute(t["x"], idx_t, w.E, w.e_lo, w.e_hi, copy_rows=False)
+    for n in ("counts", "offsets", "dest_row"):
+        assert torch.equal(q[n], p[n]), n
+    R = int(p["offsets"][-1].item())
+    assert torch.equal(q["src_row"][:R], p["src_row"][:R])
+    assert q["x_perm"] is None
+    R_cap, dt, nan = w.T * w.k, t["x"].dtype, float("nan")
+    guard = {"h_perm": torch.full((R_cap, w.I), nan, dtype=dt, device=DEV),
+             "y_perm": torch.full((R_cap, w.H), nan, dtype=dt, device=DEV),
+             "gu": torch.full((R_cap, 2 * w.I), nan, dtype=dt, device=DEV)}
+    fg = moe.moe_grouped_ffn_fwd_gather(t["x"], q["src_row"], q["offsets"], t["w_gate"], t["w_up"],
+                                        t["w_down"], R_cap, save_gu=True, out=guard)
+    torch.cuda.synchronize()
+    for n in ("h_perm", "y_perm", "gu"):
+        assert torch.equal(fg[n][:R].view(torch.int16), f[n][:R].view(torch.int16)), n
+    check_rows_untouched(fg, R, ("h_perm", "y_perm", "gu"))
+    print(f"  R = {R} routed rows, bit-equal to the permuted forward", flush=True)
+
+
+def test_inference_layer_gathers_and_equals_training_forward():
+    """MoELayer(train=False) runs the maps-only permute and the gathering FFN
+    forward; its output equals the training layer's forward bit for bit."""
+    w = EP_SHARE
+    inp = _inputs(w)
+    t = _gpu_tensors(w, inp)
+    a = moe.MoELayer(w.T, w.H, w.I, w.E, w.k, w.e_lo, w.e_hi, t["x"].dtype, DEV, train=False)
+    b = moe.MoELayer(w.T, w.H, w.I, w.E, w.k, w.e_lo, w.e_hi, t["x"].dtype, DEV, train=True)
+    assert a.buf["x_perm"] is None
+    for _ in range(2):  # the second call reuses the layer's buffers
+        ya = a.forward(t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"], bias=t["bias"]).clone()
+        yb = b.forward(t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"], bias=t["bias"])
+        torch.cuda.synchronize()
+        assert torch.equal(ya.view(torch.int16), yb.view(torch.int16))
+
+
 # ----------------------------------------------------------------------------
 # backward
 # ----------------------------------------------------------------------------
