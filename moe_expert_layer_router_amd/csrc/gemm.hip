@@ -1374,13 +1374,21 @@ __device__ __forceinline__ void setup_operands(const GemmArgs& p, const Tile& t,
       // of the previous tile has drained the memory counter, so these index
       // loads are the only memory operations in flight here.)
       opA.rsrc = make_rsrc(p.a, (uint32_t)((long)p.a_nrows * p.lda * 2));
+      // every index load first (rows clamped into the tile, no branch), then
+      // one wait for all of them
+      int g[NIA];
 #pragma unroll
       for (int u = 0; u < NIA; ++u) {
         int r, c;
         kc_rows<NIA, BKX>(wave, lane, u, r, c);
-        const bool in = row0 + r < row1;
-        const int g = p.a_rows[in ? row0 + r : row0];
-        opA.voff[u] = in ? (uint32_t)((long)g * p.lda * 2 + c * 16) : kDmaKill;
+        g[u] = p.a_rows[min(row0 + r, row1 - 1)];
+      }
+#pragma unroll
+      for (int u = 0; u < NIA; ++u) {
+        int r, c;
+        kc_rows<NIA, BKX>(wave, lane, u, r, c);
+        const uint32_t o = (uint32_t)(g[u] * (uint32_t)p.lda * 2u + (uint32_t)c * 16u);
+        opA.voff[u] = row0 + r < row1 ? o : kDmaKill;
       }
     } else {
       // the tile's rows [row0, row1) of A; rows past row1 read as zero
