@@ -222,6 +222,19 @@ int moe_grouped_ffn_fwd_fp8(const uint8_t* x_q, const float* x_scale, const int3
                             void* gu_saved, void* h_perm, void* y_perm, void* ws, size_t ws_bytes,
                             void* stream);
 
+/* moe_grouped_ffn_fwd_fp8 with the permutation folded into the gate/up
+ * product's operand loads (as moe_grouped_ffn_fwd_gather does in bf16): x_q
+ * holds the T token code rows [T,H] of moe_quantize_fp8 and grouped row r is
+ * x_q[src_row[r]], so moe_permute (MOE_FP8) needs no x_perm.  Results, rounding
+ * and workspace are moe_grouped_ffn_fwd_fp8's: the same products over the
+ * same code rows, the same bits.  T*H < 2^31. */
+int moe_grouped_ffn_fwd_fp8_gather(const uint8_t* x_q, const float* x_scale, const int32_t* src_row,
+                                   const int32_t* offsets, int E_l, int R_cap, int T, int H, int I,
+                                   const uint8_t* wg_q, const float* wg_scale, const uint8_t* wu_q,
+                                   const float* wu_scale, const uint8_t* wd_q, const float* wd_scale,
+                                   void* gu_saved, void* h_perm, void* y_perm, void* ws,
+                                   size_t ws_bytes, void* stream);
+
 /* Per-input-channel E4M3 codes of expert weights, for the FP8 data
  * gradients (same scale rule as moe_quantize_fp8, applied to the columns):
  * with src0 (and src1, or NULL) [batch,N,K] bf16, row k of batch b of the

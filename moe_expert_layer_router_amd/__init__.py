@@ -69,6 +69,8 @@ def _load():
         "moe_quantize_fp8": ([P, I32, I32, I32, P, P, P, P], I32),
         "moe_quantize_fp8_t": ([P, P, I32, I32, I32, I32, P, P, P], I32),
         "moe_grouped_ffn_dgrad_fp8": ([P, P, P, P, I32, I32, I32, I32, P, P, P, P, P, P, P, SZ, P], I32),
+        "moe_grouped_ffn_fwd_fp8_gather": ([P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P,
+                                            P, P, SZ, P], I32),
         "moe_grouped_ffn_fwd_fp8": ([P, P, P, P, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, P,
                                      SZ, P], I32),
         "moe_quantize_fp8_group_t": ([P, P, I32, P, I32, I32, P, I32, P, P, P], I32),
@@ -400,12 +402,15 @@ def moe_quantize_fp8(src: torch.Tensor, nrows: Optional[torch.Tensor] = None,
 def moe_grouped_ffn_fwd_fp8(x_q: torch.Tensor, x_scale: torch.Tensor, src_row: torch.Tensor,
                             offsets: torch.Tensor, wg: tuple, wu: tuple, wd: tuple,
                             save_gu: bool = False, ws: Optional[torch.Tensor] = None,
-                            out: Optional[Dict[str, torch.Tensor]] = None):
+                            out: Optional[Dict[str, torch.Tensor]] = None, R_cap: Optional[int] = None):
     """Grouped SwiGLU FFN forward on E4M3 codes.  x_q [R_cap, H] uint8 (permuted
     rows), x_scale [T] per-token scales, src_row [R_cap]; wg / wu / wd = (codes
     uint8 [E_l, N, K], scales fp32 [E_l, N]).  Returns dict h_perm, y_perm (bf16)
-    and gu (or None)."""
-    R_cap, H = x_q.shape
+    and gu (or None).  With R_cap given, x_q is the token code rows [T, H] read
+    through src_row (moe_grouped_ffn_fwd_fp8_gather)."""
+    gather = R_cap is not None
+    T, H = x_q.shape
+    R_cap = R_cap if gather else T
     E_l, I, _ = wg[0].shape
     dev = x_q.device
     o = dict(out or {})
@@ -420,6 +425,13 @@ def moe_grouped_ffn_fwd_fp8(x_q: torch.Tensor, x_scale: torch.Tensor, src_row: t
     if nb < 0:
         _check(int(nb), "moe_workspace_bytes")
     ws = _ws(int(nb), dev, ws)
+    if gather:
+        _check(lib.moe_grouped_ffn_fwd_fp8_gather(
+            _ptr(x_q), _ptr(x_scale), _ptr(src_row), _ptr(offsets), E_l, R_cap, T, H, I, _ptr(wg[0]),
+            _ptr(wg[1]), _ptr(wu[0]), _ptr(wu[1]), _ptr(wd[0]), _ptr(wd[1]), _ptr(o["gu"]),
+            _ptr(o["h_perm"]), _ptr(o["y_perm"]), _ptr(ws), _nbytes(ws), _stream()),
+            "moe_grouped_ffn_fwd_fp8_gather")
+        return o
     _check(lib.moe_grouped_ffn_fwd_fp8(_ptr(x_q), _ptr(x_scale), _ptr(src_row), _ptr(offsets), E_l,
                                        R_cap, H, I, _ptr(wg[0]), _ptr(wg[1]), _ptr(wu[0]),
                                        _ptr(wu[1]), _ptr(wd[0]), _ptr(wd[1]), _ptr(o["gu"]),

@@ -448,6 +448,41 @@ int moe_grouped_ffn_fwd_fp8(const uint8_t* x_q, const float* x_scale, const int3
                     fn);
 }
 
+int moe_grouped_ffn_fwd_fp8_gather(const uint8_t* x_q, const float* x_scale, const int32_t* src_row,
+                                   const int32_t* offsets, int E_l, int R_cap, int T, int H, int I,
+                                   const uint8_t* wg_q, const float* wg_scale, const uint8_t* wu_q,
+                                   const float* wu_scale, const uint8_t* wd_q, const float* wd_scale,
+                                   void* gu_saved, void* h_perm, void* y_perm, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  const char* fn = "moe_grouped_ffn_fwd_fp8_gather";
+  if (int rc = check_ffn_shape(E_l, R_cap, H, I, MOE_FP8, fn)) return rc;
+  if (H % 128 != 0 || I % 128 != 0)
+    return fail(MOE_EUNSUPPORTED, "%s: needs H %% 128 == 0 and I %% 128 == 0 (H=%d, I=%d)", fn, H, I);
+  if (T < 0) return fail(MOE_EINVAL, "%s: T must be >= 0 (got %d)", fn, T);
+  if (int rc = check_range((int64_t)T * H, "x_q", fn)) return rc;
+  if (int rc = check_ptr(offsets, "offsets", fn)) return rc;
+  if (int rc = check_ptr(wg_q, "wg_q", fn, true)) return rc;
+  if (int rc = check_ptr(wu_q, "wu_q", fn, true)) return rc;
+  if (int rc = check_ptr(wd_q, "wd_q", fn, true)) return rc;
+  if (int rc = check_ptr(wg_scale, "wg_scale", fn, true)) return rc;
+  if (int rc = check_ptr(wu_scale, "wu_scale", fn, true)) return rc;
+  if (int rc = check_ptr(wd_scale, "wd_scale", fn, true)) return rc;
+  if (R_cap > 0) {
+    if (int rc = check_ptr(x_q, "x_q", fn, true)) return rc;
+    if (int rc = check_ptr(x_scale, "x_scale", fn)) return rc;
+    if (int rc = check_ptr(src_row, "src_row", fn)) return rc;
+    if (int rc = check_ptr(h_perm, "h_perm", fn, true)) return rc;
+    if (int rc = check_ptr(y_perm, "y_perm", fn, true)) return rc;
+  }
+  if (gu_saved != nullptr && !aligned16(gu_saved)) return fail(MOE_EINVAL, "%s: gu_saved must be 16-byte aligned", fn);
+  if (int rc = check_ws(ws, ws_bytes, ffn_fwd_fp8_ws_bytes(R_cap, E_l, I), fn)) return rc;
+  if (R_cap == 0) return MOE_OK;
+  return hip_status(launch_ffn_fwd_fp8(x_q, x_scale, src_row, offsets, E_l, R_cap, H, I, wg_q,
+                                       wg_scale, wu_q, wu_scale, wd_q, wd_scale, (bf16_t*)gu_saved,
+                                       (bf16_t*)h_perm, (bf16_t*)y_perm, ws, begin_launch(stream), T),
+                    fn);
+}
+
 int moe_quantize_fp8_t(const void* src0, const void* src1, int batch, int N, int K, int dtype,
                        uint8_t* q, float* scale, void* stream) {
   const char* fn = "moe_quantize_fp8_t";

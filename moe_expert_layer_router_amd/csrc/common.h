@@ -211,7 +211,8 @@ hipError_t launch_ffn_fwd_fp8(const uint8_t* x_q, const float* x_scale, const in
                               const int32_t* offsets, int E_l, int R_cap, int H, int I,
                               const uint8_t* wg_q, const float* wg_s, const uint8_t* wu_q,
                               const float* wu_s, const uint8_t* wd_q, const float* wd_s,
-                              bf16_t* gu, bf16_t* h_perm, bf16_t* y_perm, void* ws, hipStream_t s);
+                              bf16_t* gu, bf16_t* h_perm, bf16_t* y_perm, void* ws, hipStream_t s,
+                              int gather_T = -1);  // >= 0: x_q holds the T token rows, read through src_row
 hipError_t launch_quantize_fp8(const void* src, int rows, int cols, bool bf16,
                                const int32_t* nrows, uint8_t* q, float* scale, hipStream_t s);
 // per-input-channel (transposed) weight codes and the SiLU derivative + row

@@ -2121,7 +2121,7 @@ hipError_t launch_ffn_fwd_fp8(const uint8_t* x_q, const float* x_scale, const in
                               const uint8_t* wg_q, const float* wg_s, const uint8_t* wu_q,
                               const float* wu_s, const uint8_t* wd_q, const float* wd_s,
                               bf16_t* gu, bf16_t* h_perm, bf16_t* y_perm, void* ws,
-                              hipStream_t s) {
+                              hipStream_t s, int gather_T) {
   char* w = (char*)ws;
   int32_t* sched = (int32_t*)w;
   w += ffn_sched_bytes(R_cap, E_l);
@@ -2143,6 +2143,10 @@ hipError_t launch_ffn_fwd_fp8(const uint8_t* x_q, const float* x_scale, const in
   GemmArgs g{};
   g.a = (const bf16_t*)x_q;
   g.lda = H / 2;
+  if (gather_T >= 0) {  // token code rows, grouped row r = row src_row[r]
+    g.a_rows = src_row;
+    g.a_nrows = gather_T;
+  }
   g.b0 = (const bf16_t*)wg_q;
   g.b1 = (const bf16_t*)wu_q;
   g.ldb = H / 2;

@@ -15,8 +15,9 @@ workspace, and the current stream waits for the second one before
 backward() returns.
 
 With fp8=True the expert FFN runs the library's FP8 recipe (E4M3 codes with
-power-of-two scales): tokens are quantized per row before the permute (which
-then moves code rows); every forward quantizes the weights per output channel
+power-of-two scales): tokens are quantized per row, the permute writes its maps
+alone and the FP8 gate/up product reads the token code rows through src_row;
+every forward quantizes the weights per output channel
 and, for training, per input channel as well (both layouts in one pass pair,
 on the second stream beside routing and permute; the backward uses these
 codes, so it must be given the forward's weights); the
@@ -69,7 +70,8 @@ class MoELayer:
         b["src_row"] = torch.empty(T * k, dtype=i32, device=dev)
         # A bf16 layer built for the forward alone reads the token rows through
         # src_row in its first product (moe_grouped_ffn_fwd_gather): no grouped
-        # copy.  (FP8: the permute moves code rows; training keeps x_perm for
+        # copy.  (FP8: the permute writes maps only, its FFN gathers the token
+        # code rows the same way; training keeps x_perm for
         # the weight gradients.)
         can_gather = not train and not fp8 and dtype == torch.bfloat16
         if gather and not can_gather:
@@ -95,7 +97,6 @@ class MoELayer:
             u8 = torch.uint8
             b["x_q"] = torch.empty((T, H), dtype=u8, device=dev)
             b["x_scale"] = torch.empty(T, dtype=f32, device=dev)
-            b["xq_perm"] = torch.empty((R, H), dtype=u8, device=dev)
             b["wg_q"] = torch.empty((E_l, I, H), dtype=u8, device=dev)
             b["wu_q"] = torch.empty((E_l, I, H), dtype=u8, device=dev)
             b["wd_q"] = torch.empty((E_l, H, I), dtype=u8, device=dev)
@@ -188,20 +189,21 @@ class MoELayer:
                                       _p(b["wdt_s"]) if tr else None, ws, wsb, side), "moe_quantize_fp8_w")
 
     def _forward_ffn_fp8(self, x, w_gate, w_up, w_down, ws, wsb, s):
-        """Token rows quantized, code rows permuted, then (once the side
-        stream's weight codes are there) the FP8 grouped FFN (h, g and u kept in
-        bf16)."""
+        """Token rows quantized, the permutation's maps, then (once the side
+        stream's weight codes are there) the FP8 grouped FFN reading the token
+        code rows through src_row (h, g and u kept in bf16)."""
         b, T, H, I, E, k, E_l = self.buf, self.T, self.H, self.I, self.E, self.k, self.E_l
         self._quantize_rows(x, T, H, b["x_q"], b["x_scale"], s)
-        _check(lib.moe_permute(_p(b["x_q"]), _p(b["topk_idx"]), T, H, E, k, self.e_lo, self.e_hi,
+        _check(lib.moe_permute(None, _p(b["topk_idx"]), T, H, E, k, self.e_lo, self.e_hi,
                                MOE_FP8, _p(b["counts"]), _p(b["offsets"]), _p(b["dest_row"]),
-                               _p(b["src_row"]), _p(b["xq_perm"]), ws, wsb, s), "moe_permute")
+                               _p(b["src_row"]), None, ws, wsb, s), "moe_permute")
         torch.cuda.current_stream().wait_stream(self.side)
-        _check(lib.moe_grouped_ffn_fwd_fp8(_p(b["xq_perm"]), _p(b["x_scale"]), _p(b["src_row"]),
-                                           _p(b["offsets"]), E_l, self.R_cap, H, I, _p(b["wg_q"]),
-                                           _p(b["wg_s"]), _p(b["wu_q"]), _p(b["wu_s"]), _p(b["wd_q"]),
-                                           _p(b["wd_s"]), _p(b["gu"]), _p(b["h_perm"]),
-                                           _p(b["y_perm"]), ws, wsb, s), "moe_grouped_ffn_fwd_fp8")
+        _check(lib.moe_grouped_ffn_fwd_fp8_gather(_p(b["x_q"]), _p(b["x_scale"]), _p(b["src_row"]),
+                                                  _p(b["offsets"]), E_l, self.R_cap, T, H, I,
+                                                  _p(b["wg_q"]), _p(b["wg_s"]), _p(b["wu_q"]),
+                                                  _p(b["wu_s"]), _p(b["wd_q"]), _p(b["wd_s"]),
+                                                  _p(b["gu"]), _p(b["h_perm"]), _p(b["y_perm"]), ws,
+                                                  wsb, s), "moe_grouped_ffn_fwd_fp8_gather")
 
     def _route_bwd(self, x, w_router, stream):
         b, T, H, E, k = self.buf, self.T, self.H, self.E, self.k

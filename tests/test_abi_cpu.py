@@ -153,6 +153,19 @@ def test_ffn_fwd_gather_errors():
     assert g(N, N, A, 16, 0, 0, 128, 64, A, A, A, BF16, N, N, N, A, big, S) == OK            # nothing routed
 
 
+def test_ffn_fwd_fp8_gather_errors():
+    g = lambda *a: L.moe_grouped_ffn_fwd_fp8_gather(*a)
+    big = 1 << 30
+    # (x_q, x_scale, src_row, offsets, E_l, R_cap, T, H, I, wg, wgs, wu, wus, wd, wds, gu, h, y, ws, nb, s)
+    assert g(A, A, N, A, 16, 512, 64, 256, 128, A, A, A, A, A, A, N, A, A, A, big, S) == EINVAL and "src_row" in _err()
+    assert g(A, A, A, A, 16, 512, 64, 192, 128, A, A, A, A, A, A, N, A, A, A, big, S) == EUNSUP      # H % 128
+    assert g(A, A, A, A, 16, 512, -1, 256, 128, A, A, A, A, A, A, N, A, A, A, big, S) == EINVAL
+    assert g(A, A, A, A, 16, 512, 1 << 20, 2048, 128, A, A, A, A, A, A, N, A, A, A, big, S) == EUNSUP
+    assert "x_q spans" in _err()
+    assert g(A, A, A, A, 16, 512, 64, 256, 128, A, A, A, A, A, A, N, A, A, A, 4, S) == EWS
+    assert g(N, N, N, A, 16, 0, 0, 256, 128, A, A, A, A, A, A, N, N, N, A, big, S) == OK    # nothing routed
+
+
 def test_operand_ranges_below_2gib():
     """The matrix-core kernels address operands with 32-bit byte ranges: shapes whose
     grouped-row buffers, expert weights or router input reach 2 GiB are refused on

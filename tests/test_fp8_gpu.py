@@ -132,11 +132,20 @@ def test_ffn_fwd_fp8_matches_oracle(w):
              "gu": torch.full((R_cap, 2 * w.I), nan, dtype=bf, device=DEV)}
     out = moe.moe_grouped_ffn_fwd_fp8(perm["x_perm"], sx, perm["src_row"], perm["offsets"],
                                       wq["w_gate"], wq["w_up"], wq["w_down"], save_gu=True, out=guard)
+    # the same forward reading the token code rows through src_row (the permute's
+    # maps alone): the same bits, rows >= R untouched
+    maps = moe.moe_permute(xq, torch.from_numpy(idx.astype(np.int32)).to(DEV), w.E, w.e_lo, w.e_hi,
+                           copy_rows=False)
+    guard2 = {n: torch.full_like(v, nan) for n, v in guard.items()}
+    out2 = moe.moe_grouped_ffn_fwd_fp8(xq, sx, maps["src_row"], maps["offsets"], wq["w_gate"],
+                                       wq["w_up"], wq["w_down"], save_gu=True, out=guard2, R_cap=R_cap)
     torch.cuda.synchronize()
     offsets = perm["offsets"].cpu().numpy()
     R = int(offsets[-1])
     for n in guard:
         assert torch.isnan(out[n][R:].float()).all(), f"{n}: rows >= R were written"
+        assert torch.isnan(out2[n][R:].float()).all(), f"{n} (gathering): rows >= R were written"
+        assert torch.equal(out2[n][:R].view(torch.int16), out[n][:R].view(torch.int16)), n
     src_row = perm["src_row"].cpu().numpy()[:R]
     assert np.array_equal(perm["x_perm"][:R].cpu().numpy(), ref_xq[src_row])
     h_got, y_got = _np(out["h_perm"][:R]), _np(out["y_perm"][:R])
