@@ -404,7 +404,11 @@ GATHER_CASES = [EP_SHARE, FULL, SKEWED,
                 # more gate/up tiles than persistent workgroups (second and later
                 # tiles gather their rows during the previous tile's epilogue)
                 EP_SHARE.scaled(name="gather_multitile_t4096_e16_all_local", T=4096, E=16, k=8,
-                                e_lo=0, e_hi=16)]
+                                e_lo=0, e_hi=16),
+                # one local expert (the last one), k = 1: most tokens have no local
+                # slot, and one expert's tiles gather every row
+                EP_SHARE.scaled(name="gather_one_expert_t3000_h128_i64_e8_k1", T=3000, H=128, I=64, E=8,
+                                k=1, e_lo=7, e_hi=8)]
 
 
 @pytest.mark.parametrize("w", GATHER_CASES, ids=lambda w: w.name)
