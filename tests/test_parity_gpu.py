@@ -439,6 +439,54 @@ def test_forward_gather_equals_permuted_forward(w):
     print(f"  R = {R} routed rows, bit-equal to the permuted forward", flush=True)
 
 
+def test_forward_at_the_largest_grouped_buffer():
+    """The largest shape the matrix-core path accepts: x_perm of R_cap = T k
+    rows x 2048 bf16 is 32 KiB short of 2 GiB, and with every expert local
+    the last grouped rows sit at byte offsets just below 2^31 (where the
+    kernels' dropped-load offsets begin).  The gathering forward equals the
+    forward on the copy bit for bit; 96 routed rows, the last ones included,
+    are checked against the oracle."""
+    w = EP_SHARE.scaled(name="max_grouped_t65535_h2048_i768_e16_k8", T=65535, E=16, k=8,
+                        e_lo=0, e_hi=16)
+    R_cap = w.T * w.k
+    assert R_cap * w.H * 2 < 2 ** 31 <= (R_cap + 8) * w.H * 2
+    inp = make_inputs(w)
+    t = _gpu_tensors(w, inp)
+    idx_t, _, _ = moe.moe_route(t["x"], t["w_router"], w.k)
+    nan = float("nan")
+    p = moe.moe_permute(t["x"], idx_t, w.E, w.e_lo, w.e_hi,
+                        out={"x_perm": torch.full((R_cap, w.H), nan, dtype=torch.bfloat16, device=DEV)})
+    outs = []
+    for gather in (False, True):
+        guard = {"h_perm": torch.full((R_cap, w.I), nan, dtype=torch.bfloat16, device=DEV),
+                 "y_perm": torch.full((R_cap, w.H), nan, dtype=torch.bfloat16, device=DEV)}
+        if gather:
+            f = moe.moe_grouped_ffn_fwd_gather(t["x"], p["src_row"], p["offsets"], t["w_gate"], t["w_up"],
+                                               t["w_down"], R_cap, save_gu=False, out=guard)
+        else:
+            f = moe.moe_grouped_ffn_fwd(p["x_perm"], p["offsets"], t["w_gate"], t["w_up"], t["w_down"],
+                                        save_gu=False, out=guard)
+        outs.append(f)
+    torch.cuda.synchronize()
+    R = int(p["offsets"][-1].item())
+    print(f"  R = {R} of capacity {R_cap}; last grouped row at byte {(R - 1) * w.H * 2}", flush=True)
+    assert R == R_cap and R_cap * w.H * 2 > 2 ** 31 - 2 ** 16
+    for n in ("h_perm", "y_perm"):
+        assert torch.equal(outs[1][n][:R].view(torch.int16), outs[0][n][:R].view(torch.int16)), n
+    off = p["offsets"].cpu().numpy()
+    src = p["src_row"][:R].cpu().numpy()
+    rows = np.unique(np.concatenate([np.linspace(0, R - 1, 64).astype(np.int64), np.arange(R - 32, R)]))
+    chk = Checker(w.dtype)
+    for e in range(w.E_l):
+        sel = rows[(rows >= off[e]) & (rows < off[e + 1])]
+        if sel.size == 0:
+            continue
+        m = expert_forward_magnitudes(inp["x"][src[sel]], inp["w_gate"][e], inp["w_up"][e], inp["w_down"][e])
+        chk("h_perm", _np(outs[0]["h_perm"][torch.from_numpy(sel).to(DEV)]), m["h"], m["Mh"])
+        chk("y_perm", _np(outs[0]["y_perm"][torch.from_numpy(sel).to(DEV)]), m["o"], m["Mo"])
+    chk.done()
+
+
 def test_inference_layer_gathers_and_equals_training_forward():
     """MoELayer(train=False) runs the maps-only permute and the gathering FFN
     forward; its output equals the training layer's forward bit for bit."""
