@@ -109,13 +109,14 @@ __global__ __launch_bounds__(kPermBlock) void hist_rank_kernel(const int32_t* __
 }
 
 // One workgroup of kMaxE threads; thread e owns local expert e.  Block counts
-// are read 32 blocks at a time with all loads in flight together.
+// are read 64 blocks at a time with all loads in flight together (one round
+// trip up to 16384 tokens).
 __global__ __launch_bounds__(kMaxE) void scan_kernel(const int32_t* __restrict__ block_counts,
                                                      int nblk, int E_l,
                                                      int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ base) {
-  constexpr int CH = 32;
+  constexpr int CH = 64;
   __shared__ int s[kMaxE / kWave];
   const int e = threadIdx.x;
   const bool own = e < E_l;
