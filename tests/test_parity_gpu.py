@@ -487,6 +487,66 @@ def test_forward_at_the_largest_grouped_buffer():
     chk.done()
 
 
+def test_ffn_backward_at_the_largest_grouped_buffer():
+    """The expert backward at the largest grouped buffer (R_cap = 524280 rows x
+    2048, every expert local, ~32768 rows per expert, so each expert's weight
+    gradients run as several K chunks): sampled rows of dx_perm, the last ones
+    included, and sampled elements of the first and last experts' dW_gate,
+    dW_up and dW_down against the oracle on the same bf16 operands."""
+    w = EP_SHARE.scaled(name="max_grouped_t65535_h2048_i768_e16_k8", T=65535, E=16, k=8,
+                        e_lo=0, e_hi=16)
+    R_cap, H, I = w.T * w.k, w.H, w.I
+    inp = make_inputs(w)
+    t = _gpu_tensors(w, inp)
+    idx_t, _, _ = moe.moe_route(t["x"], t["w_router"], w.k)
+    p = moe.moe_permute(t["x"], idx_t, w.E, w.e_lo, w.e_hi)
+    f = moe.moe_grouped_ffn_fwd(p["x_perm"], p["offsets"], t["w_gate"], t["w_up"], t["w_down"],
+                                save_gu=True)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(0)
+    dy_perm = torch.randn((R_cap, H), generator=gen, device=DEV).to(torch.bfloat16)
+    g = moe.moe_grouped_ffn_bwd(dy_perm, p["x_perm"], f["gu"], f["h_perm"], p["offsets"], t["w_gate"],
+                                t["w_up"], t["w_down"])
+    torch.cuda.synchronize()
+    off = p["offsets"].cpu().numpy()
+    R = int(off[-1])
+    assert R == R_cap
+    wg = [inp["w_gate"][e].astype(np.float64) for e in range(w.E_l)]
+    wu = [inp["w_up"][e].astype(np.float64) for e in range(w.E_l)]
+    wd = [inp["w_down"][e].astype(np.float64) for e in range(w.E_l)]
+    chk = Checker(w.dtype)
+    # dx_perm on sampled rows: dh = W_down^T dy, [dg, du] from the saved g, u, then
+    # dx = W_gate^T dg + W_up^T du
+    rows = np.unique(np.concatenate([np.linspace(0, R - 1, 64).astype(np.int64), np.arange(R - 32, R)]))
+    rt = torch.from_numpy(rows).to(DEV)
+    dy_s, gu_s, dx_s = _np(dy_perm[rt]), _np(f["gu"][rt]), _np(g["dx_perm"][rt])
+    for n, r in enumerate(rows):
+        e = int(np.searchsorted(off, r, side="right") - 1)
+        dh = dy_s[n] @ wd[e]
+        dg, du = O.swiglu_grad(dh, gu_s[n, :I], gu_s[n, I:])
+        ref = wg[e].T @ dg + wu[e].T @ du
+        mag = np.abs(wg[e]).T @ np.abs(dg) + np.abs(wu[e]).T @ np.abs(du)
+        chk("dx_perm", dx_s[n], ref, mag)
+    # weight gradients of the first and the last expert on sampled elements
+    rng = np.random.default_rng(1)
+    for e in (0, w.E_l - 1):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        dy_e, x_e, h_e = _np(dy_perm[r0:r1]), _np(p["x_perm"][r0:r1]), _np(f["h_perm"][r0:r1])
+        gu_e = _np(f["gu"][r0:r1])
+        ii, jj = rng.integers(0, H, 16), rng.integers(0, I, 16)
+        ref = np.einsum("ri,ri->i", dy_e[:, ii], h_e[:, jj])
+        mag = np.einsum("ri,ri->i", np.abs(dy_e[:, ii]), np.abs(h_e[:, jj]))
+        chk("dw_down", _np(g["dw_down"][e])[ii, jj], ref, mag)
+        ci, ch = rng.integers(0, I, 8), rng.integers(0, H, 8)
+        dh = dy_e @ wd[e][:, ci]                       # [rows, 8] columns of dh
+        dg, du = O.swiglu_grad(dh, gu_e[:, ci], gu_e[:, I + ci])
+        for name, d in (("dw_gate", dg), ("dw_up", du)):
+            ref = np.einsum("ri,ri->i", d, x_e[:, ch])
+            mag = np.einsum("ri,ri->i", np.abs(d), np.abs(x_e[:, ch]))
+            chk(name, _np(g[name][e])[ci, ch], ref, mag)
+    chk.done()
+
+
 def test_inference_layer_gathers_and_equals_training_forward():
     """MoELayer(train=False) runs the maps-only permute and the gathering FFN
     forward; its output equals the training layer's forward bit for bit."""
